@@ -1,0 +1,287 @@
+"""fp64 CPU oracle for exact softmax attention: forward (O, LSE) and backward
+(dQ, dK, dV).
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product imports this module; only the
+tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline leg may call
+it.  It shares no code with the HIP kernels and is deliberately slow: it
+materialises the score matrix S, the probabilities P and the score gradient dS
+(row chunks bound the memory), in float64, with NumPy's ``exp``/``log`` and
+BLAS matrix products as the only library steps.
+
+What is computed (the tiled method of the pages reaches exactly this gradient,
+up to rounding order, because it only reorders the same sums):
+
+* scores      S = scale * Q_h K_g^T, with masked entries set to -inf
+  (rustytorch "flash_attention_backward.cu": the score recompute and causal mask
+  step of the tiled backward kernel; Triton issue "Extra transposes cause 8x
+  speedup ...": ``qk = q k^T * scale`` in ``_bwd_kernel``);
+* LSE_i       = log sum_j exp(S_ij), natural log, in the scaled-score domain;
+  P = exp(S - LSE) (the same two pages: probabilities rebuilt from the stored
+  per-row log-sum-exp);
+* O           = P V;
+* D_i         = sum_d dO_id O_id (rustytorch page: the per-row dot product of dO
+  and O; Triton page: the precomputed ``D`` loaded per query row);
+* dP          = dO V^T;  dS = P o (dP - D)  (rustytorch page: the dS step;
+  Triton page: ``ds = p * (dp - Di)``);
+* dQ          = scale * dS K;  dK = sum_{h in g} scale * dS^T Q_h;
+  dV          = sum_{h in g} P^T dO_h (rustytorch page: the dQ/dK/dV
+  accumulation; Triton page: ``dv += p^T do``, ``dk += ds^T q``, ``dq = ds k``).
+
+Readings where the pages are silent or disagree (each is listed in the design doc):
+
+* Causal masking is bottom-right aligned: query i may see key j iff
+  j <= i + (N_kv - N_q).  (The rustytorch kernel masks k_pos > q_pos with one
+  shared length, which is the N_q = N_kv special case of this rule.)
+* GQA maps query head h to key/value head h // (Hq/Hkv): consecutive query
+  heads share a key/value head (the Liger-Kernel pull request "[Kernel] Flash
+  attention 2" lists GQA without fixing the mapping).
+* A query row with no visible key (causal with N_q > N_kv, or N_kv = 0) has
+  O = 0, LSE = -inf and a zero dQ row; it contributes nothing to dK and dV.
+* The rustytorch kernel sums dQ over every row of a tile into one vector and
+  stores it to each row; that is a defect, and the oracle follows the
+  definition dQ = scale * dS K row by row instead.
+* The scale is applied to dS once, in the dQ and dK products; folding it into
+  dS first (Triton page) is the same number.
+
+Pinned (tests/test_oracle_cpu.py) by central finite differences of
+L = <dO, O>, the identities sum_j dS_ij = 0, sum_j dK_j = 0,
+sum_keys dV = sum_queries dO, <Q, dQ> = <K, dK>, <V, dV> = <dO, O>, closed forms
+(N_kv = 1; Q = 0), an independently written naive softmax forward, pure-Python
+brute force on a tiny case, and analytic golden fixtures.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Rows of S handled at once; bounds the temporary S/P/dS blocks to
+# ROW_CHUNK * N_kv float64 values each.
+ROW_CHUNK = 1024
+
+
+def as_f64(x) -> np.ndarray:
+    """Exact upcast of a float16/bfloat16/float32 tensor or array to float64."""
+    if hasattr(x, "detach"):  # torch tensor: go through float32, which is exact
+        x = x.detach().to("cpu").float().numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def kv_head_index(h: int, Hq: int, Hkv: int) -> int:
+    """Key/value head serving query head h: consecutive groups of Hq/Hkv."""
+    return h // (Hq // Hkv)
+
+
+def keep_mask(rows: np.ndarray, Nq: int, Nkv: int, causal: bool) -> np.ndarray:
+    """Boolean [len(rows), Nkv]: True where query row i may attend key j.
+
+    Causal is bottom-right aligned: keep iff j <= i + (Nkv - Nq).
+    """
+    rows = np.asarray(rows)
+    if not causal:
+        return np.ones((rows.shape[0], Nkv), dtype=bool)
+    j = np.arange(Nkv)
+    return j[None, :] <= rows[:, None] + (Nkv - Nq)
+
+
+def masked_scores(q_rows: np.ndarray, k: np.ndarray, scale: float,
+                  keep: np.ndarray) -> np.ndarray:
+    """S = scale * q_rows k^T with masked entries at -inf."""
+    s = scale * (q_rows @ k.T)
+    return np.where(keep, s, -np.inf)
+
+
+def log_sum_exp(s: np.ndarray) -> np.ndarray:
+    """Per-row natural-log sum of exp(S); -inf for a row with every entry masked."""
+    m = s.max(axis=1) if s.shape[1] > 0 else np.full(s.shape[0], -np.inf)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    with np.errstate(under="ignore"):
+        tot = np.exp(s - m_safe[:, None]).sum(axis=1)
+    out = m_safe + np.log(np.where(empty, 1.0, tot))
+    return np.where(empty, -np.inf, out)
+
+
+def probabilities(s: np.ndarray, lse: np.ndarray) -> np.ndarray:
+    """P = exp(S - LSE); zero on masked entries and on empty rows."""
+    lse_safe = np.where(np.isfinite(lse), lse, np.inf)
+    with np.errstate(under="ignore", invalid="ignore"):
+        p = np.exp(s - lse_safe[:, None])
+    return np.where(np.isfinite(s) & np.isfinite(lse)[:, None], p, 0.0)
+
+
+def row_delta(do_rows: np.ndarray, o_rows: np.ndarray) -> np.ndarray:
+    """D_i = sum_d dO_id * O_id."""
+    return (do_rows * o_rows).sum(axis=1)
+
+
+def score_grad(p: np.ndarray, dp: np.ndarray, dlt: np.ndarray) -> np.ndarray:
+    """dS = P o (dP - D): gradient of the loss with respect to the scaled scores."""
+    return p * (dp - dlt[:, None])
+
+
+def grad_q(ds: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
+    return scale * (ds @ k)
+
+
+def grad_k(ds: np.ndarray, q_rows: np.ndarray, scale: float) -> np.ndarray:
+    return scale * (ds.T @ q_rows)
+
+
+def grad_v(p: np.ndarray, do_rows: np.ndarray) -> np.ndarray:
+    return p.T @ do_rows
+
+
+def _check_shapes(q, k, v):
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nkv, dk = k.shape
+    if v.shape != k.shape or Bk != B or dk != d or Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError(f"bad shapes q={q.shape} k={k.shape} v={v.shape}")
+    return B, Hq, Hkv, Nq, Nkv, d
+
+
+def _row_chunks(rows: np.ndarray):
+    for s in range(0, rows.shape[0], ROW_CHUNK):
+        yield rows[s:s + ROW_CHUNK]
+
+
+def forward(q, k, v, scale: float, causal: bool):
+    """O [B,Hq,Nq,d] and LSE [B,Hq,Nq] in float64."""
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    B, Hq, Hkv, Nq, Nkv, d = _check_shapes(q, k, v)
+    o = np.zeros((B, Hq, Nq, d))
+    lse = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_index(h, Hq, Hkv)
+            for rows in _row_chunks(np.arange(Nq)):
+                s = masked_scores(q[b, h, rows], k[b, g], scale,
+                                  keep_mask(rows, Nq, Nkv, causal))
+                l_ = log_sum_exp(s)
+                p = probabilities(s, l_)
+                o[b, h, rows] = p @ v[b, g]
+                lse[b, h, rows] = l_
+    return o, lse
+
+
+def backward(q, k, v, do, scale: float, causal: bool, return_delta: bool = False):
+    """dQ, dK, dV in float64 from the definition (O and LSE recomputed here).
+
+    With ``return_delta`` also returns D [B,Hq,Nq] computed from the oracle's
+    own float64 O.
+    """
+    q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    B, Hq, Hkv, Nq, Nkv, d = _check_shapes(q, k, v)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dlt_all = np.zeros((B, Hq, Nq))
+    for b in range(B):
+        for h in range(Hq):
+            g = kv_head_index(h, Hq, Hkv)
+            for rows in _row_chunks(np.arange(Nq)):
+                qr, dor = q[b, h, rows], do[b, h, rows]
+                s = masked_scores(qr, k[b, g], scale, keep_mask(rows, Nq, Nkv, causal))
+                p = probabilities(s, log_sum_exp(s))
+                o_rows = p @ v[b, g]
+                dlt = row_delta(dor, o_rows)
+                dp = dor @ v[b, g].T
+                ds = score_grad(p, dp, dlt)
+                dq[b, h, rows] = grad_q(ds, k[b, g], scale)
+                dk[b, g] += grad_k(ds, qr, scale)
+                dv[b, g] += grad_v(p, dor)
+                dlt_all[b, h, rows] = dlt
+    if return_delta:
+        return dq, dk, dv, dlt_all
+    return dq, dk, dv
+
+
+def score_grad_matrix(q, k, v, do, scale: float, causal: bool, b: int, h: int):
+    """The full dS matrix of one (batch, query head); for identity checks."""
+    q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    B, Hq, Hkv, Nq, Nkv, d = _check_shapes(q, k, v)
+    g = kv_head_index(h, Hq, Hkv)
+    rows = np.arange(Nq)
+    s = masked_scores(q[b, h], k[b, g], scale, keep_mask(rows, Nq, Nkv, causal))
+    p = probabilities(s, log_sum_exp(s))
+    dlt = row_delta(do[b, h], p @ v[b, g])
+    return score_grad(p, do[b, h] @ v[b, g].T, dlt)
+
+
+def naive_forward(q, k, v, scale: float, causal: bool):
+    """softmax(scale * Q K^T) V written without a log-sum-exp: normalise
+    exp(S - rowmax) by its row sum.  Written separately from ``forward`` so the
+    two can be compared; O only."""
+    q, k, v = as_f64(q), as_f64(k), as_f64(v)
+    B, Hq, Hkv, Nq, Nkv, d = _check_shapes(q, k, v)
+    out = np.zeros((B, Hq, Nq, d))
+    for b in range(B):
+        for h in range(Hq):
+            kk = k[b, h // (Hq // Hkv)]
+            vv = v[b, h // (Hq // Hkv)]
+            for i in range(Nq):
+                allowed = [j for j in range(Nkv) if (not causal) or j - i <= Nkv - Nq]
+                if not allowed:
+                    continue
+                logits = np.array([scale * float(np.dot(q[b, h, i], kk[j])) for j in allowed])
+                w = np.exp(logits - logits.max())
+                w = w / w.sum()
+                out[b, h, i] = w @ vv[allowed]
+    return out
+
+
+# --- Row-sampled variants for shapes too large to materialise whole --------------
+
+def forward_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows):
+    """O and LSE of selected query rows of one (batch, head); cost O(len(rows)*Nkv*d)."""
+    rows = np.asarray(rows)
+    Hq, Hkv = q.shape[1], k.shape[1]
+    Nq, Nkv = q.shape[2], k.shape[2]
+    g = kv_head_index(h, Hq, Hkv)
+    qr = as_f64(q[b, h][rows])
+    kg, vg = as_f64(k[b, g]), as_f64(v[b, g])
+    s = masked_scores(qr, kg, scale, keep_mask(rows, Nq, Nkv, causal))
+    l_ = log_sum_exp(s)
+    return probabilities(s, l_) @ vg, l_
+
+
+def dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: int, rows):
+    """dQ of selected query rows; each row needs only its own S, P and dP rows."""
+    rows = np.asarray(rows)
+    Hq, Hkv = q.shape[1], k.shape[1]
+    Nq, Nkv = q.shape[2], k.shape[2]
+    g = kv_head_index(h, Hq, Hkv)
+    qr, dor = as_f64(q[b, h][rows]), as_f64(do[b, h][rows])
+    kg, vg = as_f64(k[b, g]), as_f64(v[b, g])
+    s = masked_scores(qr, kg, scale, keep_mask(rows, Nq, Nkv, causal))
+    p = probabilities(s, log_sum_exp(s))
+    ds = score_grad(p, dor @ vg.T, row_delta(dor, p @ vg))
+    return grad_q(ds, kg, scale)
+
+
+def dkdv_rows(q, k, v, do, scale: float, causal: bool, b: int, g: int, kv_rows):
+    """dK and dV of selected key rows of one (batch, kv head).
+
+    Only query rows that can see one of the selected keys contribute; with a
+    causal mask and keys near the end of the sequence that is a short tail, so
+    this stays cheap at any length.
+    """
+    kv_rows = np.asarray(kv_rows)
+    Hq, Hkv = q.shape[1], k.shape[1]
+    Nq, Nkv, d = q.shape[2], k.shape[2], q.shape[3]
+    kg, vg = as_f64(k[b, g]), as_f64(v[b, g])
+    dk_out = np.zeros((kv_rows.shape[0], d))
+    dv_out = np.zeros((kv_rows.shape[0], d))
+    first = 0
+    if causal and kv_rows.shape[0] > 0:
+        first = max(0, int(kv_rows.min()) - (Nkv - Nq))
+    contributing = np.arange(first, Nq)
+    for h in range(Hq):
+        if kv_head_index(h, Hq, Hkv) != g:
+            continue
+        for rows in _row_chunks(contributing):
+            qr, dor = as_f64(q[b, h][rows]), as_f64(do[b, h][rows])
+            s = masked_scores(qr, kg, scale, keep_mask(rows, Nq, Nkv, causal))
+            p = probabilities(s, log_sum_exp(s))
+            ds = score_grad(p, dor @ vg.T, row_delta(dor, p @ vg))
+            dk_out += grad_k(ds[:, kv_rows], qr, scale)
+            dv_out += grad_v(p[:, kv_rows], dor)
+    return dk_out, dv_out
