@@ -1,0 +1,207 @@
+// C entry points of libfa_mi355x.so: argument checks, workspace carve-up and
+// kernel sequencing.  Every check runs on the host before the first launch, so a
+// rejected call enqueues nothing and writes nothing.
+#include "fa_mi355x.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_internal.hpp"
+
+namespace fa {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WorkspaceLayout workspace_layout(const Problem& pb, bool atomic_dq) {
+  const size_t rows = (size_t)pb.B * pb.Hq * pb.Nq;
+  WorkspaceLayout L;
+  L.delta_off = 0;
+  L.lse2_off = align256(rows * sizeof(float));
+  L.dqacc_off = L.lse2_off + align256(rows * sizeof(float));
+  L.total = L.dqacc_off + (atomic_dq ? align256(rows * pb.d * sizeof(float)) : 0);
+  if (rows == 0) L.total = 0;
+  return L;
+}
+
+static int check_problem(int B, int Hq, int Hkv, int Nq, int Nkv, int d, float scale, int dtype,
+                         Problem* out) {
+  if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (B < 0 || Nq < 0 || Nkv < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (B > 65535 || Hq > 65535) return FA_ERR_SHAPE;  // grid y/z limits
+  if ((int64_t)Nq * d >= ((int64_t)1 << 31) || (int64_t)Nkv * d >= ((int64_t)1 << 31))
+    return FA_ERR_SHAPE;
+  // total element counts must stay well inside size_t arithmetic
+  if ((double)B * Hq * (double)Nq * d > 9.0e15 || (double)B * Hkv * (double)Nkv * d > 9.0e15)
+    return FA_ERR_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+  out->B = B;
+  out->Hq = Hq;
+  out->Hkv = Hkv;
+  out->Nq = Nq;
+  out->Nkv = Nkv;
+  out->d = d;
+  out->scale = scale;
+  out->dtype = dtype;
+  out->causal = false;
+  return FA_OK;
+}
+
+// A pointer is acceptable when the tensor is empty, or when it is non-NULL and
+// 16-byte aligned.
+static int check_ptr(const void* ptr, size_t elems) {
+  if (elems == 0) return FA_OK;
+  if (ptr == nullptr) return FA_ERR_NULLPTR;
+  if (((uintptr_t)ptr & 15u) != 0) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+static int resolve_dq_mode(const Problem& pb, int mode) {
+  if (mode == FA_DQ_ATOMIC || mode == FA_DQ_SEPARATE) return mode;
+  (void)pb;
+  return FA_DQ_ATOMIC;
+}
+
+}  // namespace fa
+
+using namespace fa;
+
+#define FA_TRY(expr)            \
+  do {                          \
+    const int _st = (expr);     \
+    if (_st != FA_OK) return _st; \
+  } while (0)
+
+extern "C" {
+
+int fa_version(void) { return 100; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULLPTR: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "invalid shape (B, Hq, Hkv, N_q, N_kv), Hq % Hkv != 0, or a size limit exceeded";
+    case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
+    case FA_ERR_SCALE: return "softmax_scale must be finite and > 0";
+    case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned, or smaller than required";
+    case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case FA_ERR_HIP: return "a HIP kernel launch failed";
+    case FA_ERR_MODE: return "unknown dq_mode";
+    default: return "unknown status";
+  }
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+           int Nq, int Nkv, int d, float softmax_scale, int causal, int dtype, void* stream) {
+  Problem pb;
+  FA_TRY(check_problem(B, Hq, Hkv, Nq, Nkv, d, softmax_scale, dtype, &pb));
+  pb.causal = causal != 0;
+  const size_t nq = (size_t)B * Hq * Nq * d, nk = (size_t)B * Hkv * Nkv * d;
+  const size_t nrows = (size_t)B * Hq * Nq;
+  // K and V are read only when some query row exists.
+  const size_t nk_used = nrows ? nk : 0;
+  FA_TRY(check_ptr(q, nq));
+  FA_TRY(check_ptr(k, nk_used));
+  FA_TRY(check_ptr(v, nk_used));
+  FA_TRY(check_ptr(o, nq));
+  FA_TRY(check_ptr(lse, nrows));
+  FwdArgs a{pb, q, k, v, o, lse};
+  if (nrows == 0) return FA_OK;  // nothing to compute; no HIP call at all
+  (void)hipGetLastError();
+  if (launch_fwd(a, (hipStream_t)stream) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+size_t fa_bwd_ex_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal,
+                                 int dtype, int dq_mode) {
+  Problem pb;
+  if (check_problem(B, Hq, Hkv, Nq, Nkv, d, 1.0f, dtype, &pb) != FA_OK) return 0;
+  if (dq_mode != FA_DQ_AUTO && dq_mode != FA_DQ_ATOMIC && dq_mode != FA_DQ_SEPARATE) return 0;
+  pb.causal = causal != 0;
+  const int mode = resolve_dq_mode(pb, dq_mode);
+  return workspace_layout(pb, mode == FA_DQ_ATOMIC).total;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal,
+                              int dtype) {
+  return fa_bwd_ex_workspace_bytes(B, Hq, Hkv, Nq, Nkv, d, causal, dtype, FA_DQ_AUTO);
+}
+
+int fa_bwd_auto_dq_mode(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal, int dtype) {
+  Problem pb;
+  if (check_problem(B, Hq, Hkv, Nq, Nkv, d, 1.0f, dtype, &pb) != FA_OK) return FA_DQ_ATOMIC;
+  pb.causal = causal != 0;
+  return resolve_dq_mode(pb, FA_DQ_AUTO);
+}
+
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const float* lse,
+              const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+              int Nkv, int d, float softmax_scale, int causal, int dtype, int dq_mode,
+              void* ev_begin, void* ev_end, void* workspace, size_t workspace_bytes,
+              void* stream) {
+  Problem pb;
+  FA_TRY(check_problem(B, Hq, Hkv, Nq, Nkv, d, softmax_scale, dtype, &pb));
+  pb.causal = causal != 0;
+  if (dq_mode != FA_DQ_AUTO && dq_mode != FA_DQ_ATOMIC && dq_mode != FA_DQ_SEPARATE)
+    return FA_ERR_MODE;
+  const size_t nq = (size_t)B * Hq * Nq * d, nk = (size_t)B * Hkv * Nkv * d;
+  const size_t nrows = (size_t)B * Hq * Nq;
+  // dK/dV are written whenever they have elements (zeros when N_q = 0).
+  FA_TRY(check_ptr(q, nq));
+  FA_TRY(check_ptr(k, nk));
+  FA_TRY(check_ptr(v, nk));
+  FA_TRY(check_ptr(o, nq));
+  FA_TRY(check_ptr(lse, nrows));
+  FA_TRY(check_ptr(dout, nq));
+  FA_TRY(check_ptr(dq, nq));
+  FA_TRY(check_ptr(dk, nk));
+  FA_TRY(check_ptr(dv, nk));
+  const int mode = resolve_dq_mode(pb, dq_mode);
+  const bool atomic = mode == FA_DQ_ATOMIC;
+  const WorkspaceLayout L = workspace_layout(pb, atomic);
+  if (L.total > 0) {
+    if (workspace == nullptr || ((uintptr_t)workspace & 15u) != 0 || workspace_bytes < L.total)
+      return FA_ERR_WORKSPACE;
+  }
+  char* ws = static_cast<char*>(workspace);
+  BwdArgs a;
+  a.pb = pb;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = L.total ? reinterpret_cast<float*>(ws + L.delta_off) : nullptr;
+  a.lse2 = L.total ? reinterpret_cast<float*>(ws + L.lse2_off) : nullptr;
+  a.dq_acc = (L.total && atomic) ? reinterpret_cast<float*>(ws + L.dqacc_off) : nullptr;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (nrows == 0 && nk == 0) return FA_OK;  // nothing to compute; no HIP call at all
+  (void)hipGetLastError();
+  if (launch_bwd_pre(a, atomic, s) != hipSuccess) return FA_ERR_HIP;
+  if (ev_begin && hipEventRecord((hipEvent_t)ev_begin, s) != hipSuccess) return FA_ERR_HIP;
+  if (launch_bwd_dkdv(a, atomic, s) != hipSuccess) return FA_ERR_HIP;
+  if (ev_end && hipEventRecord((hipEvent_t)ev_end, s) != hipSuccess) return FA_ERR_HIP;
+  if (atomic) {
+    if (launch_bwd_dq_convert(a, s) != hipSuccess) return FA_ERR_HIP;
+  } else {
+    if (launch_bwd_dq(a, s) != hipSuccess) return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+           int Nkv, int d, float softmax_scale, int causal, int dtype, void* workspace,
+           size_t workspace_bytes, void* stream) {
+  return fa_bwd_ex(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, d, softmax_scale,
+                   causal, dtype, FA_DQ_AUTO, nullptr, nullptr, workspace, workspace_bytes,
+                   stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,488 @@
+// Backward kernels of exact softmax attention.
+//
+//   bwd_pre   D_i = sum_d dO_id O_id per query row (rustytorch
+//             "flash_attention_backward.cu" computes this row dot product inside
+//             its tiled kernel; the Triton issue "Extra transposes cause 8x speedup
+//             for sequence-parallel Flash Attention backward" loads it precomputed),
+//             LSE rescaled to the log2 domain, and, for the atomic dQ path, the
+//             float32 dQ buffer cleared.
+//   bwd_dkdv  key/value-block-parallel dK and dV (the Triton issue's _bwd_kernel
+//             structure: one program per key block, K and V resident, a loop over
+//             query blocks).  Optionally also dQ += dS K with float atomics.
+//   bwd_dq    query-block-parallel dQ pass (the decomposition of the rustytorch
+//             kernel's grid), recomputing S, P, dP and dS; writes dQ once.
+//   dq_convert  float32 dQ buffer -> dtype.
+//
+// Per (query tile i, key tile j) the math is, with s the softmax scale:
+//   S = s Q_i K_j^T,  P = exp(S - LSE_i),  dV_j += P^T dO_i,  dP = dO_i V_j^T,
+//   dS = P o (dP - D_i),  dK_j += s dS^T Q_i,  dQ_i += s dS K_j.
+// Exponentials run in the log2 domain: P = exp2(S * s * log2 e - LSE_i * log2 e).
+#include "fa_common.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;
+  float* lse2;
+  float* dq_acc;
+  int Hq, Hkv, Nq, Nkv, G, off;  // off = Nkv - Nq (bottom-right causal offset)
+  float scale, scale_log2;
+  size_t rows;  // B * Hq * Nq
+};
+
+static BwdParams make_params(const BwdArgs& a) {
+  BwdParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.o = static_cast<const uint16_t*>(a.o);
+  p.dout = static_cast<const uint16_t*>(a.dout);
+  p.lse = a.lse;
+  p.dq = static_cast<uint16_t*>(a.dq);
+  p.dk = static_cast<uint16_t*>(a.dk);
+  p.dv = static_cast<uint16_t*>(a.dv);
+  p.delta = a.delta;
+  p.lse2 = a.lse2;
+  p.dq_acc = a.dq_acc;
+  p.Hq = a.pb.Hq;
+  p.Hkv = a.pb.Hkv;
+  p.Nq = a.pb.Nq;
+  p.Nkv = a.pb.Nkv;
+  p.G = a.pb.Hq / a.pb.Hkv;
+  p.off = a.pb.Nkv - a.pb.Nq;
+  p.scale = a.pb.scale;
+  p.scale_log2 = a.pb.scale * kLog2e;
+  p.rows = (size_t)a.pb.B * a.pb.Hq * a.pb.Nq;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// Row preprocess.  D/8 lanes share a row; each lane reads 16 bytes of O and dO.
+template <int DT, int D, bool ZERO_DQ>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float s = 0.f;
+  if (row < p.rows) {
+    const u32x4 a = ld16(p.o + row * D + part * 8);
+    const u32x4 c = ld16(p.dout + row * D + part * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      s += Dt<DT>::lo(a[j]) * Dt<DT>::lo(c[j]) + Dt<DT>::hi(a[j]) * Dt<DT>::hi(c[j]);
+    if (ZERO_DQ) {
+      float* z = p.dq_acc + row * D + part * 8;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(z) = zero;
+      *reinterpret_cast<f32x4*>(z + 4) = zero;
+    }
+  }
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (row < p.rows && part == 0) {
+    p.delta[row] = s;
+    const float L = p.lse[row];
+    p.lse2[row] = (L == -INFINITY) ? INFINITY : L * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV kernel.  Workgroup = 4 waves = 128 key rows of one (batch, kv head); wave w
+// owns key rows 32w..32w+31 of the tile and keeps their K and V as MFMA operands in
+// registers and their dK and dV as float32 accumulators.  The loop runs over the
+// G query heads of the group and, per head, over 64-row query tiles from the first
+// one that can see the key tile (causal) to the end.
+//
+// S = Q K^T is computed with the key index in the lane (C column), so P^T and
+// dS^T feed dV += P^T dO and dK += dS^T Q directly from the accumulators; dO and Q
+// are then needed with the query index along the operand slots, which a transposed
+// LDS copy provides.
+template <int DT, int D, bool CAUSAL, bool ATOMIC_DQ>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int BN = 128, BM = 64;
+  constexpr int LDR = D + 8;    // row-major Q / dO tiles [query][d]
+  constexpr int LDT = BM + 4;   // transposed Q / dO tiles [d][query]
+  constexpr int LDSS = BN + 8;  // dS tile [query][key]
+  constexpr int LDKT = BN + 8;  // transposed K tile [d][key]
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[BM * LDR];
+  __shared__ __attribute__((aligned(16))) uint16_t dOs[BM * LDR];
+  __shared__ __attribute__((aligned(16))) uint16_t QTs[D * LDT];
+  __shared__ __attribute__((aligned(16))) uint16_t dOTs[D * LDT];
+  __shared__ float lse_s[BM];
+  __shared__ float dlt_s[BM];
+  __shared__ __attribute__((aligned(16))) uint16_t dSs[ATOMIC_DQ ? BM * LDSS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t KTs[ATOMIC_DQ ? D * LDKT : 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int hk = blockIdx.y, b = blockIdx.z;
+  const int kv0 = blockIdx.x * BN;
+  const int kvw = kv0 + 32 * w;
+  const int kv_lane = kvw + l32;  // key row this lane carries as S column
+  const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
+  const uint16_t* __restrict__ K = p.k + kbase * D;
+  const uint16_t* __restrict__ V = p.v + kbase * D;
+
+  u32x4 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    kf[s] = kv_lane < p.Nkv ? ld16(K + (size_t)kv_lane * D + 16 * s + 8 * g) : zero_u4();
+    vf[s] = kv_lane < p.Nkv ? ld16(V + (size_t)kv_lane * D + 16 * s + 8 * g) : zero_u4();
+  }
+  if (ATOMIC_DQ) {
+    for (int c = tid; c < BN * D / 8; c += 256) {
+      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int kr = kv0 + r;
+      const u32x4 kk = kr < p.Nkv ? ld16(K + (size_t)kr * D + col) : zero_u4();
+      lds_store_transposed(KTs, LDKT, r, col, kk);
+    }
+  }
+
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) {
+    dk[n] = zero16();
+    dv[n] = zero16();
+  }
+
+  const int q_begin = CAUSAL ? max(0, kv0 - p.off) : 0;
+  const int nqt = (p.Nq + BM - 1) / BM;
+  const int qt_begin = q_begin < p.Nq ? q_begin / BM : nqt;
+
+  for (int hh = 0; hh < p.G; ++hh) {
+    const int h = hk * p.G + hh;
+    const size_t qbase = ((size_t)b * p.Hq + h) * (size_t)p.Nq;
+    const uint16_t* __restrict__ Qh = p.q + qbase * D;
+    const uint16_t* __restrict__ dOh = p.dout + qbase * D;
+    const float* __restrict__ L2 = p.lse2 + qbase;
+    const float* __restrict__ DL = p.delta + qbase;
+
+    for (int qt = qt_begin; qt < nqt; ++qt) {
+      const int q0 = qt * BM;
+      __syncthreads();
+#pragma unroll
+      for (int c = tid; c < BM * D / 8; c += 256) {
+        const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+        const int qr = q0 + r;
+        u32x4 qa = zero_u4(), da = zero_u4();
+        if (qr < p.Nq) {
+          qa = ld16(Qh + (size_t)qr * D + col);
+          da = ld16(dOh + (size_t)qr * D + col);
+        }
+        *reinterpret_cast<u32x4*>(Qs + r * LDR + col) = qa;
+        *reinterpret_cast<u32x4*>(dOs + r * LDR + col) = da;
+        lds_store_transposed(QTs, LDT, r, col, qa);
+        lds_store_transposed(dOTs, LDT, r, col, da);
+      }
+      if (tid < BM) {
+        const int qr = q0 + tid;
+        lse_s[tid] = qr < p.Nq ? L2[qr] : INFINITY;
+        dlt_s[tid] = qr < p.Nq ? DL[qr] : 0.f;
+      }
+      __syncthreads();
+
+      f32x16 sp[BM / 32], dp[BM / 32];
+#pragma unroll
+      for (int t = 0; t < BM / 32; ++t) {
+        sp[t] = zero16();
+        dp[t] = zero16();
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(Qs + (32 * t + l32) * LDR + 16 * s + 8 * g);
+          sp[t] = Dt<DT>::mma(a, kf[s], sp[t]);
+          const u32x4 a2 = *reinterpret_cast<const u32x4*>(dOs + (32 * t + l32) * LDR + 16 * s + 8 * g);
+          dp[t] = Dt<DT>::mma(a2, vf[s], dp[t]);
+        }
+      }
+
+      // P and dS in place (sp <- P, dp <- dS), indexed [query row crow][key kv_lane].
+#pragma unroll
+      for (int t = 0; t < BM / 32; ++t) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int ql = 32 * t + crow_of(i, g);
+          const bool masked = kv_lane >= p.Nkv || (CAUSAL && kv_lane > q0 + ql + p.off);
+          float pv = fast_exp2(sp[t][i] * p.scale_log2 - lse_s[ql]);
+          pv = masked ? 0.f : pv;
+          sp[t][i] = pv;
+          dp[t][i] = pv * (dp[t][i] - dlt_s[ql]);
+        }
+      }
+
+#pragma unroll
+      for (int t = 0; t < BM / 32; ++t) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const u32x4 pa = pack_c_slice<DT>(sp[t], c);
+          const u32x4 sa = pack_c_slice<DT>(dp[t], c);
+#pragma unroll
+          for (int n = 0; n < D / 32; ++n) {
+            const u32x4 bo = lds_read_crow_operand(dOTs, LDT, 32 * n + l32, 32 * t, c, g);
+            dv[n] = Dt<DT>::mma(pa, bo, dv[n]);
+            const u32x4 bq = lds_read_crow_operand(QTs, LDT, 32 * n + l32, 32 * t, c, g);
+            dk[n] = Dt<DT>::mma(sa, bq, dk[n]);
+          }
+        }
+      }
+
+      if (ATOMIC_DQ) {
+#pragma unroll
+        for (int t = 0; t < BM / 32; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            dSs[(32 * t + crow_of(i, g)) * LDSS + 32 * w + l32] = Dt<DT>::one(dp[t][i]);
+        __syncthreads();
+        float* __restrict__ dQacc = p.dq_acc + qbase * D;
+        constexpr int NT = (BM / 32) * (D / 32);
+        for (int tt = w; tt < NT; tt += 4) {
+          const int tq = tt / (D / 32), tn = tt % (D / 32);
+          f32x16 acc = zero16();
+#pragma unroll
+          for (int ks = 0; ks < BN / 16; ++ks) {
+            const u32x4 a = *reinterpret_cast<const u32x4*>(dSs + (32 * tq + l32) * LDSS + 16 * ks + 8 * g);
+            const u32x4 bk = *reinterpret_cast<const u32x4*>(KTs + (32 * tn + l32) * LDKT + 16 * ks + 8 * g);
+            acc = Dt<DT>::mma(a, bk, acc);
+          }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qg = q0 + 32 * tq + crow_of(i, g);
+            if (qg < p.Nq) atomicAdd(dQacc + (size_t)qg * D + 32 * tn + l32, acc[i] * p.scale);
+          }
+        }
+      }
+    }
+  }
+
+  uint16_t* __restrict__ dK = p.dk + kbase * D;
+  uint16_t* __restrict__ dV = p.dv + kbase * D;
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kr = kvw + crow_of(i, g);
+      if (kr < p.Nkv) {
+        dK[(size_t)kr * D + 32 * n + l32] = Dt<DT>::one(dk[n][i] * p.scale);
+        dV[(size_t)kr * D + 32 * n + l32] = Dt<DT>::one(dv[n][i]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Separate dQ pass.  Workgroup = 4 waves = 128 query rows of one (batch, query
+// head); wave w owns 32 of them and keeps their Q and dO as MFMA operands in
+// registers.  S^T = K Q^T puts the query index in the lane, so dS feeds
+// dQ += dS K straight from the accumulators; K is read from a transposed LDS copy.
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
+  constexpr int BM = 128, BN = 64;
+  constexpr int LDR = D + 8;
+  constexpr int LDKT = BN + 4;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * LDR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * LDR];
+  __shared__ __attribute__((aligned(16))) uint16_t KTs[D * LDKT];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / p.G;
+  const int q0 = blockIdx.x * BM;
+  const int qrow = q0 + 32 * w + l32;
+  const size_t qbase = ((size_t)b * p.Hq + h) * (size_t)p.Nq;
+  const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
+  const uint16_t* __restrict__ K = p.k + kbase * D;
+  const uint16_t* __restrict__ V = p.v + kbase * D;
+
+  u32x4 qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    qf[s] = qrow < p.Nq ? ld16(p.q + (qbase + qrow) * D + 16 * s + 8 * g) : zero_u4();
+    df[s] = qrow < p.Nq ? ld16(p.dout + (qbase + qrow) * D + 16 * s + 8 * g) : zero_u4();
+  }
+  const float lse_q = qrow < p.Nq ? p.lse2[qbase + qrow] : INFINITY;
+  const float dlt_q = qrow < p.Nq ? p.delta[qbase + qrow] : 0.f;
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) acc[n] = zero16();
+
+  int kv_end = p.Nkv;
+  if (CAUSAL) {
+    const int q_last = min(q0 + BM, p.Nq) - 1;
+    kv_end = min(p.Nkv, q_last + p.off + 1);
+  }
+  const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int kv0 = kt * BN;
+    __syncthreads();
+#pragma unroll
+    for (int c = tid; c < BN * D / 8; c += 256) {
+      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int kr = kv0 + r;
+      u32x4 kk = zero_u4(), vv = zero_u4();
+      if (kr < p.Nkv) {
+        kk = ld16(K + (size_t)kr * D + col);
+        vv = ld16(V + (size_t)kr * D + col);
+      }
+      *reinterpret_cast<u32x4*>(Ks + r * LDR + col) = kk;
+      *reinterpret_cast<u32x4*>(Vs + r * LDR + col) = vv;
+      lds_store_transposed(KTs, LDKT, r, col, kk);
+    }
+    __syncthreads();
+
+    f32x16 st[BN / 32], dpt[BN / 32];
+#pragma unroll
+    for (int t = 0; t < BN / 32; ++t) {
+      st[t] = zero16();
+      dpt[t] = zero16();
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(Ks + (32 * t + l32) * LDR + 16 * s + 8 * g);
+        st[t] = Dt<DT>::mma(a, qf[s], st[t]);
+        const u32x4 a2 = *reinterpret_cast<const u32x4*>(Vs + (32 * t + l32) * LDR + 16 * s + 8 * g);
+        dpt[t] = Dt<DT>::mma(a2, df[s], dpt[t]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < BN / 32; ++t) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kv = kv0 + 32 * t + crow_of(i, g);
+        const bool masked = kv >= p.Nkv || (CAUSAL && kv > qrow + p.off);
+        float pv = fast_exp2(st[t][i] * p.scale_log2 - lse_q);
+        pv = masked ? 0.f : pv;
+        dpt[t][i] = pv * (dpt[t][i] - dlt_q);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < BN / 32; ++t) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 a = pack_c_slice<DT>(dpt[t], c);
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n) {
+          const u32x4 bk = lds_read_crow_operand(KTs, LDKT, 32 * n + l32, 32 * t, c, g);
+          acc[n] = Dt<DT>::mma(a, bk, acc[n]);
+        }
+      }
+    }
+  }
+
+  uint16_t* __restrict__ dQ = p.dq + qbase * D;
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int qr = q0 + 32 * w + crow_of(i, g);
+      if (qr < p.Nq) dQ[(size_t)qr * D + 32 * n + l32] = Dt<DT>::one(acc[n][i] * p.scale);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int DT>
+__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ src,
+                                                         uint16_t* __restrict__ dst, size_t n8) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const f32x4 a = *reinterpret_cast<const f32x4*>(src + 8 * i);
+  const f32x4 c = *reinterpret_cast<const f32x4*>(src + 8 * i + 4);
+  u32x4 r;
+  r[0] = Dt<DT>::pack2(a[0], a[1]);
+  r[1] = Dt<DT>::pack2(a[2], a[3]);
+  r[2] = Dt<DT>::pack2(c[0], c[1]);
+  r[3] = Dt<DT>::pack2(c[2], c[3]);
+  st16(dst + 8 * i, r);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+static inline int dispatch_key(const Problem& pb) {
+  return pb.dtype * 4 + (pb.d == 128 ? 2 : 0) + (pb.causal ? 1 : 0);
+}
+
+#define FA_DISPATCH(KEY, FN, ...)                        \
+  switch (KEY) {                                         \
+    case 0: return FN<0, 64, false>(__VA_ARGS__);        \
+    case 1: return FN<0, 64, true>(__VA_ARGS__);         \
+    case 2: return FN<0, 128, false>(__VA_ARGS__);       \
+    case 3: return FN<0, 128, true>(__VA_ARGS__);        \
+    case 4: return FN<1, 64, false>(__VA_ARGS__);        \
+    case 5: return FN<1, 64, true>(__VA_ARGS__);         \
+    case 6: return FN<1, 128, false>(__VA_ARGS__);       \
+    default: return FN<1, 128, true>(__VA_ARGS__);       \
+  }
+
+template <int DT, int D, bool CAUSAL>
+static hipError_t pre_t(const BwdArgs& a, bool zero, hipStream_t s) {
+  const BwdParams p = make_params(a);
+  constexpr int RPB = 256 / (D / 8);
+  const dim3 grid((unsigned)((p.rows + RPB - 1) / RPB));
+  if (zero)
+    hipLaunchKernelGGL((bwd_pre_kernel<DT, D, true>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_pre_kernel<DT, D, false>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pre(const BwdArgs& a, bool zero_dq_acc, hipStream_t s) {
+  if ((size_t)a.pb.B * a.pb.Hq * a.pb.Nq == 0) return hipSuccess;
+  FA_DISPATCH(dispatch_key(a.pb), pre_t, a, zero_dq_acc, s)
+}
+
+template <int DT, int D, bool CAUSAL>
+static hipError_t dkdv_t(const BwdArgs& a, bool atomic, hipStream_t s) {
+  const BwdParams p = make_params(a);
+  const dim3 grid((a.pb.Nkv + 127) / 128, a.pb.Hkv, a.pb.B);
+  if (atomic)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL, true>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL, false>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, bool atomic_dq, hipStream_t s) {
+  if ((size_t)a.pb.B * a.pb.Nkv == 0) return hipSuccess;
+  FA_DISPATCH(dispatch_key(a.pb), dkdv_t, a, atomic_dq, s)
+}
+
+template <int DT, int D, bool CAUSAL>
+static hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
+  const BwdParams p = make_params(a);
+  const dim3 grid((a.pb.Nq + 127) / 128, a.pb.Hq, a.pb.B);
+  hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
+  if ((size_t)a.pb.B * a.pb.Nq == 0) return hipSuccess;
+  FA_DISPATCH(dispatch_key(a.pb), dq_t, a, s)
+}
+
+hipError_t launch_bwd_dq_convert(const BwdArgs& a, hipStream_t s) {
+  const size_t n = (size_t)a.pb.B * a.pb.Hq * a.pb.Nq * a.pb.d;
+  if (n == 0) return hipSuccess;
+  const size_t n8 = n / 8;  // d is a multiple of 8
+  const dim3 grid((unsigned)((n8 + 255) / 256));
+  if (a.pb.dtype == 0)
+    hipLaunchKernelGGL((dq_convert_kernel<0>), grid, dim3(256), 0, s, a.dq_acc,
+                       static_cast<uint16_t*>(a.dq), n8);
+  else
+    hipLaunchKernelGGL((dq_convert_kernel<1>), grid, dim3(256), 0, s, a.dq_acc,
+                       static_cast<uint16_t*>(a.dq), n8);
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -1,0 +1,200 @@
+// Forward kernel: O and LSE of exact softmax attention.
+//
+// The backward needs the per-row log-sum-exp of the scaled scores (rustytorch
+// "flash_attention_backward.cu" and the Triton issue "Extra transposes cause 8x
+// speedup for sequence-parallel Flash Attention backward" both rebuild P as
+// exp(S - LSE) from it); no page prints a forward kernel, so this one is the
+// usual streaming (online) softmax over key tiles.
+//
+// One workgroup = 4 waves = 128 query rows of one (batch, query head); each wave
+// owns 32 rows.  Per key tile of 64 rows:
+//   S^T = K Q^T       (MFMA; Q stays in registers as the B operand for the whole
+//                      loop, K is read from LDS)
+//   online max / sum  (each lane owns one query column of S^T, so the row
+//                      reductions are in-lane plus one swap between lane halves)
+//   O^T += V^T P^T    (MFMA; P^T comes straight from the S^T accumulators, V^T is
+//                      read from a transposed LDS copy)
+// Scores are kept in the log2 domain (scale * log2 e folded in) so the exponent is
+// one v_exp_f32.
+#include "fa_common.hpp"
+#include "fa_internal.hpp"
+
+namespace fa {
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int Hq, Hkv, Nq, Nkv, G, off;  // off = Nkv - Nq (bottom-right causal offset)
+  float scale_log2;
+};
+
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
+  constexpr int BM = 128, BN = 64;
+  constexpr int LDK = D + 8;    // row-major K tile, padded against bank conflicts
+  constexpr int LDVT = BN + 4;  // transposed V tile [d][key]
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t VTs[D * LDVT];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / p.G;
+  const int q0 = blockIdx.x * BM;
+  const size_t qbase = ((size_t)b * p.Hq + h) * (size_t)p.Nq;
+  const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
+  const uint16_t* __restrict__ Q = p.q + qbase * D;
+  const uint16_t* __restrict__ K = p.k + kbase * D;
+  const uint16_t* __restrict__ V = p.v + kbase * D;
+  const int qrow = q0 + 32 * w + l32;  // this lane's query row
+
+  u32x4 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    qf[s] = qrow < p.Nq ? ld16(Q + (size_t)qrow * D + 16 * s + 8 * g) : zero_u4();
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) acc[n] = zero16();
+  float m = -INFINITY, l = 0.f;
+
+  int kv_end = p.Nkv;
+  if (CAUSAL) {
+    const int q_last = min(q0 + BM, p.Nq) - 1;
+    kv_end = min(p.Nkv, q_last + p.off + 1);
+  }
+  const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int kv0 = kt * BN;
+    __syncthreads();
+#pragma unroll
+    for (int c = tid; c < BN * D / 8; c += 256) {
+      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int kr = kv0 + r;
+      u32x4 kk = zero_u4(), vv = zero_u4();
+      if (kr < p.Nkv) {
+        kk = ld16(K + (size_t)kr * D + col);
+        vv = ld16(V + (size_t)kr * D + col);
+      }
+      *reinterpret_cast<u32x4*>(Ks + r * LDK + col) = kk;
+      lds_store_transposed(VTs, LDVT, r, col, vv);
+    }
+    __syncthreads();
+
+    f32x16 st[BN / 32];
+#pragma unroll
+    for (int t = 0; t < BN / 32; ++t) {
+      st[t] = zero16();
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(Ks + (32 * t + l32) * LDK + 16 * s + 8 * g);
+        st[t] = Dt<DT>::mma(a, qf[s], st[t]);
+      }
+    }
+
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < BN / 32; ++t) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kv = kv0 + 32 * t + crow_of(i, g);
+        const bool masked = kv >= p.Nkv || (CAUSAL && kv > qrow + p.off);
+        const float x = masked ? -INFINITY : st[t][i] * p.scale_log2;
+        st[t][i] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(m, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    float rs = 0.f;
+#pragma unroll
+    for (int t = 0; t < BN / 32; ++t) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float e = fast_exp2(st[t][i] - m_use);
+        st[t][i] = e;
+        rs += e;
+      }
+    }
+    rs += __shfl_xor(rs, 32);
+    l = l * alpha + rs;
+    m = m_new;
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[n][i] *= alpha;
+
+#pragma unroll
+    for (int t = 0; t < BN / 32; ++t) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 pb = pack_c_slice<DT>(st[t], c);
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n) {
+          const u32x4 a = lds_read_crow_operand(VTs, LDVT, 32 * n + l32, 32 * t, c, g);
+          acc[n] = Dt<DT>::mma(a, pb, acc[n]);
+        }
+      }
+    }
+  }
+
+  if (qrow < p.Nq) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    uint16_t* O = p.o + (qbase + qrow) * D;
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 w2;
+        w2[0] = Dt<DT>::pack2(acc[n][4 * j + 0] * inv, acc[n][4 * j + 1] * inv);
+        w2[1] = Dt<DT>::pack2(acc[n][4 * j + 2] * inv, acc[n][4 * j + 3] * inv);
+        *reinterpret_cast<u32x2*>(O + 32 * n + 8 * j + 4 * g) = w2;
+      }
+    }
+    if (g == 0) p.lse[qbase + qrow] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int DT, int D, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
+  const Problem& pb = a.pb;
+  FwdParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.o = static_cast<uint16_t*>(a.o);
+  p.lse = a.lse;
+  p.Hq = pb.Hq;
+  p.Hkv = pb.Hkv;
+  p.Nq = pb.Nq;
+  p.Nkv = pb.Nkv;
+  p.G = pb.Hq / pb.Hkv;
+  p.off = pb.Nkv - pb.Nq;
+  p.scale_log2 = pb.scale * kLog2e;
+  dim3 grid((pb.Nq + 127) / 128, pb.Hq, pb.B);
+  hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
+  if ((size_t)a.pb.B * a.pb.Nq == 0) return hipSuccess;
+  const int key = a.pb.dtype * 4 + (a.pb.d == 128 ? 2 : 0) + (a.pb.causal ? 1 : 0);
+  switch (key) {
+    case 0: return launch_fwd_t<0, 64, false>(a, s);
+    case 1: return launch_fwd_t<0, 64, true>(a, s);
+    case 2: return launch_fwd_t<0, 128, false>(a, s);
+    case 3: return launch_fwd_t<0, 128, true>(a, s);
+    case 4: return launch_fwd_t<1, 64, false>(a, s);
+    case 5: return launch_fwd_t<1, 64, true>(a, s);
+    case 6: return launch_fwd_t<1, 128, false>(a, s);
+    default: return launch_fwd_t<1, 128, true>(a, s);
+  }
+}
+
+}  // namespace fa

@@ -1,0 +1,56 @@
+// Host-side plumbing shared by the C entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Validated arguments of one call (sizes already checked, pointers device-side).
+struct Problem {
+  int B, Hq, Hkv, Nq, Nkv, d;
+  float scale;
+  bool causal;
+  int dtype;  // 0 fp16, 1 bf16
+};
+
+struct FwdArgs {
+  Problem pb;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+};
+
+struct BwdArgs {
+  Problem pb;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;   // [B*Hq*Nq]      rowsum(dO o O)
+  float* lse2;    // [B*Hq*Nq]      LSE * log2(e), +inf for rows that see no key
+  float* dq_acc;  // [B*Hq*Nq*d]    float32 dQ accumulator (atomic path only)
+};
+
+// Workspace carve-up; every region starts on a 256-byte boundary.
+struct WorkspaceLayout {
+  size_t delta_off, lse2_off, dqacc_off, total;
+};
+WorkspaceLayout workspace_layout(const Problem& pb, bool atomic_dq);
+
+// Kernel launchers (return hipSuccess or the launch error).
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_pre(const BwdArgs& a, bool zero_dq_acc, hipStream_t s);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, bool atomic_dq, hipStream_t s);
+hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dq_convert(const BwdArgs& a, hipStream_t s);
+
+}  // namespace fa

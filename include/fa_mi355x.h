@@ -1,0 +1,144 @@
+/*
+ * fa_mi355x.h - exact softmax attention, forward and backward, for AMD Instinct
+ * MI355X (gfx950).  C ABI of libfa_mi355x.so.
+ *
+ * The operation (softmax attention and its gradient):
+ *   S   = scale * Q_h K_g^T            (g = h / (Hq/Hkv): consecutive query heads
+ *                                        share a key/value head)
+ *   LSE = log sum_j exp(S_ij)           (natural log, scaled-score domain)
+ *   P   = exp(S - LSE),  O = P V
+ *   D   = rowsum(dO o O),  dP = dO V^T,  dS = P o (dP - D)
+ *   dQ  = scale * dS K,  dK = scale * sum_{h in g} dS^T Q_h,  dV = sum_{h in g} P^T dO_h
+ * The backward recomputes S and P tile by tile from Q, K and the stored LSE and
+ * never writes an N_q x N_kv matrix to memory (rustytorch
+ * "flash_attention_backward.cu", header comment and tiled backward kernel;
+ * Triton issue "Extra transposes cause 8x speedup for sequence-parallel Flash
+ * Attention backward", the key/value-block-parallel _bwd_kernel).  GQA, causal
+ * masking and N_q != N_kv follow the feature list of the Liger-Kernel pull
+ * request "[Kernel] Flash attention 2".
+ *
+ * Causal masking is bottom-right aligned: query i sees key j iff
+ * j <= i + (N_kv - N_q).  A query row that sees no key gets O = 0, LSE = -inf
+ * and a zero dQ row.
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers owned by the caller.  The library allocates
+ *     nothing and keeps no state between calls; calls are safe from several host
+ *     threads on different streams.
+ *   - Layout: contiguous row-major, head dimension fastest.
+ *       q, o, dout, dq : [B, Hq,  N_q,  d]
+ *       k, v, dk, dv   : [B, Hkv, N_kv, d]
+ *       lse            : [B, Hq,  N_q]  float32
+ *   - dtype: FA_DTYPE_FP16 or FA_DTYPE_BF16; every 16-bit tensor of a call has
+ *     that dtype.  Accumulation is float32; 16-bit results are rounded to
+ *     nearest even.
+ *   - Every pointer must be 16-byte aligned.  A pointer may be NULL only when its
+ *     tensor has no element.
+ *   - d is 64 or 128.  B, N_q, N_kv >= 0 (zero-size calls are valid), Hq and Hkv
+ *     >= 1 with Hq % Hkv == 0, N * d < 2^31 per head, B and Hq <= 65535.
+ *   - softmax_scale must be finite and > 0.  causal: 0 = off, nonzero = on.
+ *   - stream: a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *     enqueued asynchronously; no call synchronises.
+ *   - Errors: every argument is checked on the host before anything is enqueued;
+ *     on error nothing is launched and no output is written, and a negative
+ *     FA_ERR_* code is returned.  FA_ERR_HIP reports a failed kernel launch.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_OK            0
+#define FA_ERR_NULLPTR  -1  /* required pointer is NULL */
+#define FA_ERR_SHAPE    -2  /* bad B/Hq/Hkv/N_q/N_kv, Hq % Hkv != 0, or size limits */
+#define FA_ERR_HEADDIM  -3  /* d not in {64, 128} */
+#define FA_ERR_DTYPE    -4  /* dtype not FP16/BF16 */
+#define FA_ERR_SCALE    -5  /* softmax_scale not finite or <= 0 */
+#define FA_ERR_WORKSPACE -6 /* workspace NULL/misaligned or smaller than required */
+#define FA_ERR_ALIGN    -7  /* a tensor pointer is not 16-byte aligned */
+#define FA_ERR_HIP      -8  /* a kernel launch failed (hipGetLastError) */
+#define FA_ERR_MODE     -9  /* unknown dq_mode */
+
+#define FA_DTYPE_FP16 0
+#define FA_DTYPE_BF16 1
+
+/* How fa_bwd_ex produces dQ (the spec comparison of two dQ paths). */
+#define FA_DQ_AUTO     0  /* the faster path, as measured for this shape class */
+#define FA_DQ_ATOMIC   1  /* dS K tiles added into a float32 buffer by the dK/dV
+                             kernel with float atomics, then rounded to dtype */
+#define FA_DQ_SEPARATE 2  /* a query-block-parallel kernel recomputes S, P, dP and
+                             dS and writes dQ once; no atomics, bitwise repeatable */
+
+/*
+ * Forward: O and LSE from Q, K, V.
+ * Writes o [B,Hq,N_q,d] (dtype) and lse [B,Hq,N_q] (float32, natural log of the
+ * row sum of exp(scale * q.k) over visible keys; -inf for a row with none).
+ * Reads q, k, v.  Returns FA_OK or an FA_ERR_* code.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+           float softmax_scale, int causal, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these arguments (0 when the call
+ * needs none).  Returns 0 for invalid arguments as well; fa_bwd then reports the
+ * error.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                              int causal, int dtype);
+
+/* Workspace bytes fa_bwd_ex needs with the given dq_mode. */
+size_t fa_bwd_ex_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                                 int causal, int dtype, int dq_mode);
+
+/*
+ * Backward: dQ, dK, dV from Q, K, V, O, dO and LSE.
+ * o and lse must be what fa_fwd returns for the same q, k, v and arguments (or
+ * the same quantities computed elsewhere).  dq, dk, dv are fully overwritten
+ * (callers need not zero them).  workspace: caller-owned device memory of at
+ * least fa_bwd_workspace_bytes(...) bytes, 16-byte aligned, not shared with a
+ * concurrent call; its contents on entry do not matter.  Kernels run in order
+ * on `stream`: row preprocess (D = rowsum(dO o O)), the key/value-block-parallel
+ * dK/dV kernel, then the dQ path FA_DQ_AUTO selects.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+           float softmax_scale, int causal, int dtype,
+           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_bwd with an explicit dQ path and optional timing events.
+ * dq_mode: FA_DQ_AUTO, FA_DQ_ATOMIC or FA_DQ_SEPARATE.
+ * ev_begin / ev_end: NULL, or hipEvent_t handles (as void*) that are recorded on
+ * `stream` immediately before and after the launch of the dK/dV kernel, the
+ * dominant kernel of the backward, so a caller can time it alone.
+ * workspace_bytes must be >= fa_bwd_ex_workspace_bytes(..., dq_mode).
+ */
+int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+              int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+              float softmax_scale, int causal, int dtype, int dq_mode,
+              void* ev_begin, void* ev_end,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* The dQ path FA_DQ_AUTO resolves to for these arguments (FA_DQ_ATOMIC or
+ * FA_DQ_SEPARATE). */
+int fa_bwd_auto_dq_mode(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                        int causal, int dtype);
+
+/* Static text for a status code; never NULL. */
+const char* fa_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,153 @@
+"""The C ABI without a GPU: the library loads, exports every function the header
+declares, and rejects bad arguments on the host before touching a device.
+
+No call here passes a valid set of arguments, so nothing is ever launched.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
+
+FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_HEADDIM = 0, -1, -2, -3
+FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_MODE = -4, -5, -6, -7, -8, -9
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_attention_backward_fa_amd import _lib
+    return _lib.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_api():
+    names = header_functions()
+    from exact_attention_backward_fa_amd import _lib
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from exact_attention_backward_fa_amd import _lib
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (fa_[a-z_0-9]+)\b", out))
+    for name in header_functions():
+        assert name in exported, f"{name} not exported"
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for code in (FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE, FA_ERR_SCALE,
+                 FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_MODE, 12345):
+        s = lib.fa_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.fa_status_string(FA_ERR_HEADDIM).decode().find("64") >= 0
+    assert lib.fa_version() >= 100
+
+
+# Fake, 16-byte aligned, never dereferenced addresses: every call below fails
+# validation before anything reads them.
+P = 0x10000
+
+
+def fwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nkv=8, d=64, scale=0.125,
+             causal=0, dtype=0)
+    a.update(kw)
+    return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                      a["Nkv"], a["d"], a["scale"], a["causal"], a["dtype"], None)
+
+
+def bwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=1, Nq=8, Nkv=8,
+             d=64, scale=0.125, causal=0, dtype=0, mode=0, ws=P, wsb=1 << 40)
+    a.update(kw)
+    return lib.fa_bwd_ex(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                         a["dv"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["d"], a["scale"],
+                         a["causal"], a["dtype"], a["mode"], None, None, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("call", [fwd, bwd])
+def test_argument_errors(lib, call):
+    assert call(lib, dtype=2) == FA_ERR_DTYPE
+    assert call(lib, dtype=-1) == FA_ERR_DTYPE
+    assert call(lib, d=96) == FA_ERR_HEADDIM
+    assert call(lib, d=0) == FA_ERR_HEADDIM
+    assert call(lib, Hq=3, Hkv=2) == FA_ERR_SHAPE
+    assert call(lib, Hkv=0) == FA_ERR_SHAPE
+    assert call(lib, Hq=0) == FA_ERR_SHAPE
+    assert call(lib, B=-1) == FA_ERR_SHAPE
+    assert call(lib, Nq=-5) == FA_ERR_SHAPE
+    assert call(lib, Nkv=-1) == FA_ERR_SHAPE
+    assert call(lib, Nq=1 << 25, d=128) == FA_ERR_SHAPE  # N*d >= 2^31
+    assert call(lib, B=70000) == FA_ERR_SHAPE
+    assert call(lib, scale=0.0) == FA_ERR_SCALE
+    assert call(lib, scale=-1.0) == FA_ERR_SCALE
+    assert call(lib, scale=math.inf) == FA_ERR_SCALE
+    assert call(lib, scale=math.nan) == FA_ERR_SCALE
+    assert call(lib, q=0) == FA_ERR_NULLPTR
+    assert call(lib, q=P + 8) == FA_ERR_ALIGN
+    assert call(lib, lse=P + 4) == FA_ERR_ALIGN
+
+
+def test_bwd_specific_errors(lib):
+    for name in ("o", "do", "dq", "dk", "dv", "k", "v"):
+        assert bwd(lib, **{name: 0}) == FA_ERR_NULLPTR, name
+        assert bwd(lib, **{name: P + 2}) == FA_ERR_ALIGN, name
+    assert bwd(lib, mode=3) == FA_ERR_MODE
+    assert bwd(lib, mode=-1) == FA_ERR_MODE
+    assert bwd(lib, ws=0) == FA_ERR_WORKSPACE
+    assert bwd(lib, ws=P + 8) == FA_ERR_WORKSPACE
+    need = lib.fa_bwd_ex_workspace_bytes(1, 2, 1, 8, 8, 64, 0, 0, 1)
+    assert need > 0
+    assert bwd(lib, mode=1, wsb=need - 1) == FA_ERR_WORKSPACE
+    need_sep = lib.fa_bwd_ex_workspace_bytes(1, 2, 1, 8, 8, 64, 0, 0, 2)
+    assert bwd(lib, mode=2, wsb=need_sep - 1) == FA_ERR_WORKSPACE
+
+
+def test_workspace_sizes(lib):
+    B, Hq, Hkv, N, d = 4, 32, 8, 8192, 128
+    rows = B * Hq * N
+    atomic = lib.fa_bwd_ex_workspace_bytes(B, Hq, Hkv, N, N, d, 1, 1, 1)
+    separate = lib.fa_bwd_ex_workspace_bytes(B, Hq, Hkv, N, N, d, 1, 1, 2)
+    assert separate >= 2 * rows * 4 and separate < 2 * rows * 4 + 1024
+    assert atomic >= separate + rows * d * 4
+    auto = lib.fa_bwd_workspace_bytes(B, Hq, Hkv, N, N, d, 1, 1)
+    assert auto in (atomic, separate)
+    mode = lib.fa_bwd_auto_dq_mode(B, Hq, Hkv, N, N, d, 1, 1)
+    assert mode in (1, 2)
+    assert auto == (atomic if mode == 1 else separate)
+    # zero-size problems need no workspace; invalid ones report 0
+    assert lib.fa_bwd_workspace_bytes(0, Hq, Hkv, N, N, d, 1, 1) == 0
+    assert lib.fa_bwd_workspace_bytes(B, Hq, Hkv, 0, N, d, 1, 1) == 0
+    assert lib.fa_bwd_workspace_bytes(B, 3, 2, N, N, d, 1, 1) == 0
+    assert lib.fa_bwd_ex_workspace_bytes(B, Hq, Hkv, N, N, d, 1, 1, 7) == 0
+
+
+def test_null_pointers_allowed_for_empty_tensors_only(lib):
+    # N_q = 0: q/o/lse/do/dq are empty, so NULL is accepted for them, but dk still
+    # has elements (it is written with zeros), so a NULL dk is rejected.
+    assert bwd(lib, Nq=0, q=0, o=0, lse=0, do=0, dq=0, dk=0) == FA_ERR_NULLPTR
+    # forward with B = 0 touches nothing at all: every pointer may be NULL and the
+    # call succeeds without enqueuing work.
+    assert fwd(lib, B=0, q=0, k=0, v=0, o=0, lse=0) == FA_OK
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    import exact_attention_backward_fa_amd as fa
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q, 0.125, False)
+    with pytest.raises(ValueError):
+        fa.fwd(q.float(), q.float(), q.float(), 0.125, False)
