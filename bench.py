@@ -1,0 +1,188 @@
+"""Benchmark of the exact-attention backward on one MI355X.
+
+Workload: Llama-3-style causal GQA, B=4, Hq=32, Hkv=8, N_q=N_kv=8192, d=128, bf16,
+scale 1/sqrt(128), Q/K/V/dO ~ N(0,1) from the seeded generator (synthetic data).
+
+A step is one pass of the whole hot path on resident inputs: fa_fwd (O, LSE) then
+fa_bwd (D preprocess, the dK/dV kernel, the dQ path).  The headline value is the
+backward's throughput, fa_bwd TFLOP/s, counting 2.5x the forward's 4*Nq*Nkv*d
+flops per query head, halved for causal; it is taken from HIP events recorded on
+the launch stream around every fa_bwd call of the timed steps.
+
+Also reported: the roofline of the dominant kernel (the dK/dV kernel, timed alone
+with events that fa_bwd_ex records around its launch), the forward's rate, and a
+CPU baseline: the fp64 oracle's backward on one kv-head group of the same inputs,
+timed on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--dq-mode auto|atomic|separate]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16/fp16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(case, x) -> dict:
+    """The oracle's backward, as it stands, on one (batch 0, kv head 0) group."""
+    import oracle.attention_fp64 as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    G = case.Hq // case.Hkv
+    s = {"q": x["q"][0:1, 0:G], "k": x["k"][0:1, 0:1], "v": x["v"][0:1, 0:1], "do": x["do"][0:1, 0:G]}
+    t0 = time.perf_counter()
+    orc.backward(s["q"], s["k"], s["v"], s["do"], case.scale, case.causal)
+    dt = time.perf_counter() - t0
+    flops = 2.5 * 4.0 * G * case.Nq * case.Nkv * case.d * (0.5 if case.causal else 1.0)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 oracle backward of batch 0, kv head 0 ({G} query heads, "
+                      f"N={case.Nq}, d={case.d}, causal) = 1/{case.B * case.Hkv} of the workload; "
+                      f"{dt:.1f} s",
+            "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--dq-mode", default="auto", choices=["auto", "atomic", "separate"])
+    ap.add_argument("--workload", default=None, help="case name (default: headline workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the backward shards by (batch, kv head) group with no communication; "
+              "run --gpus 1)", file=sys.stderr, flush=True)
+        return 2
+
+    import torch
+    import exact_attention_backward_fa_amd as fa
+    from exact_attention_backward_fa_amd import inputs
+
+    case = inputs.case_by_name(args.workload or inputs.HEADLINE)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {case.name}: B={case.B} Hq={case.Hq} Hkv={case.Hkv} N={case.Nq} "
+        f"d={case.d} {case.dtype} causal={case.causal}")
+    x = inputs.make_inputs(case)
+    d = {k: v.to(dev) for k, v in x.items()}
+    o = torch.empty_like(d["q"])
+    lse = torch.empty(case.B, case.Hq, case.Nq, dtype=torch.float32, device=dev)
+    dq = torch.empty_like(d["q"])
+    dk = torch.empty_like(d["k"])
+    dv = torch.empty_like(d["v"])
+    mode = args.dq_mode
+    if mode == "auto":
+        resolved = fa.auto_dq_mode(case.B, case.Hq, case.Hkv, case.Nq, case.Nkv, case.d,
+                                   case.causal, case.torch_dtype)
+    else:
+        resolved = mode
+    ws = torch.empty(max(fa.bwd_workspace_bytes(case.B, case.Hq, case.Hkv, case.Nq, case.Nkv, case.d,
+                                                case.causal, case.torch_dtype, mode), 1),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    n = args.steps
+    ev = {k: [fa.HipEvent() for _ in range(n)] for k in ("f0", "f1", "b0", "b1", "k0", "k1")}
+
+    def step(i=None):
+        if i is not None:
+            ev["f0"][i].record(stream)
+        fa.fwd_into(d["q"], d["k"], d["v"], o, lse, case.scale, case.causal)
+        if i is not None:
+            ev["f1"][i].record(stream)
+            ev["b0"][i].record(stream)
+        fa.bwd_into(d["q"], d["k"], d["v"], o, lse, d["do"], dq, dk, dv, case.scale, case.causal,
+                    dq_mode=mode, workspace=ws,
+                    events=None if i is None else (ev["k0"][i].handle, ev["k1"][i].handle))
+        if i is not None:
+            ev["b1"][i].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    log(f"[bench] warmup done ({args.warmup} steps); timing {n} steps, dq path {resolved}")
+    t0 = time.perf_counter()
+    for i in range(n):
+        step(i)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+
+    def total(a, b):
+        return sum(ev[a][i].elapsed_ms(ev[b][i]) for i in range(n))
+
+    fwd_ms = total("f0", "f1") / n
+    bwd_ms = total("b0", "b1") / n
+    kern_ms = total("k0", "k1") / n
+    bwd_flops = case.bwd_flops()
+    fwd_flops = case.fwd_flops()
+    value = bwd_flops / (bwd_ms * 1e-3) / 1e12
+    # Algorithmic flops of the dK/dV kernel per launch: with the atomic dQ path it
+    # performs all five products of the backward (10*Nq*Nkv*d per query head, halved
+    # for causal); on the separate path it performs four of them (8*Nq*Nkv*d).
+    kern_flops = bwd_flops if resolved == "atomic" else bwd_flops * 0.8
+    achieved = kern_flops / (kern_ms * 1e-3) / 1e12
+    log(f"[bench] fwd {fwd_ms:.3f} ms ({fwd_flops / fwd_ms / 1e9:.1f} TFLOP/s)  bwd {bwd_ms:.3f} ms "
+        f"({value:.1f} TFLOP/s, {100 * value / PEAK_BF16_TFLOPS:.1f}% of peak)  dkdv kernel "
+        f"{kern_ms:.3f} ms ({achieved:.1f} TFLOP/s)")
+
+    out = {
+        "metric": "fa_bwd TFLOP/s and % of MI355X bf16 MFMA peak (causal GQA, d=128)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / n, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
+        "config": {"workload": f"{case.name}: causal GQA B={case.B} Hq={case.Hq} Hkv={case.Hkv} "
+                               f"N_q=N_kv={case.Nq} d={case.d} {case.dtype}",
+                   "global_batch": case.B, "seq_len": case.Nq, "parallelism": "single GPU",
+                   "dq_path": resolved},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "bwd_ms": round(bwd_ms, 4),
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
+        "roofline": {
+            "kernel": f"bwd_dkdv_kernel ({'with atomic dQ' if resolved == 'atomic' else 'dK/dV only'})",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel_ms": round(kern_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline: fp64 oracle backward on one kv-head group ...")
+        out["cpu_baseline"] = cpu_baseline(case, x)
+        log(f"[bench] cpu baseline {out['cpu_baseline']['value']:.4f} TFLOP/s "
+            f"({out['cpu_baseline']['seconds']:.1f} s, {out['cpu_baseline']['cores']} threads)")
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -34,6 +34,9 @@ static int check_problem(int B, int Hq, int Hkv, int Nq, int Nkv, int d, float s
   // total element counts must stay well inside size_t arithmetic
   if ((double)B * Hq * (double)Nq * d > 9.0e15 || (double)B * Hkv * (double)Nkv * d > 9.0e15)
     return FA_ERR_SHAPE;
+  // 1-D grids: (query or key tiles of >= 64 rows) x heads x batch must fit an int
+  const int64_t tiles = ((int64_t)(Nq > Nkv ? Nq : Nkv) + 63) / 64;
+  if (tiles * Hq * (int64_t)B >= ((int64_t)1 << 31)) return FA_ERR_SHAPE;
   if (!isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
   out->B = B;
   out->Hq = Hq;

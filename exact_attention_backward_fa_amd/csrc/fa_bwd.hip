@@ -20,6 +20,8 @@
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
 
+#include <type_traits>
+
 namespace fa {
 
 struct BwdParams {
@@ -35,7 +37,7 @@ struct BwdParams {
   float* delta;
   float* lse2;
   float* dq_acc;
-  int Hq, Hkv, Nq, Nkv, G, off;  // off = Nkv - Nq (bottom-right causal offset)
+  int B, Hq, Hkv, Nq, Nkv, G, off;  // off = Nkv - Nq (bottom-right causal offset)
   float scale, scale_log2;
   size_t rows;  // B * Hq * Nq
 };
@@ -54,6 +56,7 @@ static BwdParams make_params(const BwdArgs& a) {
   p.delta = a.delta;
   p.lse2 = a.lse2;
   p.dq_acc = a.dq_acc;
+  p.B = a.pb.B;
   p.Hq = a.pb.Hq;
   p.Hkv = a.pb.Hkv;
   p.Nq = a.pb.Nq;
@@ -102,32 +105,36 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // owns key rows 32w..32w+31 of the tile and keeps their K and V as MFMA operands in
 // registers and their dK and dV as float32 accumulators.  The loop runs over the
 // G query heads of the group and, per head, over 64-row query tiles from the first
-// one that can see the key tile (causal) to the end.
+// one that can see the key tile (causal) to the end.  Query tiles (Q, dO, LSE, D)
+// are double-buffered in LDS and the next one is fetched into registers while the
+// current one is used, so each iteration needs one barrier.
 //
-// S = Q K^T is computed with the key index in the lane (C column), so P^T and
-// dS^T feed dV += P^T dO and dK += dS^T Q directly from the accumulators; dO and Q
-// are then needed with the query index along the operand slots, which a transposed
-// LDS copy provides.
+// S = Q K^T is computed with the key index in the lane (C column), so P^T and dS^T
+// feed dV += P^T dO and dK += dS^T Q straight from the accumulators; dO and Q are
+// then needed with the query index along the operand slots, which transposed LDS
+// reads of the row-major tiles provide.
+//
+// With ATOMIC_DQ the workgroup also adds dQ_i += scale * dS K_j into a float32
+// buffer: dS^T is staged in LDS (double-buffered) and the product for iteration i
+// runs at the start of iteration i+1, after the barrier that publishes it.
 template <int DT, int D, bool CAUSAL, bool ATOMIC_DQ>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int BN = 128, BM = 64;
-  constexpr int LDR = D + 8;    // row-major Q / dO tiles [query][d]
-  constexpr int LDT = BM + 4;   // transposed Q / dO tiles [d][query]
-  constexpr int LDSS = BN + 8;  // dS tile [query][key]
-  constexpr int LDKT = BN + 8;  // transposed K tile [d][key]
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BM * LDR];
-  __shared__ __attribute__((aligned(16))) uint16_t dOs[BM * LDR];
-  __shared__ __attribute__((aligned(16))) uint16_t QTs[D * LDT];
-  __shared__ __attribute__((aligned(16))) uint16_t dOTs[D * LDT];
-  __shared__ float lse_s[BM];
-  __shared__ float dlt_s[BM];
-  __shared__ __attribute__((aligned(16))) uint16_t dSs[ATOMIC_DQ ? BM * LDSS : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t KTs[ATOMIC_DQ ? D * LDKT : 8];
+  constexpr int BN = 128, BM = 64, NG = D / 8;
+  constexpr int TILE = BM * D;
+  constexpr int CH = BM * NG / 256;  // 16-byte chunks per thread per Q/dO tile
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[2][TILE];
+  __shared__ __attribute__((aligned(16))) float sL[2][BM];
+  __shared__ __attribute__((aligned(16))) float sD[2][BM];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[ATOMIC_DQ ? BN * D : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t sdST[ATOMIC_DQ ? 2 : 1][ATOMIC_DQ ? BN * BM : 8];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
-  const int hk = blockIdx.y, b = blockIdx.z;
-  const int kv0 = blockIdx.x * BN;
+  const int l32 = lane & 31, g = lane >> 5, hi16 = (lane >> 4) & 1;
+  int rank, head;
+  map_block(blockIdx.x, p.B * p.Hkv, rank, head);
+  const int b = head / p.Hkv, hk = head % p.Hkv;
+  const int kv0 = rank * BN;  // rank 0 = first key tile = most query rows under the mask
   const int kvw = kv0 + 32 * w;
   const int kv_lane = kvw + l32;  // key row this lane carries as S column
   const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
@@ -141,11 +148,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     vf[s] = kv_lane < p.Nkv ? ld16(V + (size_t)kv_lane * D + 16 * s + 8 * g) : zero_u4();
   }
   if (ATOMIC_DQ) {
-    for (int c = tid; c < BN * D / 8; c += 256) {
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
+    for (int c = tid; c < BN * NG; c += 256) {
+      const int r = c / NG, j = c % NG;
       const int kr = kv0 + r;
-      const u32x4 kk = kr < p.Nkv ? ld16(K + (size_t)kr * D + col) : zero_u4();
-      lds_store_transposed(KTs, LDKT, r, col, kk);
+      *reinterpret_cast<u32x4*>(&sK[soff<NG>(r, 8 * j)]) =
+          kr < p.Nkv ? ld16(K + (size_t)kr * D + 8 * j) : zero_u4();
     }
   }
 
@@ -159,64 +166,122 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int q_begin = CAUSAL ? max(0, kv0 - p.off) : 0;
   const int nqt = (p.Nq + BM - 1) / BM;
   const int qt_begin = q_begin < p.Nq ? q_begin / BM : nqt;
+  const int per_head = nqt - qt_begin;
+  const int n_it = p.G * per_head;
 
-  for (int hh = 0; hh < p.G; ++hh) {
-    const int h = hk * p.G + hh;
-    const size_t qbase = ((size_t)b * p.Hq + h) * (size_t)p.Nq;
+  // iteration -> (query row base of the head, first query row of the tile)
+  auto tile_of = [&](int it, size_t& qbase, int& q0) {
+    const int hh = it / per_head;
+    q0 = (qt_begin + it % per_head) * BM;
+    qbase = ((size_t)b * p.Hq + (size_t)hk * p.G + hh) * (size_t)p.Nq;
+  };
+
+  u32x4 pq[CH], pd[CH];
+  float pl = 0.f, pdl = 0.f;
+  auto load = [&](int it) {
+    size_t qbase;
+    int q0;
+    tile_of(it, qbase, q0);
     const uint16_t* __restrict__ Qh = p.q + qbase * D;
     const uint16_t* __restrict__ dOh = p.dout + qbase * D;
-    const float* __restrict__ L2 = p.lse2 + qbase;
-    const float* __restrict__ DL = p.delta + qbase;
-
-    for (int qt = qt_begin; qt < nqt; ++qt) {
-      const int q0 = qt * BM;
-      __syncthreads();
 #pragma unroll
-      for (int c = tid; c < BM * D / 8; c += 256) {
-        const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-        const int qr = q0 + r;
-        u32x4 qa = zero_u4(), da = zero_u4();
-        if (qr < p.Nq) {
-          qa = ld16(Qh + (size_t)qr * D + col);
-          da = ld16(dOh + (size_t)qr * D + col);
-        }
-        *reinterpret_cast<u32x4*>(Qs + r * LDR + col) = qa;
-        *reinterpret_cast<u32x4*>(dOs + r * LDR + col) = da;
-        lds_store_transposed(QTs, LDT, r, col, qa);
-        lds_store_transposed(dOTs, LDT, r, col, da);
-      }
-      if (tid < BM) {
-        const int qr = q0 + tid;
-        lse_s[tid] = qr < p.Nq ? L2[qr] : INFINITY;
-        dlt_s[tid] = qr < p.Nq ? DL[qr] : 0.f;
-      }
-      __syncthreads();
+    for (int c = 0; c < CH; ++c) {
+      const int ch = tid + 256 * c, r = ch / NG, j = ch % NG;
+      const int qr = q0 + r;
+      pq[c] = qr < p.Nq ? ld16(Qh + (size_t)qr * D + 8 * j) : zero_u4();
+      pd[c] = qr < p.Nq ? ld16(dOh + (size_t)qr * D + 8 * j) : zero_u4();
+    }
+    if (tid < BM) {
+      const int qr = q0 + tid;
+      pl = qr < p.Nq ? p.lse2[qbase + qr] : INFINITY;
+      pdl = qr < p.Nq ? p.delta[qbase + qr] : 0.f;
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = tid + 256 * c, r = ch / NG, j = ch % NG;
+      *reinterpret_cast<u32x4*>(&sQ[buf][soff<NG>(r, 8 * j)]) = pq[c];
+      *reinterpret_cast<u32x4*>(&sdO[buf][soff<NG>(r, 8 * j)]) = pd[c];
+    }
+    if (tid < BM) {
+      sL[buf][tid] = pl;
+      sD[buf][tid] = pdl;
+    }
+  };
 
-      f32x16 sp[BM / 32], dp[BM / 32];
+  // dQ_i += scale * dS_i K_j for the query tile staged in sdST[buf]; wave w takes
+  // output tiles w, w+4, ... of the BM x D block.
+  auto dq_product = [&](int buf, int it) {
+    size_t qbase;
+    int q0;
+    tile_of(it, qbase, q0);
+    float* __restrict__ dQacc = p.dq_acc + qbase * D;
+    constexpr int NT = (BM / 32) * (D / 32);
+#pragma unroll 1
+    for (int tt = w; tt < NT; tt += 4) {
+      const int tq = tt / (D / 32), tn = tt % (D / 32);
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int ks = 0; ks < BN / 16; ++ks) {
+        const int k0 = 16 * ks + 8 * g;
+        const u32x4 a = lds_tr_operand<BM / 8>(sdST[buf], k0, k0 + 4, 32 * tq + 16 * hi16);
+        const u32x4 bk = lds_tr_operand<NG>(sK, k0, k0 + 4, 32 * tn + 16 * hi16);
+        acc = Dt<DT>::mma(a, bk, acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qg = q0 + 32 * tq + crow_of(i, g);
+        if (qg < p.Nq) atomicAdd(dQacc + (size_t)qg * D + 32 * tn + l32, acc[i] * p.scale);
+      }
+    }
+  };
+
+  // One iteration on LDS buffer CUR (a compile-time constant, so every LDS address
+  // is a fixed offset from a per-lane base).
+  auto body = [&](int it, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    if (ATOMIC_DQ && it > 0) dq_product(cur ^ 1, it - 1);
+    if (it + 1 < n_it) load(it + 1);
+    size_t qbase_unused;
+    int q0;
+    tile_of(it, qbase_unused, q0);
+
+    // Skip the math for a wave whose 32 keys are all masked for this tile.
+    const bool all_masked = kvw >= p.Nkv || (CAUSAL && kvw > q0 + BM - 1 + p.off);
+    f32x16 sp[BM / 32], dp[BM / 32];
+    if (!all_masked) {
 #pragma unroll
       for (int t = 0; t < BM / 32; ++t) {
         sp[t] = zero16();
         dp[t] = zero16();
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) {
-          const u32x4 a = *reinterpret_cast<const u32x4*>(Qs + (32 * t + l32) * LDR + 16 * s + 8 * g);
-          sp[t] = Dt<DT>::mma(a, kf[s], sp[t]);
-          const u32x4 a2 = *reinterpret_cast<const u32x4*>(dOs + (32 * t + l32) * LDR + 16 * s + 8 * g);
-          dp[t] = Dt<DT>::mma(a2, vf[s], dp[t]);
+          sp[t] = Dt<DT>::mma(lds_row16<NG>(sQ[cur], 32 * t + l32, 2 * s + g), kf[s], sp[t]);
+          dp[t] = Dt<DT>::mma(lds_row16<NG>(sdO[cur], 32 * t + l32, 2 * s + g), vf[s], dp[t]);
         }
       }
 
       // P and dS in place (sp <- P, dp <- dS), indexed [query row crow][key kv_lane].
+      const bool need_mask = kvw + 31 >= p.Nkv || (CAUSAL && kvw + 31 > q0 + p.off);
 #pragma unroll
       for (int t = 0; t < BM / 32; ++t) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int ql = 32 * t + crow_of(i, g);
-          const bool masked = kv_lane >= p.Nkv || (CAUSAL && kv_lane > q0 + ql + p.off);
-          float pv = fast_exp2(sp[t][i] * p.scale_log2 - lse_s[ql]);
-          pv = masked ? 0.f : pv;
-          sp[t][i] = pv;
-          dp[t][i] = pv * (dp[t][i] - dlt_s[ql]);
+        for (int j = 0; j < 4; ++j) {
+          const int qb = 32 * t + 8 * j + 4 * g;
+          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[cur][qb]);
+          const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[cur][qb]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * j + e;
+            float pv = fast_exp2(sp[t][i] * p.scale_log2 - L4[e]);
+            if (need_mask) {
+              const bool masked = kv_lane >= p.Nkv || (CAUSAL && kv_lane > q0 + qb + e + p.off);
+              pv = masked ? 0.f : pv;
+            }
+            sp[t][i] = pv;
+            dp[t][i] = pv * (dp[t][i] - D4[e]);
+          }
         }
       }
 
@@ -226,42 +291,53 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         for (int c = 0; c < 2; ++c) {
           const u32x4 pa = pack_c_slice<DT>(sp[t], c);
           const u32x4 sa = pack_c_slice<DT>(dp[t], c);
+          const int k0 = 32 * t + 16 * c + 4 * g;
 #pragma unroll
           for (int n = 0; n < D / 32; ++n) {
-            const u32x4 bo = lds_read_crow_operand(dOTs, LDT, 32 * n + l32, 32 * t, c, g);
+            const u32x4 bo = lds_tr_operand<NG>(sdO[cur], k0, k0 + 8, 32 * n + 16 * hi16);
             dv[n] = Dt<DT>::mma(pa, bo, dv[n]);
-            const u32x4 bq = lds_read_crow_operand(QTs, LDT, 32 * n + l32, 32 * t, c, g);
+            const u32x4 bq = lds_tr_operand<NG>(sQ[cur], k0, k0 + 8, 32 * n + 16 * hi16);
             dk[n] = Dt<DT>::mma(sa, bq, dk[n]);
           }
         }
       }
+    } else {
+#pragma unroll
+      for (int t = 0; t < BM / 32; ++t) dp[t] = zero16();
+    }
 
-      if (ATOMIC_DQ) {
+    if (ATOMIC_DQ) {
+      // dS^T[key][query]: 4 consecutive query rows per 8-byte store
 #pragma unroll
-        for (int t = 0; t < BM / 32; ++t)
+      for (int t = 0; t < BM / 32; ++t) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            dSs[(32 * t + crow_of(i, g)) * LDSS + 32 * w + l32] = Dt<DT>::one(dp[t][i]);
-        __syncthreads();
-        float* __restrict__ dQacc = p.dq_acc + qbase * D;
-        constexpr int NT = (BM / 32) * (D / 32);
-        for (int tt = w; tt < NT; tt += 4) {
-          const int tq = tt / (D / 32), tn = tt % (D / 32);
-          f32x16 acc = zero16();
-#pragma unroll
-          for (int ks = 0; ks < BN / 16; ++ks) {
-            const u32x4 a = *reinterpret_cast<const u32x4*>(dSs + (32 * tq + l32) * LDSS + 16 * ks + 8 * g);
-            const u32x4 bk = *reinterpret_cast<const u32x4*>(KTs + (32 * tn + l32) * LDKT + 16 * ks + 8 * g);
-            acc = Dt<DT>::mma(a, bk, acc);
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int qg = q0 + 32 * tq + crow_of(i, g);
-            if (qg < p.Nq) atomicAdd(dQacc + (size_t)qg * D + 32 * tn + l32, acc[i] * p.scale);
-          }
+        for (int j = 0; j < 4; ++j) {
+          u32x2 v2;
+          v2[0] = Dt<DT>::pack2(dp[t][4 * j + 0], dp[t][4 * j + 1]);
+          v2[1] = Dt<DT>::pack2(dp[t][4 * j + 2], dp[t][4 * j + 3]);
+          *reinterpret_cast<u32x2*>(&sdST[cur][soff<BM / 8>(32 * w + l32, 32 * t + 8 * j + 4 * g)]) = v2;
         }
       }
     }
+    if (it + 1 < n_it) stage(cur ^ 1);
+    __syncthreads();
+  };
+
+  if (n_it > 0) {
+    load(0);
+    stage(0);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < n_it; it += 2) {
+    body(it, std::integral_constant<int, 0>());
+    if (it + 1 < n_it) body(it + 1, std::integral_constant<int, 1>());
+  }
+  if (ATOMIC_DQ && n_it > 0) {
+    if ((n_it - 1) & 1)
+      dq_product(1, n_it - 1);
+    else
+      dq_product(0, n_it - 1);
   }
 
   uint16_t* __restrict__ dK = p.dk + kbase * D;
@@ -283,21 +359,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 // Separate dQ pass.  Workgroup = 4 waves = 128 query rows of one (batch, query
 // head); wave w owns 32 of them and keeps their Q and dO as MFMA operands in
 // registers.  S^T = K Q^T puts the query index in the lane, so dS feeds
-// dQ += dS K straight from the accumulators; K is read from a transposed LDS copy.
+// dQ += dS K straight from the accumulators; K is read transposed from the
+// row-major LDS tile.  Key/value tiles are double-buffered like the forward's.
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
-  constexpr int BM = 128, BN = 64;
-  constexpr int LDR = D + 8;
-  constexpr int LDKT = BN + 4;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * LDR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * LDR];
-  __shared__ __attribute__((aligned(16))) uint16_t KTs[D * LDKT];
+  constexpr int BM = 128, BN = 64, NG = D / 8;
+  constexpr int TILE = BN * D;
+  constexpr int CH = BN * NG / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31, g = lane >> 5;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int l32 = lane & 31, g = lane >> 5, hi16 = (lane >> 4) & 1;
+  const int nqt = (p.Nq + BM - 1) / BM;
+  int rank, head;
+  map_block(blockIdx.x, p.B * p.Hq, rank, head);
+  const int qt = CAUSAL ? nqt - 1 - rank : rank;
+  const int b = head / p.Hq, h = head % p.Hq;
   const int hk = h / p.G;
-  const int q0 = blockIdx.x * BM;
+  const int q0 = qt * BM;
   const int qrow = q0 + 32 * w + l32;
   const size_t qbase = ((size_t)b * p.Hq + h) * (size_t)p.Nq;
   const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
@@ -324,23 +404,35 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   }
   const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int kv0 = kt * BN;
-    __syncthreads();
+  u32x4 pk[CH], pv[CH];
+  auto load = [&](int kt) {
 #pragma unroll
-    for (int c = tid; c < BN * D / 8; c += 256) {
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int kr = kv0 + r;
-      u32x4 kk = zero_u4(), vv = zero_u4();
-      if (kr < p.Nkv) {
-        kk = ld16(K + (size_t)kr * D + col);
-        vv = ld16(V + (size_t)kr * D + col);
-      }
-      *reinterpret_cast<u32x4*>(Ks + r * LDR + col) = kk;
-      *reinterpret_cast<u32x4*>(Vs + r * LDR + col) = vv;
-      lds_store_transposed(KTs, LDKT, r, col, kk);
+    for (int c = 0; c < CH; ++c) {
+      const int ch = tid + 256 * c, r = ch / NG, j = ch % NG;
+      const int kr = kt * BN + r;
+      pk[c] = kr < p.Nkv ? ld16(K + (size_t)kr * D + 8 * j) : zero_u4();
+      pv[c] = kr < p.Nkv ? ld16(V + (size_t)kr * D + 8 * j) : zero_u4();
     }
-    __syncthreads();
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = tid + 256 * c, r = ch / NG, j = ch % NG;
+      *reinterpret_cast<u32x4*>(&sK[buf][soff<NG>(r, 8 * j)]) = pk[c];
+      *reinterpret_cast<u32x4*>(&sV[buf][soff<NG>(r, 8 * j)]) = pv[c];
+    }
+  };
+
+  if (nkt > 0) {
+    load(0);
+    stage(0);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int cur = kt & 1;
+    const int kv0 = kt * BN;
+    if (kt + 1 < nkt) load(kt + 1);
 
     f32x16 st[BN / 32], dpt[BN / 32];
 #pragma unroll
@@ -349,20 +441,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       dpt[t] = zero16();
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(Ks + (32 * t + l32) * LDR + 16 * s + 8 * g);
-        st[t] = Dt<DT>::mma(a, qf[s], st[t]);
-        const u32x4 a2 = *reinterpret_cast<const u32x4*>(Vs + (32 * t + l32) * LDR + 16 * s + 8 * g);
-        dpt[t] = Dt<DT>::mma(a2, df[s], dpt[t]);
+        st[t] = Dt<DT>::mma(lds_row16<NG>(sK[cur], 32 * t + l32, 2 * s + g), qf[s], st[t]);
+        dpt[t] = Dt<DT>::mma(lds_row16<NG>(sV[cur], 32 * t + l32, 2 * s + g), df[s], dpt[t]);
       }
     }
+    const bool need_mask = kv0 + BN > p.Nkv || (CAUSAL && kv0 + BN - 1 > q0 + 32 * w + p.off);
 #pragma unroll
     for (int t = 0; t < BN / 32; ++t) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kv = kv0 + 32 * t + crow_of(i, g);
-        const bool masked = kv >= p.Nkv || (CAUSAL && kv > qrow + p.off);
         float pv = fast_exp2(st[t][i] * p.scale_log2 - lse_q);
-        pv = masked ? 0.f : pv;
+        if (need_mask) {
+          const int kv = kv0 + 32 * t + crow_of(i, g);
+          if (kv >= p.Nkv || (CAUSAL && kv > qrow + p.off)) pv = 0.f;
+        }
         dpt[t][i] = pv * (dpt[t][i] - dlt_q);
       }
     }
@@ -371,13 +463,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const u32x4 a = pack_c_slice<DT>(dpt[t], c);
+        const int k0 = 32 * t + 16 * c + 4 * g;
 #pragma unroll
         for (int n = 0; n < D / 32; ++n) {
-          const u32x4 bk = lds_read_crow_operand(KTs, LDKT, 32 * n + l32, 32 * t, c, g);
+          const u32x4 bk = lds_tr_operand<NG>(sK[cur], k0, k0 + 8, 32 * n + 16 * hi16);
           acc[n] = Dt<DT>::mma(a, bk, acc[n]);
         }
       }
     }
+
+    if (kt + 1 < nkt) stage(cur ^ 1);
+    __syncthreads();
   }
 
   uint16_t* __restrict__ dQ = p.dq + qbase * D;
@@ -445,7 +541,7 @@ hipError_t launch_bwd_pre(const BwdArgs& a, bool zero_dq_acc, hipStream_t s) {
 template <int DT, int D, bool CAUSAL>
 static hipError_t dkdv_t(const BwdArgs& a, bool atomic, hipStream_t s) {
   const BwdParams p = make_params(a);
-  const dim3 grid((a.pb.Nkv + 127) / 128, a.pb.Hkv, a.pb.B);
+  const dim3 grid((unsigned)(((a.pb.Nkv + 127) / 128) * a.pb.Hkv * a.pb.B));
   if (atomic)
     hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL, true>), grid, dim3(256), 0, s, p);
   else
@@ -461,7 +557,7 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, bool atomic_dq, hipStream_t s) {
 template <int DT, int D, bool CAUSAL>
 static hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
   const BwdParams p = make_params(a);
-  const dim3 grid((a.pb.Nq + 127) / 128, a.pb.Hq, a.pb.B);
+  const dim3 grid((unsigned)(((a.pb.Nq + 127) / 128) * a.pb.Hq * a.pb.B));
   hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }

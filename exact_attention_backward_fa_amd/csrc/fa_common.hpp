@@ -98,6 +98,74 @@ __device__ __forceinline__ u32x4 pack_c_slice(const f32x16& x, int c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------------------
+// LDS tiles are row-major with rows of NG 16-byte granules (NG*8 16-bit columns)
+// and no padding; granule j of row r is stored at position j ^ swz(r).  The XOR
+// keeps both access patterns free of bank conflicts:
+//   - 16-byte row reads (an A/B operand with the contraction along the row): a run
+//     of consecutive rows at one logical granule lands on distinct granules;
+//   - transposed reads (ds_read_b64_tr_b16): 4 consecutive rows x 32 bytes land
+//     on 4 distinct granule pairs.
+template <int NG>
+__device__ __forceinline__ int swz(int r) {
+  int s = ((r & 3) << 1) | ((r >> 2) & 1);
+  if (NG >= 16) s |= ((r >> 3) & 1) << 3;
+  return s;
+}
+
+// Element offset of (row r, column c) in a swizzled tile with NG granules per row.
+template <int NG>
+__device__ __forceinline__ int soff(int r, int c) {
+  return r * (NG * 8) + (((c >> 3) ^ swz<NG>(r)) << 3) + (c & 7);
+}
+
+// 16-byte read of logical granule `gr` of row r.
+template <int NG>
+__device__ __forceinline__ u32x4 lds_row16(const uint16_t* X, int r, int gr) {
+  return *reinterpret_cast<const u32x4*>(X + r * (NG * 8) + ((gr ^ swz<NG>(r)) << 3));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i supplies the address of
+// 4 consecutive 16-bit values (row i/4, columns 4*(i%4)..+3 of a 4x16 block) and
+// receives column i of the block: the 4 values of rows 0..3.
+__device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// MFMA operand read transposed from a swizzled row-major tile X[k][n]: for column
+// n = n0 + lane%16 the lane gets slots 0..3 = X[k0 + 0..3][n] and slots
+// 4..7 = X[k1 + 0..3][n].
+template <int NG>
+__device__ __forceinline__ u32x4 lds_tr_operand(const uint16_t* X, int k0, int k1, int n0) {
+  const int i = threadIdx.x & 15;
+  const int c = n0 + 4 * (i & 3);
+  const u32x2 a = lds_tr16(X + soff<NG>(k0 + (i >> 2), c));
+  const u32x2 b = lds_tr16(X + soff<NG>(k1 + (i >> 2), c));
+  u32x4 r = {a[0], a[1], b[0], b[1]};
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup order.  Grids are 1-D; the hardware hands consecutive workgroup ids to
+// the 8 XCDs in turn.  map_block turns id L into (rank, head): heads are split
+// into 8 equal sets, one per XCD, so all tiles of a head share one L2; within an
+// XCD tiles go out rank 0 first.  Callers map rank 0 to the tile with the most
+// work under the causal mask.
+__device__ __forceinline__ void map_block(int L, int n_heads, int& rank, int& head) {
+  if ((n_heads & 7) == 0) {
+    const int x = L & 7, s = L >> 3, hpx = n_heads >> 3;
+    rank = s / hpx;
+    head = x * hpx + s % hpx;
+  } else {
+    rank = L / n_heads;
+    head = L % n_heads;
+  }
+}
+
 // 16-byte global load/store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
@@ -105,28 +173,6 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 __device__ __forceinline__ u32x4 zero_u4() {
   u32x4 z = {0u, 0u, 0u, 0u};
   return z;
-}
-
-// Store the 8 16-bit values of a 16-byte chunk, loaded from row r of a row-major
-// tile at columns c0..c0+7, into a transposed LDS tile T[col][row] with row
-// stride ldt (elements).
-__device__ __forceinline__ void lds_store_transposed(uint16_t* T, int ldt, int r, int c0, u32x4 v) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    T[(c0 + 2 * j) * ldt + r] = (uint16_t)(v[j] & 0xffffu);
-    T[(c0 + 2 * j + 1) * ldt + r] = (uint16_t)(v[j] >> 16);
-  }
-}
-
-// B (or A) operand whose slots follow C rows crow(c, g, e) + base, read from a
-// transposed LDS tile T[col][k] at column `col`.
-__device__ __forceinline__ u32x4 lds_read_crow_operand(const uint16_t* T, int ldt, int col, int base,
-                                                       int c, int g) {
-  const uint16_t* p = T + col * ldt + base + 16 * c + 4 * g;
-  u32x2 a = *reinterpret_cast<const u32x2*>(p);
-  u32x2 b = *reinterpret_cast<const u32x2*>(p + 8);
-  u32x4 r = {a[0], a[1], b[0], b[1]};
-  return r;
 }
 
 }  // namespace fa

@@ -7,13 +7,14 @@
 // usual streaming (online) softmax over key tiles.
 //
 // One workgroup = 4 waves = 128 query rows of one (batch, query head); each wave
-// owns 32 rows.  Per key tile of 64 rows:
+// owns 32 rows.  Key and value tiles of 64 rows are double-buffered in LDS: the
+// next tile is fetched into registers while the current one is used.  Per tile:
 //   S^T = K Q^T       (MFMA; Q stays in registers as the B operand for the whole
 //                      loop, K is read from LDS)
 //   online max / sum  (each lane owns one query column of S^T, so the row
 //                      reductions are in-lane plus one swap between lane halves)
 //   O^T += V^T P^T    (MFMA; P^T comes straight from the S^T accumulators, V^T is
-//                      read from a transposed LDS copy)
+//                      read from the row-major V tile with transposed LDS reads)
 // Scores are kept in the log2 domain (scale * log2 e folded in) so the exponent is
 // one v_exp_f32.
 #include "fa_common.hpp"
@@ -27,23 +28,28 @@ struct FwdParams {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
-  int Hq, Hkv, Nq, Nkv, G, off;  // off = Nkv - Nq (bottom-right causal offset)
+  int B, Hq, Hkv, Nq, Nkv, G, off;  // off = Nkv - Nq (bottom-right causal offset)
   float scale_log2;
 };
 
 template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
-  constexpr int BM = 128, BN = 64;
-  constexpr int LDK = D + 8;    // row-major K tile, padded against bank conflicts
-  constexpr int LDVT = BN + 4;  // transposed V tile [d][key]
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t VTs[D * LDVT];
+__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
+  constexpr int BM = 128, BN = 64, NG = D / 8;
+  constexpr int TILE = BN * D;           // elements of one K or V tile
+  constexpr int CH = BN * NG / 256;      // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int h = blockIdx.y, b = blockIdx.z;
+  const int nqt = (p.Nq + BM - 1) / BM;
+  int rank, head;
+  map_block(blockIdx.x, p.B * p.Hq, rank, head);
+  // causal: the last query tile sees the most keys, so it goes out first
+  const int qt = CAUSAL ? nqt - 1 - rank : rank;
+  const int b = head / p.Hq, h = head % p.Hq;
   const int hk = h / p.G;
-  const int q0 = blockIdx.x * BM;
+  const int q0 = qt * BM;
   const size_t qbase = ((size_t)b * p.Hq + h) * (size_t)p.Nq;
   const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
   const uint16_t* __restrict__ Q = p.q + qbase * D;
@@ -68,42 +74,57 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
   }
   const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int kv0 = kt * BN;
-    __syncthreads();
+  u32x4 pk[CH], pv[CH];
+  auto load = [&](int kt) {
 #pragma unroll
-    for (int c = tid; c < BN * D / 8; c += 256) {
-      const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int kr = kv0 + r;
-      u32x4 kk = zero_u4(), vv = zero_u4();
-      if (kr < p.Nkv) {
-        kk = ld16(K + (size_t)kr * D + col);
-        vv = ld16(V + (size_t)kr * D + col);
-      }
-      *reinterpret_cast<u32x4*>(Ks + r * LDK + col) = kk;
-      lds_store_transposed(VTs, LDVT, r, col, vv);
+    for (int c = 0; c < CH; ++c) {
+      const int ch = tid + 256 * c, r = ch / NG, j = ch % NG;
+      const int kr = kt * BN + r;
+      pk[c] = kr < p.Nkv ? ld16(K + (size_t)kr * D + 8 * j) : zero_u4();
+      pv[c] = kr < p.Nkv ? ld16(V + (size_t)kr * D + 8 * j) : zero_u4();
     }
-    __syncthreads();
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int ch = tid + 256 * c, r = ch / NG, j = ch % NG;
+      *reinterpret_cast<u32x4*>(&sK[buf][soff<NG>(r, 8 * j)]) = pk[c];
+      *reinterpret_cast<u32x4*>(&sV[buf][soff<NG>(r, 8 * j)]) = pv[c];
+    }
+  };
 
+  if (nkt > 0) {
+    load(0);
+    stage(0);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int cur = kt & 1;
+    const int kv0 = kt * BN;
+    if (kt + 1 < nkt) load(kt + 1);
+
+    // S^T = K Q^T for this wave's 32 query columns
     f32x16 st[BN / 32];
 #pragma unroll
     for (int t = 0; t < BN / 32; ++t) {
       st[t] = zero16();
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(Ks + (32 * t + l32) * LDK + 16 * s + 8 * g);
-        st[t] = Dt<DT>::mma(a, qf[s], st[t]);
-      }
+      for (int s = 0; s < D / 16; ++s)
+        st[t] = Dt<DT>::mma(lds_row16<NG>(sK[cur], 32 * t + l32, 2 * s + g), qf[s], st[t]);
     }
 
+    const bool need_mask = kv0 + BN > p.Nkv || (CAUSAL && kv0 + BN - 1 > q0 + 32 * w + p.off);
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < BN / 32; ++t) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kv = kv0 + 32 * t + crow_of(i, g);
-        const bool masked = kv >= p.Nkv || (CAUSAL && kv > qrow + p.off);
-        const float x = masked ? -INFINITY : st[t][i] * p.scale_log2;
+        float x = st[t][i] * p.scale_log2;
+        if (need_mask) {
+          const int kv = kv0 + 32 * t + crow_of(i, g);
+          if (kv >= p.Nkv || (CAUSAL && kv > qrow + p.off)) x = -INFINITY;
+        }
         st[t][i] = x;
         mx = fmaxf(mx, x);
       }
@@ -130,18 +151,23 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[n][i] *= alpha;
 
+    // O^T += V^T P^T; V^T comes from the row-major V tile by transposed reads
 #pragma unroll
     for (int t = 0; t < BN / 32; ++t) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const u32x4 pb = pack_c_slice<DT>(st[t], c);
+        const int k0 = 32 * t + 16 * c + 4 * g;
 #pragma unroll
         for (int n = 0; n < D / 32; ++n) {
-          const u32x4 a = lds_read_crow_operand(VTs, LDVT, 32 * n + l32, 32 * t, c, g);
+          const u32x4 a = lds_tr_operand<NG>(sV[cur], k0, k0 + 8, 32 * n + 16 * ((lane >> 4) & 1));
           acc[n] = Dt<DT>::mma(a, pb, acc[n]);
         }
       }
     }
+
+    if (kt + 1 < nkt) stage(cur ^ 1);
+    __syncthreads();
   }
 
   if (qrow < p.Nq) {
@@ -170,6 +196,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   p.v = static_cast<const uint16_t*>(a.v);
   p.o = static_cast<uint16_t*>(a.o);
   p.lse = a.lse;
+  p.B = pb.B;
   p.Hq = pb.Hq;
   p.Hkv = pb.Hkv;
   p.Nq = pb.Nq;
@@ -177,7 +204,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   p.G = pb.Hq / pb.Hkv;
   p.off = pb.Nkv - pb.Nq;
   p.scale_log2 = pb.scale * kLog2e;
-  dim3 grid((pb.Nq + 127) / 128, pb.Hq, pb.B);
+  const dim3 grid((unsigned)(((pb.Nq + 127) / 128) * pb.Hq * pb.B));
   hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
