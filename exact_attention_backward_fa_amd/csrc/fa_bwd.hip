@@ -106,8 +106,10 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // registers and their dK and dV as float32 accumulators.  The loop runs over the
 // G query heads of the group and, per head, over 64-row query tiles from the first
 // one that can see the key tile (causal) to the end.  Query tiles (Q, dO, LSE, D)
-// are double-buffered in LDS and the next one is fetched into registers while the
-// current one is used, so each iteration needs one barrier.
+// are double-buffered in LDS: the next one is copied straight from global memory
+// into the other buffer while the current one is used, so each iteration needs one
+// barrier.  Tiles that touch the causal boundary or a ragged end take a masked
+// variant of the math; interior tiles skip the per-element mask.
 //
 // S = Q K^T is computed with the key index in the lane (C column), so P^T and dS^T
 // feed dV += P^T dO and dK += dS^T Q straight from the accumulators; dO and Q are
@@ -121,7 +123,6 @@ template <int DT, int D, bool CAUSAL, bool ATOMIC_DQ>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BN = 128, BM = 64, NG = D / 8;
   constexpr int TILE = BM * D;
-  constexpr int CH = BM * NG / 256;  // 16-byte chunks per thread per Q/dO tile
   __shared__ __attribute__((aligned(16))) uint16_t sQ[2][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sdO[2][TILE];
   __shared__ __attribute__((aligned(16))) float sL[2][BM];
@@ -176,37 +177,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     qbase = ((size_t)b * p.Hq + (size_t)hk * p.G + hh) * (size_t)p.Nq;
   };
 
-  u32x4 pq[CH], pd[CH];
-  float pl = 0.f, pdl = 0.f;
-  auto load = [&](int it) {
+  // Query tile `it` straight into LDS buffer `buf`; rows past N_q repeat row
+  // N_q-1 and are masked in the math.
+  auto fetch = [&](int it, int buf) {
     size_t qbase;
     int q0;
     tile_of(it, qbase, q0);
-    const uint16_t* __restrict__ Qh = p.q + qbase * D;
-    const uint16_t* __restrict__ dOh = p.dout + qbase * D;
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ch = tid + 256 * c, r = ch / NG, j = ch % NG;
-      const int qr = q0 + r;
-      pq[c] = qr < p.Nq ? ld16(Qh + (size_t)qr * D + 8 * j) : zero_u4();
-      pd[c] = qr < p.Nq ? ld16(dOh + (size_t)qr * D + 8 * j) : zero_u4();
-    }
-    if (tid < BM) {
-      const int qr = q0 + tid;
-      pl = qr < p.Nq ? p.lse2[qbase + qr] : INFINITY;
-      pdl = qr < p.Nq ? p.delta[qbase + qr] : 0.f;
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ch = tid + 256 * c, r = ch / NG, j = ch % NG;
-      *reinterpret_cast<u32x4*>(&sQ[buf][soff<NG>(r, 8 * j)]) = pq[c];
-      *reinterpret_cast<u32x4*>(&sdO[buf][soff<NG>(r, 8 * j)]) = pd[c];
-    }
-    if (tid < BM) {
-      sL[buf][tid] = pl;
-      sD[buf][tid] = pdl;
+    dma_tile<NG, BM>(p.q + qbase * D, q0, p.Nq, sQ[buf], w, lane);
+    dma_tile<NG, BM>(p.dout + qbase * D, q0, p.Nq, sdO[buf], w, lane);
+    if (w == 0) {
+      const size_t r = qbase + min(q0 + lane, p.Nq - 1);
+      dma4(p.lse2 + r, sL[buf]);
+      dma4(p.delta + r, sD[buf]);
     }
   };
 
@@ -229,83 +211,95 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         const u32x4 bk = lds_tr_operand<NG>(sK, k0, k0 + 4, 32 * tn + 16 * hi16);
         acc = Dt<DT>::mma(a, bk, acc);
       }
+      float* rowp = dQacc + (size_t)(q0 + 32 * tq + 4 * g) * D + 32 * tn + l32;
+      if (q0 + BM <= p.Nq) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qg = q0 + 32 * tq + crow_of(i, g);
-        if (qg < p.Nq) atomicAdd(dQacc + (size_t)qg * D + 32 * tn + l32, acc[i] * p.scale);
+        for (int i = 0; i < 16; ++i) atomicAdd(rowp + (8 * (i >> 2) + (i & 3)) * D, acc[i] * p.scale);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (q0 + 32 * tq + crow_of(i, g) < p.Nq)
+            atomicAdd(rowp + (8 * (i >> 2) + (i & 3)) * D, acc[i] * p.scale);
       }
     }
   };
 
-  // One iteration on LDS buffer CUR (a compile-time constant, so every LDS address
-  // is a fixed offset from a per-lane base).
+  // The math of one query tile on LDS buffer CUR.  MASK: some (query, key) pair of
+  // this wave's block is outside the causal mask or past N_q / N_kv.
+  auto compute = [&](auto cur_c, auto mask_c, int q0, f32x16* dp) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
+    f32x16 sp[BM / 32];
+#pragma unroll
+    for (int t = 0; t < BM / 32; ++t) {
+      sp[t] = zero16();
+      dp[t] = zero16();
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        sp[t] = Dt<DT>::mma(lds_row16<NG>(sQ[cur], 32 * t + l32, 2 * s + g), kf[s], sp[t]);
+        dp[t] = Dt<DT>::mma(lds_row16<NG>(sdO[cur], 32 * t + l32, 2 * s + g), vf[s], dp[t]);
+      }
+    }
+    // P and dS in place (sp <- P, dp <- dS), indexed [query row crow][key kv_lane].
+#pragma unroll
+    for (int t = 0; t < BM / 32; ++t) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qb = 32 * t + 8 * j + 4 * g;
+        const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[cur][qb]);
+        const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[cur][qb]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * j + e;
+          float pv = fast_exp2(sp[t][i] * p.scale_log2 - L4[e]);
+          if (MASK) {
+            const int q = q0 + qb + e;
+            const bool masked = kv_lane >= p.Nkv || q >= p.Nq || (CAUSAL && kv_lane > q + p.off);
+            pv = masked ? 0.f : pv;
+          }
+          sp[t][i] = pv;
+          dp[t][i] = pv * (dp[t][i] - D4[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < BM / 32; ++t) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 pa = pack_c_slice<DT>(sp[t], c);
+        const u32x4 sa = pack_c_slice<DT>(dp[t], c);
+        const int k0 = 32 * t + 16 * c + 4 * g;
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n) {
+          const u32x4 bo = lds_tr_operand<NG>(sdO[cur], k0, k0 + 8, 32 * n + 16 * hi16);
+          dv[n] = Dt<DT>::mma(pa, bo, dv[n]);
+          const u32x4 bq = lds_tr_operand<NG>(sQ[cur], k0, k0 + 8, 32 * n + 16 * hi16);
+          dk[n] = Dt<DT>::mma(sa, bq, dk[n]);
+        }
+      }
+    }
+  };
+
+  // One iteration on LDS buffer CUR (a compile-time constant, so LDS addresses are
+  // fixed offsets from per-lane bases).
   auto body = [&](int it, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;
     if (ATOMIC_DQ && it > 0) dq_product(cur ^ 1, it - 1);
-    if (it + 1 < n_it) load(it + 1);
+    if (it + 1 < n_it) fetch(it + 1, cur ^ 1);
     size_t qbase_unused;
     int q0;
     tile_of(it, qbase_unused, q0);
-
-    // Skip the math for a wave whose 32 keys are all masked for this tile.
+    f32x16 dp[BM / 32];
     const bool all_masked = kvw >= p.Nkv || (CAUSAL && kvw > q0 + BM - 1 + p.off);
-    f32x16 sp[BM / 32], dp[BM / 32];
-    if (!all_masked) {
-#pragma unroll
-      for (int t = 0; t < BM / 32; ++t) {
-        sp[t] = zero16();
-        dp[t] = zero16();
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          sp[t] = Dt<DT>::mma(lds_row16<NG>(sQ[cur], 32 * t + l32, 2 * s + g), kf[s], sp[t]);
-          dp[t] = Dt<DT>::mma(lds_row16<NG>(sdO[cur], 32 * t + l32, 2 * s + g), vf[s], dp[t]);
-        }
-      }
-
-      // P and dS in place (sp <- P, dp <- dS), indexed [query row crow][key kv_lane].
-      const bool need_mask = kvw + 31 >= p.Nkv || (CAUSAL && kvw + 31 > q0 + p.off);
-#pragma unroll
-      for (int t = 0; t < BM / 32; ++t) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int qb = 32 * t + 8 * j + 4 * g;
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[cur][qb]);
-          const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[cur][qb]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * j + e;
-            float pv = fast_exp2(sp[t][i] * p.scale_log2 - L4[e]);
-            if (need_mask) {
-              const bool masked = kv_lane >= p.Nkv || (CAUSAL && kv_lane > q0 + qb + e + p.off);
-              pv = masked ? 0.f : pv;
-            }
-            sp[t][i] = pv;
-            dp[t][i] = pv * (dp[t][i] - D4[e]);
-          }
-        }
-      }
-
-#pragma unroll
-      for (int t = 0; t < BM / 32; ++t) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const u32x4 pa = pack_c_slice<DT>(sp[t], c);
-          const u32x4 sa = pack_c_slice<DT>(dp[t], c);
-          const int k0 = 32 * t + 16 * c + 4 * g;
-#pragma unroll
-          for (int n = 0; n < D / 32; ++n) {
-            const u32x4 bo = lds_tr_operand<NG>(sdO[cur], k0, k0 + 8, 32 * n + 16 * hi16);
-            dv[n] = Dt<DT>::mma(pa, bo, dv[n]);
-            const u32x4 bq = lds_tr_operand<NG>(sQ[cur], k0, k0 + 8, 32 * n + 16 * hi16);
-            dk[n] = Dt<DT>::mma(sa, bq, dk[n]);
-          }
-        }
-      }
-    } else {
+    const bool need_mask = kvw + 31 >= p.Nkv || q0 + BM > p.Nq || (CAUSAL && kvw + 31 > q0 + p.off);
+    if (all_masked) {
 #pragma unroll
       for (int t = 0; t < BM / 32; ++t) dp[t] = zero16();
+    } else if (need_mask) {
+      compute(cur_c, std::true_type(), q0, dp);
+    } else {
+      compute(cur_c, std::false_type(), q0, dp);
     }
-
     if (ATOMIC_DQ) {
       // dS^T[key][query]: 4 consecutive query rows per 8-byte store
 #pragma unroll
@@ -319,14 +313,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         }
       }
     }
-    if (it + 1 < n_it) stage(cur ^ 1);
+    wait_vmem();
     __syncthreads();
   };
 
-  if (n_it > 0) {
-    load(0);
-    stage(0);
-  }
+  if (n_it > 0) fetch(0, 0);
+  wait_vmem();
   __syncthreads();
 
   for (int it = 0; it < n_it; it += 2) {
@@ -360,12 +352,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 // head); wave w owns 32 of them and keeps their Q and dO as MFMA operands in
 // registers.  S^T = K Q^T puts the query index in the lane, so dS feeds
 // dQ += dS K straight from the accumulators; K is read transposed from the
-// row-major LDS tile.  Key/value tiles are double-buffered like the forward's.
+// row-major LDS tile.  Key/value tiles are double-buffered and copied straight from
+// global memory, like the forward's.
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int BM = 128, BN = 64, NG = D / 8;
   constexpr int TILE = BN * D;
-  constexpr int CH = BN * NG / 256;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][TILE];
 
@@ -378,7 +370,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   const int b = head / p.Hq, h = head % p.Hq;
   const int hk = h / p.G;
   const int q0 = qt * BM;
-  const int qrow = q0 + 32 * w + l32;
+  const int qw = q0 + 32 * w;  // first query row of this wave
+  const int qrow = qw + l32;
   const size_t qbase = ((size_t)b * p.Hq + h) * (size_t)p.Nq;
   const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
   const uint16_t* __restrict__ K = p.k + kbase * D;
@@ -404,36 +397,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   }
   const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
-  u32x4 pk[CH], pv[CH];
-  auto load = [&](int kt) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ch = tid + 256 * c, r = ch / NG, j = ch % NG;
-      const int kr = kt * BN + r;
-      pk[c] = kr < p.Nkv ? ld16(K + (size_t)kr * D + 8 * j) : zero_u4();
-      pv[c] = kr < p.Nkv ? ld16(V + (size_t)kr * D + 8 * j) : zero_u4();
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ch = tid + 256 * c, r = ch / NG, j = ch % NG;
-      *reinterpret_cast<u32x4*>(&sK[buf][soff<NG>(r, 8 * j)]) = pk[c];
-      *reinterpret_cast<u32x4*>(&sV[buf][soff<NG>(r, 8 * j)]) = pv[c];
-    }
+  auto fetch = [&](int kt, int buf) {
+    dma_tile<NG, BN>(K, kt * BN, p.Nkv, sK[buf], w, lane);
+    dma_tile<NG, BN>(V, kt * BN, p.Nkv, sV[buf], w, lane);
   };
 
-  if (nkt > 0) {
-    load(0);
-    stage(0);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    const int kv0 = kt * BN;
-    if (kt + 1 < nkt) load(kt + 1);
-
+  auto compute = [&](auto cur_c, auto mask_c, int kv0) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
     f32x16 st[BN / 32], dpt[BN / 32];
 #pragma unroll
     for (int t = 0; t < BN / 32; ++t) {
@@ -445,13 +416,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         dpt[t] = Dt<DT>::mma(lds_row16<NG>(sV[cur], 32 * t + l32, 2 * s + g), df[s], dpt[t]);
       }
     }
-    const bool need_mask = kv0 + BN > p.Nkv || (CAUSAL && kv0 + BN - 1 > q0 + 32 * w + p.off);
 #pragma unroll
     for (int t = 0; t < BN / 32; ++t) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float pv = fast_exp2(st[t][i] * p.scale_log2 - lse_q);
-        if (need_mask) {
+        if (MASK) {
           const int kv = kv0 + 32 * t + crow_of(i, g);
           if (kv >= p.Nkv || (CAUSAL && kv > qrow + p.off)) pv = 0.f;
         }
@@ -471,9 +441,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         }
       }
     }
+  };
 
-    if (kt + 1 < nkt) stage(cur ^ 1);
+  auto body = [&](int kt, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    if (kt + 1 < nkt) fetch(kt + 1, cur ^ 1);
+    const int kv0 = kt * BN;
+    const bool need_mask = kv0 + BN > p.Nkv || (CAUSAL && kv0 + BN - 1 > qw + p.off);
+    const bool all_masked = CAUSAL && kv0 > qw + 31 + p.off;
+    if (!all_masked) {
+      if (need_mask)
+        compute(cur_c, std::true_type(), kv0);
+      else
+        compute(cur_c, std::false_type(), kv0);
+    }
+    wait_vmem();
     __syncthreads();
+  };
+
+  if (nkt > 0) fetch(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; kt += 2) {
+    body(kt, std::integral_constant<int, 0>());
+    if (kt + 1 < nkt) body(kt + 1, std::integral_constant<int, 1>());
   }
 
   uint16_t* __restrict__ dQ = p.dq + qbase * D;
@@ -481,7 +472,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   for (int n = 0; n < D / 32; ++n) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int qr = q0 + 32 * w + crow_of(i, g);
+      const int qr = qw + crow_of(i, g);
       if (qr < p.Nq) dQ[(size_t)qr * D + 32 * n + l32] = Dt<DT>::one(acc[n][i] * p.scale);
     }
   }

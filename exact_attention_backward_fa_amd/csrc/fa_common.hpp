@@ -166,6 +166,40 @@ __device__ __forceinline__ void map_block(int L, int n_heads, int& rank, int& he
   }
 }
 
+// ---------------------------------------------------------------------------
+// Direct global -> LDS copies (global_load_lds_dwordx4 / _dword).  Every lane
+// supplies its own global address; the data of lane L lands at lds_base + size*L,
+// so one wave instruction fills 64*size contiguous LDS bytes.  The copy is tracked
+// by vmcnt only: wait_vmem() must run before the barrier that publishes it.
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gsrc,
+                                   (void __attribute__((address_space(3)))*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gsrc,
+                                   (void __attribute__((address_space(3)))*)lds_base, 4, 0, 0);
+}
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Fill a swizzled ROWS x (NG*8) tile from rows row0.. of a row-major matrix with
+// NG*8 columns; rows at or past n_rows read row n_rows-1 instead (callers mask
+// them).  256 threads; each wave issues ROWS*NG/256 copies of 1 KB.
+template <int NG, int ROWS>
+__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ g, int row0, int n_rows,
+                                         uint16_t* lds, int w, int lane) {
+  constexpr int PER_WAVE = ROWS * NG / 256;
+#pragma unroll
+  for (int c = 0; c < PER_WAVE; ++c) {
+    const int blk = PER_WAVE * w + c;
+    const int ph = blk * 64 + lane;  // physical granule this lane fills
+    const int r = ph / NG;
+    const int j = (ph % NG) ^ swz<NG>(r);
+    const int rr = min(row0 + r, n_rows - 1);
+    dma16(g + (size_t)rr * (NG * 8) + 8 * j, lds + blk * 64 * 8);
+  }
+}
+
 // 16-byte global load/store helpers.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

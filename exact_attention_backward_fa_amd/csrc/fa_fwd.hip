@@ -8,7 +8,8 @@
 //
 // One workgroup = 4 waves = 128 query rows of one (batch, query head); each wave
 // owns 32 rows.  Key and value tiles of 64 rows are double-buffered in LDS: the
-// next tile is fetched into registers while the current one is used.  Per tile:
+// next tile is copied straight from global memory into the other buffer while the
+// current one is used.  Per tile:
 //   S^T = K Q^T       (MFMA; Q stays in registers as the B operand for the whole
 //                      loop, K is read from LDS)
 //   online max / sum  (each lane owns one query column of S^T, so the row
@@ -19,6 +20,8 @@
 // one v_exp_f32.
 #include "fa_common.hpp"
 #include "fa_internal.hpp"
+
+#include <type_traits>
 
 namespace fa {
 
@@ -36,7 +39,6 @@ template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   constexpr int BM = 128, BN = 64, NG = D / 8;
   constexpr int TILE = BN * D;           // elements of one K or V tile
-  constexpr int CH = BN * NG / 256;      // 16-byte chunks per thread per tile
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][TILE];
 
@@ -74,36 +76,16 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   }
   const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
-  u32x4 pk[CH], pv[CH];
-  auto load = [&](int kt) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ch = tid + 256 * c, r = ch / NG, j = ch % NG;
-      const int kr = kt * BN + r;
-      pk[c] = kr < p.Nkv ? ld16(K + (size_t)kr * D + 8 * j) : zero_u4();
-      pv[c] = kr < p.Nkv ? ld16(V + (size_t)kr * D + 8 * j) : zero_u4();
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int ch = tid + 256 * c, r = ch / NG, j = ch % NG;
-      *reinterpret_cast<u32x4*>(&sK[buf][soff<NG>(r, 8 * j)]) = pk[c];
-      *reinterpret_cast<u32x4*>(&sV[buf][soff<NG>(r, 8 * j)]) = pv[c];
-    }
+  auto fetch = [&](int kt, int buf) {
+    dma_tile<NG, BN>(K, kt * BN, p.Nkv, sK[buf], w, lane);
+    dma_tile<NG, BN>(V, kt * BN, p.Nkv, sV[buf], w, lane);
   };
 
-  if (nkt > 0) {
-    load(0);
-    stage(0);
-  }
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    const int kv0 = kt * BN;
-    if (kt + 1 < nkt) load(kt + 1);
-
+  // One key tile on LDS buffer CUR; MASK: the tile crosses the causal boundary of
+  // this wave's rows or the end of the keys.
+  auto compute = [&](auto cur_c, auto mask_c, int kv0) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
     // S^T = K Q^T for this wave's 32 query columns
     f32x16 st[BN / 32];
 #pragma unroll
@@ -113,15 +95,13 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       for (int s = 0; s < D / 16; ++s)
         st[t] = Dt<DT>::mma(lds_row16<NG>(sK[cur], 32 * t + l32, 2 * s + g), qf[s], st[t]);
     }
-
-    const bool need_mask = kv0 + BN > p.Nkv || (CAUSAL && kv0 + BN - 1 > q0 + 32 * w + p.off);
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < BN / 32; ++t) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float x = st[t][i] * p.scale_log2;
-        if (need_mask) {
+        if (MASK) {
           const int kv = kv0 + 32 * t + crow_of(i, g);
           if (kv >= p.Nkv || (CAUSAL && kv > qrow + p.off)) x = -INFINITY;
         }
@@ -165,9 +145,31 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         }
       }
     }
+  };
 
-    if (kt + 1 < nkt) stage(cur ^ 1);
+  const int qw = q0 + 32 * w;  // first query row of this wave
+  auto body = [&](int kt, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    if (kt + 1 < nkt) fetch(kt + 1, cur ^ 1);
+    const int kv0 = kt * BN;
+    const bool need_mask = kv0 + BN > p.Nkv || (CAUSAL && kv0 + BN - 1 > qw + p.off);
+    const bool all_masked = CAUSAL && kv0 > qw + 31 + p.off;
+    if (!all_masked) {
+      if (need_mask)
+        compute(cur_c, std::true_type(), kv0);
+      else
+        compute(cur_c, std::false_type(), kv0);
+    }
+    wait_vmem();
     __syncthreads();
+  };
+
+  if (nkt > 0) fetch(0, 0);
+  wait_vmem();
+  __syncthreads();
+  for (int kt = 0; kt < nkt; kt += 2) {
+    body(kt, std::integral_constant<int, 0>());
+    if (kt + 1 < nkt) body(kt + 1, std::integral_constant<int, 1>());
   }
 
   if (qrow < p.Nq) {
