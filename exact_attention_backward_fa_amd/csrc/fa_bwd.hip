@@ -226,58 +226,119 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   // The math of one query tile on LDS buffer CUR.  MASK: some (query, key) pair of
   // this wave's block is outside the causal mask or past N_q / N_kv.
+  //
+  // The iteration is one stream of 4*NM MFMAs (NM = D/8), in four quarters:
+  //   S_0, dP_0 | S_1, dP_1 | dV, dK from half 0 | dV, dK from half 1
+  // (half t = query rows 32t..32t+31 of the tile).  Step j issues the LDS reads of
+  // the operand of MFMA j+LA, then MFMA j, then a fixed share of the VALU work:
+  // the softmax of half 0 rides on quarter 1, that of half 1 on quarter 2, and
+  // each half's P / dS operands are packed just before they are consumed.  A fence
+  // after every step keeps this order, so LDS latency hides behind LA MFMAs and the
+  // VALU behind the matrix pipe.
   auto compute = [&](auto cur_c, auto mask_c, int q0, f32x16* dp) {
     constexpr int cur = decltype(cur_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
-    f32x16 sp[BM / 32];
+    constexpr int NM = D / 8;  // MFMAs per quarter
+    constexpr int NS = 4 * NM;
+    constexpr int LA = 4;      // operand lookahead, in MFMAs
+    f32x16 sp[2];
+    u32x4 pa[2][2], sa[2][2];  // packed P^T / dS^T operands [half][k-step]
+    f32x4 L4[4], D4[4];
+
+    // operand of MFMA J
+    auto operand = [&](auto jc) -> u32x4 {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j < 2 * NM) {
+        constexpr int t = j / NM, s = (j % NM) / 2;
+        if constexpr (j & 1)
+          return lds_row16<NG>(sdO[cur], 32 * t + l32, 2 * s + g);
+        else
+          return lds_row16<NG>(sQ[cur], 32 * t + l32, 2 * s + g);
+      } else {
+        constexpr int jj = j - 2 * NM, t = jj / NM, k = jj % NM;
+        constexpr int c = k / (NM / 2), n = (k % (NM / 2)) / 2;
+        const int k0 = 32 * t + 16 * c + 4 * g;
+        if constexpr (k & 1)
+          return lds_tr_operand<NG>(sQ[cur], k0, k0 + 8, 32 * n + 16 * hi16);
+        else
+          return lds_tr_operand<NG>(sdO[cur], k0, k0 + 8, 32 * n + 16 * hi16);
+      }
+    };
+    auto mfma = [&](auto jc, const u32x4& op) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j < 2 * NM) {
+        constexpr int t = j / NM, s = (j % NM) / 2;
+        if constexpr (j & 1)
+          dp[t] = Dt<DT>::mma(op, vf[s], dp[t]);
+        else
+          sp[t] = Dt<DT>::mma(op, kf[s], sp[t]);
+      } else {
+        constexpr int jj = j - 2 * NM, t = jj / NM, k = jj % NM;
+        constexpr int c = k / (NM / 2), n = (k % (NM / 2)) / 2;
+        if constexpr (k & 1)
+          dk[n] = Dt<DT>::mma(sa[t][c], op, dk[n]);
+        else
+          dv[n] = Dt<DT>::mma(pa[t][c], op, dv[n]);
+      }
+    };
+    // P and dS for element I of half T, in place (sp <- P, dp <- dS)
+    auto softmax_elem = [&](auto tc, auto ic) {
+      constexpr int t = decltype(tc)::value, i = decltype(ic)::value;
+      constexpr int j4 = i >> 2, e = i & 3;
+      float x = sp[t][i] * p.scale_log2 - L4[j4][e];
+      if constexpr (MASK) {
+        const int q = q0 + 32 * t + 8 * j4 + 4 * g + e;
+        const bool masked = kv_lane >= p.Nkv || q >= p.Nq || (CAUSAL && kv_lane > q + p.off);
+        x = masked ? -INFINITY : x;
+      }
+      const float pv = fast_exp2(x);
+      sp[t][i] = pv;
+      dp[t][i] = pv * (dp[t][i] - D4[j4][e]);
+    };
+    auto load_lse = [&](int t) {
 #pragma unroll
-    for (int t = 0; t < BM / 32; ++t) {
+      for (int j4 = 0; j4 < 4; ++j4) {
+        L4[j4] = *reinterpret_cast<const f32x4*>(&sL[cur][32 * t + 8 * j4 + 4 * g]);
+        D4[j4] = *reinterpret_cast<const f32x4*>(&sD[cur][32 * t + 8 * j4 + 4 * g]);
+      }
+    };
+    // VALU share of step J: half 0's softmax rides on quarter 1 (steps NM..2NM-1,
+    // spread over its first NM-4 steps, then its packing), half 1's on quarter 2.
+    auto valu = [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      static_for<2>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int base = (t + 1) * NM;
+        constexpr int r = j - base;
+        if constexpr (j == base - 2) load_lse(t);
+        if constexpr (r >= 0 && r < NM - 4) {
+          constexpr int e0 = (16 * r) / (NM - 4), e1 = (16 * (r + 1)) / (NM - 4);
+          static_for<e1 - e0>([&](auto ic) {
+            softmax_elem(tc, std::integral_constant<int, e0 + decltype(ic)::value>());
+          });
+        }
+        if constexpr (r == NM - 4) pa[t][0] = pack_c_slice<DT>(sp[t], 0);
+        if constexpr (r == NM - 3) pa[t][1] = pack_c_slice<DT>(sp[t], 1);
+        if constexpr (r == NM - 2) sa[t][0] = pack_c_slice<DT>(dp[t], 0);
+        if constexpr (r == NM - 1) sa[t][1] = pack_c_slice<DT>(dp[t], 1);
+      });
+    };
+
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
       sp[t] = zero16();
       dp[t] = zero16();
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        sp[t] = Dt<DT>::mma(lds_row16<NG>(sQ[cur], 32 * t + l32, 2 * s + g), kf[s], sp[t]);
-        dp[t] = Dt<DT>::mma(lds_row16<NG>(sdO[cur], 32 * t + l32, 2 * s + g), vf[s], dp[t]);
-      }
     }
-    // P and dS in place (sp <- P, dp <- dS), indexed [query row crow][key kv_lane].
-#pragma unroll
-    for (int t = 0; t < BM / 32; ++t) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int qb = 32 * t + 8 * j + 4 * g;
-        const f32x4 L4 = *reinterpret_cast<const f32x4*>(&sL[cur][qb]);
-        const f32x4 D4 = *reinterpret_cast<const f32x4*>(&sD[cur][qb]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * j + e;
-          float pv = fast_exp2(sp[t][i] * p.scale_log2 - L4[e]);
-          if (MASK) {
-            const int q = q0 + qb + e;
-            const bool masked = kv_lane >= p.Nkv || q >= p.Nq || (CAUSAL && kv_lane > q + p.off);
-            pv = masked ? 0.f : pv;
-          }
-          sp[t][i] = pv;
-          dp[t][i] = pv * (dp[t][i] - D4[e]);
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < BM / 32; ++t) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4 pa = pack_c_slice<DT>(sp[t], c);
-        const u32x4 sa = pack_c_slice<DT>(dp[t], c);
-        const int k0 = 32 * t + 16 * c + 4 * g;
-#pragma unroll
-        for (int n = 0; n < D / 32; ++n) {
-          const u32x4 bo = lds_tr_operand<NG>(sdO[cur], k0, k0 + 8, 32 * n + 16 * hi16);
-          dv[n] = Dt<DT>::mma(pa, bo, dv[n]);
-          const u32x4 bq = lds_tr_operand<NG>(sQ[cur], k0, k0 + 8, 32 * n + 16 * hi16);
-          dk[n] = Dt<DT>::mma(sa, bq, dk[n]);
-        }
-      }
-    }
+    u32x4 ops[LA];
+    static_for<LA>([&](auto jc) { ops[decltype(jc)::value] = operand(jc); });
+    static_for<NS>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const u32x4 op = ops[j % LA];
+      if constexpr (j + LA < NS) ops[j % LA] = operand(std::integral_constant<int, j + LA>());
+      mfma(jc, op);
+      valu(jc);
+      sched_fence();
+    });
   };
 
   // One iteration on LDS buffer CUR (a compile-time constant, so LDS addresses are

@@ -15,6 +15,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -198,6 +201,24 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ g, int row
     const int rr = min(row0 + r, n_rows - 1);
     dma16(g + (size_t)rr * (NG * 8) + 8 * j, lds + blk * 64 * 8);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Instruction-scheduling hints (LLVM AMDGPU sched_group_barrier): ask the
+// scheduler to place the next `n` instructions of a class here, in program order
+// of the hints; sched_fence() keeps instructions from moving across it.
+enum : int { SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM = 0x010, SG_DSR = 0x100, SG_DSW = 0x200 };
+#define sched_group(mask, n) __builtin_amdgcn_sched_group_barrier((mask), (n), 0)
+#define sched_fence() __builtin_amdgcn_sched_barrier(0)
+
+// Compile-time loop: f(std::integral_constant<int, 0>()), ..., f(..., N-1>()).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>()), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>());
 }
 
 // 16-byte global load/store helpers.
