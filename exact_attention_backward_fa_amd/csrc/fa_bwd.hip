@@ -463,45 +463,98 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     dma_tile<NG, BN>(V, kt * BN, p.Nkv, sV[buf], w, lane);
   };
 
+  // One key tile on LDS buffer CUR; MASK: the tile crosses the causal boundary of
+  // this wave's rows or the end of the keys.  The tile is one compile-time stream
+  // of MFMAs in four parts:
+  //   S^T_0, dP^T_0 | S^T_1, dP^T_1 | dQ from keys 0..31 | dQ from keys 32..63
+  // (NS1 = D/8 MFMAs per score part, NQ = D/16 per dQ part).  Step j issues the
+  // LDS reads of the operand LA MFMAs ahead, MFMA j, and a share of the VALU: half
+  // 0's dS rides on part 1, half 1's on part 2; a fence after every step keeps the
+  // order.
   auto compute = [&](auto cur_c, auto mask_c, int kv0) {
     constexpr int cur = decltype(cur_c)::value;
     constexpr bool MASK = decltype(mask_c)::value;
-    f32x16 st[BN / 32], dpt[BN / 32];
+    constexpr int NS1 = D / 8, NQ = D / 16;
+    constexpr int NS = 2 * NS1 + 2 * NQ;
+    constexpr int LA = 4;
+    f32x16 st[2], dpt[2];
+    u32x4 da[2][2];  // packed dS operands [half][k-step]
+
+    auto operand = [&](auto jc) -> u32x4 {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j < 2 * NS1) {
+        constexpr int t = j / NS1, s = (j % NS1) / 2;
+        if constexpr (j & 1)
+          return lds_row16<NG>(sV[cur], 32 * t + l32, 2 * s + g);
+        else
+          return lds_row16<NG>(sK[cur], 32 * t + l32, 2 * s + g);
+      } else {
+        constexpr int jj = j - 2 * NS1, t = jj / NQ, k = jj % NQ;
+        constexpr int c = k / (NQ / 2), n = k % (NQ / 2);
+        const int k0 = 32 * t + 16 * c + 4 * g;
+        return lds_tr_operand<NG>(sK[cur], k0, k0 + 8, 32 * n + 16 * hi16);
+      }
+    };
+    auto mfma = [&](auto jc, const u32x4& op) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j < 2 * NS1) {
+        constexpr int t = j / NS1, s = (j % NS1) / 2;
+        if constexpr (j & 1)
+          dpt[t] = Dt<DT>::mma(op, df[s], dpt[t]);
+        else
+          st[t] = Dt<DT>::mma(op, qf[s], st[t]);
+      } else {
+        constexpr int jj = j - 2 * NS1, t = jj / NQ, k = jj % NQ;
+        constexpr int c = k / (NQ / 2), n = k % (NQ / 2);
+        acc[n] = Dt<DT>::mma(da[t][c], op, acc[n]);
+      }
+    };
+    // dS for element I of half T, in place in dpt
+    auto ds_elem = [&](auto tc, auto ic) {
+      constexpr int t = decltype(tc)::value, i = decltype(ic)::value;
+      float x = st[t][i] * p.scale_log2 - lse_q;
+      if constexpr (MASK) {
+        const int kv = kv0 + 32 * t + crow_of(i, g);
+        if (kv >= p.Nkv || (CAUSAL && kv > qrow + p.off)) x = -INFINITY;
+      }
+      const float pv = fast_exp2(x);
+      dpt[t][i] = pv * (dpt[t][i] - dlt_q);
+    };
+    // VALU share of step J: half t's dS is spread over the first steps of the part
+    // after its scores, then packed in the last two steps of that part.
+    auto valu = [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      static_for<2>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        constexpr int base = t == 0 ? NS1 : 2 * NS1;
+        constexpr int len = t == 0 ? NS1 : NQ;
+        constexpr int r = j - base;
+        if constexpr (r >= 0 && r < len - 2) {
+          constexpr int e0 = (16 * r) / (len - 2), e1 = (16 * (r + 1)) / (len - 2);
+          static_for<e1 - e0>([&](auto ic) {
+            ds_elem(tc, std::integral_constant<int, e0 + decltype(ic)::value>());
+          });
+        }
+        if constexpr (r == len - 2) da[t][0] = pack_c_slice<DT>(dpt[t], 0);
+        if constexpr (r == len - 1) da[t][1] = pack_c_slice<DT>(dpt[t], 1);
+      });
+    };
+
 #pragma unroll
-    for (int t = 0; t < BN / 32; ++t) {
+    for (int t = 0; t < 2; ++t) {
       st[t] = zero16();
       dpt[t] = zero16();
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        st[t] = Dt<DT>::mma(lds_row16<NG>(sK[cur], 32 * t + l32, 2 * s + g), qf[s], st[t]);
-        dpt[t] = Dt<DT>::mma(lds_row16<NG>(sV[cur], 32 * t + l32, 2 * s + g), df[s], dpt[t]);
-      }
     }
-#pragma unroll
-    for (int t = 0; t < BN / 32; ++t) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float pv = fast_exp2(st[t][i] * p.scale_log2 - lse_q);
-        if (MASK) {
-          const int kv = kv0 + 32 * t + crow_of(i, g);
-          if (kv >= p.Nkv || (CAUSAL && kv > qrow + p.off)) pv = 0.f;
-        }
-        dpt[t][i] = pv * (dpt[t][i] - dlt_q);
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < BN / 32; ++t) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const u32x4 a = pack_c_slice<DT>(dpt[t], c);
-        const int k0 = 32 * t + 16 * c + 4 * g;
-#pragma unroll
-        for (int n = 0; n < D / 32; ++n) {
-          const u32x4 bk = lds_tr_operand<NG>(sK[cur], k0, k0 + 8, 32 * n + 16 * hi16);
-          acc[n] = Dt<DT>::mma(a, bk, acc[n]);
-        }
-      }
-    }
+    u32x4 ops[LA];
+    static_for<LA>([&](auto jc) { ops[decltype(jc)::value] = operand(jc); });
+    static_for<NS>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const u32x4 op = ops[j % LA];
+      if constexpr (j + LA < NS) ops[j % LA] = operand(std::integral_constant<int, j + LA>());
+      mfma(jc, op);
+      valu(jc);
+      sched_fence();
+    });
   };
 
   auto body = [&](int kt, auto cur_c) {
