@@ -123,10 +123,14 @@ template <int DT, int D, bool CAUSAL, bool ATOMIC_DQ>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BN = 128, BM = 64, NG = D / 8;
   constexpr int TILE = BM * D;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[2][TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sdO[2][TILE];
-  __shared__ __attribute__((aligned(16))) float sL[2][BM];
-  __shared__ __attribute__((aligned(16))) float sD[2][BM];
+  // Query tiles in flight: fetched NBUF-1 iterations ahead (the atomic variant's
+  // LDS holds the K and dS^T tiles as well, so it keeps two buffers).
+  constexpr int NBUF = ATOMIC_DQ ? 2 : 3;
+  constexpr int OPS = 2 * (BM * NG / 256) + 2;  // copy instructions per fetch per wave
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) float sL[NBUF][BM];
+  __shared__ __attribute__((aligned(16))) float sD[NBUF][BM];
   __shared__ __attribute__((aligned(16))) uint16_t sK[ATOMIC_DQ ? BN * D : 8];
   __shared__ __attribute__((aligned(16))) uint16_t sdST[ATOMIC_DQ ? 2 : 1][ATOMIC_DQ ? BN * BM : 8];
 
@@ -185,11 +189,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     tile_of(it, qbase, q0);
     dma_tile<NG, BM>(p.q + qbase * D, q0, p.Nq, sQ[buf], w, lane);
     dma_tile<NG, BM>(p.dout + qbase * D, q0, p.Nq, sdO[buf], w, lane);
-    if (w == 0) {
-      const size_t r = qbase + min(q0 + lane, p.Nq - 1);
-      dma4(p.lse2 + r, sL[buf]);
-      dma4(p.delta + r, sD[buf]);
-    }
+    // every wave copies LSE and D (identical bytes to the same place), so all
+    // waves issue OPS copies per fetch and can share one vmcnt immediate
+    const size_t r = qbase + min(q0 + lane, p.Nq - 1);
+    dma4(p.lse2 + r, sL[buf]);
+    dma4(p.delta + r, sD[buf]);
   };
 
   // dQ_i += scale * dS_i K_j for the query tile staged in sdST[buf]; wave w takes
@@ -345,8 +349,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   // fixed offsets from per-lane bases).
   auto body = [&](int it, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;
-    if (ATOMIC_DQ && it > 0) dq_product(cur ^ 1, it - 1);
-    if (it + 1 < n_it) fetch(it + 1, cur ^ 1);
+    constexpr int last = (cur + NBUF - 1) % NBUF;  // buffer of iteration it-1 and it+NBUF-1
+    if (ATOMIC_DQ && it > 0) dq_product(last, it - 1);
+    const bool ahead = it + NBUF - 1 < n_it;
+    if (ahead) fetch(it + NBUF - 1, last);
     size_t qbase_unused;
     int q0;
     tile_of(it, qbase_unused, q0);
@@ -374,23 +380,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         }
       }
     }
-    wait_vmem();
-    __syncthreads();
+    // tile it+1 must have landed; the fetch of tile it+NBUF-1 may stay in flight
+    if (ahead)
+      wait_vmem_n<OPS * (NBUF - 2)>();
+    else
+      wait_vmem();
+    lds_barrier();
   };
 
-  if (n_it > 0) fetch(0, 0);
-  wait_vmem();
-  __syncthreads();
+  static_for<NBUF - 1>([&](auto bc) {
+    constexpr int k = decltype(bc)::value;
+    if (k < n_it) fetch(k, k);
+  });
+  if (n_it >= NBUF - 1)
+    wait_vmem_n<OPS * (NBUF - 2)>();
+  else
+    wait_vmem();
+  lds_barrier();
 
-  for (int it = 0; it < n_it; it += 2) {
-    body(it, std::integral_constant<int, 0>());
-    if (it + 1 < n_it) body(it + 1, std::integral_constant<int, 1>());
+  for (int it = 0; it < n_it; it += NBUF) {
+    static_for<NBUF>([&](auto bc) {
+      if (it + decltype(bc)::value < n_it) body(it + decltype(bc)::value, bc);
+    });
   }
   if (ATOMIC_DQ && n_it > 0) {
-    if ((n_it - 1) & 1)
-      dq_product(1, n_it - 1);
-    else
-      dq_product(0, n_it - 1);
+    static_for<NBUF>([&](auto bc) {
+      if ((n_it - 1) % NBUF == decltype(bc)::value) dq_product(decltype(bc)::value, n_it - 1);
+    });
   }
 
   uint16_t* __restrict__ dK = p.dk + kbase * D;
@@ -409,6 +425,272 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// dK/dV kernel for the separate-dQ path: two waves per SIMD with split roles.
+//
+// Workgroup = 8 waves = 128 key rows of one (batch, kv head).  Wave w works on key
+// rows 32*(w%4) .. +31 (its "key group", kg) with role w/4:
+//   role 0: S = Q K^T, P = exp(S - LSE) (masked), hands P to its partner through
+//           LDS, then dV += P^T dO;            keeps K and dV in registers;
+//   role 1: dP = dO V^T, then (with the partner's P) dS = P o (dP - D),
+//           dK += dS^T Q;                      keeps V and dK in registers.
+// The two waves of a key group run on the same SIMD, so while one runs VALU
+// (softmax, dS) the other's MFMAs keep the matrix pipe busy.  Each wave needs about
+// half the registers of a single wave doing all five steps.  The loop over query
+// tiles (all G heads of the group) has two barriers per tile: after P is published
+// and at the end of the tile.  Query tiles are triple-buffered in LDS and filled by
+// direct copies, two tiles ahead.
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_rs_kernel(BwdParams p) {
+  constexpr int NT = 512;
+  constexpr int BN = 128, BM = 64, NG = D / 8;
+  constexpr int TILE = BM * D;
+  constexpr int NBUF = 3;
+  constexpr int OPS = 2 * (BM * NG / NT) + 2;  // copy instructions per fetch per wave
+  constexpr int NM = D / 8;                    // MFMAs per product per tile and wave
+  __shared__ __attribute__((aligned(16))) uint16_t sQ[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sdO[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) float sL[NBUF][BM];
+  __shared__ __attribute__((aligned(16))) float sD[NBUF][BM];
+  __shared__ __attribute__((aligned(16))) u32x4 sP[4][2][2][64];  // [kg][half][k-step][lane]
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int kg = w & 3, role = w >> 2;
+  const int l32 = lane & 31, g = lane >> 5, hi16 = (lane >> 4) & 1;
+  int rank, head;
+  map_block(blockIdx.x, p.B * p.Hkv, rank, head);
+  const int b = head / p.Hkv, hk = head % p.Hkv;
+  const int kv0 = rank * BN;
+  const int kvw = kv0 + 32 * kg;
+  const int kv_lane = kvw + l32;
+  const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
+
+  // role 0 holds K (B operand of S = Q K^T), role 1 holds V (of dP = dO V^T)
+  const uint16_t* __restrict__ KV = (role == 0 ? p.k : p.v) + kbase * D;
+  u32x4 bf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    bf[s] = kv_lane < p.Nkv ? ld16(KV + (size_t)kv_lane * D + 16 * s + 8 * g) : zero_u4();
+
+  f32x16 acc[D / 32];  // role 0: dV, role 1: dK
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) acc[n] = zero16();
+
+  const int q_begin = CAUSAL ? max(0, kv0 - p.off) : 0;
+  const int nqt = (p.Nq + BM - 1) / BM;
+  const int qt_begin = q_begin < p.Nq ? q_begin / BM : nqt;
+  const int per_head = nqt - qt_begin;
+  const int n_it = p.G * per_head;
+
+  auto tile_of = [&](int it, size_t& qbase, int& q0) {
+    const int hh = it / per_head;
+    q0 = (qt_begin + it % per_head) * BM;
+    qbase = ((size_t)b * p.Hq + (size_t)hk * p.G + hh) * (size_t)p.Nq;
+  };
+  auto fetch = [&](int it, int buf) {
+    size_t qbase;
+    int q0;
+    tile_of(it, qbase, q0);
+    dma_tile<NG, BM, NT>(p.q + qbase * D, q0, p.Nq, sQ[buf], w, lane);
+    dma_tile<NG, BM, NT>(p.dout + qbase * D, q0, p.Nq, sdO[buf], w, lane);
+    const size_t r = qbase + min(q0 + lane, p.Nq - 1);
+    dma4(p.lse2 + r, sL[buf]);
+    dma4(p.delta + r, sD[buf]);
+  };
+
+  // First product of the tile: role 0 S = Q K^T, role 1 dP = dO V^T (NM MFMAs,
+  // operands 4 ahead).  Role 0 starts its softmax of half 0 once that half's scores
+  // are done.
+  auto scores = [&](auto cur_c, const uint16_t* X, f32x16* sc, auto valu) {
+    constexpr int cur = decltype(cur_c)::value;
+    (void)cur;
+    constexpr int LA = 4;
+    auto operand = [&](auto jc) -> u32x4 {
+      constexpr int j = decltype(jc)::value, t = j / (NM / 2), s = j % (NM / 2);
+      return lds_row16<NG>(X, 32 * t + l32, 2 * s + g);
+    };
+    sc[0] = zero16();
+    sc[1] = zero16();
+    u32x4 ops[LA];
+    static_for<LA>([&](auto jc) { ops[decltype(jc)::value] = operand(jc); });
+    static_for<NM>([&](auto jc) {
+      constexpr int j = decltype(jc)::value, t = j / (NM / 2), s = j % (NM / 2);
+      const u32x4 op = ops[j % LA];
+      if constexpr (j + LA < NM) ops[j % LA] = operand(std::integral_constant<int, j + LA>());
+      sc[t] = Dt<DT>::mma(op, bf[s], sc[t]);
+      valu(jc);
+      sched_fence();
+    });
+  };
+  // Second product: acc[n] += A[t][c]^T-operand x (transposed read of X); NM MFMAs.
+  auto grads = [&](const uint16_t* X, const u32x4 (*A)[2], auto valu) {
+    constexpr int LA = 4;
+    auto operand = [&](auto jc) -> u32x4 {
+      constexpr int j = decltype(jc)::value, t = j / (NM / 2), k = j % (NM / 2);
+      constexpr int c = k / (NM / 4), n = k % (NM / 4);
+      const int k0 = 32 * t + 16 * c + 4 * g;
+      return lds_tr_operand<NG>(X, k0, k0 + 8, 32 * n + 16 * hi16);
+    };
+    u32x4 ops[LA];
+    static_for<LA>([&](auto jc) { ops[decltype(jc)::value] = operand(jc); });
+    static_for<NM>([&](auto jc) {
+      constexpr int j = decltype(jc)::value, t = j / (NM / 2), k = j % (NM / 2);
+      constexpr int c = k / (NM / 4), n = k % (NM / 4);
+      const u32x4 op = ops[j % LA];
+      if constexpr (j + LA < NM) ops[j % LA] = operand(std::integral_constant<int, j + LA>());
+      acc[n] = Dt<DT>::mma(A[t][c], op, acc[n]);
+      valu(jc);
+      sched_fence();
+    });
+  };
+
+  // Role 0: S, P (masked), publish P.
+  auto role0_first = [&](auto cur_c, auto mask_c, int q0, u32x4 (*pa)[2]) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr bool MASK = decltype(mask_c)::value;
+    f32x16 sp[2];
+    f32x4 L4[2][4];
+    auto softmax_elem = [&](auto tc, auto ic) {
+      constexpr int t = decltype(tc)::value, i = decltype(ic)::value, j4 = i >> 2, e = i & 3;
+      float x = sp[t][i] * p.scale_log2 - L4[t][j4][e];
+      if constexpr (MASK) {
+        const int q = q0 + 32 * t + 8 * j4 + 4 * g + e;
+        const bool masked = kv_lane >= p.Nkv || q >= p.Nq || (CAUSAL && kv_lane > q + p.off);
+        x = masked ? -INFINITY : x;
+      }
+      sp[t][i] = fast_exp2(x);
+    };
+    auto load_l = [&](int t) {
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+        L4[t][j4] = *reinterpret_cast<const f32x4*>(&sL[cur][32 * t + 8 * j4 + 4 * g]);
+    };
+    // half 0's softmax rides on the MFMAs of half 1
+    constexpr int H = NM / 2;
+    scores(cur_c, sQ[cur], sp, [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j == H - 2) load_l(0);
+      if constexpr (j >= H + 1) {
+        constexpr int r = j - (H + 1), steps = H - 1;
+        constexpr int e0 = (16 * r) / steps, e1 = (16 * (r + 1)) / steps;
+        static_for<e1 - e0>([&](auto ic) {
+          softmax_elem(std::integral_constant<int, 0>(), std::integral_constant<int, e0 + decltype(ic)::value>());
+        });
+      }
+    });
+    load_l(1);
+    static_for<16>([&](auto ic) { softmax_elem(std::integral_constant<int, 1>(), ic); });
+    static_for<2>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      static_for<2>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        pa[t][c] = pack_c_slice<DT>(sp[t], c);
+        sP[kg][t][c][lane] = pa[t][c];
+      });
+    });
+  };
+
+  // Role 1 after the barrier: dS = P o (dP - D) from the published P, then dK.
+  auto role1_second = [&](auto cur_c, f32x16* dp) {
+    constexpr int cur = decltype(cur_c)::value;
+    u32x4 pk[2][2], sa[2][2];
+    f32x4 D4[2][4];
+    static_for<2>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      static_for<2>([&](auto cc) { pk[t][decltype(cc)::value] = sP[kg][t][decltype(cc)::value][lane]; });
+#pragma unroll
+      for (int j4 = 0; j4 < 4; ++j4)
+        D4[t][j4] = *reinterpret_cast<const f32x4*>(&sD[cur][32 * t + 8 * j4 + 4 * g]);
+    });
+    auto ds_elem = [&](auto tc, auto ic) {
+      constexpr int t = decltype(tc)::value, i = decltype(ic)::value;
+      constexpr int c = i >> 3, e = i & 7, j4 = i >> 2;
+      const uint32_t wd = pk[t][c][e >> 1];
+      const float pv = (e & 1) ? Dt<DT>::hi(wd) : Dt<DT>::lo(wd);
+      dp[t][i] = pv * (dp[t][i] - D4[t][j4][i & 3]);
+    };
+    static_for<16>([&](auto ic) { ds_elem(std::integral_constant<int, 0>(), ic); });
+    sa[0][0] = pack_c_slice<DT>(dp[0], 0);
+    sa[0][1] = pack_c_slice<DT>(dp[0], 1);
+    // half 1's dS rides on the MFMAs of half 0
+    constexpr int H = NM / 2;
+    grads(sQ[cur], sa, [&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j < H - 2) {
+        constexpr int steps = H - 2;
+        constexpr int e0 = (16 * j) / steps, e1 = (16 * (j + 1)) / steps;
+        static_for<e1 - e0>([&](auto ic) {
+          ds_elem(std::integral_constant<int, 1>(), std::integral_constant<int, e0 + decltype(ic)::value>());
+        });
+      }
+      if constexpr (j == H - 2) sa[1][0] = pack_c_slice<DT>(dp[1], 0);
+      if constexpr (j == H - 1) sa[1][1] = pack_c_slice<DT>(dp[1], 1);
+    });
+  };
+
+  auto body = [&](int it, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    constexpr int last = (cur + NBUF - 1) % NBUF;
+    const bool ahead = it + NBUF - 1 < n_it;
+    if (ahead) fetch(it + NBUF - 1, last);
+    size_t qbase_unused;
+    int q0;
+    tile_of(it, qbase_unused, q0);
+    const bool all_masked = kvw >= p.Nkv || (CAUSAL && kvw > q0 + BM - 1 + p.off);
+    const bool need_mask = kvw + 31 >= p.Nkv || q0 + BM > p.Nq || (CAUSAL && kvw + 31 > q0 + p.off);
+    u32x4 pa[2][2];
+    f32x16 dp[2];
+    if (!all_masked) {
+      if (role == 0) {
+        if (need_mask)
+          role0_first(cur_c, std::true_type(), q0, pa);
+        else
+          role0_first(cur_c, std::false_type(), q0, pa);
+      } else {
+        scores(cur_c, sdO[cur], dp, [&](auto) {});
+      }
+    }
+    lds_barrier();  // P published
+    if (!all_masked) {
+      if (role == 0)
+        grads(sdO[cur], pa, [&](auto) {});
+      else
+        role1_second(cur_c, dp);
+    }
+    if (ahead)
+      wait_vmem_n<OPS * (NBUF - 2)>();
+    else
+      wait_vmem();
+    lds_barrier();
+  };
+
+  static_for<NBUF - 1>([&](auto bc) {
+    constexpr int k = decltype(bc)::value;
+    if (k < n_it) fetch(k, k);
+  });
+  if (n_it >= NBUF - 1)
+    wait_vmem_n<OPS * (NBUF - 2)>();
+  else
+    wait_vmem();
+  lds_barrier();
+  for (int it = 0; it < n_it; it += NBUF) {
+    static_for<NBUF>([&](auto bc) {
+      if (it + decltype(bc)::value < n_it) body(it + decltype(bc)::value, bc);
+    });
+  }
+
+  uint16_t* __restrict__ out = (role == 0 ? p.dv : p.dk) + kbase * D;
+  const float oscale = role == 0 ? 1.f : p.scale;
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kr = kvw + crow_of(i, g);
+      if (kr < p.Nkv) out[(size_t)kr * D + 32 * n + l32] = Dt<DT>::one(acc[n][i] * oscale);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Separate dQ pass.  Workgroup = 4 waves = 128 query rows of one (batch, query
 // head); wave w owns 32 of them and keeps their Q and dO as MFMA operands in
 // registers.  S^T = K Q^T puts the query index in the lane, so dS feeds
@@ -419,8 +701,10 @@ template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int BM = 128, BN = 64, NG = D / 8;
   constexpr int TILE = BN * D;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][TILE];
+  constexpr int NBUF = 3;                   // key/value tiles fetched two ahead
+  constexpr int OPS = 2 * (BN * NG / 256);  // copy instructions per fetch per wave
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5, hi16 = (lane >> 4) & 1;
@@ -559,7 +843,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 
   auto body = [&](int kt, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;
-    if (kt + 1 < nkt) fetch(kt + 1, cur ^ 1);
+    constexpr int last = (cur + NBUF - 1) % NBUF;
+    const bool ahead = kt + NBUF - 1 < nkt;
+    if (ahead) fetch(kt + NBUF - 1, last);
     const int kv0 = kt * BN;
     const bool need_mask = kv0 + BN > p.Nkv || (CAUSAL && kv0 + BN - 1 > qw + p.off);
     const bool all_masked = CAUSAL && kv0 > qw + 31 + p.off;
@@ -569,16 +855,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       else
         compute(cur_c, std::false_type(), kv0);
     }
-    wait_vmem();
-    __syncthreads();
+    if (ahead)
+      wait_vmem_n<OPS * (NBUF - 2)>();
+    else
+      wait_vmem();
+    lds_barrier();
   };
 
-  if (nkt > 0) fetch(0, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int kt = 0; kt < nkt; kt += 2) {
-    body(kt, std::integral_constant<int, 0>());
-    if (kt + 1 < nkt) body(kt + 1, std::integral_constant<int, 1>());
+  static_for<NBUF - 1>([&](auto bc) {
+    constexpr int k = decltype(bc)::value;
+    if (k < nkt) fetch(k, k);
+  });
+  if (nkt >= NBUF - 1)
+    wait_vmem_n<OPS * (NBUF - 2)>();
+  else
+    wait_vmem();
+  lds_barrier();
+  for (int kt = 0; kt < nkt; kt += NBUF) {
+    static_for<NBUF>([&](auto bc) {
+      if (kt + decltype(bc)::value < nkt) body(kt + decltype(bc)::value, bc);
+    });
   }
 
   uint16_t* __restrict__ dQ = p.dq + qbase * D;
@@ -650,7 +946,7 @@ static hipError_t dkdv_t(const BwdArgs& a, bool atomic, hipStream_t s) {
   if (atomic)
     hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL, true>), grid, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL, false>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_dkdv_rs_kernel<DT, D, CAUSAL>), grid, dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

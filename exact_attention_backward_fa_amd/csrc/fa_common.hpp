@@ -184,14 +184,37 @@ __device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
 }
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave still
+// outstanding.  Vector memory loads complete in issue order, so this waits for all
+// but the N most recent.
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier for LDS tiles.  __syncthreads() carries a release fence that
+// the compiler implements with vmcnt(0), which would also wait for direct copies
+// still in flight for later tiles.  Here each wave first waits for exactly the
+// copies it needs (wait_vmem / wait_vmem_n), then for its own LDS stores; the asm
+// clobbers keep the compiler from moving memory accesses across, and the
+// LDS-only acquire fence orders later LDS reads after the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  asm volatile("" ::: "memory");
+}
 
 // Fill a swizzled ROWS x (NG*8) tile from rows row0.. of a row-major matrix with
 // NG*8 columns; rows at or past n_rows read row n_rows-1 instead (callers mask
-// them).  256 threads; each wave issues ROWS*NG/256 copies of 1 KB.
-template <int NG, int ROWS>
+// them).  NT threads; each wave issues ROWS*NG/NT copies of 1 KB.
+template <int NG, int ROWS, int NT = 256>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ g, int row0, int n_rows,
                                          uint16_t* lds, int w, int lane) {
-  constexpr int PER_WAVE = ROWS * NG / 256;
+  constexpr int PER_WAVE = ROWS * NG / NT;
+  static_assert(PER_WAVE >= 1 && PER_WAVE * NT == ROWS * NG, "tile must split evenly over waves");
 #pragma unroll
   for (int c = 0; c < PER_WAVE; ++c) {
     const int blk = PER_WAVE * w + c;

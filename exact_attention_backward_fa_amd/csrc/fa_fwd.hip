@@ -38,9 +38,11 @@ struct FwdParams {
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   constexpr int BM = 128, BN = 64, NG = D / 8;
-  constexpr int TILE = BN * D;           // elements of one K or V tile
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][TILE];
+  constexpr int TILE = BN * D;              // elements of one K or V tile
+  constexpr int NBUF = 3;                   // key/value tiles fetched two ahead
+  constexpr int OPS = 2 * (BN * NG / 256);  // copy instructions per fetch per wave
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NBUF][TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NBUF][TILE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -150,7 +152,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   const int qw = q0 + 32 * w;  // first query row of this wave
   auto body = [&](int kt, auto cur_c) {
     constexpr int cur = decltype(cur_c)::value;
-    if (kt + 1 < nkt) fetch(kt + 1, cur ^ 1);
+    constexpr int last = (cur + NBUF - 1) % NBUF;
+    const bool ahead = kt + NBUF - 1 < nkt;
+    if (ahead) fetch(kt + NBUF - 1, last);
     const int kv0 = kt * BN;
     const bool need_mask = kv0 + BN > p.Nkv || (CAUSAL && kv0 + BN - 1 > qw + p.off);
     const bool all_masked = CAUSAL && kv0 > qw + 31 + p.off;
@@ -160,16 +164,26 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       else
         compute(cur_c, std::false_type(), kv0);
     }
-    wait_vmem();
-    __syncthreads();
+    if (ahead)
+      wait_vmem_n<OPS * (NBUF - 2)>();
+    else
+      wait_vmem();
+    lds_barrier();
   };
 
-  if (nkt > 0) fetch(0, 0);
-  wait_vmem();
-  __syncthreads();
-  for (int kt = 0; kt < nkt; kt += 2) {
-    body(kt, std::integral_constant<int, 0>());
-    if (kt + 1 < nkt) body(kt + 1, std::integral_constant<int, 1>());
+  static_for<NBUF - 1>([&](auto bc) {
+    constexpr int k = decltype(bc)::value;
+    if (k < nkt) fetch(k, k);
+  });
+  if (nkt >= NBUF - 1)
+    wait_vmem_n<OPS * (NBUF - 2)>();
+  else
+    wait_vmem();
+  lds_barrier();
+  for (int kt = 0; kt < nkt; kt += NBUF) {
+    static_for<NBUF>([&](auto bc) {
+      if (kt + decltype(bc)::value < nkt) body(kt + decltype(bc)::value, bc);
+    });
   }
 
   if (qrow < p.Nq) {

@@ -232,11 +232,17 @@ def test_separate_path_is_bitwise_repeatable(device):
     a = fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], case.scale, True, dq_mode="separate")
     b = fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], case.scale, True, dq_mode="separate")
     c = fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], case.scale, True, dq_mode="atomic")
+    d = fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], case.scale, True, dq_mode="atomic")
     for t1, t2 in zip(a, b):
         assert torch.equal(t1.view(torch.int16), t2.view(torch.int16))
-    # dK and dV never use atomics: identical in both modes
-    assert torch.equal(a[1].view(torch.int16), c[1].view(torch.int16))
-    assert torch.equal(a[2].view(torch.int16), c[2].view(torch.int16))
+    # dK and dV never use atomics, so they repeat bitwise on the atomic path too
+    for t1, t2 in zip(c[1:], d[1:]):
+        assert torch.equal(t1.view(torch.int16), t2.view(torch.int16))
+    # the two paths compute dK/dV with different kernels (different summation
+    # order): they agree to rounding
+    for t1, t2 in zip(a, c):
+        err = float((t1.float() - t2.float()).abs().max() / t2.float().abs().max())
+        assert err <= 1e-2, err
 
 
 def test_outputs_need_no_initialisation(device):
