@@ -153,8 +153,8 @@ def main() -> int:
     # was taken from the current kernel sources (None otherwise).
     from exact_attention_backward_fa_amd import profiling
     dt_id = 1 if case.dtype == "bf16" else 0
-    kname = (f"bwd_dkdv_kernel<{dt_id}, {case.d}, {'true' if case.causal else 'false'}, "
-             f"{'true' if resolved == 'atomic' else 'false'}>")
+    kname = (f"{'bwd_dkdv_atomic_kernel' if resolved == 'atomic' else 'bwd_dkdv_kernel'}"
+             f"<{dt_id}, {case.d}, {'true' if case.causal else 'false'}>")
     traffic = profiling.read_traffic(kname)
     log(f"[bench] fwd {fwd_ms:.3f} ms ({fwd_flops / fwd_ms / 1e9:.1f} TFLOP/s)  bwd {bwd_ms:.3f} ms "
         f"({value:.1f} TFLOP/s, {100 * value / PEAK_BF16_TFLOPS:.1f}% of peak)  dkdv kernel "
@@ -182,7 +182,7 @@ def main() -> int:
         "fwd_ms": round(fwd_ms, 4),
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
         "roofline": {
-            "kernel": f"bwd_dkdv_kernel ({'with atomic dQ' if resolved == 'atomic' else 'dK/dV only'})",
+            "kernel": kname,
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,

@@ -22,6 +22,9 @@ LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
+# fa_bwd_inst.hip is compiled once per backward template instance:
+# (dtype 0 fp16 / 1 bf16, head dim, causal).
+INSTANCES = [(dt, d, c) for dt in (0, 1) for d in (64, 128) for c in (0, 1)]
 
 ARCH = "gfx950"
 HIP_FLAGS = [
@@ -59,19 +62,36 @@ def build(verbose: bool = False) -> str:
     cc = hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     t0 = time.time()
-    procs = []
+    jobs = []
     objs = []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmd = [cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
-                                            text=True)))
+        jobs.append((src, [cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
+    for dt, d, c in INSTANCES:
+        obj = os.path.join(BUILD_DIR, f"fa_bwd_inst_{dt}_{d}_{c}.o")
+        objs.append(obj)
+        jobs.append((f"fa_bwd_inst.hip [{dt},{d},{c}]",
+                     [cc, *HIP_FLAGS, f"-DFA_DT={dt}", f"-DFA_D={d}", f"-DFA_CAUSAL={c}", "-c",
+                      os.path.join(CSRC, "fa_bwd_inst.hip"), "-o", obj]))
+    # the heaviest compilations first, at most one per CPU
+    jobs.sort(key=lambda j: "inst" not in j[0])
+    width = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    procs = []
+    pending = list(jobs)
     failed = []
-    for src, p in procs:
+    results = []
+    while pending or procs:
+        while pending and len(procs) < width:
+            src, cmd = pending.pop(0)
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                                text=True)))
+        src, p = procs.pop(0)
         out, _ = p.communicate()
+        results.append((src, p, out))
+    for src, p, out in results:
         msg = _filter_noise(out or "")
         if p.returncode != 0:
             failed.append(src)

@@ -1,0 +1,638 @@
+// Backward kernels of exact softmax attention.
+//
+//   bwd_pre   D_i = sum_d dO_id O_id per query row (rustytorch
+//             "flash_attention_backward.cu" computes this row dot product inside
+//             its tiled kernel; the Triton issue "Extra transposes cause 8x speedup
+//             for sequence-parallel Flash Attention backward" loads it precomputed),
+//             LSE rescaled to the log2 domain, and, for the atomic dQ path, the
+//             float32 dQ buffer cleared.
+//   bwd_dkdv  key/value-block-parallel dK and dV (the Triton issue's _bwd_kernel
+//             structure: one program per key block, K and V resident, a loop over
+//             query blocks).
+//   bwd_dq    query-block-parallel dQ pass (the decomposition of the rustytorch
+//             kernel's grid), recomputing S, P, dP and dS; writes dQ once.
+//   dq_convert  float32 dQ buffer -> dtype (atomic path).
+//
+// Per (query tile i, key tile j) the math is, with s the softmax scale:
+//   S = s Q_i K_j^T,  P = exp(S - LSE_i),  dV_j += P^T dO_i,  dP = dO_i V_j^T,
+//   dS = P o (dP - D_i),  dK_j += s dS^T Q_i,  dQ_i += s dS K_j.
+// Exponentials run in the log2 domain: P = exp2(S * s * log2 e - LSE_i * log2 e).
+//
+// Both main kernels give each wave 64 resident rows (keys for dK/dV, queries for
+// dQ) so that every operand read from LDS feeds several MFMAs: the score products
+// (S, dP or their transposes) are 16x16x32 MFMAs whose LDS operand serves 4 tiles
+// of 16 resident rows, and the gradient products are 32x32x16 MFMAs whose LDS
+// operand serves 2 tiles of 32.  The streamed tile is processed in sub-blocks of
+// 16 rows, software-pipelined so that the softmax / dS arithmetic of one sub-block
+// runs while the matrix pipe works on the products of the next.
+#pragma once
+
+#include "fa_bwd_common.hpp"
+
+#include <type_traits>
+
+namespace fa {
+
+// One pipeline step: up to four stages of MFMAs issued in order; stage k has Nk
+// operands read from LDS, each feeding Gk consecutive MFMAs.
+template <int N0, int G0, int N1, int G1, int N2, int G2, int N3, int G3>
+struct StepPlan {
+  static constexpr int B1 = N0 * G0, B2 = B1 + N1 * G1, B3 = B2 + N2 * G2, NM = B3 + N3 * G3;
+  static constexpr int O1 = N0, O2 = O1 + N1, O3 = O2 + N2, NOP = O3 + N3;
+  static constexpr int stage(int m) { return m < B1 ? 0 : m < B2 ? 1 : m < B3 ? 2 : 3; }
+  static constexpr int start(int k) { return k == 0 ? 0 : k == 1 ? B1 : k == 2 ? B2 : B3; }
+  static constexpr int gsz(int k) { return k == 0 ? G0 : k == 1 ? G1 : k == 2 ? G2 : G3; }
+  static constexpr int obase(int k) { return k == 0 ? 0 : k == 1 ? O1 : k == 2 ? O2 : O3; }
+  static constexpr int local(int m) { return m - start(stage(m)); }
+  static constexpr int op_of(int m) { return obase(stage(m)) + local(m) / gsz(stage(m)); }
+  static constexpr bool first(int m) { return local(m) % gsz(stage(m)) == 0; }
+  static constexpr int op_stage(int o) { return o < O1 ? 0 : o < O2 ? 1 : o < O3 ? 2 : 3; }
+  static constexpr int op_local(int o) { return o - obase(op_stage(o)); }
+};
+
+// floor(a / b) for b > 0 and any sign of a.
+__device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }
+
+// Slot (MFMA index) after which VALU item e of E runs when the items are spread
+// evenly over the MFMA slots [a, b).
+__host__ __device__ constexpr int spread_slot(int e, int E, int a, int b) {
+  return a + (e * (b - a)) / E;
+}
+
+// Issue the MFMAs of one step in order.  operand(o) reads operand o from LDS; it
+// is issued LA operands ahead of its first use.  mfma(m, op) issues MFMA m;
+// valu(m) emits the VALU work placed after MFMA m.  A scheduling fence after each
+// slot keeps this order.
+template <class Plan, int LA, class FOp, class FMma, class FValu>
+__device__ __forceinline__ void run_step(FOp&& operand, FMma&& mfma, FValu&& valu) {
+  constexpr int PRE = LA < Plan::NOP ? LA : Plan::NOP;
+  u32x4 ops[LA + 1];
+  static_for<PRE>([&](auto oc) { ops[decltype(oc)::value] = operand(oc); });
+  static_for<Plan::NM>([&](auto mc) {
+    constexpr int m = decltype(mc)::value;
+    constexpr int o = Plan::op_of(m);
+    if constexpr (Plan::first(m) && o + LA < Plan::NOP)
+      ops[(o + LA) % (LA + 1)] = operand(std::integral_constant<int, o + LA>());
+    mfma(mc, ops[o % (LA + 1)]);
+    valu(mc);
+    sched_fence();
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Row preprocess.  D/8 lanes share a row; each lane reads 16 bytes of O and dO.
+template <int DT, int D, bool ZERO_DQ>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+  constexpr int LPR = D / 8;
+  constexpr int RPB = 256 / LPR;
+  const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float s = 0.f;
+  if (row < p.rows) {
+    const u32x4 a = ld16(p.o + row * D + part * 8);
+    const u32x4 c = ld16(p.dout + row * D + part * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      s += Dt<DT>::lo(a[j]) * Dt<DT>::lo(c[j]) + Dt<DT>::hi(a[j]) * Dt<DT>::hi(c[j]);
+    if (ZERO_DQ) {
+      float* z = p.dq_acc + row * D + part * 8;
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(z) = zero;
+      *reinterpret_cast<f32x4*>(z + 4) = zero;
+    }
+  }
+#pragma unroll
+  for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  if (row < p.rows && part == 0) {
+    p.delta[row] = s;
+    const float L = p.lse[row];
+    p.lse2[row] = (L == -INFINITY) ? INFINITY : L * kLog2e;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK/dV kernel.  Workgroup = 4 waves = 256 key rows of one (batch, kv head); wave w
+// owns keys kvw = kv0 + 64w .. +63 and keeps
+//   K and V as the B operands of S = Q K^T and dP = dO V^T (16x16x32; key tile kt
+//   of 16 keys, contraction step s of 32 head dims), and
+//   dK and dV as float32 32x32 accumulators (key half h, head-dim tile n).
+// The loop runs over the G query heads of the group and their 64-row query tiles
+// from the first one that can see the key block (causal) to the end.  Query tiles
+// (Q, dO, LSE, D) are triple-buffered in LDS and copied straight from global
+// memory two iterations ahead.  A tile is processed in four 16-row sub-blocks; per
+// sub-block a wave computes
+//   S (4 key tiles), P = exp2(S s log2e - LSE log2e), dP, dS = P o (dP - D),
+//   dV += P^T dO and dK += dS^T Q (32x32x16, contraction over the 16 query rows).
+// P and dS come out of the 16x16 accumulators with the key in the lane; one
+// v_permlane16_swap per register pair turns two 16-key tiles into the 32-key A
+// operand of the 32x32x16 product, whose B operand (dO or Q with the query along
+// the slots) is a transposed LDS read.
+//
+// Sub-blocks are software-pipelined: step st issues the MFMA stream
+//   S_st | dK_{st-1} | dP_st | dV_st
+// with P_st computed under dK_{st-1} and dP_st, and dS_st under dV_st.  A final
+// step issues dK of the last sub-block.  Tiles that cross the causal
+// boundary or a ragged end of this wave's block take a masked variant of the
+// softmax.
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
+  constexpr int KW = 64, BN = 4 * KW, BM = 64, NSB = BM / 16;
+  constexpr int NG = D / 8, NK = D / 32;
+  constexpr int TILE = BM * D;
+  constexpr int NBUF = 3;
+  constexpr int OPS = 2 * (BM * NG / 256) + 2;  // copy instructions per fetch per wave
+  constexpr int LA = 2;                          // operand lookahead
+  // Q and dO of a buffer are adjacent (as are LSE and D), so both tiles are read
+  // through the same per-lane address registers with different immediate offsets.
+  __shared__ __attribute__((aligned(16))) uint16_t sQdO[NBUF][2][TILE];
+  __shared__ __attribute__((aligned(16))) float sLD[NBUF][2][BM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int l16 = lane & 15, j4 = lane >> 4;  // 16x16 tiles: column, row group
+  const int l32 = lane & 31, g = lane >> 5, hi16 = j4 & 1;
+  int rank, head;
+  map_block(blockIdx.x, p.B * p.Hkv, rank, head);
+  const int b = head / p.Hkv, hk = head % p.Hkv;
+  const int kv0 = rank * BN;  // rank 0 = first key block = most query rows under the mask
+  const int kvw = kv0 + KW * w;
+  const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
+
+  u32x4 kb[4][NK], vb[4][NK];
+  {
+    const uint16_t* __restrict__ K = p.k + kbase * D;
+    const uint16_t* __restrict__ V = p.v + kbase * D;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int key = kvw + 16 * kt + l16;
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+        kb[kt][s] = key < p.Nkv ? ld16(K + (size_t)key * D + 32 * s + 8 * j4) : zero_u4();
+        vb[kt][s] = key < p.Nkv ? ld16(V + (size_t)key * D + 32 * s + 8 * j4) : zero_u4();
+      }
+    }
+  }
+  f32x16 dk[2][NK], dv[2][NK];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+      dk[h][n] = zero16();
+      dv[h][n] = zero16();
+    }
+  }
+
+  const int q_begin = CAUSAL ? max(0, kv0 - p.off) : 0;
+  const int nqt = (p.Nq + BM - 1) / BM;
+  const int qt_begin = q_begin < p.Nq ? q_begin / BM : nqt;
+  const int per_head = nqt - qt_begin;
+  const int n_it = p.G * per_head;
+
+  // Iteration it covers query tile qt_begin + it / G of query head it % G of the
+  // group (tiles outer, heads inner, so the tiles that need the causal mask come
+  // first).  Query tile (fqt, fhh) goes straight into LDS buffer `buf`; rows past
+  // N_q repeat row N_q-1 and are masked in the math.  Every wave copies LSE and D
+  // (identical bytes to the same place), so all waves issue OPS copies per fetch
+  // and share one vmcnt bound.
+  int fqt = qt_begin, fhh = 0;  // next tile to fetch
+  auto fetch = [&](int buf) {
+    const size_t qbase = ((size_t)b * p.Hq + (size_t)hk * p.G + fhh) * (size_t)p.Nq;
+    const int q0 = fqt * BM;
+    dma_tile<NG, BM>(p.q + qbase * D, q0, p.Nq, sQdO[buf][0], w, lane);
+    dma_tile<NG, BM>(p.dout + qbase * D, q0, p.Nq, sQdO[buf][1], w, lane);
+    const size_t r = qbase + min(q0 + lane, p.Nq - 1);
+    dma4(p.lse2 + r, sLD[buf][0]);
+    dma4(p.delta + r, sLD[buf][1]);
+    if (++fhh == p.G) {
+      fhh = 0;
+      ++fqt;
+    }
+  };
+
+  auto compute = [&](int cur, auto mask_c, int q0) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    const uint16_t* Qt = sQdO[cur][0];
+    const uint16_t* dOt = Qt + TILE;
+    const float* Lt = sLD[cur][0];
+    const float* Dtl = Lt + BM;
+    f32x4 sc[4];         // S, then P, of the current sub-block, per key tile
+    f32x4 dp[4];         // dP, then dS
+    u32x4 pa[2], sa[2];  // P^T and dS^T A operands, per key half
+    f32x4 lq, dn;        // LSE*log2e and D of the current sub-block's rows
+    const int keyl = kvw + l16;    // key of this lane's column in key tile 0
+    const int qrow = q0 + 4 * j4;  // query row of element 0 in sub-block 0
+
+    // P_st item e of 18: 16 elements, then after each key half its operand
+    auto p_item = [&](auto ec, auto st_c) {
+      constexpr int e = decltype(ec)::value, st = decltype(st_c)::value;
+      if constexpr (e == 8) {
+        pa[0] = c16_pair_to_a32(pack_c4<DT>(sc[0]), pack_c4<DT>(sc[1]));
+      } else if constexpr (e == 17) {
+        pa[1] = c16_pair_to_a32(pack_c4<DT>(sc[2]), pack_c4<DT>(sc[3]));
+      } else {
+        constexpr int x = e < 8 ? e : e - 1, kt = x / 4, i = x % 4;
+        float v = sc[kt][i] * p.scale_log2 - lq[i];
+        if constexpr (MASK) {
+          const int key = keyl + 16 * kt, q = qrow + 16 * st + i;
+          if (key >= p.Nkv || q >= p.Nq || (CAUSAL && key > q + p.off)) v = -INFINITY;
+        }
+        sc[kt][i] = fast_exp2(v);
+      }
+    };
+    // dS_st item e of 18, same order
+    auto ds_item = [&](auto ec) {
+      constexpr int e = decltype(ec)::value;
+      if constexpr (e == 8) {
+        sa[0] = c16_pair_to_a32(pack_c4<DT>(dp[0]), pack_c4<DT>(dp[1]));
+      } else if constexpr (e == 17) {
+        sa[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
+      } else {
+        constexpr int x = e < 8 ? e : e - 1, kt = x / 4, i = x % 4;
+        dp[kt][i] = sc[kt][i] * (dp[kt][i] - dn[i]);
+      }
+    };
+
+    static_for<NSB + 1>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      constexpr bool HS = st < NSB;  // S_st, dP_st, dV_st (and P_st, dS_st) in this step
+      constexpr bool HK = st > 0;    // dK_{st-1} in this step
+      using Plan = StepPlan<HS ? NK : 0, 4, HK ? NK : 0, 2, HS ? NK : 0, 4, HS ? NK : 0, 2>;
+      if constexpr (HS) {
+        lq = *reinterpret_cast<const f32x4*>(&Lt[16 * st + 4 * j4]);
+        dn = *reinterpret_cast<const f32x4*>(&Dtl[16 * st + 4 * j4]);
+      }
+      auto operand = [&](auto oc) -> u32x4 {
+        constexpr int o = decltype(oc)::value;
+        constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
+        if constexpr (k == 0) {
+          return lds_row16<NG>(Qt, 16 * st + l16, 4 * n + j4);
+        } else if constexpr (k == 1) {
+          const int k0 = 16 * (st - 1) + 8 * g;
+          return lds_tr_operand<NG>(Qt, k0, k0 + 4, 32 * n + 16 * hi16);
+        } else if constexpr (k == 2) {
+          return lds_row16<NG>(dOt, 16 * st + l16, 4 * n + j4);
+        } else {
+          const int k0 = 16 * st + 8 * g;
+          return lds_tr_operand<NG>(dOt, k0, k0 + 4, 32 * n + 16 * hi16);
+        }
+      };
+      auto mfma = [&](auto mc, const u32x4& op) {
+        constexpr int m = decltype(mc)::value;
+        constexpr int k = Plan::stage(m), loc = Plan::local(m);
+        if constexpr (k == 0) {
+          constexpr int s = loc / 4, kt = loc % 4;
+          if constexpr (s == 0)
+            sc[kt] = Mx<DT>::first16(op, kb[kt][s]);
+          else
+            Mx<DT>::acc16(sc[kt], op, kb[kt][s]);
+        } else if constexpr (k == 1) {
+          constexpr int n = loc / 2, h = loc % 2;
+          Mx<DT>::acc32(dk[h][n], sa[h], op);
+        } else if constexpr (k == 2) {
+          constexpr int s = loc / 4, kt = loc % 4;
+          if constexpr (s == 0)
+            dp[kt] = Mx<DT>::first16(op, vb[kt][s]);
+          else
+            Mx<DT>::acc16(dp[kt], op, vb[kt][s]);
+        } else {
+          constexpr int n = loc / 2, h = loc % 2;
+          Mx<DT>::acc32(dv[h][n], pa[h], op);
+        }
+      };
+      auto valu = [&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (HS) {
+          static_for<18>([&](auto ec) {
+            if constexpr (spread_slot(decltype(ec)::value, 18, Plan::B1, Plan::B3) == m)
+              p_item(ec, stc);
+            if constexpr (spread_slot(decltype(ec)::value, 18, Plan::B3, Plan::NM) == m)
+              ds_item(ec);
+          });
+        }
+      };
+      run_step<Plan, LA>(operand, mfma, valu);
+    });
+  };
+
+  // This wave's split of the query tiles (each phase runs one variant of the
+  // math, so the loops carry the accumulators without branches around MFMAs):
+  //   [qt_begin, qa)  no query sees the wave's keys         skipped
+  //   [qa, qb)        causal boundary or ragged key end     masked
+  //   [qb, qe)        every pair visible                    unmasked
+  //   [qe, nqt)       ragged query end                      masked
+  int qa = qt_begin, qb = qt_begin, qe = nqt;
+  if (kvw >= p.Nkv) {
+    qa = qb = qe = nqt;
+  } else {
+    if (CAUSAL) {
+      qa = max(qt_begin, floor_div(kvw - p.off - (BM - 1) + BM - 1, BM));  // q0 + BM - 1 >= kvw - off
+      qb = max(qa, floor_div(kvw + KW - 1 - p.off + BM - 1, BM));        // q0 >= kvw + KW - 1 - off
+    }
+    if (kvw + KW > p.Nkv) qb = nqt;  // ragged key end: every visible tile is masked
+    qa = min(qa, nqt);
+    qb = min(qb, nqt);
+    qe = max(qb, min(nqt, p.Nq / BM));
+  }
+  static_for<NBUF - 1>([&](auto bc) {
+    if (decltype(bc)::value < n_it) fetch(decltype(bc)::value);
+  });
+  if (n_it >= NBUF - 1)
+    wait_vmem_n<OPS * (NBUF - 2)>();
+  else
+    wait_vmem();
+  lds_barrier();
+  // iteration it works on buffer it % NBUF while tile it+NBUF-1 is copied into the
+  // buffer of iteration it-1
+  int it = 0, cur = 0;
+  auto phase = [&](int qt_end, auto variant) {
+    constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
+    for (const int end = (qt_end - qt_begin) * p.G; it < end; ++it) {
+      const bool ahead = it + NBUF - 1 < n_it;
+      if (ahead) fetch(cur == 0 ? NBUF - 1 : cur - 1);
+      const int q0 = (qt_begin + it / p.G) * BM;
+      if constexpr (VAR == 1) compute(cur, std::true_type(), q0);
+      if constexpr (VAR == 2) compute(cur, std::false_type(), q0);
+      // tile it+1 must have landed; the fetch of tile it+NBUF-1 may stay in flight
+      if (ahead)
+        wait_vmem_n<OPS * (NBUF - 2)>();
+      else
+        wait_vmem();
+      lds_barrier();
+      cur = cur == NBUF - 1 ? 0 : cur + 1;
+    }
+  };
+  phase(qa, std::integral_constant<int, 0>());
+  phase(qb, std::integral_constant<int, 1>());
+  phase(qe, std::integral_constant<int, 2>());
+  phase(nqt, std::integral_constant<int, 1>());
+
+  wait_mfma();
+  uint16_t* __restrict__ dK = p.dk + kbase * D;
+  uint16_t* __restrict__ dV = p.dv + kbase * D;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kr = kvw + 32 * h + crow_of(i, g);
+        if (kr < p.Nkv) {
+          dK[(size_t)kr * D + 32 * n + l32] = Dt<DT>::one(dk[h][n][i] * p.scale);
+          dV[(size_t)kr * D + 32 * n + l32] = Dt<DT>::one(dv[h][n][i]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Separate dQ pass.  Workgroup = 4 waves = 256 query rows of one (batch, query
+// head); wave w owns queries qw = q0 + 64w .. +63 and keeps
+//   Q and dO as the B operands of S^T = K Q^T and dP^T = V dO^T (16x16x32; query
+//   tile t of 16 queries, contraction step s of 32 head dims), their LSE and D,
+//   and dQ as float32 32x32 accumulators (query half h, head-dim tile n).
+// Key/value tiles of 64 rows are triple-buffered in LDS and copied straight from
+// global memory.  A tile is processed in four 16-key sub-blocks; per sub-block a
+// wave computes S^T and dP^T (4 query tiles), P^T and dS^T, and
+// dQ += dS K (32x32x16; dS from two 16x16 accumulators through v_permlane16_swap,
+// K with the key along the slots from a transposed LDS read).
+//
+// Step st issues the MFMA stream  S^T_st | dQ_{st-1} | dP^T_st  with dS_{st-1}
+// computed under S^T_st and P_st under dQ_{st-1} and dP^T_st.
+template <int DT, int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
+  constexpr int QW = 64, BM = 4 * QW, BN = 64, NSB = BN / 16;
+  constexpr int NG = D / 8, NK = D / 32;
+  constexpr int TILE = BN * D;
+  constexpr int NBUF = 3;                   // key/value tiles fetched two ahead
+  constexpr int OPS = 2 * (BN * NG / 256);  // copy instructions per fetch per wave
+  constexpr int LA = 2;
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[NBUF][2][TILE];  // K, V adjacent
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+  const int l16 = lane & 15, j4 = lane >> 4;
+  const int l32 = lane & 31, g = lane >> 5, hi16 = j4 & 1;
+  const int nqt = (p.Nq + BM - 1) / BM;
+  int rank, head;
+  map_block(blockIdx.x, p.B * p.Hq, rank, head);
+  const int qt = CAUSAL ? nqt - 1 - rank : rank;
+  const int b = head / p.Hq, h = head % p.Hq;
+  const int hk = h / p.G;
+  const int q0 = qt * BM;
+  const int qw = q0 + QW * w;  // first query row of this wave
+  const size_t qbase = ((size_t)b * p.Hq + h) * (size_t)p.Nq;
+  const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
+  const uint16_t* __restrict__ K = p.k + kbase * D;
+  const uint16_t* __restrict__ V = p.v + kbase * D;
+
+  u32x4 qb[4][NK], db[4][NK];
+  float lq[4], dl[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int q = qw + 16 * t + l16;
+    const bool ok = q < p.Nq;
+#pragma unroll
+    for (int s = 0; s < NK; ++s) {
+      qb[t][s] = ok ? ld16(p.q + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
+      db[t][s] = ok ? ld16(p.dout + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
+    }
+    lq[t] = ok ? p.lse2[qbase + q] : INFINITY;
+    dl[t] = ok ? p.delta[qbase + q] : 0.f;
+  }
+  f32x16 acc[2][NK];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int n = 0; n < NK; ++n) acc[hh][n] = zero16();
+  }
+
+  int kv_end = p.Nkv;
+  if (CAUSAL) {
+    const int q_last = min(q0 + BM, p.Nq) - 1;
+    kv_end = min(p.Nkv, q_last + p.off + 1);
+  }
+  const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+
+  auto fetch = [&](int kt, int buf) {
+    dma_tile<NG, BN>(K, kt * BN, p.Nkv, sKV[buf][0], w, lane);
+    dma_tile<NG, BN>(V, kt * BN, p.Nkv, sKV[buf][1], w, lane);
+  };
+
+  auto compute = [&](int cur, auto mask_c, int kv0) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    const uint16_t* Kt = sKV[cur][0];
+    const uint16_t* Vt = Kt + TILE;
+    f32x4 sc[2][4];  // S^T, then P^T, of sub-block st in sc[st % 2], per query tile
+    f32x4 dp[4];     // dP^T, then dS^T, of the sub-block being finished
+    u32x4 da[2];     // dS A operands, per query half
+    const int krow = kv0 + 4 * j4;  // key of element 0 in sub-block 0
+    const int qcol = qw + l16;      // query of this lane's column in query tile 0
+
+    auto ds_item = [&](auto ec, auto cp_c) {
+      constexpr int e = decltype(ec)::value, cp = decltype(cp_c)::value;
+      if constexpr (e == 8) {
+        da[0] = c16_pair_to_a32(pack_c4<DT>(dp[0]), pack_c4<DT>(dp[1]));
+      } else if constexpr (e == 17) {
+        da[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
+      } else {
+        constexpr int x = e < 8 ? e : e - 1, t = x / 4, i = x % 4;
+        dp[t][i] = sc[cp][t][i] * (dp[t][i] - dl[t]);
+      }
+    };
+    auto p_item = [&](auto ec, auto st_c) {
+      constexpr int e = decltype(ec)::value, st = decltype(st_c)::value, cs = st & 1;
+      constexpr int t = e / 4, i = e % 4;
+      float v = sc[cs][t][i] * p.scale_log2 - lq[t];
+      if constexpr (MASK) {
+        const int key = krow + 16 * st + i, q = qcol + 16 * t;
+        if (key >= p.Nkv || (CAUSAL && key > q + p.off)) v = -INFINITY;
+      }
+      sc[cs][t][i] = fast_exp2(v);
+    };
+
+    static_for<NSB + 1>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      constexpr bool HS = st < NSB, HK = st > 0;
+      constexpr int cs = st & 1, cp = cs ^ 1;
+      using Plan = StepPlan<HS ? NK : 0, 4, HK ? NK : 0, 2, HS ? NK : 0, 4, 0, 1>;
+      if constexpr (!HS) {
+        static_for<18>([&](auto ec) { ds_item(ec, std::integral_constant<int, cp>()); });
+      }
+      auto operand = [&](auto oc) -> u32x4 {
+        constexpr int o = decltype(oc)::value;
+        constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
+        if constexpr (k == 0) {
+          return lds_row16<NG>(Kt, 16 * st + l16, 4 * n + j4);
+        } else if constexpr (k == 1) {
+          const int k0 = 16 * (st - 1) + 8 * g;
+          return lds_tr_operand<NG>(Kt, k0, k0 + 4, 32 * n + 16 * hi16);
+        } else {
+          return lds_row16<NG>(Vt, 16 * st + l16, 4 * n + j4);
+        }
+      };
+      auto mfma = [&](auto mc, const u32x4& op) {
+        constexpr int m = decltype(mc)::value;
+        constexpr int k = Plan::stage(m), loc = Plan::local(m);
+        if constexpr (k == 0) {
+          constexpr int s = loc / 4, t = loc % 4;
+          if constexpr (s == 0)
+            sc[cs][t] = Mx<DT>::first16(op, qb[t][s]);
+          else
+            Mx<DT>::acc16(sc[cs][t], op, qb[t][s]);
+        } else if constexpr (k == 1) {
+          constexpr int n = loc / 2, hh = loc % 2;
+          Mx<DT>::acc32(acc[hh][n], da[hh], op);
+        } else {
+          constexpr int s = loc / 4, t = loc % 4;
+          if constexpr (s == 0)
+            dp[t] = Mx<DT>::first16(op, db[t][s]);
+          else
+            Mx<DT>::acc16(dp[t], op, db[t][s]);
+        }
+      };
+      auto valu = [&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if constexpr (HS && HK) {
+          static_for<18>([&](auto ec) {
+            if constexpr (spread_slot(decltype(ec)::value, 18, 0, Plan::B1) == m)
+              ds_item(ec, std::integral_constant<int, cp>());
+          });
+        }
+        if constexpr (HS) {
+          static_for<16>([&](auto ec) {
+            if constexpr (spread_slot(decltype(ec)::value, 16, Plan::B1, Plan::NM) == m)
+              p_item(ec, stc);
+          });
+        }
+      };
+      run_step<Plan, LA>(operand, mfma, valu);
+    });
+  };
+
+  // This wave's split of the key tiles (one variant of the math per loop):
+  //   [0, n_un)      every pair visible          unmasked
+  //   [n_un, n_vis)  causal boundary / ragged    masked
+  //   [n_vis, nkt)   no key visible to the wave  skipped
+  int n_vis = nkt;
+  if (qw >= p.Nq) n_vis = 0;
+  else if (CAUSAL) n_vis = min(nkt, max(0, floor_div(qw + QW - 1 + p.off, BN) + 1));
+  int n_un = min(n_vis, p.Nkv / BN);
+  if (CAUSAL) n_un = min(n_un, max(0, floor_div(qw + p.off - (BN - 1), BN) + 1));
+
+  static_for<NBUF - 1>([&](auto bc) {
+    constexpr int k = decltype(bc)::value;
+    if (k < nkt) fetch(k, k);
+  });
+  if (nkt >= NBUF - 1)
+    wait_vmem_n<OPS * (NBUF - 2)>();
+  else
+    wait_vmem();
+  lds_barrier();
+  int kt = 0, cur = 0;
+  auto phase = [&](int end, auto variant) {
+    constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
+    for (; kt < end; ++kt) {
+      const bool ahead = kt + NBUF - 1 < nkt;
+      if (ahead) fetch(kt + NBUF - 1, cur == 0 ? NBUF - 1 : cur - 1);
+      if constexpr (VAR == 1) compute(cur, std::true_type(), kt * BN);
+      if constexpr (VAR == 2) compute(cur, std::false_type(), kt * BN);
+      if (ahead)
+        wait_vmem_n<OPS * (NBUF - 2)>();
+      else
+        wait_vmem();
+      lds_barrier();
+      cur = cur == NBUF - 1 ? 0 : cur + 1;
+    }
+  };
+  phase(n_un, std::integral_constant<int, 2>());
+  phase(n_vis, std::integral_constant<int, 1>());
+  phase(nkt, std::integral_constant<int, 0>());
+
+  wait_mfma();
+  uint16_t* __restrict__ dQ = p.dq + qbase * D;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+    for (int n = 0; n < NK; ++n) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qr = qw + 32 * hh + crow_of(i, g);
+        if (qr < p.Nq) dQ[(size_t)qr * D + 32 * n + l32] = Dt<DT>::one(acc[hh][n][i] * p.scale);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers of one template instance (explicitly instantiated per instance in
+// fa_bwd_inst.hip, so the instances compile in parallel).
+template <int DT, int D, bool CAUSAL>
+hipError_t run_pre(const BwdArgs& a, bool zero, hipStream_t s) {
+  const BwdParams p = make_params(a);
+  constexpr int RPB = 256 / (D / 8);
+  const dim3 grid((unsigned)((p.rows + RPB - 1) / RPB));
+  if (zero)
+    hipLaunchKernelGGL((bwd_pre_kernel<DT, D, true>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((bwd_pre_kernel<DT, D, false>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int DT, int D, bool CAUSAL>
+hipError_t run_dkdv(const BwdArgs& a, hipStream_t s) {
+  const BwdParams p = make_params(a);
+  const dim3 grid((unsigned)(((a.pb.Nkv + 255) / 256) * a.pb.Hkv * a.pb.B));
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int DT, int D, bool CAUSAL>
+hipError_t run_dq(const BwdArgs& a, hipStream_t s) {
+  const BwdParams p = make_params(a);
+  const dim3 grid((unsigned)(((a.pb.Nq + 255) / 256) * a.pb.Hq * a.pb.B));
+  hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace fa

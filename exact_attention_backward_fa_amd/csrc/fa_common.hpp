@@ -32,6 +32,13 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// The 16x16x32 products (v_mfma_f32_16x16x32_{f16,bf16}) use, with l16 = lane % 16
+// and j4 = lane / 16:
+//   A: lane holds 8 16-bit values of row l16, at contraction slots 8*j4..8*j4+7;
+//   B: lane holds 8 16-bit values of column l16, at the same slots;
+//   C: lane holds 4 floats; element i is row 4*j4 + i, column l16.
+// (Both layouts were checked on the GPU with an in-bounds probe.)
+
 // Row of a 32x32 C tile held in element i by lane group g.
 __device__ __forceinline__ constexpr int crow_of(int i, int g) {
   return 8 * (i >> 2) + 4 * g + (i & 3);
@@ -43,6 +50,10 @@ template <int DT> struct Dt;
 template <> struct Dt<0> {
   static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
   }
   // Two floats to two fp16 in one dword, round to nearest even.
@@ -66,6 +77,10 @@ template <> struct Dt<1> {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
   }
+  static __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
   static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     bf16x2 r = {(__bf16)lo, (__bf16)hi};
     return __builtin_bit_cast(uint32_t, r);
@@ -80,6 +95,49 @@ template <> struct Dt<1> {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
   }
 };
+
+// MFMAs with explicit register placement.  With one wave per SIMD a kernel has
+// 512 registers per lane: 256 VGPRs and 256 AGPRs.  The compiler, once a kernel
+// may use more than 256, gives every MFMA an AGPR accumulator, which does not fit
+// kernels whose long-lived accumulators alone fill the AGPRs.  These wrappers put
+// the long-lived accumulators (dK, dV, dQ) in AGPRs ("a") and the short-lived
+// score tiles in VGPRs ("v").  Being inline assembly, they are outside the
+// compiler's hazard tracking, so the kernels keep at least one other MFMA between
+// writing a tile and reading it from VALU code, and between producing an operand
+// with VALU code and the MFMA that reads it; before the accumulators are read at
+// the end, wait_mfma() lets the last MFMAs drain.
+template <int DT> struct Mx;
+template <> struct Mx<0> {
+  static __device__ __forceinline__ void acc32(f32x16& c, const u32x4& a, const u32x4& b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ f32x4 first16(const u32x4& a, const u32x4& b) {
+    f32x4 d;
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+    return d;
+  }
+  static __device__ __forceinline__ void acc16(f32x4& c, const u32x4& a, const u32x4& b) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  }
+};
+template <> struct Mx<1> {
+  static __device__ __forceinline__ void acc32(f32x16& c, const u32x4& a, const u32x4& b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ f32x4 first16(const u32x4& a, const u32x4& b) {
+    f32x4 d;
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+    return d;
+  }
+  static __device__ __forceinline__ void acc16(f32x4& c, const u32x4& a, const u32x4& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  }
+};
+// Enough idle issue cycles for any MFMA in flight to retire (a 32x32x16 MFMA is
+// 8 passes of 4 cycles).
+__device__ __forceinline__ void wait_mfma() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
 
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -101,19 +159,48 @@ __device__ __forceinline__ u32x4 pack_c_slice(const f32x16& x, int c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+__device__ __forceinline__ f32x4 zero4() {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return z;
+}
+
+// Two 16x16 C tiles X (columns 0..15) and Y (columns 16..31) of the same 16 rows,
+// each packed to 16 bits (x, y: 2 dwords = rows 4*j4 .. 4*j4+3 of the lane's
+// column), become the 32x32x16 A operand of the transposed 32 x 16 block: lane l
+// gets column l % 32 of [X | Y] with slot e holding row 8*(l/32) + e.
+// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with the
+// even rows of its second, which is exactly the exchange needed.
+__device__ __forceinline__ u32x4 c16_pair_to_a32(u32x2 x, u32x2 y) {
+  const auto s0 = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+  u32x4 r = {s0[0], s1[0], s0[1], s1[1]};
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ u32x2 pack_c4(const f32x4& x) {
+  u32x2 r = {Dt<DT>::pack2(x[0], x[1]), Dt<DT>::pack2(x[2], x[3])};
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // LDS tiles are row-major with rows of NG 16-byte granules (NG*8 16-bit columns)
-// and no padding; granule j of row r is stored at position j ^ swz(r).  The XOR
-// keeps both access patterns free of bank conflicts:
-//   - 16-byte row reads (an A/B operand with the contraction along the row): a run
-//     of consecutive rows at one logical granule lands on distinct granules;
-//   - transposed reads (ds_read_b64_tr_b16): 4 consecutive rows x 32 bytes land
-//     on 4 distinct granule pairs.
+// and no padding; granule j of row r is stored at position j ^ swz(r).  With 64
+// banks of 4 bytes, a 16-byte read serves 16 lanes per cycle and a transposed
+// 8-byte read 32 lanes per cycle; the XOR keeps the kernels' access patterns free
+// of bank conflicts:
+//   - 16-byte row reads: 16 consecutive rows at one logical granule (16x16x32
+//     operands) or 32 rows at one granule (32x32x16 operands) land on distinct
+//     positions of the 256-byte bank window;
+//   - transposed reads (ds_read_b64_tr_b16): 4 consecutive rows (aligned to 4) x 4
+//     consecutive granules (an aligned group of 4) land on 16 distinct positions.
+// For NG = 16 (256-byte rows) row bits 0-1 pick the granule quad and row bits 2-3
+// the granule within it; for NG = 8 two rows share the window, so row bit 1 picks
+// the quad and row bits 2-3 the granule.
 template <int NG>
 __device__ __forceinline__ int swz(int r) {
-  int s = ((r & 3) << 1) | ((r >> 2) & 1);
-  if (NG >= 16) s |= ((r >> 3) & 1) << 3;
-  return s;
+  if (NG >= 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // Element offset of (row r, column c) in a swizzled tile with NG granules per row.
