@@ -26,8 +26,9 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("csrc/fa_bwd.hip", "csrc/fa_bwd_atomic.hip", "csrc/fa_bwd_common.hpp",
-                  "csrc/fa_fwd.hip", "csrc/fa_common.hpp")
+KERNEL_SOURCES = ("csrc/fa_bwd.hip", "csrc/fa_bwd_inst.hip", "csrc/fa_bwd_kernels.hpp",
+                  "csrc/fa_bwd_atomic.hpp", "csrc/fa_bwd_common.hpp", "csrc/fa_fwd.hip",
+                  "csrc/fa_common.hpp")
 COPY_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_llama_gqa_bf16_8192.md")
 
