@@ -59,25 +59,89 @@ __host__ __device__ constexpr int spread_slot(int e, int E, int a, int b) {
   return a + (e * (b - a)) / E;
 }
 
-// Issue the MFMAs of one step in order.  operand(o) reads operand o from LDS; it
-// is issued LA operands ahead of its first use.  mfma(m, op) issues MFMA m;
-// valu(m) emits the VALU work placed after MFMA m.  A scheduling fence after each
-// slot keeps this order.
-template <class Plan, int LA, class FOp, class FMma, class FValu>
-__device__ __forceinline__ void run_step(FOp&& operand, FMma&& mfma, FValu&& valu) {
-  constexpr int PRE = LA < Plan::NOP ? LA : Plan::NOP;
+// The steps 0..NS-1 of one tile (StepPlan PlanOf<st> each) concatenated into one
+// MFMA stream, so the operand lookahead runs across step boundaries.
+template <template <int> class PlanOf, int... S>
+struct TileStreamImpl {
+  static constexpr int NS = sizeof...(S);
+  static constexpr int nms[NS] = {PlanOf<S>::NM...};
+  static constexpr int nops[NS] = {PlanOf<S>::NOP...};
+  static constexpr int NM = (0 + ... + PlanOf<S>::NM);
+  static constexpr int NOP = (0 + ... + PlanOf<S>::NOP);
+  static constexpr int step_of_m(int m) {
+    int st = 0;
+    while (st < NS - 1 && m >= nms[st]) m -= nms[st++];
+    return st;
+  }
+  static constexpr int m_base(int st) {
+    int a = 0;
+    for (int i = 0; i < st; ++i) a += nms[i];
+    return a;
+  }
+  static constexpr int step_of_o(int o) {
+    int st = 0;
+    while (st < NS - 1 && o >= nops[st]) o -= nops[st++];
+    return st;
+  }
+  static constexpr int o_base(int st) {
+    int a = 0;
+    for (int i = 0; i < st; ++i) a += nops[i];
+    return a;
+  }
+};
+template <template <int> class PlanOf, class Seq>
+struct TileStreamOf;
+template <template <int> class PlanOf, int... S>
+struct TileStreamOf<PlanOf, std::integer_sequence<int, S...>> {
+  using type = TileStreamImpl<PlanOf, S...>;
+};
+
+// Issue the MFMAs of one tile in order.  begin(st) runs before the first MFMA of
+// step st; operand(st, o) reads operand o of step st from LDS, LA operands ahead of
+// its first use; mfma(st, m, op) issues MFMA m of step st; valu(st, m) emits the
+// VALU work placed after it.  A scheduling fence after each slot keeps this order.
+template <template <int> class PlanOf, int NS, int LA, class FBegin, class FOp, class FMma,
+          class FValu>
+__device__ __forceinline__ void run_tile(FBegin&& begin, FOp&& operand, FMma&& mfma, FValu&& valu) {
+  using T = typename TileStreamOf<PlanOf, std::make_integer_sequence<int, NS>>::type;
+  using ic0 = std::integral_constant<int, 0>;
+  constexpr int PRE = LA < T::NOP ? LA : T::NOP;
   u32x4 ops[LA + 1];
-  static_for<PRE>([&](auto oc) { ops[decltype(oc)::value] = operand(oc); });
-  static_for<Plan::NM>([&](auto mc) {
-    constexpr int m = decltype(mc)::value;
-    constexpr int o = Plan::op_of(m);
-    if constexpr (Plan::first(m) && o + LA < Plan::NOP)
-      ops[(o + LA) % (LA + 1)] = operand(std::integral_constant<int, o + LA>());
-    mfma(mc, ops[o % (LA + 1)]);
-    valu(mc);
+  begin(ic0());
+  static_for<PRE>([&](auto oc) {
+    constexpr int o = decltype(oc)::value, st = T::step_of_o(o);
+    ops[o] = operand(std::integral_constant<int, st>(), std::integral_constant<int, o - T::o_base(st)>());
+  });
+  static_for<T::NM>([&](auto mc) {
+    constexpr int m = decltype(mc)::value, st = T::step_of_m(m), ml = m - T::m_base(st);
+    using P = PlanOf<st>;
+    using stc = std::integral_constant<int, st>;
+    if constexpr (ml == 0 && st > 0) begin(stc());
+    constexpr int o = T::o_base(st) + P::op_of(ml);
+    if constexpr (P::first(ml) && o + LA < T::NOP) {
+      constexpr int o2 = o + LA, st2 = T::step_of_o(o2);
+      ops[o2 % (LA + 1)] = operand(std::integral_constant<int, st2>(),
+                                   std::integral_constant<int, o2 - T::o_base(st2)>());
+    }
+    mfma(stc(), std::integral_constant<int, ml>(), ops[o % (LA + 1)]);
+    valu(stc(), std::integral_constant<int, ml>());
     sched_fence();
   });
 }
+
+// Step plans.  dK/dV: S_st | dK_{st-1} | dP_st | dV_st over NSB sub-blocks plus a
+// final dK step.  dQ: S^T_st | dQ_{st-1} | dP^T_st, plus a final dQ step.
+template <int NK, int NSB>
+struct DkdvSteps {
+  template <int ST>
+  using P = StepPlan<ST < NSB ? NK : 0, 4, (ST > 0) ? NK : 0, 2, ST < NSB ? NK : 0, 4,
+                     ST < NSB ? NK : 0, 2>;
+};
+template <int NK, int NSB>
+struct DqSteps {
+  template <int ST>
+  using P = StepPlan<ST < NSB ? NK : 0, 4, (ST > 0) ? NK : 0, 2, ST < NSB ? NK : 0, 4, 0, 1>;
+};
 
 // ---------------------------------------------------------------------------
 // Row preprocess.  D/8 lanes share a row; each lane reads 16 bytes of O and dO.
@@ -252,66 +316,67 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
     };
 
-    static_for<NSB + 1>([&](auto stc) {
+    using Steps = DkdvSteps<NK, NSB>;
+    auto begin = [&](auto stc) {
       constexpr int st = decltype(stc)::value;
-      constexpr bool HS = st < NSB;  // S_st, dP_st, dV_st (and P_st, dS_st) in this step
-      constexpr bool HK = st > 0;    // dK_{st-1} in this step
-      using Plan = StepPlan<HS ? NK : 0, 4, HK ? NK : 0, 2, HS ? NK : 0, 4, HS ? NK : 0, 2>;
-      if constexpr (HS) {
+      if constexpr (st < NSB) {
         lq = *reinterpret_cast<const f32x4*>(&Lt[16 * st + 4 * j4]);
         dn = *reinterpret_cast<const f32x4*>(&Dtl[16 * st + 4 * j4]);
       }
-      auto operand = [&](auto oc) -> u32x4 {
-        constexpr int o = decltype(oc)::value;
-        constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
-        if constexpr (k == 0) {
-          return lds_row16<NG>(Qt, 16 * st + l16, 4 * n + j4);
-        } else if constexpr (k == 1) {
-          const int k0 = 16 * (st - 1) + 8 * g;
-          return lds_tr_operand<NG>(Qt, k0, k0 + 4, 32 * n + 16 * hi16);
-        } else if constexpr (k == 2) {
-          return lds_row16<NG>(dOt, 16 * st + l16, 4 * n + j4);
-        } else {
-          const int k0 = 16 * st + 8 * g;
-          return lds_tr_operand<NG>(dOt, k0, k0 + 4, 32 * n + 16 * hi16);
-        }
-      };
-      auto mfma = [&](auto mc, const u32x4& op) {
-        constexpr int m = decltype(mc)::value;
-        constexpr int k = Plan::stage(m), loc = Plan::local(m);
-        if constexpr (k == 0) {
-          constexpr int s = loc / 4, kt = loc % 4;
-          if constexpr (s == 0)
-            sc[kt] = Mx<DT>::first16(op, kb[kt][s]);
-          else
-            Mx<DT>::acc16(sc[kt], op, kb[kt][s]);
-        } else if constexpr (k == 1) {
-          constexpr int n = loc / 2, h = loc % 2;
-          Mx<DT>::acc32(dk[h][n], sa[h], op);
-        } else if constexpr (k == 2) {
-          constexpr int s = loc / 4, kt = loc % 4;
-          if constexpr (s == 0)
-            dp[kt] = Mx<DT>::first16(op, vb[kt][s]);
-          else
-            Mx<DT>::acc16(dp[kt], op, vb[kt][s]);
-        } else {
-          constexpr int n = loc / 2, h = loc % 2;
-          Mx<DT>::acc32(dv[h][n], pa[h], op);
-        }
-      };
-      auto valu = [&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        if constexpr (HS) {
-          static_for<18>([&](auto ec) {
-            if constexpr (spread_slot(decltype(ec)::value, 18, Plan::B1, Plan::B3) == m)
-              p_item(ec, stc);
-            if constexpr (spread_slot(decltype(ec)::value, 18, Plan::B3, Plan::NM) == m)
-              ds_item(ec);
-          });
-        }
-      };
-      run_step<Plan, LA>(operand, mfma, valu);
-    });
+    };
+    auto operand = [&](auto stc, auto oc) -> u32x4 {
+      constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
+      using Plan = typename Steps::template P<st>;
+      constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
+      if constexpr (k == 0) {
+        return lds_row16<NG>(Qt, 16 * st + l16, 4 * n + j4);
+      } else if constexpr (k == 1) {
+        const int k0 = 16 * (st - 1) + 8 * g;
+        return lds_tr_operand<NG>(Qt, k0, k0 + 4, 32 * n + 16 * hi16);
+      } else if constexpr (k == 2) {
+        return lds_row16<NG>(dOt, 16 * st + l16, 4 * n + j4);
+      } else {
+        const int k0 = 16 * st + 8 * g;
+        return lds_tr_operand<NG>(dOt, k0, k0 + 4, 32 * n + 16 * hi16);
+      }
+    };
+    auto mfma = [&](auto stc, auto mc, const u32x4& op) {
+      constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
+      using Plan = typename Steps::template P<st>;
+      constexpr int k = Plan::stage(m), loc = Plan::local(m);
+      if constexpr (k == 0) {
+        constexpr int s = loc / 4, kt = loc % 4;
+        if constexpr (s == 0)
+          sc[kt] = Mx<DT>::first16(op, kb[kt][s]);
+        else
+          Mx<DT>::acc16(sc[kt], op, kb[kt][s]);
+      } else if constexpr (k == 1) {
+        constexpr int n = loc / 2, h = loc % 2;
+        Mx<DT>::acc32(dk[h][n], sa[h], op);
+      } else if constexpr (k == 2) {
+        constexpr int s = loc / 4, kt = loc % 4;
+        if constexpr (s == 0)
+          dp[kt] = Mx<DT>::first16(op, vb[kt][s]);
+        else
+          Mx<DT>::acc16(dp[kt], op, vb[kt][s]);
+      } else {
+        constexpr int n = loc / 2, h = loc % 2;
+        Mx<DT>::acc32(dv[h][n], pa[h], op);
+      }
+    };
+    auto valu = [&](auto stc, auto mc) {
+      constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
+      using Plan = typename Steps::template P<st>;
+      if constexpr (st < NSB) {
+        static_for<18>([&](auto ec) {
+          if constexpr (spread_slot(decltype(ec)::value, 18, Plan::B1, Plan::B3) == m)
+            p_item(ec, stc);
+          if constexpr (spread_slot(decltype(ec)::value, 18, Plan::B3, Plan::NM) == m)
+            ds_item(ec);
+        });
+      }
+    };
+    run_tile<Steps::template P, NSB + 1, LA>(begin, operand, mfma, valu);
   };
 
   // This wave's split of the query tiles (each phase runs one variant of the
@@ -491,63 +556,64 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       sc[cs][t][i] = fast_exp2(v);
     };
 
-    static_for<NSB + 1>([&](auto stc) {
+    using Steps = DqSteps<NK, NSB>;
+    // the final step has no scores to hide dS of the last sub-block under
+    auto begin = [&](auto stc) {
       constexpr int st = decltype(stc)::value;
-      constexpr bool HS = st < NSB, HK = st > 0;
-      constexpr int cs = st & 1, cp = cs ^ 1;
-      using Plan = StepPlan<HS ? NK : 0, 4, HK ? NK : 0, 2, HS ? NK : 0, 4, 0, 1>;
-      if constexpr (!HS) {
-        static_for<18>([&](auto ec) { ds_item(ec, std::integral_constant<int, cp>()); });
+      if constexpr (st == NSB)
+        static_for<18>([&](auto ec) { ds_item(ec, std::integral_constant<int, (st + 1) & 1>()); });
+    };
+    auto operand = [&](auto stc, auto oc) -> u32x4 {
+      constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
+      using Plan = typename Steps::template P<st>;
+      constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
+      if constexpr (k == 0) {
+        return lds_row16<NG>(Kt, 16 * st + l16, 4 * n + j4);
+      } else if constexpr (k == 1) {
+        const int k0 = 16 * (st - 1) + 8 * g;
+        return lds_tr_operand<NG>(Kt, k0, k0 + 4, 32 * n + 16 * hi16);
+      } else {
+        return lds_row16<NG>(Vt, 16 * st + l16, 4 * n + j4);
       }
-      auto operand = [&](auto oc) -> u32x4 {
-        constexpr int o = decltype(oc)::value;
-        constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
-        if constexpr (k == 0) {
-          return lds_row16<NG>(Kt, 16 * st + l16, 4 * n + j4);
-        } else if constexpr (k == 1) {
-          const int k0 = 16 * (st - 1) + 8 * g;
-          return lds_tr_operand<NG>(Kt, k0, k0 + 4, 32 * n + 16 * hi16);
-        } else {
-          return lds_row16<NG>(Vt, 16 * st + l16, 4 * n + j4);
-        }
-      };
-      auto mfma = [&](auto mc, const u32x4& op) {
-        constexpr int m = decltype(mc)::value;
-        constexpr int k = Plan::stage(m), loc = Plan::local(m);
-        if constexpr (k == 0) {
-          constexpr int s = loc / 4, t = loc % 4;
-          if constexpr (s == 0)
-            sc[cs][t] = Mx<DT>::first16(op, qb[t][s]);
-          else
-            Mx<DT>::acc16(sc[cs][t], op, qb[t][s]);
-        } else if constexpr (k == 1) {
-          constexpr int n = loc / 2, hh = loc % 2;
-          Mx<DT>::acc32(acc[hh][n], da[hh], op);
-        } else {
-          constexpr int s = loc / 4, t = loc % 4;
-          if constexpr (s == 0)
-            dp[t] = Mx<DT>::first16(op, db[t][s]);
-          else
-            Mx<DT>::acc16(dp[t], op, db[t][s]);
-        }
-      };
-      auto valu = [&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        if constexpr (HS && HK) {
-          static_for<18>([&](auto ec) {
-            if constexpr (spread_slot(decltype(ec)::value, 18, 0, Plan::B1) == m)
-              ds_item(ec, std::integral_constant<int, cp>());
-          });
-        }
-        if constexpr (HS) {
-          static_for<16>([&](auto ec) {
-            if constexpr (spread_slot(decltype(ec)::value, 16, Plan::B1, Plan::NM) == m)
-              p_item(ec, stc);
-          });
-        }
-      };
-      run_step<Plan, LA>(operand, mfma, valu);
-    });
+    };
+    auto mfma = [&](auto stc, auto mc, const u32x4& op) {
+      constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cs = st & 1;
+      using Plan = typename Steps::template P<st>;
+      constexpr int k = Plan::stage(m), loc = Plan::local(m);
+      if constexpr (k == 0) {
+        constexpr int s = loc / 4, t = loc % 4;
+        if constexpr (s == 0)
+          sc[cs][t] = Mx<DT>::first16(op, qb[t][s]);
+        else
+          Mx<DT>::acc16(sc[cs][t], op, qb[t][s]);
+      } else if constexpr (k == 1) {
+        constexpr int n = loc / 2, hh = loc % 2;
+        Mx<DT>::acc32(acc[hh][n], da[hh], op);
+      } else {
+        constexpr int s = loc / 4, t = loc % 4;
+        if constexpr (s == 0)
+          dp[t] = Mx<DT>::first16(op, db[t][s]);
+        else
+          Mx<DT>::acc16(dp[t], op, db[t][s]);
+      }
+    };
+    auto valu = [&](auto stc, auto mc) {
+      constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cp = (st + 1) & 1;
+      using Plan = typename Steps::template P<st>;
+      if constexpr (st < NSB && st > 0) {
+        static_for<18>([&](auto ec) {
+          if constexpr (spread_slot(decltype(ec)::value, 18, 0, Plan::B1) == m)
+            ds_item(ec, std::integral_constant<int, cp>());
+        });
+      }
+      if constexpr (st < NSB) {
+        static_for<16>([&](auto ec) {
+          if constexpr (spread_slot(decltype(ec)::value, 16, Plan::B1, Plan::NM) == m)
+            p_item(ec, stc);
+        });
+      }
+    };
+    run_tile<Steps::template P, NSB + 1, LA>(begin, operand, mfma, valu);
   };
 
   // This wave's split of the key tiles (one variant of the math per loop):
