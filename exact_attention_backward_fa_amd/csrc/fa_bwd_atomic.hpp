@@ -70,6 +70,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_atomic_kernel(BwdParams p) {
     }
   }
 
+  // The tile copies below are not visible to the compiler's wait counting, so the
+  // register and K-tile preloads are waited for here, before the first copy.
+  wait_vmem();
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) {

@@ -236,6 +236,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
     }
   }
+  // The tile copies below are not visible to the compiler's wait counting, so the
+  // register preloads are waited for here, before the first copy is issued.
+  wait_vmem();
   f32x16 dk[2][NK], dv[2][NK];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -252,13 +255,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int per_head = nqt - qt_begin;
   const int n_it = p.G * per_head;
 
-  // Iteration it covers query tile qt_begin + it / G of query head it % G of the
-  // group (tiles outer, heads inner, so the tiles that need the causal mask come
-  // first).  Query tile (fqt, fhh) goes straight into LDS buffer `buf`; rows past
-  // N_q repeat row N_q-1 and are masked in the math.  Every wave copies LSE and D
+  // Iteration it covers query tile nqt - 1 - it / G of query head it % G of the
+  // group: tiles outer, last tile first, heads inner.  Every key block of a group
+  // starts at the last query tile, so the workgroups of a group resident together
+  // read the same query tiles at about the same time and share them through L2.
+  // Query tile (fqt, fhh) goes straight into LDS buffer `buf`; rows past N_q
+  // repeat row N_q-1 and are masked in the math.  Every wave copies LSE and D
   // (identical bytes to the same place), so all waves issue OPS copies per fetch
   // and share one vmcnt bound.
-  int fqt = qt_begin, fhh = 0;  // next tile to fetch
+  int fqt = nqt - 1, fhh = 0;  // next tile to fetch
   auto fetch = [&](int buf) {
     const size_t qbase = ((size_t)b * p.Hq + (size_t)hk * p.G + fhh) * (size_t)p.Nq;
     const int q0 = fqt * BM;
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     dma4(p.delta + r, sLD[buf][1]);
     if (++fhh == p.G) {
       fhh = 0;
-      ++fqt;
+      --fqt;
     }
   };
 
@@ -380,11 +385,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   };
 
   // This wave's split of the query tiles (each phase runs one variant of the
-  // math, so the loops carry the accumulators without branches around MFMAs):
-  //   [qt_begin, qa)  no query sees the wave's keys         skipped
-  //   [qa, qb)        causal boundary or ragged key end     masked
-  //   [qb, qe)        every pair visible                    unmasked
+  // math, so the loops carry the accumulators without branches around MFMAs);
+  // in iteration order:
   //   [qe, nqt)       ragged query end                      masked
+  //   [qb, qe)        every pair visible                    unmasked
+  //   [qa, qb)        causal boundary or ragged key end     masked
+  //   [qt_begin, qa)  no query sees the wave's keys         skipped
   int qa = qt_begin, qb = qt_begin, qe = nqt;
   if (kvw >= p.Nkv) {
     qa = qb = qe = nqt;
@@ -409,12 +415,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   // iteration it works on buffer it % NBUF while tile it+NBUF-1 is copied into the
   // buffer of iteration it-1
   int it = 0, cur = 0;
-  auto phase = [&](int qt_end, auto variant) {
+  auto phase = [&](int qt_low, auto variant) {  // down to query tile qt_low
     constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
-    for (const int end = (qt_end - qt_begin) * p.G; it < end; ++it) {
+    for (const int end = (nqt - qt_low) * p.G; it < end; ++it) {
       const bool ahead = it + NBUF - 1 < n_it;
       if (ahead) fetch(cur == 0 ? NBUF - 1 : cur - 1);
-      const int q0 = (qt_begin + it / p.G) * BM;
+      const int q0 = (nqt - 1 - it / p.G) * BM;
       if constexpr (VAR == 1) compute(cur, std::true_type(), q0);
       if constexpr (VAR == 2) compute(cur, std::false_type(), q0);
       // tile it+1 must have landed; the fetch of tile it+NBUF-1 may stay in flight
@@ -426,10 +432,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       cur = cur == NBUF - 1 ? 0 : cur + 1;
     }
   };
-  phase(qa, std::integral_constant<int, 0>());
-  phase(qb, std::integral_constant<int, 1>());
-  phase(qe, std::integral_constant<int, 2>());
-  phase(nqt, std::integral_constant<int, 1>());
+  phase(qe, std::integral_constant<int, 1>());
+  phase(qb, std::integral_constant<int, 2>());
+  phase(qa, std::integral_constant<int, 1>());
+  phase(qt_begin, std::integral_constant<int, 0>());
 
   wait_mfma();
   uint16_t* __restrict__ dK = p.dk + kbase * D;
@@ -511,6 +517,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int n = 0; n < NK; ++n) acc[hh][n] = zero16();
   }
+
+  // The tile copies below are not visible to the compiler's wait counting, so the
+  // register preloads are waited for here, before the first copy is issued.
+  wait_vmem();
 
   int kv_end = p.Nkv;
   if (CAUSAL) {

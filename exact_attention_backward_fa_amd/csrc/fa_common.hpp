@@ -259,15 +259,32 @@ __device__ __forceinline__ void map_block(int L, int n_heads, int& rank, int& he
 // ---------------------------------------------------------------------------
 // Direct global -> LDS copies (global_load_lds_dwordx4 / _dword).  Every lane
 // supplies its own global address; the data of lane L lands at lds_base + size*L,
-// so one wave instruction fills 64*size contiguous LDS bytes.  The copy is tracked
-// by vmcnt only: wait_vmem() must run before the barrier that publishes it.
+// so one wave instruction fills 64*size contiguous LDS bytes.  lds_base must be
+// wave-uniform (it goes through M0).  The copy is tracked by vmcnt only: the
+// kernels wait for it explicitly (wait_vmem / wait_vmem_n) before the barrier
+// that publishes it.
+//
+// The copies are issued as inline assembly.  Through the compiler builtin, every
+// LDS read that the compiler cannot prove disjoint from an in-flight copy gets an
+// s_waitcnt vmcnt(0) in front of it; with the LDS buffer chosen at run time that
+// is every read, so each tile would wait for the copy of the tile two ahead that
+// it has just started.  The kernels never read a buffer while a copy into it is in
+// flight (the buffer being filled is the one consumed two iterations earlier).
+// 32-bit LDS address of a wave-uniform LDS pointer, in a scalar register.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const void __attribute__((address_space(3)))*)p);
+}
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gsrc,
-                                   (void __attribute__((address_space(3)))*)lds_base, 16, 0, 0);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(lds_addr(lds_base))
+               : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gsrc,
-                                   (void __attribute__((address_space(3)))*)lds_base, 4, 0, 0);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gsrc), "s"(lds_addr(lds_base))
+               : "memory", "m0");
 }
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }

@@ -66,6 +66,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   for (int s = 0; s < D / 16; ++s)
     qf[s] = qrow < p.Nq ? ld16(Q + (size_t)qrow * D + 16 * s + 8 * g) : zero_u4();
 
+  // The tile copies below are not visible to the compiler's wait counting, so the
+  // register preload is waited for here, before the first copy is issued.
+  wait_vmem();
   f32x16 acc[D / 32];
 #pragma unroll
   for (int n = 0; n < D / 32; ++n) acc[n] = zero16();
