@@ -65,7 +65,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_atomic_kernel(BwdParams p) {
     for (int c = tid; c < BN * NG; c += 256) {
       const int r = c / NG, j = c % NG;
       const int kr = kv0 + r;
-      *reinterpret_cast<u32x4*>(&sK[soff<NG>(r, 8 * j)]) =
+      *reinterpret_cast<u32x4*>(&sK[soff<NG, SW_LOWREG>(r, 8 * j)]) =
           kr < p.Nkv ? ld16(K + (size_t)kr * D + 8 * j) : zero_u4();
     }
   }
@@ -99,8 +99,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_atomic_kernel(BwdParams p) {
     size_t qbase;
     int q0;
     tile_of(it, qbase, q0);
-    dma_tile<NG, BM>(p.q + qbase * D, q0, p.Nq, sQ[buf], w, lane);
-    dma_tile<NG, BM>(p.dout + qbase * D, q0, p.Nq, sdO[buf], w, lane);
+    dma_tile<NG, BM, 256, SW_LOWREG>(p.q + qbase * D, q0, p.Nq, sQ[buf], w, lane);
+    dma_tile<NG, BM, 256, SW_LOWREG>(p.dout + qbase * D, q0, p.Nq, sdO[buf], w, lane);
     // every wave copies LSE and D (identical bytes to the same place), so all
     // waves issue OPS copies per fetch and can share one vmcnt immediate
     const size_t r = qbase + min(q0 + lane, p.Nq - 1);
@@ -123,8 +123,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_atomic_kernel(BwdParams p) {
 #pragma unroll
       for (int ks = 0; ks < BN / 16; ++ks) {
         const int k0 = 16 * ks + 8 * g;
-        const u32x4 a = lds_tr_operand<BM / 8>(sdST[buf], k0, k0 + 4, 32 * tq + 16 * hi16);
-        const u32x4 bk = lds_tr_operand<NG>(sK, k0, k0 + 4, 32 * tn + 16 * hi16);
+        const u32x4 a = lds_tr_operand<BM / 8, SW_LOWREG>(sdST[buf], k0, k0 + 4, 32 * tq + 16 * hi16);
+        const u32x4 bk = lds_tr_operand<NG, SW_LOWREG>(sK, k0, k0 + 4, 32 * tn + 16 * hi16);
         acc = Dt<DT>::mma(a, bk, acc);
       }
       float* rowp = dQacc + (size_t)(q0 + 32 * tq + 4 * g) * D + 32 * tn + l32;
@@ -167,17 +167,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_atomic_kernel(BwdParams p) {
       if constexpr (j < 2 * NM) {
         constexpr int t = j / NM, s = (j % NM) / 2;
         if constexpr (j & 1)
-          return lds_row16<NG>(sdO[cur], 32 * t + l32, 2 * s + g);
+          return lds_row16<NG, SW_LOWREG>(sdO[cur], 32 * t + l32, 2 * s + g);
         else
-          return lds_row16<NG>(sQ[cur], 32 * t + l32, 2 * s + g);
+          return lds_row16<NG, SW_LOWREG>(sQ[cur], 32 * t + l32, 2 * s + g);
       } else {
         constexpr int jj = j - 2 * NM, t = jj / NM, k = jj % NM;
         constexpr int c = k / (NM / 2), n = (k % (NM / 2)) / 2;
         const int k0 = 32 * t + 16 * c + 4 * g;
         if constexpr (k & 1)
-          return lds_tr_operand<NG>(sQ[cur], k0, k0 + 8, 32 * n + 16 * hi16);
+          return lds_tr_operand<NG, SW_LOWREG>(sQ[cur], k0, k0 + 8, 32 * n + 16 * hi16);
         else
-          return lds_tr_operand<NG>(sdO[cur], k0, k0 + 8, 32 * n + 16 * hi16);
+          return lds_tr_operand<NG, SW_LOWREG>(sdO[cur], k0, k0 + 8, 32 * n + 16 * hi16);
       }
     };
     auto mfma = [&](auto jc, const u32x4& op) {
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_atomic_kernel(BwdParams p) {
           u32x2 v2;
           v2[0] = Dt<DT>::pack2(dp[t][4 * j + 0], dp[t][4 * j + 1]);
           v2[1] = Dt<DT>::pack2(dp[t][4 * j + 2], dp[t][4 * j + 3]);
-          *reinterpret_cast<u32x2*>(&sdST[cur][soff<BM / 8>(32 * w + l32, 32 * t + 8 * j + 4 * g)]) = v2;
+          *reinterpret_cast<u32x2*>(&sdST[cur][soff<BM / 8, SW_LOWREG>(32 * w + l32, 32 * t + 8 * j + 4 * g)]) = v2;
         }
       }
     }

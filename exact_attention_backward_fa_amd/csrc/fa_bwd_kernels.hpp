@@ -201,14 +201,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int KW = 64, BN = 4 * KW, BM = 64, NSB = BM / 16;
-  constexpr int NG = D / 8, NK = D / 32;
-  constexpr int TILE = BM * D;
+  constexpr int NK = D / 32;
   constexpr int NBUF = 3;
-  constexpr int OPS = 2 * (BM * NG / 256) + 2;  // copy instructions per fetch per wave
-  constexpr int LA = 2;                          // operand lookahead
-  // Q and dO of a buffer are adjacent (as are LSE and D), so both tiles are read
-  // through the same per-lane address registers with different immediate offsets.
-  __shared__ __attribute__((aligned(16))) uint16_t sQdO[NBUF][2][TILE];
+  constexpr int RS = PadTile<D>::RS;
+  constexpr int OPS = 2 * BM * PadTile<D>::GR / 256 + 2;  // copy instructions per fetch per wave
+  constexpr int LA = 2;                                     // operand lookahead
+  // Q and dO of a buffer are one padded tile pair (as are LSE and D), so both are
+  // read through the same per-lane address registers with immediate offsets.
+  __shared__ __attribute__((aligned(16))) uint16_t sQdO[NBUF][2 * BM * RS];
   __shared__ __attribute__((aligned(16))) float sLD[NBUF][2][BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -267,8 +267,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   auto fetch = [&](int buf) {
     const size_t qbase = ((size_t)b * p.Hq + (size_t)hk * p.G + fhh) * (size_t)p.Nq;
     const int q0 = fqt * BM;
-    dma_tile<NG, BM>(p.q + qbase * D, q0, p.Nq, sQdO[buf][0], w, lane);
-    dma_tile<NG, BM>(p.dout + qbase * D, q0, p.Nq, sQdO[buf][1], w, lane);
+    dma_pad_pair<D, BM>(p.q + qbase * D, p.dout + qbase * D, q0, p.Nq, sQdO[buf], w, lane);
     const size_t r = qbase + min(q0 + lane, p.Nq - 1);
     dma4(p.lse2 + r, sLD[buf][0]);
     dma4(p.delta + r, sLD[buf][1]);
@@ -280,8 +279,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 
   auto compute = [&](int cur, auto mask_c, int q0) {
     constexpr bool MASK = decltype(mask_c)::value;
-    const uint16_t* Qt = sQdO[cur][0];
-    const uint16_t* dOt = Qt + TILE;
+    const uint16_t* Qt = sQdO[cur];
+    const uint16_t* dOt = Qt + BM * RS;
     const float* Lt = sLD[cur][0];
     const float* Dtl = Lt + BM;
     f32x4 sc[4];         // S, then P, of the current sub-block, per key tile
@@ -334,15 +333,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       using Plan = typename Steps::template P<st>;
       constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
       if constexpr (k == 0) {
-        return lds_row16<NG>(Qt, 16 * st + l16, 4 * n + j4);
+        return pad_row16<D>(Qt, 16 * st + l16, 4 * n + j4);
       } else if constexpr (k == 1) {
         const int k0 = 16 * (st - 1) + 8 * g;
-        return lds_tr_operand<NG>(Qt, k0, k0 + 4, 32 * n + 16 * hi16);
+        return pad_tr_operand<D>(Qt, k0, k0 + 4, 32 * n + 16 * hi16);
       } else if constexpr (k == 2) {
-        return lds_row16<NG>(dOt, 16 * st + l16, 4 * n + j4);
+        return pad_row16<D>(dOt, 16 * st + l16, 4 * n + j4);
       } else {
         const int k0 = 16 * st + 8 * g;
-        return lds_tr_operand<NG>(dOt, k0, k0 + 4, 32 * n + 16 * hi16);
+        return pad_tr_operand<D>(dOt, k0, k0 + 4, 32 * n + 16 * hi16);
       }
     };
     auto mfma = [&](auto stc, auto mc, const u32x4& op) {
@@ -473,12 +472,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int QW = 64, BM = 4 * QW, BN = 64, NSB = BN / 16;
-  constexpr int NG = D / 8, NK = D / 32;
-  constexpr int TILE = BN * D;
+  constexpr int NK = D / 32;
   constexpr int NBUF = 3;                   // key/value tiles fetched two ahead
-  constexpr int OPS = 2 * (BN * NG / 256);  // copy instructions per fetch per wave
+  constexpr int RS = PadTile<D>::RS;
+  constexpr int OPS = 2 * BN * PadTile<D>::GR / 256;  // copy instructions per fetch per wave
   constexpr int LA = 2;
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[NBUF][2][TILE];  // K, V adjacent
+  __shared__ __attribute__((aligned(16))) uint16_t sKV[NBUF][2 * BN * RS];  // K, V: a padded pair
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
@@ -530,14 +529,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
   auto fetch = [&](int kt, int buf) {
-    dma_tile<NG, BN>(K, kt * BN, p.Nkv, sKV[buf][0], w, lane);
-    dma_tile<NG, BN>(V, kt * BN, p.Nkv, sKV[buf][1], w, lane);
+    dma_pad_pair<D, BN>(K, V, kt * BN, p.Nkv, sKV[buf], w, lane);
   };
 
   auto compute = [&](int cur, auto mask_c, int kv0) {
     constexpr bool MASK = decltype(mask_c)::value;
-    const uint16_t* Kt = sKV[cur][0];
-    const uint16_t* Vt = Kt + TILE;
+    const uint16_t* Kt = sKV[cur];
+    const uint16_t* Vt = Kt + BN * RS;
     f32x4 sc[2][4];  // S^T, then P^T, of sub-block st in sc[st % 2], per query tile
     f32x4 dp[4];     // dP^T, then dS^T, of the sub-block being finished
     u32x4 da[2];     // dS A operands, per query half
@@ -578,12 +576,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       using Plan = typename Steps::template P<st>;
       constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
       if constexpr (k == 0) {
-        return lds_row16<NG>(Kt, 16 * st + l16, 4 * n + j4);
+        return pad_row16<D>(Kt, 16 * st + l16, 4 * n + j4);
       } else if constexpr (k == 1) {
         const int k0 = 16 * (st - 1) + 8 * g;
-        return lds_tr_operand<NG>(Kt, k0, k0 + 4, 32 * n + 16 * hi16);
+        return pad_tr_operand<D>(Kt, k0, k0 + 4, 32 * n + 16 * hi16);
       } else {
-        return lds_row16<NG>(Vt, 16 * st + l16, 4 * n + j4);
+        return pad_row16<D>(Vt, 16 * st + l16, 4 * n + j4);
       }
     };
     auto mfma = [&](auto stc, auto mc, const u32x4& op) {

@@ -185,34 +185,42 @@ __device__ __forceinline__ u32x2 pack_c4(const f32x4& x) {
 
 // ---------------------------------------------------------------------------
 // LDS tiles are row-major with rows of NG 16-byte granules (NG*8 16-bit columns)
-// and no padding; granule j of row r is stored at position j ^ swz(r).  With 64
-// banks of 4 bytes, a 16-byte read serves 16 lanes per cycle and a transposed
-// 8-byte read 32 lanes per cycle; the XOR keeps the kernels' access patterns free
-// of bank conflicts:
-//   - 16-byte row reads: 16 consecutive rows at one logical granule (16x16x32
-//     operands) or 32 rows at one granule (32x32x16 operands) land on distinct
-//     positions of the 256-byte bank window;
-//   - transposed reads (ds_read_b64_tr_b16): 4 consecutive rows (aligned to 4) x 4
-//     consecutive granules (an aligned group of 4) land on 16 distinct positions.
-// For NG = 16 (256-byte rows) row bits 0-1 pick the granule quad and row bits 2-3
-// the granule within it; for NG = 8 two rows share the window, so row bit 1 picks
-// the quad and row bits 2-3 the granule.
-template <int NG>
+// and no padding; granule j of row r is stored at position j ^ swz(r), so that
+// both access patterns of the kernels avoid LDS bank conflicts:
+//   - 16-byte row reads of an MFMA operand: 16 (16x16x32) or 32 (32x32x16)
+//     consecutive rows at one logical granule;
+//   - transposed reads (ds_read_b64_tr_b16): 4 consecutive rows x 32 bytes.
+// For NG = 16 the XOR value takes row bits (r0, r2, r3, r1^r3) as granule bits
+// 0..3; for NG = 8 it is row bits 1..3.  It was chosen by timing every invertible map whose granule bits are XORs
+// of at most two row bits on an MI355X: it reads the 16x16x32 operand patterns at
+// about 170 B/clk (rows) and 99 B/clk (transposed) per CU, and the 32x32x16 ones
+// at 174 and 113, the best of all maps tried for both.
+//
+// SW selects the map: SW_MIN (the map above) or SW_LOWREG, an older map that reads
+// the 32x32x16 patterns at the same rate (174 / 113 B/clk) and whose per-lane XOR
+// values the compiler keeps in fewer registers; the fused atomic-dQ kernel, which
+// is short of registers, uses it.
+enum : int { SW_MIN = 0, SW_LOWREG = 1 };
+template <int NG, int SW = SW_MIN>
 __device__ __forceinline__ int swz(int r) {
-  if (NG >= 16) return ((r & 3) << 2) | ((r >> 2) & 3);
-  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  if (NG >= 16) {
+    if (SW == SW_LOWREG) return ((r & 3) << 1) | ((r >> 2) & 1) | (((r >> 3) & 1) << 3);
+    return (r & 1) | ((r >> 1) & 6) | ((((r >> 1) ^ (r >> 3)) & 1) << 3);
+  }
+  if (SW == SW_LOWREG) return ((r & 3) << 1) | ((r >> 2) & 1);
+  return (r >> 1) & 7;  // NG = 8: two rows share the 256-byte bank window
 }
 
 // Element offset of (row r, column c) in a swizzled tile with NG granules per row.
-template <int NG>
+template <int NG, int SW = SW_MIN>
 __device__ __forceinline__ int soff(int r, int c) {
-  return r * (NG * 8) + (((c >> 3) ^ swz<NG>(r)) << 3) + (c & 7);
+  return r * (NG * 8) + (((c >> 3) ^ swz<NG, SW>(r)) << 3) + (c & 7);
 }
 
 // 16-byte read of logical granule `gr` of row r.
-template <int NG>
+template <int NG, int SW = SW_MIN>
 __device__ __forceinline__ u32x4 lds_row16(const uint16_t* X, int r, int gr) {
-  return *reinterpret_cast<const u32x4*>(X + r * (NG * 8) + ((gr ^ swz<NG>(r)) << 3));
+  return *reinterpret_cast<const u32x4*>(X + r * (NG * 8) + ((gr ^ swz<NG, SW>(r)) << 3));
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -229,12 +237,12 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
 // MFMA operand read transposed from a swizzled row-major tile X[k][n]: for column
 // n = n0 + lane%16 the lane gets slots 0..3 = X[k0 + 0..3][n] and slots
 // 4..7 = X[k1 + 0..3][n].
-template <int NG>
+template <int NG, int SW = SW_MIN>
 __device__ __forceinline__ u32x4 lds_tr_operand(const uint16_t* X, int k0, int k1, int n0) {
   const int i = threadIdx.x & 15;
   const int c = n0 + 4 * (i & 3);
-  const u32x2 a = lds_tr16(X + soff<NG>(k0 + (i >> 2), c));
-  const u32x2 b = lds_tr16(X + soff<NG>(k1 + (i >> 2), c));
+  const u32x2 a = lds_tr16(X + soff<NG, SW>(k0 + (i >> 2), c));
+  const u32x2 b = lds_tr16(X + soff<NG, SW>(k1 + (i >> 2), c));
   u32x4 r = {a[0], a[1], b[0], b[1]};
   return r;
 }
@@ -314,7 +322,7 @@ __device__ __forceinline__ void lds_barrier() {
 // Fill a swizzled ROWS x (NG*8) tile from rows row0.. of a row-major matrix with
 // NG*8 columns; rows at or past n_rows read row n_rows-1 instead (callers mask
 // them).  NT threads; each wave issues ROWS*NG/NT copies of 1 KB.
-template <int NG, int ROWS, int NT = 256>
+template <int NG, int ROWS, int NT = 256, int SW = SW_MIN>
 __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ g, int row0, int n_rows,
                                          uint16_t* lds, int w, int lane) {
   constexpr int PER_WAVE = ROWS * NG / NT;
@@ -324,9 +332,67 @@ __device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ g, int row
     const int blk = PER_WAVE * w + c;
     const int ph = blk * 64 + lane;  // physical granule this lane fills
     const int r = ph / NG;
-    const int j = (ph % NG) ^ swz<NG>(r);
+    const int j = (ph % NG) ^ swz<NG, SW>(r);
     const int rr = min(row0 + r, n_rows - 1);
     dma16(g + (size_t)rr * (NG * 8) + 8 * j, lds + blk * 64 * 8);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Padded LDS tiles (the kernels whose score products are 16x16x32 MFMAs).  A pair
+// of ROWS-row tiles of the same shape (Q and dO, or K and V) is stored as 2*ROWS
+// rows of D + 16 16-bit elements: the 32-byte pad per row spreads the rows over
+// the banks.  Measured on an MI355X for the 16x16x32 operand patterns (16-byte
+// reads of 16 consecutive rows, transposed reads of 4 rows x 32 bytes), the
+// 288-byte (D = 128) and 160-byte (D = 64) strides run within a few percent of the
+// best XOR swizzle, and every operand of a tile is then a fixed offset from one
+// per-lane base address, which keeps address registers out of the inner loop.
+template <int D>
+struct PadTile {
+  static constexpr int RS = D + 16;           // row stride in elements
+  static constexpr int GR = RS / 8;           // 16-byte granules per row, pad included
+  static constexpr int NG = D / 8;            // data granules per row
+};
+
+// 16-byte read of granule gr of row r.
+template <int D>
+__device__ __forceinline__ u32x4 pad_row16(const uint16_t* X, int r, int gr) {
+  return *reinterpret_cast<const u32x4*>(X + r * PadTile<D>::RS + 8 * gr);
+}
+
+// Transposed MFMA operand (as lds_tr_operand) from a padded tile.
+template <int D>
+__device__ __forceinline__ u32x4 pad_tr_operand(const uint16_t* X, int k0, int k1, int n0) {
+  const int i = threadIdx.x & 15;
+  const int c = n0 + 4 * (i & 3);
+  const u32x2 a = lds_tr16(X + (k0 + (i >> 2)) * PadTile<D>::RS + c);
+  const u32x2 b = lds_tr16(X + (k1 + (i >> 2)) * PadTile<D>::RS + c);
+  u32x4 r = {a[0], a[1], b[0], b[1]};
+  return r;
+}
+
+// Fill a pair of padded ROWS-row tiles (tile 0 from g0, tile 1 from g1; matrices of
+// D columns, rows row0..; rows at or past n_rows read row n_rows-1, callers mask
+// them).  The pair is 2*ROWS*GR granules, copied by 4 waves in 1-KB instructions;
+// each wave's instructions fall in one tile.  Pad granules receive a copy of
+// granule 0 of their row.
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_pad_pair(const uint16_t* __restrict__ g0,
+                                             const uint16_t* __restrict__ g1, int row0, int n_rows,
+                                             uint16_t* lds, int w, int lane) {
+  using T = PadTile<D>;
+  constexpr int TILE_SLOTS = ROWS * T::GR;
+  constexpr int PER_WAVE = 2 * TILE_SLOTS / (4 * 64);
+  static_assert(PER_WAVE * 4 * 64 == 2 * TILE_SLOTS && TILE_SLOTS % (2 * 64) == 0,
+                "each wave must copy whole instructions within one tile");
+  const uint16_t* __restrict__ src = w < 2 ? g0 : g1;
+#pragma unroll
+  for (int c = 0; c < PER_WAVE; ++c) {
+    const int blk = PER_WAVE * w + c;
+    const int slot = blk * 64 + lane - (w < 2 ? 0 : TILE_SLOTS);  // slot within its tile
+    const int r = slot / T::GR, gr = slot % T::GR;
+    const int rr = min(row0 + r, n_rows - 1);
+    dma16(src + (size_t)rr * D + 8 * (gr < T::NG ? gr : 0), lds + blk * 64 * 8);
   }
 }
 
