@@ -98,8 +98,9 @@ struct TileStreamOf<PlanOf, std::integer_sequence<int, S...>> {
 
 // Issue the MFMAs of one tile in order.  begin(st) runs before the first MFMA of
 // step st; operand(st, o) reads operand o of step st from LDS, LA operands ahead of
-// its first use; mfma(st, m, op) issues MFMA m of step st; valu(st, m) emits the
-// VALU work placed after it.  A scheduling fence after each slot keeps this order.
+// its first use; mfma(st, m, op) issues MFMA m of step st; valu(st, m, g) emits the
+// work placed after it (g: index of the MFMA in the whole tile).  A scheduling fence
+// after each slot keeps this order.
 template <template <int> class PlanOf, int NS, int LA, class FBegin, class FOp, class FMma,
           class FValu>
 __device__ __forceinline__ void run_tile(FBegin&& begin, FOp&& operand, FMma&& mfma, FValu&& valu) {
@@ -124,9 +125,14 @@ __device__ __forceinline__ void run_tile(FBegin&& begin, FOp&& operand, FMma&& m
                                    std::integral_constant<int, o2 - T::o_base(st2)>());
     }
     mfma(stc(), std::integral_constant<int, ml>(), ops[o % (LA + 1)]);
-    valu(stc(), std::integral_constant<int, ml>());
+    valu(stc(), std::integral_constant<int, ml>(), mc);
     sched_fence();
   });
+}
+
+template <template <int> class PlanOf, int NS>
+constexpr int tile_mfmas() {
+  return TileStreamOf<PlanOf, std::make_integer_sequence<int, NS>>::type::NM;
 }
 
 // Step plans.  dK/dV: S_st | dK_{st-1} | dP_st | dV_st over NSB sub-blocks plus a
@@ -259,25 +265,47 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   // group: tiles outer, last tile first, heads inner.  Every key block of a group
   // starts at the last query tile, so the workgroups of a group resident together
   // read the same query tiles at about the same time and share them through L2.
-  // Query tile (fqt, fhh) goes straight into LDS buffer `buf`; rows past N_q
-  // repeat row N_q-1 and are masked in the math.  Every wave copies LSE and D
-  // (identical bytes to the same place), so all waves issue OPS copies per fetch
-  // and share one vmcnt bound.
-  int fqt = nqt - 1, fhh = 0;  // next tile to fetch
-  auto fetch = [&](int buf) {
-    const size_t qbase = ((size_t)b * p.Hq + (size_t)hk * p.G + fhh) * (size_t)p.Nq;
-    const int q0 = fqt * BM;
-    dma_pad_pair<D, BM>(p.q + qbase * D, p.dout + qbase * D, q0, p.Nq, sQdO[buf], w, lane);
-    const size_t r = qbase + min(q0 + lane, p.Nq - 1);
-    dma4(p.lse2 + r, sLD[buf][0]);
-    dma4(p.delta + r, sLD[buf][1]);
-    if (++fhh == p.G) {
-      fhh = 0;
-      --fqt;
-    }
+  //
+  // Iteration it copies tile it + NBUF - 1 into the buffer of iteration it - 1; past
+  // the last tile it copies the last tile again, into a buffer no later iteration
+  // reads, so every iteration issues the same OPS copies per wave (spread over its
+  // MFMA stream) and one vmcnt bound covers them.  Rows past N_q repeat row N_q-1
+  // and are masked in the math.  Every wave copies LSE and D (identical bytes to
+  // the same place).
+  struct Src {
+    const uint16_t* q;
+    const uint16_t* d;
+    const float* l;
+    const float* dl;
+    int q0;
+  };
+  auto src_of = [&](int fit) {
+    fit = min(fit, n_it - 1);
+    const int hh = fit % p.G;
+    const size_t qbase = ((size_t)b * p.Hq + (size_t)hk * p.G + hh) * (size_t)p.Nq;
+    Src sr;
+    sr.q0 = (nqt - 1 - fit / p.G) * BM;
+    sr.q = p.q + qbase * D;
+    sr.d = p.dout + qbase * D;
+    const size_t r = qbase + min(sr.q0 + lane, p.Nq - 1);
+    sr.l = p.lse2 + r;
+    sr.dl = p.delta + r;
+    return sr;
+  };
+  using Copy = PadPairCopy<D, BM>;
+  auto copy_part = [&](int c, const Src& sr, int buf) {
+    if (c < Copy::PER_WAVE)
+      Copy::part(c, sr.q, sr.d, sr.q0, p.Nq, sQdO[buf], w, lane);
+    else if (c == Copy::PER_WAVE)
+      dma4(sr.l, sLD[buf][0]);
+    else
+      dma4(sr.dl, sLD[buf][1]);
+  };
+  auto copy_all = [&](const Src& sr, int buf) {
+    for (int c = 0; c < OPS; ++c) copy_part(c, sr, buf);
   };
 
-  auto compute = [&](int cur, auto mask_c, int q0) {
+  auto compute = [&](int cur, auto mask_c, int q0, const Src& fsrc, int fbuf) {
     constexpr bool MASK = decltype(mask_c)::value;
     const uint16_t* Qt = sQdO[cur];
     const uint16_t* dOt = Qt + BM * RS;
@@ -368,8 +396,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         Mx<DT>::acc32(dv[h][n], pa[h], op);
       }
     };
-    auto valu = [&](auto stc, auto mc) {
-      constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
+    constexpr int NMT = tile_mfmas<Steps::template P, NSB + 1>();
+    auto valu = [&](auto stc, auto mc, auto gc) {
+      constexpr int st = decltype(stc)::value, m = decltype(mc)::value, gm = decltype(gc)::value;
       using Plan = typename Steps::template P<st>;
       if constexpr (st < NSB) {
         static_for<18>([&](auto ec) {
@@ -379,6 +408,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
             ds_item(ec);
         });
       }
+      // the copies of a later tile, spread over the stream
+      static_for<OPS>([&](auto cc) {
+        if constexpr (spread_slot(decltype(cc)::value, OPS, 0, NMT) == gm)
+          copy_part(decltype(cc)::value, fsrc, fbuf);
+      });
     };
     run_tile<Steps::template P, NSB + 1, LA>(begin, operand, mfma, valu);
   };
@@ -403,30 +437,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     qb = min(qb, nqt);
     qe = max(qb, min(nqt, p.Nq / BM));
   }
-  static_for<NBUF - 1>([&](auto bc) {
-    if (decltype(bc)::value < n_it) fetch(decltype(bc)::value);
-  });
-  if (n_it >= NBUF - 1)
+  if (n_it > 0) {
+    static_for<NBUF - 1>([&](auto bc) { copy_all(src_of(decltype(bc)::value), decltype(bc)::value); });
     wait_vmem_n<OPS * (NBUF - 2)>();
-  else
-    wait_vmem();
-  lds_barrier();
+    lds_barrier();
+  }
   // iteration it works on buffer it % NBUF while tile it+NBUF-1 is copied into the
   // buffer of iteration it-1
   int it = 0, cur = 0;
   auto phase = [&](int qt_low, auto variant) {  // down to query tile qt_low
     constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
     for (const int end = (nqt - qt_low) * p.G; it < end; ++it) {
-      const bool ahead = it + NBUF - 1 < n_it;
-      if (ahead) fetch(cur == 0 ? NBUF - 1 : cur - 1);
+      const Src fsrc = src_of(it + NBUF - 1);
+      const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
       const int q0 = (nqt - 1 - it / p.G) * BM;
-      if constexpr (VAR == 1) compute(cur, std::true_type(), q0);
-      if constexpr (VAR == 2) compute(cur, std::false_type(), q0);
-      // tile it+1 must have landed; the fetch of tile it+NBUF-1 may stay in flight
-      if (ahead)
-        wait_vmem_n<OPS * (NBUF - 2)>();
-      else
-        wait_vmem();
+      if constexpr (VAR == 0) copy_all(fsrc, fbuf);
+      if constexpr (VAR == 1) compute(cur, std::true_type(), q0, fsrc, fbuf);
+      if constexpr (VAR == 2) compute(cur, std::false_type(), q0, fsrc, fbuf);
+      // tile it+1 must have landed; the copies issued in this iteration may stay in
+      // flight
+      wait_vmem_n<OPS * (NBUF - 2)>();
       lds_barrier();
       cur = cur == NBUF - 1 ? 0 : cur + 1;
     }
@@ -435,6 +465,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   phase(qb, std::integral_constant<int, 2>());
   phase(qa, std::integral_constant<int, 1>());
   phase(qt_begin, std::integral_constant<int, 0>());
+  wait_vmem();  // no copy may land in LDS after the workgroup ends
 
   wait_mfma();
   uint16_t* __restrict__ dK = p.dk + kbase * D;
@@ -528,11 +559,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   }
   const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
-  auto fetch = [&](int kt, int buf) {
-    dma_pad_pair<D, BN>(K, V, kt * BN, p.Nkv, sKV[buf], w, lane);
+  // Iteration kt copies key/value tile kt + NBUF - 1 into the buffer of iteration
+  // kt - 1 (past the last tile, the last tile again, into a buffer no later
+  // iteration reads), OPS copies per wave spread over its MFMA stream.
+  using Copy = PadPairCopy<D, BN>;
+  auto copy_all = [&](int kt, int buf) {
+    dma_pad_pair<D, BN>(K, V, min(kt, nkt - 1) * BN, p.Nkv, sKV[buf], w, lane);
   };
 
-  auto compute = [&](int cur, auto mask_c, int kv0) {
+  auto compute = [&](int cur, auto mask_c, int kv0, int fkv0, int fbuf) {
     constexpr bool MASK = decltype(mask_c)::value;
     const uint16_t* Kt = sKV[cur];
     const uint16_t* Vt = Kt + BN * RS;
@@ -605,8 +640,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
           Mx<DT>::acc16(dp[t], op, db[t][s]);
       }
     };
-    auto valu = [&](auto stc, auto mc) {
+    constexpr int NMT = tile_mfmas<Steps::template P, NSB + 1>();
+    auto valu = [&](auto stc, auto mc, auto gc) {
       constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cp = (st + 1) & 1;
+      constexpr int gm = decltype(gc)::value;
       using Plan = typename Steps::template P<st>;
       if constexpr (st < NSB && st > 0) {
         static_for<18>([&](auto ec) {
@@ -620,6 +657,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
             p_item(ec, stc);
         });
       }
+      static_for<OPS>([&](auto cc) {
+        if constexpr (spread_slot(decltype(cc)::value, OPS, 0, NMT) == gm)
+          Copy::part(decltype(cc)::value, K, V, fkv0, p.Nkv, sKV[fbuf], w, lane);
+      });
     };
     run_tile<Steps::template P, NSB + 1, LA>(begin, operand, mfma, valu);
   };
@@ -634,27 +675,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   int n_un = min(n_vis, p.Nkv / BN);
   if (CAUSAL) n_un = min(n_un, max(0, floor_div(qw + p.off - (BN - 1), BN) + 1));
 
-  static_for<NBUF - 1>([&](auto bc) {
-    constexpr int k = decltype(bc)::value;
-    if (k < nkt) fetch(k, k);
-  });
-  if (nkt >= NBUF - 1)
+  if (nkt > 0) {
+    static_for<NBUF - 1>([&](auto bc) { copy_all(decltype(bc)::value, decltype(bc)::value); });
     wait_vmem_n<OPS * (NBUF - 2)>();
-  else
-    wait_vmem();
-  lds_barrier();
+    lds_barrier();
+  }
   int kt = 0, cur = 0;
   auto phase = [&](int end, auto variant) {
     constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
     for (; kt < end; ++kt) {
-      const bool ahead = kt + NBUF - 1 < nkt;
-      if (ahead) fetch(kt + NBUF - 1, cur == 0 ? NBUF - 1 : cur - 1);
-      if constexpr (VAR == 1) compute(cur, std::true_type(), kt * BN);
-      if constexpr (VAR == 2) compute(cur, std::false_type(), kt * BN);
-      if (ahead)
-        wait_vmem_n<OPS * (NBUF - 2)>();
-      else
-        wait_vmem();
+      const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
+      const int fkv0 = min(kt + NBUF - 1, nkt - 1) * BN;
+      if constexpr (VAR == 0) copy_all(kt + NBUF - 1, fbuf);
+      if constexpr (VAR == 1) compute(cur, std::true_type(), kt * BN, fkv0, fbuf);
+      if constexpr (VAR == 2) compute(cur, std::false_type(), kt * BN, fkv0, fbuf);
+      // tile kt+1 must have landed; this iteration's copies may stay in flight
+      wait_vmem_n<OPS * (NBUF - 2)>();
       lds_barrier();
       cur = cur == NBUF - 1 ? 0 : cur + 1;
     }
@@ -662,6 +698,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   phase(n_un, std::integral_constant<int, 2>());
   phase(n_vis, std::integral_constant<int, 1>());
   phase(nkt, std::integral_constant<int, 0>());
+  wait_vmem();  // no copy may land in LDS after the workgroup ends
 
   wait_mfma();
   uint16_t* __restrict__ dQ = p.dq + qbase * D;

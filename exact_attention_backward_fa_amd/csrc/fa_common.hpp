@@ -373,27 +373,36 @@ __device__ __forceinline__ u32x4 pad_tr_operand(const uint16_t* X, int k0, int k
 
 // Fill a pair of padded ROWS-row tiles (tile 0 from g0, tile 1 from g1; matrices of
 // D columns, rows row0..; rows at or past n_rows read row n_rows-1, callers mask
-// them).  The pair is 2*ROWS*GR granules, copied by 4 waves in 1-KB instructions;
-// each wave's instructions fall in one tile.  Pad granules receive a copy of
-// granule 0 of their row.
+// them).  The pair is 2*ROWS*GR granules, copied by 4 waves in 1-KB instructions
+// (PER_WAVE each); each wave's instructions fall in one tile.  Pad granules receive
+// a copy of granule 0 of their row.  part(c, ...) issues instruction c of the
+// calling wave, so the copy can be spread over a stream of other work.
 template <int D, int ROWS>
-__device__ __forceinline__ void dma_pad_pair(const uint16_t* __restrict__ g0,
-                                             const uint16_t* __restrict__ g1, int row0, int n_rows,
-                                             uint16_t* lds, int w, int lane) {
+struct PadPairCopy {
   using T = PadTile<D>;
-  constexpr int TILE_SLOTS = ROWS * T::GR;
-  constexpr int PER_WAVE = 2 * TILE_SLOTS / (4 * 64);
+  static constexpr int TILE_SLOTS = ROWS * T::GR;
+  static constexpr int PER_WAVE = 2 * TILE_SLOTS / (4 * 64);
   static_assert(PER_WAVE * 4 * 64 == 2 * TILE_SLOTS && TILE_SLOTS % (2 * 64) == 0,
                 "each wave must copy whole instructions within one tile");
-  const uint16_t* __restrict__ src = w < 2 ? g0 : g1;
-#pragma unroll
-  for (int c = 0; c < PER_WAVE; ++c) {
+  static __device__ __forceinline__ void part(int c, const uint16_t* __restrict__ g0,
+                                              const uint16_t* __restrict__ g1, int row0, int n_rows,
+                                              uint16_t* lds, int w, int lane) {
+    const uint16_t* __restrict__ src = w < 2 ? g0 : g1;
     const int blk = PER_WAVE * w + c;
     const int slot = blk * 64 + lane - (w < 2 ? 0 : TILE_SLOTS);  // slot within its tile
     const int r = slot / T::GR, gr = slot % T::GR;
     const int rr = min(row0 + r, n_rows - 1);
     dma16(src + (size_t)rr * D + 8 * (gr < T::NG ? gr : 0), lds + blk * 64 * 8);
   }
+};
+
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_pad_pair(const uint16_t* __restrict__ g0,
+                                             const uint16_t* __restrict__ g1, int row0, int n_rows,
+                                             uint16_t* lds, int w, int lane) {
+#pragma unroll
+  for (int c = 0; c < PadPairCopy<D, ROWS>::PER_WAVE; ++c)
+    PadPairCopy<D, ROWS>::part(c, g0, g1, row0, n_rows, lds, w, lane);
 }
 
 // ---------------------------------------------------------------------------
