@@ -396,7 +396,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         Mx<DT>::acc32(dv[h][n], pa[h], op);
       }
     };
-    constexpr int NMT = tile_mfmas<Steps::template P, NSB + 1>();
     auto valu = [&](auto stc, auto mc, auto gc) {
       constexpr int st = decltype(stc)::value, m = decltype(mc)::value, gm = decltype(gc)::value;
       using Plan = typename Steps::template P<st>;
@@ -408,11 +407,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
             ds_item(ec);
         });
       }
-      // the copies of a later tile, spread over the stream
-      static_for<OPS>([&](auto cc) {
-        if constexpr (spread_slot(decltype(cc)::value, OPS, 0, NMT) == gm)
-          copy_part(decltype(cc)::value, fsrc, fbuf);
-      });
+      // The copies of a later tile ride on the score stages (S_st), which carry no
+      // other VALU work: copy c goes after MFMA slot(c) of the concatenated S stages.
+      (void)gm;
+      if constexpr (st < NSB && m < Plan::B1) {
+        static_for<OPS>([&](auto cc) {
+          if constexpr (spread_slot(decltype(cc)::value, OPS, 0, NSB * Plan::B1) == st * Plan::B1 + m)
+            copy_part(decltype(cc)::value, fsrc, fbuf);
+        });
+      }
     };
     run_tile<Steps::template P, NSB + 1, LA>(begin, operand, mfma, valu);
   };
@@ -657,6 +660,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
             p_item(ec, stc);
         });
       }
+      // the copies of a later tile, spread over the whole stream
       static_for<OPS>([&](auto cc) {
         if constexpr (spread_slot(decltype(cc)::value, OPS, 0, NMT) == gm)
           Copy::part(decltype(cc)::value, K, V, fkv0, p.Nkv, sKV[fbuf], w, lane);
