@@ -158,6 +158,12 @@ EDGE = [
     (3, 6, 3, 65, 200, 64, "bf16", True),
     (1, 2, 1, 513, 31, 64, "fp16", False),
     (1, 4, 4, 64, 128, 128, "fp16", True),
+    # around the 256-row key blocks of the dK/dV kernel and query blocks of the dQ pass
+    (1, 4, 1, 257, 513, 128, "bf16", True),
+    (2, 8, 2, 255, 255, 64, "fp16", True),
+    (1, 2, 1, 1000, 300, 128, "fp16", True),  # N_q > N_kv: the first 700 rows see no key
+    (1, 2, 2, 64, 700, 128, "bf16", False),
+    (1, 8, 8, 320, 320, 128, "bf16", True),
 ]
 
 
