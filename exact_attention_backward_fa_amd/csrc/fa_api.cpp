@@ -15,7 +15,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 WorkspaceLayout workspace_layout(const Problem& pb, bool atomic_dq) {
   const size_t rows = (size_t)pb.B * pb.Hq * pb.Nq;
   WorkspaceLayout L;
-  L.delta_off = 0;
+  L.ndelta_off = 0;
   L.lse2_off = align256(rows * sizeof(float));
   L.dqacc_off = L.lse2_off + align256(rows * sizeof(float));
   L.total = L.dqacc_off + (atomic_dq ? align256(rows * pb.d * sizeof(float)) : 0);
@@ -184,7 +184,7 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.delta = L.total ? reinterpret_cast<float*>(ws + L.delta_off) : nullptr;
+  a.ndelta = L.total ? reinterpret_cast<float*>(ws + L.ndelta_off) : nullptr;
   a.lse2 = L.total ? reinterpret_cast<float*>(ws + L.lse2_off) : nullptr;
   a.dq_acc = (L.total && atomic) ? reinterpret_cast<float*>(ws + L.dqacc_off) : nullptr;
 

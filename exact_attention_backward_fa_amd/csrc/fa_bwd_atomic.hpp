@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_atomic_kernel(BwdParams p) {
     // waves issue OPS copies per fetch and can share one vmcnt immediate
     const size_t r = qbase + min(q0 + lane, p.Nq - 1);
     dma4(p.lse2 + r, sL[buf]);
-    dma4(p.delta + r, sD[buf]);
+    dma4(p.ndelta + r, sD[buf]);
   };
 
   // dQ_i += scale * dS_i K_j for the query tile staged in sdST[buf]; wave w takes
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_atomic_kernel(BwdParams p) {
       }
       const float pv = fast_exp2(x);
       sp[t][i] = pv;
-      dp[t][i] = pv * (dp[t][i] - D4[j4][e]);
+      dp[t][i] = pv * (dp[t][i] + D4[j4][e]);  // sD holds -D
     };
     auto load_lse = [&](int t) {
 #pragma unroll

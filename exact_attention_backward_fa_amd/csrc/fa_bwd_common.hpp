@@ -16,7 +16,7 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* delta;
+  float* ndelta;  // minus D per query row
   float* lse2;
   float* dq_acc;
   int B, Hq, Hkv, Nq, Nkv, G, off;  // off = Nkv - Nq (bottom-right causal offset)
@@ -35,7 +35,7 @@ inline BwdParams make_params(const BwdArgs& a) {
   p.dq = static_cast<uint16_t*>(a.dq);
   p.dk = static_cast<uint16_t*>(a.dk);
   p.dv = static_cast<uint16_t*>(a.dv);
-  p.delta = a.delta;
+  p.ndelta = a.ndelta;
   p.lse2 = a.lse2;
   p.dq_acc = a.dq_acc;
   p.B = a.pb.B;

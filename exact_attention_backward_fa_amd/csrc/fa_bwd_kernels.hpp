@@ -174,7 +174,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 #pragma unroll
   for (int o = LPR / 2; o > 0; o >>= 1) s += __shfl_xor(s, o);
   if (row < p.rows && part == 0) {
-    p.delta[row] = s;
+    p.ndelta[row] = -s;
     const float L = p.lse[row];
     p.lse2[row] = (L == -INFINITY) ? INFINITY : L * kLog2e;
   }
@@ -269,37 +269,37 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   // Iteration it copies tile it + NBUF - 1 into the buffer of iteration it - 1; past
   // the last tile it copies the last tile again, into a buffer no later iteration
   // reads, so every iteration issues the same OPS copies per wave (spread over its
-  // MFMA stream) and one vmcnt bound covers them.  Rows past N_q repeat row N_q-1
-  // and are masked in the math.  Every wave copies LSE and D (identical bytes to
-  // the same place).
+  // MFMA stream) and one vmcnt bound covers them.  Waves 0-1 copy the Q tile,
+  // waves 2-3 the dO tile, each through a buffer resource based at the tile's first
+  // row; rows past N_q arrive as zeros (and are masked in the math).  Every wave
+  // copies LSE and -D (identical bytes to the same place).
+  using Copy = PadPairDma<D, BM>;
   struct Src {
-    const uint16_t* q;
-    const uint16_t* d;
-    const float* l;
-    const float* dl;
-    int q0;
+    i32x4 t, l, d;  // this wave's Q or dO tile; LSE*log2e; -D
   };
+  const uint16_t* __restrict__ tsrc = w < 2 ? p.q : p.dout;
   auto src_of = [&](int fit) {
     fit = min(fit, n_it - 1);
     const int hh = fit % p.G;
-    const size_t qbase = ((size_t)b * p.Hq + (size_t)hk * p.G + hh) * (size_t)p.Nq;
+    const int q0 = (nqt - 1 - fit / p.G) * BM;
+    const size_t row = ((size_t)b * p.Hq + (size_t)hk * p.G + hh) * (size_t)p.Nq + q0;
+    const int left = p.Nq - q0;
     Src sr;
-    sr.q0 = (nqt - 1 - fit / p.G) * BM;
-    sr.q = p.q + qbase * D;
-    sr.d = p.dout + qbase * D;
-    const size_t r = qbase + min(sr.q0 + lane, p.Nq - 1);
-    sr.l = p.lse2 + r;
-    sr.dl = p.delta + r;
+    sr.t = buf_rsrc(tsrc + row * D, left * D * 2);
+    sr.l = buf_rsrc(p.lse2 + row, left * 4);
+    sr.d = buf_rsrc(p.ndelta + row, left * 4);
     return sr;
   };
-  using Copy = PadPairCopy<D, BM>;
+  int voff[Copy::PER_WAVE];
+#pragma unroll
+  for (int c = 0; c < Copy::PER_WAVE; ++c) voff[c] = Copy::src_offset(c, w, lane);
   auto copy_part = [&](int c, const Src& sr, int buf) {
     if (c < Copy::PER_WAVE)
-      Copy::part(c, sr.q, sr.d, sr.q0, p.Nq, sQdO[buf], w, lane);
+      bdma16(voff[c], sr.t, lds_u32(sQdO[buf]) + Copy::lds_offset(c, w));
     else if (c == Copy::PER_WAVE)
-      dma4(sr.l, sLD[buf][0]);
+      bdma4(4 * lane, sr.l, lds_u32(sLD[buf][0]));
     else
-      dma4(sr.dl, sLD[buf][1]);
+      bdma4(4 * lane, sr.d, lds_u32(sLD[buf][1]));
   };
   auto copy_all = [&](const Src& sr, int buf) {
     for (int c = 0; c < OPS; ++c) copy_part(c, sr, buf);
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     f32x4 sc[4];         // S, then P, of the current sub-block, per key tile
     f32x4 dp[4];         // dP, then dS
     u32x4 pa[2], sa[2];  // P^T and dS^T A operands, per key half
-    f32x4 lq, dn;        // LSE*log2e and D of the current sub-block's rows
+    f32x4 lq, dn;        // LSE*log2e and -D of the current sub-block's rows
     const int keyl = kvw + l16;    // key of this lane's column in key tile 0
     const int qrow = q0 + 4 * j4;  // query row of element 0 in sub-block 0
 
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         sa[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
       } else {
         constexpr int x = e < 8 ? e : e - 1, kt = x / 4, i = x % 4;
-        dp[kt][i] = sc[kt][i] * (dp[kt][i] - dn[i]);
+        dp[kt][i] = sc[kt][i] * dp[kt][i];  // dP - D: the dP product starts from -D
       }
     };
 
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       } else if constexpr (k == 2) {
         constexpr int s = loc / 4, kt = loc % 4;
         if constexpr (s == 0)
-          dp[kt] = Mx<DT>::first16(op, vb[kt][s]);
+          dp[kt] = Mx<DT>::first16c(op, vb[kt][s], dn);
         else
           Mx<DT>::acc16(dp[kt], op, vb[kt][s]);
       } else {
@@ -531,7 +531,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   const uint16_t* __restrict__ V = p.v + kbase * D;
 
   u32x4 qb[4][NK], db[4][NK];
-  float lq[4], dl[4];
+  float lq[4];
+  f32x4 nd[4];  // -D of the lane's query, in every element: where dP^T starts
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int q = qw + 16 * t + l16;
@@ -542,7 +543,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       db[t][s] = ok ? ld16(p.dout + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
     }
     lq[t] = ok ? p.lse2[qbase + q] : INFINITY;
-    dl[t] = ok ? p.delta[qbase + q] : 0.f;
+    const float x = ok ? p.ndelta[qbase + q] : 0.f;
+    nd[t][0] = x;
+    nd[t][1] = x;
+    nd[t][2] = x;
+    nd[t][3] = x;
   }
   f32x16 acc[2][NK];
 #pragma unroll
@@ -564,13 +569,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 
   // Iteration kt copies key/value tile kt + NBUF - 1 into the buffer of iteration
   // kt - 1 (past the last tile, the last tile again, into a buffer no later
-  // iteration reads), OPS copies per wave spread over its MFMA stream.
-  using Copy = PadPairCopy<D, BN>;
+  // iteration reads), OPS copies per wave spread over its MFMA stream.  Waves 0-1
+  // copy the K tile, waves 2-3 the V tile, through a buffer resource based at the
+  // tile's first row; rows past N_kv arrive as zeros (and are masked in the math).
+  using Copy = PadPairDma<D, BN>;
+  const uint16_t* __restrict__ tsrc = w < 2 ? K : V;
+  auto src_of = [&](int kt) {
+    const int k0 = min(kt, nkt - 1) * BN;
+    return buf_rsrc(tsrc + (size_t)k0 * D, (p.Nkv - k0) * D * 2);
+  };
+  int voff[Copy::PER_WAVE];
+#pragma unroll
+  for (int c = 0; c < Copy::PER_WAVE; ++c) voff[c] = Copy::src_offset(c, w, lane);
+  auto copy_part = [&](int c, const i32x4& sr, int buf) {
+    bdma16(voff[c], sr, lds_u32(sKV[buf]) + Copy::lds_offset(c, w));
+  };
   auto copy_all = [&](int kt, int buf) {
-    dma_pad_pair<D, BN>(K, V, min(kt, nkt - 1) * BN, p.Nkv, sKV[buf], w, lane);
+    const i32x4 sr = src_of(kt);
+#pragma unroll
+    for (int c = 0; c < OPS; ++c) copy_part(c, sr, buf);
   };
 
-  auto compute = [&](int cur, auto mask_c, int kv0, int fkv0, int fbuf) {
+  auto compute = [&](int cur, auto mask_c, int kv0, const i32x4& fsrc, int fbuf) {
     constexpr bool MASK = decltype(mask_c)::value;
     const uint16_t* Kt = sKV[cur];
     const uint16_t* Vt = Kt + BN * RS;
@@ -588,7 +608,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         da[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
       } else {
         constexpr int x = e < 8 ? e : e - 1, t = x / 4, i = x % 4;
-        dp[t][i] = sc[cp][t][i] * (dp[t][i] - dl[t]);
+        dp[t][i] = sc[cp][t][i] * dp[t][i];  // dP - D: the dP^T product starts from -D
       }
     };
     auto p_item = [&](auto ec, auto st_c) {
@@ -638,7 +658,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       } else {
         constexpr int s = loc / 4, t = loc % 4;
         if constexpr (s == 0)
-          dp[t] = Mx<DT>::first16(op, db[t][s]);
+          dp[t] = Mx<DT>::first16c(op, db[t][s], nd[t]);
         else
           Mx<DT>::acc16(dp[t], op, db[t][s]);
       }
@@ -663,7 +683,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       // the copies of a later tile, spread over the whole stream
       static_for<OPS>([&](auto cc) {
         if constexpr (spread_slot(decltype(cc)::value, OPS, 0, NMT) == gm)
-          Copy::part(decltype(cc)::value, K, V, fkv0, p.Nkv, sKV[fbuf], w, lane);
+          copy_part(decltype(cc)::value, fsrc, fbuf);
       });
     };
     run_tile<Steps::template P, NSB + 1, LA>(begin, operand, mfma, valu);
@@ -689,10 +709,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
     for (; kt < end; ++kt) {
       const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
-      const int fkv0 = min(kt + NBUF - 1, nkt - 1) * BN;
+      const i32x4 fsrc = src_of(kt + NBUF - 1);
       if constexpr (VAR == 0) copy_all(kt + NBUF - 1, fbuf);
-      if constexpr (VAR == 1) compute(cur, std::true_type(), kt * BN, fkv0, fbuf);
-      if constexpr (VAR == 2) compute(cur, std::false_type(), kt * BN, fkv0, fbuf);
+      if constexpr (VAR == 1) compute(cur, std::true_type(), kt * BN, fsrc, fbuf);
+      if constexpr (VAR == 2) compute(cur, std::false_type(), kt * BN, fsrc, fbuf);
       // tile kt+1 must have landed; this iteration's copies may stay in flight
       wait_vmem_n<OPS * (NBUF - 2)>();
       lds_barrier();

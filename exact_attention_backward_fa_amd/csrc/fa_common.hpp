@@ -119,6 +119,12 @@ template <> struct Mx<0> {
   static __device__ __forceinline__ void acc16(f32x4& c, const u32x4& a, const u32x4& b) {
     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
   }
+  // first16 with the accumulator starting at c instead of zero
+  static __device__ __forceinline__ f32x4 first16c(const u32x4& a, const u32x4& b, const f32x4& c) {
+    f32x4 d;
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+  }
 };
 template <> struct Mx<1> {
   static __device__ __forceinline__ void acc32(f32x16& c, const u32x4& a, const u32x4& b) {
@@ -131,6 +137,12 @@ template <> struct Mx<1> {
   }
   static __device__ __forceinline__ void acc16(f32x4& c, const u32x4& a, const u32x4& b) {
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
+  }
+  // first16 with the accumulator starting at c instead of zero
+  static __device__ __forceinline__ f32x4 first16c(const u32x4& a, const u32x4& b, const f32x4& c) {
+    f32x4 d;
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %3" : "=&v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
   }
 };
 // Enough idle issue cycles for any MFMA in flight to retire (a 32x32x16 MFMA is
@@ -294,6 +306,42 @@ __device__ __forceinline__ void dma4(const void* gsrc, void* lds_base) {
                : "v"(gsrc), "s"(lds_addr(lds_base))
                : "memory", "m0");
 }
+
+// Copies through a buffer resource.  A raw resource (no stride, no swizzle) covers
+// `bytes` bytes from `base`; a lane whose offset lies at or past the end reads
+// zeros, and an LDS-destination load writes those zeros.  With the resource based
+// at the first row of a tile and sized to the rows that exist, each lane's offset
+// is the same for every tile, so the offsets stay in registers, a copy costs no
+// vector ALU work and rows past the end arrive as zeros.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 buf_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = 0x00020000;  // 32-bit data format: plain byte addressing on gfx9-family parts
+  return r;
+}
+// LDS byte address of a wave-uniform pointer into LDS (the low half of its
+// generic address), in a scalar register.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
+}
+// 16 bytes per lane from rsrc + voff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void bdma16(int voff, const i32x4& rsrc, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
+}
+// 4 bytes per lane from rsrc + voff into LDS at lds + 4 * lane.
+__device__ __forceinline__ void bdma4(int voff, const i32x4& rsrc, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
+}
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // s_waitcnt vmcnt(N): at most N vector-memory operations of this wave still
@@ -393,6 +441,27 @@ struct PadPairCopy {
     const int r = slot / T::GR, gr = slot % T::GR;
     const int rr = min(row0 + r, n_rows - 1);
     dma16(src + (size_t)rr * D + 8 * (gr < T::NG ? gr : 0), lds + blk * 64 * 8);
+  }
+};
+
+// The same pair fill through buffer resources (one per source tile, based at the
+// tile's first row): instruction c of wave w copies LDS bytes lds_offset(c, w) ..
+// +1023 of the pair from byte src_offset(c, w, lane) of its tile, per lane.  Rows
+// past the resource's end arrive as zeros.
+template <int D, int ROWS>
+struct PadPairDma {
+  using T = PadTile<D>;
+  static constexpr int TILE_SLOTS = ROWS * T::GR;
+  static constexpr int PER_WAVE = 2 * TILE_SLOTS / (4 * 64);
+  static_assert(PER_WAVE * 4 * 64 == 2 * TILE_SLOTS && TILE_SLOTS % (2 * 64) == 0,
+                "each wave must copy whole instructions within one tile");
+  static __device__ __forceinline__ int src_offset(int c, int w, int lane) {
+    const int slot = (PER_WAVE * w + c) * 64 + lane - (w < 2 ? 0 : TILE_SLOTS);
+    const int r = slot / T::GR, gr = slot % T::GR;
+    return 2 * (r * D + 8 * (gr < T::NG ? gr : 0));
+  }
+  static __device__ __forceinline__ uint32_t lds_offset(int c, int w) {
+    return (uint32_t)((PER_WAVE * w + c) * 1024);
   }
 };
 

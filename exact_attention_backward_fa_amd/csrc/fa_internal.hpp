@@ -35,14 +35,14 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;   // [B*Hq*Nq]      rowsum(dO o O)
+  float* ndelta;  // [B*Hq*Nq]      -rowsum(dO o O)
   float* lse2;    // [B*Hq*Nq]      LSE * log2(e), +inf for rows that see no key
   float* dq_acc;  // [B*Hq*Nq*d]    float32 dQ accumulator (atomic path only)
 };
 
 // Workspace carve-up; every region starts on a 256-byte boundary.
 struct WorkspaceLayout {
-  size_t delta_off, lse2_off, dqacc_off, total;
+  size_t ndelta_off, lse2_off, dqacc_off, total;
 };
 WorkspaceLayout workspace_layout(const Problem& pb, bool atomic_dq);
 
