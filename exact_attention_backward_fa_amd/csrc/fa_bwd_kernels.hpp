@@ -48,6 +48,9 @@ struct StepPlan {
   static constexpr bool first(int m) { return local(m) % gsz(stage(m)) == 0; }
   static constexpr int op_stage(int o) { return o < O1 ? 0 : o < O2 ? 1 : o < O3 ? 2 : 3; }
   static constexpr int op_local(int o) { return o - obase(op_stage(o)); }
+  // issue time of MFMA m in units of a 16x16x32 MFMA: the odd stages of both
+  // kernels' plans are 32x32x16 products (twice the cycles)
+  static constexpr int weight(int m) { return (stage(m) & 1) ? 2 : 1; }
 };
 
 // floor(a / b) for b > 0 and any sign of a.
@@ -57,6 +60,20 @@ __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b :
 // evenly over the MFMA slots [a, b).
 __host__ __device__ constexpr int spread_slot(int e, int E, int a, int b) {
   return a + (e * (b - a)) / E;
+}
+// The same, spread evenly over the issue time of the slots (Plan::weight): a
+// 32x32x16 MFMA hides about twice the VALU work of a 16x16x32 one.
+template <class Plan>
+__host__ __device__ constexpr int spread_timed(int e, int E, int a, int b) {
+  int total = 0;
+  for (int m = a; m < b; ++m) total += Plan::weight(m);
+  const int u = (e * total) / E;  // item e starts at time unit u
+  int acc = 0;
+  for (int m = a; m < b; ++m) {
+    acc += Plan::weight(m);
+    if (acc > u) return m;
+  }
+  return b - 1;
 }
 
 // The steps 0..NS-1 of one tile (StepPlan PlanOf<st> each) concatenated into one
@@ -130,6 +147,42 @@ __device__ __forceinline__ void run_tile(FBegin&& begin, FOp&& operand, FMma&& m
   });
 }
 
+// run_tile for a stream of tiles: the first LA operands of this tile come from
+// `carry`, and the first LA operands of the next tile are read into it
+// (next(o) reads operand o of the next tile) as the lookahead passes the end of
+// this one, so no tile starts by waiting for its operands.
+template <template <int> class PlanOf, int NS, int LA, class FBegin, class FOp, class FNext, class FMma,
+          class FValu>
+__device__ __forceinline__ void run_tile_carry(u32x4 (&carry)[LA], FBegin&& begin, FOp&& operand,
+                                               FNext&& next, FMma&& mfma, FValu&& valu) {
+  using T = typename TileStreamOf<PlanOf, std::make_integer_sequence<int, NS>>::type;
+  using ic0 = std::integral_constant<int, 0>;
+  static_assert(T::NOP >= LA, "a tile must have at least LA operands");
+  u32x4 ops[LA + 1];
+  static_for<LA>([&](auto oc) { ops[decltype(oc)::value] = carry[decltype(oc)::value]; });
+  begin(ic0());
+  static_for<T::NM>([&](auto mc) {
+    constexpr int m = decltype(mc)::value, st = T::step_of_m(m), ml = m - T::m_base(st);
+    using P = PlanOf<st>;
+    using stc = std::integral_constant<int, st>;
+    if constexpr (ml == 0 && st > 0) begin(stc());
+    constexpr int o = T::o_base(st) + P::op_of(ml);
+    if constexpr (P::first(ml)) {
+      constexpr int o2 = o + LA;
+      if constexpr (o2 < T::NOP) {
+        constexpr int st2 = T::step_of_o(o2);
+        ops[o2 % (LA + 1)] = operand(std::integral_constant<int, st2>(),
+                                     std::integral_constant<int, o2 - T::o_base(st2)>());
+      } else {
+        carry[o2 - T::NOP] = next(std::integral_constant<int, o2 - T::NOP>());
+      }
+    }
+    mfma(stc(), std::integral_constant<int, ml>(), ops[o % (LA + 1)]);
+    valu(stc(), std::integral_constant<int, ml>(), mc);
+    sched_fence();
+  });
+}
+
 template <template <int> class PlanOf, int NS>
 constexpr int tile_mfmas() {
   return TileStreamOf<PlanOf, std::make_integer_sequence<int, NS>>::type::NM;
@@ -137,16 +190,22 @@ constexpr int tile_mfmas() {
 
 // Step plans.  dK/dV: S_st | dK_{st-1} | dP_st | dV_st over NSB sub-blocks plus a
 // final dK step.  dQ: S^T_st | dQ_{st-1} | dP^T_st, plus a final dQ step.
-template <int NK, int NSB>
+// The gradient product of a tile's last sub-block is issued in step 0 of the next
+// tile (and after the last tile by a flush step), so every step of a tile has the
+// same shape.
+template <int NK>
 struct DkdvSteps {
   template <int ST>
-  using P = StepPlan<ST < NSB ? NK : 0, 4, (ST > 0) ? NK : 0, 2, ST < NSB ? NK : 0, 4,
-                     ST < NSB ? NK : 0, 2>;
+  using P = StepPlan<NK, 4, NK, 2, NK, 4, NK, 2>;
+  template <int ST>
+  using Flush = StepPlan<0, 4, NK, 2, 0, 4, 0, 2>;
 };
-template <int NK, int NSB>
+template <int NK>
 struct DqSteps {
   template <int ST>
-  using P = StepPlan<ST < NSB ? NK : 0, 4, (ST > 0) ? NK : 0, 2, ST < NSB ? NK : 0, 4, 0, 1>;
+  using P = StepPlan<NK, 4, NK, 2, NK, 4, 0, 1>;
+  template <int ST>
+  using Flush = StepPlan<0, 4, NK, 2, 0, 4, 0, 1>;
 };
 
 // ---------------------------------------------------------------------------
@@ -277,44 +336,75 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   struct Src {
     i32x4 t, l, d;  // this wave's Q or dO tile; LSE*log2e; -D
   };
-  const uint16_t* __restrict__ tsrc = w < 2 ? p.q : p.dout;
-  auto src_of = [&](int fit) {
-    fit = min(fit, n_it - 1);
-    const int hh = fit % p.G;
-    const int q0 = (nqt - 1 - fit / p.G) * BM;
-    const size_t row = ((size_t)b * p.Hq + (size_t)hk * p.G + hh) * (size_t)p.Nq + q0;
-    const int left = p.Nq - q0;
+  // Fetch cursor: the tile of iteration c_fit (query head c_hh of the group, rows
+  // from the start of this wave's Q or dO tile, LSE and -D), moved one iteration
+  // per copy round and held at the last one.
+  const size_t row0 = ((size_t)b * p.Hq + (size_t)hk * p.G) * (size_t)p.Nq + (size_t)(nqt - 1) * BM;
+  const uint16_t* __restrict__ ct = (w < 2 ? p.q : p.dout) + row0 * D;
+  const float* __restrict__ cl = p.lse2 + row0;
+  const float* __restrict__ cd = p.ndelta + row0;
+  int c_left = p.Nq - (nqt - 1) * BM, c_hh = 0, c_fit = 0;
+  auto src_now = [&]() {
     Src sr;
-    sr.t = buf_rsrc(tsrc + row * D, left * D * 2);
-    sr.l = buf_rsrc(p.lse2 + row, left * 4);
-    sr.d = buf_rsrc(p.ndelta + row, left * 4);
+    sr.t = buf_rsrc(ct, c_left * D * 2);
+    sr.l = buf_rsrc(cl, c_left * 4);
+    sr.d = buf_rsrc(cd, c_left * 4);
     return sr;
+  };
+  auto advance = [&]() {
+    if (c_fit < n_it - 1) {
+      ++c_fit;
+      if (++c_hh == p.G) {  // next (earlier) query tile of head 0
+        c_hh = 0;
+        const ptrdiff_t back = (ptrdiff_t)(p.G - 1) * p.Nq + BM;
+        ct -= back * D;
+        cl -= back;
+        cd -= back;
+        c_left += BM;
+      } else {
+        ct += (size_t)p.Nq * D;
+        cl += p.Nq;
+        cd += p.Nq;
+      }
+    }
   };
   int voff[Copy::PER_WAVE];
 #pragma unroll
   for (int c = 0; c < Copy::PER_WAVE; ++c) voff[c] = Copy::src_offset(c, w, lane);
-  auto copy_part = [&](int c, const Src& sr, int buf) {
-    if (c < Copy::PER_WAVE)
-      bdma16(voff[c], sr.t, lds_u32(sQdO[buf]) + Copy::lds_offset(c, w));
-    else if (c == Copy::PER_WAVE)
+  const uint32_t wave_off = Copy::lds_wave_offset(w);
+  auto copy_part = [&](auto cc, const Src& sr, int buf) {
+    constexpr int c = decltype(cc)::value;
+    if constexpr (c < Copy::PER_WAVE)
+      bdma16<Copy::template lds_offset<c>>(voff[c], sr.t, lds_u32(sQdO[buf]) + wave_off);
+    else if constexpr (c == Copy::PER_WAVE)
       bdma4(4 * lane, sr.l, lds_u32(sLD[buf][0]));
     else
       bdma4(4 * lane, sr.d, lds_u32(sLD[buf][1]));
   };
   auto copy_all = [&](const Src& sr, int buf) {
-    for (int c = 0; c < OPS; ++c) copy_part(c, sr, buf);
+    static_for<OPS>([&](auto cc) { copy_part(cc, sr, buf); });
   };
 
-  auto compute = [&](int cur, auto mask_c, int q0, const Src& fsrc, int fbuf) {
+  // Carried from tile to tile: the first LA operands of the next tile, and the
+  // dS^T operands of the last sub-block, whose dK product is issued in step 0 of
+  // the next tile with Q read from the previous buffer (zero before the first tile,
+  // which makes that product a no-op).
+  u32x4 carry[LA];
+  u32x4 sa[2] = {zero_u4(), zero_u4()};  // dS^T A operands, per key half
+  int prev = 0;                          // buffer of the previous tile
+
+  auto compute = [&](int cur, int nxt, auto mask_c, int q0, const Src& fsrc, int fbuf) {
     constexpr bool MASK = decltype(mask_c)::value;
     const uint16_t* Qt = sQdO[cur];
     const uint16_t* dOt = Qt + BM * RS;
+    const uint16_t* Qp = sQdO[prev];
+    const uint16_t* Qn = sQdO[nxt];
     const float* Lt = sLD[cur][0];
     const float* Dtl = Lt + BM;
-    f32x4 sc[4];         // S, then P, of the current sub-block, per key tile
-    f32x4 dp[4];         // dP, then dS
-    u32x4 pa[2], sa[2];  // P^T and dS^T A operands, per key half
-    f32x4 lq, dn;        // LSE*log2e and -D of the current sub-block's rows
+    f32x4 sc[4];    // S, then P, of the current sub-block, per key tile
+    f32x4 dp[4];    // dP, then dS
+    u32x4 pa[2];    // P^T A operands, per key half
+    f32x4 lq, dn;   // LSE*log2e and -D of the current sub-block's rows
     const int keyl = kvw + l16;    // key of this lane's column in key tile 0
     const int qrow = q0 + 4 * j4;  // query row of element 0 in sub-block 0
 
@@ -348,12 +438,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
     };
 
-    using Steps = DkdvSteps<NK, NSB>;
+    using Steps = DkdvSteps<NK>;
     auto begin = [&](auto stc) {
       constexpr int st = decltype(stc)::value;
-      if constexpr (st < NSB) {
-        lq = *reinterpret_cast<const f32x4*>(&Lt[16 * st + 4 * j4]);
-        dn = *reinterpret_cast<const f32x4*>(&Dtl[16 * st + 4 * j4]);
+      lq = *reinterpret_cast<const f32x4*>(&Lt[16 * st + 4 * j4]);
+      dn = *reinterpret_cast<const f32x4*>(&Dtl[16 * st + 4 * j4]);
+      if constexpr (st == 2) {
+        // Mid-tile: every wave is past step 0 (its last reads of the previous
+        // buffer) and, once its own copies have landed, the next tile is complete,
+        // so the copies of steps 2-3 may refill the previous buffer.
+        wait_vmem();
+        tile_barrier();
       }
     };
     auto operand = [&](auto stc, auto oc) -> u32x4 {
@@ -363,14 +458,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       if constexpr (k == 0) {
         return pad_row16<D>(Qt, 16 * st + l16, 4 * n + j4);
       } else if constexpr (k == 1) {
-        const int k0 = 16 * (st - 1) + 8 * g;
-        return pad_tr_operand<D>(Qt, k0, k0 + 4, 32 * n + 16 * hi16);
+        if constexpr (st == 0) {
+          const int k0 = 16 * (NSB - 1) + 8 * g;
+          return pad_tr_operand<D>(Qp, k0, k0 + 4, 32 * n + 16 * hi16);
+        } else {
+          const int k0 = 16 * (st - 1) + 8 * g;
+          return pad_tr_operand<D>(Qt, k0, k0 + 4, 32 * n + 16 * hi16);
+        }
       } else if constexpr (k == 2) {
         return pad_row16<D>(dOt, 16 * st + l16, 4 * n + j4);
       } else {
         const int k0 = 16 * st + 8 * g;
         return pad_tr_operand<D>(dOt, k0, k0 + 4, 32 * n + 16 * hi16);
       }
+    };
+    auto next = [&](auto oc) -> u32x4 {  // operand oc of the next tile: S of sub-block 0
+      return pad_row16<D>(Qn, l16, 4 * decltype(oc)::value + j4);
     };
     auto mfma = [&](auto stc, auto mc, const u32x4& op) {
       constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
@@ -397,27 +500,44 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
     };
     auto valu = [&](auto stc, auto mc, auto gc) {
-      constexpr int st = decltype(stc)::value, m = decltype(mc)::value, gm = decltype(gc)::value;
+      constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
       using Plan = typename Steps::template P<st>;
-      if constexpr (st < NSB) {
-        static_for<18>([&](auto ec) {
-          if constexpr (spread_slot(decltype(ec)::value, 18, Plan::B1, Plan::B3) == m)
-            p_item(ec, stc);
-          if constexpr (spread_slot(decltype(ec)::value, 18, Plan::B3, Plan::NM) == m)
-            ds_item(ec);
-        });
-      }
-      // The copies of a later tile ride on the score stages (S_st), which carry no
-      // other VALU work: copy c goes after MFMA slot(c) of the concatenated S stages.
-      (void)gm;
-      if constexpr (st < NSB && m < Plan::B1) {
+      (void)gc;
+      static_for<18>([&](auto ec) {
+        if constexpr (spread_timed<Plan>(decltype(ec)::value, 18, Plan::B1, Plan::B3) == m)
+          p_item(ec, stc);
+        if constexpr (spread_slot(decltype(ec)::value, 18, Plan::B3, Plan::NM) == m)
+          ds_item(ec);
+      });
+      // The copies of a later tile ride on the score stages (S_st) of steps 2-3,
+      // which carry no other VALU work.
+      if constexpr (st >= 2 && m < Plan::B1) {
         static_for<OPS>([&](auto cc) {
-          if constexpr (spread_slot(decltype(cc)::value, OPS, 0, NSB * Plan::B1) == st * Plan::B1 + m)
-            copy_part(decltype(cc)::value, fsrc, fbuf);
+          if constexpr (spread_slot(decltype(cc)::value, OPS, 0, 2 * Plan::B1) == (st - 2) * Plan::B1 + m)
+            copy_part(cc, fsrc, fbuf);
         });
       }
     };
-    run_tile<Steps::template P, NSB + 1, LA>(begin, operand, mfma, valu);
+    run_tile_carry<Steps::template P, NSB, LA>(carry, begin, operand, next, mfma, valu);
+  };
+  // dK of the last computed tile's last sub-block (a no-op when no tile was
+  // computed; the operand is zeroed when no tile was even copied).
+  auto flush = [&]() {
+    const uint16_t* Qp = sQdO[prev];
+    using Steps = DkdvSteps<NK>;
+    run_tile<Steps::template Flush, 1, LA>(
+        [&](auto) {},
+        [&](auto, auto oc) -> u32x4 {
+          constexpr int n = decltype(oc)::value;
+          const int k0 = 16 * (NSB - 1) + 8 * g;
+          const u32x4 op = pad_tr_operand<D>(Qp, k0, k0 + 4, 32 * n + 16 * hi16);
+          return n_it > 0 ? op : zero_u4();
+        },
+        [&](auto, auto mc, const u32x4& op) {
+          constexpr int loc = decltype(mc)::value, n = loc / 2, h = loc % 2;
+          Mx<DT>::acc32(dk[h][n], sa[h], op);
+        },
+        [&](auto, auto, auto) {});
   };
 
   // This wave's split of the query tiles (each phase runs one variant of the
@@ -441,32 +561,42 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     qe = max(qb, min(nqt, p.Nq / BM));
   }
   if (n_it > 0) {
-    static_for<NBUF - 1>([&](auto bc) { copy_all(src_of(decltype(bc)::value), decltype(bc)::value); });
+    static_for<NBUF - 1>([&](auto bc) {
+      copy_all(src_now(), decltype(bc)::value);
+      advance();
+    });
     wait_vmem_n<OPS * (NBUF - 2)>();
     lds_barrier();
   }
-  // iteration it works on buffer it % NBUF while tile it+NBUF-1 is copied into the
-  // buffer of iteration it-1
+  static_for<LA>([&](auto oc) {
+    carry[decltype(oc)::value] = pad_row16<D>(sQdO[0], l16, 4 * decltype(oc)::value + j4);
+  });
+  // Iteration it works on buffer it % NBUF; from its middle on it copies tile
+  // it + NBUF - 1 into the buffer of iteration it - 1.
   int it = 0, cur = 0;
   auto phase = [&](int qt_low, auto variant) {  // down to query tile qt_low
     constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
     for (const int end = (nqt - qt_low) * p.G; it < end; ++it) {
-      const Src fsrc = src_of(it + NBUF - 1);
+      const Src fsrc = src_now();  // tile it + NBUF - 1
+      advance();
       const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
+      const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
       const int q0 = (nqt - 1 - it / p.G) * BM;
-      if constexpr (VAR == 0) copy_all(fsrc, fbuf);
-      if constexpr (VAR == 1) compute(cur, std::true_type(), q0, fsrc, fbuf);
-      if constexpr (VAR == 2) compute(cur, std::false_type(), q0, fsrc, fbuf);
-      // tile it+1 must have landed; the copies issued in this iteration may stay in
-      // flight
-      wait_vmem_n<OPS * (NBUF - 2)>();
-      lds_barrier();
-      cur = cur == NBUF - 1 ? 0 : cur + 1;
+      if constexpr (VAR == 0) {
+        wait_vmem();
+        tile_barrier();
+        copy_all(fsrc, fbuf);
+      }
+      if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), q0, fsrc, fbuf);
+      if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), q0, fsrc, fbuf);
+      prev = cur;
+      cur = nxt;
     }
   };
   phase(qe, std::integral_constant<int, 1>());
   phase(qb, std::integral_constant<int, 2>());
   phase(qa, std::integral_constant<int, 1>());
+  flush();
   phase(qt_begin, std::integral_constant<int, 0>());
   wait_vmem();  // no copy may land in LDS after the workgroup ends
 
@@ -581,22 +711,37 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   int voff[Copy::PER_WAVE];
 #pragma unroll
   for (int c = 0; c < Copy::PER_WAVE; ++c) voff[c] = Copy::src_offset(c, w, lane);
-  auto copy_part = [&](int c, const i32x4& sr, int buf) {
-    bdma16(voff[c], sr, lds_u32(sKV[buf]) + Copy::lds_offset(c, w));
+  const uint32_t wave_off = Copy::lds_wave_offset(w);
+  auto copy_part = [&](auto cc, const i32x4& sr, int buf) {
+    constexpr int c = decltype(cc)::value;
+    bdma16<Copy::template lds_offset<c>>(voff[c], sr, lds_u32(sKV[buf]) + wave_off);
   };
   auto copy_all = [&](int kt, int buf) {
     const i32x4 sr = src_of(kt);
-#pragma unroll
-    for (int c = 0; c < OPS; ++c) copy_part(c, sr, buf);
+    static_for<OPS>([&](auto cc) { copy_part(cc, sr, buf); });
   };
 
-  auto compute = [&](int cur, auto mask_c, int kv0, const i32x4& fsrc, int fbuf) {
+  // Carried from tile to tile: the first LA operands of the next tile, and P^T and
+  // dP^T of the last sub-block (sc[1], dp), whose dS^T and dQ product run in
+  // step 0 of the next tile with K read from the previous buffer (zero before the
+  // first tile, which makes that product a no-op).
+  u32x4 carry[LA];
+  f32x4 sc[2][4];  // S^T, then P^T, of sub-block st in sc[st % 2], per query tile
+  f32x4 dp[4];     // dP^T, then dS^T, of the sub-block being finished
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    sc[1][t] = zero4();
+    dp[t] = zero4();
+  }
+  int prev = 0;  // buffer of the previous tile
+
+  auto compute = [&](int cur, int nxt, auto mask_c, int kv0, const i32x4& fsrc, int fbuf) {
     constexpr bool MASK = decltype(mask_c)::value;
     const uint16_t* Kt = sKV[cur];
     const uint16_t* Vt = Kt + BN * RS;
-    f32x4 sc[2][4];  // S^T, then P^T, of sub-block st in sc[st % 2], per query tile
-    f32x4 dp[4];     // dP^T, then dS^T, of the sub-block being finished
-    u32x4 da[2];     // dS A operands, per query half
+    const uint16_t* Kp = sKV[prev];
+    const uint16_t* Kn = sKV[nxt];
+    u32x4 da[2];  // dS A operands, per query half
     const int krow = kv0 + 4 * j4;  // key of element 0 in sub-block 0
     const int qcol = qw + l16;      // query of this lane's column in query tile 0
 
@@ -622,12 +767,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       sc[cs][t][i] = fast_exp2(v);
     };
 
-    using Steps = DqSteps<NK, NSB>;
-    // the final step has no scores to hide dS of the last sub-block under
+    using Steps = DqSteps<NK>;
     auto begin = [&](auto stc) {
       constexpr int st = decltype(stc)::value;
-      if constexpr (st == NSB)
-        static_for<18>([&](auto ec) { ds_item(ec, std::integral_constant<int, (st + 1) & 1>()); });
+      if constexpr (st == 2) {
+        // Mid-tile: every wave is past step 0 (its last reads of the previous
+        // buffer) and, once its own copies have landed, the next tile is complete,
+        // so the copies of steps 2-3 may refill the previous buffer.
+        wait_vmem();
+        tile_barrier();
+      }
     };
     auto operand = [&](auto stc, auto oc) -> u32x4 {
       constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
@@ -636,11 +785,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       if constexpr (k == 0) {
         return pad_row16<D>(Kt, 16 * st + l16, 4 * n + j4);
       } else if constexpr (k == 1) {
-        const int k0 = 16 * (st - 1) + 8 * g;
-        return pad_tr_operand<D>(Kt, k0, k0 + 4, 32 * n + 16 * hi16);
+        if constexpr (st == 0) {
+          const int k0 = 16 * (NSB - 1) + 8 * g;
+          return pad_tr_operand<D>(Kp, k0, k0 + 4, 32 * n + 16 * hi16);
+        } else {
+          const int k0 = 16 * (st - 1) + 8 * g;
+          return pad_tr_operand<D>(Kt, k0, k0 + 4, 32 * n + 16 * hi16);
+        }
       } else {
         return pad_row16<D>(Vt, 16 * st + l16, 4 * n + j4);
       }
+    };
+    auto next = [&](auto oc) -> u32x4 {  // operand oc of the next tile: S^T of sub-block 0
+      return pad_row16<D>(Kn, l16, 4 * decltype(oc)::value + j4);
     };
     auto mfma = [&](auto stc, auto mc, const u32x4& op) {
       constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cs = st & 1;
@@ -663,30 +820,55 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
           Mx<DT>::acc16(dp[t], op, db[t][s]);
       }
     };
-    constexpr int NMT = tile_mfmas<Steps::template P, NSB + 1>();
+    constexpr int NMT = tile_mfmas<Steps::template P, NSB>();
+    constexpr int M2 = NMT / 2;  // first MFMA of step 2
     auto valu = [&](auto stc, auto mc, auto gc) {
       constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cp = (st + 1) & 1;
       constexpr int gm = decltype(gc)::value;
       using Plan = typename Steps::template P<st>;
-      if constexpr (st < NSB && st > 0) {
-        static_for<18>([&](auto ec) {
-          if constexpr (spread_slot(decltype(ec)::value, 18, 0, Plan::B1) == m)
-            ds_item(ec, std::integral_constant<int, cp>());
-        });
-      }
-      if constexpr (st < NSB) {
-        static_for<16>([&](auto ec) {
-          if constexpr (spread_slot(decltype(ec)::value, 16, Plan::B1, Plan::NM) == m)
-            p_item(ec, stc);
-        });
-      }
-      // the copies of a later tile, spread over the whole stream
+      // dS of the previous sub-block (of the previous tile in step 0) under S^T_st
+      static_for<18>([&](auto ec) {
+        if constexpr (spread_slot(decltype(ec)::value, 18, 0, Plan::B1) == m)
+          ds_item(ec, std::integral_constant<int, cp>());
+      });
+      static_for<16>([&](auto ec) {
+        if constexpr (spread_timed<Plan>(decltype(ec)::value, 16, Plan::B1, Plan::NM) == m)
+          p_item(ec, stc);
+      });
+      // the copies of a later tile, spread over steps 2-3
       static_for<OPS>([&](auto cc) {
-        if constexpr (spread_slot(decltype(cc)::value, OPS, 0, NMT) == gm)
-          copy_part(decltype(cc)::value, fsrc, fbuf);
+        if constexpr (spread_slot(decltype(cc)::value, OPS, M2, NMT) == gm)
+          copy_part(cc, fsrc, fbuf);
       });
     };
-    run_tile<Steps::template P, NSB + 1, LA>(begin, operand, mfma, valu);
+    run_tile_carry<Steps::template P, NSB, LA>(carry, begin, operand, next, mfma, valu);
+  };
+  // dS and dQ of the last computed tile's last sub-block (a no-op when no tile was
+  // computed; the operand is zeroed when no tile was even copied).
+  auto flush = [&]() {
+    const uint16_t* Kp = sKV[prev];
+    u32x4 da[2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dp[t][i] = sc[1][t][i] * dp[t][i];
+    }
+    da[0] = c16_pair_to_a32(pack_c4<DT>(dp[0]), pack_c4<DT>(dp[1]));
+    da[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
+    using Steps = DqSteps<NK>;
+    run_tile<Steps::template Flush, 1, LA>(
+        [&](auto) {},
+        [&](auto, auto oc) -> u32x4 {
+          constexpr int n = decltype(oc)::value;
+          const int k0 = 16 * (NSB - 1) + 8 * g;
+          const u32x4 op = pad_tr_operand<D>(Kp, k0, k0 + 4, 32 * n + 16 * hi16);
+          return nkt > 0 ? op : zero_u4();
+        },
+        [&](auto, auto mc, const u32x4& op) {
+          constexpr int loc = decltype(mc)::value, n = loc / 2, hh = loc % 2;
+          Mx<DT>::acc32(acc[hh][n], da[hh], op);
+        },
+        [&](auto, auto, auto) {});
   };
 
   // This wave's split of the key tiles (one variant of the math per loop):
@@ -704,23 +886,32 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     wait_vmem_n<OPS * (NBUF - 2)>();
     lds_barrier();
   }
+  static_for<LA>([&](auto oc) {
+    carry[decltype(oc)::value] = pad_row16<D>(sKV[0], l16, 4 * decltype(oc)::value + j4);
+  });
+  // Iteration kt works on buffer kt % NBUF; from its middle on it copies tile
+  // kt + NBUF - 1 into the buffer of iteration kt - 1.
   int kt = 0, cur = 0;
   auto phase = [&](int end, auto variant) {
     constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
     for (; kt < end; ++kt) {
       const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
+      const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
       const i32x4 fsrc = src_of(kt + NBUF - 1);
-      if constexpr (VAR == 0) copy_all(kt + NBUF - 1, fbuf);
-      if constexpr (VAR == 1) compute(cur, std::true_type(), kt * BN, fsrc, fbuf);
-      if constexpr (VAR == 2) compute(cur, std::false_type(), kt * BN, fsrc, fbuf);
-      // tile kt+1 must have landed; this iteration's copies may stay in flight
-      wait_vmem_n<OPS * (NBUF - 2)>();
-      lds_barrier();
-      cur = cur == NBUF - 1 ? 0 : cur + 1;
+      if constexpr (VAR == 0) {
+        wait_vmem();
+        tile_barrier();
+        copy_all(kt + NBUF - 1, fbuf);
+      }
+      if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), kt * BN, fsrc, fbuf);
+      if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), kt * BN, fsrc, fbuf);
+      prev = cur;
+      cur = nxt;
     }
   };
   phase(n_un, std::integral_constant<int, 2>());
   phase(n_vis, std::integral_constant<int, 1>());
+  flush();
   phase(nkt, std::integral_constant<int, 0>());
   wait_vmem();  // no copy may land in LDS after the workgroup ends
 

@@ -328,12 +328,13 @@ __device__ __forceinline__ i32x4 buf_rsrc(const void* base, int bytes) {
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(p));
 }
-// 16 bytes per lane from rsrc + voff into LDS at lds + 16 * lane.
+// 16 bytes per lane from rsrc + voff into LDS at lds + OFF + 16 * lane.
+template <int OFF>
 __device__ __forceinline__ void bdma16(int voff, const i32x4& rsrc, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+  asm volatile("s_add_u32 m0, %2, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(lds)
-               : "memory", "m0");
+               : "v"(voff), "s"(rsrc), "s"(lds), "n"(OFF)
+               : "memory", "m0", "scc");
 }
 // 4 bytes per lane from rsrc + voff into LDS at lds + 4 * lane.
 __device__ __forceinline__ void bdma4(int voff, const i32x4& rsrc, uint32_t lds) {
@@ -359,6 +360,14 @@ __device__ __forceinline__ void wait_vmem_n() {
 // copies it needs (wait_vmem / wait_vmem_n), then for its own LDS stores; the asm
 // clobbers keep the compiler from moving memory accesses across, and the
 // LDS-only acquire fence orders later LDS reads after the barrier.
+// Workgroup barrier that leaves the wave's LDS reads in flight: for barriers whose
+// purpose is ordering the direct-to-LDS copies of other buffers (the operand
+// reads outstanding at the barrier are of the buffer being computed on).
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -445,9 +454,10 @@ struct PadPairCopy {
 };
 
 // The same pair fill through buffer resources (one per source tile, based at the
-// tile's first row): instruction c of wave w copies LDS bytes lds_offset(c, w) ..
-// +1023 of the pair from byte src_offset(c, w, lane) of its tile, per lane.  Rows
-// past the resource's end arrive as zeros.
+// tile's first row): instruction c of wave w copies LDS bytes
+// lds_wave_offset(w) + lds_offset<c> .. +1023 of the pair from byte
+// src_offset(c, w, lane) of its tile, per lane.  Rows past the resource's end
+// arrive as zeros.
 template <int D, int ROWS>
 struct PadPairDma {
   using T = PadTile<D>;
@@ -460,9 +470,10 @@ struct PadPairDma {
     const int r = slot / T::GR, gr = slot % T::GR;
     return 2 * (r * D + 8 * (gr < T::NG ? gr : 0));
   }
-  static __device__ __forceinline__ uint32_t lds_offset(int c, int w) {
-    return (uint32_t)((PER_WAVE * w + c) * 1024);
-  }
+  // (the wave index enters at run time, the instruction index as an immediate)
+  static __device__ __forceinline__ uint32_t lds_wave_offset(int w) { return (uint32_t)(PER_WAVE * w * 1024); }
+  template <int C>
+  static constexpr int lds_offset = C * 1024;
 };
 
 template <int D, int ROWS>
