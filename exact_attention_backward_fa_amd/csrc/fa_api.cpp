@@ -18,7 +18,8 @@ WorkspaceLayout workspace_layout(const Problem& pb, bool atomic_dq) {
   L.ndelta_off = 0;
   L.lse2_off = align256(rows * sizeof(float));
   L.dqacc_off = L.lse2_off + align256(rows * sizeof(float));
-  L.total = L.dqacc_off + (atomic_dq ? align256(rows * pb.d * sizeof(float)) : 0);
+  L.sched_off = L.dqacc_off + (atomic_dq ? align256(rows * pb.d * sizeof(float)) : 0);
+  L.total = L.sched_off + 256;
   if (rows == 0) L.total = 0;
   return L;
 }
@@ -187,6 +188,7 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
   a.ndelta = L.total ? reinterpret_cast<float*>(ws + L.ndelta_off) : nullptr;
   a.lse2 = L.total ? reinterpret_cast<float*>(ws + L.lse2_off) : nullptr;
   a.dq_acc = (L.total && atomic) ? reinterpret_cast<float*>(ws + L.dqacc_off) : nullptr;
+  a.sched = L.total ? reinterpret_cast<int*>(ws + L.sched_off) : nullptr;
 
   hipStream_t s = (hipStream_t)stream;
   if (nrows == 0 && nk == 0) return FA_OK;  // nothing to compute; no HIP call at all

@@ -3,6 +3,9 @@
 // fa_bwd_inst.hip) and the float32 -> dtype conversion of the atomic dQ buffer.
 #include "fa_bwd_common.hpp"
 
+#include <stdlib.h>
+#include <string.h>
+
 namespace fa {
 
 // ---------------------------------------------------------------------------
@@ -21,6 +24,26 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
   st16(dst + 8 * i, r);
 }
 
+
+// ---------------------------------------------------------------------------
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev] = n;
+  return n;
+}
+
+bool sched_static() {
+  static const int v = [] {
+    const char* e = getenv("FA_SCHED");
+    return (e && strcmp(e, "static") == 0) ? 1 : 0;
+  }();
+  return v != 0;
+}
 
 // ---------------------------------------------------------------------------
 // Dispatch.

@@ -208,6 +208,38 @@ struct DqSteps {
   using Flush = StepPlan<0, 4, NK, 2, 0, 4, 0, 1>;
 };
 
+// Store a wave's 64 x D block held in 32x32 accumulators (acc[h][n] element i of
+// lane (l32, g) is row 32h + crow_of(i, g), column 32n + l32), times `scale`, to
+// rows row0.. of a row-major [*, D] tensor; rows at or past n_rows are skipped.
+// The block goes through the wave's own LDS staging area (64 rows of D + 8
+// elements): 2-byte writes in the accumulator layout, then 16-byte row reads, so
+// the global stores are whole 16-byte pieces of consecutive rows instead of 2-byte
+// pieces of 64 rows each.
+template <int DT, int D>
+__device__ __forceinline__ void store_block64(const f32x16 (&acc)[2][D / 32], float scale,
+                                              uint16_t* __restrict__ stage, uint16_t* __restrict__ dst,
+                                              int row0, int n_rows, int lane) {
+  constexpr int SS = D + 8;     // staging row stride (elements)
+  constexpr int CPR = D / 8;    // 16-byte pieces per row
+  constexpr int RPI = 64 / CPR; // rows per read instruction
+  const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int n = 0; n < D / 32; ++n) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        stage[(32 * h + crow_of(i, g)) * SS + 32 * n + l32] = Dt<DT>::one(acc[h][n][i] * scale);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 64 / RPI; ++k) {
+    const int r = k * RPI + lane / CPR, c = lane % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * SS + 8 * c);
+    if (row0 + r < n_rows) st16(dst + (size_t)(row0 + r) * D + 8 * c, v);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Row preprocess.  D/8 lanes share a row; each lane reads 16 bytes of O and dO.
 template <int DT, int D, bool ZERO_DQ>
@@ -216,6 +248,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   constexpr int RPB = 256 / LPR;
   const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
+  if (blockIdx.x == 0 && threadIdx.x < 32 && p.sched) p.sched[threadIdx.x] = 0;
   float s = 0.f;
   if (row < p.rows) {
     const u32x4 a = ld16(p.o + row * D + part * 8);
@@ -274,348 +307,347 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   // Q and dO of a buffer are one padded tile pair (as are LSE and D), so both are
   // read through the same per-lane address registers with immediate offsets.
   __shared__ __attribute__((aligned(16))) uint16_t sQdO[NBUF][2 * BM * RS];
+  static_assert(NBUF * 2 * BM * RS >= 4 * 64 * (D + 8), "the output staging must fit the tile buffers");
   __shared__ __attribute__((aligned(16))) float sLD[NBUF][2][BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int l16 = lane & 15, j4 = lane >> 4;  // 16x16 tiles: column, row group
   const int l32 = lane & 31, g = lane >> 5, hi16 = j4 & 1;
-  int rank, head;
-  map_block(blockIdx.x, p.B * p.Hkv, rank, head);
-  const int b = head / p.Hkv, hk = head % p.Hkv;
-  const int kv0 = rank * BN;  // rank 0 = first key block = most query rows under the mask
-  const int kvw = kv0 + KW * w;
-  const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
+  __shared__ int s_item;
+  const WorkQueue wq(p.sched, p.B * p.Hkv, (p.Nkv + BN - 1) / BN);
+  long long ticket = tid == 0 ? wq.first() : 0;
+  for (;;) {
+    if (tid == 0) s_item = wq.resolve(ticket);
+    lds_barrier();  // also: the previous item's staging reads are done
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item < 0 || item >= wq.n_items) break;
+    if (tid == 0) ticket = wq.next_ticket(ticket);
+    const int rank = item / wq.n_heads, head = item % wq.n_heads;
+    const int b = head / p.Hkv, hk = head % p.Hkv;
+    const int kv0 = rank * BN;  // rank 0 = first key block = most query rows under the mask
+    const int kvw = kv0 + KW * w;
+    const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
 
-  u32x4 kb[4][NK], vb[4][NK];
-  {
-    const uint16_t* __restrict__ K = p.k + kbase * D;
-    const uint16_t* __restrict__ V = p.v + kbase * D;
+    u32x4 kb[4][NK], vb[4][NK];
+    {
+      const uint16_t* __restrict__ K = p.k + kbase * D;
+      const uint16_t* __restrict__ V = p.v + kbase * D;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int key = kvw + 16 * kt + l16;
+      for (int kt = 0; kt < 4; ++kt) {
+        const int key = kvw + 16 * kt + l16;
 #pragma unroll
-      for (int s = 0; s < NK; ++s) {
-        kb[kt][s] = key < p.Nkv ? ld16(K + (size_t)key * D + 32 * s + 8 * j4) : zero_u4();
-        vb[kt][s] = key < p.Nkv ? ld16(V + (size_t)key * D + 32 * s + 8 * j4) : zero_u4();
-      }
-    }
-  }
-  // The tile copies below are not visible to the compiler's wait counting, so the
-  // register preloads are waited for here, before the first copy is issued.
-  wait_vmem();
-  f32x16 dk[2][NK], dv[2][NK];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int n = 0; n < NK; ++n) {
-      dk[h][n] = zero16();
-      dv[h][n] = zero16();
-    }
-  }
-
-  const int q_begin = CAUSAL ? max(0, kv0 - p.off) : 0;
-  const int nqt = (p.Nq + BM - 1) / BM;
-  const int qt_begin = q_begin < p.Nq ? q_begin / BM : nqt;
-  const int per_head = nqt - qt_begin;
-  const int n_it = p.G * per_head;
-
-  // Iteration it covers query tile nqt - 1 - it / G of query head it % G of the
-  // group: tiles outer, last tile first, heads inner.  Every key block of a group
-  // starts at the last query tile, so the workgroups of a group resident together
-  // read the same query tiles at about the same time and share them through L2.
-  //
-  // Iteration it copies tile it + NBUF - 1 into the buffer of iteration it - 1; past
-  // the last tile it copies the last tile again, into a buffer no later iteration
-  // reads, so every iteration issues the same OPS copies per wave (spread over its
-  // MFMA stream) and one vmcnt bound covers them.  Waves 0-1 copy the Q tile,
-  // waves 2-3 the dO tile, each through a buffer resource based at the tile's first
-  // row; rows past N_q arrive as zeros (and are masked in the math).  Every wave
-  // copies LSE and -D (identical bytes to the same place).
-  using Copy = PadPairDma<D, BM>;
-  struct Src {
-    i32x4 t, l, d;  // this wave's Q or dO tile; LSE*log2e; -D
-  };
-  // Fetch cursor: the tile of iteration c_fit (query head c_hh of the group, rows
-  // from the start of this wave's Q or dO tile, LSE and -D), moved one iteration
-  // per copy round and held at the last one.
-  const size_t row0 = ((size_t)b * p.Hq + (size_t)hk * p.G) * (size_t)p.Nq + (size_t)(nqt - 1) * BM;
-  const uint16_t* __restrict__ ct = (w < 2 ? p.q : p.dout) + row0 * D;
-  const float* __restrict__ cl = p.lse2 + row0;
-  const float* __restrict__ cd = p.ndelta + row0;
-  int c_left = p.Nq - (nqt - 1) * BM, c_hh = 0, c_fit = 0;
-  auto src_now = [&]() {
-    Src sr;
-    sr.t = buf_rsrc(ct, c_left * D * 2);
-    sr.l = buf_rsrc(cl, c_left * 4);
-    sr.d = buf_rsrc(cd, c_left * 4);
-    return sr;
-  };
-  auto advance = [&]() {
-    if (c_fit < n_it - 1) {
-      ++c_fit;
-      if (++c_hh == p.G) {  // next (earlier) query tile of head 0
-        c_hh = 0;
-        const ptrdiff_t back = (ptrdiff_t)(p.G - 1) * p.Nq + BM;
-        ct -= back * D;
-        cl -= back;
-        cd -= back;
-        c_left += BM;
-      } else {
-        ct += (size_t)p.Nq * D;
-        cl += p.Nq;
-        cd += p.Nq;
-      }
-    }
-  };
-  int voff[Copy::PER_WAVE];
-#pragma unroll
-  for (int c = 0; c < Copy::PER_WAVE; ++c) voff[c] = Copy::src_offset(c, w, lane);
-  const uint32_t wave_off = Copy::lds_wave_offset(w);
-  auto copy_part = [&](auto cc, const Src& sr, int buf) {
-    constexpr int c = decltype(cc)::value;
-    if constexpr (c < Copy::PER_WAVE)
-      bdma16<Copy::template lds_offset<c>>(voff[c], sr.t, lds_u32(sQdO[buf]) + wave_off);
-    else if constexpr (c == Copy::PER_WAVE)
-      bdma4(4 * lane, sr.l, lds_u32(sLD[buf][0]));
-    else
-      bdma4(4 * lane, sr.d, lds_u32(sLD[buf][1]));
-  };
-  auto copy_all = [&](const Src& sr, int buf) {
-    static_for<OPS>([&](auto cc) { copy_part(cc, sr, buf); });
-  };
-
-  // Carried from tile to tile: the first LA operands of the next tile, and the
-  // dS^T operands of the last sub-block, whose dK product is issued in step 0 of
-  // the next tile with Q read from the previous buffer (zero before the first tile,
-  // which makes that product a no-op).
-  u32x4 carry[LA];
-  u32x4 sa[2] = {zero_u4(), zero_u4()};  // dS^T A operands, per key half
-  int prev = 0;                          // buffer of the previous tile
-
-  auto compute = [&](int cur, int nxt, auto mask_c, int q0, const Src& fsrc, int fbuf) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    const uint16_t* Qt = sQdO[cur];
-    const uint16_t* dOt = Qt + BM * RS;
-    const uint16_t* Qp = sQdO[prev];
-    const uint16_t* Qn = sQdO[nxt];
-    const float* Lt = sLD[cur][0];
-    const float* Dtl = Lt + BM;
-    f32x4 sc[4];    // S, then P, of the current sub-block, per key tile
-    f32x4 dp[4];    // dP, then dS
-    u32x4 pa[2];    // P^T A operands, per key half
-    f32x4 lq, dn;   // LSE*log2e and -D of the current sub-block's rows
-    const int keyl = kvw + l16;    // key of this lane's column in key tile 0
-    const int qrow = q0 + 4 * j4;  // query row of element 0 in sub-block 0
-
-    // P_st item e of 18: 16 elements, then after each key half its operand
-    auto p_item = [&](auto ec, auto st_c) {
-      constexpr int e = decltype(ec)::value, st = decltype(st_c)::value;
-      if constexpr (e == 8) {
-        pa[0] = c16_pair_to_a32(pack_c4<DT>(sc[0]), pack_c4<DT>(sc[1]));
-      } else if constexpr (e == 17) {
-        pa[1] = c16_pair_to_a32(pack_c4<DT>(sc[2]), pack_c4<DT>(sc[3]));
-      } else {
-        constexpr int x = e < 8 ? e : e - 1, kt = x / 4, i = x % 4;
-        float v = sc[kt][i] * p.scale_log2 - lq[i];
-        if constexpr (MASK) {
-          const int key = keyl + 16 * kt, q = qrow + 16 * st + i;
-          if (key >= p.Nkv || q >= p.Nq || (CAUSAL && key > q + p.off)) v = -INFINITY;
+        for (int s = 0; s < NK; ++s) {
+          kb[kt][s] = key < p.Nkv ? ld16(K + (size_t)key * D + 32 * s + 8 * j4) : zero_u4();
+          vb[kt][s] = key < p.Nkv ? ld16(V + (size_t)key * D + 32 * s + 8 * j4) : zero_u4();
         }
-        sc[kt][i] = fast_exp2(v);
       }
-    };
-    // dS_st item e of 18, same order
-    auto ds_item = [&](auto ec) {
-      constexpr int e = decltype(ec)::value;
-      if constexpr (e == 8) {
-        sa[0] = c16_pair_to_a32(pack_c4<DT>(dp[0]), pack_c4<DT>(dp[1]));
-      } else if constexpr (e == 17) {
-        sa[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
-      } else {
-        constexpr int x = e < 8 ? e : e - 1, kt = x / 4, i = x % 4;
-        dp[kt][i] = sc[kt][i] * dp[kt][i];  // dP - D: the dP product starts from -D
+    }
+    f32x16 dk[2][NK], dv[2][NK];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int n = 0; n < NK; ++n) {
+        dk[h][n] = zero16();
+        dv[h][n] = zero16();
       }
-    };
+    }
 
-    using Steps = DkdvSteps<NK>;
-    auto begin = [&](auto stc) {
-      constexpr int st = decltype(stc)::value;
-      lq = *reinterpret_cast<const f32x4*>(&Lt[16 * st + 4 * j4]);
-      dn = *reinterpret_cast<const f32x4*>(&Dtl[16 * st + 4 * j4]);
-      if constexpr (st == 2) {
-        // Mid-tile: every wave is past step 0 (its last reads of the previous
-        // buffer) and, once its own copies have landed, the next tile is complete,
-        // so the copies of steps 2-3 may refill the previous buffer.
-        wait_vmem();
-        tile_barrier();
-      }
+    const int q_begin = CAUSAL ? max(0, kv0 - p.off) : 0;
+    const int nqt = (p.Nq + BM - 1) / BM;
+    const int qt_begin = q_begin < p.Nq ? q_begin / BM : nqt;
+    const int per_head = nqt - qt_begin;
+    const int n_it = p.G * per_head;
+
+    // Iteration it covers query tile nqt - 1 - it / G of query head it % G of the
+    // group: tiles outer, last tile first, heads inner.  Every key block of a group
+    // starts at the last query tile, so the workgroups of a group resident together
+    // read the same query tiles at about the same time and share them through L2.
+    //
+    // Iteration it copies tile it + NBUF - 1 into the buffer of iteration it - 1; past
+    // the last tile it copies the last tile again, into a buffer no later iteration
+    // reads, so every iteration issues the same OPS copies per wave (spread over its
+    // MFMA stream) and one vmcnt bound covers them.  Waves 0-1 copy the Q tile,
+    // waves 2-3 the dO tile, each through a buffer resource based at the tile's first
+    // row; rows past N_q arrive as zeros (and are masked in the math).  Every wave
+    // copies LSE and -D (identical bytes to the same place).
+    using Copy = PadPairDma<D, BM>;
+    struct Src {
+      i32x4 t, l, d;  // this wave's Q or dO tile; LSE*log2e; -D
     };
-    auto operand = [&](auto stc, auto oc) -> u32x4 {
-      constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
-      using Plan = typename Steps::template P<st>;
-      constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
-      if constexpr (k == 0) {
-        return pad_row16<D>(Qt, 16 * st + l16, 4 * n + j4);
-      } else if constexpr (k == 1) {
-        if constexpr (st == 0) {
-          const int k0 = 16 * (NSB - 1) + 8 * g;
-          return pad_tr_operand<D>(Qp, k0, k0 + 4, 32 * n + 16 * hi16);
+    // Fetch cursor: the tile of iteration c_fit (query head c_hh of the group, rows
+    // from the start of this wave's Q or dO tile, LSE and -D), moved one iteration
+    // per copy round and held at the last one.
+    const size_t row0 = ((size_t)b * p.Hq + (size_t)hk * p.G) * (size_t)p.Nq + (size_t)(nqt - 1) * BM;
+    const uint16_t* __restrict__ ct = (w < 2 ? p.q : p.dout) + row0 * D;
+    const float* __restrict__ cl = p.lse2 + row0;
+    const float* __restrict__ cd = p.ndelta + row0;
+    int c_left = p.Nq - (nqt - 1) * BM, c_hh = 0, c_fit = 0;
+    auto src_now = [&]() {
+      Src sr;
+      sr.t = buf_rsrc(ct, c_left * D * 2);
+      sr.l = buf_rsrc(cl, c_left * 4);
+      sr.d = buf_rsrc(cd, c_left * 4);
+      return sr;
+    };
+    auto advance = [&]() {
+      if (c_fit < n_it - 1) {
+        ++c_fit;
+        if (++c_hh == p.G) {  // next (earlier) query tile of head 0
+          c_hh = 0;
+          const ptrdiff_t back = (ptrdiff_t)(p.G - 1) * p.Nq + BM;
+          ct -= back * D;
+          cl -= back;
+          cd -= back;
+          c_left += BM;
         } else {
-          const int k0 = 16 * (st - 1) + 8 * g;
-          return pad_tr_operand<D>(Qt, k0, k0 + 4, 32 * n + 16 * hi16);
+          ct += (size_t)p.Nq * D;
+          cl += p.Nq;
+          cd += p.Nq;
         }
-      } else if constexpr (k == 2) {
-        return pad_row16<D>(dOt, 16 * st + l16, 4 * n + j4);
-      } else {
-        const int k0 = 16 * st + 8 * g;
-        return pad_tr_operand<D>(dOt, k0, k0 + 4, 32 * n + 16 * hi16);
       }
     };
-    auto next = [&](auto oc) -> u32x4 {  // operand oc of the next tile: S of sub-block 0
-      return pad_row16<D>(Qn, l16, 4 * decltype(oc)::value + j4);
+    int voff[Copy::PER_WAVE];
+#pragma unroll
+    for (int c = 0; c < Copy::PER_WAVE; ++c) voff[c] = Copy::src_offset(c, w, lane);
+    const uint32_t wave_off = Copy::lds_wave_offset(w);
+    auto copy_part = [&](auto cc, const Src& sr, int buf) {
+      constexpr int c = decltype(cc)::value;
+      if constexpr (c < Copy::PER_WAVE)
+        bdma16<Copy::template lds_offset<c>>(voff[c], sr.t, lds_u32(sQdO[buf]) + wave_off);
+      else if constexpr (c == Copy::PER_WAVE)
+        bdma4(4 * lane, sr.l, lds_u32(sLD[buf][0]));
+      else
+        bdma4(4 * lane, sr.d, lds_u32(sLD[buf][1]));
     };
-    auto mfma = [&](auto stc, auto mc, const u32x4& op) {
-      constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
-      using Plan = typename Steps::template P<st>;
-      constexpr int k = Plan::stage(m), loc = Plan::local(m);
-      if constexpr (k == 0) {
-        constexpr int s = loc / 4, kt = loc % 4;
-        if constexpr (s == 0)
-          sc[kt] = Mx<DT>::first16(op, kb[kt][s]);
-        else
-          Mx<DT>::acc16(sc[kt], op, kb[kt][s]);
-      } else if constexpr (k == 1) {
-        constexpr int n = loc / 2, h = loc % 2;
-        Mx<DT>::acc32(dk[h][n], sa[h], op);
-      } else if constexpr (k == 2) {
-        constexpr int s = loc / 4, kt = loc % 4;
-        if constexpr (s == 0)
-          dp[kt] = Mx<DT>::first16c(op, vb[kt][s], dn);
-        else
-          Mx<DT>::acc16(dp[kt], op, vb[kt][s]);
-      } else {
-        constexpr int n = loc / 2, h = loc % 2;
-        Mx<DT>::acc32(dv[h][n], pa[h], op);
-      }
+    auto copy_all = [&](const Src& sr, int buf) {
+      static_for<OPS>([&](auto cc) { copy_part(cc, sr, buf); });
     };
-    auto valu = [&](auto stc, auto mc, auto gc) {
-      constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
-      using Plan = typename Steps::template P<st>;
-      (void)gc;
-      static_for<18>([&](auto ec) {
-        if constexpr (spread_timed<Plan>(decltype(ec)::value, 18, Plan::B1, Plan::B3) == m)
-          p_item(ec, stc);
-        if constexpr (spread_slot(decltype(ec)::value, 18, Plan::B3, Plan::NM) == m)
-          ds_item(ec);
-      });
-      // The copies of a later tile ride on the score stages (S_st) of steps 2-3,
-      // which carry no other VALU work.
-      if constexpr (st >= 2 && m < Plan::B1) {
-        static_for<OPS>([&](auto cc) {
-          if constexpr (spread_slot(decltype(cc)::value, OPS, 0, 2 * Plan::B1) == (st - 2) * Plan::B1 + m)
-            copy_part(cc, fsrc, fbuf);
-        });
-      }
-    };
-    run_tile_carry<Steps::template P, NSB, LA>(carry, begin, operand, next, mfma, valu);
-  };
-  // dK of the last computed tile's last sub-block (a no-op when no tile was
-  // computed; the operand is zeroed when no tile was even copied).
-  auto flush = [&]() {
-    const uint16_t* Qp = sQdO[prev];
-    using Steps = DkdvSteps<NK>;
-    run_tile<Steps::template Flush, 1, LA>(
-        [&](auto) {},
-        [&](auto, auto oc) -> u32x4 {
-          constexpr int n = decltype(oc)::value;
-          const int k0 = 16 * (NSB - 1) + 8 * g;
-          const u32x4 op = pad_tr_operand<D>(Qp, k0, k0 + 4, 32 * n + 16 * hi16);
-          return n_it > 0 ? op : zero_u4();
-        },
-        [&](auto, auto mc, const u32x4& op) {
-          constexpr int loc = decltype(mc)::value, n = loc / 2, h = loc % 2;
+
+    // Carried from tile to tile: the first LA operands of the next tile, and the
+    // dS^T operands of the last sub-block, whose dK product is issued in step 0 of
+    // the next tile with Q read from the previous buffer (zero before the first tile,
+    // which makes that product a no-op).
+    u32x4 carry[LA];
+    u32x4 sa[2] = {zero_u4(), zero_u4()};  // dS^T A operands, per key half
+    int prev = 0;                          // buffer of the previous tile
+
+    auto compute = [&](int cur, int nxt, auto mask_c, int q0, const Src& fsrc, int fbuf) {
+      constexpr bool MASK = decltype(mask_c)::value;
+      const uint16_t* Qt = sQdO[cur];
+      const uint16_t* dOt = Qt + BM * RS;
+      const uint16_t* Qp = sQdO[prev];
+      const uint16_t* Qn = sQdO[nxt];
+      const float* Lt = sLD[cur][0];
+      const float* Dtl = Lt + BM;
+      f32x4 sc[4];    // S, then P, of the current sub-block, per key tile
+      f32x4 dp[4];    // dP, then dS
+      u32x4 pa[2];    // P^T A operands, per key half
+      f32x4 lq, dn;   // LSE*log2e and -D of the current sub-block's rows
+      const int keyl = kvw + l16;    // key of this lane's column in key tile 0
+      const int qrow = q0 + 4 * j4;  // query row of element 0 in sub-block 0
+
+      // P_st item e of 18: 16 elements, then after each key half its operand
+      auto p_item = [&](auto ec, auto st_c) {
+        constexpr int e = decltype(ec)::value, st = decltype(st_c)::value;
+        if constexpr (e == 8) {
+          pa[0] = c16_pair_to_a32(pack_c4<DT>(sc[0]), pack_c4<DT>(sc[1]));
+        } else if constexpr (e == 17) {
+          pa[1] = c16_pair_to_a32(pack_c4<DT>(sc[2]), pack_c4<DT>(sc[3]));
+        } else {
+          constexpr int x = e < 8 ? e : e - 1, kt = x / 4, i = x % 4;
+          float v = sc[kt][i] * p.scale_log2 - lq[i];
+          if constexpr (MASK) {
+            const int key = keyl + 16 * kt, q = qrow + 16 * st + i;
+            if (key >= p.Nkv || q >= p.Nq || (CAUSAL && key > q + p.off)) v = -INFINITY;
+          }
+          sc[kt][i] = fast_exp2(v);
+        }
+      };
+      // dS_st item e of 18, same order
+      auto ds_item = [&](auto ec) {
+        constexpr int e = decltype(ec)::value;
+        if constexpr (e == 8) {
+          sa[0] = c16_pair_to_a32(pack_c4<DT>(dp[0]), pack_c4<DT>(dp[1]));
+        } else if constexpr (e == 17) {
+          sa[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
+        } else {
+          constexpr int x = e < 8 ? e : e - 1, kt = x / 4, i = x % 4;
+          dp[kt][i] = sc[kt][i] * dp[kt][i];  // dP - D: the dP product starts from -D
+        }
+      };
+
+      using Steps = DkdvSteps<NK>;
+      auto begin = [&](auto stc) {
+        constexpr int st = decltype(stc)::value;
+        lq = *reinterpret_cast<const f32x4*>(&Lt[16 * st + 4 * j4]);
+        dn = *reinterpret_cast<const f32x4*>(&Dtl[16 * st + 4 * j4]);
+        if constexpr (st == 2) {
+          // Mid-tile: every wave is past step 0 (its last reads of the previous
+          // buffer) and, once its own copies have landed, the next tile is complete,
+          // so the copies of steps 2-3 may refill the previous buffer.
+          wait_vmem();
+          tile_barrier();
+        }
+      };
+      auto operand = [&](auto stc, auto oc) -> u32x4 {
+        constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
+        using Plan = typename Steps::template P<st>;
+        constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
+        if constexpr (k == 0) {
+          return pad_row16<D>(Qt, 16 * st + l16, 4 * n + j4);
+        } else if constexpr (k == 1) {
+          if constexpr (st == 0) {
+            const int k0 = 16 * (NSB - 1) + 8 * g;
+            return pad_tr_operand<D>(Qp, k0, k0 + 4, 32 * n + 16 * hi16);
+          } else {
+            const int k0 = 16 * (st - 1) + 8 * g;
+            return pad_tr_operand<D>(Qt, k0, k0 + 4, 32 * n + 16 * hi16);
+          }
+        } else if constexpr (k == 2) {
+          return pad_row16<D>(dOt, 16 * st + l16, 4 * n + j4);
+        } else {
+          const int k0 = 16 * st + 8 * g;
+          return pad_tr_operand<D>(dOt, k0, k0 + 4, 32 * n + 16 * hi16);
+        }
+      };
+      auto next = [&](auto oc) -> u32x4 {  // operand oc of the next tile: S of sub-block 0
+        return pad_row16<D>(Qn, l16, 4 * decltype(oc)::value + j4);
+      };
+      auto mfma = [&](auto stc, auto mc, const u32x4& op) {
+        constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
+        using Plan = typename Steps::template P<st>;
+        constexpr int k = Plan::stage(m), loc = Plan::local(m);
+        if constexpr (k == 0) {
+          constexpr int s = loc / 4, kt = loc % 4;
+          if constexpr (s == 0)
+            sc[kt] = Mx<DT>::first16(op, kb[kt][s]);
+          else
+            Mx<DT>::acc16(sc[kt], op, kb[kt][s]);
+        } else if constexpr (k == 1) {
+          constexpr int n = loc / 2, h = loc % 2;
           Mx<DT>::acc32(dk[h][n], sa[h], op);
-        },
-        [&](auto, auto, auto) {});
-  };
-
-  // This wave's split of the query tiles (each phase runs one variant of the
-  // math, so the loops carry the accumulators without branches around MFMAs);
-  // in iteration order:
-  //   [qe, nqt)       ragged query end                      masked
-  //   [qb, qe)        every pair visible                    unmasked
-  //   [qa, qb)        causal boundary or ragged key end     masked
-  //   [qt_begin, qa)  no query sees the wave's keys         skipped
-  int qa = qt_begin, qb = qt_begin, qe = nqt;
-  if (kvw >= p.Nkv) {
-    qa = qb = qe = nqt;
-  } else {
-    if (CAUSAL) {
-      qa = max(qt_begin, floor_div(kvw - p.off - (BM - 1) + BM - 1, BM));  // q0 + BM - 1 >= kvw - off
-      qb = max(qa, floor_div(kvw + KW - 1 - p.off + BM - 1, BM));        // q0 >= kvw + KW - 1 - off
-    }
-    if (kvw + KW > p.Nkv) qb = nqt;  // ragged key end: every visible tile is masked
-    qa = min(qa, nqt);
-    qb = min(qb, nqt);
-    qe = max(qb, min(nqt, p.Nq / BM));
-  }
-  if (n_it > 0) {
-    static_for<NBUF - 1>([&](auto bc) {
-      copy_all(src_now(), decltype(bc)::value);
-      advance();
-    });
-    wait_vmem_n<OPS * (NBUF - 2)>();
-    lds_barrier();
-  }
-  static_for<LA>([&](auto oc) {
-    carry[decltype(oc)::value] = pad_row16<D>(sQdO[0], l16, 4 * decltype(oc)::value + j4);
-  });
-  // Iteration it works on buffer it % NBUF; from its middle on it copies tile
-  // it + NBUF - 1 into the buffer of iteration it - 1.
-  int it = 0, cur = 0;
-  auto phase = [&](int qt_low, auto variant) {  // down to query tile qt_low
-    constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
-    for (const int end = (nqt - qt_low) * p.G; it < end; ++it) {
-      const Src fsrc = src_now();  // tile it + NBUF - 1
-      advance();
-      const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
-      const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
-      const int q0 = (nqt - 1 - it / p.G) * BM;
-      if constexpr (VAR == 0) {
-        wait_vmem();
-        tile_barrier();
-        copy_all(fsrc, fbuf);
-      }
-      if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), q0, fsrc, fbuf);
-      if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), q0, fsrc, fbuf);
-      prev = cur;
-      cur = nxt;
-    }
-  };
-  phase(qe, std::integral_constant<int, 1>());
-  phase(qb, std::integral_constant<int, 2>());
-  phase(qa, std::integral_constant<int, 1>());
-  flush();
-  phase(qt_begin, std::integral_constant<int, 0>());
-  wait_vmem();  // no copy may land in LDS after the workgroup ends
-
-  wait_mfma();
-  uint16_t* __restrict__ dK = p.dk + kbase * D;
-  uint16_t* __restrict__ dV = p.dv + kbase * D;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int n = 0; n < NK; ++n) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kr = kvw + 32 * h + crow_of(i, g);
-        if (kr < p.Nkv) {
-          dK[(size_t)kr * D + 32 * n + l32] = Dt<DT>::one(dk[h][n][i] * p.scale);
-          dV[(size_t)kr * D + 32 * n + l32] = Dt<DT>::one(dv[h][n][i]);
+        } else if constexpr (k == 2) {
+          constexpr int s = loc / 4, kt = loc % 4;
+          if constexpr (s == 0)
+            dp[kt] = Mx<DT>::first16c(op, vb[kt][s], dn);
+          else
+            Mx<DT>::acc16(dp[kt], op, vb[kt][s]);
+        } else {
+          constexpr int n = loc / 2, h = loc % 2;
+          Mx<DT>::acc32(dv[h][n], pa[h], op);
         }
+      };
+      auto valu = [&](auto stc, auto mc, auto gc) {
+        constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
+        using Plan = typename Steps::template P<st>;
+        (void)gc;
+        static_for<18>([&](auto ec) {
+          if constexpr (spread_timed<Plan>(decltype(ec)::value, 18, Plan::B1, Plan::B3) == m)
+            p_item(ec, stc);
+          if constexpr (spread_slot(decltype(ec)::value, 18, Plan::B3, Plan::NM) == m)
+            ds_item(ec);
+        });
+        // The copies of a later tile ride on the score stages (S_st) of steps 2-3,
+        // which carry no other VALU work.
+        if constexpr (st >= 2 && m < Plan::B1) {
+          static_for<OPS>([&](auto cc) {
+            if constexpr (spread_slot(decltype(cc)::value, OPS, 0, 2 * Plan::B1) == (st - 2) * Plan::B1 + m)
+              copy_part(cc, fsrc, fbuf);
+          });
+        }
+      };
+      run_tile_carry<Steps::template P, NSB, LA>(carry, begin, operand, next, mfma, valu);
+    };
+    // dK of the last computed tile's last sub-block (a no-op when no tile was
+    // computed; the operand is zeroed when no tile was even copied).
+    auto flush = [&]() {
+      const uint16_t* Qp = sQdO[prev];
+      using Steps = DkdvSteps<NK>;
+      run_tile<Steps::template Flush, 1, LA>(
+          [&](auto) {},
+          [&](auto, auto oc) -> u32x4 {
+            constexpr int n = decltype(oc)::value;
+            const int k0 = 16 * (NSB - 1) + 8 * g;
+            const u32x4 op = pad_tr_operand<D>(Qp, k0, k0 + 4, 32 * n + 16 * hi16);
+            return n_it > 0 ? op : zero_u4();
+          },
+          [&](auto, auto mc, const u32x4& op) {
+            constexpr int loc = decltype(mc)::value, n = loc / 2, h = loc % 2;
+            Mx<DT>::acc32(dk[h][n], sa[h], op);
+          },
+          [&](auto, auto, auto) {});
+    };
+
+    // This wave's split of the query tiles (each phase runs one variant of the
+    // math, so the loops carry the accumulators without branches around MFMAs);
+    // in iteration order:
+    //   [qe, nqt)       ragged query end                      masked
+    //   [qb, qe)        every pair visible                    unmasked
+    //   [qa, qb)        causal boundary or ragged key end     masked
+    //   [qt_begin, qa)  no query sees the wave's keys         skipped
+    int qa = qt_begin, qb = qt_begin, qe = nqt;
+    if (kvw >= p.Nkv) {
+      qa = qb = qe = nqt;
+    } else {
+      if (CAUSAL) {
+        qa = max(qt_begin, floor_div(kvw - p.off - (BM - 1) + BM - 1, BM));  // q0 + BM - 1 >= kvw - off
+        qb = max(qa, floor_div(kvw + KW - 1 - p.off + BM - 1, BM));        // q0 >= kvw + KW - 1 - off
       }
+      if (kvw + KW > p.Nkv) qb = nqt;  // ragged key end: every visible tile is masked
+      qa = min(qa, nqt);
+      qb = min(qb, nqt);
+      qe = max(qb, min(nqt, p.Nq / BM));
     }
+    if (n_it > 0) {
+      static_for<NBUF - 1>([&](auto bc) {
+        copy_all(src_now(), decltype(bc)::value);
+        advance();
+      });
+    }
+    // The register preloads and the first tiles' copies are in flight together.  The
+    // copies are not visible to the compiler's wait counting, so everything is waited
+    // for here: the compiler then knows the preloads have landed and puts no wait of
+    // its own (which would count the copies wrongly) into the loop.
+    wait_vmem();
+    lds_barrier();
+    static_for<LA>([&](auto oc) {
+      carry[decltype(oc)::value] = pad_row16<D>(sQdO[0], l16, 4 * decltype(oc)::value + j4);
+    });
+    // Iteration it works on buffer it % NBUF; from its middle on it copies tile
+    // it + NBUF - 1 into the buffer of iteration it - 1.
+    int it = 0, cur = 0;
+    auto phase = [&](int qt_low, auto variant) {  // down to query tile qt_low
+      constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
+      for (const int end = (nqt - qt_low) * p.G; it < end; ++it) {
+        const Src fsrc = src_now();  // tile it + NBUF - 1
+        advance();
+        const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
+        const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
+        const int q0 = (nqt - 1 - it / p.G) * BM;
+        if constexpr (VAR == 0) {
+          wait_vmem();
+          tile_barrier();
+          copy_all(fsrc, fbuf);
+        }
+        if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), q0, fsrc, fbuf);
+        if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), q0, fsrc, fbuf);
+        prev = cur;
+        cur = nxt;
+      }
+    };
+    phase(qe, std::integral_constant<int, 1>());
+    phase(qb, std::integral_constant<int, 2>());
+    phase(qa, std::integral_constant<int, 1>());
+    flush();
+    phase(qt_begin, std::integral_constant<int, 0>());
+    wait_vmem();    // no copy may land in LDS after the tile buffers are reused below
+    lds_barrier();  // every wave is done with the tile buffers
+    settle(dk);
+    settle(dv);
+    uint16_t* stage = &sQdO[0][0] + w * 64 * (D + 8);
+    store_block64<DT, D>(dk, p.scale, stage, p.dk + kbase * D, kvw, p.Nkv, lane);
+    store_block64<DT, D>(dv, 1.f, stage, p.dv + kbase * D, kvw, p.Nkv, lane);
   }
 }
 
@@ -642,291 +674,292 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int OPS = 2 * BN * PadTile<D>::GR / 256;  // copy instructions per fetch per wave
   constexpr int LA = 2;
   __shared__ __attribute__((aligned(16))) uint16_t sKV[NBUF][2 * BN * RS];  // K, V: a padded pair
+  static_assert(NBUF * 2 * BN * RS >= 4 * 64 * (D + 8), "the output staging must fit the tile buffers");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int l16 = lane & 15, j4 = lane >> 4;
   const int l32 = lane & 31, g = lane >> 5, hi16 = j4 & 1;
   const int nqt = (p.Nq + BM - 1) / BM;
-  int rank, head;
-  map_block(blockIdx.x, p.B * p.Hq, rank, head);
-  const int qt = CAUSAL ? nqt - 1 - rank : rank;
-  const int b = head / p.Hq, h = head % p.Hq;
-  const int hk = h / p.G;
-  const int q0 = qt * BM;
-  const int qw = q0 + QW * w;  // first query row of this wave
-  const size_t qbase = ((size_t)b * p.Hq + h) * (size_t)p.Nq;
-  const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
-  const uint16_t* __restrict__ K = p.k + kbase * D;
-  const uint16_t* __restrict__ V = p.v + kbase * D;
+  __shared__ int s_item;
+  const WorkQueue wq(p.sched ? p.sched + 16 : nullptr, p.B * p.Hq, nqt);
+  long long ticket = tid == 0 ? wq.first() : 0;
+  for (;;) {
+    if (tid == 0) s_item = wq.resolve(ticket);
+    lds_barrier();  // also: the previous item's staging reads are done
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item < 0 || item >= wq.n_items) break;
+    if (tid == 0) ticket = wq.next_ticket(ticket);
+    const int rank = item / wq.n_heads, head = item % wq.n_heads;
+    const int qt = CAUSAL ? nqt - 1 - rank : rank;
+    const int b = head / p.Hq, h = head % p.Hq;
+    const int hk = h / p.G;
+    const int q0 = qt * BM;
+    const int qw = q0 + QW * w;  // first query row of this wave
+    const size_t qbase = ((size_t)b * p.Hq + h) * (size_t)p.Nq;
+    const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
+    const uint16_t* __restrict__ K = p.k + kbase * D;
+    const uint16_t* __restrict__ V = p.v + kbase * D;
 
-  u32x4 qb[4][NK], db[4][NK];
-  float lq[4];
-  f32x4 nd[4];  // -D of the lane's query, in every element: where dP^T starts
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int q = qw + 16 * t + l16;
-    const bool ok = q < p.Nq;
-#pragma unroll
-    for (int s = 0; s < NK; ++s) {
-      qb[t][s] = ok ? ld16(p.q + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
-      db[t][s] = ok ? ld16(p.dout + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
-    }
-    lq[t] = ok ? p.lse2[qbase + q] : INFINITY;
-    const float x = ok ? p.ndelta[qbase + q] : 0.f;
-    nd[t][0] = x;
-    nd[t][1] = x;
-    nd[t][2] = x;
-    nd[t][3] = x;
-  }
-  f32x16 acc[2][NK];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-    for (int n = 0; n < NK; ++n) acc[hh][n] = zero16();
-  }
-
-  // The tile copies below are not visible to the compiler's wait counting, so the
-  // register preloads are waited for here, before the first copy is issued.
-  wait_vmem();
-
-  int kv_end = p.Nkv;
-  if (CAUSAL) {
-    const int q_last = min(q0 + BM, p.Nq) - 1;
-    kv_end = min(p.Nkv, q_last + p.off + 1);
-  }
-  const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
-
-  // Iteration kt copies key/value tile kt + NBUF - 1 into the buffer of iteration
-  // kt - 1 (past the last tile, the last tile again, into a buffer no later
-  // iteration reads), OPS copies per wave spread over its MFMA stream.  Waves 0-1
-  // copy the K tile, waves 2-3 the V tile, through a buffer resource based at the
-  // tile's first row; rows past N_kv arrive as zeros (and are masked in the math).
-  using Copy = PadPairDma<D, BN>;
-  const uint16_t* __restrict__ tsrc = w < 2 ? K : V;
-  auto src_of = [&](int kt) {
-    const int k0 = min(kt, nkt - 1) * BN;
-    return buf_rsrc(tsrc + (size_t)k0 * D, (p.Nkv - k0) * D * 2);
-  };
-  int voff[Copy::PER_WAVE];
-#pragma unroll
-  for (int c = 0; c < Copy::PER_WAVE; ++c) voff[c] = Copy::src_offset(c, w, lane);
-  const uint32_t wave_off = Copy::lds_wave_offset(w);
-  auto copy_part = [&](auto cc, const i32x4& sr, int buf) {
-    constexpr int c = decltype(cc)::value;
-    bdma16<Copy::template lds_offset<c>>(voff[c], sr, lds_u32(sKV[buf]) + wave_off);
-  };
-  auto copy_all = [&](int kt, int buf) {
-    const i32x4 sr = src_of(kt);
-    static_for<OPS>([&](auto cc) { copy_part(cc, sr, buf); });
-  };
-
-  // Carried from tile to tile: the first LA operands of the next tile, and P^T and
-  // dP^T of the last sub-block (sc[1], dp), whose dS^T and dQ product run in
-  // step 0 of the next tile with K read from the previous buffer (zero before the
-  // first tile, which makes that product a no-op).
-  u32x4 carry[LA];
-  f32x4 sc[2][4];  // S^T, then P^T, of sub-block st in sc[st % 2], per query tile
-  f32x4 dp[4];     // dP^T, then dS^T, of the sub-block being finished
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    sc[1][t] = zero4();
-    dp[t] = zero4();
-  }
-  int prev = 0;  // buffer of the previous tile
-
-  auto compute = [&](int cur, int nxt, auto mask_c, int kv0, const i32x4& fsrc, int fbuf) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    const uint16_t* Kt = sKV[cur];
-    const uint16_t* Vt = Kt + BN * RS;
-    const uint16_t* Kp = sKV[prev];
-    const uint16_t* Kn = sKV[nxt];
-    u32x4 da[2];  // dS A operands, per query half
-    const int krow = kv0 + 4 * j4;  // key of element 0 in sub-block 0
-    const int qcol = qw + l16;      // query of this lane's column in query tile 0
-
-    auto ds_item = [&](auto ec, auto cp_c) {
-      constexpr int e = decltype(ec)::value, cp = decltype(cp_c)::value;
-      if constexpr (e == 8) {
-        da[0] = c16_pair_to_a32(pack_c4<DT>(dp[0]), pack_c4<DT>(dp[1]));
-      } else if constexpr (e == 17) {
-        da[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
-      } else {
-        constexpr int x = e < 8 ? e : e - 1, t = x / 4, i = x % 4;
-        dp[t][i] = sc[cp][t][i] * dp[t][i];  // dP - D: the dP^T product starts from -D
-      }
-    };
-    auto p_item = [&](auto ec, auto st_c) {
-      constexpr int e = decltype(ec)::value, st = decltype(st_c)::value, cs = st & 1;
-      constexpr int t = e / 4, i = e % 4;
-      float v = sc[cs][t][i] * p.scale_log2 - lq[t];
-      if constexpr (MASK) {
-        const int key = krow + 16 * st + i, q = qcol + 16 * t;
-        if (key >= p.Nkv || (CAUSAL && key > q + p.off)) v = -INFINITY;
-      }
-      sc[cs][t][i] = fast_exp2(v);
-    };
-
-    using Steps = DqSteps<NK>;
-    auto begin = [&](auto stc) {
-      constexpr int st = decltype(stc)::value;
-      if constexpr (st == 2) {
-        // Mid-tile: every wave is past step 0 (its last reads of the previous
-        // buffer) and, once its own copies have landed, the next tile is complete,
-        // so the copies of steps 2-3 may refill the previous buffer.
-        wait_vmem();
-        tile_barrier();
-      }
-    };
-    auto operand = [&](auto stc, auto oc) -> u32x4 {
-      constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
-      using Plan = typename Steps::template P<st>;
-      constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
-      if constexpr (k == 0) {
-        return pad_row16<D>(Kt, 16 * st + l16, 4 * n + j4);
-      } else if constexpr (k == 1) {
-        if constexpr (st == 0) {
-          const int k0 = 16 * (NSB - 1) + 8 * g;
-          return pad_tr_operand<D>(Kp, k0, k0 + 4, 32 * n + 16 * hi16);
-        } else {
-          const int k0 = 16 * (st - 1) + 8 * g;
-          return pad_tr_operand<D>(Kt, k0, k0 + 4, 32 * n + 16 * hi16);
-        }
-      } else {
-        return pad_row16<D>(Vt, 16 * st + l16, 4 * n + j4);
-      }
-    };
-    auto next = [&](auto oc) -> u32x4 {  // operand oc of the next tile: S^T of sub-block 0
-      return pad_row16<D>(Kn, l16, 4 * decltype(oc)::value + j4);
-    };
-    auto mfma = [&](auto stc, auto mc, const u32x4& op) {
-      constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cs = st & 1;
-      using Plan = typename Steps::template P<st>;
-      constexpr int k = Plan::stage(m), loc = Plan::local(m);
-      if constexpr (k == 0) {
-        constexpr int s = loc / 4, t = loc % 4;
-        if constexpr (s == 0)
-          sc[cs][t] = Mx<DT>::first16(op, qb[t][s]);
-        else
-          Mx<DT>::acc16(sc[cs][t], op, qb[t][s]);
-      } else if constexpr (k == 1) {
-        constexpr int n = loc / 2, hh = loc % 2;
-        Mx<DT>::acc32(acc[hh][n], da[hh], op);
-      } else {
-        constexpr int s = loc / 4, t = loc % 4;
-        if constexpr (s == 0)
-          dp[t] = Mx<DT>::first16c(op, db[t][s], nd[t]);
-        else
-          Mx<DT>::acc16(dp[t], op, db[t][s]);
-      }
-    };
-    constexpr int NMT = tile_mfmas<Steps::template P, NSB>();
-    constexpr int M2 = NMT / 2;  // first MFMA of step 2
-    auto valu = [&](auto stc, auto mc, auto gc) {
-      constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cp = (st + 1) & 1;
-      constexpr int gm = decltype(gc)::value;
-      using Plan = typename Steps::template P<st>;
-      // dS of the previous sub-block (of the previous tile in step 0) under S^T_st
-      static_for<18>([&](auto ec) {
-        if constexpr (spread_slot(decltype(ec)::value, 18, 0, Plan::B1) == m)
-          ds_item(ec, std::integral_constant<int, cp>());
-      });
-      static_for<16>([&](auto ec) {
-        if constexpr (spread_timed<Plan>(decltype(ec)::value, 16, Plan::B1, Plan::NM) == m)
-          p_item(ec, stc);
-      });
-      // the copies of a later tile, spread over steps 2-3
-      static_for<OPS>([&](auto cc) {
-        if constexpr (spread_slot(decltype(cc)::value, OPS, M2, NMT) == gm)
-          copy_part(cc, fsrc, fbuf);
-      });
-    };
-    run_tile_carry<Steps::template P, NSB, LA>(carry, begin, operand, next, mfma, valu);
-  };
-  // dS and dQ of the last computed tile's last sub-block (a no-op when no tile was
-  // computed; the operand is zeroed when no tile was even copied).
-  auto flush = [&]() {
-    const uint16_t* Kp = sKV[prev];
-    u32x4 da[2];
+    u32x4 qb[4][NK], db[4][NK];
+    float lq[4];
+    f32x4 nd[4];  // -D of the lane's query, in every element: where dP^T starts
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      const int q = qw + 16 * t + l16;
+      const bool ok = q < p.Nq;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dp[t][i] = sc[1][t][i] * dp[t][i];
+      for (int s = 0; s < NK; ++s) {
+        qb[t][s] = ok ? ld16(p.q + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
+        db[t][s] = ok ? ld16(p.dout + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
+      }
+      lq[t] = ok ? p.lse2[qbase + q] : INFINITY;
+      const float x = ok ? p.ndelta[qbase + q] : 0.f;
+      nd[t][0] = x;
+      nd[t][1] = x;
+      nd[t][2] = x;
+      nd[t][3] = x;
     }
-    da[0] = c16_pair_to_a32(pack_c4<DT>(dp[0]), pack_c4<DT>(dp[1]));
-    da[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
-    using Steps = DqSteps<NK>;
-    run_tile<Steps::template Flush, 1, LA>(
-        [&](auto) {},
-        [&](auto, auto oc) -> u32x4 {
-          constexpr int n = decltype(oc)::value;
-          const int k0 = 16 * (NSB - 1) + 8 * g;
-          const u32x4 op = pad_tr_operand<D>(Kp, k0, k0 + 4, 32 * n + 16 * hi16);
-          return nkt > 0 ? op : zero_u4();
-        },
-        [&](auto, auto mc, const u32x4& op) {
-          constexpr int loc = decltype(mc)::value, n = loc / 2, hh = loc % 2;
+    f32x16 acc[2][NK];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+      for (int n = 0; n < NK; ++n) acc[hh][n] = zero16();
+    }
+
+
+    int kv_end = p.Nkv;
+    if (CAUSAL) {
+      const int q_last = min(q0 + BM, p.Nq) - 1;
+      kv_end = min(p.Nkv, q_last + p.off + 1);
+    }
+    const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+
+    // Iteration kt copies key/value tile kt + NBUF - 1 into the buffer of iteration
+    // kt - 1 (past the last tile, the last tile again, into a buffer no later
+    // iteration reads), OPS copies per wave spread over its MFMA stream.  Waves 0-1
+    // copy the K tile, waves 2-3 the V tile, through a buffer resource based at the
+    // tile's first row; rows past N_kv arrive as zeros (and are masked in the math).
+    using Copy = PadPairDma<D, BN>;
+    const uint16_t* __restrict__ tsrc = w < 2 ? K : V;
+    auto src_of = [&](int kt) {
+      const int k0 = min(kt, nkt - 1) * BN;
+      return buf_rsrc(tsrc + (size_t)k0 * D, (p.Nkv - k0) * D * 2);
+    };
+    int voff[Copy::PER_WAVE];
+#pragma unroll
+    for (int c = 0; c < Copy::PER_WAVE; ++c) voff[c] = Copy::src_offset(c, w, lane);
+    const uint32_t wave_off = Copy::lds_wave_offset(w);
+    auto copy_part = [&](auto cc, const i32x4& sr, int buf) {
+      constexpr int c = decltype(cc)::value;
+      bdma16<Copy::template lds_offset<c>>(voff[c], sr, lds_u32(sKV[buf]) + wave_off);
+    };
+    auto copy_all = [&](int kt, int buf) {
+      const i32x4 sr = src_of(kt);
+      static_for<OPS>([&](auto cc) { copy_part(cc, sr, buf); });
+    };
+
+    // Carried from tile to tile: the first LA operands of the next tile, and P^T and
+    // dP^T of the last sub-block (sc[1], dp), whose dS^T and dQ product run in
+    // step 0 of the next tile with K read from the previous buffer (zero before the
+    // first tile, which makes that product a no-op).
+    u32x4 carry[LA];
+    f32x4 sc[2][4];  // S^T, then P^T, of sub-block st in sc[st % 2], per query tile
+    f32x4 dp[4];     // dP^T, then dS^T, of the sub-block being finished
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sc[1][t] = zero4();
+      dp[t] = zero4();
+    }
+    int prev = 0;  // buffer of the previous tile
+
+    auto compute = [&](int cur, int nxt, auto mask_c, int kv0, const i32x4& fsrc, int fbuf) {
+      constexpr bool MASK = decltype(mask_c)::value;
+      const uint16_t* Kt = sKV[cur];
+      const uint16_t* Vt = Kt + BN * RS;
+      const uint16_t* Kp = sKV[prev];
+      const uint16_t* Kn = sKV[nxt];
+      u32x4 da[2];  // dS A operands, per query half
+      const int krow = kv0 + 4 * j4;  // key of element 0 in sub-block 0
+      const int qcol = qw + l16;      // query of this lane's column in query tile 0
+
+      auto ds_item = [&](auto ec, auto cp_c) {
+        constexpr int e = decltype(ec)::value, cp = decltype(cp_c)::value;
+        if constexpr (e == 8) {
+          da[0] = c16_pair_to_a32(pack_c4<DT>(dp[0]), pack_c4<DT>(dp[1]));
+        } else if constexpr (e == 17) {
+          da[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
+        } else {
+          constexpr int x = e < 8 ? e : e - 1, t = x / 4, i = x % 4;
+          dp[t][i] = sc[cp][t][i] * dp[t][i];  // dP - D: the dP^T product starts from -D
+        }
+      };
+      auto p_item = [&](auto ec, auto st_c) {
+        constexpr int e = decltype(ec)::value, st = decltype(st_c)::value, cs = st & 1;
+        constexpr int t = e / 4, i = e % 4;
+        float v = sc[cs][t][i] * p.scale_log2 - lq[t];
+        if constexpr (MASK) {
+          const int key = krow + 16 * st + i, q = qcol + 16 * t;
+          if (key >= p.Nkv || (CAUSAL && key > q + p.off)) v = -INFINITY;
+        }
+        sc[cs][t][i] = fast_exp2(v);
+      };
+
+      using Steps = DqSteps<NK>;
+      auto begin = [&](auto stc) {
+        constexpr int st = decltype(stc)::value;
+        if constexpr (st == 2) {
+          // Mid-tile: every wave is past step 0 (its last reads of the previous
+          // buffer) and, once its own copies have landed, the next tile is complete,
+          // so the copies of steps 2-3 may refill the previous buffer.
+          wait_vmem();
+          tile_barrier();
+        }
+      };
+      auto operand = [&](auto stc, auto oc) -> u32x4 {
+        constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
+        using Plan = typename Steps::template P<st>;
+        constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
+        if constexpr (k == 0) {
+          return pad_row16<D>(Kt, 16 * st + l16, 4 * n + j4);
+        } else if constexpr (k == 1) {
+          if constexpr (st == 0) {
+            const int k0 = 16 * (NSB - 1) + 8 * g;
+            return pad_tr_operand<D>(Kp, k0, k0 + 4, 32 * n + 16 * hi16);
+          } else {
+            const int k0 = 16 * (st - 1) + 8 * g;
+            return pad_tr_operand<D>(Kt, k0, k0 + 4, 32 * n + 16 * hi16);
+          }
+        } else {
+          return pad_row16<D>(Vt, 16 * st + l16, 4 * n + j4);
+        }
+      };
+      auto next = [&](auto oc) -> u32x4 {  // operand oc of the next tile: S^T of sub-block 0
+        return pad_row16<D>(Kn, l16, 4 * decltype(oc)::value + j4);
+      };
+      auto mfma = [&](auto stc, auto mc, const u32x4& op) {
+        constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cs = st & 1;
+        using Plan = typename Steps::template P<st>;
+        constexpr int k = Plan::stage(m), loc = Plan::local(m);
+        if constexpr (k == 0) {
+          constexpr int s = loc / 4, t = loc % 4;
+          if constexpr (s == 0)
+            sc[cs][t] = Mx<DT>::first16(op, qb[t][s]);
+          else
+            Mx<DT>::acc16(sc[cs][t], op, qb[t][s]);
+        } else if constexpr (k == 1) {
+          constexpr int n = loc / 2, hh = loc % 2;
           Mx<DT>::acc32(acc[hh][n], da[hh], op);
-        },
-        [&](auto, auto, auto) {});
-  };
+        } else {
+          constexpr int s = loc / 4, t = loc % 4;
+          if constexpr (s == 0)
+            dp[t] = Mx<DT>::first16c(op, db[t][s], nd[t]);
+          else
+            Mx<DT>::acc16(dp[t], op, db[t][s]);
+        }
+      };
+      constexpr int NMT = tile_mfmas<Steps::template P, NSB>();
+      constexpr int M2 = NMT / 2;  // first MFMA of step 2
+      auto valu = [&](auto stc, auto mc, auto gc) {
+        constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cp = (st + 1) & 1;
+        constexpr int gm = decltype(gc)::value;
+        using Plan = typename Steps::template P<st>;
+        // dS of the previous sub-block (of the previous tile in step 0) under S^T_st
+        static_for<18>([&](auto ec) {
+          if constexpr (spread_slot(decltype(ec)::value, 18, 0, Plan::B1) == m)
+            ds_item(ec, std::integral_constant<int, cp>());
+        });
+        static_for<16>([&](auto ec) {
+          if constexpr (spread_timed<Plan>(decltype(ec)::value, 16, Plan::B1, Plan::NM) == m)
+            p_item(ec, stc);
+        });
+        // the copies of a later tile, spread over steps 2-3
+        static_for<OPS>([&](auto cc) {
+          if constexpr (spread_slot(decltype(cc)::value, OPS, M2, NMT) == gm)
+            copy_part(cc, fsrc, fbuf);
+        });
+      };
+      run_tile_carry<Steps::template P, NSB, LA>(carry, begin, operand, next, mfma, valu);
+    };
+    // dS and dQ of the last computed tile's last sub-block (a no-op when no tile was
+    // computed; the operand is zeroed when no tile was even copied).
+    auto flush = [&]() {
+      const uint16_t* Kp = sKV[prev];
+      u32x4 da[2];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dp[t][i] = sc[1][t][i] * dp[t][i];
+      }
+      da[0] = c16_pair_to_a32(pack_c4<DT>(dp[0]), pack_c4<DT>(dp[1]));
+      da[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
+      using Steps = DqSteps<NK>;
+      run_tile<Steps::template Flush, 1, LA>(
+          [&](auto) {},
+          [&](auto, auto oc) -> u32x4 {
+            constexpr int n = decltype(oc)::value;
+            const int k0 = 16 * (NSB - 1) + 8 * g;
+            const u32x4 op = pad_tr_operand<D>(Kp, k0, k0 + 4, 32 * n + 16 * hi16);
+            return nkt > 0 ? op : zero_u4();
+          },
+          [&](auto, auto mc, const u32x4& op) {
+            constexpr int loc = decltype(mc)::value, n = loc / 2, hh = loc % 2;
+            Mx<DT>::acc32(acc[hh][n], da[hh], op);
+          },
+          [&](auto, auto, auto) {});
+    };
 
-  // This wave's split of the key tiles (one variant of the math per loop):
-  //   [0, n_un)      every pair visible          unmasked
-  //   [n_un, n_vis)  causal boundary / ragged    masked
-  //   [n_vis, nkt)   no key visible to the wave  skipped
-  int n_vis = nkt;
-  if (qw >= p.Nq) n_vis = 0;
-  else if (CAUSAL) n_vis = min(nkt, max(0, floor_div(qw + QW - 1 + p.off, BN) + 1));
-  int n_un = min(n_vis, p.Nkv / BN);
-  if (CAUSAL) n_un = min(n_un, max(0, floor_div(qw + p.off - (BN - 1), BN) + 1));
+    // This wave's split of the key tiles (one variant of the math per loop):
+    //   [0, n_un)      every pair visible          unmasked
+    //   [n_un, n_vis)  causal boundary / ragged    masked
+    //   [n_vis, nkt)   no key visible to the wave  skipped
+    int n_vis = nkt;
+    if (qw >= p.Nq) n_vis = 0;
+    else if (CAUSAL) n_vis = min(nkt, max(0, floor_div(qw + QW - 1 + p.off, BN) + 1));
+    int n_un = min(n_vis, p.Nkv / BN);
+    if (CAUSAL) n_un = min(n_un, max(0, floor_div(qw + p.off - (BN - 1), BN) + 1));
 
-  if (nkt > 0) {
-    static_for<NBUF - 1>([&](auto bc) { copy_all(decltype(bc)::value, decltype(bc)::value); });
-    wait_vmem_n<OPS * (NBUF - 2)>();
+    if (nkt > 0) {
+      static_for<NBUF - 1>([&](auto bc) { copy_all(decltype(bc)::value, decltype(bc)::value); });
+    }
+    // The register preloads and the first tiles' copies are in flight together.  The
+    // copies are not visible to the compiler's wait counting, so everything is waited
+    // for here: the compiler then knows the preloads have landed and puts no wait of
+    // its own (which would count the copies wrongly) into the loop.
+    wait_vmem();
     lds_barrier();
-  }
-  static_for<LA>([&](auto oc) {
-    carry[decltype(oc)::value] = pad_row16<D>(sKV[0], l16, 4 * decltype(oc)::value + j4);
-  });
-  // Iteration kt works on buffer kt % NBUF; from its middle on it copies tile
-  // kt + NBUF - 1 into the buffer of iteration kt - 1.
-  int kt = 0, cur = 0;
-  auto phase = [&](int end, auto variant) {
-    constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
-    for (; kt < end; ++kt) {
-      const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
-      const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
-      const i32x4 fsrc = src_of(kt + NBUF - 1);
-      if constexpr (VAR == 0) {
-        wait_vmem();
-        tile_barrier();
-        copy_all(kt + NBUF - 1, fbuf);
+    static_for<LA>([&](auto oc) {
+      carry[decltype(oc)::value] = pad_row16<D>(sKV[0], l16, 4 * decltype(oc)::value + j4);
+    });
+    // Iteration kt works on buffer kt % NBUF; from its middle on it copies tile
+    // kt + NBUF - 1 into the buffer of iteration kt - 1.
+    int kt = 0, cur = 0;
+    auto phase = [&](int end, auto variant) {
+      constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
+      for (; kt < end; ++kt) {
+        const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
+        const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
+        const i32x4 fsrc = src_of(kt + NBUF - 1);
+        if constexpr (VAR == 0) {
+          wait_vmem();
+          tile_barrier();
+          copy_all(kt + NBUF - 1, fbuf);
+        }
+        if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), kt * BN, fsrc, fbuf);
+        if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), kt * BN, fsrc, fbuf);
+        prev = cur;
+        cur = nxt;
       }
-      if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), kt * BN, fsrc, fbuf);
-      if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), kt * BN, fsrc, fbuf);
-      prev = cur;
-      cur = nxt;
-    }
-  };
-  phase(n_un, std::integral_constant<int, 2>());
-  phase(n_vis, std::integral_constant<int, 1>());
-  flush();
-  phase(nkt, std::integral_constant<int, 0>());
-  wait_vmem();  // no copy may land in LDS after the workgroup ends
-
-  wait_mfma();
-  uint16_t* __restrict__ dQ = p.dq + qbase * D;
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-    for (int n = 0; n < NK; ++n) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qr = qw + 32 * hh + crow_of(i, g);
-        if (qr < p.Nq) dQ[(size_t)qr * D + 32 * n + l32] = Dt<DT>::one(acc[hh][n][i] * p.scale);
-      }
-    }
+    };
+    phase(n_un, std::integral_constant<int, 2>());
+    phase(n_vis, std::integral_constant<int, 1>());
+    flush();
+    phase(nkt, std::integral_constant<int, 0>());
+    wait_vmem();    // no copy may land in LDS after the tile buffers are reused below
+    lds_barrier();  // every wave is done with the tile buffers
+    settle(acc);
+    uint16_t* stage = &sKV[0][0] + w * 64 * (D + 8);
+    store_block64<DT, D>(acc, p.scale, stage, p.dq + qbase * D, qw, p.Nq, lane);
   }
 }
 
@@ -947,16 +980,24 @@ hipError_t run_pre(const BwdArgs& a, bool zero, hipStream_t s) {
 
 template <int DT, int D, bool CAUSAL>
 hipError_t run_dkdv(const BwdArgs& a, hipStream_t s) {
-  const BwdParams p = make_params(a);
-  const dim3 grid((unsigned)(((a.pb.Nkv + 255) / 256) * a.pb.Hkv * a.pb.B));
+  BwdParams p = make_params(a);
+  // One item per workgroup in rank order: measured on an MI355X at the causal GQA
+  // N=8192 shape, the work queues cost the dK/dV kernel about 1% (its items are
+  // long, four per compute unit) where they save the dQ pass 2-3%.
+  const int items = ((a.pb.Nkv + 255) / 256) * a.pb.Hkv * a.pb.B;
+  p.sched = nullptr;
+  const dim3 grid((unsigned)items);
   hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 template <int DT, int D, bool CAUSAL>
 hipError_t run_dq(const BwdArgs& a, hipStream_t s) {
-  const BwdParams p = make_params(a);
-  const dim3 grid((unsigned)(((a.pb.Nq + 255) / 256) * a.pb.Hq * a.pb.B));
+  BwdParams p = make_params(a);
+  const int items = ((a.pb.Nq + 255) / 256) * a.pb.Hq * a.pb.B;
+  const int ncu = device_cu_count();
+  if (sched_static()) p.sched = nullptr;
+  const dim3 grid((unsigned)(p.sched && ncu > 0 && ncu < items ? ncu : items));
   hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }

@@ -151,6 +151,19 @@ __device__ __forceinline__ void wait_mfma() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
+// wait_mfma() for a set of accumulators about to be read: the empty asm statements
+// (ordered after the nops, as all volatile asm) tell the compiler the
+// accumulators change there, so no read of them is scheduled before the wait.
+template <int N0, int N1>
+__device__ __forceinline__ void settle(f32x16 (&acc)[N0][N1]) {
+  wait_mfma();
+#pragma unroll
+  for (int i = 0; i < N0; ++i) {
+#pragma unroll
+    for (int j = 0; j < N1; ++j) asm volatile("" : "+a"(acc[i][j]));
+  }
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll

@@ -38,11 +38,13 @@ struct BwdArgs {
   float* ndelta;  // [B*Hq*Nq]      -rowsum(dO o O)
   float* lse2;    // [B*Hq*Nq]      LSE * log2(e), +inf for rows that see no key
   float* dq_acc;  // [B*Hq*Nq*d]    float32 dQ accumulator (atomic path only)
+  int* sched;     // [32]           work-queue counters of the dK/dV and dQ kernels (zeroed
+                  //                by the preprocess); null: static work split
 };
 
 // Workspace carve-up; every region starts on a 256-byte boundary.
 struct WorkspaceLayout {
-  size_t ndelta_off, lse2_off, dqacc_off, total;
+  size_t ndelta_off, lse2_off, dqacc_off, sched_off, total;
 };
 WorkspaceLayout workspace_layout(const Problem& pb, bool atomic_dq);
 
@@ -52,5 +54,11 @@ hipError_t launch_bwd_pre(const BwdArgs& a, bool zero_dq_acc, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, bool atomic_dq, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq_convert(const BwdArgs& a, hipStream_t s);
+
+// Compute units of the current device (cached per device; 0 if it cannot be read).
+int device_cu_count();
+// FA_SCHED=static in the environment: the persistent kernels take one work item
+// per workgroup in a fixed order instead of the work queues (for comparisons).
+bool sched_static();
 
 }  // namespace fa
