@@ -34,8 +34,9 @@
 namespace fa {
 
 // One pipeline step: up to four stages of MFMAs issued in order; stage k has Nk
-// operands read from LDS, each feeding Gk consecutive MFMAs.
-template <int N0, int G0, int N1, int G1, int N2, int G2, int N3, int G3>
+// operands read from LDS, each feeding Gk consecutive MFMAs.  WODD: issue time of an
+// MFMA of the odd stages in units of a 16x16x32 MFMA (2 for 32x32x16 products).
+template <int N0, int G0, int N1, int G1, int N2, int G2, int N3, int G3, int WODD = 2>
 struct StepPlan {
   static constexpr int B1 = N0 * G0, B2 = B1 + N1 * G1, B3 = B2 + N2 * G2, NM = B3 + N3 * G3;
   static constexpr int O1 = N0, O2 = O1 + N1, O3 = O2 + N2, NOP = O3 + N3;
@@ -48,9 +49,8 @@ struct StepPlan {
   static constexpr bool first(int m) { return local(m) % gsz(stage(m)) == 0; }
   static constexpr int op_stage(int o) { return o < O1 ? 0 : o < O2 ? 1 : o < O3 ? 2 : 3; }
   static constexpr int op_local(int o) { return o - obase(op_stage(o)); }
-  // issue time of MFMA m in units of a 16x16x32 MFMA: the odd stages of both
-  // kernels' plans are 32x32x16 products (twice the cycles)
-  static constexpr int weight(int m) { return (stage(m) & 1) ? 2 : 1; }
+  // issue time of MFMA m in units of a 16x16x32 MFMA
+  static constexpr int weight(int m) { return (stage(m) & 1) ? WODD : 1; }
 };
 
 // floor(a / b) for b > 0 and any sign of a.
@@ -189,10 +189,14 @@ constexpr int tile_mfmas() {
 }
 
 // Step plans.  dK/dV: S_st | dK_{st-1} | dP_st | dV_st over NSB sub-blocks plus a
-// final dK step.  dQ: S^T_st | dQ_{st-1} | dP^T_st, plus a final dQ step.
-// The gradient product of a tile's last sub-block is issued in step 0 of the next
-// tile (and after the last tile by a flush step), so every step of a tile has the
-// same shape.
+// final dK step.  The dK product of a tile's last sub-block is issued in step 0 of
+// the next tile (and after the last tile by a flush step), so every step of a tile
+// has the same shape.
+// dQ: S^T_st | half of a dQ product | dP^T_st.  The dQ product of a pair of
+// sub-blocks (16x16x32, contraction over their 32 keys) is issued in two halves
+// (head-dim tiles), in the two steps after the pair: steps 0-1 finish the previous
+// tile's second pair, steps 2-3 this tile's first; a flush step issues both halves
+// of the last pair.
 template <int NK>
 struct DkdvSteps {
   template <int ST>
@@ -203,9 +207,9 @@ struct DkdvSteps {
 template <int NK>
 struct DqSteps {
   template <int ST>
-  using P = StepPlan<NK, 4, NK, 2, NK, 4, 0, 1>;
+  using P = StepPlan<NK, 4, NK, 4, NK, 4, 0, 1, 1>;
   template <int ST>
-  using Flush = StepPlan<0, 4, NK, 2, 0, 4, 0, 1>;
+  using Flush = StepPlan<0, 4, 2 * NK, 4, 0, 4, 0, 1, 1>;
 };
 
 // Store a wave's 64 x D block held in 32x32 accumulators (acc[h][n] element i of
@@ -230,6 +234,33 @@ __device__ __forceinline__ void store_block64(const f32x16 (&acc)[2][D / 32], fl
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         stage[(32 * h + crow_of(i, g)) * SS + 32 * n + l32] = Dt<DT>::one(acc[h][n][i] * scale);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 64 / RPI; ++k) {
+    const int r = k * RPI + lane / CPR, c = lane % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * SS + 8 * c);
+    if (row0 + r < n_rows) st16(dst + (size_t)(row0 + r) * D + 8 * c, v);
+  }
+}
+
+// store_block64 for a block held in 16x16 accumulators: acc[t][n] element i of
+// lane (l16, j4) is row 16t + 4 j4 + i, column 16n + l16.
+template <int DT, int D>
+__device__ __forceinline__ void store_block64_c16(const f32x4 (&acc)[4][D / 16], float scale,
+                                                  uint16_t* __restrict__ stage, uint16_t* __restrict__ dst,
+                                                  int row0, int n_rows, int lane) {
+  constexpr int SS = D + 8;
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 64 / CPR;
+  const int l16 = lane & 15, j4 = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        stage[(16 * t + 4 * j4 + i) * SS + 16 * n + l16] = Dt<DT>::one(acc[t][n][i] * scale);
     }
   }
 #pragma unroll
@@ -656,15 +687,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 // head); wave w owns queries qw = q0 + 64w .. +63 and keeps
 //   Q and dO as the B operands of S^T = K Q^T and dP^T = V dO^T (16x16x32; query
 //   tile t of 16 queries, contraction step s of 32 head dims), their LSE and D,
-//   and dQ as float32 32x32 accumulators (query half h, head-dim tile n).
+//   and dQ as float32 16x16 accumulators (query tile t, head-dim tile n).
 // Key/value tiles of 64 rows are triple-buffered in LDS and copied straight from
 // global memory.  A tile is processed in four 16-key sub-blocks; per sub-block a
-// wave computes S^T and dP^T (4 query tiles), P^T and dS^T, and
-// dQ += dS K (32x32x16; dS from two 16x16 accumulators through v_permlane16_swap,
-// K with the key along the slots from a transposed LDS read).
+// wave computes S^T and dP^T (4 query tiles), P^T and dS^T.  Per pair of
+// sub-blocks it adds dQ += dS K (16x16x32 over the pair's 32 keys): a lane holds
+// keys 4 j4 .. 4 j4 + 3 of each sub-block for its query, which, put side by side,
+// are its 8 contraction slots, so the A operand is the two packed dS tiles as they
+// are; the B operand (K with the same keys along the slots) is two transposed LDS
+// reads.  All MFMAs are 16x16x32, which under the power limit sustain a higher
+// clock than 32x32x16 ones.
 //
-// Step st issues the MFMA stream  S^T_st | dQ_{st-1} | dP^T_st  with dS_{st-1}
-// computed under S^T_st and P_st under dQ_{st-1} and dP^T_st.
+// Step st issues the MFMA stream  S^T_st | dQ half | dP^T_st  with dS_{st-1}
+// computed under S^T_st and P_st under the dQ half and dP^T_st.
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int QW = 64, BM = 4 * QW, BN = 64, NSB = BN / 16;
@@ -679,7 +714,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int l16 = lane & 15, j4 = lane >> 4;
-  const int l32 = lane & 31, g = lane >> 5, hi16 = j4 & 1;
   const int nqt = (p.Nq + BM - 1) / BM;
   __shared__ int s_item;
   const WorkQueue wq(p.sched ? p.sched + 16 : nullptr, p.B * p.Hq, nqt);
@@ -720,11 +754,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       nd[t][2] = x;
       nd[t][3] = x;
     }
-    f32x16 acc[2][NK];
+    f32x4 acc[4][2 * NK];  // dQ, per query tile and 16-column head-dim tile
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int t = 0; t < 4; ++t) {
 #pragma unroll
-      for (int n = 0; n < NK; ++n) acc[hh][n] = zero16();
+      for (int n = 0; n < 2 * NK; ++n) acc[t][n] = zero4();
     }
 
 
@@ -759,17 +793,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       static_for<OPS>([&](auto cc) { copy_part(cc, sr, buf); });
     };
 
-    // Carried from tile to tile: the first LA operands of the next tile, and P^T and
-    // dP^T of the last sub-block (sc[1], dp), whose dS^T and dQ product run in
-    // step 0 of the next tile with K read from the previous buffer (zero before the
-    // first tile, which makes that product a no-op).
+    // Carried from tile to tile: the first LA operands of the next tile, P^T and
+    // dP^T of the last sub-block (sc[1], dp), whose dS^T is computed in step 0 of
+    // the next tile, and the packed dS of the second pair (da[1]), whose dQ product
+    // runs in steps 0-1 of the next tile with K read from the previous buffer (zero
+    // before the first tile, which makes that product a no-op).
     u32x4 carry[LA];
     f32x4 sc[2][4];  // S^T, then P^T, of sub-block st in sc[st % 2], per query tile
     f32x4 dp[4];     // dP^T, then dS^T, of the sub-block being finished
+    u32x4 da[2][4];  // dS A operands of sub-block pair J, per query tile
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       sc[1][t] = zero4();
       dp[t] = zero4();
+      da[1][t] = zero_u4();
     }
     int prev = 0;  // buffer of the previous tile
 
@@ -779,18 +816,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       const uint16_t* Vt = Kt + BN * RS;
       const uint16_t* Kp = sKV[prev];
       const uint16_t* Kn = sKV[nxt];
-      u32x4 da[2];  // dS A operands, per query half
       const int krow = kv0 + 4 * j4;  // key of element 0 in sub-block 0
       const int qcol = qw + l16;      // query of this lane's column in query tile 0
 
-      auto ds_item = [&](auto ec, auto cp_c) {
-        constexpr int e = decltype(ec)::value, cp = decltype(cp_c)::value;
-        if constexpr (e == 8) {
-          da[0] = c16_pair_to_a32(pack_c4<DT>(dp[0]), pack_c4<DT>(dp[1]));
-        } else if constexpr (e == 17) {
-          da[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
+      // dS of sub-block sb (kept in sc[cp], dp), item e of 20: per query tile four
+      // products, then the packed tile into its half of the pair's A operand
+      auto ds_item = [&](auto ec, auto cp_c, auto sb_c) {
+        constexpr int e = decltype(ec)::value, cp = decltype(cp_c)::value, sb = decltype(sb_c)::value;
+        constexpr int t = e / 5, i = e % 5;
+        if constexpr (i == 4) {
+          const u32x2 v = pack_c4<DT>(dp[t]);
+          da[sb / 2][t][2 * (sb % 2)] = v[0];
+          da[sb / 2][t][2 * (sb % 2) + 1] = v[1];
         } else {
-          constexpr int x = e < 8 ? e : e - 1, t = x / 4, i = x % 4;
           dp[t][i] = sc[cp][t][i] * dp[t][i];  // dP - D: the dP^T product starts from -D
         }
       };
@@ -823,13 +861,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         if constexpr (k == 0) {
           return pad_row16<D>(Kt, 16 * st + l16, 4 * n + j4);
         } else if constexpr (k == 1) {
-          if constexpr (st == 0) {
-            const int k0 = 16 * (NSB - 1) + 8 * g;
-            return pad_tr_operand<D>(Kp, k0, k0 + 4, 32 * n + 16 * hi16);
-          } else {
-            const int k0 = 16 * (st - 1) + 8 * g;
-            return pad_tr_operand<D>(Kt, k0, k0 + 4, 32 * n + 16 * hi16);
-          }
+          // half st % 2 of the dQ product of pair 1 of the previous tile (steps
+          // 0-1) or pair 0 of this one (steps 2-3): keys 4 j4 .. + 3 of both
+          // sub-blocks of the pair, head-dim tile (st % 2) NK + n
+          constexpr int J = st < 2 ? 1 : 0, nn = (st % 2) * NK + n;
+          const int k0 = 32 * J + 4 * j4;
+          return pad_tr_operand<D>(st < 2 ? Kp : Kt, k0, k0 + 16, 16 * nn);
         } else {
           return pad_row16<D>(Vt, 16 * st + l16, 4 * n + j4);
         }
@@ -848,8 +885,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
           else
             Mx<DT>::acc16(sc[cs][t], op, qb[t][s]);
         } else if constexpr (k == 1) {
-          constexpr int n = loc / 2, hh = loc % 2;
-          Mx<DT>::acc32(acc[hh][n], da[hh], op);
+          constexpr int J = st < 2 ? 1 : 0, t = loc % 4, nn = (st % 2) * NK + loc / 4;
+          Mx<DT>::acc16a(acc[t][nn], da[J][t], op);
         } else {
           constexpr int s = loc / 4, t = loc % 4;
           if constexpr (s == 0)
@@ -865,9 +902,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         constexpr int gm = decltype(gc)::value;
         using Plan = typename Steps::template P<st>;
         // dS of the previous sub-block (of the previous tile in step 0) under S^T_st
-        static_for<18>([&](auto ec) {
-          if constexpr (spread_slot(decltype(ec)::value, 18, 0, Plan::B1) == m)
-            ds_item(ec, std::integral_constant<int, cp>());
+        static_for<20>([&](auto ec) {
+          if constexpr (spread_slot(decltype(ec)::value, 20, 0, Plan::B1) == m)
+            ds_item(ec, std::integral_constant<int, cp>(), std::integral_constant<int, (st + NSB - 1) % NSB>());
         });
         static_for<16>([&](auto ec) {
           if constexpr (spread_timed<Plan>(decltype(ec)::value, 16, Plan::B1, Plan::NM) == m)
@@ -881,30 +918,33 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       };
       run_tile_carry<Steps::template P, NSB, LA>(carry, begin, operand, next, mfma, valu);
     };
-    // dS and dQ of the last computed tile's last sub-block (a no-op when no tile was
-    // computed; the operand is zeroed when no tile was even copied).
+    // dS of the last computed tile's last sub-block and the dQ product of its
+    // second pair (a no-op when no tile was computed; the operand is zeroed when no
+    // tile was even copied).
     auto flush = [&]() {
       const uint16_t* Kp = sKV[prev];
-      u32x4 da[2];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dp[t][i] = sc[1][t][i] * dp[t][i];
-      }
-      da[0] = c16_pair_to_a32(pack_c4<DT>(dp[0]), pack_c4<DT>(dp[1]));
-      da[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
+      static_for<20>([&](auto ec) {
+        constexpr int e = decltype(ec)::value, t = e / 5, i = e % 5;
+        if constexpr (i == 4) {
+          const u32x2 v = pack_c4<DT>(dp[t]);
+          da[1][t][2] = v[0];
+          da[1][t][3] = v[1];
+        } else {
+          dp[t][i] = sc[1][t][i] * dp[t][i];
+        }
+      });
       using Steps = DqSteps<NK>;
       run_tile<Steps::template Flush, 1, LA>(
           [&](auto) {},
           [&](auto, auto oc) -> u32x4 {
             constexpr int n = decltype(oc)::value;
-            const int k0 = 16 * (NSB - 1) + 8 * g;
-            const u32x4 op = pad_tr_operand<D>(Kp, k0, k0 + 4, 32 * n + 16 * hi16);
+            const int k0 = 32 + 4 * j4;
+            const u32x4 op = pad_tr_operand<D>(Kp, k0, k0 + 16, 16 * n);
             return nkt > 0 ? op : zero_u4();
           },
           [&](auto, auto mc, const u32x4& op) {
-            constexpr int loc = decltype(mc)::value, n = loc / 2, hh = loc % 2;
-            Mx<DT>::acc32(acc[hh][n], da[hh], op);
+            constexpr int loc = decltype(mc)::value, t = loc % 4, n = loc / 4;
+            Mx<DT>::acc16a(acc[t][n], da[1][t], op);
           },
           [&](auto, auto, auto) {});
     };
@@ -959,7 +999,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     lds_barrier();  // every wave is done with the tile buffers
     settle(acc);
     uint16_t* stage = &sKV[0][0] + w * 64 * (D + 8);
-    store_block64<DT, D>(acc, p.scale, stage, p.dq + qbase * D, qw, p.Nq, lane);
+    store_block64_c16<DT, D>(acc, p.scale, stage, p.dq + qbase * D, qw, p.Nq, lane);
   }
 }
 

@@ -119,6 +119,10 @@ template <> struct Mx<0> {
   static __device__ __forceinline__ void acc16(f32x4& c, const u32x4& a, const u32x4& b) {
     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
   }
+  // acc16 with a long-lived accumulator held in AGPRs
+  static __device__ __forceinline__ void acc16a(f32x4& c, const u32x4& a, const u32x4& b) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
   // first16 with the accumulator starting at c instead of zero
   static __device__ __forceinline__ f32x4 first16c(const u32x4& a, const u32x4& b, const f32x4& c) {
     f32x4 d;
@@ -138,6 +142,10 @@ template <> struct Mx<1> {
   static __device__ __forceinline__ void acc16(f32x4& c, const u32x4& a, const u32x4& b) {
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(c) : "v"(a), "v"(b));
   }
+  // acc16 with a long-lived accumulator held in AGPRs
+  static __device__ __forceinline__ void acc16a(f32x4& c, const u32x4& a, const u32x4& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
   // first16 with the accumulator starting at c instead of zero
   static __device__ __forceinline__ f32x4 first16c(const u32x4& a, const u32x4& b, const f32x4& c) {
     f32x4 d;
@@ -156,6 +164,16 @@ __device__ __forceinline__ void wait_mfma() {
 // accumulators change there, so no read of them is scheduled before the wait.
 template <int N0, int N1>
 __device__ __forceinline__ void settle(f32x16 (&acc)[N0][N1]) {
+  wait_mfma();
+#pragma unroll
+  for (int i = 0; i < N0; ++i) {
+#pragma unroll
+    for (int j = 0; j < N1; ++j) asm volatile("" : "+a"(acc[i][j]));
+  }
+}
+
+template <int N0, int N1>
+__device__ __forceinline__ void settle(f32x4 (&acc)[N0][N1]) {
   wait_mfma();
 #pragma unroll
   for (int i = 0; i < N0; ++i) {

@@ -79,23 +79,28 @@ def valu_to_mfma_hazards(ins, window=2):
     return found
 
 
-def early_result_reads(ins, wait_states=20):
+def early_result_reads(ins, wait_states=20, wait_states_16=12):
     """Vector instructions reading the result of the last inline-asm MFMA before
-    another MFMA issued and before `wait_states` wait states (s_nop N counts N+1,
-    any other instruction 1)."""
+    another MFMA issued and before `wait_states` (32x32 shapes, 16 passes) or
+    `wait_states_16` (16x16 shapes) wait states (s_nop N counts N+1, any other
+    instruction 1)."""
     found = []
-    pending, ws = set(), 0
+    pending, ws, need = set(), 0, wait_states
     for line, in_asm in ins:
+        if line.startswith("s_branch") or line.startswith("s_endpgm"):
+            pending = set()  # what follows is reached by a jump, not from here
+            continue
         if line.startswith("v_mfma"):
             ops = _operands(line)
             pending = regs(ops[0]) if (in_asm and ops) else set()
+            need = wait_states if "32x32" in line else wait_states_16
             ws = 0
             continue
         if line.startswith("s_nop"):
             ws += int(line.split()[1]) + 1
         else:
             ops = _operands(line)
-            if pending and ws < wait_states and (
+            if pending and ws < need and (
                 line.startswith("v_") or line.startswith("ds_write") or line.startswith("global_store")
                 or line.startswith("buffer_store")
             ):
@@ -105,6 +110,6 @@ def early_result_reads(ins, wait_states=20):
             if pending and line.startswith("v_") and ops:
                 pending -= regs(ops[0])  # overwritten: later reads see the new value
             ws += 1
-        if ws >= wait_states:
+        if ws >= need:
             pending = set()
     return found
