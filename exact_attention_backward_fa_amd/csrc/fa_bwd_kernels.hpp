@@ -188,10 +188,11 @@ constexpr int tile_mfmas() {
   return TileStreamOf<PlanOf, std::make_integer_sequence<int, NS>>::type::NM;
 }
 
-// Step plans.  dK/dV: S_st | dK_{st-1} | dP_st | dV_st over NSB sub-blocks plus a
-// final dK step.  The dK product of a tile's last sub-block is issued in step 0 of
-// the next tile (and after the last tile by a flush step), so every step of a tile
-// has the same shape.
+// Step plans.  dK/dV: S_st | half of a dK product | dP_st | half of a dV product;
+// the gradient products of a pair of sub-blocks (16x16x32 over their 32 query
+// rows) are issued in halves (head-dim tiles) in the steps after the pair (dV
+// from its second step on, dK one step later), so every step of a tile has the
+// same shape; a flush step issues what is left after the last tile.
 // dQ: S^T_st | half of a dQ product | dP^T_st.  The dQ product of a pair of
 // sub-blocks (16x16x32, contraction over their 32 keys) is issued in two halves
 // (head-dim tiles), in the two steps after the pair: steps 0-1 finish the previous
@@ -200,9 +201,9 @@ constexpr int tile_mfmas() {
 template <int NK>
 struct DkdvSteps {
   template <int ST>
-  using P = StepPlan<NK, 4, NK, 2, NK, 4, NK, 2>;
+  using P = StepPlan<NK, 4, NK, 4, NK, 4, NK, 4, 1>;
   template <int ST>
-  using Flush = StepPlan<0, 4, NK, 2, 0, 4, 0, 2>;
+  using Flush = StepPlan<0, 4, 2 * NK, 4, 0, 4, NK, 4, 1>;
 };
 template <int NK>
 struct DqSteps {
@@ -212,40 +213,13 @@ struct DqSteps {
   using Flush = StepPlan<0, 4, 2 * NK, 4, 0, 4, 0, 1, 1>;
 };
 
-// Store a wave's 64 x D block held in 32x32 accumulators (acc[h][n] element i of
-// lane (l32, g) is row 32h + crow_of(i, g), column 32n + l32), times `scale`, to
-// rows row0.. of a row-major [*, D] tensor; rows at or past n_rows are skipped.
-// The block goes through the wave's own LDS staging area (64 rows of D + 8
-// elements): 2-byte writes in the accumulator layout, then 16-byte row reads, so
-// the global stores are whole 16-byte pieces of consecutive rows instead of 2-byte
-// pieces of 64 rows each.
-template <int DT, int D>
-__device__ __forceinline__ void store_block64(const f32x16 (&acc)[2][D / 32], float scale,
-                                              uint16_t* __restrict__ stage, uint16_t* __restrict__ dst,
-                                              int row0, int n_rows, int lane) {
-  constexpr int SS = D + 8;     // staging row stride (elements)
-  constexpr int CPR = D / 8;    // 16-byte pieces per row
-  constexpr int RPI = 64 / CPR; // rows per read instruction
-  const int l32 = lane & 31, g = lane >> 5;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-#pragma unroll
-    for (int n = 0; n < D / 32; ++n) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        stage[(32 * h + crow_of(i, g)) * SS + 32 * n + l32] = Dt<DT>::one(acc[h][n][i] * scale);
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < 64 / RPI; ++k) {
-    const int r = k * RPI + lane / CPR, c = lane % CPR;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * SS + 8 * c);
-    if (row0 + r < n_rows) st16(dst + (size_t)(row0 + r) * D + 8 * c, v);
-  }
-}
-
-// store_block64 for a block held in 16x16 accumulators: acc[t][n] element i of
-// lane (l16, j4) is row 16t + 4 j4 + i, column 16n + l16.
+// Store a wave's 64 x D block held in 16x16 accumulators (acc[t][n] element i of
+// lane (l16, j4) is row 16t + 4 j4 + i, column 16n + l16), times `scale`, to rows
+// row0.. of a row-major [*, D] tensor; rows at or past n_rows are skipped.  The
+// block goes through the wave's own LDS staging area (64 rows of D + 8 elements):
+// 2-byte writes in the accumulator layout, then 16-byte row reads, so the global
+// stores are whole 16-byte pieces of consecutive rows instead of 2-byte pieces of
+// 64 rows each.
 template <int DT, int D>
 __device__ __forceinline__ void store_block64_c16(const f32x4 (&acc)[4][D / 16], float scale,
                                                   uint16_t* __restrict__ stage, uint16_t* __restrict__ dst,
@@ -308,25 +282,28 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // owns keys kvw = kv0 + 64w .. +63 and keeps
 //   K and V as the B operands of S = Q K^T and dP = dO V^T (16x16x32; key tile kt
 //   of 16 keys, contraction step s of 32 head dims), and
-//   dK and dV as float32 32x32 accumulators (key half h, head-dim tile n).
+//   dK and dV as float32 16x16 accumulators (key tile kt, head-dim tile n).
 // The loop runs over the G query heads of the group and their 64-row query tiles
 // from the first one that can see the key block (causal) to the end.  Query tiles
 // (Q, dO, LSE, D) are triple-buffered in LDS and copied straight from global
 // memory two iterations ahead.  A tile is processed in four 16-row sub-blocks; per
 // sub-block a wave computes
 //   S (4 key tiles), P = exp2(S s log2e - LSE log2e), dP, dS = P o (dP - D),
-//   dV += P^T dO and dK += dS^T Q (32x32x16, contraction over the 16 query rows).
-// P and dS come out of the 16x16 accumulators with the key in the lane; one
-// v_permlane16_swap per register pair turns two 16-key tiles into the 32-key A
-// operand of the 32x32x16 product, whose B operand (dO or Q with the query along
-// the slots) is a transposed LDS read.
+// and per pair of sub-blocks dV += P^T dO and dK += dS^T Q (16x16x32, contraction
+// over the pair's 32 query rows).  P and dS come out of the 16x16 accumulators
+// with the key in the lane and four query rows of the sub-block in the elements;
+// the packed tiles of the two sub-blocks side by side are the A operand's eight
+// contraction slots, with no lane exchange.  The B operand (dO or Q with the same
+// query rows along the slots) is two transposed LDS reads.  All MFMAs are
+// 16x16x32, which under the power limit sustain a higher clock than 32x32x16.
 //
 // Sub-blocks are software-pipelined: step st issues the MFMA stream
-//   S_st | dK_{st-1} | dP_st | dV_st
-// with P_st computed under dK_{st-1} and dP_st, and dS_st under dV_st.  A final
-// step issues dK of the last sub-block.  Tiles that cross the causal
-// boundary or a ragged end of this wave's block take a masked variant of the
-// softmax.
+//   S_st | half of a dK product | dP_st | half of a dV product
+// with P_st computed under the dK half and dP_st, and dS_st under the dV half.
+// The dV product of pair J runs in steps 2J+1 and 2J+2, its dK product in steps
+// 2J+2 and 2J+3 (steps 4 and 5 are steps 0 and 1 of the next tile); a final step
+// issues what is left of the last pair.  Tiles that cross the causal boundary or a
+// ragged end of this wave's block take a masked variant of the softmax.
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int KW = 64, BN = 4 * KW, BM = 64, NSB = BM / 16;
@@ -344,7 +321,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
   const int l16 = lane & 15, j4 = lane >> 4;  // 16x16 tiles: column, row group
-  const int l32 = lane & 31, g = lane >> 5, hi16 = j4 & 1;
   __shared__ int s_item;
   const WorkQueue wq(p.sched, p.B * p.Hkv, (p.Nkv + BN - 1) / BN);
   long long ticket = tid == 0 ? wq.first() : 0;
@@ -374,13 +350,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         }
       }
     }
-    f32x16 dk[2][NK], dv[2][NK];
+    f32x4 dk[4][2 * NK], dv[4][2 * NK];  // per key tile and 16-column head-dim tile
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
-      for (int n = 0; n < NK; ++n) {
-        dk[h][n] = zero16();
-        dv[h][n] = zero16();
+      for (int n = 0; n < 2 * NK; ++n) {
+        dk[kt][n] = zero4();
+        dv[kt][n] = zero4();
       }
     }
 
@@ -456,71 +432,81 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     };
 
     // Carried from tile to tile: the first LA operands of the next tile, and the
-    // dS^T operands of the last sub-block, whose dK product is issued in step 0 of
-    // the next tile with Q read from the previous buffer (zero before the first tile,
-    // which makes that product a no-op).
+    // packed P^T and dS^T of the second sub-block pair, whose dV and dK products run
+    // in steps 0-1 of the next tile with dO and Q read from the previous buffer
+    // (zero before the first tile, which makes those products no-ops).
+    //
+    // pa[J][kt] / sa[J][kt]: A operand of the dV / dK product of sub-block pair J
+    // for key tile kt: slots 0-3 the packed P^T (dS^T) of sub-block 2J (queries
+    // 4 j4 .. + 3 for this lane's key), slots 4-7 those of sub-block 2J + 1.  The
+    // first half of a pair is packed only once the previous pair's tuple has been
+    // read for the last time, so the two pairs can share registers.
     u32x4 carry[LA];
-    u32x4 sa[2] = {zero_u4(), zero_u4()};  // dS^T A operands, per key half
-    int prev = 0;                          // buffer of the previous tile
+    u32x4 pa[2][4], sa[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      pa[1][kt] = zero_u4();
+      sa[1][kt] = zero_u4();
+    }
+    int prev = 0;  // buffer of the previous tile
 
     auto compute = [&](int cur, int nxt, auto mask_c, int q0, const Src& fsrc, int fbuf) {
       constexpr bool MASK = decltype(mask_c)::value;
       const uint16_t* Qt = sQdO[cur];
       const uint16_t* dOt = Qt + BM * RS;
       const uint16_t* Qp = sQdO[prev];
+      const uint16_t* dOp = Qp + BM * RS;
       const uint16_t* Qn = sQdO[nxt];
       const float* Lt = sLD[cur][0];
       const float* Dtl = Lt + BM;
       f32x4 sc[4];    // S, then P, of the current sub-block, per key tile
       f32x4 dp[4];    // dP, then dS
-      u32x4 pa[2];    // P^T A operands, per key half
       f32x4 lq, dn;   // LSE*log2e and -D of the current sub-block's rows
       const int keyl = kvw + l16;    // key of this lane's column in key tile 0
       const int qrow = q0 + 4 * j4;  // query row of element 0 in sub-block 0
 
-      // P_st item e of 18: 16 elements, then after each key half its operand
+      using Steps = DkdvSteps<NK>;
+      // packed sub-block st into half st % 2 of pair st / 2
+      auto pack_p = [&](auto stc, auto ktc) {
+        constexpr int st = decltype(stc)::value, kt = decltype(ktc)::value;
+        const u32x2 v = pack_c4<DT>(sc[kt]);
+        pa[st / 2][kt][2 * (st % 2)] = v[0];
+        pa[st / 2][kt][2 * (st % 2) + 1] = v[1];
+      };
+      auto pack_ds = [&](auto stc, auto ktc) {
+        constexpr int st = decltype(stc)::value, kt = decltype(ktc)::value;
+        const u32x2 v = pack_c4<DT>(dp[kt]);
+        sa[st / 2][kt][2 * (st % 2)] = v[0];
+        sa[st / 2][kt][2 * (st % 2) + 1] = v[1];
+      };
+      // P_st item e of 16 (key tile e / 4, row e % 4)
       auto p_item = [&](auto ec, auto st_c) {
         constexpr int e = decltype(ec)::value, st = decltype(st_c)::value;
-        if constexpr (e == 8) {
-          pa[0] = c16_pair_to_a32(pack_c4<DT>(sc[0]), pack_c4<DT>(sc[1]));
-        } else if constexpr (e == 17) {
-          pa[1] = c16_pair_to_a32(pack_c4<DT>(sc[2]), pack_c4<DT>(sc[3]));
-        } else {
-          constexpr int x = e < 8 ? e : e - 1, kt = x / 4, i = x % 4;
-          float v = sc[kt][i] * p.scale_log2 - lq[i];
-          if constexpr (MASK) {
-            const int key = keyl + 16 * kt, q = qrow + 16 * st + i;
-            if (key >= p.Nkv || q >= p.Nq || (CAUSAL && key > q + p.off)) v = -INFINITY;
-          }
-          sc[kt][i] = fast_exp2(v);
+        constexpr int kt = e / 4, i = e % 4;
+        float v = sc[kt][i] * p.scale_log2 - lq[i];
+        if constexpr (MASK) {
+          const int key = keyl + 16 * kt, q = qrow + 16 * st + i;
+          if (key >= p.Nkv || q >= p.Nq || (CAUSAL && key > q + p.off)) v = -INFINITY;
         }
-      };
-      // dS_st item e of 18, same order
-      auto ds_item = [&](auto ec) {
-        constexpr int e = decltype(ec)::value;
-        if constexpr (e == 8) {
-          sa[0] = c16_pair_to_a32(pack_c4<DT>(dp[0]), pack_c4<DT>(dp[1]));
-        } else if constexpr (e == 17) {
-          sa[1] = c16_pair_to_a32(pack_c4<DT>(dp[2]), pack_c4<DT>(dp[3]));
-        } else {
-          constexpr int x = e < 8 ? e : e - 1, kt = x / 4, i = x % 4;
-          dp[kt][i] = sc[kt][i] * dp[kt][i];  // dP - D: the dP product starts from -D
-        }
+        sc[kt][i] = fast_exp2(v);
       };
 
-      using Steps = DkdvSteps<NK>;
       auto begin = [&](auto stc) {
         constexpr int st = decltype(stc)::value;
         lq = *reinterpret_cast<const f32x4*>(&Lt[16 * st + 4 * j4]);
         dn = *reinterpret_cast<const f32x4*>(&Dtl[16 * st + 4 * j4]);
         if constexpr (st == 2) {
-          // Mid-tile: every wave is past step 0 (its last reads of the previous
+          // Mid-tile: every wave is past steps 0-1 (its last reads of the previous
           // buffer) and, once its own copies have landed, the next tile is complete,
           // so the copies of steps 2-3 may refill the previous buffer.
           wait_vmem();
           tile_barrier();
         }
       };
+      // Stage 1 of step st: half st % 2 of the dK product of pair 1 of the previous
+      // tile (steps 0-1) or pair 0 of this one (steps 2-3).  Stage 3: half
+      // (st + 1) % 2 of the dV product of pair 0 (steps 1-2) or pair 1 (step 3, and
+      // of the previous tile in step 0).
       auto operand = [&](auto stc, auto oc) -> u32x4 {
         constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
         using Plan = typename Steps::template P<st>;
@@ -528,18 +514,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         if constexpr (k == 0) {
           return pad_row16<D>(Qt, 16 * st + l16, 4 * n + j4);
         } else if constexpr (k == 1) {
-          if constexpr (st == 0) {
-            const int k0 = 16 * (NSB - 1) + 8 * g;
-            return pad_tr_operand<D>(Qp, k0, k0 + 4, 32 * n + 16 * hi16);
-          } else {
-            const int k0 = 16 * (st - 1) + 8 * g;
-            return pad_tr_operand<D>(Qt, k0, k0 + 4, 32 * n + 16 * hi16);
-          }
+          constexpr int J = st < 2 ? 1 : 0, nn = (st % 2) * NK + n;
+          const int k0 = 32 * J + 4 * j4;
+          return pad_tr_operand<D>(st < 2 ? Qp : Qt, k0, k0 + 16, 16 * nn);
         } else if constexpr (k == 2) {
           return pad_row16<D>(dOt, 16 * st + l16, 4 * n + j4);
         } else {
-          const int k0 = 16 * st + 8 * g;
-          return pad_tr_operand<D>(dOt, k0, k0 + 4, 32 * n + 16 * hi16);
+          constexpr int J = (st == 0 || st == 3) ? 1 : 0, nn = ((st + 1) % 2) * NK + n;
+          const int k0 = 32 * J + 4 * j4;
+          return pad_tr_operand<D>(st == 0 ? dOp : dOt, k0, k0 + 16, 16 * nn);
         }
       };
       auto next = [&](auto oc) -> u32x4 {  // operand oc of the next tile: S of sub-block 0
@@ -548,37 +531,58 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       auto mfma = [&](auto stc, auto mc, const u32x4& op) {
         constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
         using Plan = typename Steps::template P<st>;
-        constexpr int k = Plan::stage(m), loc = Plan::local(m);
+        constexpr int k = Plan::stage(m), loc = Plan::local(m), o = loc / 4, kt = loc % 4;
         if constexpr (k == 0) {
-          constexpr int s = loc / 4, kt = loc % 4;
-          if constexpr (s == 0)
-            sc[kt] = Mx<DT>::first16(op, kb[kt][s]);
+          if constexpr (o == 0)
+            sc[kt] = Mx<DT>::first16(op, kb[kt][o]);
           else
-            Mx<DT>::acc16(sc[kt], op, kb[kt][s]);
+            Mx<DT>::acc16(sc[kt], op, kb[kt][o]);
         } else if constexpr (k == 1) {
-          constexpr int n = loc / 2, h = loc % 2;
-          Mx<DT>::acc32(dk[h][n], sa[h], op);
+          constexpr int J = st < 2 ? 1 : 0, nn = (st % 2) * NK + o;
+          Mx<DT>::acc16a(dk[kt][nn], sa[J][kt], op);
         } else if constexpr (k == 2) {
-          constexpr int s = loc / 4, kt = loc % 4;
-          if constexpr (s == 0)
-            dp[kt] = Mx<DT>::first16c(op, vb[kt][s], dn);
+          if constexpr (o == 0)
+            dp[kt] = Mx<DT>::first16c(op, vb[kt][o], dn);
           else
-            Mx<DT>::acc16(dp[kt], op, vb[kt][s]);
+            Mx<DT>::acc16(dp[kt], op, vb[kt][o]);
         } else {
-          constexpr int n = loc / 2, h = loc % 2;
-          Mx<DT>::acc32(dv[h][n], pa[h], op);
+          constexpr int J = (st == 0 || st == 3) ? 1 : 0, nn = ((st + 1) % 2) * NK + o;
+          Mx<DT>::acc16a(dv[kt][nn], pa[J][kt], op);
         }
       };
       auto valu = [&](auto stc, auto mc, auto gc) {
         constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
         using Plan = typename Steps::template P<st>;
+        using stp = std::integral_constant<int, st>;
         (void)gc;
-        static_for<18>([&](auto ec) {
-          if constexpr (spread_timed<Plan>(decltype(ec)::value, 18, Plan::B1, Plan::B3) == m)
-            p_item(ec, stc);
-          if constexpr (spread_slot(decltype(ec)::value, 18, Plan::B3, Plan::NM) == m)
-            ds_item(ec);
+        // P_st under the dK half and dP_st: four exponentials per key tile, then
+        // (odd st) the packed tile, before the dV half reads it
+        static_for<24>([&](auto ec) {
+          constexpr int e = decltype(ec)::value, kt = e / 6, r = e % 6;
+          if constexpr (spread_slot(e, 24, Plan::B1, Plan::B3) == m) {
+            if constexpr (r < 4)
+              p_item(std::integral_constant<int, 4 * kt + r>(), stp());
+            else if constexpr (r == 5 && st % 2 == 1)
+              pack_p(stp(), std::integral_constant<int, kt>());
+          }
         });
+        // dS_st under the dV half; odd st packs it at once
+        static_for<20>([&](auto ec) {
+          constexpr int e = decltype(ec)::value, kt = e / 5, i = e % 5;
+          if constexpr (spread_slot(e, 20, Plan::B3, Plan::NM) == m) {
+            if constexpr (i < 4)
+              dp[kt][i] = sc[kt][i] * dp[kt][i];  // dP - D: the dP product starts from -D
+            else if constexpr (st % 2 == 1)
+              pack_ds(stp(), std::integral_constant<int, kt>());
+          }
+        });
+        // even st: P_st is packed into a new pair once the dV half of this step has
+        // read key tile kt of the previous pair for the last time, and dS_{st-1}
+        // once the dK half has done the same
+        if constexpr (st % 2 == 0 && m >= Plan::NM - 4)
+          pack_p(stp(), std::integral_constant<int, m - (Plan::NM - 4)>());
+        if constexpr (st % 2 == 1 && m >= Plan::B2 - 4 && m < Plan::B2)
+          pack_ds(std::integral_constant<int, st - 1>(), std::integral_constant<int, m - (Plan::B2 - 4)>());
         // The copies of a later tile ride on the score stages (S_st) of steps 2-3,
         // which carry no other VALU work.
         if constexpr (st >= 2 && m < Plan::B1) {
@@ -590,22 +594,29 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       };
       run_tile_carry<Steps::template P, NSB, LA>(carry, begin, operand, next, mfma, valu);
     };
-    // dK of the last computed tile's last sub-block (a no-op when no tile was
-    // computed; the operand is zeroed when no tile was even copied).
+    // The dV and dK products of the last computed tile's second pair (no-ops when
+    // no tile was computed; the operands are zeroed when no tile was even copied).
     auto flush = [&]() {
       const uint16_t* Qp = sQdO[prev];
+      const uint16_t* dOp = Qp + BM * RS;
       using Steps = DkdvSteps<NK>;
+      using Plan = typename Steps::template Flush<0>;
       run_tile<Steps::template Flush, 1, LA>(
           [&](auto) {},
           [&](auto, auto oc) -> u32x4 {
-            constexpr int n = decltype(oc)::value;
-            const int k0 = 16 * (NSB - 1) + 8 * g;
-            const u32x4 op = pad_tr_operand<D>(Qp, k0, k0 + 4, 32 * n + 16 * hi16);
+            constexpr int o = decltype(oc)::value, k = Plan::op_stage(o), n = Plan::op_local(o);
+            const int k0 = 32 + 4 * j4;
+            const u32x4 op = k == 1 ? pad_tr_operand<D>(Qp, k0, k0 + 16, 16 * n)
+                                    : pad_tr_operand<D>(dOp, k0, k0 + 16, 16 * (NK + n));
             return n_it > 0 ? op : zero_u4();
           },
           [&](auto, auto mc, const u32x4& op) {
-            constexpr int loc = decltype(mc)::value, n = loc / 2, h = loc % 2;
-            Mx<DT>::acc32(dk[h][n], sa[h], op);
+            constexpr int m = decltype(mc)::value, k = Plan::stage(m), loc = Plan::local(m);
+            constexpr int o = loc / 4, kt = loc % 4;
+            if constexpr (k == 1)
+              Mx<DT>::acc16a(dk[kt][o], sa[1][kt], op);
+            else
+              Mx<DT>::acc16a(dv[kt][NK + o], pa[1][kt], op);
           },
           [&](auto, auto, auto) {});
     };
@@ -677,8 +688,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     settle(dk);
     settle(dv);
     uint16_t* stage = &sQdO[0][0] + w * 64 * (D + 8);
-    store_block64<DT, D>(dk, p.scale, stage, p.dk + kbase * D, kvw, p.Nkv, lane);
-    store_block64<DT, D>(dv, 1.f, stage, p.dv + kbase * D, kvw, p.Nkv, lane);
+    store_block64_c16<DT, D>(dk, p.scale, stage, p.dk + kbase * D, kvw, p.Nkv, lane);
+    store_block64_c16<DT, D>(dv, 1.f, stage, p.dv + kbase * D, kvw, p.Nkv, lane);
   }
 }
 

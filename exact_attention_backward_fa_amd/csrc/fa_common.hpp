@@ -108,9 +108,6 @@ template <> struct Dt<1> {
 // the end, wait_mfma() lets the last MFMAs drain.
 template <int DT> struct Mx;
 template <> struct Mx<0> {
-  static __device__ __forceinline__ void acc32(f32x16& c, const u32x4& a, const u32x4& b) {
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-  }
   static __device__ __forceinline__ f32x4 first16(const u32x4& a, const u32x4& b) {
     f32x4 d;
     asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
@@ -131,9 +128,6 @@ template <> struct Mx<0> {
   }
 };
 template <> struct Mx<1> {
-  static __device__ __forceinline__ void acc32(f32x16& c, const u32x4& a, const u32x4& b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
-  }
   static __device__ __forceinline__ f32x4 first16(const u32x4& a, const u32x4& b) {
     f32x4 d;
     asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
@@ -162,16 +156,6 @@ __device__ __forceinline__ void wait_mfma() {
 // wait_mfma() for a set of accumulators about to be read: the empty asm statements
 // (ordered after the nops, as all volatile asm) tell the compiler the
 // accumulators change there, so no read of them is scheduled before the wait.
-template <int N0, int N1>
-__device__ __forceinline__ void settle(f32x16 (&acc)[N0][N1]) {
-  wait_mfma();
-#pragma unroll
-  for (int i = 0; i < N0; ++i) {
-#pragma unroll
-    for (int j = 0; j < N1; ++j) asm volatile("" : "+a"(acc[i][j]));
-  }
-}
-
 template <int N0, int N1>
 __device__ __forceinline__ void settle(f32x4 (&acc)[N0][N1]) {
   wait_mfma();
@@ -207,19 +191,9 @@ __device__ __forceinline__ f32x4 zero4() {
   return z;
 }
 
-// Two 16x16 C tiles X (columns 0..15) and Y (columns 16..31) of the same 16 rows,
-// each packed to 16 bits (x, y: 2 dwords = rows 4*j4 .. 4*j4+3 of the lane's
-// column), become the 32x32x16 A operand of the transposed 32 x 16 block: lane l
-// gets column l % 32 of [X | Y] with slot e holding row 8*(l/32) + e.
-// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with the
-// even rows of its second, which is exactly the exchange needed.
-__device__ __forceinline__ u32x4 c16_pair_to_a32(u32x2 x, u32x2 y) {
-  const auto s0 = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
-  const auto s1 = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
-  u32x4 r = {s0[0], s1[0], s0[1], s1[1]};
-  return r;
-}
-
+// The four elements of a 16x16 C tile a lane holds (rows 4 j4 .. 4 j4 + 3 of its
+// column), packed to 16 bits: half of a 16x16x32 A/B operand whose contraction
+// runs along those rows.
 template <int DT>
 __device__ __forceinline__ u32x2 pack_c4(const f32x4& x) {
   u32x2 r = {Dt<DT>::pack2(x[0], x[1]), Dt<DT>::pack2(x[2], x[3])};
