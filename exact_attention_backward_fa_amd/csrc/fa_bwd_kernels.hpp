@@ -329,7 +329,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     lds_barrier();  // also: the previous item's staging reads are done
     const int item = __builtin_amdgcn_readfirstlane(s_item);
     if (item < 0 || item >= wq.n_items) break;
-    if (tid == 0) ticket = wq.next_ticket(ticket);
     const int rank = item / wq.n_heads, head = item % wq.n_heads;
     const int b = head / p.Hkv, hk = head % p.Hkv;
     const int kv0 = rank * BN;  // rank 0 = first key block = most query rows under the mask
@@ -683,6 +682,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     phase(qa, std::integral_constant<int, 1>());
     flush();
     phase(qt_begin, std::integral_constant<int, 0>());
+    // The next item is claimed only now (items are long: claimed at the start, the
+    // assignment would be fixed a whole item ahead); the stores below hide the
+    // atomic's latency.
+    if (tid == 0) ticket = wq.next_ticket(ticket);
     wait_vmem();    // no copy may land in LDS after the tile buffers are reused below
     lds_barrier();  // every wave is done with the tile buffers
     settle(dk);
@@ -1032,12 +1035,10 @@ hipError_t run_pre(const BwdArgs& a, bool zero, hipStream_t s) {
 template <int DT, int D, bool CAUSAL>
 hipError_t run_dkdv(const BwdArgs& a, hipStream_t s) {
   BwdParams p = make_params(a);
-  // One item per workgroup in rank order: measured on an MI355X at the causal GQA
-  // N=8192 shape, the work queues cost the dK/dV kernel about 1% (its items are
-  // long, four per compute unit) where they save the dQ pass 2-3%.
   const int items = ((a.pb.Nkv + 255) / 256) * a.pb.Hkv * a.pb.B;
-  p.sched = nullptr;
-  const dim3 grid((unsigned)items);
+  const int ncu = device_cu_count();
+  if (sched_static()) p.sched = nullptr;
+  const dim3 grid((unsigned)(p.sched && ncu > 0 && ncu < items ? ncu : items));
   hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
