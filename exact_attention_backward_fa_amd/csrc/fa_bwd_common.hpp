@@ -65,8 +65,8 @@ inline BwdParams make_params(const BwdArgs& a) {
 // in the low half, back count in the high half), so one atomic add both claims an
 // end and tells whether the item still exists.  Without counters (the problems
 // that need no workspace) item t goes to workgroup t % gridDim.x.  A ticket is
-// drawn early (next_ticket) and turned into an item later (resolve), so the
-// atomic's latency hides behind the current item.
+// drawn (next_ticket) before the current item's output stores and turned into an
+// item (resolve) after them, so the atomic's latency hides behind the stores.
 struct WorkQueue {
   unsigned long long* ctr;  // 8 zeroed counters, or null
   int n_heads, n_items, nq, hpx, per_q, x;

@@ -682,12 +682,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     phase(qa, std::integral_constant<int, 1>());
     flush();
     phase(qt_begin, std::integral_constant<int, 0>());
-    // The next item is claimed only now (items are long: claimed at the start, the
-    // assignment would be fixed a whole item ahead); the stores below hide the
-    // atomic's latency.
-    if (tid == 0) ticket = wq.next_ticket(ticket);
     wait_vmem();    // no copy may land in LDS after the tile buffers are reused below
     lds_barrier();  // every wave is done with the tile buffers
+    // The next item is claimed only now, after the last wait for memory: the stores
+    // below hide the atomic's latency (claimed at the start, it would be waited for
+    // with the item's first loads, and the assignment fixed a whole item ahead).
+    if (tid == 0) ticket = wq.next_ticket(ticket);
     settle(dk);
     settle(dv);
     uint16_t* stage = &sQdO[0][0] + w * 64 * (D + 8);
@@ -737,7 +737,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     lds_barrier();  // also: the previous item's staging reads are done
     const int item = __builtin_amdgcn_readfirstlane(s_item);
     if (item < 0 || item >= wq.n_items) break;
-    if (tid == 0) ticket = wq.next_ticket(ticket);
     const int rank = item / wq.n_heads, head = item % wq.n_heads;
     const int qt = CAUSAL ? nqt - 1 - rank : rank;
     const int b = head / p.Hq, h = head % p.Hq;
@@ -1011,6 +1010,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     phase(nkt, std::integral_constant<int, 0>());
     wait_vmem();    // no copy may land in LDS after the tile buffers are reused below
     lds_barrier();  // every wave is done with the tile buffers
+    // the next item, claimed after the last wait for memory (see the dK/dV kernel)
+    if (tid == 0) ticket = wq.next_ticket(ticket);
     settle(acc);
     uint16_t* stage = &sKV[0][0] + w * 64 * (D + 8);
     store_block64_c16<DT, D>(acc, p.scale, stage, p.dq + qbase * D, qw, p.Nq, lane);
