@@ -53,6 +53,68 @@ struct StepPlan {
   static constexpr int weight(int m) { return (stage(m) & 1) ? WODD : 1; }
 };
 
+// Issue-slot balancing.  Slot m of a step is the gap after its MFMA m.  Under one
+// 16x16x32 MFMA a wave issues about two VALU instructions at no cost (measured);
+// more work in one gap delays the next MFMA, while a gap with less leaves issue
+// time unused.  So the non-MFMA work of a step (the LDS operand reads and the waits
+// for them, the softmax and dS arithmetic, packing, copies) is placed at compile
+// time: fixed work first, then each chain of dependent items in order, every item
+// at the first slot of its window with room, else at the least loaded one.
+// Weights are in units of one full-rate VALU instruction (measured costs: an LDS
+// operand read about two, v_exp_f32 about two).
+namespace issue {
+constexpr int kRow = 2;   // one 16-byte LDS read of an operand
+constexpr int kTr = 4;    // two transposed LDS reads of an operand
+constexpr int kWait = 1;  // s_waitcnt before the first use of an operand
+constexpr int kExp = 3;   // scale-and-subtract and exponential
+constexpr int kMul = 1;
+constexpr int kPack = 2;  // two conversions
+constexpr int kCopy = 4;  // m0 set-up, its wait state and the copy
+constexpr int kCap = 3;   // fill level of a gap before the next one is used
+}  // namespace issue
+
+template <int NM>
+struct SlotLoad {
+  int load[NM];
+  int cap = issue::kCap;
+  constexpr SlotLoad() : load() {}
+  // Fill level for a chain of total weight w over slots [lo, hi]: the average
+  // load the window will carry, rounded up, and at least kCap.
+  constexpr void level(int w, int lo, int hi) {
+    int t = w;
+    for (int m = lo; m <= hi; ++m) t += load[m];
+    const int n = hi - lo + 1, avg = (t + n - 1) / n;
+    cap = avg > issue::kCap ? avg : issue::kCap;
+  }
+  // item of weight w at the first slot in [lo, hi] with room, else the least
+  // loaded one (the earliest of equals)
+  constexpr int put(int w, int lo, int hi) {
+    for (int m = lo; m <= hi; ++m) {
+      if (load[m] + w <= cap) {
+        load[m] += w;
+        return m;
+      }
+    }
+    int best = lo;
+    for (int m = lo; m <= hi; ++m)
+      if (load[m] < load[best]) best = m;
+    load[best] += w;
+    return best;
+  }
+  // the LDS reads of a plan (after the first MFMA of each operand group, for the
+  // operand LA groups ahead; odd stages are transposed) and the waits for them
+  template <class Plan, int LA>
+  constexpr void reads() {
+    for (int m = 0; m < NM; ++m) {
+      if (Plan::first(m)) {
+        const int o2 = (Plan::op_of(m) + LA) % Plan::NOP;
+        load[m] += (Plan::op_stage(o2) & 1) ? issue::kTr : issue::kRow;
+      }
+      if (m + 1 == NM || Plan::first(m + 1)) load[m] += issue::kWait;
+    }
+  }
+};
+
 // floor(a / b) for b > 0 and any sign of a.
 __device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }
 
@@ -114,10 +176,10 @@ struct TileStreamOf<PlanOf, std::integer_sequence<int, S...>> {
 };
 
 // Issue the MFMAs of one tile in order.  begin(st) runs before the first MFMA of
-// step st; operand(st, o) reads operand o of step st from LDS, LA operands ahead of
-// its first use; mfma(st, m, op) issues MFMA m of step st; valu(st, m, g) emits the
-// work placed after it (g: index of the MFMA in the whole tile).  A scheduling fence
-// after each slot keeps this order.
+// step st; operand(st, o) reads operand o of step st from LDS, right after the
+// first MFMA that uses operand o - LA; mfma(st, m, op) issues MFMA m of step st;
+// valu(st, m, g) emits the work placed after it (g: index of the MFMA in the whole
+// tile).  Scheduling fences after each MFMA and after each slot keep this order.
 template <template <int> class PlanOf, int NS, int LA, class FBegin, class FOp, class FMma,
           class FValu>
 __device__ __forceinline__ void run_tile(FBegin&& begin, FOp&& operand, FMma&& mfma, FValu&& valu) {
@@ -136,12 +198,13 @@ __device__ __forceinline__ void run_tile(FBegin&& begin, FOp&& operand, FMma&& m
     using stc = std::integral_constant<int, st>;
     if constexpr (ml == 0 && st > 0) begin(stc());
     constexpr int o = T::o_base(st) + P::op_of(ml);
+    mfma(stc(), std::integral_constant<int, ml>(), ops[o % (LA + 1)]);
+    sched_fence();
     if constexpr (P::first(ml) && o + LA < T::NOP) {
       constexpr int o2 = o + LA, st2 = T::step_of_o(o2);
       ops[o2 % (LA + 1)] = operand(std::integral_constant<int, st2>(),
                                    std::integral_constant<int, o2 - T::o_base(st2)>());
     }
-    mfma(stc(), std::integral_constant<int, ml>(), ops[o % (LA + 1)]);
     valu(stc(), std::integral_constant<int, ml>(), mc);
     sched_fence();
   });
@@ -167,6 +230,8 @@ __device__ __forceinline__ void run_tile_carry(u32x4 (&carry)[LA], FBegin&& begi
     using stc = std::integral_constant<int, st>;
     if constexpr (ml == 0 && st > 0) begin(stc());
     constexpr int o = T::o_base(st) + P::op_of(ml);
+    mfma(stc(), std::integral_constant<int, ml>(), ops[o % (LA + 1)]);
+    sched_fence();
     if constexpr (P::first(ml)) {
       constexpr int o2 = o + LA;
       if constexpr (o2 < T::NOP) {
@@ -177,7 +242,6 @@ __device__ __forceinline__ void run_tile_carry(u32x4 (&carry)[LA], FBegin&& begi
         carry[o2 - T::NOP] = next(std::integral_constant<int, o2 - T::NOP>());
       }
     }
-    mfma(stc(), std::integral_constant<int, ml>(), ops[o % (LA + 1)]);
     valu(stc(), std::integral_constant<int, ml>(), mc);
     sched_fence();
   });
@@ -211,6 +275,79 @@ struct DqSteps {
   using P = StepPlan<NK, 4, NK, 4, NK, 4, 0, 1, 1>;
   template <int ST>
   using Flush = StepPlan<0, 4, 2 * NK, 4, 0, 4, 0, 1, 1>;
+};
+
+// Slots of the non-MFMA work of dK/dV step ST (NC copies in steps 2-3):
+//   exp[kt][i] (the exponentials of P_st), pack_p[kt] (odd ST), mul[kt][i] (dS_st),
+//   pack_ds[kt] (odd ST), copy[c] (-1 where a step has no such item).
+// Fixed: the deferred packs (even ST: P_st after the dV half's last read of the
+// previous pair, slots NM-4+kt; odd ST: dS_{st-1} after the dK half's, slots
+// B2-4+kt), the next step's LSE and -D reads, the mid-tile wait.
+template <int NK, int ST, int LA, int NC>
+struct DkdvPlace {
+  using Plan = typename DkdvSteps<NK>::template P<ST>;
+  static constexpr int NM = Plan::NM;
+  int exp[4][4], pack_p[4], mul[4][4], pack_ds[4], copy[NC];
+  constexpr DkdvPlace() : exp(), pack_p(), mul(), pack_ds(), copy() {
+    SlotLoad<NM> L;
+    L.template reads<Plan, LA>();
+    L.load[NM - 1] += 2 * issue::kRow + (ST == 1 ? 2 : 0);
+    for (int kt = 0; kt < 4; ++kt) {
+      if (ST % 2 == 0) L.load[NM - 4 + kt] += issue::kPack;
+      else L.load[Plan::B2 - 4 + kt] += issue::kPack;
+    }
+    const int c0 = ST == 2 ? 0 : (NC + 1) / 2, c1 = ST == 2 ? (NC + 1) / 2 : NC;
+    for (int c = 0; c < NC; ++c) copy[c] = -1;
+    if (ST >= 2) {
+      int prev = 0;
+      L.level((c1 - c0) * issue::kCopy, 0, Plan::B1 - 1);
+      for (int c = c0; c < c1; ++c) prev = copy[c] = L.put(issue::kCopy, prev, Plan::B1 - 1);
+    }
+    int prev = Plan::B1;
+    L.level(16 * issue::kExp + (ST % 2) * 4 * issue::kPack, Plan::B1, Plan::B3 - 2);
+    for (int kt = 0; kt < 4; ++kt) {
+      for (int i = 0; i < 4; ++i) prev = exp[kt][i] = L.put(issue::kExp, prev, Plan::B3 - 2);
+      pack_p[kt] = ST % 2 == 1 ? (prev = L.put(issue::kPack, prev, Plan::B3 - 2)) : -1;
+    }
+    prev = Plan::B3;
+    L.level(16 * issue::kMul + (ST % 2) * 4 * issue::kPack, Plan::B3, NM - 1);
+    for (int kt = 0; kt < 4; ++kt) {
+      for (int i = 0; i < 4; ++i) prev = mul[kt][i] = L.put(issue::kMul, prev, NM - 1);
+      pack_ds[kt] = ST % 2 == 1 ? (prev = L.put(issue::kPack, prev, NM - 1)) : -1;
+    }
+  }
+};
+
+// Slots of the non-MFMA work of dQ step ST (NC copies in steps 2-3):
+//   mul[t][i], pack[t] (dS of the previous sub-block; the packs at least two slots
+//   before the dQ half, which may read them), exp[t][i] (P_st), copy[c].
+template <int NK, int ST, int LA, int NC>
+struct DqPlace {
+  using Plan = typename DqSteps<NK>::template P<ST>;
+  static constexpr int NM = Plan::NM;
+  int mul[4][4], pack[4], exp[4][4], copy[NC];
+  constexpr DqPlace() : mul(), pack(), exp(), copy() {
+    SlotLoad<NM> L;
+    L.template reads<Plan, LA>();
+    if (ST == 1) L.load[NM - 1] += 2;
+    int prev = 0;
+    L.level(16 * issue::kMul + 4 * issue::kPack, 0, Plan::B1 - 2);
+    for (int t = 0; t < 4; ++t) {
+      for (int i = 0; i < 4; ++i) prev = mul[t][i] = L.put(issue::kMul, prev, Plan::B1 - 2);
+      prev = pack[t] = L.put(issue::kPack, prev, Plan::B1 - 2);
+    }
+    prev = Plan::B1;
+    L.level(16 * issue::kExp, Plan::B1, NM - 1);
+    for (int t = 0; t < 4; ++t)
+      for (int i = 0; i < 4; ++i) prev = exp[t][i] = L.put(issue::kExp, prev, NM - 1);
+    const int c0 = ST == 2 ? 0 : (NC + 1) / 2, c1 = ST == 2 ? (NC + 1) / 2 : NC;
+    for (int c = 0; c < NC; ++c) copy[c] = -1;
+    if (ST >= 2) {
+      prev = 0;
+      L.level((c1 - c0) * issue::kCopy, 0, NM - 1);
+      for (int c = c0; c < c1; ++c) prev = copy[c] = L.put(issue::kCopy, prev, NM - 1);
+    }
+  }
 };
 
 // Store a wave's 64 x D block held in 16x16 accumulators (acc[t][n] element i of
@@ -553,27 +690,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
         using Plan = typename Steps::template P<st>;
         using stp = std::integral_constant<int, st>;
+        constexpr DkdvPlace<NK, st, LA, OPS> PL{};
         (void)gc;
+        // The copies of a later tile, in steps 2-3 (after the mid-tile barrier).
+        static_for<OPS>([&](auto cc) {
+          if constexpr (PL.copy[decltype(cc)::value] == m) copy_part(cc, fsrc, fbuf);
+        });
         // P_st under the dK half and dP_st: four exponentials per key tile, then
         // (odd st) the packed tile, before the dV half reads it
-        static_for<24>([&](auto ec) {
-          constexpr int e = decltype(ec)::value, kt = e / 6, r = e % 6;
-          if constexpr (spread_slot(e, 24, Plan::B1, Plan::B3) == m) {
-            if constexpr (r < 4)
-              p_item(std::integral_constant<int, 4 * kt + r>(), stp());
-            else if constexpr (r == 5 && st % 2 == 1)
-              pack_p(stp(), std::integral_constant<int, kt>());
-          }
+        static_for<4>([&](auto ktc) {
+          constexpr int kt = decltype(ktc)::value;
+          static_for<4>([&](auto ic) {
+            if constexpr (PL.exp[kt][decltype(ic)::value] == m)
+              p_item(std::integral_constant<int, 4 * kt + decltype(ic)::value>(), stp());
+          });
+          if constexpr (PL.pack_p[kt] == m) pack_p(stp(), ktc);
         });
         // dS_st under the dV half; odd st packs it at once
-        static_for<20>([&](auto ec) {
-          constexpr int e = decltype(ec)::value, kt = e / 5, i = e % 5;
-          if constexpr (spread_slot(e, 20, Plan::B3, Plan::NM) == m) {
-            if constexpr (i < 4)
-              dp[kt][i] = sc[kt][i] * dp[kt][i];  // dP - D: the dP product starts from -D
-            else if constexpr (st % 2 == 1)
-              pack_ds(stp(), std::integral_constant<int, kt>());
-          }
+        static_for<4>([&](auto ktc) {
+          constexpr int kt = decltype(ktc)::value;
+          static_for<4>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (PL.mul[kt][i] == m) dp[kt][i] = sc[kt][i] * dp[kt][i];  // the dP product starts from -D
+          });
+          if constexpr (PL.pack_ds[kt] == m) pack_ds(stp(), ktc);
         });
         // even st: P_st is packed into a new pair once the dV half of this step has
         // read key tile kt of the previous pair for the last time, and dS_{st-1}
@@ -582,19 +722,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           pack_p(stp(), std::integral_constant<int, m - (Plan::NM - 4)>());
         if constexpr (st % 2 == 1 && m >= Plan::B2 - 4 && m < Plan::B2)
           pack_ds(std::integral_constant<int, st - 1>(), std::integral_constant<int, m - (Plan::B2 - 4)>());
-        // The copies of a later tile ride on the score stages (S_st) of steps 2-3,
-        // which carry no other VALU work.
-        if constexpr (st >= 2 && m < Plan::B1) {
-          static_for<OPS>([&](auto cc) {
-            if constexpr (spread_slot(decltype(cc)::value, OPS, 0, 2 * Plan::B1) == (st - 2) * Plan::B1 + m)
-              copy_part(cc, fsrc, fbuf);
-          });
-        }
       };
       run_tile_carry<Steps::template P, NSB, LA>(carry, begin, operand, next, mfma, valu);
     };
     // The dV and dK products of the last computed tile's second pair (no-ops when
-    // no tile was computed; the operands are zeroed when no tile was even copied).
+    // no tile was computed; skipped when no tile was even copied, as the buffers
+    // then hold no data).
     auto flush = [&]() {
       const uint16_t* Qp = sQdO[prev];
       const uint16_t* dOp = Qp + BM * RS;
@@ -605,9 +738,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           [&](auto, auto oc) -> u32x4 {
             constexpr int o = decltype(oc)::value, k = Plan::op_stage(o), n = Plan::op_local(o);
             const int k0 = 32 + 4 * j4;
-            const u32x4 op = k == 1 ? pad_tr_operand<D>(Qp, k0, k0 + 16, 16 * n)
-                                    : pad_tr_operand<D>(dOp, k0, k0 + 16, 16 * (NK + n));
-            return n_it > 0 ? op : zero_u4();
+            return k == 1 ? pad_tr_operand<D>(Qp, k0, k0 + 16, 16 * n)
+                          : pad_tr_operand<D>(dOp, k0, k0 + 16, 16 * (NK + n));
           },
           [&](auto, auto mc, const u32x4& op) {
             constexpr int m = decltype(mc)::value, k = Plan::stage(m), loc = Plan::local(m);
@@ -680,7 +812,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     phase(qe, std::integral_constant<int, 1>());
     phase(qb, std::integral_constant<int, 2>());
     phase(qa, std::integral_constant<int, 1>());
-    flush();
+    if (n_it > 0) flush();
     phase(qt_begin, std::integral_constant<int, 0>());
     wait_vmem();    // no copy may land in LDS after the tile buffers are reused below
     lds_barrier();  // every wave is done with the tile buffers
@@ -908,32 +1040,30 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
             Mx<DT>::acc16(dp[t], op, db[t][s]);
         }
       };
-      constexpr int NMT = tile_mfmas<Steps::template P, NSB>();
-      constexpr int M2 = NMT / 2;  // first MFMA of step 2
       auto valu = [&](auto stc, auto mc, auto gc) {
         constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cp = (st + 1) & 1;
-        constexpr int gm = decltype(gc)::value;
-        using Plan = typename Steps::template P<st>;
+        constexpr DqPlace<NK, st, LA, OPS> PL{};
+        (void)gc;
+        // the copies of a later tile, in steps 2-3 (after the mid-tile barrier)
+        static_for<OPS>([&](auto cc) {
+          if constexpr (PL.copy[decltype(cc)::value] == m) copy_part(cc, fsrc, fbuf);
+        });
         // dS of the previous sub-block (of the previous tile in step 0) under S^T_st
         static_for<20>([&](auto ec) {
-          if constexpr (spread_slot(decltype(ec)::value, 20, 0, Plan::B1) == m)
+          constexpr int e = decltype(ec)::value, t = e / 5, i = e % 5;
+          if constexpr ((i < 4 ? PL.mul[t][i % 4] : PL.pack[t]) == m)
             ds_item(ec, std::integral_constant<int, cp>(), std::integral_constant<int, (st + NSB - 1) % NSB>());
         });
         static_for<16>([&](auto ec) {
-          if constexpr (spread_timed<Plan>(decltype(ec)::value, 16, Plan::B1, Plan::NM) == m)
-            p_item(ec, stc);
-        });
-        // the copies of a later tile, spread over steps 2-3
-        static_for<OPS>([&](auto cc) {
-          if constexpr (spread_slot(decltype(cc)::value, OPS, M2, NMT) == gm)
-            copy_part(cc, fsrc, fbuf);
+          constexpr int e = decltype(ec)::value;
+          if constexpr (PL.exp[e / 4][e % 4] == m) p_item(ec, stc);
         });
       };
       run_tile_carry<Steps::template P, NSB, LA>(carry, begin, operand, next, mfma, valu);
     };
     // dS of the last computed tile's last sub-block and the dQ product of its
-    // second pair (a no-op when no tile was computed; the operand is zeroed when no
-    // tile was even copied).
+    // second pair (a no-op when no tile was computed; skipped when no tile was
+    // even copied, as the buffers then hold no data).
     auto flush = [&]() {
       const uint16_t* Kp = sKV[prev];
       static_for<20>([&](auto ec) {
@@ -952,8 +1082,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
           [&](auto, auto oc) -> u32x4 {
             constexpr int n = decltype(oc)::value;
             const int k0 = 32 + 4 * j4;
-            const u32x4 op = pad_tr_operand<D>(Kp, k0, k0 + 16, 16 * n);
-            return nkt > 0 ? op : zero_u4();
+            return pad_tr_operand<D>(Kp, k0, k0 + 16, 16 * n);
           },
           [&](auto, auto mc, const u32x4& op) {
             constexpr int loc = decltype(mc)::value, t = loc % 4, n = loc / 4;
@@ -1006,7 +1135,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     };
     phase(n_un, std::integral_constant<int, 2>());
     phase(n_vis, std::integral_constant<int, 1>());
-    flush();
+    if (nkt > 0) flush();
     phase(nkt, std::integral_constant<int, 0>());
     wait_vmem();    // no copy may land in LDS after the tile buffers are reused below
     lds_barrier();  // every wave is done with the tile buffers
