@@ -237,4 +237,33 @@ __device__ __forceinline__ void store_block64_c16(const f32x4 (&acc)[4][D / 16],
   }
 }
 
+// store_block64_c16 with a scale per row: row 16t + 4 j4 + i of the lane's
+// accumulators is multiplied by scale[t][i]; acc holds D / 16 head-dim tiles per
+// query tile (further tiles are ignored).
+template <int DT, int D, int NT>
+__device__ __forceinline__ void store_block64_rows(const f32x4 (&acc)[4][NT], const float (&scale)[4][4],
+                                                   uint16_t* __restrict__ stage, uint16_t* __restrict__ dst,
+                                                   int row0, int n_rows, int lane) {
+  static_assert(NT >= D / 16, "a head-dim tile per 16 columns");
+  constexpr int SS = D + 8;
+  constexpr int CPR = D / 8;
+  constexpr int RPI = 64 / CPR;
+  const int l16 = lane & 15, j4 = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        stage[(16 * t + 4 * j4 + i) * SS + 16 * n + l16] = Dt<DT>::one(acc[t][n][i] * scale[t][i]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 64 / RPI; ++k) {
+    const int r = k * RPI + lane / CPR, c = lane % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * SS + 8 * c);
+    if (row0 + r < n_rows) st16(dst + (size_t)(row0 + r) * D + 8 * c, v);
+  }
+}
+
 }  // namespace fa
