@@ -1,409 +1,8 @@
-// Forward kernel: O and LSE of exact softmax attention.
-//
-// The backward needs the per-row log-sum-exp of the scaled scores (rustytorch
-// "flash_attention_backward.cu" and the Triton issue "Extra transposes cause 8x
-// speedup for sequence-parallel Flash Attention backward" both rebuild P as
-// exp(S - LSE) from it); no page prints a forward kernel, so this one is the
-// usual streaming (online) softmax over key tiles, built from the same pieces as
-// the backward's dQ pass.
-//
-// One workgroup = 4 waves = 256 query rows of one (batch, query head); wave w owns
-// queries qw = q0 + 64w .. +63 and keeps Q as the B operand of S^T = K Q^T
-// (16x16x32; query tile t of 16 queries) and O as float32 16x16 accumulators
-// (query tile t, head-dim tile n).  Key/value tiles of 64 rows are triple-buffered
-// in LDS and copied straight from global memory.  A tile is processed as two pairs
-// of 16-key sub-blocks; step J of a tile issues
-//   S^T of pair J | O += P V of the previous pair
-// P of a pair is the two sub-blocks' packed 16x16 tiles side by side (a lane holds
-// keys 4 j4 .. + 3 of each for its query), the A operand of a 16x16x32 product
-// whose B operand (V with the same keys along the slots) is two transposed reads.
-//
-// Online softmax without rescaling: each query column keeps a reference m (log2
-// domain, scale * log2 e folded in), set from the first pair in which the column
-// sees a key, and P = exp2(s c - m).  P and the float32 sums stay far from
-// overflow as long as no score exceeds m + 64 (P < 2^64; relative precision does
-// not depend on the size), so O and the row sums never need rescaling.  A score
-// above m + 64 after the first pair (logits rising by more than 44 nats along the
-// row) raises m and marks the item; the workgroup then runs the item a second time
-// from zero with the raised references, which no score can exceed by more than 64.
-// The row sums l of P are float32 (each lane sums its keys; the four lanes of a
-// column are added at the end; summing the bf16-rounded P through the matrix
-// pipe was measured to miss the LSE bound on short rows).  At the end O is divided
-// by l and LSE = ln 2 (m + log2 l).
-#include "fa_internal.hpp"
-#include "fa_pipeline.hpp"
-
-#include <type_traits>
+// Forward entry point: dispatch of a problem to its instance of the forward kernel
+// (fa_fwd_kernels.hpp).
+#include "fa_fwd_kernels.hpp"
 
 namespace fa {
-
-struct FwdParams {
-  const uint16_t* q;
-  const uint16_t* k;
-  const uint16_t* v;
-  uint16_t* o;
-  float* lse;
-  int B, Hq, Hkv, Nq, Nkv, G, off;  // off = Nkv - Nq (bottom-right causal offset)
-  float scale_log2;
-};
-
-constexpr float kHeadroom = 64.f;  // log2 headroom above the reference of a query column
-
-// Step J: S^T of pair J (2 NK operands x 4 query tiles) | P V of the previous pair
-// (2 NK head-dim tiles x 4).
-template <int NK>
-struct FwdSteps {
-  template <int ST>
-  using P = StepPlan<2 * NK, 4, 2 * NK, 4, 0, 1, 0, 1, 1>;
-  template <int ST>
-  using Flush = StepPlan<0, 4, 2 * NK, 4, 0, 1, 0, 1, 1>;
-};
-
-// Slots of the non-MFMA work of forward step ST (NC copies in step 1): mx[t] (the
-// pair's maxima), check (the test for a raised reference), exp[sb][t][i],
-// pack[sb][t] and sum[sb][t] (the tile's P into the row sums).
-template <int NK, int ST, int LA, int NC>
-struct FwdPlace {
-  using Plan = typename FwdSteps<NK>::template P<ST>;
-  static constexpr int NM = Plan::NM;
-  int mx[4], check, exp[2][4][4], pack[2][4], sum[2][4], copy[NC];
-  constexpr FwdPlace() : mx(), check(), exp(), pack(), sum(), copy() {
-    SlotLoad<NM> L;
-    L.template reads<Plan, LA>();
-    if (ST == 0) L.load[NM - 1] += 2;  // the mid-tile wait and barrier
-    int prev = Plan::B1;
-    L.level(4 * 5 + 3, Plan::B1, Plan::B1 + 11);
-    for (int t = 0; t < 4; ++t) prev = mx[t] = L.put(5, prev, Plan::B1 + 11);
-    prev = check = L.put(3, prev + 1, Plan::B1 + 12);
-    L.level(32 * issue::kExp + 8 * (issue::kPack + 4 * issue::kMul), prev + 1, NM - 2);
-    prev = prev + 1;
-    for (int g = 0; g <= 8; ++g) {
-      if (g < 8)
-        for (int i = 0; i < 4; ++i) prev = exp[g / 4][g % 4][i] = L.put(issue::kExp, prev, NM - 2);
-      if (g > 0) {
-        prev = pack[(g - 1) / 4][(g - 1) % 4] = L.put(issue::kPack, prev, NM - 2);
-        prev = sum[(g - 1) / 4][(g - 1) % 4] = L.put(4 * issue::kMul, prev, NM - 2);
-      }
-    }
-    for (int c = 0; c < NC; ++c) copy[c] = -1;
-    if (ST == 1) {
-      prev = 0;
-      L.level(NC * issue::kCopy, 0, NM - 1);
-      for (int c = 0; c < NC; ++c) prev = copy[c] = L.put(issue::kCopy, prev, NM - 1);
-    }
-  }
-};
-
-template <int DT, int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
-  constexpr int QW = 64, BM = 4 * QW, BN = 64, NST = 2;
-  constexpr int NK = D / 32;
-  constexpr int NBUF = 3;
-  constexpr int RS = PadTile<D>::RS;
-  constexpr int OPS = 2 * BN * PadTile<D>::GR / 256;  // copy instructions per fetch per wave
-  constexpr int LA = 2;
-  __shared__ __attribute__((aligned(16))) uint16_t sKV[NBUF][2 * BN * RS];  // K, V: a padded pair
-  static_assert(NBUF * 2 * BN * RS >= 4 * 64 * (D + 8), "the output staging must fit the tile buffers");
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l16 = lane & 15, j4 = lane >> 4;
-  const int nqt = (p.Nq + BM - 1) / BM;
-  const int n_heads = p.B * p.Hq;
-  const int rank = blockIdx.x / n_heads, head = blockIdx.x % n_heads;
-  // causal: the last query block sees the most keys, so it goes out first
-  const int qt = CAUSAL ? nqt - 1 - rank : rank;
-  const int b = head / p.Hq, h = head % p.Hq;
-  const int hk = h / p.G;
-  const int q0 = qt * BM;
-  const int qw = q0 + QW * w;
-  const size_t qbase = ((size_t)b * p.Hq + h) * (size_t)p.Nq;
-  const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
-  const uint16_t* __restrict__ K = p.k + kbase * D;
-  const uint16_t* __restrict__ V = p.v + kbase * D;
-  const float c = p.scale_log2;
-
-  u32x4 qb[4][NK];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int q = qw + 16 * t + l16;
-#pragma unroll
-    for (int s = 0; s < NK; ++s)
-      qb[t][s] = q < p.Nq ? ld16(p.q + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
-  }
-  f32x4 acc[4][2 * NK];  // O per query tile and head-dim tile
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-#pragma unroll
-    for (int n = 0; n < 2 * NK; ++n) acc[t][n] = zero4();
-  }
-  float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's part of its column's row sum
-  // reference of this lane's query column per query tile, and the raw-score
-  // threshold (m + 64) / c above which it is raised; finite, so that a column with
-  // no visible key yet gives exp2(-inf - m) = 0
-  constexpr float kUnset = -1e30f;
-  float m[4], thr[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    m[t] = kUnset;
-    thr[t] = (m[t] + kHeadroom) / c;
-  }
-  bool dirty = false;  // a reference was raised after it had been used
-  __shared__ int s_dirty;
-
-  int kv_end = p.Nkv;
-  if (CAUSAL) {
-    const int q_last = min(q0 + BM, p.Nq) - 1;
-    kv_end = min(p.Nkv, q_last + p.off + 1);
-  }
-  const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
-
-  using Copy = PadPairDma<D, BN>;
-  const uint16_t* __restrict__ tsrc = w < 2 ? K : V;
-  auto src_of = [&](int kt) {
-    const int k0 = min(kt, nkt - 1) * BN;
-    return buf_rsrc(tsrc + (size_t)k0 * D, (p.Nkv - k0) * D * 2);
-  };
-  int voff[Copy::PER_WAVE];
-#pragma unroll
-  for (int cc = 0; cc < Copy::PER_WAVE; ++cc) voff[cc] = Copy::src_offset(cc, w, lane);
-  const uint32_t wave_off = Copy::lds_wave_offset(w);
-  auto copy_part = [&](auto cc, const i32x4& sr, int buf) {
-    constexpr int ci = decltype(cc)::value;
-    bdma16<Copy::template lds_offset<ci>>(voff[ci], sr, lds_u32(sKV[buf]) + wave_off);
-  };
-  auto copy_all = [&](int kt, int buf) {
-    const i32x4 sr = src_of(kt);
-    static_for<OPS>([&](auto cc) { copy_part(cc, sr, buf); });
-  };
-
-  // Carried from tile to tile: the first LA operands of the next tile and the packed
-  // P of the second pair (pa[1]), whose product runs in step 0 of the next tile
-  // with V read from the previous buffer (zero before the first tile).
-  u32x4 carry[LA];
-  u32x4 pa[2][4];  // P A operands of pair J, per query tile
-  f32x4 sc[2][4];  // S^T of the current pair's sub-blocks, then P
-#pragma unroll
-  for (int t = 0; t < 4; ++t) pa[1][t] = zero_u4();
-  int prev = 0;
-
-  auto compute = [&](int cur, int nxt, auto mask_c, int kv0, const i32x4& fsrc, int fbuf) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    const uint16_t* Kt = sKV[cur];
-    const uint16_t* Vt = Kt + BN * RS;
-    const uint16_t* Vp = sKV[prev] + BN * RS;
-    const uint16_t* Kn = sKV[nxt];
-    float mx[4];
-
-    using Steps = FwdSteps<NK>;
-    auto begin = [&](auto stc) {
-      constexpr int st = decltype(stc)::value;
-      if constexpr (st == 1) {
-        // Mid-tile: every wave is past step 0 (its last read of the previous buffer)
-        // and, once its own copies have landed, the next tile is complete, so the
-        // copies of step 1 may refill the previous buffer.
-        wait_vmem();
-        tile_barrier();
-      }
-    };
-    auto operand = [&](auto stc, auto oc) -> u32x4 {
-      constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
-      using Plan = typename Steps::template P<st>;
-      constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
-      if constexpr (k == 0) {
-        return pad_row16<D>(Kt, 16 * (2 * st + n / NK) + l16, 4 * (n % NK) + j4);
-      } else {
-        // pair 1 of the previous tile (step 0) or pair 0 of this one (step 1)
-        constexpr int J = st == 0 ? 1 : 0;
-        const int k0 = 32 * J + 4 * j4;
-        return pad_tr_operand<D>(st == 0 ? Vp : Vt, k0, k0 + 16, 16 * n);
-      }
-    };
-    auto next = [&](auto oc) -> u32x4 {  // operand oc of the next tile: S^T of pair 0
-      constexpr int o = decltype(oc)::value;
-      return pad_row16<D>(Kn, 16 * (o / NK) + l16, 4 * (o % NK) + j4);
-    };
-    auto mfma = [&](auto stc, auto mc, const u32x4& op) {
-      constexpr int st = decltype(stc)::value, mi = decltype(mc)::value;
-      using Plan = typename Steps::template P<st>;
-      constexpr int k = Plan::stage(mi), loc = Plan::local(mi), o = loc / 4, t = loc % 4;
-      constexpr int J = st == 0 ? 1 : 0;
-      if constexpr (k == 0) {
-        constexpr int sb = o / NK, s = o % NK;
-        if constexpr (s == 0)
-          sc[sb][t] = Mx<DT>::first16(op, qb[t][s]);
-        else
-          Mx<DT>::acc16(sc[sb][t], op, qb[t][s]);
-      } else {
-        Mx<DT>::acc16a(acc[t][o], pa[J][t], op);
-      }
-    };
-    auto valu = [&](auto stc, auto mc, auto gc) {
-      constexpr int st = decltype(stc)::value, mi = decltype(mc)::value;
-      using Plan = typename Steps::template P<st>;
-      constexpr FwdPlace<NK, st, LA, OPS> PL{};
-      (void)gc;
-      static_for<OPS>([&](auto cc) {
-        if constexpr (PL.copy[decltype(cc)::value] == mi) copy_part(cc, fsrc, fbuf);
-      });
-      // the pair's maximum per query column (masked scores first)
-      static_for<4>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        if constexpr (PL.mx[t] == mi) {
-          if constexpr (MASK) {
-            const int q = qw + 16 * t + l16;
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int key = kv0 + 16 * (2 * st + sb) + 4 * j4 + i;
-                if (key >= p.Nkv || (CAUSAL && key > q + p.off)) sc[sb][t][i] = -INFINITY;
-              }
-            }
-          }
-          mx[t] = fmaxf(fmaxf(fmaxf(sc[0][t][0], sc[0][t][1]), fmaxf(sc[0][t][2], sc[0][t][3])),
-                        fmaxf(fmaxf(sc[1][t][0], sc[1][t][1]), fmaxf(sc[1][t][2], sc[1][t][3])));
-        }
-      });
-      if constexpr (PL.check == mi) {
-        bool any = false;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) any = any || mx[t] > thr[t];
-        if (__builtin_amdgcn_ballot_w64(any) != 0) {  // rare: set or raise references
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            float v = mx[t] * c;
-            v = fmaxf(v, __shfl_xor(v, 16));
-            v = fmaxf(v, __shfl_xor(v, 32));
-            if (v > m[t] + kHeadroom) {
-              dirty = dirty || m[t] != kUnset;
-              m[t] = v;
-              thr[t] = (v + kHeadroom) / c;
-            }
-          }
-        }
-      }
-      static_for<2>([&](auto sbc) {
-        constexpr int sb = decltype(sbc)::value;
-        static_for<4>([&](auto tc) {
-          constexpr int t = decltype(tc)::value;
-          static_for<4>([&](auto ic) {
-            constexpr int i = decltype(ic)::value;
-            if constexpr (PL.exp[sb][t][i] == mi) sc[sb][t][i] = fast_exp2(sc[sb][t][i] * c - m[t]);
-          });
-          if constexpr (PL.pack[sb][t] == mi) {
-            const u32x2 v = pack_c4<DT>(sc[sb][t]);
-            pa[st][t][2 * sb] = v[0];
-            pa[st][t][2 * sb + 1] = v[1];
-          }
-          if constexpr (PL.sum[sb][t] == mi)
-            lsum[t] += (sc[sb][t][0] + sc[sb][t][1]) + (sc[sb][t][2] + sc[sb][t][3]);
-        });
-      });
-    };
-    run_tile_carry<Steps::template P, NST, LA>(carry, begin, operand, next, mfma, valu);
-  };
-  // P V and row sums of the last computed tile's second pair (a no-op when no tile
-  // was computed).
-  auto flush = [&]() {
-    const uint16_t* Vp = sKV[prev] + BN * RS;
-    using Steps = FwdSteps<NK>;
-    using Plan = typename Steps::template Flush<0>;
-    run_tile<Steps::template Flush, 1, LA>(
-        [&](auto) {},
-        [&](auto, auto oc) -> u32x4 {
-          constexpr int n = Plan::op_local(decltype(oc)::value);
-          const int k0 = 32 + 4 * j4;
-          return pad_tr_operand<D>(Vp, k0, k0 + 16, 16 * n);
-        },
-        [&](auto, auto mc, const u32x4& op) {
-          constexpr int loc = Plan::local(decltype(mc)::value), o = loc / 4, t = loc % 4;
-          Mx<DT>::acc16a(acc[t][o], pa[1][t], op);
-        },
-        [&](auto, auto, auto) {});
-  };
-
-  // This wave's split of the key tiles (one variant of the math per loop):
-  //   [0, n_un)      every pair visible          unmasked
-  //   [n_un, n_vis)  causal boundary / ragged    masked
-  //   [n_vis, nkt)   no key visible to the wave  skipped
-  int n_vis = nkt;
-  if (qw >= p.Nq) n_vis = 0;
-  else if (CAUSAL) n_vis = min(nkt, max(0, floor_div(qw + QW - 1 + p.off, BN) + 1));
-  int n_un = min(n_vis, p.Nkv / BN);
-  if (CAUSAL) n_un = min(n_un, max(0, floor_div(qw + p.off - (BN - 1), BN) + 1));
-
-  if (tid == 0) s_dirty = 0;
-  // One pass, or two when a reference had to be raised after use (see the top).
-  for (int pass = 0;; ++pass) {
-    if (nkt > 0) {
-      static_for<NBUF - 1>([&](auto bc) { copy_all(decltype(bc)::value, decltype(bc)::value); });
-    }
-    // The register preloads and the first tiles' copies are in flight together; the
-    // copies are invisible to the compiler's wait counting, so all are waited for.
-    wait_vmem();
-    lds_barrier();
-    static_for<LA>([&](auto oc) {
-      constexpr int o = decltype(oc)::value;
-      carry[o] = pad_row16<D>(sKV[0], 16 * (o / NK) + l16, 4 * (o % NK) + j4);
-    });
-    int kt = 0, cur = 0;
-    prev = 0;
-    auto phase = [&](int end, auto variant) {
-      constexpr int VAR = decltype(variant)::value;  // 0 skip, 1 masked, 2 unmasked
-      for (; kt < end; ++kt) {
-        const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
-        const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
-        const i32x4 fsrc = src_of(kt + NBUF - 1);
-        if constexpr (VAR == 0) {
-          wait_vmem();
-          tile_barrier();
-          copy_all(kt + NBUF - 1, fbuf);
-        }
-        if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), kt * BN, fsrc, fbuf);
-        if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), kt * BN, fsrc, fbuf);
-        prev = cur;
-        cur = nxt;
-      }
-    };
-    phase(n_un, std::integral_constant<int, 2>());
-    phase(n_vis, std::integral_constant<int, 1>());
-    if (nkt > 0) flush();
-    phase(nkt, std::integral_constant<int, 0>());
-    wait_vmem();    // no copy may land in LDS after the tile buffers are reused below
-    if (dirty) s_dirty = 1;
-    lds_barrier();  // every wave is done with the tile buffers; s_dirty is final
-    if (pass > 0 || __builtin_amdgcn_readfirstlane(s_dirty) == 0) break;
-    // run again from zero with the raised references
-    settle(acc);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      pa[1][t] = zero_u4();
-      lsum[t] = 0.f;
-#pragma unroll
-      for (int n = 0; n < 2 * NK; ++n) acc[t][n] = zero4();
-    }
-    dirty = false;
-    lds_barrier();  // the s_dirty reads are done before the next pass's copies
-  }
-  settle(acc);
-
-  // O = acc / l per row; LSE = ln 2 (m + log2 l), -inf for a row that sees no key
-  float inv[4][4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    float l = lsum[t];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    const int q = qw + 16 * t + l16;
-    if (j4 == 0 && q < p.Nq) p.lse[qbase + q] = l > 0.f ? (m[t] + log2f(l)) * kLn2 : -INFINITY;
-    const float il = l > 0.f ? 1.f / l : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) inv[t][i] = __shfl(il, 4 * j4 + i);  // row 16t + 4 j4 + i
-  }
-  uint16_t* stage = &sKV[0][0] + w * 64 * (D + 8);
-  store_block64_rows<DT, D>(acc, inv, stage, p.o + qbase * D, qw, p.Nq, lane);
-}
 
 template <int DT, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {

@@ -1,6 +1,6 @@
-"""CPU check of the backward kernels' assembly for the inline-MFMA hazards the
-compiler does not track (see tests/asm_check.py).  Compiles two template
-instances of the backward kernels to gfx950 assembly (no GPU needed)."""
+"""CPU check of the kernels' assembly for the inline-MFMA hazards the compiler
+does not track (see tests/asm_check.py).  Compiles two template instances of the
+backward and the forward kernels to gfx950 assembly (no GPU needed)."""
 import os
 import shutil
 import subprocess
@@ -15,6 +15,7 @@ from tests import asm_check
 # extreme of the template parameters
 INSTANCES = [(1, 128, 1), (0, 64, 0)]
 KERNELS = ("bwd_dkdv_kernel", "bwd_dq_kernel")
+FWD_INSTANCES = [(1, 128, 1), (0, 64, 0)]
 
 
 def _have_hipcc():
@@ -39,6 +40,17 @@ def assembly():
                    os.path.join(fabuild.CSRC, "fa_bwd_inst.hip"), "-o", out]
             procs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
                                                 text=True)))
+        for dt, d, c in FWD_INSTANCES:
+            src = os.path.join(tmp, f"fwd_{dt}_{d}_{c}.hip")
+            with open(src, "w") as f:
+                f.write('#include "fa_fwd_kernels.hpp"\n'
+                        f"template __global__ void fa::fwd_kernel<{dt}, {d}, {'true' if c else 'false'}>"
+                        "(fa::FwdParams);\n")
+            out = src[:-4] + ".s"
+            cmd = [fabuild.hipcc(), *[f for f in fabuild.HIP_FLAGS if f != "-fPIC"], "-I", fabuild.CSRC,
+                   "--cuda-device-only", "-S", src, "-o", out]
+            procs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                                text=True)))
         texts = {}
         for out, p in procs:
             log, _ = p.communicate(timeout=900)
@@ -53,13 +65,13 @@ def assembly():
 def _kernels(texts):
     for name, text in texts.items():
         for sym, ins in asm_check.kernel_bodies(text).items():
-            if any(k in sym for k in KERNELS):
+            if any(k in sym for k in KERNELS) or "fwd_kernel" in sym:
                 yield f"{name}:{sym}", ins
 
 
 def test_kernels_found(assembly):
     found = [s for s, _ in _kernels(assembly)]
-    assert len(found) == len(INSTANCES) * len(KERNELS), found
+    assert len(found) == len(INSTANCES) * len(KERNELS) + len(FWD_INSTANCES), found
 
 
 def test_no_valu_write_right_before_inline_mfma(assembly):

@@ -181,6 +181,31 @@ def test_edge_shapes(shape, device):
         pu.assert_within(case, pu.compare(case, got, ref, mode))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_logits(causal, device):
+    """Scores that rise by about 115 log2 units along every row: the forward's
+    per-column softmax reference, set from the first pair of keys, is then exceeded
+    by more than its 64-unit headroom and the workgroup reruns its item with raised
+    references.  Forward and backward must still match the oracle."""
+    B, Hq, Hkv, N, d = 1, 2, 1, 384, 64
+    g = torch.Generator().manual_seed(4242)
+    u = torch.full((d,), 1.0 / np.sqrt(d))
+    ramp = torch.arange(N, dtype=torch.float32) / N
+    x = {
+        "q": (5.0 * u + 0.5 * torch.randn(B, Hq, N, d, generator=g)).to(torch.bfloat16),
+        "k": (16.0 * ramp[:, None] * u + 0.5 * torch.randn(B, Hkv, N, d, generator=g)).to(torch.bfloat16),
+        "v": torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16),
+        "do": torch.randn(B, Hq, N, d, generator=g).to(torch.bfloat16),
+    }
+    case = inputs.Case("rising", 0, 0, B, Hq, Hkv, N, N, d, "bf16", causal, 1.0)
+    o, lse = orc.forward(x["q"], x["k"], x["v"], case.scale, causal)
+    dq, dk, dv = orc.backward(x["q"], x["k"], x["v"], x["do"], case.scale, causal)
+    ref = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    res = pu.gpu_forward_backward(case, x, device)
+    got = {k: res[k].double().numpy() for k in res}
+    pu.assert_within(case, pu.compare(case, got, ref))
+
+
 @pytest.mark.parametrize("dims", [(0, 4, 2, 16, 16), (2, 4, 2, 0, 16), (2, 4, 2, 16, 0),
                                   (2, 4, 2, 0, 0)])
 def test_zero_sizes(dims, device):
