@@ -28,7 +28,7 @@ ROOT = os.path.dirname(PKG)
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("csrc/fa_bwd.hip", "csrc/fa_bwd_inst.hip", "csrc/fa_bwd_kernels.hpp",
                   "csrc/fa_bwd_atomic.hpp", "csrc/fa_bwd_common.hpp", "csrc/fa_fwd.hip",
-                  "csrc/fa_common.hpp")
+                  "csrc/fa_fwd_kernels.hpp", "csrc/fa_pipeline.hpp", "csrc/fa_common.hpp")
 COPY_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_llama_gqa_bf16_8192.md")
 
