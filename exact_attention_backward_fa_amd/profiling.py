@@ -1,7 +1,7 @@
 """Summaries of rocprofv3 output for the committed profiles.
 
     python -m exact_attention_backward_fa_amd.profiling trace  <dir> <out.md> "<command>"
-    python -m exact_attention_backward_fa_amd.profiling traffic <fetch_dir> <write_dir> <out.md> "<commands>"
+    python -m exact_attention_backward_fa_amd.profiling traffic <fetch_dir> <write_dir> <out.txt> "<commands>"
 
 ``trace`` reads the kernel statistics a ``rocprofv3 --kernel-trace --stats
 --output-format csv`` run writes and tabulates per-kernel average durations.
@@ -30,7 +30,7 @@ KERNEL_SOURCES = ("csrc/fa_bwd.hip", "csrc/fa_bwd_inst.hip", "csrc/fa_bwd_kernel
                   "csrc/fa_bwd_atomic.hpp", "csrc/fa_bwd_common.hpp", "csrc/fa_fwd.hip",
                   "csrc/fa_fwd_kernels.hpp", "csrc/fa_pipeline.hpp", "csrc/fa_common.hpp")
 COPY_BYTES = 512 << 20
-TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_llama_gqa_bf16_8192.md")
+TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_llama_gqa_bf16_8192.txt")
 
 
 def kernel_source_hash() -> str:
