@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     DQ_MODES, EXPORTS, HipEvent, auto_dq_mode, bwd, bwd_into, bwd_workspace_bytes, fwd,
     fwd_into, load, status_string,
 )
+from .autograd import attention  # noqa: F401
 
-__all__ = ["fwd", "fwd_into", "bwd", "bwd_into", "bwd_workspace_bytes", "auto_dq_mode",
+__all__ = ["attention", "fwd", "fwd_into", "bwd", "bwd_into", "bwd_workspace_bytes", "auto_dq_mode",
            "status_string", "load", "HipEvent", "DQ_MODES", "EXPORTS"]
