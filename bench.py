@@ -156,6 +156,7 @@ def main() -> int:
     kname = (f"{'bwd_dkdv_atomic_kernel' if resolved == 'atomic' else 'bwd_dkdv_kernel'}"
              f"<{dt_id}, {case.d}, {'true' if case.causal else 'false'}>")
     traffic = profiling.read_traffic(kname)
+    mfma = profiling.read_mfma(kname)
     log(f"[bench] fwd {fwd_ms:.3f} ms ({fwd_flops / fwd_ms / 1e9:.1f} TFLOP/s)  bwd {bwd_ms:.3f} ms "
         f"({value:.1f} TFLOP/s, {100 * value / PEAK_BF16_TFLOPS:.1f}% of peak)  dkdv kernel "
         f"{kern_ms:.3f} ms ({achieved:.1f} TFLOP/s)")
@@ -190,6 +191,11 @@ def main() -> int:
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "kernel_ms": round(kern_ms, 4),
+            # rocprof MfmaUtil (matrix-unit busy share of active SIMD cycles) and the
+            # MFMA flops the kernel executes per launch, from the committed counter
+            # profile of the current kernel sources; null when that profile is stale.
+            "mfma_busy_pct": None if mfma is None else mfma[0],
+            "executed_tflop": None if mfma is None else mfma[1],
         },
     }
     if args.copy_calibration:

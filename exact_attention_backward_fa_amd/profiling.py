@@ -2,6 +2,7 @@
 
     python -m exact_attention_backward_fa_amd.profiling trace  <dir> <out.md> "<command>"
     python -m exact_attention_backward_fa_amd.profiling traffic <fetch_dir> <write_dir> <out.txt> "<commands>"
+    python -m exact_attention_backward_fa_amd.profiling mfma <dir> <out.txt> "<command>"
 
 ``trace`` reads the kernel statistics a ``rocprofv3 --kernel-trace --stats
 --output-format csv`` run writes and tabulates per-kernel average durations.
@@ -10,8 +11,13 @@
 of ``bench.py --copy-calibration`` and converts the counters (KiB per dispatch) to
 HBM bytes per launch of each attention kernel, scaling each counter by what it
 reads for the calibration copy of known size (512 MiB read, 512 MiB written).
-The summary records a hash of the kernel sources so the benchmark can tell when
-the counters no longer describe the current kernels.
+
+``mfma`` reads a ``rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 MfmaFlopsF16`` run: the
+share of SIMD cycles in which the matrix unit was busy while the GPU was active,
+and the MFMA flops each launch executed.
+
+The traffic and MFMA summaries record a hash of the kernel sources so the
+benchmark can tell when the counters no longer describe the current kernels.
 """
 from __future__ import annotations
 
@@ -31,6 +37,7 @@ KERNEL_SOURCES = ("csrc/fa_bwd.hip", "csrc/fa_bwd_inst.hip", "csrc/fa_bwd_kernel
                   "csrc/fa_fwd_kernels.hpp", "csrc/fa_pipeline.hpp", "csrc/fa_common.hpp")
 COPY_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_llama_gqa_bf16_8192.txt")
+MFMA_FILE = os.path.join(PROFILES, "mfma_busy_llama_gqa_bf16_8192.txt")
 
 
 def kernel_source_hash() -> str:
@@ -104,6 +111,48 @@ def traffic_summary(fetch_dir: str, write_dir: str, commands: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def mfma_summary(d: str, command: str) -> str:
+    util = _pmc(d, "MfmaUtil")
+    flops = defaultdict(float)
+    for counter in ("MfmaFlopsBF16", "MfmaFlopsF16"):
+        for k, v in _pmc(d, counter).items():
+            flops[k] += v
+    out = ["# MFMA busy share and executed MFMA flops per launch (rocprofv3 --pmc)", "",
+           f"Command: {command}", "",
+           f"kernel_source_sha256_16: {kernel_source_hash()}", "",
+           "MfmaUtil = summed SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMD count) x 100; "
+           "MfmaFlops = MFMA MOPs (bf16 + fp16) x 512.", "",
+           "| kernel | MfmaUtil % | executed MFMA TFLOP per launch |",
+           "|---|---|---|"]
+    for k in util:
+        if not k.startswith("void fa::"):
+            continue
+        out.append(f"| `{short_name(k)}` | {util[k]:.1f} | {flops.get(k, 0.0) / 1e12:.4g} |")
+    return "\n".join(out) + "\n"
+
+
+def _read_row(path: str, kernel_prefix: str):
+    try:
+        text = open(path).read()
+    except OSError:
+        return None
+    m = re.search(r"kernel_source_sha256_16: (\w+)", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.split("|")]
+        if len(cells) > 3 and cells[1].strip("`").startswith(kernel_prefix):
+            return cells[2:-1]
+    return None
+
+
+def read_mfma(kernel_prefix: str):
+    """(MFMA busy %, executed MFMA TFLOP per launch) recorded for a kernel, or None
+    when the summary is missing or was taken from different kernel sources."""
+    cells = _read_row(MFMA_FILE, kernel_prefix)
+    return None if cells is None else (float(cells[0]), float(cells[1]))
+
+
 def read_traffic(kernel_prefix: str):
     """Traffic bytes per launch recorded for a kernel, or None when the summary is
     missing or was taken from different kernel sources."""
@@ -128,6 +177,9 @@ def main(argv) -> int:
     elif argv[1] == "traffic":
         _, _, fd, wd, out, cmd = argv
         text = traffic_summary(fd, wd, cmd)
+    elif argv[1] == "mfma":
+        _, _, d, out, cmd = argv
+        text = mfma_summary(d, cmd)
     else:
         raise SystemExit(__doc__)
     with open(out, "w") as f:
