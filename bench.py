@@ -173,9 +173,11 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": case.dtype,
-        "data": "synthetic (seeded N(0,1) Q, K, V, dO)",
-        "config": {"workload": f"{case.name}: causal GQA B={case.B} Hq={case.Hq} Hkv={case.Hkv} "
-                               f"N_q=N_kv={case.Nq} d={case.d} {case.dtype}",
+        "data": (f"synthetic (seeded {'U[0,1)' if case.dist == 'uniform' else 'N(0,1)'} Q, K, V, dO"
+                 f"{f'; Q and K x{case.qk_mult:g}' if case.qk_mult != 1.0 else ''})"),
+        "config": {"workload": f"{case.name}: {'causal' if case.causal else 'non-causal'} "
+                               f"{'GQA' if case.Hq != case.Hkv else 'MHA'} B={case.B} Hq={case.Hq} "
+                               f"Hkv={case.Hkv} N_q={case.Nq} N_kv={case.Nkv} d={case.d} {case.dtype}",
                    "global_batch": case.B, "seq_len": case.Nq, "parallelism": "single GPU",
                    "dq_path": resolved},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
