@@ -1,17 +1,25 @@
 """Builds libfa_mi355x.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m exact_attention_backward_fa_amd.build
+    python -m exact_attention_backward_fa_amd.build [--incremental]
 
-Objects go to ``_build/`` at the repository root (not tracked); the shared
-library lands next to this file, where the binding loads it.
+Every kernel template instance is its own compilation unit, so the units build in
+parallel: the forward once per (dtype, head dim, causal), the backward once per
+(dtype, head dim, causal, kernel).  Objects go to ``_build/`` at the repository
+root (not tracked); the shared library lands next to this file, where the binding
+loads it.  ``build()`` compiles every unit each time it is called;
+``build(incremental=True)`` reuses an object whose source, included headers and
+flags are unchanged (the key is a hash over all of them).
 """
 from __future__ import annotations
 
+import hashlib
 import os
+import re
 import shutil
 import subprocess
 import sys
 import time
+from typing import Dict, List, Sequence, Tuple
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
@@ -21,10 +29,12 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
+# Host-side sources (entry points, dispatch, conversions).
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
-# fa_bwd_inst.hip is compiled once per backward template instance:
-# (dtype 0 fp16 / 1 bf16, head dim, causal).
+# Template instances: (dtype 0 fp16 / 1 bf16, head dim, causal).
 INSTANCES = [(dt, d, c) for dt in (0, 1) for d in (64, 128) for c in (0, 1)]
+# Backward kernel families compiled per instance (FA_KIND in fa_bwd_inst.hip).
+BWD_KINDS = {0: "pre", 1: "dkdv", 2: "dq", 3: "atomic"}
 
 ARCH = "gfx950"
 HIP_FLAGS = [
@@ -42,11 +52,65 @@ HIP_FLAGS = [
 ]
 
 
+class Unit:
+    """One compilation: a source file plus -D defines."""
+
+    def __init__(self, name: str, src: str, defines: Sequence[Tuple[str, int]] = ()):
+        self.name = name
+        self.src = src
+        self.defines = list(defines)
+
+    def flags(self) -> List[str]:
+        return [f"-D{k}={v}" for k, v in self.defines]
+
+
+def units() -> List[Unit]:
+    out = [Unit(os.path.splitext(s)[0], s) for s in SOURCES]
+    for dt, d, c in INSTANCES:
+        out.append(Unit(f"fwd_{dt}_{d}_{c}", "fa_fwd_inst.hip",
+                        [("FA_DT", dt), ("FA_D", d), ("FA_CAUSAL", c)]))
+        for kind, kname in BWD_KINDS.items():
+            out.append(Unit(f"{kname}_{dt}_{d}_{c}", "fa_bwd_inst.hip",
+                            [("FA_DT", dt), ("FA_D", d), ("FA_CAUSAL", c), ("FA_KIND", kind)]))
+    return out
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
             return cand
     raise RuntimeError("hipcc not found (ROCm is required to build libfa_mi355x.so)")
+
+
+_INC = re.compile(r'^\s*#\s*include\s+"([^"]+)"', re.M)
+
+
+def _deps(path: str, seen: Dict[str, None]) -> None:
+    if path in seen:
+        return
+    seen[path] = None
+    with open(path) as f:
+        text = f.read()
+    for inc in _INC.findall(text):
+        for base in (os.path.dirname(path), CSRC, INCLUDE):
+            cand = os.path.join(base, inc)
+            if os.path.exists(cand):
+                _deps(os.path.abspath(cand), seen)
+                break
+
+
+def unit_key(u: Unit, extra: Sequence[str] = ()) -> str:
+    """Hash of the unit's source, every header it includes (transitively) and the
+    compile flags."""
+    seen: Dict[str, None] = {}
+    _deps(os.path.join(CSRC, u.src), seen)
+    h = hashlib.sha256()
+    for path in sorted(seen):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    h.update(" ".join(HIP_FLAGS + u.flags() + list(extra)).encode())
+    return h.hexdigest()[:16]
 
 
 def _filter_noise(text: str) -> str:
@@ -57,49 +121,59 @@ def _filter_noise(text: str) -> str:
     return "\n".join(keep).strip()
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
+def _run_jobs(jobs: List[Tuple[str, List[str]]], verbose: bool) -> None:
+    """Run compile commands in parallel (at most one per CPU, 16 at most)."""
+    width = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    pending = list(jobs)
+    running = []
+    failed = []
+    while pending or running:
+        while pending and len(running) < width:
+            name, cmd = pending.pop(0)
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            running.append((name, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                   stderr=subprocess.STDOUT, text=True)))
+        # wait for whichever job ends first
+        while True:
+            done = [r for r in running if r[1].poll() is not None]
+            if done:
+                break
+            time.sleep(0.05)
+        for name, p in done:
+            running.remove((name, p))
+            out = p.stdout.read() if p.stdout else ""
+            msg = _filter_noise(out or "")
+            if p.returncode != 0:
+                failed.append(name)
+                print(f"[build] {name} failed:\n{msg}", file=sys.stderr, flush=True)
+            elif msg and verbose:
+                print(f"[build] {name}:\n{msg}", flush=True)
+    if failed:
+        raise RuntimeError(f"HIP compilation failed for {failed}")
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every unit and link the shared library; returns its path."""
     cc = hipcc()
     os.makedirs(BUILD_DIR, exist_ok=True)
     t0 = time.time()
     jobs = []
     objs = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    for u in units():
+        obj = os.path.join(BUILD_DIR, f"{u.name}-{unit_key(u)}.o")
         objs.append(obj)
-        jobs.append((src, [cc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]))
-    for dt, d, c in INSTANCES:
-        obj = os.path.join(BUILD_DIR, f"fa_bwd_inst_{dt}_{d}_{c}.o")
-        objs.append(obj)
-        jobs.append((f"fa_bwd_inst.hip [{dt},{d},{c}]",
-                     [cc, *HIP_FLAGS, f"-DFA_DT={dt}", f"-DFA_D={d}", f"-DFA_CAUSAL={c}", "-c",
-                      os.path.join(CSRC, "fa_bwd_inst.hip"), "-o", obj]))
-    # the heaviest compilations first, at most one per CPU
-    jobs.sort(key=lambda j: "inst" not in j[0])
-    width = max(1, min(len(jobs), os.cpu_count() or 1, 16))
-    procs = []
-    pending = list(jobs)
-    failed = []
-    results = []
-    while pending or procs:
-        while pending and len(procs) < width:
-            src, cmd = pending.pop(0)
-            if verbose:
-                print(" ".join(cmd), flush=True)
-            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
-                                                text=True)))
-        src, p = procs.pop(0)
-        out, _ = p.communicate()
-        results.append((src, p, out))
-    for src, p, out in results:
-        msg = _filter_noise(out or "")
-        if p.returncode != 0:
-            failed.append(src)
-            print(f"[build] {src} failed:\n{msg}", file=sys.stderr, flush=True)
-        elif msg and verbose:
-            print(f"[build] {src}:\n{msg}", flush=True)
-    if failed:
-        raise RuntimeError(f"HIP compilation failed for {failed}")
+        if incremental and os.path.exists(obj):
+            continue
+        tmp = obj + ".part"
+        jobs.append((u.name, [cc, *HIP_FLAGS, *u.flags(), "-c", os.path.join(CSRC, u.src),
+                              "-o", tmp]))
+    # the kernel instances are the long compilations: start them first
+    jobs.sort(key=lambda j: j[0] in [os.path.splitext(s)[0] for s in SOURCES])
+    _run_jobs(jobs, verbose)
+    for obj in objs:
+        if os.path.exists(obj + ".part"):
+            os.replace(obj + ".part", obj)
     tmp = LIB_PATH + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -107,9 +181,32 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{r.stdout}")
     os.replace(tmp, LIB_PATH)
     if verbose:
-        print(f"[build] {LIB_PATH} in {time.time() - t0:.1f}s", flush=True)
+        print(f"[build] {LIB_PATH} ({len(jobs)} of {len(objs)} units compiled) in "
+              f"{time.time() - t0:.1f}s", flush=True)
     return LIB_PATH
 
 
+def device_asm(selected: Sequence[Unit], verbose: bool = False) -> Dict[str, str]:
+    """gfx950 assembly of the given units (device code only), cached in
+    ``_build/asm`` under the unit key; returns {unit name: path of the .s file}."""
+    cc = hipcc()
+    adir = os.path.join(BUILD_DIR, "asm")
+    os.makedirs(adir, exist_ok=True)
+    paths = {}
+    jobs = []
+    for u in selected:
+        path = os.path.join(adir, f"{u.name}-{unit_key(u, ['asm'])}.s")
+        paths[u.name] = path
+        if not os.path.exists(path):
+            flags = [f for f in HIP_FLAGS if f != "-fPIC"]
+            jobs.append((u.name, [cc, *flags, *u.flags(), "--cuda-device-only", "-S",
+                                  os.path.join(CSRC, u.src), "-o", path + ".part"]))
+    _run_jobs(jobs, verbose)
+    for path in paths.values():
+        if os.path.exists(path + ".part"):
+            os.replace(path + ".part", path)
+    return paths
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv[1:])

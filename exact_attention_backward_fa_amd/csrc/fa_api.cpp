@@ -71,6 +71,72 @@ static int resolve_dq_mode(const Problem& pb, int mode) {
   return FA_DQ_SEPARATE;
 }
 
+int bwd_checked(const BwdCall& c, int dq_mode, void* ev_begin, void* ev_end, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  Problem pb;
+  const int st = check_problem(c.B, c.Hq, c.Hkv, c.Nq, c.Nkv, c.d, c.scale, c.dtype, &pb);
+  if (st != FA_OK) return st;
+  pb.causal = c.causal != 0;
+  if (dq_mode != FA_DQ_AUTO && dq_mode != FA_DQ_ATOMIC && dq_mode != FA_DQ_SEPARATE)
+    return FA_ERR_MODE;
+  const size_t nq = (size_t)c.B * c.Hq * c.Nq * c.d, nk = (size_t)c.B * c.Hkv * c.Nkv * c.d;
+  const size_t nrows = (size_t)c.B * c.Hq * c.Nq;
+  // dK/dV are written whenever they have elements (zeros when N_q = 0).
+  const void* ptrs[9] = {c.q, c.k, c.v, c.o, c.lse, c.dout, c.dq, c.dk, c.dv};
+  const size_t elems[9] = {nq, nk, nk, nq, nrows, nq, nq, nk, nk};
+  for (int i = 0; i < 9; ++i) {
+    const int pst = check_ptr(ptrs[i], elems[i]);
+    if (pst != FA_OK) return pst;
+  }
+  const int mode = resolve_dq_mode(pb, dq_mode);
+  const bool atomic = mode == FA_DQ_ATOMIC;
+  const WorkspaceLayout L = workspace_layout(pb, atomic);
+  if (L.total > 0) {
+    if (workspace == nullptr || ((uintptr_t)workspace & 15u) != 0 || workspace_bytes < L.total)
+      return FA_ERR_WORKSPACE;
+  }
+  char* ws = static_cast<char*>(workspace);
+  BwdArgs a;
+  a.pb = pb;
+  a.q = c.q;
+  a.k = c.k;
+  a.v = c.v;
+  a.o = c.o;
+  a.lse = c.lse;
+  a.dout = c.dout;
+  a.dq = c.dq;
+  a.dk = c.dk;
+  a.dv = c.dv;
+  a.ndelta = L.total ? reinterpret_cast<float*>(ws + L.ndelta_off) : nullptr;
+  a.lse2 = L.total ? reinterpret_cast<float*>(ws + L.lse2_off) : nullptr;
+  a.dq_acc = (L.total && atomic) ? reinterpret_cast<float*>(ws + L.dqacc_off) : nullptr;
+  a.sched = L.total ? reinterpret_cast<int*>(ws + L.sched_off) : nullptr;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (nrows == 0 && nk == 0) return FA_OK;  // nothing to compute; no HIP call at all
+  (void)hipGetLastError();
+  if (launch_bwd_pre(a, atomic, s) != hipSuccess) return FA_ERR_HIP;
+  if (ev_begin && hipEventRecord((hipEvent_t)ev_begin, s) != hipSuccess) return FA_ERR_HIP;
+  if (launch_bwd_dkdv(a, atomic, s) != hipSuccess) return FA_ERR_HIP;
+  if (ev_end && hipEventRecord((hipEvent_t)ev_end, s) != hipSuccess) return FA_ERR_HIP;
+  if (atomic) {
+    if (launch_bwd_dq_convert(a, s) != hipSuccess) return FA_ERR_HIP;
+  } else {
+    if (launch_bwd_dq(a, s) != hipSuccess) return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+size_t bwd_workspace_checked(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal, int dtype,
+                             int dq_mode) {
+  Problem pb;
+  if (check_problem(B, Hq, Hkv, Nq, Nkv, d, 1.0f, dtype, &pb) != FA_OK) return 0;
+  if (dq_mode != FA_DQ_AUTO && dq_mode != FA_DQ_ATOMIC && dq_mode != FA_DQ_SEPARATE) return 0;
+  pb.causal = causal != 0;
+  const int mode = resolve_dq_mode(pb, dq_mode);
+  return workspace_layout(pb, mode == FA_DQ_ATOMIC).total;
+}
+
 }  // namespace fa
 
 using namespace fa;
@@ -124,12 +190,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 size_t fa_bwd_ex_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal,
                                  int dtype, int dq_mode) {
-  Problem pb;
-  if (check_problem(B, Hq, Hkv, Nq, Nkv, d, 1.0f, dtype, &pb) != FA_OK) return 0;
-  if (dq_mode != FA_DQ_AUTO && dq_mode != FA_DQ_ATOMIC && dq_mode != FA_DQ_SEPARATE) return 0;
-  pb.causal = causal != 0;
-  const int mode = resolve_dq_mode(pb, dq_mode);
-  return workspace_layout(pb, mode == FA_DQ_ATOMIC).total;
+  return bwd_workspace_checked(B, Hq, Hkv, Nq, Nkv, d, causal, dtype, dq_mode);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal,
@@ -149,60 +210,8 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
               int Nkv, int d, float softmax_scale, int causal, int dtype, int dq_mode,
               void* ev_begin, void* ev_end, void* workspace, size_t workspace_bytes,
               void* stream) {
-  Problem pb;
-  FA_TRY(check_problem(B, Hq, Hkv, Nq, Nkv, d, softmax_scale, dtype, &pb));
-  pb.causal = causal != 0;
-  if (dq_mode != FA_DQ_AUTO && dq_mode != FA_DQ_ATOMIC && dq_mode != FA_DQ_SEPARATE)
-    return FA_ERR_MODE;
-  const size_t nq = (size_t)B * Hq * Nq * d, nk = (size_t)B * Hkv * Nkv * d;
-  const size_t nrows = (size_t)B * Hq * Nq;
-  // dK/dV are written whenever they have elements (zeros when N_q = 0).
-  FA_TRY(check_ptr(q, nq));
-  FA_TRY(check_ptr(k, nk));
-  FA_TRY(check_ptr(v, nk));
-  FA_TRY(check_ptr(o, nq));
-  FA_TRY(check_ptr(lse, nrows));
-  FA_TRY(check_ptr(dout, nq));
-  FA_TRY(check_ptr(dq, nq));
-  FA_TRY(check_ptr(dk, nk));
-  FA_TRY(check_ptr(dv, nk));
-  const int mode = resolve_dq_mode(pb, dq_mode);
-  const bool atomic = mode == FA_DQ_ATOMIC;
-  const WorkspaceLayout L = workspace_layout(pb, atomic);
-  if (L.total > 0) {
-    if (workspace == nullptr || ((uintptr_t)workspace & 15u) != 0 || workspace_bytes < L.total)
-      return FA_ERR_WORKSPACE;
-  }
-  char* ws = static_cast<char*>(workspace);
-  BwdArgs a;
-  a.pb = pb;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  a.dout = dout;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.ndelta = L.total ? reinterpret_cast<float*>(ws + L.ndelta_off) : nullptr;
-  a.lse2 = L.total ? reinterpret_cast<float*>(ws + L.lse2_off) : nullptr;
-  a.dq_acc = (L.total && atomic) ? reinterpret_cast<float*>(ws + L.dqacc_off) : nullptr;
-  a.sched = L.total ? reinterpret_cast<int*>(ws + L.sched_off) : nullptr;
-
-  hipStream_t s = (hipStream_t)stream;
-  if (nrows == 0 && nk == 0) return FA_OK;  // nothing to compute; no HIP call at all
-  (void)hipGetLastError();
-  if (launch_bwd_pre(a, atomic, s) != hipSuccess) return FA_ERR_HIP;
-  if (ev_begin && hipEventRecord((hipEvent_t)ev_begin, s) != hipSuccess) return FA_ERR_HIP;
-  if (launch_bwd_dkdv(a, atomic, s) != hipSuccess) return FA_ERR_HIP;
-  if (ev_end && hipEventRecord((hipEvent_t)ev_end, s) != hipSuccess) return FA_ERR_HIP;
-  if (atomic) {
-    if (launch_bwd_dq_convert(a, s) != hipSuccess) return FA_ERR_HIP;
-  } else {
-    if (launch_bwd_dq(a, s) != hipSuccess) return FA_ERR_HIP;
-  }
-  return FA_OK;
+  BwdCall c{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, d, softmax_scale, causal, dtype};
+  return fa::bwd_checked(c, dq_mode, ev_begin, ev_end, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

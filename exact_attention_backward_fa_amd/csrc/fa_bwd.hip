@@ -3,8 +3,6 @@
 // fa_bwd_inst.hip) and the float32 -> dtype conversion of the atomic dQ buffer.
 #include "fa_bwd_common.hpp"
 
-#include <stdlib.h>
-#include <string.h>
 
 namespace fa {
 
@@ -35,14 +33,6 @@ int device_cu_count() {
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (dev < 64) cached[dev] = n;
   return n;
-}
-
-bool sched_static() {
-  static const int v = [] {
-    const char* e = getenv("FA_SCHED");
-    return (e && strcmp(e, "static") == 0) ? 1 : 0;
-  }();
-  return v != 0;
 }
 
 // ---------------------------------------------------------------------------

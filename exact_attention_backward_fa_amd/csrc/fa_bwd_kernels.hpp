@@ -917,7 +917,6 @@ hipError_t run_dkdv(const BwdArgs& a, hipStream_t s) {
   BwdParams p = make_params(a);
   const int items = ((a.pb.Nkv + 255) / 256) * a.pb.Hkv * a.pb.B;
   const int ncu = device_cu_count();
-  if (sched_static()) p.sched = nullptr;
   const dim3 grid((unsigned)(p.sched && ncu > 0 && ncu < items ? ncu : items));
   hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
@@ -928,7 +927,6 @@ hipError_t run_dq(const BwdArgs& a, hipStream_t s) {
   BwdParams p = make_params(a);
   const int items = ((a.pb.Nq + 255) / 256) * a.pb.Hq * a.pb.B;
   const int ncu = device_cu_count();
-  if (sched_static()) p.sched = nullptr;
   const dim3 grid((unsigned)(p.sched && ncu > 0 && ncu < items ? ncu : items));
   hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
   return hipGetLastError();

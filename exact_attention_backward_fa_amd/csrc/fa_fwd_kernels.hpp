@@ -20,12 +20,15 @@
 //
 // Online softmax without rescaling: each query column keeps a reference m (log2
 // domain, scale * log2 e folded in), set from the first pair in which the column
-// sees a key, and P = exp2(s c - m).  P and the float32 sums stay far from
-// overflow as long as no score exceeds m + 64 (P < 2^64; relative precision does
-// not depend on the size), so O and the row sums never need rescaling.  A score
-// above m + 64 after the first pair (logits rising by more than 44 nats along the
-// row) raises m and marks the item; the workgroup then runs the item a second time
-// from zero with the raised references, which no score can exceed by more than 64.
+// sees a key, and P = exp2(s c - m).  P is rounded to the input type for the P V
+// product, so the headroom H above m that a score may reach is set by that type's
+// range: 64 for bf16 (float32's exponent range, P < 2^64) and 15 for fp16, whose
+// largest finite value is 65504 < 2^16 (P < 2^15).  Relative precision does not
+// depend on the size of P, so O and the row sums never need rescaling while no
+// score exceeds m + H.  A score above m + H after the first pair (logits rising by
+// more than 44 nats along the row for bf16, 10.4 nats for fp16) raises m and marks
+// the item; the workgroup then runs the item a second time from zero with the
+// raised references, which no score can exceed by more than H.
 // The row sums l of P are float32 (each lane sums its keys; the four lanes of a
 // column are added at the end; summing the bf16-rounded P through the matrix
 // pipe was measured to miss the LSE bound on short rows).  At the end O is divided
@@ -49,7 +52,10 @@ struct FwdParams {
   float scale_log2;
 };
 
-constexpr float kHeadroom = 64.f;  // log2 headroom above the reference of a query column
+// log2 headroom above the reference of a query column: P = exp2(score - m) stays
+// below 2^H, inside the range of the 16-bit type P is rounded to (fp16: 65504)
+template <int DT>
+constexpr float fwd_headroom() { return DT == 0 ? 15.f : 64.f; }
 
 // Step J: S^T of pair J (2 NK operands x 4 query tiles) | P V of the previous pair
 // (2 NK head-dim tiles x 4).
@@ -141,14 +147,14 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   }
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's part of its column's row sum
   // reference of this lane's query column per query tile, and the raw-score
-  // threshold (m + 64) / c above which it is raised; finite, so that a column with
+  // threshold (m + H) / c above which it is raised; finite, so that a column with
   // no visible key yet gives exp2(-inf - m) = 0
   constexpr float kUnset = -1e30f;
   float m[4], thr[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     m[t] = kUnset;
-    thr[t] = (m[t] + kHeadroom) / c;
+    thr[t] = (m[t] + fwd_headroom<DT>()) / c;
   }
   bool dirty = false;  // a reference was raised after it had been used
   __shared__ int s_dirty;
@@ -277,10 +283,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
             float v = mx[t] * c;
             v = fmaxf(v, __shfl_xor(v, 16));
             v = fmaxf(v, __shfl_xor(v, 32));
-            if (v > m[t] + kHeadroom) {
+            if (v > m[t] + fwd_headroom<DT>()) {
               dirty = dirty || m[t] != kUnset;
               m[t] = v;
-              thr[t] = (v + kHeadroom) / c;
+              thr[t] = (v + fwd_headroom<DT>()) / c;
             }
           }
         }
@@ -405,6 +411,29 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   }
   uint16_t* stage = &sKV[0][0] + w * 64 * (D + 8);
   store_block64_rows<DT, D>(acc, inv, stage, p.o + qbase * D, qw, p.Nq, lane);
+}
+
+// Launcher of one instance (explicitly instantiated per instance in fa_fwd_inst.hip).
+template <int DT, int D, bool CAUSAL>
+hipError_t run_fwd(const FwdArgs& a, hipStream_t s) {
+  const Problem& pb = a.pb;
+  FwdParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.o = static_cast<uint16_t*>(a.o);
+  p.lse = a.lse;
+  p.B = pb.B;
+  p.Hq = pb.Hq;
+  p.Hkv = pb.Hkv;
+  p.Nq = pb.Nq;
+  p.Nkv = pb.Nkv;
+  p.G = pb.Hq / pb.Hkv;
+  p.off = pb.Nkv - pb.Nq;
+  p.scale_log2 = pb.scale * kLog2e;
+  const dim3 grid((unsigned)(((pb.Nq + 255) / 256) * pb.Hq * pb.B));
+  hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -42,6 +42,31 @@ struct BwdArgs {
                   //                by the preprocess); null: static work split
 };
 
+// Arguments of one backward call as the C entry points receive them (unchecked).
+struct BwdCall {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Nq, Nkv, d;
+  float scale;
+  int causal, dtype;
+};
+
+// Checks every argument of a backward call on the host, then enqueues the
+// kernels with `workspace` as the scratch memory; returns FA_OK or an FA_ERR_*
+// code (nothing is launched or written on error).
+int bwd_checked(const BwdCall& c, int dq_mode, void* ev_begin, void* ev_end, void* workspace,
+                size_t workspace_bytes, void* stream);
+// Workspace bytes of a backward call with this dQ path (0 for invalid arguments).
+size_t bwd_workspace_checked(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal, int dtype,
+                             int dq_mode);
+
 // Workspace carve-up; every region starts on a 256-byte boundary.
 struct WorkspaceLayout {
   size_t ndelta_off, lse2_off, dqacc_off, sched_off, total;
@@ -50,6 +75,9 @@ WorkspaceLayout workspace_layout(const Problem& pb, bool atomic_dq);
 
 // Kernel launchers (return hipSuccess or the launch error).
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s);
+// The forward launcher of one template instance (dtype 0 fp16 / 1 bf16, head dim,
+// causal), defined in fa_fwd_kernels.hpp.
+template <int DT, int D, bool CAUSAL> hipError_t run_fwd(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_pre(const BwdArgs& a, bool zero_dq_acc, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, bool atomic_dq, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
@@ -57,8 +85,5 @@ hipError_t launch_bwd_dq_convert(const BwdArgs& a, hipStream_t s);
 
 // Compute units of the current device (cached per device; 0 if it cannot be read).
 int device_cu_count();
-// FA_SCHED=static in the environment: the persistent kernels take one work item
-// per workgroup in a fixed order instead of the work queues (for comparisons).
-bool sched_static();
 
 }  // namespace fa

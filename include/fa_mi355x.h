@@ -66,7 +66,7 @@ extern "C" {
 #define FA_DTYPE_FP16 0
 #define FA_DTYPE_BF16 1
 
-/* How fa_bwd_ex produces dQ (the spec comparison of two dQ paths). */
+/* How fa_bwd_ex produces dQ (the two dQ decompositions, compared by measurement). */
 #define FA_DQ_AUTO     0  /* the faster path, as measured for this shape class */
 #define FA_DQ_ATOMIC   1  /* dS K tiles added into a float32 buffer by the dK/dV
                              kernel with float atomics, then rounded to dtype */
@@ -75,9 +75,16 @@ extern "C" {
 
 /*
  * Forward: O and LSE from Q, K, V.
+ * Source: the pages print no forward kernel; what the backward needs from it is
+ * fixed by the two backward listings, which rebuild P = exp(S - LSE) from one
+ * float per query row (rustytorch "flash_attention_backward.cu", tiled backward
+ * kernel: the probabilities recomputed from the stored row statistic; Triton issue
+ * "Extra transposes cause 8x speedup...", _bwd_kernel listing: p = exp(qk - m)
+ * with m loaded per row).  O = softmax(S) V is the forward whose gradient the
+ * backward computes.
  * Writes o [B,Hq,N_q,d] (dtype) and lse [B,Hq,N_q] (float32, natural log of the
  * row sum of exp(scale * q.k) over visible keys; -inf for a row with none).
- * Reads q, k, v.  Returns FA_OK or an FA_ERR_* code.
+ * Reads q, k, v.  Returns FA_OK or an FA_ERR_* code; on error nothing is written.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int Nq, int Nkv, int d,
@@ -85,7 +92,11 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace fa_bwd needs for these arguments (0 when the call
- * needs none).  Returns 0 for invalid arguments as well; fa_bwd then reports the
+ * needs none).  The workspace holds the per-row D = rowsum(dO o O) (precomputed
+ * per query row as the Triton issue's _bwd_kernel listing loads it), the row
+ * statistic in the kernels' log2 form, the work-queue counters and, on the atomic
+ * dQ path, the float32 dQ accumulator (the Triton harness's zeroed float32 dq
+ * buffer).  Returns 0 for invalid arguments as well; fa_bwd then reports the
  * error.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
@@ -97,13 +108,22 @@ size_t fa_bwd_ex_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
 
 /*
  * Backward: dQ, dK, dV from Q, K, V, O, dO and LSE.
+ * Source: rustytorch "flash_attention_backward.cu", tiled backward kernel (per
+ * tile: S recomputed, P = exp(S - LSE), dV += P^T dO, dP = dO V^T,
+ * dS = P o (dP - D), dK += dS^T Q, dQ += dS K, with D the row dot product of dO
+ * and O); Triton issue "Extra transposes cause 8x speedup for sequence-parallel
+ * Flash Attention backward", _bwd_kernel listing (the key-block-parallel loop over
+ * query blocks with K and V resident, D precomputed, dq accumulated with float
+ * atomics).  Where the two differ this library follows the definition (see the
+ * operation at the top).
  * o and lse must be what fa_fwd returns for the same q, k, v and arguments (or
  * the same quantities computed elsewhere).  dq, dk, dv are fully overwritten
  * (callers need not zero them).  workspace: caller-owned device memory of at
  * least fa_bwd_workspace_bytes(...) bytes, 16-byte aligned, not shared with a
  * concurrent call; its contents on entry do not matter.  Kernels run in order
  * on `stream`: row preprocess (D = rowsum(dO o O)), the key/value-block-parallel
- * dK/dV kernel, then the dQ path FA_DQ_AUTO selects.
+ * dK/dV kernel, then the dQ path FA_DQ_AUTO selects.  Returns FA_OK or an
+ * FA_ERR_* code; a rejected call launches nothing and writes nothing.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -113,6 +133,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
 
 /*
  * fa_bwd with an explicit dQ path and optional timing events.
+ * Source: the two dQ decompositions of the pages - float atomics into a float32
+ * buffer from the key-block-parallel kernel (Triton issue "Extra transposes...",
+ * _bwd_kernel listing, tl.atomic_add of dq; flash-attention-minimal "Implement
+ * backward pass", the thread's note that atomic and plain adds time differently)
+ * and a query-block-parallel pass (the grid of the rustytorch tiled backward
+ * kernel, which owns a block of query rows).
  * dq_mode: FA_DQ_AUTO, FA_DQ_ATOMIC or FA_DQ_SEPARATE.
  * ev_begin / ev_end: NULL, or hipEvent_t handles (as void*) that are recorded on
  * `stream` immediately before and after the launch of the dK/dV kernel, the

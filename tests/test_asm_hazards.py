@@ -1,21 +1,16 @@
 """CPU check of the kernels' assembly for the inline-MFMA hazards the compiler
-does not track (see tests/asm_check.py).  Compiles two template instances of the
-backward and the forward kernels to gfx950 assembly (no GPU needed)."""
-import os
-import shutil
-import subprocess
-import tempfile
-
+does not track (see tests/asm_check.py).  Every shipped template instance of the
+forward, dK/dV, dQ-pass and fused atomic kernels is compiled to gfx950 assembly
+(no GPU needed; the build caches the assembly under the units' source hash)."""
 import pytest
 
 from exact_attention_backward_fa_amd import build as fabuild
 from tests import asm_check
 
-# (dtype 0 fp16 / 1 bf16, head dim, causal): the headline instance and the other
-# extreme of the template parameters
-INSTANCES = [(1, 128, 1), (0, 64, 0)]
-KERNELS = ("bwd_dkdv_kernel", "bwd_dq_kernel")
-FWD_INSTANCES = [(1, 128, 1), (0, 64, 0)]
+# kernel units whose assembly is scanned: every instance of every kernel family
+# that issues inline-assembly MFMAs
+KINDS = ("fwd", "dkdv", "dq", "atomic")
+KERNELS = ("fwd_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel", "bwd_dkdv_atomic_kernel")
 
 
 def _have_hipcc():
@@ -26,52 +21,32 @@ def _have_hipcc():
         return False
 
 
+def _scanned_units():
+    return [u for u in fabuild.units() if u.name.split("_")[0] in KINDS]
+
+
 @pytest.fixture(scope="module")
 def assembly():
     if not _have_hipcc():
         pytest.skip("hipcc not available")
-    tmp = tempfile.mkdtemp(prefix="fa_asm_")
-    try:
-        procs = []
-        for dt, d, c in INSTANCES:
-            out = os.path.join(tmp, f"inst_{dt}_{d}_{c}.s")
-            cmd = [fabuild.hipcc(), *[f for f in fabuild.HIP_FLAGS if f != "-fPIC"],
-                   f"-DFA_DT={dt}", f"-DFA_D={d}", f"-DFA_CAUSAL={c}", "--cuda-device-only", "-S",
-                   os.path.join(fabuild.CSRC, "fa_bwd_inst.hip"), "-o", out]
-            procs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
-                                                text=True)))
-        for dt, d, c in FWD_INSTANCES:
-            src = os.path.join(tmp, f"fwd_{dt}_{d}_{c}.hip")
-            with open(src, "w") as f:
-                f.write('#include "fa_fwd_kernels.hpp"\n'
-                        f"template __global__ void fa::fwd_kernel<{dt}, {d}, {'true' if c else 'false'}>"
-                        "(fa::FwdParams);\n")
-            out = src[:-4] + ".s"
-            cmd = [fabuild.hipcc(), *[f for f in fabuild.HIP_FLAGS if f != "-fPIC"], "-I", fabuild.CSRC,
-                   "--cuda-device-only", "-S", src, "-o", out]
-            procs.append((out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
-                                                text=True)))
-        texts = {}
-        for out, p in procs:
-            log, _ = p.communicate(timeout=900)
-            assert p.returncode == 0, log[-2000:]
-            with open(out) as f:
-                texts[os.path.basename(out)] = f.read()
-        return texts
-    finally:
-        shutil.rmtree(tmp, ignore_errors=True)
+    paths = fabuild.device_asm(_scanned_units())
+    texts = {}
+    for name, path in paths.items():
+        with open(path) as f:
+            texts[name] = f.read()
+    return texts
 
 
 def _kernels(texts):
     for name, text in texts.items():
         for sym, ins in asm_check.kernel_bodies(text).items():
-            if any(k in sym for k in KERNELS) or "fwd_kernel" in sym:
+            if any(k in sym for k in KERNELS):
                 yield f"{name}:{sym}", ins
 
 
 def test_kernels_found(assembly):
     found = [s for s, _ in _kernels(assembly)]
-    assert len(found) == len(INSTANCES) * len(KERNELS) + len(FWD_INSTANCES), found
+    assert len(found) == len(_scanned_units()), found
 
 
 def test_no_valu_write_right_before_inline_mfma(assembly):

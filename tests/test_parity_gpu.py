@@ -3,9 +3,10 @@
 Gate: max|g - ref| / max|ref| <= 1e-2 (fp16) / 2e-2 (bf16) for O, dQ, dK, dV and
 max|LSE - ref| <= 1e-3, on every workload family.  Shapes the oracle can afford
 whole are compared element by element on sampled (batch, kv-head) groups; the
-longest sequences are compared on sampled rows (O, LSE and dQ rows, and the
-trailing key rows of dK/dV whose contributing queries are few under the causal
-mask) plus identities that hold at any size.
+longest sequences are compared on sampled rows (O, LSE and dQ rows; the
+leading key rows of dK/dV, which accumulate over every query tile of the group,
+and the trailing ones, which see the fewest) plus identities that hold at any
+size.
 """
 import numpy as np
 import pytest
@@ -87,8 +88,13 @@ def test_long_d64(device):
     _run_groups(case, [(0, 0), (0, 11)], device)
 
 
-def _sampled_check(case, device, seed_rows=1234):
-    """Row-sampled parity for sequences too long to materialise whole."""
+def _sampled_check(case, device, lead, seed_rows=1234):
+    """Row-sampled parity for sequences too long to materialise whole.
+
+    Key rows compared element by element: the trailing 48 (the fewest
+    contributing queries under the causal mask) and, for the first sampled group,
+    the leading ``lead`` (every query of the group's G heads contributes: the
+    dK/dV kernel's longest accumulations)."""
     x = inputs.make_inputs(case)
     rng = np.random.default_rng(seed_rows + case.seed)
     N = case.Nq
@@ -96,22 +102,26 @@ def _sampled_check(case, device, seed_rows=1234):
     tail = np.arange(N - 48, N)
     picks = [(0, 0, 0), (case.B - 1, case.Hq - 1, case.Hkv - 1)]
     ref = {}
-    for (b, h, g) in picks:
-        pu.log(f"[oracle] {case.name} rows b={b} h={h} g={g}")
+    keys = {}
+    for n, (b, h, g) in enumerate(picks):
+        kv_rows = np.concatenate([np.arange(lead), tail]) if n == 0 else tail
+        keys[(b, h, g)] = kv_rows
+        pu.log(f"[oracle] {case.name} rows b={b} h={h} g={g} ({len(kv_rows)} key rows)")
         o, l_ = orc.forward_rows(x["q"], x["k"], x["v"], case.scale, case.causal, b, h, rows)
         dq = orc.dq_rows(x["q"], x["k"], x["v"], x["do"], case.scale, case.causal, b, h, rows)
-        dk, dv = orc.dkdv_rows(x["q"], x["k"], x["v"], x["do"], case.scale, case.causal, b, g, tail)
+        dk, dv = pu.dkdv_rows_by_head(case, x, b, g, kv_rows)
         ref[(b, h, g)] = {"o": o, "lse": l_, "dq": dq, "dk": dk, "dv": dv}
     for mode in MODES:
         pu.log(f"[gpu] {case.name} mode={mode} seed={case.seed}")
         res = pu.gpu_forward_backward(case, x, device, dq_mode=mode)
         for (b, h, g), r in ref.items():
+            kv_rows = keys[(b, h, g)]
             got = {
                 "o": res["o"][b, h, rows].double().numpy(),
                 "lse": res["lse"][b, h, rows].double().numpy(),
                 "dq": res["dq"][b, h, rows].double().numpy(),
-                "dk": res["dk"][b, g, tail].double().numpy(),
-                "dv": res["dv"][b, g, tail].double().numpy(),
+                "dk": res["dk"][b, g, kv_rows].double().numpy(),
+                "dv": res["dv"][b, g, kv_rows].double().numpy(),
             }
             pu.assert_within(case, pu.compare(case, got, r, f"{mode} rows b={b} h={h}"))
         _identities_any_size(case, x, res)
@@ -139,10 +149,10 @@ def _identities_any_size(case, x, res):
             assert abs(lhs - rhs) <= tol * max(mag, 1e-30)
 
 
-@pytest.mark.parametrize("name", ["llama_gqa_fp16_16384", "llama_gqa_bf16_16384",
-                                  "long_gqa_32768"])
-def test_long_sampled(name, device):
-    _sampled_check(inputs.case_by_name(name), device)
+@pytest.mark.parametrize("name,lead", [("llama_gqa_fp16_16384", 64), ("llama_gqa_bf16_16384", 64),
+                                       ("long_gqa_32768", 16)])
+def test_long_sampled(name, lead, device):
+    _sampled_check(inputs.case_by_name(name), device, lead)
 
 
 # --- edge cases --------------------------------------------------------------------
@@ -181,29 +191,90 @@ def test_edge_shapes(shape, device):
         pu.assert_within(case, pu.compare(case, got, ref, mode))
 
 
+RISING = [("bf16", 80.0), ("fp16", 12.0), ("fp16", 30.0)]
+
+
+@pytest.mark.parametrize("dtype,rise", RISING, ids=[f"{d}_{r:g}nats" for d, r in RISING])
 @pytest.mark.parametrize("causal", [False, True])
-def test_rising_logits(causal, device):
-    """Scores that rise by about 115 log2 units along every row: the forward's
-    per-column softmax reference, set from the first pair of keys, is then exceeded
-    by more than its 64-unit headroom and the workgroup reruns its item with raised
-    references.  Forward and backward must still match the oracle."""
+def test_rising_logits(dtype, rise, causal, device):
+    """Scores that rise by about ``rise`` nats along every row.  The forward sets
+    each query column's softmax reference from the first pair of keys it sees and
+    lets a later score exceed it by a type-dependent headroom (64 log2 units for
+    bf16, 15 for fp16, whose P would be infinite from 2^16 on); a larger rise
+    makes the workgroup rerun its item with raised references.  12 nats (17.3 log2
+    units) passes the fp16 headroom, 30 and 80 pass it by far, and 80 nats passes
+    the bf16 one.  Forward and backward must still match the oracle on both dQ
+    paths."""
     B, Hq, Hkv, N, d = 1, 2, 1, 384, 64
     g = torch.Generator().manual_seed(4242)
     u = torch.full((d,), 1.0 / np.sqrt(d))
     ramp = torch.arange(N, dtype=torch.float32) / N
+    # score ~ (5 u) . (amp * ramp * u) = 5 * amp * ramp nats, plus noise
+    amp = rise / 5.0
+    tdt = inputs.TORCH_DTYPE[dtype]
     x = {
-        "q": (5.0 * u + 0.5 * torch.randn(B, Hq, N, d, generator=g)).to(torch.bfloat16),
-        "k": (16.0 * ramp[:, None] * u + 0.5 * torch.randn(B, Hkv, N, d, generator=g)).to(torch.bfloat16),
-        "v": torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16),
-        "do": torch.randn(B, Hq, N, d, generator=g).to(torch.bfloat16),
+        "q": (5.0 * u + 0.5 * torch.randn(B, Hq, N, d, generator=g)).to(tdt),
+        "k": (amp * ramp[:, None] * u + 0.5 * torch.randn(B, Hkv, N, d, generator=g)).to(tdt),
+        "v": torch.randn(B, Hkv, N, d, generator=g).to(tdt),
+        "do": torch.randn(B, Hq, N, d, generator=g).to(tdt),
     }
-    case = inputs.Case("rising", 0, 0, B, Hq, Hkv, N, N, d, "bf16", causal, 1.0)
+    case = inputs.Case("rising", 0, 0, B, Hq, Hkv, N, N, d, dtype, causal, 1.0)
     o, lse = orc.forward(x["q"], x["k"], x["v"], case.scale, causal)
     dq, dk, dv = orc.backward(x["q"], x["k"], x["v"], x["do"], case.scale, causal)
     ref = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
-    res = pu.gpu_forward_backward(case, x, device)
-    got = {k: res[k].double().numpy() for k in res}
-    pu.assert_within(case, pu.compare(case, got, ref))
+    # most rows really pass the headroom: a later score exceeds the maximum over
+    # the first 32 keys by more than H log2 units (H = 15 fp16, 64 bf16)
+    sc = orc.as_f64(x["q"][0]) @ orc.as_f64(x["k"][0, 0]).T
+    over = (sc[:, :, 32:].max(-1) - sc[:, :, :32].max(-1)) / np.log(2.0)
+    assert (over > (15.0 if dtype == "fp16" else 64.0)).mean() > 0.5
+    for mode in MODES:
+        res = pu.gpu_forward_backward(case, x, device, dq_mode=mode)
+        got = {k: res[k].double().numpy() for k in res}
+        assert all(bool(np.isfinite(got[k]).all()) for k in ("o", "dq", "dk", "dv"))
+        pu.assert_within(case, pu.compare(case, got, ref, mode))
+
+
+def test_fa_bwd_entry_point(device):
+    """fa_bwd itself (the dQ path FA_DQ_AUTO picks, workspace of exactly
+    fa_bwd_workspace_bytes bytes), called through ctypes, against the oracle."""
+    import ctypes
+
+    import exact_attention_backward_fa_amd as fa
+    from exact_attention_backward_fa_amd import _lib
+    lib = _lib.load()
+    for name, groups in (("ragged_100x333_c", [(0, 1), (1, 3)]), ("llama_gqa_bf16_1024", [(2, 5)])):
+        case = inputs.case_by_name(name)
+        x = inputs.make_inputs(case)
+        d = pu.to_dev(x, device)
+        o, lse = fa.fwd(d["q"], d["k"], d["v"], case.scale, case.causal)
+        dq = torch.full_like(d["q"], float("nan"))
+        dk = torch.full_like(d["k"], float("nan"))
+        dv = torch.full_like(d["v"], float("nan"))
+        dt = _lib.FA_DTYPE[case.torch_dtype]
+        need = lib.fa_bwd_workspace_bytes(case.B, case.Hq, case.Hkv, case.Nq, case.Nkv, case.d,
+                                          int(case.causal), dt)
+        assert need > 0
+        ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=device)
+        stream = torch.cuda.current_stream(device).cuda_stream
+        rc = lib.fa_bwd(d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), o.data_ptr(),
+                        lse.data_ptr(), d["do"].data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                        dv.data_ptr(), case.B, case.Hq, case.Hkv, case.Nq, case.Nkv, case.d,
+                        ctypes.c_float(case.scale), int(case.causal), dt, ws.data_ptr(),
+                        ctypes.c_size_t(need), stream)
+        assert rc == 0, _lib.status_string(rc)
+        # one byte short of the requirement is rejected before any launch
+        rc = lib.fa_bwd(d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), o.data_ptr(),
+                        lse.data_ptr(), d["do"].data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                        dv.data_ptr(), case.B, case.Hq, case.Hkv, case.Nq, case.Nkv, case.d,
+                        ctypes.c_float(case.scale), int(case.causal), dt, ws.data_ptr(),
+                        ctypes.c_size_t(need - 1), stream)
+        assert rc == -6
+        torch.cuda.synchronize(device)
+        res = {"o": o.cpu(), "lse": lse.cpu(), "dq": dq.cpu(), "dk": dk.cpu(), "dv": dv.cpu()}
+        for (b, g) in groups:
+            ref = pu.oracle_group(case, x, b, g)
+            pu.assert_within(case, pu.compare(case, pu.gpu_group(case, res, b, g), ref,
+                                              f"fa_bwd b={b} g={g}"))
 
 
 @pytest.mark.parametrize("dims", [(0, 4, 2, 16, 16), (2, 4, 2, 0, 16), (2, 4, 2, 16, 0),
