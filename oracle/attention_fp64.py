@@ -279,9 +279,13 @@ def dkdv_rows(q, k, v, do, scale: float, causal: bool, b: int, g: int, kv_rows):
             continue
         for rows in _row_chunks(contributing):
             qr, dor = as_f64(q[b, h][rows]), as_f64(do[b, h][rows])
+            # LSE and D need whole rows of S and P; dP and dS only the selected
+            # key columns
             s = masked_scores(qr, kg, scale, keep_mask(rows, Nq, Nkv, causal))
             p = probabilities(s, log_sum_exp(s))
-            ds = score_grad(p, dor @ vg.T, row_delta(dor, p @ vg))
-            dk_out += grad_k(ds[:, kv_rows], qr, scale)
-            dv_out += grad_v(p[:, kv_rows], dor)
+            dlt = row_delta(dor, p @ vg)
+            p_sel = p[:, kv_rows]
+            ds_sel = score_grad(p_sel, dor @ vg[kv_rows].T, dlt)
+            dk_out += grad_k(ds_sel, qr, scale)
+            dv_out += grad_v(p_sel, dor)
     return dk_out, dv_out
