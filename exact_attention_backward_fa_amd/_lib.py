@@ -23,6 +23,7 @@ DQ_MODE_NAMES = {v: k for k, v in DQ_MODES.items()}
 EXPORTS = (
     "fa_fwd", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes",
     "fa_bwd_ex_workspace_bytes", "fa_bwd_auto_dq_mode", "fa_status_string", "fa_version",
+    "fa_bwd_noalloc", "fa_bwd_noalloc_max_scratch_bytes",
 )
 
 _lib = None
@@ -56,6 +57,10 @@ def load() -> ctypes.CDLL:
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = _i
+    lib.fa_bwd_noalloc.argtypes = [_p] * 9 + [_i] * 6 + [_f, _i, _i, _p]
+    lib.fa_bwd_noalloc.restype = _i
+    lib.fa_bwd_noalloc_max_scratch_bytes.argtypes = []
+    lib.fa_bwd_noalloc_max_scratch_bytes.restype = _sz
     _lib = lib
     return lib
 

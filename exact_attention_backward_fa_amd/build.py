@@ -30,7 +30,7 @@ LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
 # Host-side sources (entry points, dispatch, conversions).
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp", "fa_noalloc.hip"]
 # Template instances: (dtype 0 fp16 / 1 bf16, head dim, causal).
 INSTANCES = [(dt, d, c) for dt in (0, 1) for d in (64, 128) for c in (0, 1)]
 # Backward kernel families compiled per instance (FA_KIND in fa_bwd_inst.hip).

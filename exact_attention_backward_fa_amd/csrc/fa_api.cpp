@@ -71,8 +71,7 @@ static int resolve_dq_mode(const Problem& pb, int mode) {
   return FA_DQ_SEPARATE;
 }
 
-int bwd_checked(const BwdCall& c, int dq_mode, void* ev_begin, void* ev_end, void* workspace,
-                size_t workspace_bytes, void* stream) {
+int bwd_validate(const BwdCall& c, int dq_mode, size_t* workspace_need) {
   Problem pb;
   const int st = check_problem(c.B, c.Hq, c.Hkv, c.Nq, c.Nkv, c.d, c.scale, c.dtype, &pb);
   if (st != FA_OK) return st;
@@ -88,6 +87,20 @@ int bwd_checked(const BwdCall& c, int dq_mode, void* ev_begin, void* ev_end, voi
     const int pst = check_ptr(ptrs[i], elems[i]);
     if (pst != FA_OK) return pst;
   }
+  *workspace_need = workspace_layout(pb, resolve_dq_mode(pb, dq_mode) == FA_DQ_ATOMIC).total;
+  return FA_OK;
+}
+
+int bwd_checked(const BwdCall& c, int dq_mode, void* ev_begin, void* ev_end, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  const int st = bwd_validate(c, dq_mode, &need);
+  if (st != FA_OK) return st;
+  Problem pb;
+  (void)check_problem(c.B, c.Hq, c.Hkv, c.Nq, c.Nkv, c.d, c.scale, c.dtype, &pb);
+  pb.causal = c.causal != 0;
+  const size_t nk = (size_t)c.B * c.Hkv * c.Nkv * c.d;
+  const size_t nrows = (size_t)c.B * c.Hq * c.Nq;
   const int mode = resolve_dq_mode(pb, dq_mode);
   const bool atomic = mode == FA_DQ_ATOMIC;
   const WorkspaceLayout L = workspace_layout(pb, atomic);
@@ -163,6 +176,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_HIP: return "a HIP kernel launch failed";
     case FA_ERR_MODE: return "unknown dq_mode";
+    case FA_ERR_SCRATCH:
+      return "the problem needs more scratch than fa_bwd_noalloc holds (FA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

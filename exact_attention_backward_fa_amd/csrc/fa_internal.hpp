@@ -58,6 +58,9 @@ struct BwdCall {
   int causal, dtype;
 };
 
+// Checks every argument of a backward call on the host (no device call); on
+// FA_OK sets *workspace_need to the workspace bytes the call needs.
+int bwd_validate(const BwdCall& c, int dq_mode, size_t* workspace_need);
 // Checks every argument of a backward call on the host, then enqueues the
 // kernels with `workspace` as the scratch memory; returns FA_OK or an FA_ERR_*
 // code (nothing is launched or written on error).

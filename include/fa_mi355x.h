@@ -62,6 +62,7 @@ extern "C" {
 #define FA_ERR_ALIGN    -7  /* a tensor pointer is not 16-byte aligned */
 #define FA_ERR_HIP      -8  /* a kernel launch failed (hipGetLastError) */
 #define FA_ERR_MODE     -9  /* unknown dq_mode */
+#define FA_ERR_SCRATCH  -10 /* fa_bwd_noalloc: the call needs more scratch than it holds */
 
 #define FA_DTYPE_FP16 0
 #define FA_DTYPE_BF16 1
@@ -156,6 +157,30 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
  * FA_DQ_SEPARATE). */
 int fa_bwd_auto_dq_mode(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
                         int causal, int dtype);
+
+/*
+ * Allocation-free backward, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, checks, kernels and results as fa_bwd with the separate dQ
+ * path (FA_DQ_SEPARATE), minus the workspace: its scratch (8 bytes per query row
+ * plus 256 bytes of work-queue counters, each region 256-byte aligned) lives in a
+ * static device array of FA_NOALLOC_SCRATCH_BYTES bytes that each device holds
+ * from the library's first use on it until the process ends.  The call allocates
+ * nothing and calls no allocating routine.  Returns FA_ERR_SCRATCH, launching
+ * nothing, when the problem needs more (with 16 MiB: B*Hq*N_q up to about 2.09
+ * million query rows).  Every call on a device shares that device's array: calls
+ * that overlap on one device (several streams or host threads) race and must be
+ * serialised by the caller.  Each call's preprocess kernel clears the counters
+ * that must start at zero.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                   const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                   float softmax_scale, int causal, int dtype, void* stream);
+
+/* FA_NOALLOC_SCRATCH_BYTES as built into the library. */
+size_t fa_bwd_noalloc_max_scratch_bytes(void);
 
 /* Static text for a status code; never NULL. */
 const char* fa_status_string(int status);

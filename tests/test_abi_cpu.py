@@ -16,6 +16,7 @@ HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
 
 FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_HEADDIM = 0, -1, -2, -3
 FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_MODE = -4, -5, -6, -7, -8, -9
+FA_ERR_SCRATCH = -10
 
 
 @pytest.fixture(scope="module")
@@ -48,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     for code in (FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE, FA_ERR_SCALE,
-                 FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_MODE, 12345):
+                 FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_MODE, FA_ERR_SCRATCH, 12345):
         s = lib.fa_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
     assert lib.fa_status_string(FA_ERR_HEADDIM).decode().find("64") >= 0
@@ -151,3 +152,39 @@ def test_python_binding_refuses_cpu_tensors():
         fa.fwd(q, q, q, 0.125, False)
     with pytest.raises(ValueError):
         fa.fwd(q.float(), q.float(), q.float(), 0.125, False)
+
+
+def noalloc(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=1, Nq=8, Nkv=8,
+             d=64, scale=0.125, causal=0, dtype=0)
+    a.update(kw)
+    return lib.fa_bwd_noalloc(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                              a["dv"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["d"],
+                              a["scale"], a["causal"], a["dtype"], None)
+
+
+def test_noalloc_checks_arguments_before_any_device_call(lib):
+    """fa_bwd_noalloc applies fa_bwd's checks, and rejects a problem whose scratch
+    exceeds its static array, before it touches a device (none exists here)."""
+    cap = lib.fa_bwd_noalloc_max_scratch_bytes()
+    assert cap == 16 << 20
+    assert b"scratch" in lib.fa_status_string(FA_ERR_SCRATCH)
+    assert noalloc(lib, d=96) == FA_ERR_HEADDIM
+    assert noalloc(lib, Hq=3, Hkv=2) == FA_ERR_SHAPE
+    assert noalloc(lib, scale=-1.0) == FA_ERR_SCALE
+    assert noalloc(lib, dtype=5) == FA_ERR_DTYPE
+    assert noalloc(lib, dq=0) == FA_ERR_NULLPTR
+    assert noalloc(lib, dv=P + 2) == FA_ERR_ALIGN
+    # the largest problem that fits, and one query row per head more than that
+    sep = lambda B, Hq, N: lib.fa_bwd_ex_workspace_bytes(B, Hq, 1, N, N, 64, 0, 0, 2)
+    n = 1
+    while sep(1, 1, 2 * n) <= cap:
+        n *= 2
+    lo, hi = n, 2 * n
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if sep(1, 1, mid) <= cap else (lo, mid)
+    assert sep(1, 1, lo) <= cap < sep(1, 1, lo + 1)
+    assert noalloc(lib, Hq=1, Nq=lo + 1, Nkv=16) == FA_ERR_SCRATCH
+    assert noalloc(lib, B=4, Hq=32, Hkv=8, Nq=32768, Nkv=32768, d=128, causal=1,
+                   dtype=1) == FA_ERR_SCRATCH
