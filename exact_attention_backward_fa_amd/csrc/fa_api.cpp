@@ -60,11 +60,15 @@ static int check_ptr(const void* ptr, size_t elems) {
   return FA_OK;
 }
 
-// FA_DQ_AUTO: the separate query-parallel dQ pass.  Measured on MI355X at the
-// causal GQA shape (B=4, Hq=32, Hkv=8, N=8192, d=128, bf16) the backward takes
-// 9.7 ms with it against 13.4 ms with float atomics, whose read-modify-write
-// traffic (about 17 GB per call at that shape) does not stay in L2; the separate
-// pass is also bitwise repeatable.
+// FA_DQ_AUTO: the separate query-parallel dQ pass.  Measured with rocprofv3 on
+// MI355X at the causal GQA shape (B=4, Hq=32, Hkv=8, N=8192, d=128, bf16;
+// profiles/kernel_trace_llama_gqa_bf16_8192.md and
+// profiles/kernel_trace_atomic_dq_llama_gqa_bf16_8192.md): dK/dV 3.10 ms + dQ pass
+// 2.45 ms against 13.4 ms for the fused kernel with float atomics.  Its 4.36 G
+// atomic adds are performed at the memory side (WRITE_SIZE 17.6 GB per launch,
+// profiles/hbm_traffic_atomic_dq_llama_gqa_bf16_8192.txt), not in L2; even half
+// as many (256-key blocks) would move 8.8 GB.  The separate pass is also bitwise
+// repeatable.
 static int resolve_dq_mode(const Problem& pb, int mode) {
   if (mode == FA_DQ_ATOMIC || mode == FA_DQ_SEPARATE) return mode;
   (void)pb;

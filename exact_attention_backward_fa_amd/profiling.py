@@ -34,7 +34,8 @@ ROOT = os.path.dirname(PKG)
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ("csrc/fa_bwd.hip", "csrc/fa_bwd_inst.hip", "csrc/fa_bwd_kernels.hpp",
                   "csrc/fa_bwd_atomic.hpp", "csrc/fa_bwd_common.hpp", "csrc/fa_fwd.hip",
-                  "csrc/fa_fwd_kernels.hpp", "csrc/fa_pipeline.hpp", "csrc/fa_common.hpp")
+                  "csrc/fa_fwd_inst.hip", "csrc/fa_fwd_kernels.hpp", "csrc/fa_pipeline.hpp",
+                  "csrc/fa_common.hpp")
 COPY_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_llama_gqa_bf16_8192.txt")
 MFMA_FILE = os.path.join(PROFILES, "mfma_busy_llama_gqa_bf16_8192.txt")
@@ -65,6 +66,7 @@ def trace_summary(d: str, command: str) -> str:
     path = _find(d, "*kernel_stats.csv")
     rows = list(csv.DictReader(open(path)))
     out = ["# Kernel trace summary", "", f"Command: `{command}`", "",
+           f"kernel_source_sha256_16: {kernel_source_hash()}", "",
            "| kernel | calls | avg (us) | min (us) | max (us) | share |",
            "|---|---|---|---|---|---|"]
     for r in rows:
