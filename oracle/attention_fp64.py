@@ -43,6 +43,24 @@ Readings where the pages are silent or disagree (each is listed in the design doc):
 * The scale is applied to dS once, in the dQ and dK products; folding it into
   dS first (Triton page) is the same number.
 
+Two optional extensions of the scores and probabilities (both off by default,
+when the arithmetic above is exactly what runs):
+
+* an additive bias: S = scale * Q_h K_g^T + bias_h (the Liger-Kernel pull
+  request "[Kernel] Flash attention 2", Details, lists an attention mask and an
+  attention bias); the bias is part of the score, so its gradient is the score
+  gradient, dBias = dS;
+* dropout of the probabilities: O = (P o Z) V with Z = keep / (1 - p) (the same
+  page, Details: dropout in the forward, its gradient left unsolved there).  Then
+  dV = (P o Z)^T dO, dP = (dO V^T) o Z, and D = rowsum(dO o O) and
+  dS = P o (dP - D) keep their form.  The keep decisions come from the
+  counter-based generator Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
+  random numbers: as easy as 1, 2, 3", SC 2011), one call per 4 x 4 block of
+  (query, key) positions: counter (key // 4, query // 4, query head, batch), key =
+  the 64-bit seed's low and high words; element (i, j) keeps iff byte j % 4 of
+  output word i % 4 is below T = floor((1 - p) * 256 + 1/2) (float32 arithmetic),
+  so the keep probability is T / 256 and Z = 256 / T on kept elements.
+
 Pinned (tests/test_oracle_cpu.py) by central finite differences of
 L = <dO, O>, the identities sum_j dS_ij = 0, sum_j dK_j = 0,
 sum_keys dV = sum_queries dO, <Q, dQ> = <K, dK>, <V, dV> = <dO, O>, closed forms
@@ -83,9 +101,11 @@ def keep_mask(rows: np.ndarray, Nq: int, Nkv: int, causal: bool) -> np.ndarray:
 
 
 def masked_scores(q_rows: np.ndarray, k: np.ndarray, scale: float,
-                  keep: np.ndarray) -> np.ndarray:
-    """S = scale * q_rows k^T with masked entries at -inf."""
+                  keep: np.ndarray, bias_rows=None) -> np.ndarray:
+    """S = scale * q_rows k^T (+ bias_rows) with masked entries at -inf."""
     s = scale * (q_rows @ k.T)
+    if bias_rows is not None:
+        s = s + bias_rows
     return np.where(keep, s, -np.inf)
 
 
@@ -118,6 +138,81 @@ def score_grad(p: np.ndarray, dp: np.ndarray, dlt: np.ndarray) -> np.ndarray:
     return p * (dp - dlt[:, None])
 
 
+# --- Counter-based generator and dropout keep decisions ---------------------------
+
+# Philox constants of the paper: round multipliers M and key increments W (the
+# golden ratio and sqrt(3) - 1 in fixed point), per word width.
+PHILOX = {
+    32: ((0xD2511F53, 0xCD9E8D57), (0x9E3779B9, 0xBB67AE85)),
+    64: ((0xD2E7470EE14C6C93, 0xCA5A826395121157), (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)),
+}
+
+
+def _mulhilo(m: int, x: np.ndarray, bits: int):
+    """(high, low) words of the 2*bits-bit product m * x (x: uint64 array of words)."""
+    if bits == 32:
+        prod = x * np.uint64(m)
+        return prod >> np.uint64(32), prod & np.uint64(0xFFFFFFFF)
+    # 64-bit words: schoolbook product of 32-bit halves
+    lo32 = np.uint64(0xFFFFFFFF)
+    m1, m0 = np.uint64(m >> 32), np.uint64(m & 0xFFFFFFFF)
+    x1, x0 = x >> np.uint64(32), x & lo32
+    p00, p01, p10, p11 = x0 * m0, x0 * m1, x1 * m0, x1 * m1
+    mid = (p00 >> np.uint64(32)) + (p01 & lo32) + (p10 & lo32)
+    lo = (p00 & lo32) | ((mid & lo32) << np.uint64(32))
+    hi = p11 + (p01 >> np.uint64(32)) + (p10 >> np.uint64(32)) + (mid >> np.uint64(32))
+    return hi, lo
+
+
+def philox4(ctr, key, bits: int = 32, rounds: int = 10) -> np.ndarray:
+    """Philox4xW-R: counter words ctr[..., 0..3], key words (k0, k1); returns the
+    four output words [..., 4] as uint64 (each < 2^bits).  A round maps
+    (c0, c1, c2, c3) to (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+    lo(M0 c0)); the key is bumped by W before every round but the first."""
+    (m0, m1), (w0, w1) = PHILOX[bits]
+    mask = (1 << bits) - 1
+    ctr = np.asarray(ctr, dtype=np.uint64)
+    c0, c1, c2, c3 = (ctr[..., i].copy() for i in range(4))
+    k0, k1 = int(key[0]) & mask, int(key[1]) & mask
+    for r in range(rounds):
+        if r > 0:
+            k0, k1 = (k0 + w0) & mask, (k1 + w1) & mask
+        hi0, lo0 = _mulhilo(m0, c0, bits)
+        hi1, lo1 = _mulhilo(m1, c2, bits)
+        c0, c1, c2, c3 = hi1 ^ c1 ^ np.uint64(k0), lo1, hi0 ^ c3 ^ np.uint64(k1), lo0
+    return np.stack([c0, c1, c2, c3], axis=-1)
+
+
+def dropout_threshold(p: float) -> int:
+    """T = floor((1 - p) * 256 + 1/2) in float32 arithmetic, clamped to [0, 256]:
+    an element is kept iff its random byte is below T."""
+    one, p32 = np.float32(1.0), np.float32(p)
+    t = np.floor((one - p32) * np.float32(256.0) + np.float32(0.5))
+    return int(min(max(t, 0.0), 256.0))
+
+
+def dropout_factors(b: int, h: int, rows, n_keys: int, p: float, seed: int) -> np.ndarray:
+    """Z [len(rows), n_keys]: 256 / T where (query row, key) is kept, else 0."""
+    rows = np.asarray(rows, dtype=np.int64)
+    t = dropout_threshold(p)
+    if t >= 256:
+        return np.ones((rows.shape[0], n_keys))
+    if t == 0:
+        return np.zeros((rows.shape[0], n_keys))
+    kb = np.arange((n_keys + 3) // 4, dtype=np.uint64)
+    ctr = np.zeros((rows.shape[0], kb.shape[0], 4), dtype=np.uint64)
+    ctr[..., 0] = kb[None, :]
+    ctr[..., 1] = (rows >> 2).astype(np.uint64)[:, None]
+    ctr[..., 2] = h
+    ctr[..., 3] = b
+    words = philox4(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))  # [R, Kb, 4]
+    j = np.arange(n_keys)
+    w = words[:, j >> 2, :]                                                 # [R, n_keys, 4]
+    word = np.take_along_axis(w, (rows & 3)[:, None, None], axis=2)[..., 0]
+    byte = (word >> (np.uint64(8) * (j & 3).astype(np.uint64))[None, :]) & np.uint64(0xFF)
+    return np.where(byte < np.uint64(t), 256.0 / t, 0.0)
+
+
 def grad_q(ds: np.ndarray, k: np.ndarray, scale: float) -> np.ndarray:
     return scale * (ds @ k)
 
@@ -143,10 +238,26 @@ def _row_chunks(rows: np.ndarray):
         yield rows[s:s + ROW_CHUNK]
 
 
-def forward(q, k, v, scale: float, causal: bool):
-    """O [B,Hq,Nq,d] and LSE [B,Hq,Nq] in float64."""
+def _bias_of(bias, B, Hq, Nq, Nkv):
+    """The bias broadcast to [B, Hq, Nq, Nkv] in float64 (None stays None)."""
+    if bias is None:
+        return None
+    return np.broadcast_to(as_f64(bias), (B, Hq, Nq, Nkv))
+
+
+def _dropout_of(b, h, rows, Nkv, dropout_p, seed):
+    if dropout_p == 0.0:
+        return None
+    return dropout_factors(b, h, rows, Nkv, dropout_p, seed)
+
+
+def forward(q, k, v, scale: float, causal: bool, bias=None, dropout_p: float = 0.0,
+            seed: int = 0):
+    """O [B,Hq,Nq,d] and LSE [B,Hq,Nq] in float64.  ``bias``: broadcastable to
+    [B,Hq,Nq,Nkv], added to the scores; ``dropout_p``, ``seed``: dropout of P."""
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     B, Hq, Hkv, Nq, Nkv, d = _check_shapes(q, k, v)
+    bias = _bias_of(bias, B, Hq, Nq, Nkv)
     o = np.zeros((B, Hq, Nq, d))
     lse = np.full((B, Hq, Nq), -np.inf)
     for b in range(B):
@@ -154,44 +265,60 @@ def forward(q, k, v, scale: float, causal: bool):
             g = kv_head_index(h, Hq, Hkv)
             for rows in _row_chunks(np.arange(Nq)):
                 s = masked_scores(q[b, h, rows], k[b, g], scale,
-                                  keep_mask(rows, Nq, Nkv, causal))
+                                  keep_mask(rows, Nq, Nkv, causal),
+                                  None if bias is None else bias[b, h, rows])
                 l_ = log_sum_exp(s)
                 p = probabilities(s, l_)
-                o[b, h, rows] = p @ v[b, g]
+                z = _dropout_of(b, h, rows, Nkv, dropout_p, seed)
+                o[b, h, rows] = (p if z is None else p * z) @ v[b, g]
                 lse[b, h, rows] = l_
     return o, lse
 
 
-def backward(q, k, v, do, scale: float, causal: bool, return_delta: bool = False):
+def backward(q, k, v, do, scale: float, causal: bool, return_delta: bool = False,
+             bias=None, dropout_p: float = 0.0, seed: int = 0, return_dbias: bool = False):
     """dQ, dK, dV in float64 from the definition (O and LSE recomputed here).
 
     With ``return_delta`` also returns D [B,Hq,Nq] computed from the oracle's
-    own float64 O.
+    own float64 O; with ``return_dbias`` also dBias = dS [B,Hq,Nq,Nkv] (last).
+    ``bias``, ``dropout_p`` and ``seed`` as in ``forward``.
     """
     q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     B, Hq, Hkv, Nq, Nkv, d = _check_shapes(q, k, v)
+    bias = _bias_of(bias, B, Hq, Nq, Nkv)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     dlt_all = np.zeros((B, Hq, Nq))
+    dbias = np.zeros((B, Hq, Nq, Nkv)) if return_dbias else None
     for b in range(B):
         for h in range(Hq):
             g = kv_head_index(h, Hq, Hkv)
             for rows in _row_chunks(np.arange(Nq)):
                 qr, dor = q[b, h, rows], do[b, h, rows]
-                s = masked_scores(qr, k[b, g], scale, keep_mask(rows, Nq, Nkv, causal))
+                s = masked_scores(qr, k[b, g], scale, keep_mask(rows, Nq, Nkv, causal),
+                                  None if bias is None else bias[b, h, rows])
                 p = probabilities(s, log_sum_exp(s))
-                o_rows = p @ v[b, g]
+                z = _dropout_of(b, h, rows, Nkv, dropout_p, seed)
+                pz = p if z is None else p * z          # the probabilities V is weighted by
+                o_rows = pz @ v[b, g]
                 dlt = row_delta(dor, o_rows)
                 dp = dor @ v[b, g].T
+                if z is not None:
+                    dp = dp * z
                 ds = score_grad(p, dp, dlt)
                 dq[b, h, rows] = grad_q(ds, k[b, g], scale)
                 dk[b, g] += grad_k(ds, qr, scale)
-                dv[b, g] += grad_v(p, dor)
+                dv[b, g] += grad_v(pz, dor)
                 dlt_all[b, h, rows] = dlt
+                if dbias is not None:
+                    dbias[b, h, rows] = ds
+    out = (dq, dk, dv)
     if return_delta:
-        return dq, dk, dv, dlt_all
-    return dq, dk, dv
+        out = out + (dlt_all,)
+    if return_dbias:
+        out = out + (dbias,)
+    return out
 
 
 def score_grad_matrix(q, k, v, do, scale: float, causal: bool, b: int, h: int):

@@ -243,6 +243,175 @@ def pin_row_variants(orc, seed=19) -> float:
     return worst
 
 
+# --- Additive bias and dropout --------------------------------------------------
+
+EXT_FD_SHAPES = [
+    # B, Hq, Hkv, Nq, Nkv, d, causal, bias shape, dropout p
+    (1, 2, 1, 3, 6, 4, True, (1, 2, 3, 6), 0.3),
+    (1, 2, 1, 4, 4, 4, False, (1, 1, 4, 4), 0.0),     # bias shared by the heads
+    (1, 4, 2, 3, 5, 3, True, (1, 4, 1, 5), 0.5),     # per-key bias (a padding mask shape)
+    (1, 1, 1, 5, 3, 2, True, (1, 1, 5, 3), 0.25),    # rows 0 and 1 see no key
+]
+
+
+def pin_ext_finite_differences(orc, seed=23) -> float:
+    """Central differences of L = <dO, O(Q, K, V, bias)> with an additive bias and
+    dropout (a fixed keep mask from the seed) against the oracle backward, bias
+    gradient included (summed over the dimensions the bias is broadcast along)."""
+    worst = 0.0
+    rng = np.random.default_rng(seed)
+    h = 1e-5
+    for n, (B, Hq, Hkv, Nq, Nkv, d, causal, bshape, pdrop) in enumerate(EXT_FD_SHAPES):
+        q = _rand(rng, (B, Hq, Nq, d))
+        k = _rand(rng, (B, Hkv, Nkv, d))
+        v = _rand(rng, (B, Hkv, Nkv, d))
+        do = _rand(rng, (B, Hq, Nq, d))
+        bias = _rand(rng, bshape)
+        scale, rseed = 0.6, 1000 + n
+
+        def loss(args):
+            o, _ = orc.forward(args["q"], args["k"], args["v"], scale, causal, bias=args["bias"],
+                               dropout_p=pdrop, seed=rseed)
+            return float((o * do).sum())
+
+        dq, dk, dv, dbias = orc.backward(q, k, v, do, scale, causal, bias=bias, dropout_p=pdrop,
+                                         seed=rseed, return_dbias=True)
+        # the gradient of a broadcast bias sums over the broadcast dimensions
+        axes = tuple(i for i, (a, b_) in enumerate(zip(bshape, dbias.shape)) if a == 1 and b_ != 1)
+        dbias_b = dbias.sum(axis=axes, keepdims=True)
+        base = {"q": q, "k": k, "v": v, "bias": bias}
+        for name, g in (("q", dq), ("k", dk), ("v", dv), ("bias", dbias_b)):
+            x = base[name]
+            fd = np.zeros_like(x)
+            it = np.nditer(x, flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                ap = dict(base); ap[name] = x.copy(); ap[name][idx] += h
+                am = dict(base); am[name] = x.copy(); am[name][idx] -= h
+                fd[idx] = (loss(ap) - loss(am)) / (2 * h)
+            den = max(float(np.abs(fd).max()), 1.0)
+            worst = max(worst, float(np.abs(fd - g).max()) / den)
+    return worst
+
+
+def pin_ext_identities(orc, seed=29) -> float:
+    """With a bias and dropout: rowsum dS = 0, <Q,dQ> = <K,dK> (Q -> aQ, K -> K/a
+    leaves the scores unchanged), <dO,O> = <V,dV> (L is linear in V); a zero bias
+    and p = 0 reproduce the plain attention exactly; a bias constant along each
+    row leaves O unchanged and shifts LSE by that constant; a bias of -inf on a
+    set of keys is the attention over the remaining keys."""
+    worst = 0.0
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, Nq, Nkv, d = 1, 4, 2, 9, 11, 8
+    q = _rand(rng, (B, Hq, Nq, d))
+    k = _rand(rng, (B, Hkv, Nkv, d))
+    v = _rand(rng, (B, Hkv, Nkv, d))
+    do = _rand(rng, (B, Hq, Nq, d))
+    bias = _rand(rng, (B, Hq, Nq, Nkv))
+    for causal in (False, True):
+        o, _ = orc.forward(q, k, v, 0.4, causal, bias=bias, dropout_p=0.4, seed=77)
+        dq, dk, dv, ds = orc.backward(q, k, v, do, 0.4, causal, bias=bias, dropout_p=0.4, seed=77,
+                                      return_dbias=True)
+        worst = max(worst, float(np.abs(ds.sum(axis=-1)).max()) / float(np.abs(ds).max()))
+        G = Hq // Hkv
+        for g in range(Hkv):
+            heads = range(g * G, (g + 1) * G)
+            lhs = sum(float((q[0, h] * dq[0, h]).sum()) for h in heads)
+            rhs = float((k[0, g] * dk[0, g]).sum())
+            worst = max(worst, abs(lhs - rhs) / max(abs(rhs), 1e-300))
+            lhs = sum(float((do[0, h] * o[0, h]).sum()) for h in heads)
+            rhs = float((v[0, g] * dv[0, g]).sum())
+            worst = max(worst, abs(lhs - rhs) / max(abs(rhs), 1e-300))
+        plain = orc.forward(q, k, v, 0.4, causal)
+        zero = orc.forward(q, k, v, 0.4, causal, bias=np.zeros((1, 1, 1, Nkv)), dropout_p=0.0)
+        worst = max(worst, float(np.abs(plain[0] - zero[0]).max()))
+        gp = orc.backward(q, k, v, do, 0.4, causal)
+        gz = orc.backward(q, k, v, do, 0.4, causal, bias=np.zeros((1, 1, 1, Nkv)), dropout_p=0.0)
+        worst = max(worst, max(float(np.abs(a - b_).max()) for a, b_ in zip(gp, gz)))
+        shift = _rand(rng, (B, Hq, Nq, 1))
+        o_s, l_s = orc.forward(q, k, v, 0.4, causal, bias=shift)
+        fin = np.isfinite(plain[1])
+        worst = max(worst, _rel(o_s, plain[0]), float(np.abs((l_s - plain[1])[fin] - shift[..., 0][fin]).max()))
+    # -inf bias on keys 2, 5, 6 (non-causal) = attention over the other keys
+    drop = [2, 5, 6]
+    keep = [j for j in range(Nkv) if j not in drop]
+    mb = np.zeros((1, 1, 1, Nkv)); mb[..., drop] = -np.inf
+    o_m, l_m = orc.forward(q, k, v, 0.4, False, bias=mb)
+    o_r, l_r = orc.forward(q, k[:, :, keep], v[:, :, keep], 0.4, False)
+    worst = max(worst, _rel(o_m, o_r), float(np.abs(l_m - l_r).max()))
+    gm = orc.backward(q, k, v, do, 0.4, False, bias=mb)
+    gr = orc.backward(q, k[:, :, keep], v[:, :, keep], do, 0.4, False)
+    worst = max(worst, _rel(gm[0], gr[0]), _rel(gm[1][:, :, keep], gr[1]), _rel(gm[2][:, :, keep], gr[2]))
+    worst = max(worst, float(np.abs(gm[1][:, :, drop]).max()), float(np.abs(gm[2][:, :, drop]).max()))
+    return worst
+
+
+# Known-answer vectors of Philox4x32-10 published with the algorithm (the Random123
+# library's test vectors by its authors): (counter, key) -> output words.
+PHILOX4X32_KAT = [
+    ((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+    ((0xFFFFFFFF,) * 4, (0xFFFFFFFF, 0xFFFFFFFF), (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+    ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+     (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+]
+
+
+def pin_philox(orc) -> float:
+    """The generator: Philox4x32-10 against its published known-answer vectors;
+    the same code at 64-bit words (Philox4x64-10) against NumPy's Philox bit
+    generator, which increments its 256-bit counter before each block of four
+    words; the dropout keep decisions against a per-element brute force of the
+    definition; the keep rate against T / 256."""
+    worst = 0.0
+    for ctr, key, want in PHILOX4X32_KAT:
+        got = orc.philox4(np.array([ctr], dtype=np.uint64), key)[0]
+        worst = max(worst, float(sum(int(a) != b for a, b in zip(got, want))))
+    gen = np.random.Philox(counter=[5, 0, 0, 0], key=[123456789, 987654321])
+    raw = gen.random_raw(12).reshape(3, 4)
+    for blk in range(3):
+        got = orc.philox4(np.array([[6 + blk, 0, 0, 0]], dtype=np.uint64),
+                          (123456789, 987654321), bits=64)[0]
+        worst = max(worst, float(sum(int(a) != int(b) for a, b in zip(got, raw[blk]))))
+    # brute force of the keep rule on a few (b, h, i, j)
+    p, seed = 0.3, (7 << 32) | 12345
+    t = orc.dropout_threshold(p)
+    rows = np.arange(5, 14)
+    z = orc.dropout_factors(1, 3, rows, 10, p, seed)
+    for a, i in enumerate(rows):
+        for j in range(10):
+            w = orc.philox4(np.array([[j // 4, i // 4, 3, 1]], dtype=np.uint64),
+                            (seed & 0xFFFFFFFF, seed >> 32))[0][i % 4]
+            byte = (int(w) >> (8 * (j % 4))) & 0xFF
+            want = 256.0 / t if byte < t else 0.0
+            worst = max(worst, abs(z[a, j] - want))
+    # threshold rule and extremes
+    worst = max(worst, float(orc.dropout_threshold(0.0) != 256), float(orc.dropout_threshold(1.0) != 0),
+                float(orc.dropout_threshold(0.5) != 128), float(orc.dropout_threshold(0.1) != 230),
+                float(orc.dropout_threshold(0.7) != 77))  # 76.8 rounds up
+    worst = max(worst, float(np.abs(orc.dropout_factors(0, 0, rows, 10, 0.0, seed) - 1.0).max()))
+    worst = max(worst, float(np.abs(orc.dropout_factors(0, 0, rows, 10, 1.0, seed)).max()))
+    # keep rate over 512 x 512 positions: within 6 standard deviations of T / 256
+    z = orc.dropout_factors(2, 5, np.arange(512), 512, 0.2, 99)
+    t = orc.dropout_threshold(0.2)
+    rate, want = float((z > 0).mean()), t / 256.0
+    sd = math.sqrt(want * (1 - want) / z.size)
+    worst = max(worst, max(0.0, abs(rate - want) - 6 * sd))
+    return worst
+
+
+def pin_dropout_unbiased(orc) -> float:
+    """Averaged over seeds, O with dropout is O without (each weight P_ij Z_ij has
+    mean P_ij); the bound allows 6 standard errors of the mean of 400 draws."""
+    rng = np.random.default_rng(31)
+    q = _rand(rng, (1, 1, 3, 4))
+    k = _rand(rng, (1, 1, 5, 4))
+    v = _rand(rng, (1, 1, 5, 4))
+    o_ref, _ = orc.forward(q, k, v, 0.5, False)
+    draws = np.stack([orc.forward(q, k, v, 0.5, False, dropout_p=0.5, seed=s)[0] for s in range(400)])
+    mean, sem = draws.mean(axis=0), draws.std(axis=0) / math.sqrt(draws.shape[0])
+    return float(np.max(np.maximum(0.0, np.abs(mean - o_ref) - 6 * sem)))
+
+
 ALL_PINS = [
     ("finite_differences", pin_finite_differences, FD_TOL),
     ("identities", pin_identities, IDENTITY_TOL),
@@ -250,4 +419,8 @@ ALL_PINS = [
     ("naive_forward", pin_naive_forward, NAIVE_TOL),
     ("golden", pin_golden, GOLDEN_TOL),
     ("row_variants", pin_row_variants, NAIVE_TOL),
+    ("ext_finite_differences", pin_ext_finite_differences, FD_TOL),
+    ("ext_identities", pin_ext_identities, IDENTITY_TOL),
+    ("philox", pin_philox, 0.0),
+    ("dropout_unbiased", pin_dropout_unbiased, 0.0),
 ]

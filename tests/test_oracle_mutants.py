@@ -19,13 +19,42 @@ MUTANTS = {
                       else np.ones((len(rows), nkv), bool)),
     "gqa_modulo": ("kv_head_index", lambda h, hq, hkv: h % hkv),
     "lse_log2": ("log_sum_exp", lambda s: orc_lse_log2(s)),
+    # additive bias and dropout
+    "bias_subtracted": ("masked_scores", lambda q, k, scale, keep, bias=None:
+                        _ORIG_SCORES(q, k, scale, keep, None if bias is None else -bias)),
+    "dropout_not_rescaled": ("dropout_factors", lambda *a: np.minimum(_ORIG_DROP(*a), 1.0)),
+    "dropout_keeps_above_threshold": ("dropout_factors", lambda *a: orc_drop_inverted(*a)),
+    "philox_no_key_bump": ("philox4", lambda ctr, key, bits=32, rounds=10:
+                           orc_philox_no_bump(ctr, key, bits, rounds)),
+    "threshold_truncated": ("dropout_threshold", lambda p: int(np.floor((np.float32(1) - np.float32(p))
+                                                                        * np.float32(256)))),
 }
 
 _ORIG_LSE = orc.log_sum_exp
+_ORIG_SCORES = orc.masked_scores
+_ORIG_DROP = orc.dropout_factors
+_ORIG_PHILOX = orc.philox4
 
 
 def orc_lse_log2(s):
     return _ORIG_LSE(s) / np.log(2.0)
+
+
+def orc_drop_inverted(b, h, rows, n_keys, p, seed):
+    """keep where the byte is at or above the threshold (the complement rule)"""
+    z = _ORIG_DROP(b, h, rows, n_keys, p, seed)
+    t = orc.dropout_threshold(p)
+    if t in (0, 256):
+        return z
+    return np.where(z > 0, 0.0, 256.0 / (256 - t))
+
+
+def orc_philox_no_bump(ctr, key, bits, rounds):
+    """every round with the unbumped key"""
+    out = np.asarray(ctr, dtype=np.uint64)
+    for _ in range(rounds):
+        out = _ORIG_PHILOX(out, key, bits, 1)
+    return out
 
 
 @pytest.mark.parametrize("mutant", sorted(MUTANTS))
