@@ -32,7 +32,10 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 # Host-side sources (entry points, dispatch, conversions).
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp", "fa_noalloc.hip"]
 # Template instances: (dtype 0 fp16 / 1 bf16, head dim, causal).
-INSTANCES = [(dt, d, c) for dt in (0, 1) for d in (64, 128) for c in (0, 1)]
+HEAD_DIMS = (32, 64, 96, 128, 256)
+INSTANCES = [(dt, d, c) for dt in (0, 1) for d in HEAD_DIMS for c in (0, 1)]
+# The fused atomic dK/dV/dQ kernel is built for these head dims only.
+ATOMIC_HEAD_DIMS = (64, 128)
 # Backward kernel families compiled per instance (FA_KIND in fa_bwd_inst.hip).
 BWD_KINDS = {0: "pre", 1: "dkdv", 2: "dq", 3: "atomic"}
 
@@ -70,6 +73,8 @@ def units() -> List[Unit]:
         out.append(Unit(f"fwd_{dt}_{d}_{c}", "fa_fwd_inst.hip",
                         [("FA_DT", dt), ("FA_D", d), ("FA_CAUSAL", c)]))
         for kind, kname in BWD_KINDS.items():
+            if kname == "atomic" and d not in ATOMIC_HEAD_DIMS:
+                continue
             out.append(Unit(f"{kname}_{dt}_{d}_{c}", "fa_bwd_inst.hip",
                             [("FA_DT", dt), ("FA_D", d), ("FA_CAUSAL", c), ("FA_KIND", kind)]))
     return out

@@ -27,7 +27,7 @@ WorkspaceLayout workspace_layout(const Problem& pb, bool atomic_dq) {
 static int check_problem(int B, int Hq, int Hkv, int Nq, int Nkv, int d, float scale, int dtype,
                          Problem* out) {
   if (dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16) return FA_ERR_DTYPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!head_dim_supported(d)) return FA_ERR_HEADDIM;
   if (B < 0 || Nq < 0 || Nkv < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (B > 65535 || Hq > 65535) return FA_ERR_SHAPE;  // grid y/z limits
   if ((int64_t)Nq * d >= ((int64_t)1 << 31) || (int64_t)Nkv * d >= ((int64_t)1 << 31))
@@ -91,7 +91,9 @@ int bwd_validate(const BwdCall& c, int dq_mode, size_t* workspace_need) {
     const int pst = check_ptr(ptrs[i], elems[i]);
     if (pst != FA_OK) return pst;
   }
-  *workspace_need = workspace_layout(pb, resolve_dq_mode(pb, dq_mode) == FA_DQ_ATOMIC).total;
+  const int mode = resolve_dq_mode(pb, dq_mode);
+  if (mode == FA_DQ_ATOMIC && !atomic_head_dim(pb.d)) return FA_ERR_HEADDIM;
+  *workspace_need = workspace_layout(pb, mode == FA_DQ_ATOMIC).total;
   return FA_OK;
 }
 
@@ -151,6 +153,7 @@ size_t bwd_workspace_checked(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int
   if (dq_mode != FA_DQ_AUTO && dq_mode != FA_DQ_ATOMIC && dq_mode != FA_DQ_SEPARATE) return 0;
   pb.causal = causal != 0;
   const int mode = resolve_dq_mode(pb, dq_mode);
+  if (mode == FA_DQ_ATOMIC && !atomic_head_dim(pb.d)) return 0;
   return workspace_layout(pb, mode == FA_DQ_ATOMIC).total;
 }
 
@@ -173,7 +176,8 @@ const char* fa_status_string(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULLPTR: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (B, Hq, Hkv, N_q, N_kv), Hq % Hkv != 0, or a size limit exceeded";
-    case FA_ERR_HEADDIM: return "head dimension d must be 64 or 128";
+    case FA_ERR_HEADDIM:
+      return "head dimension d must be 32, 64, 96, 128 or 256 (the atomic dQ path: 64 or 128)";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "softmax_scale must be finite and > 0";
     case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned, or smaller than required";

@@ -39,20 +39,31 @@ int device_cu_count() {
 // Dispatch.
 hipError_t launch_bwd_pre(const BwdArgs& a, bool zero_dq_acc, hipStream_t s) {
   if ((size_t)a.pb.B * a.pb.Hq * a.pb.Nq == 0) return hipSuccess;
-  FA_DISPATCH(dispatch_key(a.pb), run_pre, a, zero_dq_acc, s)
+  FA_DISPATCH(a.pb, run_pre, a, zero_dq_acc, s);
+  return hipErrorInvalidValue;
+}
+
+// The fused atomic kernel exists for d = 64 and 128 (the API rejects the atomic
+// path for other head dims).
+template <int DT, int D, bool CAUSAL>
+static hipError_t run_dkdv_atomic_if_built(const BwdArgs& a, hipStream_t s) {
+  if constexpr (atomic_head_dim(D)) return run_dkdv_atomic<DT, D, CAUSAL>(a, s);
+  (void)a;
+  (void)s;
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, bool atomic_dq, hipStream_t s) {
   if ((size_t)a.pb.B * a.pb.Nkv == 0) return hipSuccess;
-  if (atomic_dq) {
-    FA_DISPATCH(dispatch_key(a.pb), run_dkdv_atomic, a, s)
-  }
-  FA_DISPATCH(dispatch_key(a.pb), run_dkdv, a, s)
+  if (atomic_dq) FA_DISPATCH(a.pb, run_dkdv_atomic_if_built, a, s);
+  FA_DISPATCH(a.pb, run_dkdv, a, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
   if ((size_t)a.pb.B * a.pb.Nq == 0) return hipSuccess;
-  FA_DISPATCH(dispatch_key(a.pb), run_dq, a, s)
+  FA_DISPATCH(a.pb, run_dq, a, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_dq_convert(const BwdArgs& a, hipStream_t s) {

@@ -117,21 +117,4 @@ template <int DT, int D, bool CAUSAL> hipError_t run_dkdv(const BwdArgs& a, hipS
 template <int DT, int D, bool CAUSAL> hipError_t run_dq(const BwdArgs& a, hipStream_t s);
 template <int DT, int D, bool CAUSAL> hipError_t run_dkdv_atomic(const BwdArgs& a, hipStream_t s);
 
-// Template instance for a problem: dtype (0 fp16, 1 bf16), head dim, causal.
-inline int dispatch_key(const Problem& pb) {
-  return pb.dtype * 4 + (pb.d == 128 ? 2 : 0) + (pb.causal ? 1 : 0);
-}
-
-#define FA_DISPATCH(KEY, FN, ...)                        \
-  switch (KEY) {                                         \
-    case 0: return FN<0, 64, false>(__VA_ARGS__);        \
-    case 1: return FN<0, 64, true>(__VA_ARGS__);         \
-    case 2: return FN<0, 128, false>(__VA_ARGS__);       \
-    case 3: return FN<0, 128, true>(__VA_ARGS__);        \
-    case 4: return FN<1, 64, false>(__VA_ARGS__);        \
-    case 5: return FN<1, 64, true>(__VA_ARGS__);         \
-    case 6: return FN<1, 128, false>(__VA_ARGS__);       \
-    default: return FN<1, 128, true>(__VA_ARGS__);       \
-  }
-
 }  // namespace fa

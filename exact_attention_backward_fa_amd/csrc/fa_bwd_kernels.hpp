@@ -44,19 +44,30 @@ namespace fa {
 // (head-dim tiles), in the two steps after the pair: steps 0-1 finish the previous
 // tile's second pair, steps 2-3 this tile's first; a flush step issues both halves
 // of the last pair.
-template <int NK>
+template <int NK, int KT>
 struct DkdvSteps {
   template <int ST>
-  using P = StepPlan<NK, 4, NK, 4, NK, 4, NK, 4, 1>;
+  using P = StepPlan<NK, KT, NK, KT, NK, KT, NK, KT, 1>;
   template <int ST>
-  using Flush = StepPlan<0, 4, 2 * NK, 4, 0, 4, NK, 4, 1>;
+  using Flush = StepPlan<0, KT, 2 * NK, KT, 0, KT, NK, KT, 1>;
 };
-template <int NK>
+template <int NK, int QT>
 struct DqSteps {
   template <int ST>
-  using P = StepPlan<NK, 4, NK, 4, NK, 4, 0, 1, 1>;
+  using P = StepPlan<NK, QT, NK, QT, NK, QT, 0, 1, 1>;
   template <int ST>
-  using Flush = StepPlan<0, 4, 2 * NK, 4, 0, 4, 0, 1, 1>;
+  using Flush = StepPlan<0, QT, 2 * NK, QT, 0, QT, 0, 1, 1>;
+};
+
+// Resident rows per wave and LDS buffers per head dim: 64 rows (four 16-row
+// tiles) and triple-buffered streamed tiles up to d = 128; at d = 256 the
+// resident operands and accumulators of 64 rows exceed the 512 registers of a
+// lane and three buffers the 160 KB of LDS, so a wave keeps 32 rows and the
+// streamed tiles are double-buffered.
+template <int D>
+struct TileShape {
+  static constexpr int RT = D > 128 ? 2 : 4;    // resident 16-row tiles per wave
+  static constexpr int NBUF = D > 128 ? 2 : 3;  // LDS buffers of the streamed tiles
 };
 
 // Slots of the non-MFMA work of dK/dV step ST (NC copies in steps 2-3):
@@ -65,18 +76,18 @@ struct DqSteps {
 // Fixed: the deferred packs (even ST: P_st after the dV half's last read of the
 // previous pair, slots NM-4+kt; odd ST: dS_{st-1} after the dK half's, slots
 // B2-4+kt), the next step's LSE and -D reads, the mid-tile wait.
-template <int NK, int ST, int LA, int NC>
+template <int NK, int KT, int ST, int LA, int NC>
 struct DkdvPlace {
-  using Plan = typename DkdvSteps<NK>::template P<ST>;
+  using Plan = typename DkdvSteps<NK, KT>::template P<ST>;
   static constexpr int NM = Plan::NM;
-  int exp[4][4], pack_p[4], mul[4][4], pack_ds[4], copy[NC];
+  int exp[KT][4], pack_p[KT], mul[KT][4], pack_ds[KT], copy[NC];
   constexpr DkdvPlace() : exp(), pack_p(), mul(), pack_ds(), copy() {
     SlotLoad<NM> L;
     L.template reads<Plan, LA>();
     L.load[NM - 1] += 2 * issue::kRow + (ST == 1 ? 2 : 0);
-    for (int kt = 0; kt < 4; ++kt) {
-      if (ST % 2 == 0) L.load[NM - 4 + kt] += issue::kPack;
-      else L.load[Plan::B2 - 4 + kt] += issue::kPack;
+    for (int kt = 0; kt < KT; ++kt) {
+      if (ST % 2 == 0) L.load[NM - KT + kt] += issue::kPack;
+      else L.load[Plan::B2 - KT + kt] += issue::kPack;
     }
     const int c0 = ST == 2 ? 0 : (NC + 1) / 2, c1 = ST == 2 ? (NC + 1) / 2 : NC;
     for (int c = 0; c < NC; ++c) copy[c] = -1;
@@ -86,14 +97,14 @@ struct DkdvPlace {
       for (int c = c0; c < c1; ++c) prev = copy[c] = L.put(issue::kCopy, prev, Plan::B1 - 1);
     }
     int prev = Plan::B1;
-    L.level(16 * issue::kExp + (ST % 2) * 4 * issue::kPack, Plan::B1, Plan::B3 - 2);
-    for (int kt = 0; kt < 4; ++kt) {
+    L.level(4 * KT * issue::kExp + (ST % 2) * KT * issue::kPack, Plan::B1, Plan::B3 - 2);
+    for (int kt = 0; kt < KT; ++kt) {
       for (int i = 0; i < 4; ++i) prev = exp[kt][i] = L.put(issue::kExp, prev, Plan::B3 - 2);
       pack_p[kt] = ST % 2 == 1 ? (prev = L.put(issue::kPack, prev, Plan::B3 - 2)) : -1;
     }
     prev = Plan::B3;
-    L.level(16 * issue::kMul + (ST % 2) * 4 * issue::kPack, Plan::B3, NM - 1);
-    for (int kt = 0; kt < 4; ++kt) {
+    L.level(4 * KT * issue::kMul + (ST % 2) * KT * issue::kPack, Plan::B3, NM - 1);
+    for (int kt = 0; kt < KT; ++kt) {
       for (int i = 0; i < 4; ++i) prev = mul[kt][i] = L.put(issue::kMul, prev, NM - 1);
       pack_ds[kt] = ST % 2 == 1 ? (prev = L.put(issue::kPack, prev, NM - 1)) : -1;
     }
@@ -103,46 +114,56 @@ struct DkdvPlace {
 // Slots of the non-MFMA work of dQ step ST (NC copies in steps 2-3):
 //   mul[t][i], pack[t] (dS of the previous sub-block; the packs at least two slots
 //   before the dQ half, which may read them), exp[t][i] (P_st), copy[c].
-template <int NK, int ST, int LA, int NC>
+// EARLY: the copies go under the S^T MFMAs of steps 2-3 (double buffering waits
+// for them before the last operand reads of the tile, which read the next tile).
+template <int NK, int QT, int ST, int LA, int NC, bool EARLY>
 struct DqPlace {
-  using Plan = typename DqSteps<NK>::template P<ST>;
+  using Plan = typename DqSteps<NK, QT>::template P<ST>;
   static constexpr int NM = Plan::NM;
-  int mul[4][4], pack[4], exp[4][4], copy[NC];
+  int mul[QT][4], pack[QT], exp[QT][4], copy[NC];
   constexpr DqPlace() : mul(), pack(), exp(), copy() {
     SlotLoad<NM> L;
     L.template reads<Plan, LA>();
     if (ST == 1) L.load[NM - 1] += 2;
     int prev = 0;
-    L.level(16 * issue::kMul + 4 * issue::kPack, 0, Plan::B1 - 2);
-    for (int t = 0; t < 4; ++t) {
+    L.level(4 * QT * issue::kMul + QT * issue::kPack, 0, Plan::B1 - 2);
+    for (int t = 0; t < QT; ++t) {
       for (int i = 0; i < 4; ++i) prev = mul[t][i] = L.put(issue::kMul, prev, Plan::B1 - 2);
       prev = pack[t] = L.put(issue::kPack, prev, Plan::B1 - 2);
     }
     prev = Plan::B1;
-    L.level(16 * issue::kExp, Plan::B1, NM - 1);
-    for (int t = 0; t < 4; ++t)
+    L.level(4 * QT * issue::kExp, Plan::B1, NM - 1);
+    for (int t = 0; t < QT; ++t)
       for (int i = 0; i < 4; ++i) prev = exp[t][i] = L.put(issue::kExp, prev, NM - 1);
     const int c0 = ST == 2 ? 0 : (NC + 1) / 2, c1 = ST == 2 ? (NC + 1) / 2 : NC;
     for (int c = 0; c < NC; ++c) copy[c] = -1;
     if (ST >= 2) {
+      const int hi = EARLY ? Plan::B1 - 1 : NM - 1;
       prev = 0;
-      L.level((c1 - c0) * issue::kCopy, 0, NM - 1);
-      for (int c = c0; c < c1; ++c) prev = copy[c] = L.put(issue::kCopy, prev, NM - 1);
+      L.level((c1 - c0) * issue::kCopy, 0, hi);
+      for (int c = c0; c < c1; ++c) prev = copy[c] = L.put(issue::kCopy, prev, hi);
     }
   }
 };
 
 // ---------------------------------------------------------------------------
-// Row preprocess.  D/8 lanes share a row; each lane reads 16 bytes of O and dO.
+// Row preprocess.  A row is handled by LPR lanes (D/8 rounded up to a power of
+// two); lane `part` < D/8 reads 16 bytes of O and dO, the others add nothing.
+template <int D>
+constexpr int pre_lanes_per_row() {
+  int n = 1;
+  while (n < D / 8) n *= 2;
+  return n;
+}
 template <int DT, int D, bool ZERO_DQ>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
-  constexpr int LPR = D / 8;
+  constexpr int LPR = pre_lanes_per_row<D>();
   constexpr int RPB = 256 / LPR;
   const size_t row = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
   const int part = threadIdx.x % LPR;
   if (blockIdx.x == 0 && threadIdx.x < 32 && p.sched) p.sched[threadIdx.x] = 0;
   float s = 0.f;
-  if (row < p.rows) {
+  if (row < p.rows && part < D / 8) {
     const u32x4 a = ld16(p.o + row * D + part * 8);
     const u32x4 c = ld16(p.dout + row * D + part * 8);
 #pragma unroll
@@ -193,16 +214,17 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // ragged end of this wave's block take a masked variant of the softmax.
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int KW = 64, BN = 4 * KW, BM = 64, NSB = BM / 16;
+  constexpr int KT = TileShape<D>::RT;  // key tiles of 16 per wave
+  constexpr int KW = 16 * KT, BN = 4 * KW, BM = 64, NSB = BM / 16;
   constexpr int NK = D / 32;
-  constexpr int NBUF = 3;
+  constexpr int NBUF = TileShape<D>::NBUF;
   constexpr int RS = PadTile<D>::RS;
   constexpr int OPS = 2 * BM * PadTile<D>::GR / 256 + 2;  // copy instructions per fetch per wave
   constexpr int LA = 2;                                     // operand lookahead
   // Q and dO of a buffer are one padded tile pair (as are LSE and D), so both are
   // read through the same per-lane address registers with immediate offsets.
   __shared__ __attribute__((aligned(16))) uint16_t sQdO[NBUF][2 * BM * RS];
-  static_assert(NBUF * 2 * BM * RS >= 4 * 64 * (D + 8), "the output staging must fit the tile buffers");
+  static_assert(NBUF * 2 * BM * RS >= 4 * KW * (D + 8), "the output staging must fit the tile buffers");
   __shared__ __attribute__((aligned(16))) float sLD[NBUF][2][BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -222,12 +244,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const int kvw = kv0 + KW * w;
     const size_t kbase = ((size_t)b * p.Hkv + hk) * (size_t)p.Nkv;
 
-    u32x4 kb[4][NK], vb[4][NK];
+    u32x4 kb[KT][NK], vb[KT][NK];
     {
       const uint16_t* __restrict__ K = p.k + kbase * D;
       const uint16_t* __restrict__ V = p.v + kbase * D;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < KT; ++kt) {
         const int key = kvw + 16 * kt + l16;
 #pragma unroll
         for (int s = 0; s < NK; ++s) {
@@ -236,9 +258,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         }
       }
     }
-    f32x4 dk[4][2 * NK], dv[4][2 * NK];  // per key tile and 16-column head-dim tile
+    f32x4 dk[KT][2 * NK], dv[KT][2 * NK];  // per key tile and 16-column head-dim tile
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
       for (int n = 0; n < 2 * NK; ++n) {
         dk[kt][n] = zero4();
@@ -328,30 +350,51 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     // first half of a pair is packed only once the previous pair's tuple has been
     // read for the last time, so the two pairs can share registers.
     u32x4 carry[LA];
-    u32x4 pa[2][4], sa[2][4];
+    u32x4 pa[2][KT], sa[2][KT];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       pa[1][kt] = zero_u4();
       sa[1][kt] = zero_u4();
     }
     int prev = 0;  // buffer of the previous tile
 
+    // Operand o of step st of a tile in buffer Q_ (Q, then dO) whose previous tile
+    // is in buffer Qp_ (the operand order of DkdvSteps; see compute below).
+    auto dkdv_operand = [&](auto stc, auto oc, const uint16_t* Q_, const uint16_t* Qp_) -> u32x4 {
+      constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
+      using Plan = typename DkdvSteps<NK, KT>::template P<st>;
+      constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
+      const uint16_t* dO_ = Q_ + BM * RS;
+      const uint16_t* dOp_ = Qp_ + BM * RS;
+      if constexpr (k == 0) {
+        return pad_row16<D>(Q_, 16 * st + l16, 4 * n + j4);
+      } else if constexpr (k == 1) {
+        constexpr int J = st < 2 ? 1 : 0, nn = (st % 2) * NK + n;
+        const int k0 = 32 * J + 4 * j4;
+        return pad_tr_operand<D>(st < 2 ? Qp_ : Q_, k0, k0 + 16, 16 * nn);
+      } else if constexpr (k == 2) {
+        return pad_row16<D>(dO_, 16 * st + l16, 4 * n + j4);
+      } else {
+        constexpr int J = (st == 0 || st == 3) ? 1 : 0, nn = ((st + 1) % 2) * NK + n;
+        const int k0 = 32 * J + 4 * j4;
+        return pad_tr_operand<D>(st == 0 ? dOp_ : dO_, k0, k0 + 16, 16 * nn);
+      }
+    };
+
     auto compute = [&](int cur, int nxt, auto mask_c, int q0, const Src& fsrc, int fbuf) {
       constexpr bool MASK = decltype(mask_c)::value;
       const uint16_t* Qt = sQdO[cur];
-      const uint16_t* dOt = Qt + BM * RS;
       const uint16_t* Qp = sQdO[prev];
-      const uint16_t* dOp = Qp + BM * RS;
       const uint16_t* Qn = sQdO[nxt];
       const float* Lt = sLD[cur][0];
       const float* Dtl = Lt + BM;
-      f32x4 sc[4];    // S, then P, of the current sub-block, per key tile
-      f32x4 dp[4];    // dP, then dS
+      f32x4 sc[KT];   // S, then P, of the current sub-block, per key tile
+      f32x4 dp[KT];   // dP, then dS
       f32x4 lq, dn;   // LSE*log2e and -D of the current sub-block's rows
       const int keyl = kvw + l16;    // key of this lane's column in key tile 0
       const int qrow = q0 + 4 * j4;  // query row of element 0 in sub-block 0
 
-      using Steps = DkdvSteps<NK>;
+      using Steps = DkdvSteps<NK, KT>;
       // packed sub-block st into half st % 2 of pair st / 2
       auto pack_p = [&](auto stc, auto ktc) {
         constexpr int st = decltype(stc)::value, kt = decltype(ktc)::value;
@@ -365,7 +408,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         sa[st / 2][kt][2 * (st % 2)] = v[0];
         sa[st / 2][kt][2 * (st % 2) + 1] = v[1];
       };
-      // P_st item e of 16 (key tile e / 4, row e % 4)
+      // P_st item e of 4 KT (key tile e / 4, row e % 4)
       auto p_item = [&](auto ec, auto st_c) {
         constexpr int e = decltype(ec)::value, st = decltype(st_c)::value;
         constexpr int kt = e / 4, i = e % 4;
@@ -383,8 +426,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         dn = *reinterpret_cast<const f32x4*>(&Dtl[16 * st + 4 * j4]);
         if constexpr (st == 2) {
           // Mid-tile: every wave is past steps 0-1 (its last reads of the previous
-          // buffer) and, once its own copies have landed, the next tile is complete,
-          // so the copies of steps 2-3 may refill the previous buffer.
+          // buffer) and, once its own copies have landed, the next tile is complete
+          // (triple buffering), so the copies of steps 2-3 may refill the previous
+          // buffer.
           wait_vmem();
           tile_barrier();
         }
@@ -394,30 +438,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       // (st + 1) % 2 of the dV product of pair 0 (steps 1-2) or pair 1 (step 3, and
       // of the previous tile in step 0).
       auto operand = [&](auto stc, auto oc) -> u32x4 {
-        constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
-        using Plan = typename Steps::template P<st>;
-        constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
-        if constexpr (k == 0) {
-          return pad_row16<D>(Qt, 16 * st + l16, 4 * n + j4);
-        } else if constexpr (k == 1) {
-          constexpr int J = st < 2 ? 1 : 0, nn = (st % 2) * NK + n;
-          const int k0 = 32 * J + 4 * j4;
-          return pad_tr_operand<D>(st < 2 ? Qp : Qt, k0, k0 + 16, 16 * nn);
-        } else if constexpr (k == 2) {
-          return pad_row16<D>(dOt, 16 * st + l16, 4 * n + j4);
-        } else {
-          constexpr int J = (st == 0 || st == 3) ? 1 : 0, nn = ((st + 1) % 2) * NK + n;
-          const int k0 = 32 * J + 4 * j4;
-          return pad_tr_operand<D>(st == 0 ? dOp : dOt, k0, k0 + 16, 16 * nn);
-        }
+        return dkdv_operand(stc, oc, Qt, Qp);
       };
-      auto next = [&](auto oc) -> u32x4 {  // operand oc of the next tile: S of sub-block 0
-        return pad_row16<D>(Qn, l16, 4 * decltype(oc)::value + j4);
+      // operand oc of the next tile, whose previous buffer is this one
+      auto next = [&](auto oc) -> u32x4 {
+        if constexpr (NBUF == 2 && decltype(oc)::value == 0) {
+          // double buffering: the next tile was copied in this tile's second half
+          wait_vmem();
+          tile_barrier();
+        }
+        return dkdv_operand(std::integral_constant<int, 0>(), oc, Qn, Qt);
       };
       auto mfma = [&](auto stc, auto mc, const u32x4& op) {
         constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
         using Plan = typename Steps::template P<st>;
-        constexpr int k = Plan::stage(m), loc = Plan::local(m), o = loc / 4, kt = loc % 4;
+        constexpr int k = Plan::stage(m), loc = Plan::local(m), o = loc / KT, kt = loc % KT;
         if constexpr (k == 0) {
           if constexpr (o == 0)
             sc[kt] = Mx<DT>::first16(op, kb[kt][o]);
@@ -440,7 +475,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         constexpr int st = decltype(stc)::value, m = decltype(mc)::value;
         using Plan = typename Steps::template P<st>;
         using stp = std::integral_constant<int, st>;
-        constexpr DkdvPlace<NK, st, LA, OPS> PL{};
+        constexpr DkdvPlace<NK, KT, st, LA, OPS> PL{};
         (void)gc;
         // The copies of a later tile, in steps 2-3 (after the mid-tile barrier).
         static_for<OPS>([&](auto cc) {
@@ -448,7 +483,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         });
         // P_st under the dK half and dP_st: four exponentials per key tile, then
         // (odd st) the packed tile, before the dV half reads it
-        static_for<4>([&](auto ktc) {
+        static_for<KT>([&](auto ktc) {
           constexpr int kt = decltype(ktc)::value;
           static_for<4>([&](auto ic) {
             if constexpr (PL.exp[kt][decltype(ic)::value] == m)
@@ -457,7 +492,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           if constexpr (PL.pack_p[kt] == m) pack_p(stp(), ktc);
         });
         // dS_st under the dV half; odd st packs it at once
-        static_for<4>([&](auto ktc) {
+        static_for<KT>([&](auto ktc) {
           constexpr int kt = decltype(ktc)::value;
           static_for<4>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
@@ -468,10 +503,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         // even st: P_st is packed into a new pair once the dV half of this step has
         // read key tile kt of the previous pair for the last time, and dS_{st-1}
         // once the dK half has done the same
-        if constexpr (st % 2 == 0 && m >= Plan::NM - 4)
-          pack_p(stp(), std::integral_constant<int, m - (Plan::NM - 4)>());
-        if constexpr (st % 2 == 1 && m >= Plan::B2 - 4 && m < Plan::B2)
-          pack_ds(std::integral_constant<int, st - 1>(), std::integral_constant<int, m - (Plan::B2 - 4)>());
+        if constexpr (st % 2 == 0 && m >= Plan::NM - KT)
+          pack_p(stp(), std::integral_constant<int, m - (Plan::NM - KT)>());
+        if constexpr (st % 2 == 1 && m >= Plan::B2 - KT && m < Plan::B2)
+          pack_ds(std::integral_constant<int, st - 1>(), std::integral_constant<int, m - (Plan::B2 - KT)>());
       };
       run_tile_carry<Steps::template P, NSB, LA>(carry, begin, operand, next, mfma, valu);
     };
@@ -481,7 +516,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     auto flush = [&]() {
       const uint16_t* Qp = sQdO[prev];
       const uint16_t* dOp = Qp + BM * RS;
-      using Steps = DkdvSteps<NK>;
+      using Steps = DkdvSteps<NK, KT>;
       using Plan = typename Steps::template Flush<0>;
       run_tile<Steps::template Flush, 1, LA>(
           [&](auto) {},
@@ -493,7 +528,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           },
           [&](auto, auto mc, const u32x4& op) {
             constexpr int m = decltype(mc)::value, k = Plan::stage(m), loc = Plan::local(m);
-            constexpr int o = loc / 4, kt = loc % 4;
+            constexpr int o = loc / KT, kt = loc % KT;
             if constexpr (k == 1)
               Mx<DT>::acc16a(dk[kt][o], sa[1][kt], op);
             else
@@ -534,8 +569,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     // its own (which would count the copies wrongly) into the loop.
     wait_vmem();
     lds_barrier();
+    // the first tile's leading operands (its "previous" buffer is the same one; the
+    // previous-pair products it feeds are multiplied by zeros)
     static_for<LA>([&](auto oc) {
-      carry[decltype(oc)::value] = pad_row16<D>(sQdO[0], l16, 4 * decltype(oc)::value + j4);
+      carry[decltype(oc)::value] = dkdv_operand(std::integral_constant<int, 0>(), oc, sQdO[0], sQdO[0]);
     });
     // Iteration it works on buffer it % NBUF; from its middle on it copies tile
     // it + NBUF - 1 into the buffer of iteration it - 1.
@@ -552,6 +589,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           wait_vmem();
           tile_barrier();
           copy_all(fsrc, fbuf);
+          if constexpr (NBUF == 2) {  // the second barrier a computed tile has
+            wait_vmem();
+            tile_barrier();
+          }
         }
         if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), q0, fsrc, fbuf);
         if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), q0, fsrc, fbuf);
@@ -572,9 +613,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     if (tid == 0) ticket = wq.next_ticket(ticket);
     settle(dk);
     settle(dv);
-    uint16_t* stage = &sQdO[0][0] + w * 64 * (D + 8);
-    store_block64_c16<DT, D>(dk, p.scale, stage, p.dk + kbase * D, kvw, p.Nkv, lane);
-    store_block64_c16<DT, D>(dv, 1.f, stage, p.dv + kbase * D, kvw, p.Nkv, lane);
+    uint16_t* stage = &sQdO[0][0] + w * KW * (D + 8);
+    store_block_c16<DT, D, KT>(dk, p.scale, stage, p.dk + kbase * D, kvw, p.Nkv, lane);
+    store_block_c16<DT, D, KT>(dv, 1.f, stage, p.dv + kbase * D, kvw, p.Nkv, lane);
   }
 }
 
@@ -598,14 +639,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 // computed under S^T_st and P_st under the dQ half and dP^T_st.
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
-  constexpr int QW = 64, BM = 4 * QW, BN = 64, NSB = BN / 16;
+  constexpr int QT = TileShape<D>::RT;  // query tiles of 16 per wave
+  constexpr int QW = 16 * QT, BM = 4 * QW, BN = 64, NSB = BN / 16;
   constexpr int NK = D / 32;
-  constexpr int NBUF = 3;                   // key/value tiles fetched two ahead
+  constexpr int NBUF = TileShape<D>::NBUF;  // key/value tiles fetched NBUF - 1 ahead
   constexpr int RS = PadTile<D>::RS;
   constexpr int OPS = 2 * BN * PadTile<D>::GR / 256;  // copy instructions per fetch per wave
   constexpr int LA = 2;
   __shared__ __attribute__((aligned(16))) uint16_t sKV[NBUF][2 * BN * RS];  // K, V: a padded pair
-  static_assert(NBUF * 2 * BN * RS >= 4 * 64 * (D + 8), "the output staging must fit the tile buffers");
+  static_assert(NBUF * 2 * BN * RS >= 4 * QW * (D + 8), "the output staging must fit the tile buffers");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
@@ -630,11 +672,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     const uint16_t* __restrict__ K = p.k + kbase * D;
     const uint16_t* __restrict__ V = p.v + kbase * D;
 
-    u32x4 qb[4][NK], db[4][NK];
-    float lq[4];
-    f32x4 nd[4];  // -D of the lane's query, in every element: where dP^T starts
+    u32x4 qb[QT][NK], db[QT][NK];
+    float lq[QT];
+    f32x4 nd[QT];  // -D of the lane's query, in every element: where dP^T starts
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < QT; ++t) {
       const int q = qw + 16 * t + l16;
       const bool ok = q < p.Nq;
 #pragma unroll
@@ -649,9 +691,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       nd[t][2] = x;
       nd[t][3] = x;
     }
-    f32x4 acc[4][2 * NK];  // dQ, per query tile and 16-column head-dim tile
+    f32x4 acc[QT][2 * NK];  // dQ, per query tile and 16-column head-dim tile
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < QT; ++t) {
 #pragma unroll
       for (int n = 0; n < 2 * NK; ++n) acc[t][n] = zero4();
     }
@@ -694,27 +736,46 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     // runs in steps 0-1 of the next tile with K read from the previous buffer (zero
     // before the first tile, which makes that product a no-op).
     u32x4 carry[LA];
-    f32x4 sc[2][4];  // S^T, then P^T, of sub-block st in sc[st % 2], per query tile
-    f32x4 dp[4];     // dP^T, then dS^T, of the sub-block being finished
-    u32x4 da[2][4];  // dS A operands of sub-block pair J, per query tile
+    f32x4 sc[2][QT];  // S^T, then P^T, of sub-block st in sc[st % 2], per query tile
+    f32x4 dp[QT];     // dP^T, then dS^T, of the sub-block being finished
+    u32x4 da[2][QT];  // dS A operands of sub-block pair J, per query tile
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < QT; ++t) {
       sc[1][t] = zero4();
       dp[t] = zero4();
       da[1][t] = zero_u4();
     }
     int prev = 0;  // buffer of the previous tile
 
+    // Operand o of step st of a tile in buffer K_ (K, then V) whose previous tile is
+    // in buffer Kp_ (the operand order of DqSteps).  Stage 1: half st % 2 of the dQ
+    // product of pair 1 of the previous tile (steps 0-1) or pair 0 of this one
+    // (steps 2-3): keys 4 j4 .. + 3 of both sub-blocks of the pair, head-dim tile
+    // (st % 2) NK + n.
+    auto dq_operand = [&](auto stc, auto oc, const uint16_t* K_, const uint16_t* Kp_) -> u32x4 {
+      constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
+      using Plan = typename DqSteps<NK, QT>::template P<st>;
+      constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
+      if constexpr (k == 0) {
+        return pad_row16<D>(K_, 16 * st + l16, 4 * n + j4);
+      } else if constexpr (k == 1) {
+        constexpr int J = st < 2 ? 1 : 0, nn = (st % 2) * NK + n;
+        const int k0 = 32 * J + 4 * j4;
+        return pad_tr_operand<D>(st < 2 ? Kp_ : K_, k0, k0 + 16, 16 * nn);
+      } else {
+        return pad_row16<D>(K_ + BN * RS, 16 * st + l16, 4 * n + j4);
+      }
+    };
+
     auto compute = [&](int cur, int nxt, auto mask_c, int kv0, const i32x4& fsrc, int fbuf) {
       constexpr bool MASK = decltype(mask_c)::value;
       const uint16_t* Kt = sKV[cur];
-      const uint16_t* Vt = Kt + BN * RS;
       const uint16_t* Kp = sKV[prev];
       const uint16_t* Kn = sKV[nxt];
       const int krow = kv0 + 4 * j4;  // key of element 0 in sub-block 0
       const int qcol = qw + l16;      // query of this lane's column in query tile 0
 
-      // dS of sub-block sb (kept in sc[cp], dp), item e of 20: per query tile four
+      // dS of sub-block sb (kept in sc[cp], dp), item e of 5 QT: per query tile four
       // products, then the packed tile into its half of the pair's A operand
       auto ds_item = [&](auto ec, auto cp_c, auto sb_c) {
         constexpr int e = decltype(ec)::value, cp = decltype(cp_c)::value, sb = decltype(sb_c)::value;
@@ -738,52 +799,43 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         sc[cs][t][i] = fast_exp2(v);
       };
 
-      using Steps = DqSteps<NK>;
+      using Steps = DqSteps<NK, QT>;
       auto begin = [&](auto stc) {
         constexpr int st = decltype(stc)::value;
         if constexpr (st == 2) {
           // Mid-tile: every wave is past step 0 (its last reads of the previous
-          // buffer) and, once its own copies have landed, the next tile is complete,
-          // so the copies of steps 2-3 may refill the previous buffer.
+          // buffer) and, once its own copies have landed, the next tile is complete
+          // (triple buffering), so the copies of steps 2-3 may refill the previous
+          // buffer.
           wait_vmem();
           tile_barrier();
         }
       };
-      auto operand = [&](auto stc, auto oc) -> u32x4 {
-        constexpr int st = decltype(stc)::value, o = decltype(oc)::value;
-        using Plan = typename Steps::template P<st>;
-        constexpr int k = Plan::op_stage(o), n = Plan::op_local(o);
-        if constexpr (k == 0) {
-          return pad_row16<D>(Kt, 16 * st + l16, 4 * n + j4);
-        } else if constexpr (k == 1) {
-          // half st % 2 of the dQ product of pair 1 of the previous tile (steps
-          // 0-1) or pair 0 of this one (steps 2-3): keys 4 j4 .. + 3 of both
-          // sub-blocks of the pair, head-dim tile (st % 2) NK + n
-          constexpr int J = st < 2 ? 1 : 0, nn = (st % 2) * NK + n;
-          const int k0 = 32 * J + 4 * j4;
-          return pad_tr_operand<D>(st < 2 ? Kp : Kt, k0, k0 + 16, 16 * nn);
-        } else {
-          return pad_row16<D>(Vt, 16 * st + l16, 4 * n + j4);
+      auto operand = [&](auto stc, auto oc) -> u32x4 { return dq_operand(stc, oc, Kt, Kp); };
+      // operand oc of the next tile, whose previous buffer is this one
+      auto next = [&](auto oc) -> u32x4 {
+        if constexpr (NBUF == 2 && decltype(oc)::value == 0) {
+          // double buffering: the next tile was copied in this tile's second half
+          wait_vmem();
+          tile_barrier();
         }
-      };
-      auto next = [&](auto oc) -> u32x4 {  // operand oc of the next tile: S^T of sub-block 0
-        return pad_row16<D>(Kn, l16, 4 * decltype(oc)::value + j4);
+        return dq_operand(std::integral_constant<int, 0>(), oc, Kn, Kt);
       };
       auto mfma = [&](auto stc, auto mc, const u32x4& op) {
         constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cs = st & 1;
         using Plan = typename Steps::template P<st>;
         constexpr int k = Plan::stage(m), loc = Plan::local(m);
         if constexpr (k == 0) {
-          constexpr int s = loc / 4, t = loc % 4;
+          constexpr int s = loc / QT, t = loc % QT;
           if constexpr (s == 0)
             sc[cs][t] = Mx<DT>::first16(op, qb[t][s]);
           else
             Mx<DT>::acc16(sc[cs][t], op, qb[t][s]);
         } else if constexpr (k == 1) {
-          constexpr int J = st < 2 ? 1 : 0, t = loc % 4, nn = (st % 2) * NK + loc / 4;
+          constexpr int J = st < 2 ? 1 : 0, t = loc % QT, nn = (st % 2) * NK + loc / QT;
           Mx<DT>::acc16a(acc[t][nn], da[J][t], op);
         } else {
-          constexpr int s = loc / 4, t = loc % 4;
+          constexpr int s = loc / QT, t = loc % QT;
           if constexpr (s == 0)
             dp[t] = Mx<DT>::first16c(op, db[t][s], nd[t]);
           else
@@ -792,19 +844,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       };
       auto valu = [&](auto stc, auto mc, auto gc) {
         constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cp = (st + 1) & 1;
-        constexpr DqPlace<NK, st, LA, OPS> PL{};
+        constexpr DqPlace<NK, QT, st, LA, OPS, NBUF == 2> PL{};
         (void)gc;
         // the copies of a later tile, in steps 2-3 (after the mid-tile barrier)
         static_for<OPS>([&](auto cc) {
           if constexpr (PL.copy[decltype(cc)::value] == m) copy_part(cc, fsrc, fbuf);
         });
         // dS of the previous sub-block (of the previous tile in step 0) under S^T_st
-        static_for<20>([&](auto ec) {
+        static_for<5 * QT>([&](auto ec) {
           constexpr int e = decltype(ec)::value, t = e / 5, i = e % 5;
           if constexpr ((i < 4 ? PL.mul[t][i % 4] : PL.pack[t]) == m)
             ds_item(ec, std::integral_constant<int, cp>(), std::integral_constant<int, (st + NSB - 1) % NSB>());
         });
-        static_for<16>([&](auto ec) {
+        static_for<4 * QT>([&](auto ec) {
           constexpr int e = decltype(ec)::value;
           if constexpr (PL.exp[e / 4][e % 4] == m) p_item(ec, stc);
         });
@@ -816,7 +868,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     // even copied, as the buffers then hold no data).
     auto flush = [&]() {
       const uint16_t* Kp = sKV[prev];
-      static_for<20>([&](auto ec) {
+      static_for<5 * QT>([&](auto ec) {
         constexpr int e = decltype(ec)::value, t = e / 5, i = e % 5;
         if constexpr (i == 4) {
           const u32x2 v = pack_c4<DT>(dp[t]);
@@ -826,7 +878,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
           dp[t][i] = sc[1][t][i] * dp[t][i];
         }
       });
-      using Steps = DqSteps<NK>;
+      using Steps = DqSteps<NK, QT>;
       run_tile<Steps::template Flush, 1, LA>(
           [&](auto) {},
           [&](auto, auto oc) -> u32x4 {
@@ -835,7 +887,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
             return pad_tr_operand<D>(Kp, k0, k0 + 16, 16 * n);
           },
           [&](auto, auto mc, const u32x4& op) {
-            constexpr int loc = decltype(mc)::value, t = loc % 4, n = loc / 4;
+            constexpr int loc = decltype(mc)::value, t = loc % QT, n = loc / QT;
             Mx<DT>::acc16a(acc[t][n], da[1][t], op);
           },
           [&](auto, auto, auto) {});
@@ -860,8 +912,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     // its own (which would count the copies wrongly) into the loop.
     wait_vmem();
     lds_barrier();
+    // the first tile's leading operands (its "previous" buffer is the same one; the
+    // previous-pair product it feeds is multiplied by zeros)
     static_for<LA>([&](auto oc) {
-      carry[decltype(oc)::value] = pad_row16<D>(sKV[0], l16, 4 * decltype(oc)::value + j4);
+      carry[decltype(oc)::value] = dq_operand(std::integral_constant<int, 0>(), oc, sKV[0], sKV[0]);
     });
     // Iteration kt works on buffer kt % NBUF; from its middle on it copies tile
     // kt + NBUF - 1 into the buffer of iteration kt - 1.
@@ -876,6 +930,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
           wait_vmem();
           tile_barrier();
           copy_all(kt + NBUF - 1, fbuf);
+          if constexpr (NBUF == 2) {  // the second barrier a computed tile has
+            wait_vmem();
+            tile_barrier();
+          }
         }
         if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), kt * BN, fsrc, fbuf);
         if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), kt * BN, fsrc, fbuf);
@@ -892,8 +950,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     // the next item, claimed after the last wait for memory (see the dK/dV kernel)
     if (tid == 0) ticket = wq.next_ticket(ticket);
     settle(acc);
-    uint16_t* stage = &sKV[0][0] + w * 64 * (D + 8);
-    store_block64_c16<DT, D>(acc, p.scale, stage, p.dq + qbase * D, qw, p.Nq, lane);
+    uint16_t* stage = &sKV[0][0] + w * QW * (D + 8);
+    store_block_c16<DT, D, QT>(acc, p.scale, stage, p.dq + qbase * D, qw, p.Nq, lane);
   }
 }
 
@@ -903,7 +961,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 template <int DT, int D, bool CAUSAL>
 hipError_t run_pre(const BwdArgs& a, bool zero, hipStream_t s) {
   const BwdParams p = make_params(a);
-  constexpr int RPB = 256 / (D / 8);
+  constexpr int RPB = 256 / pre_lanes_per_row<D>();
   const dim3 grid((unsigned)((p.rows + RPB - 1) / RPB));
   if (zero)
     hipLaunchKernelGGL((bwd_pre_kernel<DT, D, true>), grid, dim3(256), 0, s, p);
@@ -915,7 +973,8 @@ hipError_t run_pre(const BwdArgs& a, bool zero, hipStream_t s) {
 template <int DT, int D, bool CAUSAL>
 hipError_t run_dkdv(const BwdArgs& a, hipStream_t s) {
   BwdParams p = make_params(a);
-  const int items = ((a.pb.Nkv + 255) / 256) * a.pb.Hkv * a.pb.B;
+  constexpr int BN = 4 * 16 * TileShape<D>::RT;  // keys per work item
+  const int items = ((a.pb.Nkv + BN - 1) / BN) * a.pb.Hkv * a.pb.B;
   const int ncu = device_cu_count();
   const dim3 grid((unsigned)(p.sched && ncu > 0 && ncu < items ? ncu : items));
   hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
@@ -925,7 +984,8 @@ hipError_t run_dkdv(const BwdArgs& a, hipStream_t s) {
 template <int DT, int D, bool CAUSAL>
 hipError_t run_dq(const BwdArgs& a, hipStream_t s) {
   BwdParams p = make_params(a);
-  const int items = ((a.pb.Nq + 255) / 256) * a.pb.Hq * a.pb.B;
+  constexpr int BM = 4 * 16 * TileShape<D>::RT;  // queries per work item
+  const int items = ((a.pb.Nq + BM - 1) / BM) * a.pb.Hq * a.pb.B;
   const int ncu = device_cu_count();
   const dim3 grid((unsigned)(p.sched && ncu > 0 && ncu < items ? ncu : items));
   hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);

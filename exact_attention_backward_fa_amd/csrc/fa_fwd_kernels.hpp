@@ -57,61 +57,78 @@ struct FwdParams {
 template <int DT>
 constexpr float fwd_headroom() { return DT == 0 ? 15.f : 64.f; }
 
-// Step J: S^T of pair J (2 NK operands x 4 query tiles) | P V of the previous pair
-// (2 NK head-dim tiles x 4).
-template <int NK>
+// Step J: S^T of pair J (2 NK operands x QT query tiles) | P V of the previous pair
+// (2 NK head-dim tiles x QT).
+template <int NK, int QT>
 struct FwdSteps {
   template <int ST>
-  using P = StepPlan<2 * NK, 4, 2 * NK, 4, 0, 1, 0, 1, 1>;
+  using P = StepPlan<2 * NK, QT, 2 * NK, QT, 0, 1, 0, 1, 1>;
   template <int ST>
-  using Flush = StepPlan<0, 4, 2 * NK, 4, 0, 1, 0, 1, 1>;
+  using Flush = StepPlan<0, QT, 2 * NK, QT, 0, 1, 0, 1, 1>;
+};
+
+// Resident query rows per wave and LDS buffers per head dim: 64 queries (four
+// 16-row tiles) and triple-buffered key/value tiles up to d = 128; at d = 256 a
+// wave keeps 32 queries (Q and the O accumulators of 64 would not fit its
+// registers) and the tiles are double-buffered (three would not fit the LDS).
+template <int D>
+struct FwdShape {
+  static constexpr int QT = D > 128 ? 2 : 4;
+  static constexpr int NBUF = D > 128 ? 2 : 3;
 };
 
 // Slots of the non-MFMA work of forward step ST (NC copies in step 1): mx[t] (the
 // pair's maxima), check (the test for a raised reference), exp[sb][t][i],
 // pack[sb][t] and sum[sb][t] (the tile's P into the row sums).
-template <int NK, int ST, int LA, int NC>
+// EARLY: the copies go under the S^T MFMAs of step 1 (double buffering waits for
+// them before the last operand reads of the tile, which read the next tile).
+template <int NK, int QT, int ST, int LA, int NC, bool EARLY>
 struct FwdPlace {
-  using Plan = typename FwdSteps<NK>::template P<ST>;
+  using Plan = typename FwdSteps<NK, QT>::template P<ST>;
   static constexpr int NM = Plan::NM;
-  int mx[4], check, exp[2][4][4], pack[2][4], sum[2][4], copy[NC];
+  int mx[QT], check, exp[2][QT][4], pack[2][QT], sum[2][QT], copy[NC];
   constexpr FwdPlace() : mx(), check(), exp(), pack(), sum(), copy() {
     SlotLoad<NM> L;
     L.template reads<Plan, LA>();
     if (ST == 0) L.load[NM - 1] += 2;  // the mid-tile wait and barrier
+    // the maxima within twelve slots after the S^T MFMAs (fewer in the short
+    // steps of small head dims, leaving room for the exponentials)
+    constexpr int HI = Plan::B1 + 11 < NM - 4 ? Plan::B1 + 11 : NM - 4;
     int prev = Plan::B1;
-    L.level(4 * 5 + 3, Plan::B1, Plan::B1 + 11);
-    for (int t = 0; t < 4; ++t) prev = mx[t] = L.put(5, prev, Plan::B1 + 11);
-    prev = check = L.put(3, prev + 1, Plan::B1 + 12);
-    L.level(32 * issue::kExp + 8 * (issue::kPack + 4 * issue::kMul), prev + 1, NM - 2);
+    L.level(QT * 5 + 3, Plan::B1, HI);
+    for (int t = 0; t < QT; ++t) prev = mx[t] = L.put(5, prev, HI);
+    prev = check = L.put(3, prev + 1, HI + 1);
+    L.level(8 * QT * issue::kExp + 2 * QT * (issue::kPack + 4 * issue::kMul), prev + 1, NM - 2);
     prev = prev + 1;
-    for (int g = 0; g <= 8; ++g) {
-      if (g < 8)
-        for (int i = 0; i < 4; ++i) prev = exp[g / 4][g % 4][i] = L.put(issue::kExp, prev, NM - 2);
+    for (int g = 0; g <= 2 * QT; ++g) {  // g: (sub-block, query tile) g / QT, g % QT
+      if (g < 2 * QT)
+        for (int i = 0; i < 4; ++i) prev = exp[g / QT][g % QT][i] = L.put(issue::kExp, prev, NM - 2);
       if (g > 0) {
-        prev = pack[(g - 1) / 4][(g - 1) % 4] = L.put(issue::kPack, prev, NM - 2);
-        prev = sum[(g - 1) / 4][(g - 1) % 4] = L.put(4 * issue::kMul, prev, NM - 2);
+        prev = pack[(g - 1) / QT][(g - 1) % QT] = L.put(issue::kPack, prev, NM - 2);
+        prev = sum[(g - 1) / QT][(g - 1) % QT] = L.put(4 * issue::kMul, prev, NM - 2);
       }
     }
     for (int c = 0; c < NC; ++c) copy[c] = -1;
     if (ST == 1) {
+      const int hi = EARLY ? Plan::B1 - 1 : NM - 1;
       prev = 0;
-      L.level(NC * issue::kCopy, 0, NM - 1);
-      for (int c = 0; c < NC; ++c) prev = copy[c] = L.put(issue::kCopy, prev, NM - 1);
+      L.level(NC * issue::kCopy, 0, hi);
+      for (int c = 0; c < NC; ++c) prev = copy[c] = L.put(issue::kCopy, prev, hi);
     }
   }
 };
 
 template <int DT, int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
-  constexpr int QW = 64, BM = 4 * QW, BN = 64, NST = 2;
+  constexpr int QT = FwdShape<D>::QT;  // query tiles of 16 per wave
+  constexpr int QW = 16 * QT, BM = 4 * QW, BN = 64, NST = 2;
   constexpr int NK = D / 32;
-  constexpr int NBUF = 3;
+  constexpr int NBUF = FwdShape<D>::NBUF;
   constexpr int RS = PadTile<D>::RS;
   constexpr int OPS = 2 * BN * PadTile<D>::GR / 256;  // copy instructions per fetch per wave
   constexpr int LA = 2;
   __shared__ __attribute__((aligned(16))) uint16_t sKV[NBUF][2 * BN * RS];  // K, V: a padded pair
-  static_assert(NBUF * 2 * BN * RS >= 4 * 64 * (D + 8), "the output staging must fit the tile buffers");
+  static_assert(NBUF * 2 * BN * RS >= 4 * QW * (D + 8), "the output staging must fit the tile buffers");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -131,28 +148,28 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   const uint16_t* __restrict__ V = p.v + kbase * D;
   const float c = p.scale_log2;
 
-  u32x4 qb[4][NK];
+  u32x4 qb[QT][NK];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < QT; ++t) {
     const int q = qw + 16 * t + l16;
 #pragma unroll
     for (int s = 0; s < NK; ++s)
       qb[t][s] = q < p.Nq ? ld16(p.q + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
   }
-  f32x4 acc[4][2 * NK];  // O per query tile and head-dim tile
+  f32x4 acc[QT][2 * NK];  // O per query tile and head-dim tile
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < QT; ++t) {
 #pragma unroll
     for (int n = 0; n < 2 * NK; ++n) acc[t][n] = zero4();
   }
-  float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's part of its column's row sum
+  float lsum[QT] = {};  // this lane's part of its column's row sum
   // reference of this lane's query column per query tile, and the raw-score
   // threshold (m + H) / c above which it is raised; finite, so that a column with
   // no visible key yet gives exp2(-inf - m) = 0
   constexpr float kUnset = -1e30f;
-  float m[4], thr[4];
+  float m[QT], thr[QT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < QT; ++t) {
     m[t] = kUnset;
     thr[t] = (m[t] + fwd_headroom<DT>()) / c;
   }
@@ -189,10 +206,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   // P of the second pair (pa[1]), whose product runs in step 0 of the next tile
   // with V read from the previous buffer (zero before the first tile).
   u32x4 carry[LA];
-  u32x4 pa[2][4];  // P A operands of pair J, per query tile
-  f32x4 sc[2][4];  // S^T of the current pair's sub-blocks, then P
+  u32x4 pa[2][QT];  // P A operands of pair J, per query tile
+  f32x4 sc[2][QT];  // S^T of the current pair's sub-blocks, then P
 #pragma unroll
-  for (int t = 0; t < 4; ++t) pa[1][t] = zero_u4();
+  for (int t = 0; t < QT; ++t) pa[1][t] = zero_u4();
   int prev = 0;
 
   auto compute = [&](int cur, int nxt, auto mask_c, int kv0, const i32x4& fsrc, int fbuf) {
@@ -201,9 +218,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     const uint16_t* Vt = Kt + BN * RS;
     const uint16_t* Vp = sKV[prev] + BN * RS;
     const uint16_t* Kn = sKV[nxt];
-    float mx[4];
+    float mx[QT];
 
-    using Steps = FwdSteps<NK>;
+    using Steps = FwdSteps<NK, QT>;
     auto begin = [&](auto stc) {
       constexpr int st = decltype(stc)::value;
       if constexpr (st == 1) {
@@ -229,12 +246,17 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     };
     auto next = [&](auto oc) -> u32x4 {  // operand oc of the next tile: S^T of pair 0
       constexpr int o = decltype(oc)::value;
+      if constexpr (NBUF == 2 && o == 0) {
+        // double buffering: the next tile was copied in this tile's second half
+        wait_vmem();
+        tile_barrier();
+      }
       return pad_row16<D>(Kn, 16 * (o / NK) + l16, 4 * (o % NK) + j4);
     };
     auto mfma = [&](auto stc, auto mc, const u32x4& op) {
       constexpr int st = decltype(stc)::value, mi = decltype(mc)::value;
       using Plan = typename Steps::template P<st>;
-      constexpr int k = Plan::stage(mi), loc = Plan::local(mi), o = loc / 4, t = loc % 4;
+      constexpr int k = Plan::stage(mi), loc = Plan::local(mi), o = loc / QT, t = loc % QT;
       constexpr int J = st == 0 ? 1 : 0;
       if constexpr (k == 0) {
         constexpr int sb = o / NK, s = o % NK;
@@ -249,13 +271,13 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     auto valu = [&](auto stc, auto mc, auto gc) {
       constexpr int st = decltype(stc)::value, mi = decltype(mc)::value;
       using Plan = typename Steps::template P<st>;
-      constexpr FwdPlace<NK, st, LA, OPS> PL{};
+      constexpr FwdPlace<NK, QT, st, LA, OPS, NBUF == 2> PL{};
       (void)gc;
       static_for<OPS>([&](auto cc) {
         if constexpr (PL.copy[decltype(cc)::value] == mi) copy_part(cc, fsrc, fbuf);
       });
       // the pair's maximum per query column (masked scores first)
-      static_for<4>([&](auto tc) {
+      static_for<QT>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         if constexpr (PL.mx[t] == mi) {
           if constexpr (MASK) {
@@ -276,10 +298,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       if constexpr (PL.check == mi) {
         bool any = false;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) any = any || mx[t] > thr[t];
+        for (int t = 0; t < QT; ++t) any = any || mx[t] > thr[t];
         if (__builtin_amdgcn_ballot_w64(any) != 0) {  // rare: set or raise references
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
+          for (int t = 0; t < QT; ++t) {
             float v = mx[t] * c;
             v = fmaxf(v, __shfl_xor(v, 16));
             v = fmaxf(v, __shfl_xor(v, 32));
@@ -293,7 +315,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       }
       static_for<2>([&](auto sbc) {
         constexpr int sb = decltype(sbc)::value;
-        static_for<4>([&](auto tc) {
+        static_for<QT>([&](auto tc) {
           constexpr int t = decltype(tc)::value;
           static_for<4>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
@@ -315,7 +337,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   // was computed).
   auto flush = [&]() {
     const uint16_t* Vp = sKV[prev] + BN * RS;
-    using Steps = FwdSteps<NK>;
+    using Steps = FwdSteps<NK, QT>;
     using Plan = typename Steps::template Flush<0>;
     run_tile<Steps::template Flush, 1, LA>(
         [&](auto) {},
@@ -325,7 +347,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
           return pad_tr_operand<D>(Vp, k0, k0 + 16, 16 * n);
         },
         [&](auto, auto mc, const u32x4& op) {
-          constexpr int loc = Plan::local(decltype(mc)::value), o = loc / 4, t = loc % 4;
+          constexpr int loc = Plan::local(decltype(mc)::value), o = loc / QT, t = loc % QT;
           Mx<DT>::acc16a(acc[t][o], pa[1][t], op);
         },
         [&](auto, auto, auto) {});
@@ -367,6 +389,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
           wait_vmem();
           tile_barrier();
           copy_all(kt + NBUF - 1, fbuf);
+          if constexpr (NBUF == 2) {  // the second barrier a computed tile has
+            wait_vmem();
+            tile_barrier();
+          }
         }
         if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), kt * BN, fsrc, fbuf);
         if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), kt * BN, fsrc, fbuf);
@@ -385,7 +411,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     // run again from zero with the raised references
     settle(acc);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < QT; ++t) {
       pa[1][t] = zero_u4();
       lsum[t] = 0.f;
 #pragma unroll
@@ -397,9 +423,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   settle(acc);
 
   // O = acc / l per row; LSE = ln 2 (m + log2 l), -inf for a row that sees no key
-  float inv[4][4];
+  float inv[QT][4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < QT; ++t) {
     float l = lsum[t];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
@@ -409,8 +435,8 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) inv[t][i] = __shfl(il, 4 * j4 + i);  // row 16t + 4 j4 + i
   }
-  uint16_t* stage = &sKV[0][0] + w * 64 * (D + 8);
-  store_block64_rows<DT, D>(acc, inv, stage, p.o + qbase * D, qw, p.Nq, lane);
+  uint16_t* stage = &sKV[0][0] + w * QW * (D + 8);
+  store_block_rows<DT, D, QT>(acc, inv, stage, p.o + qbase * D, qw, p.Nq, lane);
 }
 
 // Launcher of one instance (explicitly instantiated per instance in fa_fwd_inst.hip).
@@ -431,7 +457,8 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t s) {
   p.G = pb.Hq / pb.Hkv;
   p.off = pb.Nkv - pb.Nq;
   p.scale_log2 = pb.scale * kLog2e;
-  const dim3 grid((unsigned)(((pb.Nq + 255) / 256) * pb.Hq * pb.B));
+  constexpr int BM = 4 * 16 * FwdShape<D>::QT;  // queries per workgroup
+  const dim3 grid((unsigned)(((pb.Nq + BM - 1) / BM) * pb.Hq * pb.B));
   hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }

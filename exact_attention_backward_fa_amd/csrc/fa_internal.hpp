@@ -7,6 +7,35 @@
 
 namespace fa {
 
+// Head dims with a kernel instance (every kernel family but the fused atomic one,
+// which is built for 64 and 128 only).
+constexpr bool head_dim_supported(int d) {
+  return d == 32 || d == 64 || d == 96 || d == 128 || d == 256;
+}
+constexpr bool atomic_head_dim(int d) { return d == 64 || d == 128; }
+
+// Call FN<DT, D, CAUSAL>(args...) for a problem's (dtype, head dim, causal).
+#define FA_DISPATCH_D(DT, PB, FN, ...)                                                        \
+  switch ((PB).d) {                                                                          \
+    case 32: return (PB).causal ? FN<DT, 32, true>(__VA_ARGS__) : FN<DT, 32, false>(__VA_ARGS__); \
+    case 64: return (PB).causal ? FN<DT, 64, true>(__VA_ARGS__) : FN<DT, 64, false>(__VA_ARGS__); \
+    case 96: return (PB).causal ? FN<DT, 96, true>(__VA_ARGS__) : FN<DT, 96, false>(__VA_ARGS__); \
+    case 128:                                                                                \
+      return (PB).causal ? FN<DT, 128, true>(__VA_ARGS__) : FN<DT, 128, false>(__VA_ARGS__);   \
+    case 256:                                                                                \
+      return (PB).causal ? FN<DT, 256, true>(__VA_ARGS__) : FN<DT, 256, false>(__VA_ARGS__);   \
+    default:                                                                                 \
+      return hipErrorInvalidValue;                                                           \
+  }
+#define FA_DISPATCH(PB, FN, ...)                        \
+  do {                                                  \
+    if ((PB).dtype == 0) {                              \
+      FA_DISPATCH_D(0, PB, FN, __VA_ARGS__)             \
+    } else {                                            \
+      FA_DISPATCH_D(1, PB, FN, __VA_ARGS__)             \
+    }                                                   \
+  } while (0)
+
 // Validated arguments of one call (sizes already checked, pointers device-side).
 struct Problem {
   int B, Hq, Hkv, Nq, Nkv, d;

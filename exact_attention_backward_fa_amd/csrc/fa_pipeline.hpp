@@ -205,23 +205,51 @@ __device__ __forceinline__ void run_tile_carry(u32x4 (&carry)[LA], FBegin&& begi
   });
 }
 
-// Store a wave's 64 x D block held in 16x16 accumulators (acc[t][n] element i of
-// lane (l16, j4) is row 16t + 4 j4 + i, column 16n + l16), times `scale`, to rows
-// row0.. of a row-major [*, D] tensor; rows at or past n_rows are skipped.  The
-// block goes through the wave's own LDS staging area (64 rows of D + 8 elements):
-// 2-byte writes in the accumulator layout, then 16-byte row reads, so the global
-// stores are whole 16-byte pieces of consecutive rows instead of 2-byte pieces of
-// 64 rows each.
-template <int DT, int D>
-__device__ __forceinline__ void store_block64_c16(const f32x4 (&acc)[4][D / 16], float scale,
-                                                  uint16_t* __restrict__ stage, uint16_t* __restrict__ dst,
-                                                  int row0, int n_rows, int lane) {
+// Copy a wave's staged ROWS x D block (rows of D + 8 elements in LDS) to rows
+// row0.. of a row-major [*, D] tensor in 16-byte pieces of whole rows, skipping
+// rows at or past n_rows: lane L of round k moves granule 64 k + L of the block
+// (row (64 k + L) / (D / 8)).
+template <int D, int ROWS>
+__device__ __forceinline__ void store_staged(const uint16_t* __restrict__ stage, uint16_t* __restrict__ dst,
+                                             int row0, int n_rows, int lane) {
   constexpr int SS = D + 8;
   constexpr int CPR = D / 8;
-  constexpr int RPI = 64 / CPR;
+  static_assert((ROWS * CPR) % 64 == 0, "whole rounds of 64 granules");
+  if constexpr (64 % CPR == 0) {
+    // whole rows per round: 64 / CPR rows of CPR granules
+    constexpr int RPI = 64 / CPR;
+#pragma unroll
+    for (int k = 0; k < ROWS / RPI; ++k) {
+      const int r = k * RPI + lane / CPR, c = lane % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * SS + 8 * c);
+      if (row0 + r < n_rows) st16(dst + (size_t)(row0 + r) * D + 8 * c, v);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < ROWS * CPR / 64; ++k) {
+      const int g = 64 * k + lane;
+      const int r = g / CPR, c = g % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * SS + 8 * c);
+      if (row0 + r < n_rows) st16(dst + (size_t)(row0 + r) * D + 8 * c, v);
+    }
+  }
+}
+
+// Store a wave's (16 RT) x D block held in 16x16 accumulators (acc[t][n] element i
+// of lane (l16, j4) is row 16t + 4 j4 + i, column 16n + l16), times `scale`, to
+// rows row0.. of a row-major [*, D] tensor; rows at or past n_rows are skipped.
+// The block goes through the wave's own LDS staging area (16 RT rows of D + 8
+// elements): 2-byte writes in the accumulator layout, then 16-byte row reads, so
+// the global stores are whole 16-byte pieces of consecutive rows instead of
+// 2-byte pieces of many rows each.
+template <int DT, int D, int RT>
+__device__ __forceinline__ void store_block_c16(const f32x4 (&acc)[RT][D / 16], float scale,
+                                                uint16_t* __restrict__ stage, uint16_t* __restrict__ dst,
+                                                int row0, int n_rows, int lane) {
+  constexpr int SS = D + 8;
   const int l16 = lane & 15, j4 = lane >> 4;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < RT; ++t) {
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
 #pragma unroll
@@ -229,28 +257,21 @@ __device__ __forceinline__ void store_block64_c16(const f32x4 (&acc)[4][D / 16],
         stage[(16 * t + 4 * j4 + i) * SS + 16 * n + l16] = Dt<DT>::one(acc[t][n][i] * scale);
     }
   }
-#pragma unroll
-  for (int k = 0; k < 64 / RPI; ++k) {
-    const int r = k * RPI + lane / CPR, c = lane % CPR;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * SS + 8 * c);
-    if (row0 + r < n_rows) st16(dst + (size_t)(row0 + r) * D + 8 * c, v);
-  }
+  store_staged<D, 16 * RT>(stage, dst, row0, n_rows, lane);
 }
 
-// store_block64_c16 with a scale per row: row 16t + 4 j4 + i of the lane's
+// store_block_c16 with a scale per row: row 16t + 4 j4 + i of the lane's
 // accumulators is multiplied by scale[t][i]; acc holds D / 16 head-dim tiles per
 // query tile (further tiles are ignored).
-template <int DT, int D, int NT>
-__device__ __forceinline__ void store_block64_rows(const f32x4 (&acc)[4][NT], const float (&scale)[4][4],
-                                                   uint16_t* __restrict__ stage, uint16_t* __restrict__ dst,
-                                                   int row0, int n_rows, int lane) {
+template <int DT, int D, int RT, int NT>
+__device__ __forceinline__ void store_block_rows(const f32x4 (&acc)[RT][NT], const float (&scale)[RT][4],
+                                                 uint16_t* __restrict__ stage, uint16_t* __restrict__ dst,
+                                                 int row0, int n_rows, int lane) {
   static_assert(NT >= D / 16, "a head-dim tile per 16 columns");
   constexpr int SS = D + 8;
-  constexpr int CPR = D / 8;
-  constexpr int RPI = 64 / CPR;
   const int l16 = lane & 15, j4 = lane >> 4;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < RT; ++t) {
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) {
 #pragma unroll
@@ -258,12 +279,7 @@ __device__ __forceinline__ void store_block64_rows(const f32x4 (&acc)[4][NT], co
         stage[(16 * t + 4 * j4 + i) * SS + 16 * n + l16] = Dt<DT>::one(acc[t][n][i] * scale[t][i]);
     }
   }
-#pragma unroll
-  for (int k = 0; k < 64 / RPI; ++k) {
-    const int r = k * RPI + lane / CPR, c = lane % CPR;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * SS + 8 * c);
-    if (row0 + r < n_rows) st16(dst + (size_t)(row0 + r) * D + 8 * c, v);
-  }
+  store_staged<D, 16 * RT>(stage, dst, row0, n_rows, lane);
 }
 
 }  // namespace fa

@@ -34,8 +34,12 @@
  *     nearest even.
  *   - Every pointer must be 16-byte aligned.  A pointer may be NULL only when its
  *     tensor has no element.
- *   - d is 64 or 128.  B, N_q, N_kv >= 0 (zero-size calls are valid), Hq and Hkv
- *     >= 1 with Hq % Hkv == 0, N * d < 2^31 per head, B and Hq <= 65535.
+ *   - d is 32, 64, 96, 128 or 256 (the Liger-Kernel pull request "[Kernel] Flash
+ *     attention 2", Details, claims no restriction on the head dimension; these
+ *     are the widths with a kernel instance).  The fused atomic dQ path
+ *     (FA_DQ_ATOMIC) is built for d = 64 and 128 only.  B, N_q, N_kv >= 0
+ *     (zero-size calls are valid), Hq and Hkv >= 1 with Hq % Hkv == 0,
+ *     N * d < 2^31 per head, B and Hq <= 65535.
  *   - softmax_scale must be finite and > 0.  causal: 0 = off, nonzero = on.
  *   - stream: a hipStream_t passed as void* (NULL = the null stream).  Work is
  *     enqueued asynchronously; no call synchronises.
@@ -55,7 +59,8 @@ extern "C" {
 #define FA_OK            0
 #define FA_ERR_NULLPTR  -1  /* required pointer is NULL */
 #define FA_ERR_SHAPE    -2  /* bad B/Hq/Hkv/N_q/N_kv, Hq % Hkv != 0, or size limits */
-#define FA_ERR_HEADDIM  -3  /* d not in {64, 128} */
+#define FA_ERR_HEADDIM  -3  /* d not in {32, 64, 96, 128, 256}, or FA_DQ_ATOMIC with
+                               d not in {64, 128} */
 #define FA_ERR_DTYPE    -4  /* dtype not FP16/BF16 */
 #define FA_ERR_SCALE    -5  /* softmax_scale not finite or <= 0 */
 #define FA_ERR_WORKSPACE -6 /* workspace NULL/misaligned or smaller than required */

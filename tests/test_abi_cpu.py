@@ -52,7 +52,7 @@ def test_status_strings(lib):
                  FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_MODE, FA_ERR_SCRATCH, 12345):
         s = lib.fa_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
-    assert lib.fa_status_string(FA_ERR_HEADDIM).decode().find("64") >= 0
+    assert lib.fa_status_string(FA_ERR_HEADDIM).decode().find("96") >= 0
     assert lib.fa_version() >= 100
 
 
@@ -82,8 +82,8 @@ def bwd(lib, **kw):
 def test_argument_errors(lib, call):
     assert call(lib, dtype=2) == FA_ERR_DTYPE
     assert call(lib, dtype=-1) == FA_ERR_DTYPE
-    assert call(lib, d=96) == FA_ERR_HEADDIM
-    assert call(lib, d=0) == FA_ERR_HEADDIM
+    for d in (0, 8, 16, 48, 80, 112, 160, 192, 512, -64):
+        assert call(lib, d=d) == FA_ERR_HEADDIM, d
     assert call(lib, Hq=3, Hkv=2) == FA_ERR_SHAPE
     assert call(lib, Hkv=0) == FA_ERR_SHAPE
     assert call(lib, Hq=0) == FA_ERR_SHAPE
@@ -114,6 +114,23 @@ def test_bwd_specific_errors(lib):
     assert bwd(lib, mode=1, wsb=need - 1) == FA_ERR_WORKSPACE
     need_sep = lib.fa_bwd_ex_workspace_bytes(1, 2, 1, 8, 8, 64, 0, 0, 2)
     assert bwd(lib, mode=2, wsb=need_sep - 1) == FA_ERR_WORKSPACE
+
+
+def test_head_dims_and_the_atomic_path(lib):
+    """d in {32, 64, 96, 128, 256} is accepted (the call here then stops at the
+    workspace check); the fused atomic dQ kernel exists for 64 and 128 only."""
+    for d in (32, 64, 96, 128, 256):
+        assert bwd(lib, d=d, mode=2, ws=0) == FA_ERR_WORKSPACE, d
+        assert fwd(lib, d=d, q=0) == FA_ERR_NULLPTR, d
+        assert lib.fa_bwd_ex_workspace_bytes(1, 2, 1, 8, 8, d, 0, 0, 2) > 0
+        atomic_ws = lib.fa_bwd_ex_workspace_bytes(1, 2, 1, 8, 8, d, 0, 0, 1)
+        if d in (64, 128):
+            assert atomic_ws > 0
+            assert bwd(lib, d=d, mode=1, ws=0) == FA_ERR_WORKSPACE
+        else:
+            assert atomic_ws == 0
+            assert bwd(lib, d=d, mode=1) == FA_ERR_HEADDIM
+    assert b"256" in lib.fa_status_string(FA_ERR_HEADDIM)
 
 
 def test_workspace_sizes(lib):
@@ -169,7 +186,7 @@ def test_noalloc_checks_arguments_before_any_device_call(lib):
     cap = lib.fa_bwd_noalloc_max_scratch_bytes()
     assert cap == 16 << 20
     assert b"scratch" in lib.fa_status_string(FA_ERR_SCRATCH)
-    assert noalloc(lib, d=96) == FA_ERR_HEADDIM
+    assert noalloc(lib, d=80) == FA_ERR_HEADDIM
     assert noalloc(lib, Hq=3, Hkv=2) == FA_ERR_SHAPE
     assert noalloc(lib, scale=-1.0) == FA_ERR_SCALE
     assert noalloc(lib, dtype=5) == FA_ERR_DTYPE

@@ -191,6 +191,62 @@ def test_edge_shapes(shape, device):
         pu.assert_within(case, pu.compare(case, got, ref, mode))
 
 
+# Head dims beyond 64 and 128 (the Liger-Kernel pull request "[Kernel] Flash
+# attention 2", Details, claims no restriction on the head dimension).  d = 32 and
+# 96 run the same kernels with one and three 32-wide contraction steps; d = 256
+# keeps 32 resident rows per wave and double-buffered tiles.  Shapes are ragged on
+# both sides and span several 256-row (d = 256: 128-row) work items.
+HEAD_DIM_CASES = [
+    # B, Hq, Hkv, Nq, Nkv, d, dtype, causal
+    (2, 4, 2, 100, 333, 32, "fp16", True),
+    (1, 8, 2, 700, 700, 32, "bf16", False),
+    (2, 4, 1, 513, 257, 32, "bf16", True),     # N_q > N_kv: the first rows see no key
+    (2, 4, 2, 100, 333, 96, "bf16", True),
+    (1, 6, 3, 700, 700, 96, "fp16", False),
+    (1, 4, 4, 300, 1000, 96, "fp16", True),
+    (2, 4, 2, 100, 333, 256, "fp16", True),
+    (1, 4, 2, 600, 600, 256, "bf16", True),
+    (1, 2, 1, 333, 450, 256, "bf16", False),
+    (1, 4, 4, 129, 64, 256, "fp16", True),      # N_q > N_kv
+]
+
+
+@pytest.mark.parametrize("shape", HEAD_DIM_CASES,
+                         ids=[f"d{s[5]}_{s[0]}x{s[1]}x{s[2]}_{s[3]}x{s[4]}_{s[6]}_{'c' if s[7] else 'nc'}"
+                              for s in HEAD_DIM_CASES])
+def test_head_dims(shape, device):
+    B, Hq, Hkv, Nq, Nkv, d, dt, causal = shape
+    x = inputs.make_custom(991 + d + Nq, B, Hq, Hkv, Nq, Nkv, d, dt)
+    case = inputs.Case(f"d{d}", 0, 0, B, Hq, Hkv, Nq, Nkv, d, dt, causal, 1.0 / np.sqrt(d))
+    o, lse = orc.forward(x["q"], x["k"], x["v"], case.scale, causal)
+    dq, dk, dv = orc.backward(x["q"], x["k"], x["v"], x["do"], case.scale, causal)
+    ref = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    modes = MODES if d in (64, 128) else ("separate", "auto")
+    for mode in modes:
+        res = pu.gpu_forward_backward(case, x, device, dq_mode=mode)
+        got = {k: res[k].double().numpy() for k in res}
+        pu.assert_within(case, pu.compare(case, got, ref, mode))
+
+
+def test_head_dim_256_long_sequence(device):
+    """d = 256 at N = 4096, causal GQA bf16: many work items per head, double
+    buffering over 64 key tiles; one group compared in full."""
+    B, Hq, Hkv, N, d = 1, 8, 2, 4096, 256
+    x = inputs.make_custom(256_4096, B, Hq, Hkv, N, N, d, "bf16")
+    case = inputs.Case("d256_4096", 0, 0, B, Hq, Hkv, N, N, d, "bf16", True, 1.0 / np.sqrt(d))
+    ref = pu.oracle_group(case, x, 0, 1)
+    res = pu.gpu_forward_backward(case, x, device, dq_mode="separate")
+    pu.assert_within(case, pu.compare(case, pu.gpu_group(case, res, 0, 1), ref, "separate g=1"))
+
+
+def test_atomic_path_only_for_d64_d128(device):
+    import exact_attention_backward_fa_amd as fa
+    x = pu.to_dev(inputs.make_custom(5, 1, 2, 1, 64, 64, 96, "fp16"), device)
+    o, lse = fa.fwd(x["q"], x["k"], x["v"], 0.1, True)
+    with pytest.raises(RuntimeError, match="status -3"):
+        fa.bwd(x["q"], x["k"], x["v"], o, lse, x["do"], 0.1, True, dq_mode="atomic")
+
+
 RISING = [("bf16", 80.0), ("fp16", 12.0), ("fp16", 30.0)]
 
 
