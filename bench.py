@@ -72,6 +72,11 @@ def main() -> int:
     ap.add_argument("--dq-mode", default="auto", choices=["auto", "atomic", "separate"])
     ap.add_argument("--workload", default=None, help="case name (default: headline workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bias", default="none", choices=["none", "keys", "full"],
+                    help="additive score bias: a per-key [B,1,1,N_kv] padding mask, or a "
+                         "full [B,Hq,N_q,N_kv] bias (timed through fa_*_bias_dropout)")
+    ap.add_argument("--dbias", action="store_true", help="also write dBias [B,Hq,N_q,N_kv]")
+    ap.add_argument("--dropout", type=float, default=0.0, help="dropout probability of P")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, copy a 512 MiB buffer once (known traffic) so that "
                          "a counter profile of this run can scale FETCH_SIZE/WRITE_SIZE")
@@ -110,18 +115,51 @@ def main() -> int:
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     n = args.steps
+    features = args.bias != "none" or args.dbias or args.dropout > 0.0
+    if features and args.dq_mode == "atomic":
+        log("[bench] bias, dBias and dropout run on the separate dQ path only")
+        return 2
+    bias = dbias = None
+    if features:
+        resolved = "separate"
+        g = torch.Generator(device=dev).manual_seed(1234)
+        if args.bias == "keys":  # a padding mask: the last 1/8 of every row's keys hidden
+            bias = torch.zeros(case.B, 1, 1, (case.Nkv + 7) // 8 * 8, dtype=case.torch_dtype,
+                               device=dev)
+            bias[..., case.Nkv - case.Nkv // 8:] = float("-inf")
+            bias = bias[..., :case.Nkv]
+        elif args.bias == "full":
+            bias = torch.randn(case.B, case.Hq, case.Nq, (case.Nkv + 7) // 8 * 8, generator=g,
+                               device=dev, dtype=torch.float32).to(case.torch_dtype)
+            bias = bias[..., :case.Nkv]
+        if args.dbias:
+            dbias = torch.empty(case.B, case.Hq, case.Nq, case.Nkv, dtype=case.torch_dtype,
+                                device=dev)
+        ws = torch.empty(max(fa.bwd_workspace_bytes(case.B, case.Hq, case.Hkv, case.Nq, case.Nkv,
+                                                    case.d, case.causal, case.torch_dtype,
+                                                    "separate"), 1),
+                         dtype=torch.uint8, device=dev)
     ev = {k: [fa.HipEvent() for _ in range(n)] for k in ("f0", "f1", "b0", "b1", "k0", "k1")}
 
     def step(i=None):
         if i is not None:
             ev["f0"][i].record(stream)
-        fa.fwd_into(d["q"], d["k"], d["v"], o, lse, case.scale, case.causal)
+        if features:
+            fa.fwd_bias_dropout(d["q"], d["k"], d["v"], case.scale, case.causal, bias=bias,
+                                dropout_p=args.dropout, seed=77, o=o, lse=lse)
+        else:
+            fa.fwd_into(d["q"], d["k"], d["v"], o, lse, case.scale, case.causal)
         if i is not None:
             ev["f1"][i].record(stream)
             ev["b0"][i].record(stream)
-        fa.bwd_into(d["q"], d["k"], d["v"], o, lse, d["do"], dq, dk, dv, case.scale, case.causal,
-                    dq_mode=mode, workspace=ws,
-                    events=None if i is None else (ev["k0"][i].handle, ev["k1"][i].handle))
+        if features:
+            fa.bwd_bias_dropout(d["q"], d["k"], d["v"], o, lse, d["do"], case.scale, case.causal,
+                                bias=bias, dropout_p=args.dropout, seed=77, dq=dq, dk=dk, dv=dv,
+                                dbias=dbias, workspace=ws)
+        else:
+            fa.bwd_into(d["q"], d["k"], d["v"], o, lse, d["do"], dq, dk, dv, case.scale,
+                        case.causal, dq_mode=mode, workspace=ws,
+                        events=None if i is None else (ev["k0"][i].handle, ev["k1"][i].handle))
         if i is not None:
             ev["b1"][i].record(stream)
 
@@ -140,7 +178,9 @@ def main() -> int:
 
     fwd_ms = total("f0", "f1") / n
     bwd_ms = total("b0", "b1") / n
-    kern_ms = total("k0", "k1") / n
+    # the dK/dV kernel's own events are recorded on the plain path only (the feature
+    # runs' per-kernel split comes from a kernel trace)
+    kern_ms = None if features else total("k0", "k1") / n
     bwd_flops = case.bwd_flops()
     fwd_flops = case.fwd_flops()
     value = bwd_flops / (bwd_ms * 1e-3) / 1e12
@@ -148,18 +188,18 @@ def main() -> int:
     # performs all five products of the backward (10*Nq*Nkv*d per query head, halved
     # for causal); on the separate path it performs four of them (8*Nq*Nkv*d).
     kern_flops = bwd_flops if resolved == "atomic" else bwd_flops * 0.8
-    achieved = kern_flops / (kern_ms * 1e-3) / 1e12
+    achieved = None if kern_ms is None else kern_flops / (kern_ms * 1e-3) / 1e12
     # HBM bytes per launch of that kernel from the committed counter profile, when it
     # was taken from the current kernel sources (None otherwise).
     from exact_attention_backward_fa_amd import profiling
     dt_id = 1 if case.dtype == "bf16" else 0
     kname = (f"{'bwd_dkdv_atomic_kernel' if resolved == 'atomic' else 'bwd_dkdv_kernel'}"
              f"<{dt_id}, {case.d}, {'true' if case.causal else 'false'}>")
-    traffic = profiling.read_traffic(kname)
-    mfma = profiling.read_mfma(kname)
+    traffic = None if features else profiling.read_traffic(kname)
+    mfma = None if features else profiling.read_mfma(kname)
     log(f"[bench] fwd {fwd_ms:.3f} ms ({fwd_flops / fwd_ms / 1e9:.1f} TFLOP/s)  bwd {bwd_ms:.3f} ms "
-        f"({value:.1f} TFLOP/s, {100 * value / PEAK_BF16_TFLOPS:.1f}% of peak)  dkdv kernel "
-        f"{kern_ms:.3f} ms ({achieved:.1f} TFLOP/s)")
+        f"({value:.1f} TFLOP/s, {100 * value / PEAK_BF16_TFLOPS:.1f}% of peak)"
+        + ("" if kern_ms is None else f"  dkdv kernel {kern_ms:.3f} ms ({achieved:.1f} TFLOP/s)"))
 
     out = {
         "metric": "fa_bwd TFLOP/s and % of MI355X bf16 MFMA peak (causal GQA, d=128)",
@@ -187,12 +227,12 @@ def main() -> int:
         "roofline": {
             "kernel": kname,
             "bound": "mfma",
-            "achieved": round(achieved, 2),
+            "achieved": None if achieved is None else round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "frac": None if achieved is None else round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel_ms": round(kern_ms, 4),
+            "kernel_ms": None if kern_ms is None else round(kern_ms, 4),
             # rocprof MfmaUtil (matrix-unit busy share of active SIMD cycles) and the
             # MFMA flops the kernel executes per launch, from the committed counter
             # profile of the current kernel sources; null when that profile is stale.
@@ -200,6 +240,9 @@ def main() -> int:
             "executed_tflop": None if mfma is None else mfma[1],
         },
     }
+    if features:
+        out["config"]["features"] = {"bias": args.bias, "dbias": bool(args.dbias),
+                                     "dropout_p": args.dropout}
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.bfloat16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -208,7 +251,7 @@ def main() -> int:
         torch.cuda.synchronize(dev)
         out["copy_calibration_bytes"] = {"read": src.numel() * 2, "write": dst.numel() * 2}
         del src, dst
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not features:
         log("[bench] cpu baseline: fp64 oracle backward on one kv-head group ...")
         out["cpu_baseline"] = cpu_baseline(case, x)
         log(f"[bench] cpu baseline {out['cpu_baseline']['value']:.4f} TFLOP/s "

@@ -6,10 +6,11 @@ Python binding over it plus the seeded workload generator used by the tests and 
 benchmark.  The library is loaded on first use and there is no CPU fallback.
 """
 from ._lib import (  # noqa: F401
-    DQ_MODES, EXPORTS, HipEvent, auto_dq_mode, bwd, bwd_into, bwd_workspace_bytes, fwd,
-    fwd_into, load, status_string,
+    DQ_MODES, EXPORTS, HipEvent, auto_dq_mode, bwd, bwd_bias_dropout, bwd_into, bwd_workspace_bytes,
+    fwd, fwd_bias_dropout, fwd_into, load, status_string,
 )
 from .autograd import attention  # noqa: F401
 
 __all__ = ["attention", "fwd", "fwd_into", "bwd", "bwd_into", "bwd_workspace_bytes", "auto_dq_mode",
+           "fwd_bias_dropout", "bwd_bias_dropout",
            "status_string", "load", "HipEvent", "DQ_MODES", "EXPORTS"]

@@ -23,12 +23,14 @@ DQ_MODE_NAMES = {v: k for k, v in DQ_MODES.items()}
 EXPORTS = (
     "fa_fwd", "fa_bwd", "fa_bwd_ex", "fa_bwd_workspace_bytes",
     "fa_bwd_ex_workspace_bytes", "fa_bwd_auto_dq_mode", "fa_status_string", "fa_version",
-    "fa_bwd_noalloc", "fa_bwd_noalloc_max_scratch_bytes",
+    "fa_bwd_noalloc", "fa_bwd_noalloc_max_scratch_bytes", "fa_fwd_bias_dropout",
+    "fa_bwd_bias_dropout",
 )
 
 _lib = None
 
 _i, _f, _p, _sz = ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+_ll, _ull = ctypes.c_longlong, ctypes.c_ulonglong
 
 
 def load() -> ctypes.CDLL:
@@ -61,6 +63,12 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_noalloc.restype = _i
     lib.fa_bwd_noalloc_max_scratch_bytes.argtypes = []
     lib.fa_bwd_noalloc_max_scratch_bytes.restype = _sz
+    lib.fa_fwd_bias_dropout.argtypes = ([_p] * 5 + [_i] * 6 + [_f, _i, _i, _p, _ll, _ll, _ll, _f, _ull,
+                                                                _p])
+    lib.fa_fwd_bias_dropout.restype = _i
+    lib.fa_bwd_bias_dropout.argtypes = ([_p] * 9 + [_i] * 6 + [_f, _i, _i, _p, _ll, _ll, _ll, _p, _f,
+                                                                _ull, _p, _sz, _p])
+    lib.fa_bwd_bias_dropout.restype = _i
     _lib = lib
     return lib
 
@@ -173,6 +181,90 @@ def bwd(q, k, v, o, lse, do, scale: float, causal: bool, *, dq_mode: str = "auto
     dv = torch.empty_like(v)
     bwd_into(q, k, v, o, lse, do, dq, dk, dv, scale, causal, dq_mode=dq_mode)
     return dq, dk, dv
+
+
+# --- additive score bias and dropout ------------------------------------------
+
+def _bias_args(bias, q, k):
+    """(pointer, stride_b, stride_h, stride_q) of a bias broadcastable to
+    [B, Hq, Nq, Nkv] (a 4-D tensor whose dimensions are those sizes or 1, key
+    dimension contiguous), or (None, 0, 0, 0)."""
+    if bias is None:
+        return None, 0, 0, 0
+    B, Hq, Nq, _ = q.shape
+    Nkv = k.shape[2]
+    if bias.dim() != 4 or bias.dtype != q.dtype or bias.device != q.device:
+        raise ValueError("bias must be a 4-D tensor of q's dtype on q's device")
+    want = (B, Hq, Nq, Nkv)
+    for got, full in zip(bias.shape, want):
+        if got not in (1, full):
+            raise ValueError(f"bias shape {tuple(bias.shape)} does not broadcast to {want}")
+    if bias.shape[3] != Nkv or (Nkv > 1 and bias.stride(3) != 1):
+        raise ValueError("bias must span N_kv keys with the key dimension contiguous")
+    strides = [0 if bias.shape[i] == 1 else bias.stride(i) for i in range(3)]
+    if any(st % 8 for st in strides) or bias.data_ptr() % 16:
+        raise ValueError("bias rows must be 16-byte aligned (strides multiples of 8 elements); "
+                         "pad the key dimension of the storage to a multiple of 8")
+    # the kernels read each row in whole 16-byte pieces: N_kv rounded up to 8 elements
+    last = sum((bias.shape[i] - 1) * strides[i] for i in range(3)) + (Nkv + 7) // 8 * 8
+    end = bias.storage_offset() + last
+    if end * bias.element_size() > bias.untyped_storage().nbytes():
+        raise ValueError("each bias row must be readable for N_kv rounded up to a multiple of 8 "
+                         "elements: pad the key dimension of the storage")
+    return bias.data_ptr(), strides[0], strides[1], strides[2]
+
+
+def fwd_bias_dropout(q, k, v, scale: float, causal: bool, *, bias=None, dropout_p: float = 0.0,
+                     seed: int = 0, o=None, lse=None):
+    """fa_fwd_bias_dropout: returns (o, lse).  ``bias`` broadcasts to [B, Hq, Nq, Nkv]."""
+    B, Hq, Hkv, Nq, Nkv, d = _shapes(q, k, v)
+    _check_tensors(q.dtype, q.device, q=q, k=k, v=v)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensors(q.dtype, q.device, o=o, lse=lse)
+    bp, sb, sh, sq = _bias_args(bias, q, k)
+    lib = load()
+    _check(lib.fa_fwd_bias_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq,
+                                   Nkv, d, float(scale), int(bool(causal)), FA_DTYPE[q.dtype], bp,
+                                   sb, sh, sq, float(dropout_p), int(seed) & (2 ** 64 - 1),
+                                   _stream(q.device)),
+           "fa_fwd_bias_dropout")
+    return o, lse
+
+
+def bwd_bias_dropout(q, k, v, o, lse, do, scale: float, causal: bool, *, bias=None,
+                     want_dbias: bool = False, dropout_p: float = 0.0, seed: int = 0,
+                     dq=None, dk=None, dv=None, dbias=None, workspace=None):
+    """fa_bwd_bias_dropout: returns (dq, dk, dv, dbias or None); dbias is the full
+    [B, Hq, Nq, Nkv] gradient of the scores' bias.  Outputs and the workspace may be
+    passed in (then nothing is allocated); a given ``dbias`` implies want_dbias."""
+    B, Hq, Hkv, Nq, Nkv, d = _shapes(q, k, v)
+    _check_tensors(q.dtype, q.device, q=q, k=k, v=v, o=o, lse=lse, do=do)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if dbias is None and want_dbias:
+        dbias = torch.empty((B, Hq, Nq, Nkv), dtype=q.dtype, device=q.device)
+    _check_tensors(q.dtype, q.device, dq=dq, dk=dk, dv=dv)
+    if dq.shape != q.shape or dk.shape != k.shape or dv.shape != v.shape:
+        raise ValueError("dq, dk, dv must have the shapes of q, k, v")
+    if any(t is not None and t.dtype != q.dtype for t in (dq, dk, dv, dbias)):
+        raise ValueError("dq, dk, dv and dbias must have q's dtype")
+    if dbias is not None:
+        _check_tensors(q.dtype, q.device, dbias=dbias)
+        if tuple(dbias.shape) != (B, Hq, Nq, Nkv):
+            raise ValueError(f"dbias must be [B, Hq, Nq, Nkv] = {(B, Hq, Nq, Nkv)}")
+    bp, sb, sh, sq = _bias_args(bias, q, k)
+    need = bwd_workspace_bytes(B, Hq, Hkv, Nq, Nkv, d, causal, q.dtype, "separate")
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    lib = load()
+    _check(lib.fa_bwd_bias_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nkv, d, float(scale),
+                                   int(bool(causal)), FA_DTYPE[q.dtype], bp, sb, sh, sq,
+                                   _ptr(dbias), float(dropout_p), int(seed) & (2 ** 64 - 1),
+                                   _ptr(ws), ws.numel(), _stream(q.device)),
+           "fa_bwd_bias_dropout")
+    return dq, dk, dv, dbias
 
 
 # --- raw HIP events (timing on the exact stream the kernels run on) -------------

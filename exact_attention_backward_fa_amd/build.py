@@ -36,6 +36,10 @@ HEAD_DIMS = (32, 64, 96, 128, 256)
 INSTANCES = [(dt, d, c) for dt in (0, 1) for d in HEAD_DIMS for c in (0, 1)]
 # The fused atomic dK/dV/dQ kernel is built for these head dims only.
 ATOMIC_HEAD_DIMS = (64, 128)
+# Feature sets (1: additive score bias and its gradient, 2: bias and dropout of P)
+# are built for these head dims; every head dim has the plain set 0.
+FEATURE_HEAD_DIMS = (64, 128)
+FEATURES = (1, 2)
 # Backward kernel families compiled per instance (FA_KIND in fa_bwd_inst.hip).
 BWD_KINDS = {0: "pre", 1: "dkdv", 2: "dq", 3: "atomic"}
 
@@ -70,13 +74,19 @@ class Unit:
 def units() -> List[Unit]:
     out = [Unit(os.path.splitext(s)[0], s) for s in SOURCES]
     for dt, d, c in INSTANCES:
-        out.append(Unit(f"fwd_{dt}_{d}_{c}", "fa_fwd_inst.hip",
-                        [("FA_DT", dt), ("FA_D", d), ("FA_CAUSAL", c)]))
-        for kind, kname in BWD_KINDS.items():
-            if kname == "atomic" and d not in ATOMIC_HEAD_DIMS:
-                continue
-            out.append(Unit(f"{kname}_{dt}_{d}_{c}", "fa_bwd_inst.hip",
-                            [("FA_DT", dt), ("FA_D", d), ("FA_CAUSAL", c), ("FA_KIND", kind)]))
+        fts = (0,) + (FEATURES if d in FEATURE_HEAD_DIMS else ())
+        for ft in fts:
+            sfx = f"{dt}_{d}_{c}" + (f"_f{ft}" if ft else "")
+            out.append(Unit(f"fwd_{sfx}", "fa_fwd_inst.hip",
+                            [("FA_DT", dt), ("FA_D", d), ("FA_CAUSAL", c), ("FA_FT", ft)]))
+            for kind, kname in BWD_KINDS.items():
+                if kname == "atomic" and (d not in ATOMIC_HEAD_DIMS or ft):
+                    continue
+                if kname == "pre" and ft:
+                    continue
+                out.append(Unit(f"{kname}_{sfx}", "fa_bwd_inst.hip",
+                                [("FA_DT", dt), ("FA_D", d), ("FA_CAUSAL", c), ("FA_FT", ft),
+                                 ("FA_KIND", kind)]))
     return out
 
 

@@ -75,13 +75,43 @@ static int resolve_dq_mode(const Problem& pb, int mode) {
   return FA_DQ_SEPARATE;
 }
 
-int bwd_validate(const BwdCall& c, int dq_mode, size_t* workspace_need) {
+// Checks the score bias, its gradient and the dropout arguments; fills *x.
+static int check_extras(const Problem& pb, const void* bias, long long sb, long long sh,
+                        long long sq, void* dbias, float dropout_p, unsigned long long seed,
+                        Extras* x) {
+  if (!(dropout_p >= 0.f && dropout_p <= 1.f)) return FA_ERR_DROPOUT;  // NaN fails too
+  // keep threshold T = floor((1 - p) * 256 + 1/2), float arithmetic
+  const float t = floorf((1.0f - dropout_p) * 256.0f + 0.5f);
+  x->keep_t = (unsigned)fminf(fmaxf(t, 0.f), 256.f);
+  x->seed = seed;
+  x->bias = bias;
+  x->dbias = dbias;
+  x->bias_sb = bias ? sb : 0;
+  x->bias_sh = bias ? sh : 0;
+  x->bias_sq = bias ? sq : 0;
+  if (bias) {
+    // 16-byte aligned rows (the tiles are copied in 16-byte pieces); strides keep
+    // a tile's offsets within 32 bits
+    if (((uintptr_t)bias & 15u) != 0) return FA_ERR_ALIGN;
+    if (sb < 0 || sh < 0 || sq < 0 || (sb & 7) || (sh & 7) || (sq & 7) || sq > (1ll << 22))
+      return FA_ERR_BIAS;
+  }
+  if (dbias && ((uintptr_t)dbias & 15u) != 0) return FA_ERR_ALIGN;
+  // dBias rows of a 128-query work item are addressed with 32-bit byte offsets
+  if (dbias && pb.Nkv > (1 << 22)) return FA_ERR_BIAS;
+  if (x->ft() != FT_PLAIN && !feature_head_dim(pb.d)) return FA_ERR_HEADDIM;
+  return FA_OK;
+}
+
+int bwd_validate(const BwdCall& c, int dq_mode, size_t* workspace_need, const Extras* x) {
   Problem pb;
   const int st = check_problem(c.B, c.Hq, c.Hkv, c.Nq, c.Nkv, c.d, c.scale, c.dtype, &pb);
   if (st != FA_OK) return st;
   pb.causal = c.causal != 0;
   if (dq_mode != FA_DQ_AUTO && dq_mode != FA_DQ_ATOMIC && dq_mode != FA_DQ_SEPARATE)
     return FA_ERR_MODE;
+  // the score bias and dropout run on the separate dQ path only
+  if (x && x->ft() != FT_PLAIN && dq_mode == FA_DQ_ATOMIC) return FA_ERR_MODE;
   const size_t nq = (size_t)c.B * c.Hq * c.Nq * c.d, nk = (size_t)c.B * c.Hkv * c.Nkv * c.d;
   const size_t nrows = (size_t)c.B * c.Hq * c.Nq;
   // dK/dV are written whenever they have elements (zeros when N_q = 0).
@@ -98,9 +128,9 @@ int bwd_validate(const BwdCall& c, int dq_mode, size_t* workspace_need) {
 }
 
 int bwd_checked(const BwdCall& c, int dq_mode, void* ev_begin, void* ev_end, void* workspace,
-                size_t workspace_bytes, void* stream) {
+                size_t workspace_bytes, void* stream, const Extras* x) {
   size_t need = 0;
-  const int st = bwd_validate(c, dq_mode, &need);
+  const int st = bwd_validate(c, dq_mode, &need, x);
   if (st != FA_OK) return st;
   Problem pb;
   (void)check_problem(c.B, c.Hq, c.Hkv, c.Nq, c.Nkv, c.d, c.scale, c.dtype, &pb);
@@ -130,6 +160,7 @@ int bwd_checked(const BwdCall& c, int dq_mode, void* ev_begin, void* ev_end, voi
   a.lse2 = L.total ? reinterpret_cast<float*>(ws + L.lse2_off) : nullptr;
   a.dq_acc = (L.total && atomic) ? reinterpret_cast<float*>(ws + L.dqacc_off) : nullptr;
   a.sched = L.total ? reinterpret_cast<int*>(ws + L.sched_off) : nullptr;
+  if (x) a.x = *x;
 
   hipStream_t s = (hipStream_t)stream;
   if (nrows == 0 && nk == 0) return FA_OK;  // nothing to compute; no HIP call at all
@@ -141,6 +172,7 @@ int bwd_checked(const BwdCall& c, int dq_mode, void* ev_begin, void* ev_end, voi
   if (atomic) {
     if (launch_bwd_dq_convert(a, s) != hipSuccess) return FA_ERR_HIP;
   } else {
+    if (launch_dbias_fill(a, s) != hipSuccess) return FA_ERR_HIP;
     if (launch_bwd_dq(a, s) != hipSuccess) return FA_ERR_HIP;
   }
   return FA_OK;
@@ -177,13 +209,18 @@ const char* fa_status_string(int status) {
     case FA_ERR_NULLPTR: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (B, Hq, Hkv, N_q, N_kv), Hq % Hkv != 0, or a size limit exceeded";
     case FA_ERR_HEADDIM:
-      return "head dimension d must be 32, 64, 96, 128 or 256 (the atomic dQ path: 64 or 128)";
+      return "head dimension d must be 32, 64, 96, 128 or 256 (the atomic dQ path, a score bias "
+             "and dropout: 64 or 128)";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "softmax_scale must be finite and > 0";
     case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned, or smaller than required";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     case FA_ERR_HIP: return "a HIP kernel launch failed";
     case FA_ERR_MODE: return "unknown dq_mode";
+    case FA_ERR_BIAS:
+      return "bias strides must be >= 0, multiples of 8 elements, the row stride <= 2^22, and "
+             "N_kv <= 2^22 when dbias is requested";
+    case FA_ERR_DROPOUT: return "dropout_p must be in [0, 1]";
     case FA_ERR_SCRATCH:
       return "the problem needs more scratch than fa_bwd_noalloc holds (FA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
@@ -192,9 +229,21 @@ const char* fa_status_string(int status) {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
            int Nq, int Nkv, int d, float softmax_scale, int causal, int dtype, void* stream) {
+  return fa_fwd_bias_dropout(q, k, v, o, lse, B, Hq, Hkv, Nq, Nkv, d, softmax_scale, causal, dtype,
+                             nullptr, 0, 0, 0, 0.f, 0, stream);
+}
+
+int fa_fwd_bias_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int Hq, int Hkv, int Nq, int Nkv, int d, float softmax_scale, int causal,
+                        int dtype, const void* bias, long long bias_stride_b,
+                        long long bias_stride_h, long long bias_stride_q, float dropout_p,
+                        unsigned long long seed, void* stream) {
   Problem pb;
   FA_TRY(check_problem(B, Hq, Hkv, Nq, Nkv, d, softmax_scale, dtype, &pb));
   pb.causal = causal != 0;
+  Extras x;
+  FA_TRY(check_extras(pb, bias, bias_stride_b, bias_stride_h, bias_stride_q, nullptr, dropout_p,
+                      seed, &x));
   const size_t nq = (size_t)B * Hq * Nq * d, nk = (size_t)B * Hkv * Nkv * d;
   const size_t nrows = (size_t)B * Hq * Nq;
   // K and V are read only when some query row exists.
@@ -204,7 +253,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
   FA_TRY(check_ptr(v, nk_used));
   FA_TRY(check_ptr(o, nq));
   FA_TRY(check_ptr(lse, nrows));
-  FwdArgs a{pb, q, k, v, o, lse};
+  FwdArgs a{pb, q, k, v, o, lse, x};
   if (nrows == 0) return FA_OK;  // nothing to compute; no HIP call at all
   (void)hipGetLastError();
   if (launch_fwd(a, (hipStream_t)stream) != hipSuccess) return FA_ERR_HIP;
@@ -235,6 +284,24 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const 
               void* stream) {
   BwdCall c{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, d, softmax_scale, causal, dtype};
   return fa::bwd_checked(c, dq_mode, ev_begin, ev_end, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_bias_dropout(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                        int Hq, int Hkv, int Nq, int Nkv, int d, float softmax_scale, int causal,
+                        int dtype, const void* bias, long long bias_stride_b,
+                        long long bias_stride_h, long long bias_stride_q, void* dbias,
+                        float dropout_p, unsigned long long seed, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Problem pb;
+  FA_TRY(check_problem(B, Hq, Hkv, Nq, Nkv, d, softmax_scale, dtype, &pb));
+  pb.causal = causal != 0;
+  Extras x;
+  FA_TRY(check_extras(pb, bias, bias_stride_b, bias_stride_h, bias_stride_q, dbias, dropout_p, seed,
+                      &x));
+  if (dbias) FA_TRY(check_ptr(dbias, (size_t)B * Hq * Nq * Nkv));
+  BwdCall c{q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nkv, d, softmax_scale, causal, dtype};
+  return bwd_checked(c, FA_DQ_SEPARATE, nullptr, nullptr, workspace, workspace_bytes, stream, &x);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

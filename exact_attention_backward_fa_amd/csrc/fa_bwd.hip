@@ -23,6 +23,28 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 }
 
 
+// dBias entries the dQ pass never visits: under the causal mask, (row i, key j)
+// with j > i + N_kv - N_q is masked, P and dS are zero there, and whole key tiles
+// of them are skipped.  Block (x, y) writes zeros to keys 2048 y .. of row x.
+__global__ __launch_bounds__(256) void dbias_fill_masked_kernel(uint16_t* __restrict__ dbias, int Nq,
+                                                                int Nkv, int off) {
+  const size_t row = blockIdx.x;  // over B * Hq * N_q
+  const int i = (int)(row % (size_t)Nq);
+  const int first = max(0, i + off + 1);  // first masked key of the row
+  uint16_t* dst = dbias + row * (size_t)Nkv;
+  for (int j = blockIdx.y * 2048 + threadIdx.x; j < min(Nkv, (int)(blockIdx.y + 1) * 2048); j += 256)
+    if (j >= first) dst[j] = 0;
+}
+
+hipError_t launch_dbias_fill(const BwdArgs& a, hipStream_t s) {
+  const size_t rows = (size_t)a.pb.B * a.pb.Hq * a.pb.Nq;
+  if (!a.pb.causal || a.x.dbias == nullptr || rows == 0 || a.pb.Nkv == 0) return hipSuccess;
+  const dim3 grid((unsigned)rows, (unsigned)((a.pb.Nkv + 2047) / 2048));
+  hipLaunchKernelGGL(dbias_fill_masked_kernel, grid, dim3(256), 0, s, static_cast<uint16_t*>(a.x.dbias),
+                     a.pb.Nq, a.pb.Nkv, a.pb.Nkv - a.pb.Nq);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 int device_cu_count() {
   static int cached[64] = {0};
@@ -37,33 +59,35 @@ int device_cu_count() {
 
 // ---------------------------------------------------------------------------
 // Dispatch.
+#define FA_TPARAMS decltype(dt)::value, decltype(d)::value, decltype(c)::value
+
 hipError_t launch_bwd_pre(const BwdArgs& a, bool zero_dq_acc, hipStream_t s) {
   if ((size_t)a.pb.B * a.pb.Hq * a.pb.Nq == 0) return hipSuccess;
-  FA_DISPATCH(a.pb, run_pre, a, zero_dq_acc, s);
-  return hipErrorInvalidValue;
-}
-
-// The fused atomic kernel exists for d = 64 and 128 (the API rejects the atomic
-// path for other head dims).
-template <int DT, int D, bool CAUSAL>
-static hipError_t run_dkdv_atomic_if_built(const BwdArgs& a, hipStream_t s) {
-  if constexpr (atomic_head_dim(D)) return run_dkdv_atomic<DT, D, CAUSAL>(a, s);
-  (void)a;
-  (void)s;
-  return hipErrorInvalidValue;
+  return dispatch(a.pb, FT_PLAIN, [&](auto dt, auto d, auto c, auto) {
+    return run_pre<FA_TPARAMS>(a, zero_dq_acc, s);
+  });
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, bool atomic_dq, hipStream_t s) {
   if ((size_t)a.pb.B * a.pb.Nkv == 0) return hipSuccess;
-  if (atomic_dq) FA_DISPATCH(a.pb, run_dkdv_atomic_if_built, a, s);
-  FA_DISPATCH(a.pb, run_dkdv, a, s);
-  return hipErrorInvalidValue;
+  if (atomic_dq) {
+    // the fused atomic kernel exists for d = 64 and 128 without extras (the API
+    // rejects the atomic path otherwise)
+    return dispatch(a.pb, FT_PLAIN, [&](auto dt, auto d, auto c, auto) -> hipError_t {
+      if constexpr (atomic_head_dim(decltype(d)::value)) return run_dkdv_atomic<FA_TPARAMS>(a, s);
+      return hipErrorInvalidValue;
+    });
+  }
+  return dispatch(a.pb, a.x.ft(), [&](auto dt, auto d, auto c, auto ft) {
+    return run_dkdv<FA_TPARAMS, decltype(ft)::value>(a, s);
+  });
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s) {
   if ((size_t)a.pb.B * a.pb.Nq == 0) return hipSuccess;
-  FA_DISPATCH(a.pb, run_dq, a, s);
-  return hipErrorInvalidValue;
+  return dispatch(a.pb, a.x.ft(), [&](auto dt, auto d, auto c, auto ft) {
+    return run_dq<FA_TPARAMS, decltype(ft)::value>(a, s);
+  });
 }
 
 hipError_t launch_bwd_dq_convert(const BwdArgs& a, hipStream_t s) {

@@ -23,6 +23,14 @@ struct BwdParams {
   int B, Hq, Hkv, Nq, Nkv, G, off;  // off = Nkv - Nq (bottom-right causal offset)
   float scale, scale_log2;
   size_t rows;  // B * Hq * Nq
+  // score bias (null: zero) with element strides, its gradient (null: not wanted),
+  // and dropout (keep iff the element's random byte < keep_t; kept P scaled by
+  // drop_scale = 256 / keep_t; Philox key = seed words)
+  const uint16_t* bias;
+  long long bias_sb, bias_sh, bias_sq;
+  uint16_t* dbias;
+  unsigned keep_t, seed_lo, seed_hi;
+  float drop_scale;
 };
 
 inline BwdParams make_params(const BwdArgs& a) {
@@ -50,6 +58,15 @@ inline BwdParams make_params(const BwdArgs& a) {
   p.scale = a.pb.scale;
   p.scale_log2 = a.pb.scale * kLog2e;
   p.rows = (size_t)a.pb.B * a.pb.Hq * a.pb.Nq;
+  p.bias = static_cast<const uint16_t*>(a.x.bias);
+  p.bias_sb = a.x.bias_sb;
+  p.bias_sh = a.x.bias_sh;
+  p.bias_sq = a.x.bias_sq;
+  p.dbias = static_cast<uint16_t*>(a.x.dbias);
+  p.keep_t = a.x.keep_t;
+  p.seed_lo = (unsigned)(a.x.seed & 0xffffffffu);
+  p.seed_hi = (unsigned)(a.x.seed >> 32);
+  p.drop_scale = a.x.keep_t > 0 ? 256.f / (float)a.x.keep_t : 0.f;
   return p;
 }
 
@@ -113,8 +130,8 @@ struct WorkQueue {
 // Launchers of one template instance; each is explicitly instantiated in its own
 // compilation of fa_bwd_inst.hip.
 template <int DT, int D, bool CAUSAL> hipError_t run_pre(const BwdArgs& a, bool zero, hipStream_t s);
-template <int DT, int D, bool CAUSAL> hipError_t run_dkdv(const BwdArgs& a, hipStream_t s);
-template <int DT, int D, bool CAUSAL> hipError_t run_dq(const BwdArgs& a, hipStream_t s);
+template <int DT, int D, bool CAUSAL, int FT> hipError_t run_dkdv(const BwdArgs& a, hipStream_t s);
+template <int DT, int D, bool CAUSAL, int FT> hipError_t run_dq(const BwdArgs& a, hipStream_t s);
 template <int DT, int D, bool CAUSAL> hipError_t run_dkdv_atomic(const BwdArgs& a, hipStream_t s);
 
 }  // namespace fa

@@ -59,15 +59,18 @@ struct DqSteps {
   using Flush = StepPlan<0, QT, 2 * NK, QT, 0, QT, 0, 1, 1>;
 };
 
-// Resident rows per wave and LDS buffers per head dim: 64 rows (four 16-row
-// tiles) and triple-buffered streamed tiles up to d = 128; at d = 256 the
-// resident operands and accumulators of 64 rows exceed the 512 registers of a
-// lane and three buffers the 160 KB of LDS, so a wave keeps 32 rows and the
-// streamed tiles are double-buffered.
-template <int D>
+// Resident rows per wave and LDS buffers per head dim and feature set: 64 rows
+// (four 16-row tiles) and triple-buffered streamed tiles up to d = 128; at
+// d = 256 the resident operands and accumulators of 64 rows exceed the 512
+// registers of a lane and three buffers the 160 KB of LDS, so a wave keeps 32
+// rows and the streamed tiles are double-buffered.  The bias and dropout
+// instances take the same shape: the bias tiles need the LDS, the bias and
+// dropout work the registers.
+template <int D, int FT = 0>
 struct TileShape {
-  static constexpr int RT = D > 128 ? 2 : 4;    // resident 16-row tiles per wave
-  static constexpr int NBUF = D > 128 ? 2 : 3;  // LDS buffers of the streamed tiles
+  static constexpr bool SMALL = D > 128 || FT != 0;
+  static constexpr int RT = SMALL ? 2 : 4;    // resident 16-row tiles per wave
+  static constexpr int NBUF = SMALL ? 2 : 3;  // LDS buffers of the streamed tiles
 };
 
 // Slots of the non-MFMA work of dK/dV step ST (NC copies in steps 2-3):
@@ -212,20 +215,28 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // 2J+2 and 2J+3 (steps 4 and 5 are steps 0 and 1 of the next tile); a final step
 // issues what is left of the last pair.  Tiles that cross the causal boundary or a
 // ragged end of this wave's block take a masked variant of the softmax.
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int FT>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr int KT = TileShape<D>::RT;  // key tiles of 16 per wave
+  constexpr bool BIAS = FT >= FT_BIAS, DROP = FT == FT_DROPOUT;
+  constexpr int KT = TileShape<D, FT>::RT;  // key tiles of 16 per wave
   constexpr int KW = 16 * KT, BN = 4 * KW, BM = 64, NSB = BM / 16;
   constexpr int NK = D / 32;
-  constexpr int NBUF = TileShape<D>::NBUF;
+  constexpr int NBUF = TileShape<D, FT>::NBUF;
   constexpr int RS = PadTile<D>::RS;
-  constexpr int OPS = 2 * BM * PadTile<D>::GR / 256 + 2;  // copy instructions per fetch per wave
+  // bias tile of a query tile: BM rows x the workgroup's BN keys (4 pad granules a
+  // row: 320-byte rows for BN = 128)
+  using BiasDma = StridedTileDma<BM, BN, 4>;
+  constexpr int BRS = BiasDma::RS;
+  constexpr int BPW = BIAS ? BiasDma::PER_WAVE : 0;
+  // copy instructions per fetch per wave: Q or dO, LSE, -D, bias
+  constexpr int OPS = 2 * BM * PadTile<D>::GR / 256 + 2 + BPW;
   constexpr int LA = 2;                                     // operand lookahead
   // Q and dO of a buffer are one padded tile pair (as are LSE and D), so both are
   // read through the same per-lane address registers with immediate offsets.
   __shared__ __attribute__((aligned(16))) uint16_t sQdO[NBUF][2 * BM * RS];
   static_assert(NBUF * 2 * BM * RS >= 4 * KW * (D + 8), "the output staging must fit the tile buffers");
   __shared__ __attribute__((aligned(16))) float sLD[NBUF][2][BM];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[BIAS ? NBUF : 1][BIAS ? BM * BRS : 8];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
@@ -288,7 +299,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     // copies LSE and -D (identical bytes to the same place).
     using Copy = PadPairDma<D, BM>;
     struct Src {
-      i32x4 t, l, d;  // this wave's Q or dO tile; LSE*log2e; -D
+      i32x4 t, l, d, bs;  // this wave's Q or dO tile; LSE*log2e; -D; bias (bias instances)
     };
     // Fetch cursor: the tile of iteration c_fit (query head c_hh of the group, rows
     // from the start of this wave's Q or dO tile, LSE and -D), moved one iteration
@@ -298,11 +309,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     const float* __restrict__ cl = p.lse2 + row0;
     const float* __restrict__ cd = p.ndelta + row0;
     int c_left = p.Nq - (nqt - 1) * BM, c_hh = 0, c_fit = 0;
+    // bias element offset of the cursor's tile: its first row, this block's first key
+    long long cb = BIAS ? (long long)b * p.bias_sb + (long long)hk * p.G * p.bias_sh +
+                              (long long)(nqt - 1) * BM * p.bias_sq + kv0
+                        : 0;
     auto src_now = [&]() {
       Src sr;
       sr.t = buf_rsrc(ct, c_left * D * 2);
       sr.l = buf_rsrc(cl, c_left * 4);
       sr.d = buf_rsrc(cd, c_left * 4);
+      if constexpr (BIAS) {
+        // rows past N_q and a null bias read zeros (the resource ends there); a row is
+        // read in whole 16-byte pieces, up to N_kv rounded up to 8 elements; a row is
+      // read in whole 16-byte pieces, up to N_kv rounded up to 8 elements
+        const int rows = min(BM, c_left);
+        const int bytes = p.bias ? 2 * ((rows - 1) * (int)p.bias_sq + (((p.Nkv + 7) & ~7) - kv0)) : 0;
+        sr.bs = buf_rsrc(p.bias ? p.bias + cb : p.k, bytes);
+      }
       return sr;
     };
     auto advance = [&]() {
@@ -315,10 +338,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           cl -= back;
           cd -= back;
           c_left += BM;
+          if constexpr (BIAS) cb -= (long long)(p.G - 1) * p.bias_sh + (long long)BM * p.bias_sq;
         } else {
           ct += (size_t)p.Nq * D;
           cl += p.Nq;
           cd += p.Nq;
+          if constexpr (BIAS) cb += p.bias_sh;
         }
       }
     };
@@ -326,14 +351,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int c = 0; c < Copy::PER_WAVE; ++c) voff[c] = Copy::src_offset(c, w, lane);
     const uint32_t wave_off = Copy::lds_wave_offset(w);
+    int voffb[BIAS ? BPW : 1];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int c = 0; c < BPW; ++c) voffb[c] = BiasDma::src_offset(c, w, lane, (int)p.bias_sq);
+    }
     auto copy_part = [&](auto cc, const Src& sr, int buf) {
       constexpr int c = decltype(cc)::value;
       if constexpr (c < Copy::PER_WAVE)
         bdma16<Copy::template lds_offset<c>>(voff[c], sr.t, lds_u32(sQdO[buf]) + wave_off);
       else if constexpr (c == Copy::PER_WAVE)
         bdma4(4 * lane, sr.l, lds_u32(sLD[buf][0]));
-      else
+      else if constexpr (c == Copy::PER_WAVE + 1)
         bdma4(4 * lane, sr.d, lds_u32(sLD[buf][1]));
+      else {
+        constexpr int cb_ = c - Copy::PER_WAVE - 2;
+        bdma16<BiasDma::template lds_offset<cb_>>(voffb[cb_], sr.bs,
+                                                  lds_u32(sB[buf]) + BiasDma::lds_wave_offset(w));
+      }
     };
     auto copy_all = [&](const Src& sr, int buf) {
       static_for<OPS>([&](auto cc) { copy_part(cc, sr, buf); });
@@ -381,7 +416,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       }
     };
 
-    auto compute = [&](int cur, int nxt, auto mask_c, int q0, const Src& fsrc, int fbuf) {
+    auto compute = [&](int cur, int nxt, auto mask_c, int q0, int hq, const Src& fsrc, int fbuf) {
       constexpr bool MASK = decltype(mask_c)::value;
       const uint16_t* Qt = sQdO[cur];
       const uint16_t* Qp = sQdO[prev];
@@ -391,6 +426,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       f32x4 sc[KT];   // S, then P, of the current sub-block, per key tile
       f32x4 dp[KT];   // dP, then dS
       f32x4 lq, dn;   // LSE*log2e and -D of the current sub-block's rows
+      u32x2 bv[KT];   // bias of the current sub-block per key tile (rows in elements)
+      f32x4 zf[KT];   // dropout keep factors of the current sub-block per key tile
+      (void)hq;
       const int keyl = kvw + l16;    // key of this lane's column in key tile 0
       const int qrow = q0 + 4 * j4;  // query row of element 0 in sub-block 0
 
@@ -398,13 +436,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       // packed sub-block st into half st % 2 of pair st / 2
       auto pack_p = [&](auto stc, auto ktc) {
         constexpr int st = decltype(stc)::value, kt = decltype(ktc)::value;
-        const u32x2 v = pack_c4<DT>(sc[kt]);
+        // dV is weighted by the kept probabilities P o Z
+        u32x2 v = pack_c4<DT>(DROP ? sc[kt] * zf[kt] : sc[kt]);
+        pin<FT != FT_PLAIN>(v);
         pa[st / 2][kt][2 * (st % 2)] = v[0];
         pa[st / 2][kt][2 * (st % 2) + 1] = v[1];
       };
       auto pack_ds = [&](auto stc, auto ktc) {
         constexpr int st = decltype(stc)::value, kt = decltype(ktc)::value;
-        const u32x2 v = pack_c4<DT>(dp[kt]);
+        u32x2 v = pack_c4<DT>(dp[kt]);
+        pin<FT != FT_PLAIN>(v);
         sa[st / 2][kt][2 * (st % 2)] = v[0];
         sa[st / 2][kt][2 * (st % 2) + 1] = v[1];
       };
@@ -412,7 +453,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       auto p_item = [&](auto ec, auto st_c) {
         constexpr int e = decltype(ec)::value, st = decltype(st_c)::value;
         constexpr int kt = e / 4, i = e % 4;
-        float v = sc[kt][i] * p.scale_log2 - lq[i];
+        if constexpr (DROP && i == 0) {
+          // one Philox call for the 4 x 4 block (keys key & ~3 .., queries of rows
+          // 0..3 of this lane's row group): word i is row i, byte key % 4 the key
+          const int key = keyl + 16 * kt, q = qrow + 16 * st;
+          const u32x4 ctr = {(uint32_t)key >> 2, (uint32_t)q >> 2, (uint32_t)hq, (uint32_t)b};
+          const u32x4 x = philox4x32_10(ctr, p.seed_lo, p.seed_hi);
+          const int byte = key & 3;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) zf[kt][r] = keep_factor(x[r], byte, p.keep_t, p.drop_scale);
+        }
+        float v;
+        if constexpr (BIAS)
+          v = fmaf(sc[kt][i], p.scale_log2, fmaf(elem4<DT>(bv[kt], i), kLog2e, -lq[i]));
+        else
+          v = sc[kt][i] * p.scale_log2 - lq[i];
         if constexpr (MASK) {
           const int key = keyl + 16 * kt, q = qrow + 16 * st + i;
           if (key >= p.Nkv || q >= p.Nq || (CAUSAL && key > q + p.off)) v = -INFINITY;
@@ -424,6 +479,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         constexpr int st = decltype(stc)::value;
         lq = *reinterpret_cast<const f32x4*>(&Lt[16 * st + 4 * j4]);
         dn = *reinterpret_cast<const f32x4*>(&Dtl[16 * st + 4 * j4]);
+        if constexpr (BIAS) {
+          // the bias of the 16x16 S tiles of this sub-block in their C layout: one
+          // transposed read per key tile (lane l16 addresses row l16 / 4 of its row
+          // group and receives column l16)
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+            bv[kt] = lds_tr16(sB[cur] + (16 * st + 4 * j4 + (l16 >> 2)) * BRS + KW * w + 16 * kt +
+                              4 * (l16 & 3));
+        }
         if constexpr (st == 2) {
           // Mid-tile: every wave is past steps 0-1 (its last reads of the previous
           // buffer) and, once its own copies have landed, the next tile is complete
@@ -462,7 +526,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           constexpr int J = st < 2 ? 1 : 0, nn = (st % 2) * NK + o;
           Mx<DT>::acc16a(dk[kt][nn], sa[J][kt], op);
         } else if constexpr (k == 2) {
-          if constexpr (o == 0)
+          // dP - D (dropout: dP alone, as the keep factors apply to dP before D)
+          if constexpr (o == 0 && DROP)
+            dp[kt] = Mx<DT>::first16(op, vb[kt][o]);
+          else if constexpr (o == 0)
             dp[kt] = Mx<DT>::first16c(op, vb[kt][o], dn);
           else
             Mx<DT>::acc16(dp[kt], op, vb[kt][o]);
@@ -496,7 +563,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           constexpr int kt = decltype(ktc)::value;
           static_for<4>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            if constexpr (PL.mul[kt][i] == m) dp[kt][i] = sc[kt][i] * dp[kt][i];  // the dP product starts from -D
+            if constexpr (PL.mul[kt][i] == m) {
+              if constexpr (DROP)
+                dp[kt][i] = sc[kt][i] * fmaf(zf[kt][i], dp[kt][i], dn[i]);  // P o (Z o dP - D)
+              else
+                dp[kt][i] = sc[kt][i] * dp[kt][i];  // the dP product starts from -D
+            }
           });
           if constexpr (PL.pack_ds[kt] == m) pack_ds(stp(), ktc);
         });
@@ -585,6 +657,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
         const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
         const int q0 = (nqt - 1 - it / p.G) * BM;
+        const int hq = hk * p.G + it % p.G;  // query head of this iteration
         if constexpr (VAR == 0) {
           wait_vmem();
           tile_barrier();
@@ -594,8 +667,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
             tile_barrier();
           }
         }
-        if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), q0, fsrc, fbuf);
-        if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), q0, fsrc, fbuf);
+        if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), q0, hq, fsrc, fbuf);
+        if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), q0, hq, fsrc, fbuf);
         prev = cur;
         cur = nxt;
       }
@@ -637,16 +710,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 //
 // Step st issues the MFMA stream  S^T_st | dQ half | dP^T_st  with dS_{st-1}
 // computed under S^T_st and P_st under the dQ half and dP^T_st.
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int FT>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
-  constexpr int QT = TileShape<D>::RT;  // query tiles of 16 per wave
+  constexpr bool BIAS = FT >= FT_BIAS, DROP = FT == FT_DROPOUT;
+  constexpr int QT = TileShape<D, FT>::RT;  // query tiles of 16 per wave
   constexpr int QW = 16 * QT, BM = 4 * QW, BN = 64, NSB = BN / 16;
   constexpr int NK = D / 32;
-  constexpr int NBUF = TileShape<D>::NBUF;  // key/value tiles fetched NBUF - 1 ahead
+  constexpr int NBUF = TileShape<D, FT>::NBUF;  // key/value tiles fetched NBUF - 1 ahead
   constexpr int RS = PadTile<D>::RS;
-  constexpr int OPS = 2 * BN * PadTile<D>::GR / 256;  // copy instructions per fetch per wave
+  // bias tile of a key tile: the workgroup's BM queries x BN keys (2 pad granules a
+  // row: 160-byte rows)
+  using BiasDma = StridedTileDma<BM, BN, 2>;
+  constexpr int BRS = BiasDma::RS;
+  constexpr int BPW = BIAS ? BiasDma::PER_WAVE : 0;
+  constexpr int KVPW = 2 * BN * PadTile<D>::GR / 256;
+  constexpr int OPS = KVPW + BPW;  // copy instructions per fetch per wave: K or V, bias
   constexpr int LA = 2;
   __shared__ __attribute__((aligned(16))) uint16_t sKV[NBUF][2 * BN * RS];  // K, V: a padded pair
+  __shared__ __attribute__((aligned(16))) uint16_t sB[BIAS ? NBUF : 1][BIAS ? BM * BRS : 8];
   static_assert(NBUF * 2 * BN * RS >= 4 * QW * (D + 8), "the output staging must fit the tile buffers");
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -712,22 +793,73 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     // copy the K tile, waves 2-3 the V tile, through a buffer resource based at the
     // tile's first row; rows past N_kv arrive as zeros (and are masked in the math).
     using Copy = PadPairDma<D, BN>;
+    static_assert(Copy::PER_WAVE == KVPW, "key/value copies per wave");
     const uint16_t* __restrict__ tsrc = w < 2 ? K : V;
+    struct Src {
+      i32x4 t, bs;  // this wave's K or V tile; bias tile (bias instances)
+    };
+    // bias element offset of this item's first query row (key 0)
+    const long long bq0 = BIAS ? (long long)b * p.bias_sb + (long long)h * p.bias_sh +
+                                     (long long)q0 * p.bias_sq
+                               : 0;
     auto src_of = [&](int kt) {
       const int k0 = min(kt, nkt - 1) * BN;
-      return buf_rsrc(tsrc + (size_t)k0 * D, (p.Nkv - k0) * D * 2);
+      Src sr;
+      sr.t = buf_rsrc(tsrc + (size_t)k0 * D, (p.Nkv - k0) * D * 2);
+      if constexpr (BIAS) {
+        // rows past N_q and a null bias read zeros (the resource ends there); a row is
+        // read in whole 16-byte pieces, up to N_kv rounded up to 8 elements; a row is
+      // read in whole 16-byte pieces, up to N_kv rounded up to 8 elements
+        const int rows = min(BM, p.Nq - q0);
+        const int bytes = p.bias ? 2 * ((rows - 1) * (int)p.bias_sq + (((p.Nkv + 7) & ~7) - k0)) : 0;
+        sr.bs = buf_rsrc(p.bias ? p.bias + bq0 + k0 : p.k, bytes);
+      }
+      return sr;
     };
     int voff[Copy::PER_WAVE];
 #pragma unroll
     for (int c = 0; c < Copy::PER_WAVE; ++c) voff[c] = Copy::src_offset(c, w, lane);
     const uint32_t wave_off = Copy::lds_wave_offset(w);
-    auto copy_part = [&](auto cc, const i32x4& sr, int buf) {
+    int voffb[BIAS ? BPW : 1];
+    if constexpr (BIAS) {
+#pragma unroll
+      for (int c = 0; c < BPW; ++c) voffb[c] = BiasDma::src_offset(c, w, lane, (int)p.bias_sq);
+    }
+    auto copy_part = [&](auto cc, const Src& sr, int buf) {
       constexpr int c = decltype(cc)::value;
-      bdma16<Copy::template lds_offset<c>>(voff[c], sr, lds_u32(sKV[buf]) + wave_off);
+      if constexpr (c < KVPW) {
+        bdma16<Copy::template lds_offset<c>>(voff[c], sr.t, lds_u32(sKV[buf]) + wave_off);
+      } else {
+        constexpr int cb_ = c - KVPW;
+        bdma16<BiasDma::template lds_offset<cb_>>(voffb[cb_], sr.bs,
+                                                  lds_u32(sB[buf]) + BiasDma::lds_wave_offset(w));
+      }
     };
     auto copy_all = [&](int kt, int buf) {
-      const i32x4 sr = src_of(kt);
+      const Src sr = src_of(kt);
       static_for<OPS>([&](auto cc) { copy_part(cc, sr, buf); });
+    };
+    // dS^T of a finished sub-block (packed: keys key0 .. key0 + 3 of query q) into
+    // dBias = dS, row q of this head, through a resource over this item's rows:
+    // rows past N_q fall past its end, and elements with a key past N_kv, or of the
+    // sub-block "before" the first tile (key0 < 0, all zeros), get an offset past
+    // it, so no branch splits the MFMA stream (which would make the register
+    // allocator move the AGPR accumulators).
+    const i32x4 dbr = BIAS && p.dbias
+                          ? buf_rsrc(p.dbias + (qbase + q0) * (size_t)p.Nkv,
+                                     2 * min(BM, p.Nq - q0) * p.Nkv)
+                          : buf_rsrc(p.k, 0);
+    auto store_dbias = [&](const u32x2& v, int q, int key0) {
+      const int base = 2 * ((q - q0) * p.Nkv + key0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool ok = key0 + r >= 0 && key0 + r < p.Nkv;
+        const int off = ok ? base + 2 * r : 0x7ffffff0;
+        if (r & 1)
+          bstore16_hi(v[r >> 1], off, dbr);
+        else
+          bstore16_lo(v[r >> 1], off, dbr);
+      }
     };
 
     // Carried from tile to tile: the first LA operands of the next tile, P^T and
@@ -739,13 +871,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     f32x4 sc[2][QT];  // S^T, then P^T, of sub-block st in sc[st % 2], per query tile
     f32x4 dp[QT];     // dP^T, then dS^T, of the sub-block being finished
     u32x4 da[2][QT];  // dS A operands of sub-block pair J, per query tile
+    f32x4 zf[2][QT];  // dropout keep factors of sub-block st in zf[st % 2]
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       sc[1][t] = zero4();
       dp[t] = zero4();
       da[1][t] = zero_u4();
+      zf[1][t] = zero4();
     }
-    int prev = 0;  // buffer of the previous tile
+    int prev = 0;     // buffer of the previous tile
+    int kv_last = 0;  // first key of the last computed tile
 
     // Operand o of step st of a tile in buffer K_ (K, then V) whose previous tile is
     // in buffer Kp_ (the operand order of DqSteps).  Stage 1: half st % 2 of the dQ
@@ -767,13 +902,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       }
     };
 
-    auto compute = [&](int cur, int nxt, auto mask_c, int kv0, const i32x4& fsrc, int fbuf) {
+    auto compute = [&](int cur, int nxt, auto mask_c, int kv0, const Src& fsrc, int fbuf) {
       constexpr bool MASK = decltype(mask_c)::value;
       const uint16_t* Kt = sKV[cur];
       const uint16_t* Kp = sKV[prev];
       const uint16_t* Kn = sKV[nxt];
       const int krow = kv0 + 4 * j4;  // key of element 0 in sub-block 0
       const int qcol = qw + l16;      // query of this lane's column in query tile 0
+      u32x2 bv[QT];  // bias of the current sub-block per query tile (keys in elements)
 
       // dS of sub-block sb (kept in sc[cp], dp), item e of 5 QT: per query tile four
       // products, then the packed tile into its half of the pair's A operand
@@ -781,9 +917,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         constexpr int e = decltype(ec)::value, cp = decltype(cp_c)::value, sb = decltype(sb_c)::value;
         constexpr int t = e / 5, i = e % 5;
         if constexpr (i == 4) {
-          const u32x2 v = pack_c4<DT>(dp[t]);
+          u32x2 v = pack_c4<DT>(dp[t]);
+          pin<FT != FT_PLAIN>(v);
           da[sb / 2][t][2 * (sb % 2)] = v[0];
           da[sb / 2][t][2 * (sb % 2) + 1] = v[1];
+          if constexpr (BIAS) {
+            // the finished sub-block is sub-block sb of this tile, or the last one of
+            // the previous tile (step 0); without dBias the resource is empty
+            store_dbias(v, qcol + 16 * t, (sb == NSB - 1 ? kv0 - BN : kv0) + 16 * sb + 4 * j4);
+          }
+        } else if constexpr (DROP) {
+          dp[t][i] = sc[cp][t][i] * fmaf(zf[cp][t][i], dp[t][i], nd[t][i]);  // P o (Z o dP - D)
         } else {
           dp[t][i] = sc[cp][t][i] * dp[t][i];  // dP - D: the dP^T product starts from -D
         }
@@ -791,7 +935,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       auto p_item = [&](auto ec, auto st_c) {
         constexpr int e = decltype(ec)::value, st = decltype(st_c)::value, cs = st & 1;
         constexpr int t = e / 4, i = e % 4;
-        float v = sc[cs][t][i] * p.scale_log2 - lq[t];
+        if constexpr (DROP && i == 0) {
+          // one Philox call for the 4 x 4 block (queries q & ~3 .., keys of this
+          // lane's 4-key group): word q % 4 is this lane's query, byte r key r
+          const u32x4 ctr = {(uint32_t)(krow + 16 * st) >> 2, (uint32_t)(qcol + 16 * t) >> 2,
+                             (uint32_t)h, (uint32_t)b};
+          const u32x4 x = philox4x32_10(ctr, p.seed_lo, p.seed_hi);
+          const int qi = l16 & 3;
+          const uint32_t word = qi == 0 ? x[0] : qi == 1 ? x[1] : qi == 2 ? x[2] : x[3];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) zf[cs][t][r] = keep_factor(word, r, p.keep_t, p.drop_scale);
+        }
+        float v;
+        if constexpr (BIAS)
+          v = fmaf(sc[cs][t][i], p.scale_log2, fmaf(elem4<DT>(bv[t], i), kLog2e, -lq[t]));
+        else
+          v = sc[cs][t][i] * p.scale_log2 - lq[t];
         if constexpr (MASK) {
           const int key = krow + 16 * st + i, q = qcol + 16 * t;
           if (key >= p.Nkv || (CAUSAL && key > q + p.off)) v = -INFINITY;
@@ -802,6 +961,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       using Steps = DqSteps<NK, QT>;
       auto begin = [&](auto stc) {
         constexpr int st = decltype(stc)::value;
+        if constexpr (BIAS) {
+          // bias of this sub-block: 4 keys of this lane's query per query tile
+#pragma unroll
+          for (int t = 0; t < QT; ++t)
+            bv[t] = *reinterpret_cast<const u32x2*>(sB[cur] + (QW * w + 16 * t + l16) * BRS + 16 * st + 4 * j4);
+        }
         if constexpr (st == 2) {
           // Mid-tile: every wave is past step 0 (its last reads of the previous
           // buffer) and, once its own copies have landed, the next tile is complete
@@ -835,8 +1000,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
           constexpr int J = st < 2 ? 1 : 0, t = loc % QT, nn = (st % 2) * NK + loc / QT;
           Mx<DT>::acc16a(acc[t][nn], da[J][t], op);
         } else {
+          // dP^T - D (dropout: dP^T alone, as the keep factors apply to dP before D)
           constexpr int s = loc / QT, t = loc % QT;
-          if constexpr (s == 0)
+          if constexpr (s == 0 && DROP)
+            dp[t] = Mx<DT>::first16(op, db[t][s]);
+          else if constexpr (s == 0)
             dp[t] = Mx<DT>::first16c(op, db[t][s], nd[t]);
           else
             Mx<DT>::acc16(dp[t], op, db[t][s]);
@@ -874,6 +1042,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
           const u32x2 v = pack_c4<DT>(dp[t]);
           da[1][t][2] = v[0];
           da[1][t][3] = v[1];
+          if constexpr (BIAS) store_dbias(v, qw + l16 + 16 * t, kv_last + 16 * (NSB - 1) + 4 * j4);
+        } else if constexpr (DROP) {
+          dp[t][i] = sc[1][t][i] * fmaf(zf[1][t][i], dp[t][i], nd[t][i]);
         } else {
           dp[t][i] = sc[1][t][i] * dp[t][i];
         }
@@ -925,7 +1096,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       for (; kt < end; ++kt) {
         const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
         const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
-        const i32x4 fsrc = src_of(kt + NBUF - 1);
+        const Src fsrc = src_of(kt + NBUF - 1);
         if constexpr (VAR == 0) {
           wait_vmem();
           tile_barrier();
@@ -937,6 +1108,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         }
         if constexpr (VAR == 1) compute(cur, nxt, std::true_type(), kt * BN, fsrc, fbuf);
         if constexpr (VAR == 2) compute(cur, nxt, std::false_type(), kt * BN, fsrc, fbuf);
+        if constexpr (VAR != 0) kv_last = kt * BN;
         prev = cur;
         cur = nxt;
       }
@@ -970,25 +1142,25 @@ hipError_t run_pre(const BwdArgs& a, bool zero, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int FT>
 hipError_t run_dkdv(const BwdArgs& a, hipStream_t s) {
   BwdParams p = make_params(a);
-  constexpr int BN = 4 * 16 * TileShape<D>::RT;  // keys per work item
+  constexpr int BN = 4 * 16 * TileShape<D, FT>::RT;  // keys per work item
   const int items = ((a.pb.Nkv + BN - 1) / BN) * a.pb.Hkv * a.pb.B;
   const int ncu = device_cu_count();
   const dim3 grid((unsigned)(p.sched && ncu > 0 && ncu < items ? ncu : items));
-  hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<DT, D, CAUSAL, FT>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int FT>
 hipError_t run_dq(const BwdArgs& a, hipStream_t s) {
   BwdParams p = make_params(a);
-  constexpr int BM = 4 * 16 * TileShape<D>::RT;  // queries per work item
+  constexpr int BM = 4 * 16 * TileShape<D, FT>::RT;  // queries per work item
   const int items = ((a.pb.Nq + BM - 1) / BM) * a.pb.Hq * a.pb.B;
   const int ncu = device_cu_count();
   const dim3 grid((unsigned)(p.sched && ncu > 0 && ncu < items ? ncu : items));
-  hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL, FT>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

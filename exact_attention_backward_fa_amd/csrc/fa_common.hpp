@@ -348,6 +348,17 @@ __device__ __forceinline__ void bdma4(int voff, const i32x4& rsrc, uint32_t lds)
                : "v"(voff), "s"(rsrc), "s"(lds)
                : "memory", "m0");
 }
+// 16-bit stores through a buffer resource: the low (store16_lo) or high
+// (store16_hi) half of `data` to rsrc + voff.  A lane whose offset lies at or past
+// the resource's end stores nothing, so out-of-range elements need no branch.
+__device__ __forceinline__ void bstore16_lo(uint32_t data, int voff, const i32x4& rsrc) {
+  asm volatile("buffer_store_short %0, %1, %2, 0 offen" : : "v"(data), "v"(voff), "s"(rsrc) : "memory");
+}
+__device__ __forceinline__ void bstore16_hi(uint32_t data, int voff, const i32x4& rsrc) {
+  asm volatile("buffer_store_short_d16_hi %0, %1, %2, 0 offen" : : "v"(data), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // s_waitcnt vmcnt(N): at most N vector-memory operations of this wave still
@@ -481,6 +492,28 @@ struct PadPairDma {
   static constexpr int lds_offset = C * 1024;
 };
 
+// A ROWS x COLS block of a 16-bit matrix with a run-time row stride (elements; rows
+// 16-byte aligned) copied to LDS as rows of COLS + 8 PADG elements (the PADG pad
+// granules of a row receive a copy of its granule 0), in 1-KB wave instructions:
+// instruction c of wave w fills LDS bytes lds_wave_offset(w) + lds_offset<c> ..
+// +1023 from byte src_offset(c, w, lane, stride) of a buffer resource based at the
+// block's first element.  Rows beyond the resource's end arrive as zeros.
+template <int ROWS, int COLS, int PADG>
+struct StridedTileDma {
+  static constexpr int RS = COLS + 8 * PADG;  // LDS row stride, elements
+  static constexpr int GR = COLS / 8 + PADG;  // 16-byte granules per LDS row
+  static constexpr int PER_WAVE = ROWS * GR / 256;
+  static_assert(PER_WAVE * 256 == ROWS * GR, "whole 1-KB instructions per wave");
+  static __device__ __forceinline__ int src_offset(int c, int w, int lane, int stride) {
+    const int slot = (PER_WAVE * w + c) * 64 + lane;
+    const int r = slot / GR, g = slot % GR;
+    return 2 * (r * stride + 8 * (g < COLS / 8 ? g : 0));
+  }
+  static __device__ __forceinline__ uint32_t lds_wave_offset(int w) { return (uint32_t)(PER_WAVE * w * 1024); }
+  template <int C>
+  static constexpr int lds_offset = C * 1024;
+};
+
 template <int D, int ROWS>
 __device__ __forceinline__ void dma_pad_pair(const uint16_t* __restrict__ g0,
                                              const uint16_t* __restrict__ g1, int row0, int n_rows,
@@ -506,6 +539,51 @@ __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>());
+}
+
+// Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw
+// ("Parallel random numbers: as easy as 1, 2, 3", SC 2011): ten rounds, each
+// (c0, c1, c2, c3) -> (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+// lo(M0 c0)), with the key bumped by the Weyl constants before every round but the
+// first.  The dropout mask draws one call per 4 x 4 block of (query, key) positions.
+__device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1) {
+  constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
+  constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += kW0;
+      k1 += kW1;
+    }
+    const uint64_t p0 = (uint64_t)kM0 * c[0];
+    const uint64_t p1 = (uint64_t)kM1 * c[2];
+    const uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+    const uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+    u32x4 n = {hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0};
+    c = n;
+  }
+  return c;
+}
+
+// Keep factors of the four elements of one 4 x 4 block that a lane holds: byte
+// `byte_of(e)` of word `word_of(e)` below keep_t keeps element e, with factor
+// scale; word and byte positions come from the caller's layout.
+__device__ __forceinline__ float keep_factor(uint32_t word, int byte, uint32_t keep_t, float scale) {
+  return ((word >> (8 * byte)) & 0xffu) < keep_t ? scale : 0.f;
+}
+
+// Makes a value opaque to the compiler (ON): it is computed once, where placed,
+// and not rematerialized next to its use (a repack right before the MFMA that
+// reads it would be a VALU write of an MFMA source without wait states).
+template <bool ON>
+__device__ __forceinline__ void pin(u32x2& v) {
+  if constexpr (ON) asm volatile("" : "+v"(v));
+}
+
+// Element i (0..3) of four 16-bit values packed in a u32x2, as float.
+template <int DT>
+__device__ __forceinline__ float elem4(const u32x2& w, int i) {
+  return (i & 1) ? Dt<DT>::hi(w[i >> 1]) : Dt<DT>::lo(w[i >> 1]);
 }
 
 // 16-byte global load/store helpers.

@@ -6,8 +6,9 @@ namespace fa {
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s) {
   if ((size_t)a.pb.B * a.pb.Nq == 0) return hipSuccess;
-  FA_DISPATCH(a.pb, run_fwd, a, s);
-  return hipErrorInvalidValue;
+  return dispatch(a.pb, a.x.ft(), [&](auto dt, auto d, auto c, auto ft) {
+    return run_fwd<decltype(dt)::value, decltype(d)::value, decltype(c)::value, decltype(ft)::value>(a, s);
+  });
 }
 
 }  // namespace fa

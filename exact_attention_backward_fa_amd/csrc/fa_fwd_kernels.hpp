@@ -50,6 +50,12 @@ struct FwdParams {
   float* lse;
   int B, Hq, Hkv, Nq, Nkv, G, off;  // off = Nkv - Nq (bottom-right causal offset)
   float scale_log2;
+  // score bias (null: zero) with element strides; dropout of the P that weights V
+  // (keep iff the element's random byte < keep_t, kept P scaled by drop_scale)
+  const uint16_t* bias;
+  long long bias_sb, bias_sh, bias_sq;
+  unsigned keep_t, seed_lo, seed_hi;
+  float drop_scale;
 };
 
 // log2 headroom above the reference of a query column: P = exp2(score - m) stays
@@ -71,10 +77,13 @@ struct FwdSteps {
 // 16-row tiles) and triple-buffered key/value tiles up to d = 128; at d = 256 a
 // wave keeps 32 queries (Q and the O accumulators of 64 would not fit its
 // registers) and the tiles are double-buffered (three would not fit the LDS).
-template <int D>
+// The bias and dropout instances take the small shape too (the bias tiles need the
+// LDS, the bias and dropout work the registers).
+template <int D, int FT = 0>
 struct FwdShape {
-  static constexpr int QT = D > 128 ? 2 : 4;
-  static constexpr int NBUF = D > 128 ? 2 : 3;
+  static constexpr bool SMALL = D > 128 || FT != 0;
+  static constexpr int QT = SMALL ? 2 : 4;
+  static constexpr int NBUF = SMALL ? 2 : 3;
 };
 
 // Slots of the non-MFMA work of forward step ST (NC copies in step 1): mx[t] (the
@@ -118,16 +127,24 @@ struct FwdPlace {
   }
 };
 
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int FT>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
-  constexpr int QT = FwdShape<D>::QT;  // query tiles of 16 per wave
+  constexpr bool BIAS = FT >= FT_BIAS, DROP = FT == FT_DROPOUT;
+  constexpr int QT = FwdShape<D, FT>::QT;  // query tiles of 16 per wave
   constexpr int QW = 16 * QT, BM = 4 * QW, BN = 64, NST = 2;
   constexpr int NK = D / 32;
-  constexpr int NBUF = FwdShape<D>::NBUF;
+  constexpr int NBUF = FwdShape<D, FT>::NBUF;
   constexpr int RS = PadTile<D>::RS;
-  constexpr int OPS = 2 * BN * PadTile<D>::GR / 256;  // copy instructions per fetch per wave
+  // bias tile of a key tile: the workgroup's BM queries x BN keys (2 pad granules a
+  // row: 160-byte rows)
+  using BiasDma = StridedTileDma<BM, BN, 2>;
+  constexpr int BRS = BiasDma::RS;
+  constexpr int BPW = BIAS ? BiasDma::PER_WAVE : 0;
+  constexpr int KVPW = 2 * BN * PadTile<D>::GR / 256;
+  constexpr int OPS = KVPW + BPW;  // copy instructions per fetch per wave: K or V, bias
   constexpr int LA = 2;
   __shared__ __attribute__((aligned(16))) uint16_t sKV[NBUF][2 * BN * RS];  // K, V: a padded pair
+  __shared__ __attribute__((aligned(16))) uint16_t sB[BIAS ? NBUF : 1][BIAS ? BM * BRS : 8];
   static_assert(NBUF * 2 * BN * RS >= 4 * QW * (D + 8), "the output staging must fit the tile buffers");
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -163,15 +180,16 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     for (int n = 0; n < 2 * NK; ++n) acc[t][n] = zero4();
   }
   float lsum[QT] = {};  // this lane's part of its column's row sum
-  // reference of this lane's query column per query tile, and the raw-score
-  // threshold (m + H) / c above which it is raised; finite, so that a column with
-  // no visible key yet gives exp2(-inf - m) = 0
+  // reference of this lane's query column per query tile, and the threshold above
+  // which it is raised: (m + H) / c on raw scores, or m + H on the biased log2
+  // logits of the bias instances; finite, so that a column with no visible key yet
+  // gives exp2(-inf - m) = 0
   constexpr float kUnset = -1e30f;
   float m[QT], thr[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     m[t] = kUnset;
-    thr[t] = (m[t] + fwd_headroom<DT>()) / c;
+    thr[t] = BIAS ? m[t] + fwd_headroom<DT>() : (m[t] + fwd_headroom<DT>()) / c;
   }
   bool dirty = false;  // a reference was raised after it had been used
   __shared__ int s_dirty;
@@ -184,21 +202,49 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   const int nkt = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
 
   using Copy = PadPairDma<D, BN>;
+  static_assert(Copy::PER_WAVE == KVPW, "key/value copies per wave");
   const uint16_t* __restrict__ tsrc = w < 2 ? K : V;
+  struct Src {
+    i32x4 t, bs;  // this wave's K or V tile; bias tile (bias instances)
+  };
+  // bias element offset of this workgroup's first query row (key 0)
+  const long long bq0 = BIAS ? (long long)b * p.bias_sb + (long long)h * p.bias_sh +
+                                   (long long)q0 * p.bias_sq
+                             : 0;
   auto src_of = [&](int kt) {
     const int k0 = min(kt, nkt - 1) * BN;
-    return buf_rsrc(tsrc + (size_t)k0 * D, (p.Nkv - k0) * D * 2);
+    Src sr;
+    sr.t = buf_rsrc(tsrc + (size_t)k0 * D, (p.Nkv - k0) * D * 2);
+    if constexpr (BIAS) {
+      // rows past N_q and a null bias read zeros (the resource ends there); a row is
+      // read in whole 16-byte pieces, up to N_kv rounded up to 8 elements
+      const int rows = min(BM, p.Nq - q0);
+      const int bytes = p.bias ? 2 * ((rows - 1) * (int)p.bias_sq + (((p.Nkv + 7) & ~7) - k0)) : 0;
+      sr.bs = buf_rsrc(p.bias ? p.bias + bq0 + k0 : p.k, bytes);
+    }
+    return sr;
   };
   int voff[Copy::PER_WAVE];
 #pragma unroll
   for (int cc = 0; cc < Copy::PER_WAVE; ++cc) voff[cc] = Copy::src_offset(cc, w, lane);
   const uint32_t wave_off = Copy::lds_wave_offset(w);
-  auto copy_part = [&](auto cc, const i32x4& sr, int buf) {
+  int voffb[BIAS ? BPW : 1];
+  if constexpr (BIAS) {
+#pragma unroll
+    for (int cc = 0; cc < BPW; ++cc) voffb[cc] = BiasDma::src_offset(cc, w, lane, (int)p.bias_sq);
+  }
+  auto copy_part = [&](auto cc, const Src& sr, int buf) {
     constexpr int ci = decltype(cc)::value;
-    bdma16<Copy::template lds_offset<ci>>(voff[ci], sr, lds_u32(sKV[buf]) + wave_off);
+    if constexpr (ci < KVPW) {
+      bdma16<Copy::template lds_offset<ci>>(voff[ci], sr.t, lds_u32(sKV[buf]) + wave_off);
+    } else {
+      constexpr int cb_ = ci - KVPW;
+      bdma16<BiasDma::template lds_offset<cb_>>(voffb[cb_], sr.bs,
+                                                lds_u32(sB[buf]) + BiasDma::lds_wave_offset(w));
+    }
   };
   auto copy_all = [&](int kt, int buf) {
-    const i32x4 sr = src_of(kt);
+    const Src sr = src_of(kt);
     static_for<OPS>([&](auto cc) { copy_part(cc, sr, buf); });
   };
 
@@ -212,17 +258,29 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   for (int t = 0; t < QT; ++t) pa[1][t] = zero_u4();
   int prev = 0;
 
-  auto compute = [&](int cur, int nxt, auto mask_c, int kv0, const i32x4& fsrc, int fbuf) {
+  auto compute = [&](int cur, int nxt, auto mask_c, int kv0, const Src& fsrc, int fbuf) {
     constexpr bool MASK = decltype(mask_c)::value;
     const uint16_t* Kt = sKV[cur];
     const uint16_t* Vt = Kt + BN * RS;
     const uint16_t* Vp = sKV[prev] + BN * RS;
     const uint16_t* Kn = sKV[nxt];
     float mx[QT];
+    u32x2 bv[2][QT];  // bias of the pair's sub-blocks per query tile (keys in elements)
+    f32x4 zf[2][QT];  // dropout keep factors of the pair's sub-blocks
 
     using Steps = FwdSteps<NK, QT>;
     auto begin = [&](auto stc) {
       constexpr int st = decltype(stc)::value;
+      if constexpr (BIAS) {
+        // bias of sub-blocks 2 st and 2 st + 1: 4 keys of this lane's query each
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+          for (int t = 0; t < QT; ++t)
+            bv[sb][t] = *reinterpret_cast<const u32x2*>(sB[cur] + (QW * w + 16 * t + l16) * BRS +
+                                                        16 * (2 * st + sb) + 4 * j4);
+        }
+      }
       if constexpr (st == 1) {
         // Mid-tile: every wave is past step 0 (its last read of the previous buffer)
         // and, once its own copies have landed, the next tile is complete, so the
@@ -280,6 +338,15 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       static_for<QT>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         if constexpr (PL.mx[t] == mi) {
+          if constexpr (BIAS) {
+            // biased logits in log2 units: s c + bias log2 e
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                sc[sb][t][i] = fmaf(sc[sb][t][i], c, elem4<DT>(bv[sb][t], i) * kLog2e);
+            }
+          }
           if constexpr (MASK) {
             const int q = qw + 16 * t + l16;
 #pragma unroll
@@ -302,13 +369,13 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         if (__builtin_amdgcn_ballot_w64(any) != 0) {  // rare: set or raise references
 #pragma unroll
           for (int t = 0; t < QT; ++t) {
-            float v = mx[t] * c;
+            float v = BIAS ? mx[t] : mx[t] * c;
             v = fmaxf(v, __shfl_xor(v, 16));
             v = fmaxf(v, __shfl_xor(v, 32));
             if (v > m[t] + fwd_headroom<DT>()) {
               dirty = dirty || m[t] != kUnset;
               m[t] = v;
-              thr[t] = (v + fwd_headroom<DT>()) / c;
+              thr[t] = BIAS ? v + fwd_headroom<DT>() : (v + fwd_headroom<DT>()) / c;
             }
           }
         }
@@ -319,10 +386,25 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
           constexpr int t = decltype(tc)::value;
           static_for<4>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            if constexpr (PL.exp[sb][t][i] == mi) sc[sb][t][i] = fast_exp2(sc[sb][t][i] * c - m[t]);
+            if constexpr (PL.exp[sb][t][i] == mi) {
+              if constexpr (DROP && i == 0) {
+                // one Philox call for the 4 x 4 block (queries q & ~3 .., this lane's
+                // 4 keys): word q % 4 is this lane's query, byte r key r
+                const u32x4 ctr = {(uint32_t)(kv0 + 16 * (2 * st + sb) + 4 * j4) >> 2,
+                                   (uint32_t)(qw + 16 * t + l16) >> 2, (uint32_t)h, (uint32_t)b};
+                const u32x4 x = philox4x32_10(ctr, p.seed_lo, p.seed_hi);
+                const int qi = l16 & 3;
+                const uint32_t word = qi == 0 ? x[0] : qi == 1 ? x[1] : qi == 2 ? x[2] : x[3];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) zf[sb][t][r] = keep_factor(word, r, p.keep_t, p.drop_scale);
+              }
+              sc[sb][t][i] = BIAS ? fast_exp2(sc[sb][t][i] - m[t]) : fast_exp2(sc[sb][t][i] * c - m[t]);
+            }
           });
           if constexpr (PL.pack[sb][t] == mi) {
-            const u32x2 v = pack_c4<DT>(sc[sb][t]);
+            // V is weighted by the kept probabilities P o Z; the row sums take P
+            u32x2 v = pack_c4<DT>(DROP ? sc[sb][t] * zf[sb][t] : sc[sb][t]);
+            pin<FT != FT_PLAIN>(v);
             pa[st][t][2 * sb] = v[0];
             pa[st][t][2 * sb + 1] = v[1];
           }
@@ -384,7 +466,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       for (; kt < end; ++kt) {
         const int fbuf = cur == 0 ? NBUF - 1 : cur - 1;
         const int nxt = cur == NBUF - 1 ? 0 : cur + 1;
-        const i32x4 fsrc = src_of(kt + NBUF - 1);
+        const Src fsrc = src_of(kt + NBUF - 1);
         if constexpr (VAR == 0) {
           wait_vmem();
           tile_barrier();
@@ -440,7 +522,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
 }
 
 // Launcher of one instance (explicitly instantiated per instance in fa_fwd_inst.hip).
-template <int DT, int D, bool CAUSAL>
+template <int DT, int D, bool CAUSAL, int FT>
 hipError_t run_fwd(const FwdArgs& a, hipStream_t s) {
   const Problem& pb = a.pb;
   FwdParams p;
@@ -457,9 +539,17 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t s) {
   p.G = pb.Hq / pb.Hkv;
   p.off = pb.Nkv - pb.Nq;
   p.scale_log2 = pb.scale * kLog2e;
-  constexpr int BM = 4 * 16 * FwdShape<D>::QT;  // queries per workgroup
+  p.bias = static_cast<const uint16_t*>(a.x.bias);
+  p.bias_sb = a.x.bias_sb;
+  p.bias_sh = a.x.bias_sh;
+  p.bias_sq = a.x.bias_sq;
+  p.keep_t = a.x.keep_t;
+  p.seed_lo = (unsigned)(a.x.seed & 0xffffffffu);
+  p.seed_hi = (unsigned)(a.x.seed >> 32);
+  p.drop_scale = a.x.keep_t > 0 ? 256.f / (float)a.x.keep_t : 0.f;
+  constexpr int BM = 4 * 16 * FwdShape<D, FT>::QT;  // queries per workgroup
   const dim3 grid((unsigned)(((pb.Nq + BM - 1) / BM) * pb.Hq * pb.B));
-  hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL, FT>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 // Head dims with a kernel instance (every kernel family but the fused atomic one,
@@ -13,28 +15,12 @@ constexpr bool head_dim_supported(int d) {
   return d == 32 || d == 64 || d == 96 || d == 128 || d == 256;
 }
 constexpr bool atomic_head_dim(int d) { return d == 64 || d == 128; }
+// Head dims with the score-bias and dropout instances.
+constexpr bool feature_head_dim(int d) { return d == 64 || d == 128; }
 
-// Call FN<DT, D, CAUSAL>(args...) for a problem's (dtype, head dim, causal).
-#define FA_DISPATCH_D(DT, PB, FN, ...)                                                        \
-  switch ((PB).d) {                                                                          \
-    case 32: return (PB).causal ? FN<DT, 32, true>(__VA_ARGS__) : FN<DT, 32, false>(__VA_ARGS__); \
-    case 64: return (PB).causal ? FN<DT, 64, true>(__VA_ARGS__) : FN<DT, 64, false>(__VA_ARGS__); \
-    case 96: return (PB).causal ? FN<DT, 96, true>(__VA_ARGS__) : FN<DT, 96, false>(__VA_ARGS__); \
-    case 128:                                                                                \
-      return (PB).causal ? FN<DT, 128, true>(__VA_ARGS__) : FN<DT, 128, false>(__VA_ARGS__);   \
-    case 256:                                                                                \
-      return (PB).causal ? FN<DT, 256, true>(__VA_ARGS__) : FN<DT, 256, false>(__VA_ARGS__);   \
-    default:                                                                                 \
-      return hipErrorInvalidValue;                                                           \
-  }
-#define FA_DISPATCH(PB, FN, ...)                        \
-  do {                                                  \
-    if ((PB).dtype == 0) {                              \
-      FA_DISPATCH_D(0, PB, FN, __VA_ARGS__)             \
-    } else {                                            \
-      FA_DISPATCH_D(1, PB, FN, __VA_ARGS__)             \
-    }                                                   \
-  } while (0)
+// Kernel feature set of an instance: 0 plain attention, 1 with an additive score
+// bias (and its gradient), 2 with the bias and dropout of P.
+enum : int { FT_PLAIN = 0, FT_BIAS = 1, FT_DROPOUT = 2 };
 
 // Validated arguments of one call (sizes already checked, pointers device-side).
 struct Problem {
@@ -44,6 +30,16 @@ struct Problem {
   int dtype;  // 0 fp16, 1 bf16
 };
 
+// Optional score bias and dropout of a call (defaults: neither).
+struct Extras {
+  const void* bias = nullptr;  // element (b, h, i, j) at b*sb + h*sh + i*sq + j; null: zero
+  long long bias_sb = 0, bias_sh = 0, bias_sq = 0;
+  void* dbias = nullptr;       // [B, Hq, N_q, N_kv] contiguous, or null
+  unsigned keep_t = 256;       // dropout: keep iff the element's random byte < keep_t
+  unsigned long long seed = 0;
+  int ft() const { return keep_t < 256 ? FT_DROPOUT : (bias || dbias) ? FT_BIAS : FT_PLAIN; }
+};
+
 struct FwdArgs {
   Problem pb;
   const void* q;
@@ -51,6 +47,7 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
+  Extras x;
 };
 
 struct BwdArgs {
@@ -69,6 +66,7 @@ struct BwdArgs {
   float* dq_acc;  // [B*Hq*Nq*d]    float32 dQ accumulator (atomic path only)
   int* sched;     // [32]           work-queue counters of the dK/dV and dQ kernels (zeroed
                   //                by the preprocess); null: static work split
+  Extras x;
 };
 
 // Arguments of one backward call as the C entry points receive them (unchecked).
@@ -89,12 +87,13 @@ struct BwdCall {
 
 // Checks every argument of a backward call on the host (no device call); on
 // FA_OK sets *workspace_need to the workspace bytes the call needs.
-int bwd_validate(const BwdCall& c, int dq_mode, size_t* workspace_need);
+int bwd_validate(const BwdCall& c, int dq_mode, size_t* workspace_need,
+                 const Extras* x = nullptr);
 // Checks every argument of a backward call on the host, then enqueues the
 // kernels with `workspace` as the scratch memory; returns FA_OK or an FA_ERR_*
 // code (nothing is launched or written on error).
 int bwd_checked(const BwdCall& c, int dq_mode, void* ev_begin, void* ev_end, void* workspace,
-                size_t workspace_bytes, void* stream);
+                size_t workspace_bytes, void* stream, const Extras* x = nullptr);
 // Workspace bytes of a backward call with this dQ path (0 for invalid arguments).
 size_t bwd_workspace_checked(int B, int Hq, int Hkv, int Nq, int Nkv, int d, int causal, int dtype,
                              int dq_mode);
@@ -108,12 +107,44 @@ WorkspaceLayout workspace_layout(const Problem& pb, bool atomic_dq);
 // Kernel launchers (return hipSuccess or the launch error).
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t s);
 // The forward launcher of one template instance (dtype 0 fp16 / 1 bf16, head dim,
-// causal), defined in fa_fwd_kernels.hpp.
-template <int DT, int D, bool CAUSAL> hipError_t run_fwd(const FwdArgs& a, hipStream_t s);
+// causal, feature set), defined in fa_fwd_kernels.hpp.
+template <int DT, int D, bool CAUSAL, int FT> hipError_t run_fwd(const FwdArgs& a, hipStream_t s);
+
+// Calls f(dtype, head dim, causal, feature set) - each a std::integral_constant -
+// for a problem's instance; hipErrorInvalidValue when none is built.
+template <class F>
+hipError_t dispatch(const Problem& pb, int ft, F&& f) {
+  using std::integral_constant;
+  auto by_ft = [&](auto dt, auto d, auto c) -> hipError_t {
+    if constexpr (feature_head_dim(decltype(d)::value)) {
+      if (ft == FT_BIAS) return f(dt, d, c, integral_constant<int, FT_BIAS>());
+      if (ft == FT_DROPOUT) return f(dt, d, c, integral_constant<int, FT_DROPOUT>());
+    }
+    if (ft != FT_PLAIN) return hipErrorInvalidValue;
+    return f(dt, d, c, integral_constant<int, FT_PLAIN>());
+  };
+  auto by_c = [&](auto dt, auto d) -> hipError_t {
+    return pb.causal ? by_ft(dt, d, integral_constant<bool, true>())
+                     : by_ft(dt, d, integral_constant<bool, false>());
+  };
+  auto by_d = [&](auto dt) -> hipError_t {
+    switch (pb.d) {
+      case 32: return by_c(dt, integral_constant<int, 32>());
+      case 64: return by_c(dt, integral_constant<int, 64>());
+      case 96: return by_c(dt, integral_constant<int, 96>());
+      case 128: return by_c(dt, integral_constant<int, 128>());
+      case 256: return by_c(dt, integral_constant<int, 256>());
+      default: return hipErrorInvalidValue;
+    }
+  };
+  return pb.dtype == 0 ? by_d(integral_constant<int, 0>()) : by_d(integral_constant<int, 1>());
+}
 hipError_t launch_bwd_pre(const BwdArgs& a, bool zero_dq_acc, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, bool atomic_dq, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq_convert(const BwdArgs& a, hipStream_t s);
+// zeros into the dBias entries the causal mask hides (no-op without dBias or mask)
+hipError_t launch_dbias_fill(const BwdArgs& a, hipStream_t s);
 
 // Compute units of the current device (cached per device; 0 if it cannot be read).
 int device_cu_count();

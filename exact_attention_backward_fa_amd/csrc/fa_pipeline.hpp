@@ -145,6 +145,11 @@ __device__ __forceinline__ void run_tile(FBegin&& begin, FOp&& operand, FMma&& m
   using ic0 = std::integral_constant<int, 0>;
   constexpr int PRE = LA < T::NOP ? LA : T::NOP;
   u32x4 ops[LA + 1];
+  // A stand-alone stream (a flush) may follow VALU code that packed its first
+  // operands: two wait states before its first MFMA.
+  sched_fence();
+  asm volatile("s_nop 1" ::: "memory");
+  sched_fence();
   begin(ic0());
   static_for<PRE>([&](auto oc) {
     constexpr int o = decltype(oc)::value, st = T::step_of_o(o);

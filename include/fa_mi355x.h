@@ -59,15 +59,18 @@ extern "C" {
 #define FA_OK            0
 #define FA_ERR_NULLPTR  -1  /* required pointer is NULL */
 #define FA_ERR_SHAPE    -2  /* bad B/Hq/Hkv/N_q/N_kv, Hq % Hkv != 0, or size limits */
-#define FA_ERR_HEADDIM  -3  /* d not in {32, 64, 96, 128, 256}, or FA_DQ_ATOMIC with
-                               d not in {64, 128} */
+#define FA_ERR_HEADDIM  -3  /* d not in {32, 64, 96, 128, 256}, or FA_DQ_ATOMIC, a bias
+                               or dropout with d not in {64, 128} */
 #define FA_ERR_DTYPE    -4  /* dtype not FP16/BF16 */
 #define FA_ERR_SCALE    -5  /* softmax_scale not finite or <= 0 */
 #define FA_ERR_WORKSPACE -6 /* workspace NULL/misaligned or smaller than required */
 #define FA_ERR_ALIGN    -7  /* a tensor pointer is not 16-byte aligned */
 #define FA_ERR_HIP      -8  /* a kernel launch failed (hipGetLastError) */
-#define FA_ERR_MODE     -9  /* unknown dq_mode */
+#define FA_ERR_MODE     -9  /* unknown dq_mode, or FA_DQ_ATOMIC with a bias or dropout */
 #define FA_ERR_SCRATCH  -10 /* fa_bwd_noalloc: the call needs more scratch than it holds */
+#define FA_ERR_BIAS     -11 /* bias strides negative, not multiples of 8, or too large;
+                               or dbias with N_kv > 2^22 */
+#define FA_ERR_DROPOUT  -12 /* dropout_p not in [0, 1] */
 
 #define FA_DTYPE_FP16 0
 #define FA_DTYPE_BF16 1
@@ -162,6 +165,63 @@ int fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
  * FA_DQ_SEPARATE). */
 int fa_bwd_auto_dq_mode(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
                         int causal, int dtype);
+
+/*
+ * Forward with an additive score bias and dropout of the probabilities.
+ * Source: the Liger-Kernel pull request "[Kernel] Flash attention 2", Details,
+ * which lists an attention mask / attention bias and dropout (forward only there;
+ * the backward of both is fa_bwd_bias_dropout below).  Definitions:
+ *   S = scale * Q_h K_g^T + bias_h,  LSE and P from S as in fa_fwd,
+ *   O = (P o Z) V  with Z_ij = 256 / T if element (i, j) is kept, else 0.
+ * bias: NULL (no bias), or 16-bit values of the call's dtype, 16-byte aligned;
+ *   element (b, h, i, j) of the [B, Hq, N_q, N_kv] bias sits at
+ *   b * bias_stride_b + h * bias_stride_h + i * bias_stride_q + j (elements), so a
+ *   zero stride broadcasts that dimension (e.g. a per-key padding mask [B,1,1,N_kv]:
+ *   stride_h = stride_q = 0).  Strides are >= 0 and multiples of 8 (16-byte rows),
+ *   bias_stride_q <= 2^22.  Rows are read in whole 16-byte pieces: each row must be
+ *   readable for N_kv rounded up to a multiple of 8 elements (the values past N_kv
+ *   are ignored).  -inf entries mask keys; a row whose every visible key is masked
+ *   gets O = 0 and LSE = -inf.
+ * dropout_p in [0, 1]: element (b, h, i, j) is kept iff byte j % 4 of word i % 4 of
+ *   Philox4x32-10 (Salmon et al., SC 2011) with counter (j / 4, i / 4, h, b) and key
+ *   (seed low word, seed high word) is below T = floor((1 - p) * 256 + 1/2); the
+ *   keep probability is T / 256 (p rounded to a multiple of 1/256).  LSE is that of
+ *   the undropped P, so the backward can rebuild P from it.
+ * With bias NULL and dropout_p = 0 this is fa_fwd.  A bias or dropout needs
+ * d = 64 or 128 (FA_ERR_HEADDIM otherwise).  Returns FA_OK or an FA_ERR_* code;
+ * on error nothing is launched or written.
+ */
+int fa_fwd_bias_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                        float softmax_scale, int causal, int dtype,
+                        const void* bias, long long bias_stride_b, long long bias_stride_h,
+                        long long bias_stride_q, float dropout_p, unsigned long long seed,
+                        void* stream);
+
+/*
+ * Backward of fa_fwd_bias_dropout: dQ, dK, dV and, if dbias is not NULL, the bias
+ * gradient dBias = dS.
+ * Source: as fa_bwd; the bias is part of the score, so its gradient is the score
+ * gradient; with dropout dV = (P o Z)^T dO, dP = (dO V^T) o Z, and D = rowsum(dO o O),
+ * dS = P o (dP - D) keep their form (Liger-Kernel pull request "[Kernel] Flash
+ * attention 2", Details: bias and dropout).
+ * bias, strides, dropout_p and seed: exactly those given to the forward that made
+ * o and lse.  dbias: NULL, or [B, Hq, N_q, N_kv] contiguous in the call's dtype,
+ * 16-byte aligned, fully overwritten (zeros where the causal mask hides a key);
+ * the gradient of a bias broadcast along some dimension is this tensor summed along
+ * it (left to the caller).  The dQ path is the separate pass (FA_DQ_SEPARATE);
+ * workspace as for fa_bwd_ex with FA_DQ_SEPARATE.  With bias and dbias NULL and
+ * dropout_p = 0 this is fa_bwd with that path.  Returns FA_OK or an FA_ERR_* code;
+ * on error nothing is launched or written.
+ */
+int fa_bwd_bias_dropout(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        int B, int Hq, int Hkv, int Nq, int Nkv, int d,
+                        float softmax_scale, int causal, int dtype,
+                        const void* bias, long long bias_stride_b, long long bias_stride_h,
+                        long long bias_stride_q, void* dbias, float dropout_p,
+                        unsigned long long seed, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * Allocation-free backward, for callers that cannot allocate device memory (code

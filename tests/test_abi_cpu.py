@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
 
 FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_HEADDIM = 0, -1, -2, -3
 FA_ERR_DTYPE, FA_ERR_SCALE, FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_MODE = -4, -5, -6, -7, -8, -9
-FA_ERR_SCRATCH = -10
+FA_ERR_SCRATCH, FA_ERR_BIAS, FA_ERR_DROPOUT = -10, -11, -12
 
 
 @pytest.fixture(scope="module")
@@ -49,7 +49,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     for code in (FA_OK, FA_ERR_NULLPTR, FA_ERR_SHAPE, FA_ERR_HEADDIM, FA_ERR_DTYPE, FA_ERR_SCALE,
-                 FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_MODE, FA_ERR_SCRATCH, 12345):
+                 FA_ERR_WORKSPACE, FA_ERR_ALIGN, FA_ERR_HIP, FA_ERR_MODE, FA_ERR_SCRATCH, FA_ERR_BIAS,
+                 FA_ERR_DROPOUT, 12345):
         s = lib.fa_status_string(code)
         assert isinstance(s, bytes) and len(s) > 0
     assert lib.fa_status_string(FA_ERR_HEADDIM).decode().find("96") >= 0
@@ -205,3 +206,49 @@ def test_noalloc_checks_arguments_before_any_device_call(lib):
     assert noalloc(lib, Hq=1, Nq=lo + 1, Nkv=16) == FA_ERR_SCRATCH
     assert noalloc(lib, B=4, Hq=32, Hkv=8, Nq=32768, Nkv=32768, d=128, causal=1,
                    dtype=1) == FA_ERR_SCRATCH
+
+
+def fwd_bd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=1, Nq=8, Nkv=8, d=64, scale=0.125,
+             causal=0, dtype=0, bias=P, sb=0, sh=0, sq=8, p=0.0, seed=1)
+    a.update(kw)
+    return lib.fa_fwd_bias_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                   a["Nq"], a["Nkv"], a["d"], a["scale"], a["causal"], a["dtype"],
+                                   a["bias"], a["sb"], a["sh"], a["sq"], a["p"], a["seed"], None)
+
+
+def bwd_bd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=1, Nq=8, Nkv=8,
+             d=64, scale=0.125, causal=0, dtype=0, bias=P, sb=0, sh=0, sq=8, dbias=P, p=0.0, seed=1,
+             ws=0, wsb=0)
+    a.update(kw)
+    return lib.fa_bwd_bias_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                                   a["dv"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nkv"], a["d"],
+                                   a["scale"], a["causal"], a["dtype"], a["bias"], a["sb"], a["sh"],
+                                   a["sq"], a["dbias"], a["p"], a["seed"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("call", [fwd_bd, bwd_bd])
+def test_bias_dropout_argument_errors(lib, call):
+    """Checked on the host before any device call (none exists here)."""
+    for p in (-0.01, 1.01, math.nan, math.inf):
+        assert call(lib, p=p) == FA_ERR_DROPOUT, p
+    assert call(lib, sq=4) == FA_ERR_BIAS        # rows not 16-byte aligned
+    assert call(lib, sq=-8) == FA_ERR_BIAS
+    assert call(lib, sh=12) == FA_ERR_BIAS
+    assert call(lib, sq=(1 << 22) + 8) == FA_ERR_BIAS
+    assert call(lib, bias=P + 8) == FA_ERR_ALIGN
+    assert call(lib, d=96) == FA_ERR_HEADDIM     # bias needs d = 64 or 128
+    assert call(lib, d=96, bias=0, p=0.5) == FA_ERR_HEADDIM
+    assert call(lib, d=96, bias=0, sq=3, p=0.0, **({"dbias": 0} if call is bwd_bd else {})) != FA_ERR_HEADDIM
+    assert call(lib, q=0) == FA_ERR_NULLPTR
+    assert call(lib, scale=0.0) == FA_ERR_SCALE
+
+
+def test_bias_dropout_backward_specific_errors(lib):
+    assert bwd_bd(lib, dbias=P + 4) == FA_ERR_ALIGN
+    # valid arguments stop at the workspace check (separate dQ path sizes)
+    assert bwd_bd(lib) == FA_ERR_WORKSPACE
+    assert bwd_bd(lib, p=0.3, bias=0, dbias=0) == FA_ERR_WORKSPACE
+    # without bias, dbias and dropout the call is the plain backward
+    assert bwd_bd(lib, d=96, bias=0, dbias=0) == FA_ERR_WORKSPACE
