@@ -193,8 +193,9 @@ def main() -> int:
     # was taken from the current kernel sources (None otherwise).
     from exact_attention_backward_fa_amd import profiling
     dt_id = 1 if case.dtype == "bf16" else 0
-    kname = (f"{'bwd_dkdv_atomic_kernel' if resolved == 'atomic' else 'bwd_dkdv_kernel'}"
-             f"<{dt_id}, {case.d}, {'true' if case.causal else 'false'}>")
+    causal = "true" if case.causal else "false"
+    kname = (f"bwd_dkdv_atomic_kernel<{dt_id}, {case.d}, {causal}>" if resolved == "atomic"
+             else f"bwd_dkdv_kernel<{dt_id}, {case.d}, {causal}, 0>")
     traffic = None if features else profiling.read_traffic(kname)
     mfma = None if features else profiling.read_mfma(kname)
     log(f"[bench] fwd {fwd_ms:.3f} ms ({fwd_flops / fwd_ms / 1e9:.1f} TFLOP/s)  bwd {bwd_ms:.3f} ms "

@@ -3,8 +3,8 @@
     python -m exact_attention_backward_fa_amd.build [--incremental]
 
 Every kernel template instance is its own compilation unit, so the units build in
-parallel: the forward once per (dtype, head dim, causal), the backward once per
-(dtype, head dim, causal, kernel).  Objects go to ``_build/`` at the repository
+parallel: the forward once per (dtype, head dim, causal, feature set), the backward
+once per (dtype, head dim, causal, feature set, kernel).  Objects go to ``_build/`` at the repository
 root (not tracked); the shared library lands next to this file, where the binding
 loads it.  ``build()`` compiles every unit each time it is called;
 ``build(incremental=True)`` reuses an object whose source, included headers and
@@ -13,13 +13,14 @@ flags are unchanged (the key is a hash over all of them).
 from __future__ import annotations
 
 import hashlib
+import json
 import os
 import re
 import shutil
 import subprocess
 import sys
 import time
-from typing import Dict, List, Sequence, Tuple
+from typing import Dict, List, Optional, Sequence, Tuple
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
@@ -42,6 +43,12 @@ FEATURE_HEAD_DIMS = (64, 128)
 FEATURES = (1, 2)
 # Backward kernel families compiled per instance (FA_KIND in fa_bwd_inst.hip).
 BWD_KINDS = {0: "pre", 1: "dkdv", 2: "dq", 3: "atomic"}
+
+# Units whose kernels the committed counter profiles describe (the bf16, d = 128,
+# causal instance).  After linking, build() hashes their device assembly into
+# CODE_HASHES, so a profile can tell whether it still describes the kernels built.
+PROFILED_UNITS = ("fwd_1_128_1", "pre_1_128_1", "dkdv_1_128_1", "dq_1_128_1", "atomic_1_128_1")
+CODE_HASHES = os.path.join(PKG_DIR, "kernel_code.json")
 
 ARCH = "gfx950"
 HIP_FLAGS = [
@@ -195,6 +202,7 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}")
     os.replace(tmp, LIB_PATH)
+    write_code_hashes(verbose)
     if verbose:
         print(f"[build] {LIB_PATH} ({len(jobs)} of {len(objs)} units compiled) in "
               f"{time.time() - t0:.1f}s", flush=True)
@@ -221,6 +229,50 @@ def device_asm(selected: Sequence[Unit], verbose: bool = False) -> Dict[str, str
         if os.path.exists(path + ".part"):
             os.replace(path + ".part", path)
     return paths
+
+
+def asm_code_hash(path: str) -> str:
+    """Hash of a unit's device assembly with comments, file/tool notes and the
+    per-compilation unit id removed: equal for two builds that generate the same
+    instructions and metadata."""
+    h = hashlib.sha256()
+    with open(path) as f:
+        for line in f:
+            line = line.split(";", 1)[0].rstrip()
+            if not line or line.lstrip().startswith((".file", ".ident")):
+                continue
+            line = re.sub(r"__hip_cuid_[0-9a-f]+", "__hip_cuid", line)
+            h.update(line.encode() + b"\n")
+    return h.hexdigest()[:16]
+
+
+def write_code_hashes(verbose: bool = False) -> Dict[str, str]:
+    """Hashes the device code of PROFILED_UNITS into CODE_HASHES ({unit: hash})."""
+    sel = [u for u in units() if u.name in PROFILED_UNITS]
+    paths = device_asm(sel, verbose)
+    hashes = {name: asm_code_hash(path) for name, path in sorted(paths.items())}
+    tmp = CODE_HASHES + ".tmp"
+    with open(tmp, "w") as f:
+        json.dump(hashes, f, indent=1, sort_keys=True)
+    os.replace(tmp, CODE_HASHES)
+    return hashes
+
+
+_KERNEL_UNIT = {"fwd_kernel": "fwd", "bwd_pre_kernel": "pre", "bwd_dkdv_kernel": "dkdv",
+                "bwd_dq_kernel": "dq", "bwd_dkdv_atomic_kernel": "atomic"}
+
+
+def unit_of_kernel(kernel: str) -> Optional[str]:
+    """Compilation unit of a kernel named as a profiler prints it, e.g.
+    ``bwd_dkdv_kernel<1, 128, true, 0>`` -> ``dkdv_1_128_1``; None for others."""
+    m = re.match(r"(?:fa::)?(\w+)<(\d+), (\d+), (true|false)(?:, (\d+))?>", kernel)
+    if not m or m.group(1) not in _KERNEL_UNIT:
+        return None
+    fam = _KERNEL_UNIT[m.group(1)]
+    # the preprocess's bool is its dQ-buffer clearing, not causality: both units hold it
+    causal = "1" if fam == "pre" or m.group(4) == "true" else "0"
+    ft = int(m.group(5) or 0)
+    return f"{fam}_{m.group(2)}_{m.group(3)}_{causal}" + (f"_f{ft}" if ft else "")
 
 
 if __name__ == "__main__":

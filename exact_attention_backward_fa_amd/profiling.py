@@ -16,14 +16,16 @@ reads for the calibration copy of known size (512 MiB read, 512 MiB written).
 share of SIMD cycles in which the matrix unit was busy while the GPU was active,
 and the MFMA flops each launch executed.
 
-The traffic and MFMA summaries record a hash of the kernel sources so the
-benchmark can tell when the counters no longer describe the current kernels.
+Every summary records, per kernel, a hash of the kernel's generated device code
+(written by the build next to the library), so the benchmark can tell when the
+counters no longer describe the kernels built: a change elsewhere in the sources
+that leaves a kernel's instructions alone keeps its profile valid.
 """
 from __future__ import annotations
 
 import csv
 import glob
-import hashlib
+import json
 import os
 import re
 import sys
@@ -32,21 +34,32 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ("csrc/fa_bwd.hip", "csrc/fa_bwd_inst.hip", "csrc/fa_bwd_kernels.hpp",
-                  "csrc/fa_bwd_atomic.hpp", "csrc/fa_bwd_common.hpp", "csrc/fa_fwd.hip",
-                  "csrc/fa_fwd_inst.hip", "csrc/fa_fwd_kernels.hpp", "csrc/fa_pipeline.hpp",
-                  "csrc/fa_common.hpp")
 COPY_BYTES = 512 << 20
 TRAFFIC_FILE = os.path.join(PROFILES, "hbm_traffic_llama_gqa_bf16_8192.txt")
+# the fused atomic-dQ path's counters, taken in a run of their own
+TRAFFIC_FILE_ATOMIC = os.path.join(PROFILES, "hbm_traffic_atomic_dq_llama_gqa_bf16_8192.txt")
 MFMA_FILE = os.path.join(PROFILES, "mfma_busy_llama_gqa_bf16_8192.txt")
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(PKG, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def kernel_code_hash(kernel: str):
+    """Hash of the device code built for a kernel (short name), or None when the
+    build recorded none for it."""
+    from . import build
+    unit = build.unit_of_kernel(kernel)
+    try:
+        with open(build.CODE_HASHES) as f:
+            return json.load(f).get(unit) if unit else None
+    except (OSError, ValueError):
+        return None
+
+
+def _code_lines(kernels) -> list:
+    out = []
+    for k in kernels:
+        h = kernel_code_hash(short_name(k))
+        if h:
+            out.append(f"code_sha256_16 `{short_name(k)}`: {h}")
+    return out + [""] if out else []
 
 
 def short_name(name: str) -> str:
@@ -66,7 +79,7 @@ def trace_summary(d: str, command: str) -> str:
     path = _find(d, "*kernel_stats.csv")
     rows = list(csv.DictReader(open(path)))
     out = ["# Kernel trace summary", "", f"Command: `{command}`", "",
-           f"kernel_source_sha256_16: {kernel_source_hash()}", "",
+           *_code_lines(r["Name"] for r in rows),
            "| kernel | calls | avg (us) | min (us) | max (us) | share |",
            "|---|---|---|---|---|---|"]
     for r in rows:
@@ -97,7 +110,7 @@ def traffic_summary(fetch_dir: str, write_dir: str, commands: str) -> str:
     w_scale = COPY_BYTES / (write[ck] * 1024.0)
     out = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
            f"Commands: {commands}", "",
-           f"kernel_source_sha256_16: {kernel_source_hash()}", "",
+           *_code_lines(fetch),
            f"Calibration: `{short_name(ck)}` copying 512 MiB reads FETCH_SIZE = "
            f"{fetch[ck]:.0f} KiB and WRITE_SIZE = {write[ck]:.0f} KiB; scale factors "
            f"fetch x{f_scale:.3f}, write x{w_scale:.3f}.", "",
@@ -121,7 +134,7 @@ def mfma_summary(d: str, command: str) -> str:
             flops[k] += v
     out = ["# MFMA busy share and executed MFMA flops per launch (rocprofv3 --pmc)", "",
            f"Command: {command}", "",
-           f"kernel_source_sha256_16: {kernel_source_hash()}", "",
+           *_code_lines(util),
            "MfmaUtil = summed SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMD count) x 100; "
            "MfmaFlops = MFMA MOPs (bf16 + fp16) x 512.", "",
            "| kernel | MfmaUtil % | executed MFMA TFLOP per launch |",
@@ -134,16 +147,21 @@ def mfma_summary(d: str, command: str) -> str:
 
 
 def _read_row(path: str, kernel_prefix: str):
+    """Cells of the row of the first kernel whose name starts with kernel_prefix,
+    or None when the file or the row is missing, or the code hash it recorded for
+    that kernel is not the hash of the kernel built now."""
     try:
         text = open(path).read()
     except OSError:
         return None
-    m = re.search(r"kernel_source_sha256_16: (\w+)", text)
-    if not m or m.group(1) != kernel_source_hash():
-        return None
     for line in text.splitlines():
         cells = [c.strip() for c in line.split("|")]
         if len(cells) > 3 and cells[1].strip("`").startswith(kernel_prefix):
+            name = cells[1].strip("`")
+            m = re.search(r"code_sha256_16 `" + re.escape(name) + r"`: (\w+)", text)
+            now = kernel_code_hash(name)
+            if not m or now is None or m.group(1) != now:
+                return None
             return cells[2:-1]
     return None
 
@@ -157,18 +175,11 @@ def read_mfma(kernel_prefix: str):
 
 def read_traffic(kernel_prefix: str):
     """Traffic bytes per launch recorded for a kernel, or None when the summary is
-    missing or was taken from different kernel sources."""
-    try:
-        text = open(TRAFFIC_FILE).read()
-    except OSError:
-        return None
-    m = re.search(r"kernel_source_sha256_16: (\w+)", text)
-    if not m or m.group(1) != kernel_source_hash():
-        return None
-    for line in text.splitlines():
-        cells = [c.strip() for c in line.split("|")]
-        if len(cells) > 6 and cells[1].strip("`").startswith(kernel_prefix):
-            return float(cells[6])
+    missing or was taken from different kernel code."""
+    for path in (TRAFFIC_FILE, TRAFFIC_FILE_ATOMIC):
+        cells = _read_row(path, kernel_prefix)
+        if cells is not None and len(cells) >= 5:
+            return float(cells[4])
     return None
 
 
