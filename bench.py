@@ -4,17 +4,20 @@ Workload: Llama-3-style causal GQA, B=4, Hq=32, Hkv=8, N_q=N_kv=8192, d=128, bf1
 scale 1/sqrt(128), Q/K/V/dO ~ N(0,1) from the seeded generator (synthetic data).
 
 A step is one pass of the whole hot path on resident inputs: fa_fwd (O, LSE) then
-fa_bwd (D preprocess, the dK/dV kernel, the dQ path).  The headline value is the
+fa_bwd (the dQ pass with the D preprocess of its rows, then the dK/dV kernel; or,
+on the atomic path, the preprocess, the fused kernel and the dQ conversion).  The headline value is the
 backward's throughput, fa_bwd TFLOP/s, counting 2.5x the forward's 4*Nq*Nkv*d
 flops per query head, halved for causal; it is taken from HIP events recorded on
 the launch stream around every fa_bwd call of the timed steps.
 
 Also reported: the roofline of the dominant kernel (the dK/dV kernel, timed alone
 with events that fa_bwd_ex records around its launch), the forward's rate, and a
-CPU baseline: the fp64 oracle's backward on one kv-head group of the same inputs,
-timed on the host cores.
+CPU baseline: the fp64 oracle's backward on kv-head groups of the same inputs,
+timed on the host cores, with the host's CPU model, BLAS library and one-thread
+oracle timings of the small workloads.
 
     python bench.py [--steps K] [--warmup W] [--dq-mode auto|atomic|separate]
+                    [--workload NAME[,NAME...]] [--bias keys|full] [--dbias] [--dropout P]
 """
 from __future__ import annotations
 
@@ -36,15 +39,19 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
+def _threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(case, x, min_seconds: float = 10.0, max_groups: int = 8) -> dict:
     """The oracle's backward, as it stands, on whole (batch, kv head) groups of the
     same inputs, one group after another until about ``min_seconds`` of CPU work."""
     import oracle.attention_fp64 as orc
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads = _threads()
     G = case.Hq // case.Hkv
     groups = [(b, g) for b in range(case.B) for g in range(case.Hkv)][:max_groups]
     done, t0 = 0, time.perf_counter()
@@ -64,40 +71,66 @@ def cpu_baseline(case, x, min_seconds: float = 10.0, max_groups: int = 8) -> dic
             "seconds": dt}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--dq-mode", default="auto", choices=["auto", "atomic", "separate"])
-    ap.add_argument("--workload", default=None, help="case name (default: headline workload)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--bias", default="none", choices=["none", "keys", "full"],
-                    help="additive score bias: a per-key [B,1,1,N_kv] padding mask, or a "
-                         "full [B,Hq,N_q,N_kv] bias (timed through fa_*_bias_dropout)")
-    ap.add_argument("--dbias", action="store_true", help="also write dBias [B,Hq,N_q,N_kv]")
-    ap.add_argument("--dropout", type=float, default=0.0, help="dropout probability of P")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="after timing, copy a 512 MiB buffer once (known traffic) so that "
-                         "a counter profile of this run can scale FETCH_SIZE/WRITE_SIZE")
-    args = ap.parse_args()
+def cpu_context() -> dict:
+    """The host the oracle runs on (CPU model, BLAS library and its threads), and the
+    oracle's backward on one thread for the three small workload families: the
+    single head, the ragged family (all 8 cases) and 4 of the 32 (batch, head)
+    pairs of the uniform 2048 x 2048 shape."""
+    import oracle.attention_fp64 as orc
+    from exact_attention_backward_fa_amd import inputs
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        libs = [f"{p.get('internal_api')} {p.get('version')} ({p.get('num_threads')} threads)"
+                for p in threadpool_info() if p.get("user_api") == "blas"]
+        blas = "; ".join(libs) or blas
+    except Exception:
+        threadpool_limits = None
+    samples = [("single", inputs.cases_of_family(1), None),
+               ("ragged (8 cases)", inputs.cases_of_family(2), None),
+               ("uniform, 4 of 32 (batch, head)", inputs.cases_of_family(3), 4)]
+    rows = []
+    for label, cases, heads in samples:
+        flops, t = 0.0, 0.0
+        for case in cases:
+            x = inputs.make_inputs(case)
+            if heads is not None:
+                x = {k: v[:1, :heads] for k, v in x.items()}
+            Hq = x["q"].shape[1]
+            ctx = threadpool_limits(limits=1) if threadpool_limits else None
+            t0 = time.perf_counter()
+            if ctx is not None:
+                with ctx:
+                    orc.backward(x["q"], x["k"], x["v"], x["do"], case.scale, case.causal)
+            else:
+                orc.backward(x["q"], x["k"], x["v"], x["do"], case.scale, case.causal)
+            t += time.perf_counter() - t0
+            flops += (x["q"].shape[0] * Hq * 10.0 * case.Nq * case.Nkv * case.d
+                      * (0.5 if case.causal else 1.0))
+        rows.append({"workload": label, "seconds": round(t, 3),
+                     "value": round(flops / t / 1e12, 6) if t > 0 else None, "unit": "TFLOP/s",
+                     "threads": 1})
+    return {"cpu_model": model, "blas": blas, "os_cpus": os.cpu_count(), "single_thread": rows}
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the backward shards by (batch, kv head) group with no communication; "
-              "run --gpus 1)", file=sys.stderr, flush=True)
-        return 2
 
+def measure(case, args, dev, log_prefix="[bench]") -> tuple:
+    """Times args.steps steps of the hot path on one workload; returns the JSON
+    object of the line (without the CPU baseline) and the host inputs."""
     import torch
     import exact_attention_backward_fa_amd as fa
-    from exact_attention_backward_fa_amd import inputs
+    from exact_attention_backward_fa_amd import profiling
 
-    case = inputs.case_by_name(args.workload or inputs.HEADLINE)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    log(f"[bench] workload {case.name}: B={case.B} Hq={case.Hq} Hkv={case.Hkv} N={case.Nq} "
+    log(f"{log_prefix} workload {case.name}: B={case.B} Hq={case.Hq} Hkv={case.Hkv} N={case.Nq} "
         f"d={case.d} {case.dtype} causal={case.causal}")
-    x = inputs.make_inputs(case)
+    x = inputs_of(case)
     d = {k: v.to(dev) for k, v in x.items()}
     o = torch.empty_like(d["q"])
     lse = torch.empty(case.B, case.Hq, case.Nq, dtype=torch.float32, device=dev)
@@ -110,18 +143,12 @@ def main() -> int:
                                    case.causal, case.torch_dtype)
     else:
         resolved = mode
-    ws = torch.empty(max(fa.bwd_workspace_bytes(case.B, case.Hq, case.Hkv, case.Nq, case.Nkv, case.d,
-                                                case.causal, case.torch_dtype, mode), 1),
-                     dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     n = args.steps
     features = args.bias != "none" or args.dbias or args.dropout > 0.0
-    if features and args.dq_mode == "atomic":
-        log("[bench] bias, dBias and dropout run on the separate dQ path only")
-        return 2
     bias = dbias = None
     if features:
-        resolved = "separate"
+        mode = resolved = "separate"
         g = torch.Generator(device=dev).manual_seed(1234)
         if args.bias == "keys":  # a padding mask: the last 1/8 of every row's keys hidden
             bias = torch.zeros(case.B, 1, 1, (case.Nkv + 7) // 8 * 8, dtype=case.torch_dtype,
@@ -135,10 +162,9 @@ def main() -> int:
         if args.dbias:
             dbias = torch.empty(case.B, case.Hq, case.Nq, case.Nkv, dtype=case.torch_dtype,
                                 device=dev)
-        ws = torch.empty(max(fa.bwd_workspace_bytes(case.B, case.Hq, case.Hkv, case.Nq, case.Nkv,
-                                                    case.d, case.causal, case.torch_dtype,
-                                                    "separate"), 1),
-                         dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(fa.bwd_workspace_bytes(case.B, case.Hq, case.Hkv, case.Nq, case.Nkv, case.d,
+                                                case.causal, case.torch_dtype, mode), 1),
+                     dtype=torch.uint8, device=dev)
     ev = {k: [fa.HipEvent() for _ in range(n)] for k in ("f0", "f1", "b0", "b1", "k0", "k1")}
 
     def step(i=None):
@@ -166,7 +192,7 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
-    log(f"[bench] warmup done ({args.warmup} steps); timing {n} steps, dq path {resolved}")
+    log(f"{log_prefix} warmup done ({args.warmup} steps); timing {n} steps, dq path {resolved}")
     t0 = time.perf_counter()
     for i in range(n):
         step(i)
@@ -189,16 +215,15 @@ def main() -> int:
     # for causal); on the separate path it performs four of them (8*Nq*Nkv*d).
     kern_flops = bwd_flops if resolved == "atomic" else bwd_flops * 0.8
     achieved = None if kern_ms is None else kern_flops / (kern_ms * 1e-3) / 1e12
-    # HBM bytes per launch of that kernel from the committed counter profile, when it
-    # was taken from the current kernel sources (None otherwise).
-    from exact_attention_backward_fa_amd import profiling
+    # HBM bytes per launch of that kernel and its MFMA counters from the committed
+    # counter profiles, when they were taken from the kernel code built now.
     dt_id = 1 if case.dtype == "bf16" else 0
     causal = "true" if case.causal else "false"
     kname = (f"bwd_dkdv_atomic_kernel<{dt_id}, {case.d}, {causal}>" if resolved == "atomic"
              else f"bwd_dkdv_kernel<{dt_id}, {case.d}, {causal}, 0>")
     traffic = None if features else profiling.read_traffic(kname)
     mfma = None if features else profiling.read_mfma(kname)
-    log(f"[bench] fwd {fwd_ms:.3f} ms ({fwd_flops / fwd_ms / 1e9:.1f} TFLOP/s)  bwd {bwd_ms:.3f} ms "
+    log(f"{log_prefix} fwd {fwd_ms:.3f} ms ({fwd_flops / fwd_ms / 1e9:.1f} TFLOP/s)  bwd {bwd_ms:.3f} ms "
         f"({value:.1f} TFLOP/s, {100 * value / PEAK_BF16_TFLOPS:.1f}% of peak)"
         + ("" if kern_ms is None else f"  dkdv kernel {kern_ms:.3f} ms ({achieved:.1f} TFLOP/s)"))
 
@@ -236,7 +261,7 @@ def main() -> int:
             "kernel_ms": None if kern_ms is None else round(kern_ms, 4),
             # rocprof MfmaUtil (matrix-unit busy share of active SIMD cycles) and the
             # MFMA flops the kernel executes per launch, from the committed counter
-            # profile of the current kernel sources; null when that profile is stale.
+            # profile of the kernel code built now; null when that profile is stale.
             "mfma_busy_pct": None if mfma is None else mfma[0],
             "executed_tflop": None if mfma is None else mfma[1],
         },
@@ -244,20 +269,71 @@ def main() -> int:
     if features:
         out["config"]["features"] = {"bias": args.bias, "dbias": bool(args.dbias),
                                      "dropout_p": args.dropout}
-    if args.copy_calibration:
-        src = torch.empty(256 << 20, dtype=torch.bfloat16, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize(dev)
-        dst.copy_(src)
-        torch.cuda.synchronize(dev)
-        out["copy_calibration_bytes"] = {"read": src.numel() * 2, "write": dst.numel() * 2}
-        del src, dst
-    if not args.no_cpu_baseline and not features:
-        log("[bench] cpu baseline: fp64 oracle backward on one kv-head group ...")
-        out["cpu_baseline"] = cpu_baseline(case, x)
-        log(f"[bench] cpu baseline {out['cpu_baseline']['value']:.4f} TFLOP/s "
-            f"({out['cpu_baseline']['seconds']:.1f} s, {out['cpu_baseline']['cores']} threads)")
-    print(json.dumps(out), flush=True)
+    return out, x
+
+
+def inputs_of(case):
+    from exact_attention_backward_fa_amd import inputs
+    return inputs.make_inputs(case)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--dq-mode", default="auto", choices=["auto", "atomic", "separate"])
+    ap.add_argument("--workload", default=None,
+                    help="case name, or several separated by commas (one JSON line each); "
+                         "default: the headline workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bias", default="none", choices=["none", "keys", "full"],
+                    help="additive score bias: a per-key [B,1,1,N_kv] padding mask, or a "
+                         "full [B,Hq,N_q,N_kv] bias (timed through fa_*_bias_dropout)")
+    ap.add_argument("--dbias", action="store_true", help="also write dBias [B,Hq,N_q,N_kv]")
+    ap.add_argument("--dropout", type=float, default=0.0, help="dropout probability of P")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, copy a 512 MiB buffer once (known traffic) so that "
+                         "a counter profile of this run can scale FETCH_SIZE/WRITE_SIZE")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the backward shards by (batch, kv head) group with no communication; "
+              "run --gpus 1)", file=sys.stderr, flush=True)
+        return 2
+    features = args.bias != "none" or args.dbias or args.dropout > 0.0
+    if features and args.dq_mode == "atomic":
+        log("[bench] bias, dBias and dropout run on the separate dQ path only")
+        return 2
+
+    import torch
+    from exact_attention_backward_fa_amd import inputs
+
+    names = (args.workload or inputs.HEADLINE).split(",")
+    cases = [inputs.case_by_name(nm.strip()) for nm in names]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    for case in cases:
+        out, x = measure(case, args, dev)
+        if args.copy_calibration:
+            src = torch.empty(256 << 20, dtype=torch.bfloat16, device=dev).fill_(1.0)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize(dev)
+            dst.copy_(src)
+            torch.cuda.synchronize(dev)
+            out["copy_calibration_bytes"] = {"read": src.numel() * 2, "write": dst.numel() * 2}
+            del src, dst
+        if not args.no_cpu_baseline and not features and len(cases) == 1:
+            log("[bench] cpu baseline: fp64 oracle backward on one kv-head group ...")
+            out["cpu_baseline"] = cpu_baseline(case, x)
+            log(f"[bench] cpu baseline {out['cpu_baseline']['value']:.4f} TFLOP/s "
+                f"({out['cpu_baseline']['seconds']:.1f} s, {out['cpu_baseline']['cores']} threads)")
+            log("[bench] cpu context: model, BLAS, single-thread oracle on the small families ...")
+            out["cpu_baseline"]["context"] = cpu_context()
+        print(json.dumps(out), flush=True)
+        del x
+        torch.cuda.empty_cache()
     return 0
 
 

@@ -165,16 +165,23 @@ int bwd_checked(const BwdCall& c, int dq_mode, void* ev_begin, void* ev_end, voi
   hipStream_t s = (hipStream_t)stream;
   if (nrows == 0 && nk == 0) return FA_OK;  // nothing to compute; no HIP call at all
   (void)hipGetLastError();
-  if (launch_bwd_pre(a, atomic, s) != hipSuccess) return FA_ERR_HIP;
-  if (ev_begin && hipEventRecord((hipEvent_t)ev_begin, s) != hipSuccess) return FA_ERR_HIP;
-  if (launch_bwd_dkdv(a, atomic, s) != hipSuccess) return FA_ERR_HIP;
-  if (ev_end && hipEventRecord((hipEvent_t)ev_end, s) != hipSuccess) return FA_ERR_HIP;
   if (atomic) {
+    // preprocess (rows, counters, float32 dQ buffer) -> fused dK/dV/dQ -> convert
+    if (launch_bwd_pre(a, true, s) != hipSuccess) return FA_ERR_HIP;
+    if (ev_begin && hipEventRecord((hipEvent_t)ev_begin, s) != hipSuccess) return FA_ERR_HIP;
+    if (launch_bwd_dkdv(a, true, s) != hipSuccess) return FA_ERR_HIP;
+    if (ev_end && hipEventRecord((hipEvent_t)ev_end, s) != hipSuccess) return FA_ERR_HIP;
     if (launch_bwd_dq_convert(a, s) != hipSuccess) return FA_ERR_HIP;
-  } else {
-    if (launch_dbias_fill(a, s) != hipSuccess) return FA_ERR_HIP;
-    if (launch_bwd_dq(a, s) != hipSuccess) return FA_ERR_HIP;
+    return FA_OK;
   }
+  // counters -> dQ pass (which also leaves -D and LSE * log2 e of every query row
+  // for the next kernel) -> dK/dV
+  if (launch_sched_clear(a, s) != hipSuccess) return FA_ERR_HIP;
+  if (launch_dbias_fill(a, s) != hipSuccess) return FA_ERR_HIP;
+  if (launch_bwd_dq(a, s) != hipSuccess) return FA_ERR_HIP;
+  if (ev_begin && hipEventRecord((hipEvent_t)ev_begin, s) != hipSuccess) return FA_ERR_HIP;
+  if (launch_bwd_dkdv(a, false, s) != hipSuccess) return FA_ERR_HIP;
+  if (ev_end && hipEventRecord((hipEvent_t)ev_end, s) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
 

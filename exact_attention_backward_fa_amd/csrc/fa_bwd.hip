@@ -23,6 +23,18 @@ __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict
 }
 
 
+// Clears the dK/dV and dQ work-queue counters (the row preprocess does it on the
+// atomic path).
+__global__ __launch_bounds__(64) void sched_clear_kernel(int* __restrict__ sched) {
+  if (threadIdx.x < 32) sched[threadIdx.x] = 0;
+}
+
+hipError_t launch_sched_clear(const BwdArgs& a, hipStream_t s) {
+  if (a.sched == nullptr) return hipSuccess;
+  hipLaunchKernelGGL(sched_clear_kernel, dim3(1), dim3(64), 0, s, a.sched);
+  return hipGetLastError();
+}
+
 // dBias entries the dQ pass never visits: under the causal mask, (row i, key j)
 // with j > i + N_kv - N_q is masked, P and dS are zero there, and whole key tiles
 // of them are skipped.  Block (x, y) writes zeros to keys 2048 y .. of row x.

@@ -1,16 +1,18 @@
 // Backward kernels of exact softmax attention.
 //
-//   bwd_pre   D_i = sum_d dO_id O_id per query row (rustytorch
-//             "flash_attention_backward.cu" computes this row dot product inside
-//             its tiled kernel; the Triton issue "Extra transposes cause 8x speedup
-//             for sequence-parallel Flash Attention backward" loads it precomputed),
-//             LSE rescaled to the log2 domain, and, for the atomic dQ path, the
-//             float32 dQ buffer cleared.
+//   bwd_dq    query-block-parallel dQ pass (the decomposition of the rustytorch
+//             kernel's grid), recomputing S, P, dP and dS; writes dQ once.  It runs
+//             first and also does the row preprocess of its rows: D_i = sum_d
+//             dO_id O_id (rustytorch "flash_attention_backward.cu" computes this
+//             row dot product inside its tiled kernel; the Triton issue "Extra
+//             transposes cause 8x speedup for sequence-parallel Flash Attention
+//             backward" loads it precomputed) and LSE in the log2 domain, stored
+//             for the dK/dV kernel.
 //   bwd_dkdv  key/value-block-parallel dK and dV (the Triton issue's _bwd_kernel
 //             structure: one program per key block, K and V resident, a loop over
 //             query blocks).
-//   bwd_dq    query-block-parallel dQ pass (the decomposition of the rustytorch
-//             kernel's grid), recomputing S, P, dP and dS; writes dQ once.
+//   bwd_pre   the row preprocess as a kernel of its own, for the atomic dQ path,
+//             which also needs its float32 dQ buffer cleared.
 //   dq_convert  float32 dQ buffer -> dtype (atomic path).
 //
 // Per (query tile i, key tile j) the math is, with s the softmax scale:
@@ -19,12 +21,13 @@
 // Exponentials run in the log2 domain: P = exp2(S * s * log2 e - LSE_i * log2 e).
 //
 // Both main kernels give each wave 64 resident rows (keys for dK/dV, queries for
-// dQ) so that every operand read from LDS feeds several MFMAs: the score products
-// (S, dP or their transposes) are 16x16x32 MFMAs whose LDS operand serves 4 tiles
-// of 16 resident rows, and the gradient products are 32x32x16 MFMAs whose LDS
-// operand serves 2 tiles of 32.  The streamed tile is processed in sub-blocks of
-// 16 rows, software-pipelined so that the softmax / dS arithmetic of one sub-block
-// runs while the matrix pipe works on the products of the next.
+// dQ; 32 at d = 256 and in the bias / dropout instances) so that every operand
+// read from LDS feeds several MFMAs: all products are 16x16x32 MFMAs; an LDS
+// operand of a score product (S, dP or their transposes) serves the 4 tiles of 16
+// resident rows, and one of a gradient product serves every head-dim tile of the
+// accumulator.  The streamed tile is processed in sub-blocks of 16 rows,
+// software-pipelined so that the softmax / dS arithmetic of one sub-block runs
+// while the matrix pipe works on the products of the next.
 #pragma once
 
 #include "fa_bwd_common.hpp"
@@ -150,8 +153,11 @@ struct DqPlace {
 };
 
 // ---------------------------------------------------------------------------
-// Row preprocess.  A row is handled by LPR lanes (D/8 rounded up to a power of
-// two); lane `part` < D/8 reads 16 bytes of O and dO, the others add nothing.
+// Row preprocess of the atomic dQ path (on the separate path the dQ pass does it
+// for its own rows): -D, LSE * log2(e), the work-queue counters cleared and the
+// float32 dQ buffer zeroed.  A row is handled by LPR lanes (D/8 rounded up to a
+// power of two); lane `part` < D/8 reads 16 bytes of O and dO, the others add
+// nothing.
 template <int D>
 constexpr int pre_lanes_per_row() {
   int n = 1;
@@ -753,6 +759,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     const uint16_t* __restrict__ K = p.k + kbase * D;
     const uint16_t* __restrict__ V = p.v + kbase * D;
 
+    // The row preprocess of this item's query rows: D = rowsum(dO o O) and
+    // LSE * log2(e) (+inf for a row that sees no key), kept for the softmax here
+    // and stored for the dK/dV kernel, which runs after this pass.  A query row's
+    // head dims are spread over the four lanes j4 = 0..3 of its column, as its Q
+    // and dO operands are.
     u32x4 qb[QT][NK], db[QT][NK];
     float lq[QT];
     f32x4 nd[QT];  // -D of the lane's query, in every element: where dP^T starts
@@ -760,17 +771,28 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     for (int t = 0; t < QT; ++t) {
       const int q = qw + 16 * t + l16;
       const bool ok = q < p.Nq;
+      float dsum = 0.f;
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
         qb[t][s] = ok ? ld16(p.q + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
         db[t][s] = ok ? ld16(p.dout + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
+        const u32x4 ov = ok ? ld16(p.o + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          dsum += Dt<DT>::lo(ov[j]) * Dt<DT>::lo(db[t][s][j]) + Dt<DT>::hi(ov[j]) * Dt<DT>::hi(db[t][s][j]);
       }
-      lq[t] = ok ? p.lse2[qbase + q] : INFINITY;
-      const float x = ok ? p.ndelta[qbase + q] : 0.f;
-      nd[t][0] = x;
-      nd[t][1] = x;
-      nd[t][2] = x;
-      nd[t][3] = x;
+      dsum += __shfl_xor(dsum, 16);
+      dsum += __shfl_xor(dsum, 32);
+      const float L = ok ? p.lse[qbase + q] : -INFINITY;
+      lq[t] = L == -INFINITY ? INFINITY : L * kLog2e;
+      if (ok && j4 == 0) {
+        p.ndelta[qbase + q] = -dsum;
+        p.lse2[qbase + q] = lq[t];
+      }
+      nd[t][0] = -dsum;
+      nd[t][1] = -dsum;
+      nd[t][2] = -dsum;
+      nd[t][3] = -dsum;
     }
     f32x4 acc[QT][2 * NK];  // dQ, per query tile and 16-column head-dim tile
 #pragma unroll

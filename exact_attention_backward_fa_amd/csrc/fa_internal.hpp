@@ -65,7 +65,7 @@ struct BwdArgs {
   float* lse2;    // [B*Hq*Nq]      LSE * log2(e), +inf for rows that see no key
   float* dq_acc;  // [B*Hq*Nq*d]    float32 dQ accumulator (atomic path only)
   int* sched;     // [32]           work-queue counters of the dK/dV and dQ kernels (zeroed
-                  //                by the preprocess); null: static work split
+                  //                before them); null: static work split
   Extras x;
 };
 
@@ -139,7 +139,11 @@ hipError_t dispatch(const Problem& pb, int ft, F&& f) {
   };
   return pb.dtype == 0 ? by_d(integral_constant<int, 0>()) : by_d(integral_constant<int, 1>());
 }
+// Row preprocess kernel (-D, LSE * log2 e, counters cleared, float32 dQ buffer
+// zeroed when asked): the atomic dQ path only; on the separate path the dQ pass
+// does the row preprocess and launch_sched_clear clears the counters.
 hipError_t launch_bwd_pre(const BwdArgs& a, bool zero_dq_acc, hipStream_t s);
+hipError_t launch_sched_clear(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, bool atomic_dq, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dq_convert(const BwdArgs& a, hipStream_t s);

@@ -1,13 +1,13 @@
 // fa_bwd_noalloc: the backward for callers that cannot allocate (code under HIP
 // graph capture, tight serving loops, harnesses that forbid hipMalloc).  Its
-// scratch memory - the per-row -D and LSE*log2(e) of the preprocess and the
-// dK/dV and dQ work-queue counters - lives in a file-scope device array instead
-// of a caller workspace.  Each device holds its own copy of the array until the
-// process ends; host code reaches it only through the address hipGetSymbolAddress
-// returns for the current device (the array's name is a host-side stand-in, not
-// a device address).  Every call on a device shares that device's array, so calls
-// that overlap on one device race; the preprocess kernel of every call clears the
-// counters before the kernels that use them run.
+// scratch memory - the per-row -D and LSE*log2(e) that the dQ pass leaves for the
+// dK/dV kernel, and the two kernels' work-queue counters - lives in a file-scope
+// device array instead of a caller workspace.  Each device holds its own copy of
+// the array until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (the array's name is a
+// host-side stand-in, not a device address).  Every call on a device shares that device's array, so calls
+// that overlap on one device race; every call clears the counters (with a kernel,
+// not a memset) before the kernels that use them run.
 #include "fa_mi355x.h"
 
 #include <mutex>

@@ -3,6 +3,7 @@
     python -m exact_attention_backward_fa_amd.profiling trace  <dir> <out.md> "<command>"
     python -m exact_attention_backward_fa_amd.profiling traffic <fetch_dir> <write_dir> <out.txt> "<commands>"
     python -m exact_attention_backward_fa_amd.profiling mfma <dir> <out.txt> "<command>"
+    python -m exact_attention_backward_fa_amd.profiling workloads <lines.jsonl> <out.md> "<command>"
 
 ``trace`` reads the kernel statistics a ``rocprofv3 --kernel-trace --stats
 --output-format csv`` run writes and tabulates per-kernel average durations.
@@ -183,6 +184,29 @@ def read_traffic(kernel_prefix: str):
     return None
 
 
+def workloads_summary(jsonl: str, command: str) -> str:
+    """A table of the benchmark's JSON lines (one per workload)."""
+    out = ["# fa_bwd throughput per workload (bench.py JSON lines)", "",
+           f"Command: `{command}`", "",
+           "TFLOP/s counts 2.5x the forward's 4*N_q*N_kv*d flops per query head, halved "
+           "for causal; % is of the 2516.6 TFLOP/s dense bf16/fp16 MFMA peak.", "",
+           "| workload | dQ path | fwd ms | bwd ms | bwd TFLOP/s | % of peak | dK/dV kernel ms | "
+           "dK/dV TFLOP/s |",
+           "|---|---|---|---|---|---|---|---|"]
+    for line in open(jsonl):
+        line = line.strip()
+        if not line.startswith("{"):
+            continue
+        r = json.loads(line)
+        rf = r.get("roofline") or {}
+        km = rf.get("kernel_ms")
+        ach = rf.get("achieved")
+        out.append(f"| {r['config']['workload']} | {r['config'].get('dq_path')} | {r['fwd_ms']:.4g} | "
+                   f"{r['bwd_ms']:.4g} | {r['value']:.1f} | {r['pct_of_peak']:.1f} | "
+                   f"{'-' if km is None else f'{km:.4g}'} | {'-' if ach is None else f'{ach:.1f}'} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv) -> int:
     if argv[1] == "trace":
         _, _, d, out, cmd = argv
@@ -193,6 +217,9 @@ def main(argv) -> int:
     elif argv[1] == "mfma":
         _, _, d, out, cmd = argv
         text = mfma_summary(d, cmd)
+    elif argv[1] == "workloads":
+        _, _, jsonl, out, cmd = argv
+        text = workloads_summary(jsonl, cmd)
     else:
         raise SystemExit(__doc__)
     with open(out, "w") as f:

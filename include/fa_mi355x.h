@@ -130,9 +130,11 @@ size_t fa_bwd_ex_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
  * (callers need not zero them).  workspace: caller-owned device memory of at
  * least fa_bwd_workspace_bytes(...) bytes, 16-byte aligned, not shared with a
  * concurrent call; its contents on entry do not matter.  Kernels run in order
- * on `stream`: row preprocess (D = rowsum(dO o O)), the key/value-block-parallel
- * dK/dV kernel, then the dQ path FA_DQ_AUTO selects.  Returns FA_OK or an
- * FA_ERR_* code; a rejected call launches nothing and writes nothing.
+ * on `stream`, for the dQ path FA_DQ_AUTO selects: with the separate pass, the
+ * query-block-parallel dQ pass (which also computes D = rowsum(dO o O) of its
+ * rows) and then the key/value-block-parallel dK/dV kernel; with float atomics,
+ * a row preprocess (D), the fused dK/dV/dQ kernel and a dQ conversion.  Returns
+ * FA_OK or an FA_ERR_* code; a rejected call launches nothing and writes nothing.
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -235,8 +237,8 @@ int fa_bwd_bias_dropout(const void* q, const void* k, const void* v, const void*
  * nothing, when the problem needs more (with 16 MiB: B*Hq*N_q up to about 2.09
  * million query rows).  Every call on a device shares that device's array: calls
  * that overlap on one device (several streams or host threads) race and must be
- * serialised by the caller.  Each call's preprocess kernel clears the counters
- * that must start at zero.
+ * serialised by the caller.  Each call clears the counters that must start at
+ * zero.
  */
 #define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
 int fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
