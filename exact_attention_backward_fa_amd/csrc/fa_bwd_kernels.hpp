@@ -761,38 +761,25 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 
     // The row preprocess of this item's query rows: D = rowsum(dO o O) and
     // LSE * log2(e) (+inf for a row that sees no key), kept for the softmax here
-    // and stored for the dK/dV kernel, which runs after this pass.  A query row's
-    // head dims are spread over the four lanes j4 = 0..3 of its column, as its Q
-    // and dO operands are.
-    u32x4 qb[QT][NK], db[QT][NK];
+    // and stored at the end of the item for the dK/dV kernel, which runs after
+    // this pass.  A query row's head dims are spread over the four lanes
+    // j4 = 0..3 of its column, as its Q and dO operands are.  O is loaded with the
+    // other preloads and D formed after the one wait for them below.
+    u32x4 qb[QT][NK], db[QT][NK], ob[QT][NK];
     float lq[QT];
     f32x4 nd[QT];  // -D of the lane's query, in every element: where dP^T starts
 #pragma unroll
     for (int t = 0; t < QT; ++t) {
       const int q = qw + 16 * t + l16;
       const bool ok = q < p.Nq;
-      float dsum = 0.f;
 #pragma unroll
       for (int s = 0; s < NK; ++s) {
         qb[t][s] = ok ? ld16(p.q + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
         db[t][s] = ok ? ld16(p.dout + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
-        const u32x4 ov = ok ? ld16(p.o + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          dsum += Dt<DT>::lo(ov[j]) * Dt<DT>::lo(db[t][s][j]) + Dt<DT>::hi(ov[j]) * Dt<DT>::hi(db[t][s][j]);
+        ob[t][s] = ok ? ld16(p.o + (qbase + q) * D + 32 * s + 8 * j4) : zero_u4();
       }
-      dsum += __shfl_xor(dsum, 16);
-      dsum += __shfl_xor(dsum, 32);
       const float L = ok ? p.lse[qbase + q] : -INFINITY;
       lq[t] = L == -INFINITY ? INFINITY : L * kLog2e;
-      if (ok && j4 == 0) {
-        p.ndelta[qbase + q] = -dsum;
-        p.lse2[qbase + q] = lq[t];
-      }
-      nd[t][0] = -dsum;
-      nd[t][1] = -dsum;
-      nd[t][2] = -dsum;
-      nd[t][3] = -dsum;
     }
     f32x4 acc[QT][2 * NK];  // dQ, per query tile and 16-column head-dim tile
 #pragma unroll
@@ -1104,6 +1091,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     // for here: the compiler then knows the preloads have landed and puts no wait of
     // its own (which would count the copies wrongly) into the loop.
     wait_vmem();
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      float dsum = 0.f;
+#pragma unroll
+      for (int s = 0; s < NK; ++s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dsum = Dt<DT>::dot2(ob[t][s][j], db[t][s][j], dsum);
+      }
+      dsum += __shfl_xor(dsum, 16);
+      dsum += __shfl_xor(dsum, 32);
+      nd[t][0] = -dsum;
+      nd[t][1] = -dsum;
+      nd[t][2] = -dsum;
+      nd[t][3] = -dsum;
+    }
     lds_barrier();
     // the first tile's leading operands (its "previous" buffer is the same one; the
     // previous-pair product it feeds is multiplied by zeros)
@@ -1146,6 +1148,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     settle(acc);
     uint16_t* stage = &sKV[0][0] + w * QW * (D + 8);
     store_block_c16<DT, D, QT>(acc, p.scale, stage, p.dq + qbase * D, qw, p.Nq, lane);
+#pragma unroll
+    for (int t = 0; t < QT; ++t) {
+      const int q = qw + 16 * t + l16;
+      if (q < p.Nq && j4 == 0) {
+        p.ndelta[qbase + q] = nd[t][0];
+        p.lse2[qbase + q] = lq[t];
+      }
+    }
   }
 }
 

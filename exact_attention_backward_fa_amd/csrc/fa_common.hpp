@@ -70,6 +70,10 @@ template <> struct Dt<0> {
   static __device__ __forceinline__ uint16_t one(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
   }
+  // c + a.lo * b.lo + a.hi * b.hi (v_dot2c_f32_f16)
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+  }
 };
 
 template <> struct Dt<1> {
@@ -93,6 +97,11 @@ template <> struct Dt<1> {
   }
   static __device__ __forceinline__ uint16_t one(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+  // c + a.lo * b.lo + a.hi * b.hi (v_dot2c_f32_bf16)
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
+                                           c, false);
   }
 };
 
