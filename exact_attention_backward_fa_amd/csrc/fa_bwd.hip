@@ -37,24 +37,48 @@ hipError_t launch_sched_clear(const BwdArgs& a, hipStream_t s) {
 
 // dBias entries the dQ pass never visits: under the causal mask, (row i, key j)
 // with j > i + N_kv - N_q is masked, P and dS are zero there, and whole key tiles
-// of them are skipped.  Block (x, y) writes zeros to keys 2048 y .. of row x.
+// of them are skipped.  Block (x, y) writes zeros to the masked keys among
+// 8192 y .. 8192 y + 8191 of row x, in groups of 8 keys that are 16-byte aligned
+// in memory: a whole group with one 16-byte store, a group cut by the range or
+// the row's ends key by key.
+constexpr int kFillKeys = 8192;
 __global__ __launch_bounds__(256) void dbias_fill_masked_kernel(uint16_t* __restrict__ dbias, int Nq,
-                                                                int Nkv, int off) {
-  const size_t row = blockIdx.x;  // over B * Hq * N_q
+                                                                int Nkv, int off, size_t row0) {
+  const size_t row = row0 + blockIdx.x;  // over B * Hq * N_q
   const int i = (int)(row % (size_t)Nq);
-  const int first = max(0, i + off + 1);  // first masked key of the row
+  const int lo = max(max(0, i + off + 1), (int)blockIdx.y * kFillKeys);  // first masked key
+  const int hi = min(Nkv, (int)(blockIdx.y + 1) * kFillKeys);
+  if (lo >= hi) return;
   uint16_t* dst = dbias + row * (size_t)Nkv;
-  for (int j = blockIdx.y * 2048 + threadIdx.x; j < min(Nkv, (int)(blockIdx.y + 1) * 2048); j += 256)
-    if (j >= first) dst[j] = 0;
+  // e0: the first key whose address is 16-byte aligned (rows are 2-byte aligned)
+  const int e0 = (int)(((16u - ((uint32_t)(uintptr_t)dst & 15u)) & 15u) >> 1);
+  const int g0 = (lo - e0 >= 0) ? (lo - e0) / 8 : -((e0 - lo + 7) / 8);  // floor
+  const int g1 = (hi - e0 + 7 >= 0) ? (hi - e0 + 7) / 8 : 0;              // ceil, exclusive
+  for (int g = g0 + (int)threadIdx.x; g < g1; g += 256) {
+    const int a = e0 + 8 * g;
+    if (a >= lo && a + 8 <= hi) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(dst + a) = z;
+    } else {
+      for (int k = 0; k < 8; ++k)
+        if (a + k >= lo && a + k < hi) dst[a + k] = 0;
+    }
+  }
 }
 
 hipError_t launch_dbias_fill(const BwdArgs& a, hipStream_t s) {
   const size_t rows = (size_t)a.pb.B * a.pb.Hq * a.pb.Nq;
   if (!a.pb.causal || a.x.dbias == nullptr || rows == 0 || a.pb.Nkv == 0) return hipSuccess;
-  const dim3 grid((unsigned)rows, (unsigned)((a.pb.Nkv + 2047) / 2048));
-  hipLaunchKernelGGL(dbias_fill_masked_kernel, grid, dim3(256), 0, s, static_cast<uint16_t*>(a.x.dbias),
-                     a.pb.Nq, a.pb.Nkv, a.pb.Nkv - a.pb.Nq);
-  return hipGetLastError();
+  constexpr size_t kMaxRows = (size_t)1 << 30;  // per launch (grid x limit)
+  for (size_t r0 = 0; r0 < rows; r0 += kMaxRows) {
+    const size_t n = rows - r0 < kMaxRows ? rows - r0 : kMaxRows;
+    const dim3 grid((unsigned)n, (unsigned)((a.pb.Nkv + kFillKeys - 1) / kFillKeys));
+    hipLaunchKernelGGL(dbias_fill_masked_kernel, grid, dim3(256), 0, s,
+                       static_cast<uint16_t*>(a.x.dbias), a.pb.Nq, a.pb.Nkv, a.pb.Nkv - a.pb.Nq, r0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

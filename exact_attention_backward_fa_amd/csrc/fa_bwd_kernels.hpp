@@ -716,7 +716,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 //
 // Step st issues the MFMA stream  S^T_st | dQ half | dP^T_st  with dS_{st-1}
 // computed under S^T_st and P_st under the dQ half and dP^T_st.
-template <int DT, int D, bool CAUSAL, int FT>
+// DBW (bias instances): dBias chunks of 4 keys stored as one 8-byte piece, which
+// needs N_kv % 4 == 0 (8-byte aligned rows, and no chunk straddles a row end);
+// otherwise each key is stored on its own.
+template <int DT, int D, bool CAUSAL, int FT, bool DBW = false>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr bool BIAS = FT >= FT_BIAS, DROP = FT == FT_DROPOUT;
   constexpr int QT = TileShape<D, FT>::RT;  // query tiles of 16 per wave
@@ -860,14 +863,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
                           : buf_rsrc(p.k, 0);
     auto store_dbias = [&](const u32x2& v, int q, int key0) {
       const int base = 2 * ((q - q0) * p.Nkv + key0);
+      if constexpr (DBW) {
+        // key0 and N_kv are multiples of 4: the chunk is wholly in or out of the row
+        bstore64(v, key0 >= 0 && key0 < p.Nkv ? base : 0x7ffffff0, dbr);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool ok = key0 + r >= 0 && key0 + r < p.Nkv;
-        const int off = ok ? base + 2 * r : 0x7ffffff0;
-        if (r & 1)
-          bstore16_hi(v[r >> 1], off, dbr);
-        else
-          bstore16_lo(v[r >> 1], off, dbr);
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = key0 + r >= 0 && key0 + r < p.Nkv;
+          const int off = ok ? base + 2 * r : 0x7ffffff0;
+          if (r & 1)
+            bstore16_hi(v[r >> 1], off, dbr);
+          else
+            bstore16_lo(v[r >> 1], off, dbr);
+        }
       }
     };
 
@@ -1192,6 +1200,12 @@ hipError_t run_dq(const BwdArgs& a, hipStream_t s) {
   const int items = ((a.pb.Nq + BM - 1) / BM) * a.pb.Hq * a.pb.B;
   const int ncu = device_cu_count();
   const dim3 grid((unsigned)(p.sched && ncu > 0 && ncu < items ? ncu : items));
+  if constexpr (FT != FT_PLAIN) {
+    if (p.dbias && p.Nkv % 4 == 0) {
+      hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL, FT, true>), grid, dim3(256), 0, s, p);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL, FT>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }

@@ -368,6 +368,13 @@ __device__ __forceinline__ void bstore16_hi(uint32_t data, int voff, const i32x4
                : "memory");
 }
 
+// 8-byte store of `data` to rsrc + voff (voff a multiple of 8); a lane whose offset
+// lies at or past the resource's end stores nothing.
+__device__ __forceinline__ void bstore64(const u32x2& data, int voff, const i32x4& rsrc) {
+  asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen" : : "v"(data), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // s_waitcnt vmcnt(N): at most N vector-memory operations of this wave still

@@ -95,6 +95,9 @@ BIAS_CASES = [
     # first visible pair (fp16: 10.4 nats, bf16: 44 nats): the rerun path with a bias
     ("rising_bias_fp16", 1, 4, 2, 200, 333, 64, "fp16", False, "ramp", 0.0),
     ("rising_bias_bf16_c", 1, 4, 2, 300, 300, 128, "bf16", True, "ramp", 0.1),
+    # dBias rows longer than one 8192-key block of the masked-entry fill, rows
+    # alternating between two 16-byte alignments (8204 keys), 8-byte dBias stores
+    ("long_rows_dbias_c", 1, 1, 1, 8204, 8204, 64, "fp16", True, None, 0.0),
 ]
 
 
