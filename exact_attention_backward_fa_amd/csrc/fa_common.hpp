@@ -588,6 +588,15 @@ __device__ __forceinline__ float keep_factor(uint32_t word, int byte, uint32_t k
   return ((word >> (8 * byte)) & 0xffu) < keep_t ? scale : 0.f;
 }
 
+// max(a, b, c) in one v_max3_f32.  fmaxf on MFMA results costs a canonicalizing
+// v_max_f32 per input as well (the IEEE mode quiets signalling NaNs first); the
+// scores here are finite or -inf.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Makes a value opaque to the compiler (ON): it is computed once, where placed,
 // and not rematerialized next to its use (a repack right before the MFMA that
 // reads it would be a VALU write of an MFMA source without wait states).

@@ -104,8 +104,8 @@ struct FwdPlace {
     // steps of small head dims, leaving room for the exponentials)
     constexpr int HI = Plan::B1 + 11 < NM - 4 ? Plan::B1 + 11 : NM - 4;
     int prev = Plan::B1;
-    L.level(QT * 5 + 3, Plan::B1, HI);
-    for (int t = 0; t < QT; ++t) prev = mx[t] = L.put(5, prev, HI);
+    L.level(QT * 4 + 3, Plan::B1, HI);
+    for (int t = 0; t < QT; ++t) prev = mx[t] = L.put(4, prev, HI);
     prev = check = L.put(3, prev + 1, HI + 1);
     L.level(8 * QT * issue::kExp + 2 * QT * (issue::kPack + 4 * issue::kMul), prev + 1, NM - 2);
     prev = prev + 1;
@@ -358,8 +358,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
               }
             }
           }
-          mx[t] = fmaxf(fmaxf(fmaxf(sc[0][t][0], sc[0][t][1]), fmaxf(sc[0][t][2], sc[0][t][3])),
-                        fmaxf(fmaxf(sc[1][t][0], sc[1][t][1]), fmaxf(sc[1][t][2], sc[1][t][3])));
+          const float m0 = vmax3(sc[0][t][0], sc[0][t][1], sc[0][t][2]);
+          const float m1 = vmax3(sc[0][t][3], sc[1][t][0], sc[1][t][1]);
+          mx[t] = vmax3(m0, m1, vmax3(sc[1][t][2], sc[1][t][3], sc[1][t][3]));
         }
       });
       if constexpr (PL.check == mi) {
