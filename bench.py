@@ -64,10 +64,14 @@ def cpu_baseline(case, x, min_seconds: float = 10.0, max_groups: int = 8) -> dic
             break
     dt = time.perf_counter() - t0
     flops = done * 2.5 * 4.0 * G * case.Nq * case.Nkv * case.d * (0.5 if case.causal else 1.0)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    rate = flops / dt / 1e12
+    return {"value": rate, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            # the whole workload at the sample's rate (extrapolated, not measured)
+            "extrapolated_full_seconds": round(case.bwd_flops() / (rate * 1e12), 1),
             "sample": f"fp64 oracle backward of {done} (batch, kv head) group(s) of {G} query heads "
-                      f"(N={case.Nq}, d={case.d}, causal) = {done}/{case.B * case.Hkv} of the "
-                      f"workload, {dt:.1f} s; flops counted as the metric counts them",
+                      f"(N={case.Nq}, d={case.d}, {'causal' if case.causal else 'non-causal'}) = "
+                      f"{done}/{case.B * case.Hkv} of the workload, {dt:.1f} s; flops counted as "
+                      f"the metric counts them",
             "seconds": dt}
 
 
@@ -204,12 +208,17 @@ def measure(case, args, dev, log_prefix="[bench]") -> tuple:
 
     fwd_ms = total("f0", "f1") / n
     bwd_ms = total("b0", "b1") / n
+    bwd_each = sorted(ev["b0"][i].elapsed_ms(ev["b1"][i]) for i in range(n))
+    bwd_median = bwd_each[n // 2] if n % 2 else 0.5 * (bwd_each[n // 2 - 1] + bwd_each[n // 2])
     # the dK/dV kernel's own events are recorded on the plain path only (the feature
     # runs' per-kernel split comes from a kernel trace)
     kern_ms = None if features else total("k0", "k1") / n
     bwd_flops = case.bwd_flops()
     fwd_flops = case.fwd_flops()
     value = bwd_flops / (bwd_ms * 1e-3) / 1e12
+    elt = 2  # fp16 / bf16
+    io_bytes = (elt * (4 * case.B * case.Hq * case.Nq * case.d + 4 * case.B * case.Hkv * case.Nkv * case.d)
+                + 8 * case.B * case.Hq * case.Nq)
     # Algorithmic flops of the dK/dV kernel per launch: with the atomic dQ path it
     # performs all five products of the backward (10*Nq*Nkv*d per query head, halved
     # for causal); on the separate path it performs four of them (8*Nq*Nkv*d).
@@ -248,6 +257,11 @@ def measure(case, args, dev, log_prefix="[bench]") -> tuple:
                    "dq_path": resolved},
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "bwd_ms": round(bwd_ms, 4),
+        "bwd_ms_median": round(bwd_median, 4),
+        "bwd_ms_min": round(bwd_each[0], 4),
+        # inputs and outputs that fit the 256 MB Infinity Cache stay cache-resident
+        # from step to step: such timings are warm-cache ones
+        "cache": "warm" if io_bytes < (256 << 20) else "cold",
         "fwd_ms": round(fwd_ms, 4),
         "fwd_tflops": round(fwd_flops / (fwd_ms * 1e-3) / 1e12, 2),
         "roofline": {
@@ -258,6 +272,8 @@ def measure(case, args, dev, log_prefix="[bench]") -> tuple:
             "unit": "TFLOP/s",
             "frac": None if achieved is None else round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
+            "traffic_gbs": None if traffic is None or kern_ms is None
+                           else round(traffic / (kern_ms * 1e-3) / 1e9, 1),
             "kernel_ms": None if kern_ms is None else round(kern_ms, 4),
             # rocprof MfmaUtil (matrix-unit busy share of active SIMD cycles) and the
             # MFMA flops the kernel executes per launch, from the committed counter
