@@ -40,7 +40,7 @@ ATOMIC_HEAD_DIMS = (64, 128)
 # Feature sets (1: additive score bias and its gradient, 2: bias and dropout of P)
 # are built for these head dims; every head dim has the plain set 0.
 FEATURE_HEAD_DIMS = (64, 128)
-FEATURES = (1, 2)
+FEATURES = (1, 2, 3)
 # Backward kernel families compiled per instance (FA_KIND in fa_bwd_inst.hip).
 BWD_KINDS = {0: "pre", 1: "dkdv", 2: "dq", 3: "atomic"}
 

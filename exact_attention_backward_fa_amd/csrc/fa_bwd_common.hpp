@@ -21,7 +21,7 @@ struct BwdParams {
   float* dq_acc;
   int* sched;  // work-queue counters (8 x 64 bits each for dK/dV and dQ) or null
   int B, Hq, Hkv, Nq, Nkv, G, off;  // off = Nkv - Nq (bottom-right causal offset)
-  float scale, scale_log2;
+  float scale, scale_log2, inv_scale;
   size_t rows;  // B * Hq * Nq
   // score bias (null: zero) with element strides, its gradient (null: not wanted),
   // and dropout (keep iff the element's random byte < keep_t; kept P scaled by
@@ -57,6 +57,7 @@ inline BwdParams make_params(const BwdArgs& a) {
   p.off = a.pb.Nkv - a.pb.Nq;
   p.scale = a.pb.scale;
   p.scale_log2 = a.pb.scale * kLog2e;
+  p.inv_scale = 1.0f / a.pb.scale;
   p.rows = (size_t)a.pb.B * a.pb.Hq * a.pb.Nq;
   p.bias = static_cast<const uint16_t*>(a.x.bias);
   p.bias_sb = a.x.bias_sb;

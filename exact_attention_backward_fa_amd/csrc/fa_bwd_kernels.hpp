@@ -71,7 +71,7 @@ struct DqSteps {
 // dropout work the registers.
 template <int D, int FT = 0>
 struct TileShape {
-  static constexpr bool SMALL = D > 128 || FT != 0;
+  static constexpr bool SMALL = D > 128 || tile_bias(FT);
   static constexpr int RT = SMALL ? 2 : 4;    // resident 16-row tiles per wave
   static constexpr int NBUF = SMALL ? 2 : 3;  // LDS buffers of the streamed tiles
 };
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // ragged end of this wave's block take a masked variant of the softmax.
 template <int DT, int D, bool CAUSAL, int FT>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr bool BIAS = FT >= FT_BIAS, DROP = FT == FT_DROPOUT;
+  constexpr bool BIAS = tile_bias(FT), DROP = FT == FT_DROPOUT, KB = FT == FT_KEYBIAS;
   constexpr int KT = TileShape<D, FT>::RT;  // key tiles of 16 per wave
   constexpr int KW = 16 * KT, BN = 4 * KW, BM = 64, NSB = BM / 16;
   constexpr int NK = D / 32;
@@ -273,6 +273,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           kb[kt][s] = key < p.Nkv ? ld16(K + (size_t)key * D + 32 * s + 8 * j4) : zero_u4();
           vb[kt][s] = key < p.Nkv ? ld16(V + (size_t)key * D + 32 * s + 8 * j4) : zero_u4();
         }
+      }
+    }
+    // key-bias instances: bias * log2(e) of this lane's key per key tile (the key is
+    // the lane's column of every score tile)
+    float bl[KB ? KT : 1];
+    if constexpr (KB) {
+      const uint16_t* __restrict__ brow = p.bias + (long long)b * p.bias_sb;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+        const int key = kvw + 16 * kt + l16;
+        bl[kt] = key < p.Nkv ? Dt<DT>::lo(brow[key]) * kLog2e : 0.f;
       }
     }
     f32x4 dk[KT][2 * NK], dv[KT][2 * NK];  // per key tile and 16-column head-dim tile
@@ -472,6 +483,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         float v;
         if constexpr (BIAS)
           v = fmaf(sc[kt][i], p.scale_log2, fmaf(elem4<DT>(bv[kt], i), kLog2e, -lq[i]));
+        else if constexpr (KB)
+          v = fmaf(sc[kt][i], p.scale_log2, bl[kt] - lq[i]);
         else
           v = sc[kt][i] * p.scale_log2 - lq[i];
         if constexpr (MASK) {
@@ -721,7 +734,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 // otherwise each key is stored on its own.
 template <int DT, int D, bool CAUSAL, int FT, bool DBW = false>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
-  constexpr bool BIAS = FT >= FT_BIAS, DROP = FT == FT_DROPOUT;
+  constexpr bool BIAS = tile_bias(FT), DROP = FT == FT_DROPOUT, KB = FT == FT_KEYBIAS;
   constexpr int QT = TileShape<D, FT>::RT;  // query tiles of 16 per wave
   constexpr int QW = 16 * QT, BM = 4 * QW, BN = 64, NSB = BN / 16;
   constexpr int NK = D / 32;
@@ -733,10 +746,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
   constexpr int BRS = BiasDma::RS;
   constexpr int BPW = BIAS ? BiasDma::PER_WAVE : 0;
   constexpr int KVPW = 2 * BN * PadTile<D>::GR / 256;
-  constexpr int OPS = KVPW + BPW;  // copy instructions per fetch per wave: K or V, bias
+  // copy instructions per fetch per wave: K or V, bias tile, key-bias row
+  constexpr int OPS = KVPW + BPW + (KB ? 1 : 0);
   constexpr int LA = 2;
   __shared__ __attribute__((aligned(16))) uint16_t sKV[NBUF][2 * BN * RS];  // K, V: a padded pair
   __shared__ __attribute__((aligned(16))) uint16_t sB[BIAS ? NBUF : 1][BIAS ? BM * BRS : 8];
+  // key-bias instances: each wave's copy of the tile's keys' bias (keys k0 .. k0 + 63
+  // in its first 128 bytes; a 16-byte-per-lane copy fills 1 KB)
+  __shared__ __attribute__((aligned(16))) uint16_t sKB[KB ? NBUF : 1][KB ? 4 * 512 : 8];
   static_assert(NBUF * 2 * BN * RS >= 4 * QW * (D + 8), "the output staging must fit the tile buffers");
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -808,12 +825,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     static_assert(Copy::PER_WAVE == KVPW, "key/value copies per wave");
     const uint16_t* __restrict__ tsrc = w < 2 ? K : V;
     struct Src {
-      i32x4 t, bs;  // this wave's K or V tile; bias tile (bias instances)
+      i32x4 t, bs;  // this wave's K or V tile; bias tile or key-bias row (bias instances)
     };
     // bias element offset of this item's first query row (key 0)
     const long long bq0 = BIAS ? (long long)b * p.bias_sb + (long long)h * p.bias_sh +
                                      (long long)q0 * p.bias_sq
-                               : 0;
+                               : KB ? (long long)b * p.bias_sb : 0;
     auto src_of = [&](int kt) {
       const int k0 = min(kt, nkt - 1) * BN;
       Src sr;
@@ -825,6 +842,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         const int rows = min(BM, p.Nq - q0);
         const int bytes = p.bias ? 2 * ((rows - 1) * (int)p.bias_sq + (((p.Nkv + 7) & ~7) - k0)) : 0;
         sr.bs = buf_rsrc(p.bias ? p.bias + bq0 + k0 : p.k, bytes);
+      }
+      if constexpr (KB) {
+        // the row of batch b from key k0, readable up to N_kv rounded up to 8
+        sr.bs = buf_rsrc(p.bias + bq0 + k0, 2 * (((p.Nkv + 7) & ~7) - k0));
       }
       return sr;
     };
@@ -841,6 +862,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       constexpr int c = decltype(cc)::value;
       if constexpr (c < KVPW) {
         bdma16<Copy::template lds_offset<c>>(voff[c], sr.t, lds_u32(sKV[buf]) + wave_off);
+      } else if constexpr (KB) {
+        bdma16<0>(16 * lane, sr.bs, lds_u32(sKB[buf]) + 1024 * w);
       } else {
         constexpr int cb_ = c - KVPW;
         bdma16<BiasDma::template lds_offset<cb_>>(voffb[cb_], sr.bs,
@@ -878,6 +901,19 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         }
       }
     };
+
+    // key-bias instances: bias / scale of keys 4 j4 .. + 3 of sub-block sb of the
+    // tile in buffer buf, the accumulator the S^T product starts from (so that
+    // c (S + b / scale) = c S + b log2 e); cbk[sb % 2] for sub-block sb, filled one
+    // step ahead
+    auto key_bias = [&](int buf, int sb) -> f32x4 {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(sKB[buf] + 512 * w + 16 * sb + 4 * j4);
+      f32x4 r;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[i] = elem4<DT>(v, i) * p.inv_scale;
+      return r;
+    };
+    f32x4 cbk[2];
 
     // Carried from tile to tile: the first LA operands of the next tile, P^T and
     // dP^T of the last sub-block (sc[1], dp), whose dS^T is computed in step 0 of
@@ -992,6 +1028,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
           wait_vmem();
           tile_barrier();
         }
+        if constexpr (KB) {
+          // the next sub-block's: of this tile, or (step 3, after the mid-tile
+          // barrier) the next tile's first; past the last tile a buffer no product
+          // reads
+          if constexpr (st < NSB - 1)
+            cbk[(st + 1) % 2] = key_bias(cur, st + 1);
+          else
+            cbk[0] = key_bias(nxt, 0);
+        }
       };
       auto operand = [&](auto stc, auto oc) -> u32x4 { return dq_operand(stc, oc, Kt, Kp); };
       // operand oc of the next tile, whose previous buffer is this one
@@ -1009,7 +1054,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         constexpr int k = Plan::stage(m), loc = Plan::local(m);
         if constexpr (k == 0) {
           constexpr int s = loc / QT, t = loc % QT;
-          if constexpr (s == 0)
+          if constexpr (s == 0 && KB)
+            sc[cs][t] = Mx<DT>::first16c(op, qb[t][s], cbk[st % 2]);
+          else if constexpr (s == 0)
             sc[cs][t] = Mx<DT>::first16(op, qb[t][s]);
           else
             Mx<DT>::acc16(sc[cs][t], op, qb[t][s]);
@@ -1120,6 +1167,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
     static_for<LA>([&](auto oc) {
       carry[decltype(oc)::value] = dq_operand(std::integral_constant<int, 0>(), oc, sKV[0], sKV[0]);
     });
+    if constexpr (KB) cbk[0] = key_bias(0, 0);
     // Iteration kt works on buffer kt % NBUF; from its middle on it copies tile
     // kt + NBUF - 1 into the buffer of iteration kt - 1.
     int kt = 0, cur = 0;
@@ -1200,7 +1248,7 @@ hipError_t run_dq(const BwdArgs& a, hipStream_t s) {
   const int items = ((a.pb.Nq + BM - 1) / BM) * a.pb.Hq * a.pb.B;
   const int ncu = device_cu_count();
   const dim3 grid((unsigned)(p.sched && ncu > 0 && ncu < items ? ncu : items));
-  if constexpr (FT != FT_PLAIN) {
+  if constexpr (tile_bias(FT)) {
     if (p.dbias && p.Nkv % 4 == 0) {
       hipLaunchKernelGGL((bwd_dq_kernel<DT, D, CAUSAL, FT, true>), grid, dim3(256), 0, s, p);
       return hipGetLastError();

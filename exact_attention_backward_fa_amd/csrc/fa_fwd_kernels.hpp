@@ -49,7 +49,7 @@ struct FwdParams {
   uint16_t* o;
   float* lse;
   int B, Hq, Hkv, Nq, Nkv, G, off;  // off = Nkv - Nq (bottom-right causal offset)
-  float scale_log2;
+  float scale_log2, inv_scale;
   // score bias (null: zero) with element strides; dropout of the P that weights V
   // (keep iff the element's random byte < keep_t, kept P scaled by drop_scale)
   const uint16_t* bias;
@@ -77,11 +77,12 @@ struct FwdSteps {
 // 16-row tiles) and triple-buffered key/value tiles up to d = 128; at d = 256 a
 // wave keeps 32 queries (Q and the O accumulators of 64 would not fit its
 // registers) and the tiles are double-buffered (three would not fit the LDS).
-// The bias and dropout instances take the small shape too (the bias tiles need the
-// LDS, the bias and dropout work the registers).
+// The bias-tile and dropout instances take the small shape too (the bias tiles need
+// the LDS, the bias and dropout work the registers); the key-bias instances keep the
+// plain shape.
 template <int D, int FT = 0>
 struct FwdShape {
-  static constexpr bool SMALL = D > 128 || FT != 0;
+  static constexpr bool SMALL = D > 128 || tile_bias(FT);
   static constexpr int QT = SMALL ? 2 : 4;
   static constexpr int NBUF = SMALL ? 2 : 3;
 };
@@ -129,7 +130,7 @@ struct FwdPlace {
 
 template <int DT, int D, bool CAUSAL, int FT>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
-  constexpr bool BIAS = FT >= FT_BIAS, DROP = FT == FT_DROPOUT;
+  constexpr bool BIAS = tile_bias(FT), DROP = FT == FT_DROPOUT, KB = FT == FT_KEYBIAS;
   constexpr int QT = FwdShape<D, FT>::QT;  // query tiles of 16 per wave
   constexpr int QW = 16 * QT, BM = 4 * QW, BN = 64, NST = 2;
   constexpr int NK = D / 32;
@@ -141,10 +142,14 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   constexpr int BRS = BiasDma::RS;
   constexpr int BPW = BIAS ? BiasDma::PER_WAVE : 0;
   constexpr int KVPW = 2 * BN * PadTile<D>::GR / 256;
-  constexpr int OPS = KVPW + BPW;  // copy instructions per fetch per wave: K or V, bias
+  // copy instructions per fetch per wave: K or V, bias tile, key-bias row
+  constexpr int OPS = KVPW + BPW + (KB ? 1 : 0);
   constexpr int LA = 2;
   __shared__ __attribute__((aligned(16))) uint16_t sKV[NBUF][2 * BN * RS];  // K, V: a padded pair
   __shared__ __attribute__((aligned(16))) uint16_t sB[BIAS ? NBUF : 1][BIAS ? BM * BRS : 8];
+  // key-bias instances: each wave's copy of the tile's keys' bias (keys k0 .. k0 + 63
+  // in its first 128 bytes; a 16-byte-per-lane copy fills 1 KB)
+  __shared__ __attribute__((aligned(16))) uint16_t sKB[KB ? NBUF : 1][KB ? 4 * 512 : 8];
   static_assert(NBUF * 2 * BN * RS >= 4 * QW * (D + 8), "the output staging must fit the tile buffers");
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -205,12 +210,12 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   static_assert(Copy::PER_WAVE == KVPW, "key/value copies per wave");
   const uint16_t* __restrict__ tsrc = w < 2 ? K : V;
   struct Src {
-    i32x4 t, bs;  // this wave's K or V tile; bias tile (bias instances)
+    i32x4 t, bs;  // this wave's K or V tile; bias tile or key-bias row (bias instances)
   };
   // bias element offset of this workgroup's first query row (key 0)
   const long long bq0 = BIAS ? (long long)b * p.bias_sb + (long long)h * p.bias_sh +
                                    (long long)q0 * p.bias_sq
-                             : 0;
+                             : KB ? (long long)b * p.bias_sb : 0;
   auto src_of = [&](int kt) {
     const int k0 = min(kt, nkt - 1) * BN;
     Src sr;
@@ -221,6 +226,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       const int rows = min(BM, p.Nq - q0);
       const int bytes = p.bias ? 2 * ((rows - 1) * (int)p.bias_sq + (((p.Nkv + 7) & ~7) - k0)) : 0;
       sr.bs = buf_rsrc(p.bias ? p.bias + bq0 + k0 : p.k, bytes);
+    }
+    if constexpr (KB) {
+      // the row of batch b from key k0, readable up to N_kv rounded up to 8
+      sr.bs = buf_rsrc(p.bias + bq0 + k0, 2 * (((p.Nkv + 7) & ~7) - k0));
     }
     return sr;
   };
@@ -237,12 +246,25 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     constexpr int ci = decltype(cc)::value;
     if constexpr (ci < KVPW) {
       bdma16<Copy::template lds_offset<ci>>(voff[ci], sr.t, lds_u32(sKV[buf]) + wave_off);
+    } else if constexpr (KB) {
+      bdma16<0>(16 * lane, sr.bs, lds_u32(sKB[buf]) + 1024 * w);
     } else {
       constexpr int cb_ = ci - KVPW;
       bdma16<BiasDma::template lds_offset<cb_>>(voffb[cb_], sr.bs,
                                                 lds_u32(sB[buf]) + BiasDma::lds_wave_offset(w));
     }
   };
+  // key-bias instances: bias / scale of keys 4 j4 .. + 3 of sub-block sb of pair J
+  // of the tile in buffer buf: the accumulator the S^T product starts from, so the
+  // scores come out biased (c (S + b / scale) = c S + b log2 e)
+  auto key_bias = [&](int buf, int J, int sb) -> f32x4 {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(sKB[buf] + 512 * w + 16 * (2 * J + sb) + 4 * j4);
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = elem4<DT>(v, i) * p.inv_scale;
+    return r;
+  };
+  f32x4 cbk[2][2];  // key bias accumulator starts of pair J, sub-block sb
   auto copy_all = [&](int kt, int buf) {
     const Src sr = src_of(kt);
     static_for<OPS>([&](auto cc) { copy_part(cc, sr, buf); });
@@ -271,6 +293,11 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     using Steps = FwdSteps<NK, QT>;
     auto begin = [&](auto stc) {
       constexpr int st = decltype(stc)::value;
+      if constexpr (KB && st == 0) {
+        // pair 1 of this tile (pair 0's products read cbk[0])
+        cbk[1][0] = key_bias(cur, 1, 0);
+        cbk[1][1] = key_bias(cur, 1, 1);
+      }
       if constexpr (BIAS) {
         // bias of sub-blocks 2 st and 2 st + 1: 4 keys of this lane's query each
 #pragma unroll
@@ -287,6 +314,12 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         // copies of step 1 may refill the previous buffer.
         wait_vmem();
         tile_barrier();
+        if constexpr (KB) {
+          // pair 0 of the next tile, complete after the barrier (pair 1 of this one
+          // reads cbk[1]); past the last tile a buffer no product reads
+          cbk[0][0] = key_bias(nxt, 0, 0);
+          cbk[0][1] = key_bias(nxt, 0, 1);
+        }
       }
     };
     auto operand = [&](auto stc, auto oc) -> u32x4 {
@@ -318,7 +351,9 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       constexpr int J = st == 0 ? 1 : 0;
       if constexpr (k == 0) {
         constexpr int sb = o / NK, s = o % NK;
-        if constexpr (s == 0)
+        if constexpr (s == 0 && KB)
+          sc[sb][t] = Mx<DT>::first16c(op, qb[t][s], cbk[st][sb]);
+        else if constexpr (s == 0)
           sc[sb][t] = Mx<DT>::first16(op, qb[t][s]);
         else
           Mx<DT>::acc16(sc[sb][t], op, qb[t][s]);
@@ -460,6 +495,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       constexpr int o = decltype(oc)::value;
       carry[o] = pad_row16<D>(sKV[0], 16 * (o / NK) + l16, 4 * (o % NK) + j4);
     });
+    if constexpr (KB) {
+      cbk[0][0] = key_bias(0, 0, 0);
+      cbk[0][1] = key_bias(0, 0, 1);
+    }
     int kt = 0, cur = 0;
     prev = 0;
     auto phase = [&](int end, auto variant) {
@@ -540,6 +579,7 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t s) {
   p.G = pb.Hq / pb.Hkv;
   p.off = pb.Nkv - pb.Nq;
   p.scale_log2 = pb.scale * kLog2e;
+  p.inv_scale = 1.0f / pb.scale;
   p.bias = static_cast<const uint16_t*>(a.x.bias);
   p.bias_sb = a.x.bias_sb;
   p.bias_sh = a.x.bias_sh;

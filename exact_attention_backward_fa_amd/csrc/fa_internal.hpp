@@ -19,8 +19,12 @@ constexpr bool atomic_head_dim(int d) { return d == 64 || d == 128; }
 constexpr bool feature_head_dim(int d) { return d == 64 || d == 128; }
 
 // Kernel feature set of an instance: 0 plain attention, 1 with an additive score
-// bias (and its gradient), 2 with the bias and dropout of P.
-enum : int { FT_PLAIN = 0, FT_BIAS = 1, FT_DROPOUT = 2 };
+// bias (and its gradient), 2 with the bias and dropout of P, 3 with a bias that
+// depends on the batch and the key only (a key-padding mask, say) and no gradient
+// for it: the plain kernels' shape, the bias entering the score products.
+enum : int { FT_PLAIN = 0, FT_BIAS = 1, FT_DROPOUT = 2, FT_KEYBIAS = 3 };
+// instances that stream 2-D bias tiles through LDS (32-row shape)
+constexpr bool tile_bias(int ft) { return ft == FT_BIAS || ft == FT_DROPOUT; }
 
 // Validated arguments of one call (sizes already checked, pointers device-side).
 struct Problem {
@@ -37,7 +41,12 @@ struct Extras {
   void* dbias = nullptr;       // [B, Hq, N_q, N_kv] contiguous, or null
   unsigned keep_t = 256;       // dropout: keep iff the element's random byte < keep_t
   unsigned long long seed = 0;
-  int ft() const { return keep_t < 256 ? FT_DROPOUT : (bias || dbias) ? FT_BIAS : FT_PLAIN; }
+  int ft() const {
+    if (keep_t < 256) return FT_DROPOUT;
+    if (dbias) return FT_BIAS;
+    if (bias) return (bias_sh == 0 && bias_sq == 0) ? FT_KEYBIAS : FT_BIAS;
+    return FT_PLAIN;
+  }
 };
 
 struct FwdArgs {
@@ -119,6 +128,7 @@ hipError_t dispatch(const Problem& pb, int ft, F&& f) {
     if constexpr (feature_head_dim(decltype(d)::value)) {
       if (ft == FT_BIAS) return f(dt, d, c, integral_constant<int, FT_BIAS>());
       if (ft == FT_DROPOUT) return f(dt, d, c, integral_constant<int, FT_DROPOUT>());
+      if (ft == FT_KEYBIAS) return f(dt, d, c, integral_constant<int, FT_KEYBIAS>());
     }
     if (ft != FT_PLAIN) return hipErrorInvalidValue;
     return f(dt, d, c, integral_constant<int, FT_PLAIN>());

@@ -190,8 +190,11 @@ int fa_bwd_auto_dq_mode(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
  *   keep probability is T / 256 (p rounded to a multiple of 1/256).  LSE is that of
  *   the undropped P, so the backward can rebuild P from it.
  * With bias NULL and dropout_p = 0 this is fa_fwd.  A bias or dropout needs
- * d = 64 or 128 (FA_ERR_HEADDIM otherwise).  Returns FA_OK or an FA_ERR_* code;
- * on error nothing is launched or written.
+ * d = 64 or 128 (FA_ERR_HEADDIM otherwise).  A bias with bias_stride_h =
+ * bias_stride_q = 0 (one value per batch and key, e.g. a key-padding mask) and no
+ * dropout runs on kernels as fast as the plain ones, as does its backward when no
+ * dbias is asked for.  Returns FA_OK or an FA_ERR_* code; on error nothing is
+ * launched or written.
  */
 int fa_fwd_bias_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int Hq, int Hkv, int Nq, int Nkv, int d,

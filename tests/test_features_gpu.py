@@ -137,6 +137,74 @@ def test_bias_dropout_parity(cfg, device):
         assert np.all(g["dbias"][hidden] == 0)
 
 
+# A bias per (batch, key) with no gradient wanted (a key-padding mask, say) runs on
+# the key-bias instances: the plain kernels' 64-row shape, the bias read once per
+# key tile (forward, dQ pass: it starts the score accumulator) or held per key
+# (dK/dV kernel).
+KEY_BIAS_CASES = [
+    # name, B, Hq, Hkv, Nq, Nkv, d, dtype, causal, kind
+    ("kb_gqa_c", 2, 4, 2, 200, 333, 64, "fp16", True, "keys"),
+    ("kb_nc", 1, 4, 4, 300, 257, 128, "bf16", False, "keys"),
+    ("kb_nq_gt_nkv_c", 1, 8, 2, 513, 257, 128, "bf16", True, "keys"),
+    ("kb_d64_bf16_c", 2, 4, 1, 129, 700, 64, "bf16", True, "keys"),
+    ("kb_long_c", 1, 8, 2, 2048, 2048, 128, "fp16", True, "keys"),
+    # rising along the keys by 0.25 nats per key: the forward's rerun with a key bias
+    ("kb_ramp_fp16", 1, 4, 2, 200, 333, 64, "fp16", False, "keyramp"),
+    ("kb_ramp_bf16_c", 1, 4, 2, 300, 300, 128, "bf16", True, "keyramp"),
+]
+
+
+@pytest.mark.parametrize("cfg", KEY_BIAS_CASES, ids=[c[0] for c in KEY_BIAS_CASES])
+def test_key_bias_parity(cfg, device):
+    name, B, Hq, Hkv, Nq, Nkv, d, dt, causal, kind = cfg
+    x = inputs.make_custom(9000 + Nq + Nkv + d, B, Hq, Hkv, Nq, Nkv, d, dt)
+    case = inputs.Case(name, 0, 0, B, Hq, Hkv, Nq, Nkv, d, dt, causal, 1.0 / np.sqrt(d))
+    if kind == "keys":
+        bias = _bias_for("keys", B, Hq, Nq, Nkv, dt, 17 + Nq)
+    else:
+        bias = _bias(17 + Nq, (B, 1, 1, Nkv), Nkv, dt, mult=0.5)
+        bias += (0.25 * torch.arange(Nkv, dtype=torch.float32)).to(bias.dtype)
+    ref = _oracle(case, x, bias, 0.0, 0, False)
+    got = _run(case, x, bias, 0.0, 0, device, False)
+    _compare(case, got, ref, name)
+
+
+def test_key_bias_fully_masked_batch(device):
+    """Every key of batch 1 masked by the key bias: its rows get O = 0, LSE = -inf
+    and zero gradients; batch 0 is ordinary."""
+    B, Hq, Hkv, Nq, Nkv, d = 2, 4, 2, 150, 200, 128
+    x = inputs.make_custom(13, B, Hq, Hkv, Nq, Nkv, d, "bf16")
+    bias = _bias(8, (B, 1, 1, Nkv), Nkv, "bf16")
+    bias[1] = float("-inf")
+    case = inputs.Case("kb_masked_batch", 0, 0, B, Hq, Hkv, Nq, Nkv, d, "bf16", True, 0.125)
+    ref = _oracle(case, x, bias, 0.0, 0, False)
+    got = _run(case, x, bias, 0.0, 0, device, False)
+    g = _compare(case, got, ref, "masked batch")
+    assert np.all(g["o"][1] == 0) and np.all(g["lse"][1] == -np.inf)
+    assert np.all(g["dq"][1] == 0) and np.all(g["dk"][1] == 0) and np.all(g["dv"][1] == 0)
+
+
+def test_autograd_key_mask_without_grad(device):
+    """attention(..., bias=mask) with a key-padding mask that needs no gradient (the
+    key-bias instances) against the oracle: O and the gradients in q, k, v."""
+    from exact_attention_backward_fa_amd import attention
+    B, Hq, Hkv, Nq, Nkv, d = 2, 8, 2, 257, 384, 128
+    x = inputs.make_custom(78, B, Hq, Hkv, Nq, Nkv, d, "bf16")
+    mask = torch.zeros(B, 1, 1, Nkv, dtype=torch.bfloat16)
+    mask[0, ..., 300:] = float("-inf")
+    mask[1, ..., 17:40] = float("-inf")
+    case = inputs.Case("autograd_key_mask", 0, 0, B, Hq, Hkv, Nq, Nkv, d, "bf16", True, 1.0 / np.sqrt(d))
+    ref = _oracle(case, x, mask, 0.0, 0, False)
+    q, k, v = (x[n].to(device).requires_grad_() for n in ("q", "k", "v"))
+    o = attention(q, k, v, causal=True, bias=mask.to(device))
+    (o.float() * x["do"].to(device).float()).sum().backward()
+    torch.cuda.synchronize(device)
+    got = {"o": o.detach().double().cpu().numpy(), "dq": q.grad.double().cpu().numpy(),
+           "dk": k.grad.double().cpu().numpy(), "dv": v.grad.double().cpu().numpy()}
+    r = {kk: ref[kk] for kk in ("o", "dq", "dk", "dv")}
+    pu.assert_within(case, pu.compare(case, got, r, "autograd key mask"))
+
+
 def test_dropout_mask_is_the_oracles(device):
     """With V = identity rows and dO = 0, O = (P o Z) V exposes the kept pattern:
     O[i, j] != 0 exactly where the oracle keeps (i, j) (P > 0 everywhere: no bias,
