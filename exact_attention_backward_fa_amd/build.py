@@ -37,8 +37,9 @@ HEAD_DIMS = (32, 64, 96, 128, 256)
 INSTANCES = [(dt, d, c) for dt in (0, 1) for d in HEAD_DIMS for c in (0, 1)]
 # The fused atomic dK/dV/dQ kernel is built for these head dims only.
 ATOMIC_HEAD_DIMS = (64, 128)
-# Feature sets (1: additive score bias and its gradient, 2: bias and dropout of P)
-# are built for these head dims; every head dim has the plain set 0.
+# Feature sets (1: additive score bias and its gradient, 2: bias and dropout of P,
+# 3: a per-(batch, key) bias without gradient) are built for these head dims; every
+# head dim has the plain set 0.
 FEATURE_HEAD_DIMS = (64, 128)
 FEATURES = (1, 2, 3)
 # Backward kernel families compiled per instance (FA_KIND in fa_bwd_inst.hip).
