@@ -90,7 +90,8 @@ def units() -> List[Unit]:
             for kind, kname in BWD_KINDS.items():
                 if kname == "atomic" and (d not in ATOMIC_HEAD_DIMS or ft):
                     continue
-                if kname == "pre" and ft:
+                # the row preprocess kernel serves the atomic path only
+                if kname == "pre" and (ft or d not in ATOMIC_HEAD_DIMS):
                     continue
                 out.append(Unit(f"{kname}_{sfx}", "fa_bwd_inst.hip",
                                 [("FA_DT", dt), ("FA_D", d), ("FA_CAUSAL", c), ("FA_FT", ft),
@@ -145,8 +146,12 @@ def _filter_noise(text: str) -> str:
 
 
 def _run_jobs(jobs: List[Tuple[str, List[str]]], verbose: bool) -> None:
-    """Run compile commands in parallel (at most one per CPU, 16 at most)."""
+    """Run compile commands in parallel (at most one per CPU, 16 at most).  Each
+    job writes its output to a file of its own, read once the job has ended (a pipe
+    read only then would block a job whose output outgrows the pipe's buffer)."""
     width = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    logs = os.path.join(BUILD_DIR, "logs")
+    os.makedirs(logs, exist_ok=True)
     pending = list(jobs)
     running = []
     failed = []
@@ -155,17 +160,19 @@ def _run_jobs(jobs: List[Tuple[str, List[str]]], verbose: bool) -> None:
             name, cmd = pending.pop(0)
             if verbose:
                 print(" ".join(cmd), flush=True)
-            running.append((name, subprocess.Popen(cmd, stdout=subprocess.PIPE,
-                                                   stderr=subprocess.STDOUT, text=True)))
+            log = os.path.join(logs, f"{name}.log")
+            with open(log, "w") as f:
+                running.append((name, subprocess.Popen(cmd, stdout=f, stderr=subprocess.STDOUT), log))
         # wait for whichever job ends first
         while True:
             done = [r for r in running if r[1].poll() is not None]
             if done:
                 break
             time.sleep(0.05)
-        for name, p in done:
-            running.remove((name, p))
-            out = p.stdout.read() if p.stdout else ""
+        for name, p, log in done:
+            running.remove((name, p, log))
+            with open(log, errors="replace") as f:
+                out = f.read()
             msg = _filter_noise(out or "")
             if p.returncode != 0:
                 failed.append(name)
@@ -183,20 +190,32 @@ def build(verbose: bool = False, incremental: bool = False) -> str:
     t0 = time.time()
     jobs = []
     objs = []
+    done = []  # (unit, object path, scratch directory) of the units compiled now
     for u in units():
         obj = os.path.join(BUILD_DIR, f"{u.name}-{unit_key(u)}.o")
         objs.append(obj)
         if incremental and os.path.exists(obj):
             continue
-        tmp = obj + ".part"
-        jobs.append((u.name, [cc, *HIP_FLAGS, *u.flags(), "-c", os.path.join(CSRC, u.src),
-                              "-o", tmp]))
+        # each unit compiles in a scratch directory of its own, keeping the compiler's
+        # intermediate files: its device assembly goes to the assembly cache, so the
+        # hazard scan of the tests needs no second compilation
+        work = os.path.join(BUILD_DIR, "tmp", u.name)
+        shutil.rmtree(work, ignore_errors=True)
+        os.makedirs(work)
+        done.append((u, obj, work))
+        jobs.append((u.name, [cc, *HIP_FLAGS, *u.flags(), "-save-temps=obj", "-c",
+                              os.path.join(CSRC, u.src), "-o", os.path.join(work, "unit.o")]))
     # the kernel instances are the long compilations: start them first
     jobs.sort(key=lambda j: j[0] in [os.path.splitext(s)[0] for s in SOURCES])
     _run_jobs(jobs, verbose)
-    for obj in objs:
-        if os.path.exists(obj + ".part"):
-            os.replace(obj + ".part", obj)
+    adir = os.path.join(BUILD_DIR, "asm")
+    os.makedirs(adir, exist_ok=True)
+    for u, obj, work in done:
+        os.replace(os.path.join(work, "unit.o"), obj)
+        dev = [f for f in os.listdir(work) if f.endswith(f"-hip-amdgcn-amd-amdhsa-{ARCH}.s")]
+        if dev:
+            os.replace(os.path.join(work, dev[0]), os.path.join(adir, f"{u.name}-{unit_key(u, ['asm'])}.s"))
+        shutil.rmtree(work, ignore_errors=True)
     tmp = LIB_PATH + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -266,11 +285,12 @@ _KERNEL_UNIT = {"fwd_kernel": "fwd", "bwd_pre_kernel": "pre", "bwd_dkdv_kernel":
 def unit_of_kernel(kernel: str) -> Optional[str]:
     """Compilation unit of a kernel named as a profiler prints it, e.g.
     ``bwd_dkdv_kernel<1, 128, true, 0>`` -> ``dkdv_1_128_1``; None for others."""
-    m = re.match(r"(?:fa::)?(\w+)<(\d+), (\d+), (true|false)(?:, (\d+))?>", kernel)
+    m = re.match(r"(?:fa::)?(\w+)<(\d+), (\d+)(?:, (true|false))?(?:, (\d+))?(?:, (?:true|false))?>",
+                 kernel)
     if not m or m.group(1) not in _KERNEL_UNIT:
         return None
     fam = _KERNEL_UNIT[m.group(1)]
-    # the preprocess's bool is its dQ-buffer clearing, not causality: both units hold it
+    # the preprocess takes no causal flag: the causal unit holds it as well
     causal = "1" if fam == "pre" or m.group(4) == "true" else "0"
     ft = int(m.group(5) or 0)
     return f"{fam}_{m.group(2)}_{m.group(3)}_{causal}" + (f"_f{ft}" if ft else "")

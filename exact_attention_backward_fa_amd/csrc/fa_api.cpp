@@ -167,7 +167,7 @@ int bwd_checked(const BwdCall& c, int dq_mode, void* ev_begin, void* ev_end, voi
   (void)hipGetLastError();
   if (atomic) {
     // preprocess (rows, counters, float32 dQ buffer) -> fused dK/dV/dQ -> convert
-    if (launch_bwd_pre(a, true, s) != hipSuccess) return FA_ERR_HIP;
+    if (launch_bwd_pre(a, s) != hipSuccess) return FA_ERR_HIP;
     if (ev_begin && hipEventRecord((hipEvent_t)ev_begin, s) != hipSuccess) return FA_ERR_HIP;
     if (launch_bwd_dkdv(a, true, s) != hipSuccess) return FA_ERR_HIP;
     if (ev_end && hipEventRecord((hipEvent_t)ev_end, s) != hipSuccess) return FA_ERR_HIP;

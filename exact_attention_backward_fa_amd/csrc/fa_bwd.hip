@@ -97,10 +97,12 @@ int device_cu_count() {
 // Dispatch.
 #define FA_TPARAMS decltype(dt)::value, decltype(d)::value, decltype(c)::value
 
-hipError_t launch_bwd_pre(const BwdArgs& a, bool zero_dq_acc, hipStream_t s) {
+hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t s) {
   if ((size_t)a.pb.B * a.pb.Hq * a.pb.Nq == 0) return hipSuccess;
-  return dispatch(a.pb, FT_PLAIN, [&](auto dt, auto d, auto c, auto) {
-    return run_pre<FA_TPARAMS>(a, zero_dq_acc, s);
+  // the atomic path's kernel: built for its head dims only
+  return dispatch(a.pb, FT_PLAIN, [&](auto dt, auto d, auto c, auto) -> hipError_t {
+    if constexpr (atomic_head_dim(decltype(d)::value)) return run_pre<FA_TPARAMS>(a, s);
+    return hipErrorInvalidValue;
   });
 }
 

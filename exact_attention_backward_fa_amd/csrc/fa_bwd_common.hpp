@@ -130,7 +130,7 @@ struct WorkQueue {
 
 // Launchers of one template instance; each is explicitly instantiated in its own
 // compilation of fa_bwd_inst.hip.
-template <int DT, int D, bool CAUSAL> hipError_t run_pre(const BwdArgs& a, bool zero, hipStream_t s);
+template <int DT, int D, bool CAUSAL> hipError_t run_pre(const BwdArgs& a, hipStream_t s);
 template <int DT, int D, bool CAUSAL, int FT> hipError_t run_dkdv(const BwdArgs& a, hipStream_t s);
 template <int DT, int D, bool CAUSAL, int FT> hipError_t run_dq(const BwdArgs& a, hipStream_t s);
 template <int DT, int D, bool CAUSAL> hipError_t run_dkdv_atomic(const BwdArgs& a, hipStream_t s);

@@ -164,7 +164,7 @@ constexpr int pre_lanes_per_row() {
   while (n < D / 8) n *= 2;
   return n;
 }
-template <int DT, int D, bool ZERO_DQ>
+template <int DT, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   constexpr int LPR = pre_lanes_per_row<D>();
   constexpr int RPB = 256 / LPR;
@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       s += Dt<DT>::lo(a[j]) * Dt<DT>::lo(c[j]) + Dt<DT>::hi(a[j]) * Dt<DT>::hi(c[j]);
-    if (ZERO_DQ) {
+    {
       float* z = p.dq_acc + row * D + part * 8;
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       *reinterpret_cast<f32x4*>(z) = zero;
@@ -1219,14 +1219,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
 // Launchers of one template instance (explicitly instantiated per instance in
 // fa_bwd_inst.hip, so the instances compile in parallel).
 template <int DT, int D, bool CAUSAL>
-hipError_t run_pre(const BwdArgs& a, bool zero, hipStream_t s) {
+hipError_t run_pre(const BwdArgs& a, hipStream_t s) {
   const BwdParams p = make_params(a);
   constexpr int RPB = 256 / pre_lanes_per_row<D>();
   const dim3 grid((unsigned)((p.rows + RPB - 1) / RPB));
-  if (zero)
-    hipLaunchKernelGGL((bwd_pre_kernel<DT, D, true>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((bwd_pre_kernel<DT, D, false>), grid, dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_pre_kernel<DT, D>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

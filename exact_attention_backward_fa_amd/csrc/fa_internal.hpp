@@ -149,10 +149,10 @@ hipError_t dispatch(const Problem& pb, int ft, F&& f) {
   };
   return pb.dtype == 0 ? by_d(integral_constant<int, 0>()) : by_d(integral_constant<int, 1>());
 }
-// Row preprocess kernel (-D, LSE * log2 e, counters cleared, float32 dQ buffer
-// zeroed when asked): the atomic dQ path only; on the separate path the dQ pass
-// does the row preprocess and launch_sched_clear clears the counters.
-hipError_t launch_bwd_pre(const BwdArgs& a, bool zero_dq_acc, hipStream_t s);
+// Row preprocess kernel of the atomic dQ path (-D, LSE * log2 e, counters
+// cleared, float32 dQ buffer zeroed); on the separate path the dQ pass does the
+// row preprocess and launch_sched_clear clears the counters.
+hipError_t launch_bwd_pre(const BwdArgs& a, hipStream_t s);
 hipError_t launch_sched_clear(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, bool atomic_dq, hipStream_t s);
 hipError_t launch_bwd_dq(const BwdArgs& a, hipStream_t s);
