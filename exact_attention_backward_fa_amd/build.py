@@ -285,7 +285,7 @@ _KERNEL_UNIT = {"fwd_kernel": "fwd", "bwd_pre_kernel": "pre", "bwd_dkdv_kernel":
 def unit_of_kernel(kernel: str) -> Optional[str]:
     """Compilation unit of a kernel named as a profiler prints it, e.g.
     ``bwd_dkdv_kernel<1, 128, true, 0>`` -> ``dkdv_1_128_1``; None for others."""
-    m = re.match(r"(?:fa::)?(\w+)<(\d+), (\d+)(?:, (true|false))?(?:, (\d+))?(?:, (?:true|false))?>",
+    m = re.match(r"(?:fa::)?(\w+)<(\d+), (\d+)(?:, (true|false))?(?:, (\d+))?(?:, (?:true|false|\d+))?>",
                  kernel)
     if not m or m.group(1) not in _KERNEL_UNIT:
         return None

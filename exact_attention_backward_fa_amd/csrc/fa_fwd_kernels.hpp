@@ -29,6 +29,14 @@
 // more than 44 nats along the row for bf16, 10.4 nats for fp16) raises m and marks
 // the item; the workgroup then runs the item a second time from zero with the
 // raised references, which no score can exceed by more than H.
+// The plain instances run in two launches.  The first (MODE 1) sets each column's
+// reference from the first pair before its loop, takes no per-pair maxima, and
+// checks at the end that no column's row sum exceeds 2^H: then no P did either and
+// the result is the one the per-pair test would have given.  Otherwise it marks
+// the item (LSE = NaN on its rows) and writes no O, and the second launch
+// (MODE 2) runs the marked items with the per-pair test; its other workgroups
+// exit at once.  The other instances run every item with the per-pair test
+// (MODE 0).
 // The row sums l of P are float32 (each lane sums its keys; the four lanes of a
 // column are added at the end; summing the bf16-rounded P through the matrix
 // pipe was measured to miss the LSE bound on short rows).  At the end O is divided
@@ -128,9 +136,11 @@ struct FwdPlace {
   }
 };
 
-template <int DT, int D, bool CAUSAL, int FT>
+template <int DT, int D, bool CAUSAL, int FT, int MODE = 0>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   constexpr bool BIAS = tile_bias(FT), DROP = FT == FT_DROPOUT, KB = FT == FT_KEYBIAS;
+  // per-pair maxima and the test for a raised reference (all but the fast pass)
+  constexpr bool FULL = MODE != 1;
   constexpr int QT = FwdShape<D, FT>::QT;  // query tiles of 16 per wave
   constexpr int QW = 16 * QT, BM = 4 * QW, BN = 64, NST = 2;
   constexpr int NK = D / 32;
@@ -169,6 +179,11 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   const uint16_t* __restrict__ K = p.k + kbase * D;
   const uint16_t* __restrict__ V = p.v + kbase * D;
   const float c = p.scale_log2;
+  if constexpr (MODE == 2) {
+    // only an item the fast pass marked (LSE of its first row NaN)
+    const float mark = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(p.lse[qbase + q0])));
+    if (!__builtin_isnan(mark)) return;
+  }
 
   u32x4 qb[QT][NK];
 #pragma unroll
@@ -393,12 +408,12 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
               }
             }
           }
-          const float m0 = vmax3(sc[0][t][0], sc[0][t][1], sc[0][t][2]);
-          const float m1 = vmax3(sc[0][t][3], sc[1][t][0], sc[1][t][1]);
-          mx[t] = vmax3(m0, m1, vmax3(sc[1][t][2], sc[1][t][3], sc[1][t][3]));
+          const float m0 = FULL ? vmax3(sc[0][t][0], sc[0][t][1], sc[0][t][2]) : 0.f;
+          const float m1 = FULL ? vmax3(sc[0][t][3], sc[1][t][0], sc[1][t][1]) : 0.f;
+          if constexpr (FULL) mx[t] = vmax3(m0, m1, vmax3(sc[1][t][2], sc[1][t][3], sc[1][t][3]));
         }
       });
-      if constexpr (PL.check == mi) {
+      if constexpr (FULL && PL.check == mi) {
         bool any = false;
 #pragma unroll
         for (int t = 0; t < QT; ++t) any = any || mx[t] > thr[t];
@@ -499,6 +514,43 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       cbk[0][0] = key_bias(0, 0, 0);
       cbk[0][1] = key_bias(0, 0, 1);
     }
+    if constexpr (MODE == 1) {
+      // each column's reference from its first pair (keys 0 .. 31), as the per-pair
+      // test would set it; unset for a column that sees none of them (an empty row)
+      if (nkt > 0) {
+#pragma unroll
+        for (int t = 0; t < QT; ++t) {
+          f32x4 s2[2];
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+            for (int s = 0; s < NK; ++s) {
+              const u32x4 op = pad_row16<D>(sKV[0], 16 * sb + l16, 4 * s + j4);
+              if (s == 0)
+                s2[sb] = Mx<DT>::first16(op, qb[t][s]);
+              else
+                Mx<DT>::acc16(s2[sb], op, qb[t][s]);
+            }
+          }
+          wait_mfma();
+          asm volatile("" : "+v"(s2[0]), "+v"(s2[1]));
+          const int q = qw + 16 * t + l16;
+          float v = -INFINITY;
+#pragma unroll
+          for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = 16 * sb + 4 * j4 + i;
+              const bool vis = key < p.Nkv && (!CAUSAL || key <= q + p.off);
+              v = fmaxf(v, vis ? s2[sb][i] : -INFINITY);
+            }
+          }
+          v = fmaxf(v, __shfl_xor(v, 16));
+          v = fmaxf(v, __shfl_xor(v, 32));
+          if (v > -INFINITY) m[t] = v * c;
+        }
+      }
+    }
     int kt = 0, cur = 0;
     prev = 0;
     auto phase = [&](int end, auto variant) {
@@ -526,10 +578,21 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     phase(n_vis, std::integral_constant<int, 1>());
     if (nkt > 0) flush();
     phase(nkt, std::integral_constant<int, 0>());
+    if constexpr (MODE == 1) {
+      // no P above 2^H if no column's row sum is (also true for inf and NaN sums)
+      const float limit = exp2f(fwd_headroom<DT>());
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        float l = lsum[t];
+        l += __shfl_xor(l, 16);
+        l += __shfl_xor(l, 32);
+        if (!(l <= limit)) dirty = true;
+      }
+    }
     wait_vmem();    // no copy may land in LDS after the tile buffers are reused below
     if (dirty) s_dirty = 1;
     lds_barrier();  // every wave is done with the tile buffers; s_dirty is final
-    if (pass > 0 || __builtin_amdgcn_readfirstlane(s_dirty) == 0) break;
+    if (MODE == 1 || pass > 0 || __builtin_amdgcn_readfirstlane(s_dirty) == 0) break;
     // run again from zero with the raised references
     settle(acc);
 #pragma unroll
@@ -543,6 +606,17 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     lds_barrier();  // the s_dirty reads are done before the next pass's copies
   }
   settle(acc);
+  if constexpr (MODE == 1) {
+    if (__builtin_amdgcn_readfirstlane(s_dirty) != 0) {
+      // marked for the second launch: LSE NaN on this wave's rows, no O
+#pragma unroll
+      for (int t = 0; t < QT; ++t) {
+        const int q = qw + 16 * t + l16;
+        if (j4 == 0 && q < p.Nq) p.lse[qbase + q] = __builtin_nanf("");
+      }
+      return;
+    }
+  }
 
   // O = acc / l per row; LSE = ln 2 (m + log2 l), -inf for a row that sees no key
   float inv[QT][4];
@@ -590,7 +664,15 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t s) {
   p.drop_scale = a.x.keep_t > 0 ? 256.f / (float)a.x.keep_t : 0.f;
   constexpr int BM = 4 * 16 * FwdShape<D, FT>::QT;  // queries per workgroup
   const dim3 grid((unsigned)(((pb.Nq + BM - 1) / BM) * pb.Hq * pb.B));
-  hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL, FT>), grid, dim3(256), 0, s, p);
+  if constexpr (FT == FT_PLAIN) {
+    // the fast pass, then the items it marked
+    hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL, FT, 1>), grid, dim3(256), 0, s, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL, FT, 2>), grid, dim3(256), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL, FT>), grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -91,6 +91,7 @@ def test_unit_of_kernel():
     assert build.unit_of_kernel("bwd_dkdv_kernel<1, 128, true, 0>") == "dkdv_1_128_1"
     assert build.unit_of_kernel("fa::bwd_dq_kernel<0, 64, false, 2>") == "dq_0_64_0_f2"
     assert build.unit_of_kernel("fwd_kernel<1, 128, true, 1>") == "fwd_1_128_1_f1"
+    assert build.unit_of_kernel("fwd_kernel<1, 128, true, 0, 1>") == "fwd_1_128_1"
     assert build.unit_of_kernel("bwd_dkdv_atomic_kernel<1, 128, true>") == "atomic_1_128_1"
     assert build.unit_of_kernel("bwd_pre_kernel<1, 128>") == "pre_1_128_1"
     assert build.unit_of_kernel("bwd_dq_kernel<1, 128, true, 1, true>") == "dq_1_128_1_f1"
