@@ -290,6 +290,42 @@ def test_rising_logits(dtype, rise, causal, device):
         pu.assert_within(case, pu.compare(case, got, ref, mode))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_row_sum_check_without_overflow(causal, device):
+    """fp16 scores that rise about 8 nats (11.5 log2 units) along every row: below
+    the fp16 headroom of 15, so no P can overflow, yet the row sums pass 2^15.
+    The plain forward's fast first pass checks the row sums, so it marks these
+    items and the second launch recomputes them with the per-pair test; O, LSE and
+    the gradients must match the oracle on both dQ paths."""
+    B, Hq, Hkv, N, d = 1, 2, 1, 384, 64
+    g = torch.Generator().manual_seed(4343)
+    u = torch.full((d,), 1.0 / np.sqrt(d))
+    ramp = torch.arange(N, dtype=torch.float32) / N
+    amp = 8.0 / 5.0
+    x = {
+        "q": (5.0 * u + 0.1 * torch.randn(B, Hq, N, d, generator=g)).half(),
+        "k": (amp * ramp[:, None] * u + 0.1 * torch.randn(B, Hkv, N, d, generator=g)).half(),
+        "v": torch.randn(B, Hkv, N, d, generator=g).half(),
+        "do": torch.randn(B, Hq, N, d, generator=g).half(),
+    }
+    case = inputs.Case("sum_check", 0, 0, B, Hq, Hkv, N, N, d, "fp16", causal, 1.0)
+    o, lse = orc.forward(x["q"], x["k"], x["v"], case.scale, causal)
+    dq, dk, dv = orc.backward(x["q"], x["k"], x["v"], x["do"], case.scale, causal)
+    ref = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+    # the premise, non-causal rows over all keys: no later score exceeds the first
+    # 32 keys' maximum by 15 log2 units, yet the sum of 2^(score - that maximum)
+    # over the row passes 2^15
+    sc = orc.as_f64(x["q"][0]) @ orc.as_f64(x["k"][0, 0]).T / np.log(2.0)
+    ref_max = sc[:, :, :32].max(-1, keepdims=True)
+    assert (sc.max(-1, keepdims=True) - ref_max).max() < 15.0
+    assert (np.exp2(sc - ref_max).sum(-1) > 2.0 ** 15).mean() > 0.5
+    for mode in MODES:
+        res = pu.gpu_forward_backward(case, x, device, dq_mode=mode)
+        got = {k: res[k].double().numpy() for k in res}
+        assert all(bool(np.isfinite(got[k]).all()) for k in ("o", "dq", "dk", "dv"))
+        pu.assert_within(case, pu.compare(case, got, ref, mode))
+
+
 def test_fa_bwd_entry_point(device):
     """fa_bwd itself (the dQ path FA_DQ_AUTO picks, workspace of exactly
     fa_bwd_workspace_bytes bytes), called through ctypes, against the oracle."""
