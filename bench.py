@@ -314,7 +314,7 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the backward shards by (batch, kv head) group with no communication; "
               "run --gpus 1)", file=sys.stderr, flush=True)
         return 2

@@ -27,7 +27,7 @@ up to rounding order, because it only reorders the same sums):
   dV          = sum_{h in g} P^T dO_h (rustytorch page: the dQ/dK/dV
   accumulation; Triton page: ``dv += p^T do``, ``dk += ds^T q``, ``dq = ds k``).
 
-Readings where the pages are silent or disagree (each is listed in the design doc):
+Readings where the pages are silent or disagree:
 
 * Causal masking is bottom-right aligned: query i may see key j iff
   j <= i + (N_kv - N_q).  (The rustytorch kernel masks k_pos > q_pos with one
