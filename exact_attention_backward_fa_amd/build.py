@@ -38,10 +38,10 @@ INSTANCES = [(dt, d, c) for dt in (0, 1) for d in HEAD_DIMS for c in (0, 1)]
 # The fused atomic dK/dV/dQ kernel is built for these head dims only.
 ATOMIC_HEAD_DIMS = (64, 128)
 # Feature sets (1: additive score bias and its gradient, 2: bias and dropout of P,
-# 3: a per-(batch, key) bias without gradient) are built for these head dims; every
-# head dim has the plain set 0.
+# 3: a per-(batch, key) bias without gradient, 4: dropout without bias) are built
+# for these head dims; every head dim has the plain set 0.
 FEATURE_HEAD_DIMS = (64, 128)
-FEATURES = (1, 2, 3)
+FEATURES = (1, 2, 3, 4)
 # Backward kernel families compiled per instance (FA_KIND in fa_bwd_inst.hip).
 BWD_KINDS = {0: "pre", 1: "dkdv", 2: "dq", 3: "atomic"}
 

@@ -69,9 +69,11 @@ struct DqSteps {
 // rows and the streamed tiles are double-buffered.  The bias and dropout
 // instances take the same shape: the bias tiles need the LDS, the bias and
 // dropout work the registers.
-template <int D, int FT = 0>
+template <int D, int FT = 0, bool KV = false>
 struct TileShape {
-  static constexpr bool SMALL = D > 128 || tile_bias(FT);
+  // KV: the dK/dV kernel, whose 64-row shape leaves no registers for dropout at
+  // d = 128
+  static constexpr bool SMALL = D > 128 || tile_bias(FT) || (KV && FT == FT_DROP && D > 64);
   static constexpr int RT = SMALL ? 2 : 4;    // resident 16-row tiles per wave
   static constexpr int NBUF = SMALL ? 2 : 3;  // LDS buffers of the streamed tiles
 };
@@ -223,11 +225,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // ragged end of this wave's block take a masked variant of the softmax.
 template <int DT, int D, bool CAUSAL, int FT>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
-  constexpr bool BIAS = tile_bias(FT), DROP = FT == FT_DROPOUT, KB = FT == FT_KEYBIAS;
-  constexpr int KT = TileShape<D, FT>::RT;  // key tiles of 16 per wave
+  constexpr bool BIAS = tile_bias(FT), DROP = FT == FT_DROPOUT || FT == FT_DROP, KB = FT == FT_KEYBIAS;
+  constexpr int KT = TileShape<D, FT, true>::RT;  // key tiles of 16 per wave
   constexpr int KW = 16 * KT, BN = 4 * KW, BM = 64, NSB = BM / 16;
   constexpr int NK = D / 32;
-  constexpr int NBUF = TileShape<D, FT>::NBUF;
+  constexpr int NBUF = TileShape<D, FT, true>::NBUF;
   constexpr int RS = PadTile<D>::RS;
   // bias tile of a query tile: BM rows x the workgroup's BN keys (4 pad granules a
   // row: 320-byte rows for BN = 128)
@@ -734,7 +736,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
 // otherwise each key is stored on its own.
 template <int DT, int D, bool CAUSAL, int FT, bool DBW = false>
 __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
-  constexpr bool BIAS = tile_bias(FT), DROP = FT == FT_DROPOUT, KB = FT == FT_KEYBIAS;
+  constexpr bool BIAS = tile_bias(FT), DROP = FT == FT_DROPOUT || FT == FT_DROP, KB = FT == FT_KEYBIAS;
   constexpr int QT = TileShape<D, FT>::RT;  // query tiles of 16 per wave
   constexpr int QW = 16 * QT, BM = 4 * QW, BN = 64, NSB = BN / 16;
   constexpr int NK = D / 32;
@@ -1230,7 +1232,7 @@ hipError_t run_pre(const BwdArgs& a, hipStream_t s) {
 template <int DT, int D, bool CAUSAL, int FT>
 hipError_t run_dkdv(const BwdArgs& a, hipStream_t s) {
   BwdParams p = make_params(a);
-  constexpr int BN = 4 * 16 * TileShape<D, FT>::RT;  // keys per work item
+  constexpr int BN = 4 * 16 * TileShape<D, FT, true>::RT;  // keys per work item
   const int items = ((a.pb.Nkv + BN - 1) / BN) * a.pb.Hkv * a.pb.B;
   const int ncu = device_cu_count();
   const dim3 grid((unsigned)(p.sched && ncu > 0 && ncu < items ? ncu : items));

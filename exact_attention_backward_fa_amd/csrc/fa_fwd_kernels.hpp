@@ -138,7 +138,7 @@ struct FwdPlace {
 
 template <int DT, int D, bool CAUSAL, int FT, int MODE = 0>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
-  constexpr bool BIAS = tile_bias(FT), DROP = FT == FT_DROPOUT, KB = FT == FT_KEYBIAS;
+  constexpr bool BIAS = tile_bias(FT), DROP = FT == FT_DROPOUT || FT == FT_DROP, KB = FT == FT_KEYBIAS;
   // per-pair maxima and the test for a raised reference (all but the fast pass)
   constexpr bool FULL = MODE != 1;
   constexpr int QT = FwdShape<D, FT>::QT;  // query tiles of 16 per wave

@@ -21,8 +21,9 @@ constexpr bool feature_head_dim(int d) { return d == 64 || d == 128; }
 // Kernel feature set of an instance: 0 plain attention, 1 with an additive score
 // bias (and its gradient), 2 with the bias and dropout of P, 3 with a bias that
 // depends on the batch and the key only (a key-padding mask, say) and no gradient
-// for it: the plain kernels' shape, the bias entering the score products.
-enum : int { FT_PLAIN = 0, FT_BIAS = 1, FT_DROPOUT = 2, FT_KEYBIAS = 3 };
+// for it: the plain kernels' shape, the bias entering the score products; 4 with
+// dropout and no bias.
+enum : int { FT_PLAIN = 0, FT_BIAS = 1, FT_DROPOUT = 2, FT_KEYBIAS = 3, FT_DROP = 4 };
 // instances that stream 2-D bias tiles through LDS (32-row shape)
 constexpr bool tile_bias(int ft) { return ft == FT_BIAS || ft == FT_DROPOUT; }
 
@@ -42,7 +43,7 @@ struct Extras {
   unsigned keep_t = 256;       // dropout: keep iff the element's random byte < keep_t
   unsigned long long seed = 0;
   int ft() const {
-    if (keep_t < 256) return FT_DROPOUT;
+    if (keep_t < 256) return (bias || dbias) ? FT_DROPOUT : FT_DROP;
     if (dbias) return FT_BIAS;
     if (bias) return (bias_sh == 0 && bias_sq == 0) ? FT_KEYBIAS : FT_BIAS;
     return FT_PLAIN;
@@ -129,6 +130,7 @@ hipError_t dispatch(const Problem& pb, int ft, F&& f) {
       if (ft == FT_BIAS) return f(dt, d, c, integral_constant<int, FT_BIAS>());
       if (ft == FT_DROPOUT) return f(dt, d, c, integral_constant<int, FT_DROPOUT>());
       if (ft == FT_KEYBIAS) return f(dt, d, c, integral_constant<int, FT_KEYBIAS>());
+      if (ft == FT_DROP) return f(dt, d, c, integral_constant<int, FT_DROP>());
     }
     if (ft != FT_PLAIN) return hipErrorInvalidValue;
     return f(dt, d, c, integral_constant<int, FT_PLAIN>());

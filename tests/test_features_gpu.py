@@ -169,6 +169,46 @@ def test_key_bias_parity(cfg, device):
     _compare(case, got, ref, name)
 
 
+# Dropout without a bias: the forward and the dQ pass keep the plain 64-row
+# shape (the dK/dV kernel at d = 64 as well).
+DROP_ONLY_CASES = [
+    # name, B, Hq, Hkv, Nq, Nkv, d, dtype, causal, p
+    ("drop_gqa_c", 2, 4, 2, 100, 333, 64, "fp16", True, 0.2),
+    ("drop_nc", 1, 4, 4, 257, 700, 128, "bf16", False, 0.5),
+    ("drop_nq_gt_nkv_c", 1, 4, 1, 200, 64, 64, "fp16", True, 0.25),
+    ("drop_d64_bf16_c", 2, 4, 2, 300, 300, 64, "bf16", True, 0.3),
+    ("drop_long_c", 1, 8, 2, 2048, 2048, 128, "bf16", True, 0.1),
+]
+
+
+@pytest.mark.parametrize("cfg", DROP_ONLY_CASES, ids=[c[0] for c in DROP_ONLY_CASES])
+def test_dropout_only_parity(cfg, device):
+    name, B, Hq, Hkv, Nq, Nkv, d, dt, causal, p = cfg
+    x = inputs.make_custom(9500 + Nq + Nkv + d, B, Hq, Hkv, Nq, Nkv, d, dt)
+    case = inputs.Case(name, 0, 0, B, Hq, Hkv, Nq, Nkv, d, dt, causal, 1.0 / np.sqrt(d))
+    seed = (0x85EBCA6B << 32) | (77 + Nq)
+    ref = _oracle(case, x, None, p, seed, False)
+    got = _run(case, x, None, p, seed, device, False)
+    _compare(case, got, ref, name)
+
+
+def test_autograd_dropout_without_bias(device):
+    """attention(..., dropout_p=, seed=) with no bias against the oracle."""
+    from exact_attention_backward_fa_amd import attention
+    B, Hq, Hkv, Nq, Nkv, d = 2, 4, 2, 190, 256, 128
+    x = inputs.make_custom(79, B, Hq, Hkv, Nq, Nkv, d, "fp16")
+    case = inputs.Case("autograd_dropout", 0, 0, B, Hq, Hkv, Nq, Nkv, d, "fp16", True, 1.0 / np.sqrt(d))
+    ref = _oracle(case, x, None, 0.2, 31337, False)
+    q, k, v = (x[n].to(device).requires_grad_() for n in ("q", "k", "v"))
+    o = attention(q, k, v, causal=True, dropout_p=0.2, seed=31337)
+    (o.float() * x["do"].to(device).float()).sum().backward()
+    torch.cuda.synchronize(device)
+    got = {"o": o.detach().double().cpu().numpy(), "dq": q.grad.double().cpu().numpy(),
+           "dk": k.grad.double().cpu().numpy(), "dv": v.grad.double().cpu().numpy()}
+    r = {kk: ref[kk] for kk in ("o", "dq", "dk", "dv")}
+    pu.assert_within(case, pu.compare(case, got, r, "autograd dropout"))
+
+
 def test_key_bias_fully_masked_batch(device):
     """Every key of batch 1 masked by the key bias: its rows get O = 0, LSE = -inf
     and zero gradients; batch 0 is ordinary."""
