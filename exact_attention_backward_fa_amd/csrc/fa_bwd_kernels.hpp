@@ -447,6 +447,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       f32x4 lq, dn;   // LSE*log2e and -D of the current sub-block's rows
       u32x2 bv[KT];   // bias of the current sub-block per key tile (rows in elements)
       f32x4 zf[KT];   // dropout keep factors of the current sub-block per key tile
+      u32x4 kw;       // keep bytes of this lane's key in the blocks drawn last
+      static_assert(!DROP || KT == 4 || (KT == 2 && NSB % 2 == 0), "dropout block draw");
       (void)hq;
       const int keyl = kvw + l16;    // key of this lane's column in key tile 0
       const int qrow = q0 + 4 * j4;  // query row of element 0 in sub-block 0
@@ -473,14 +475,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         constexpr int e = decltype(ec)::value, st = decltype(st_c)::value;
         constexpr int kt = e / 4, i = e % 4;
         if constexpr (DROP && i == 0) {
-          // one Philox call for the 4 x 4 block (keys key & ~3 .., queries of rows
-          // 0..3 of this lane's row group): word i is row i, byte key % 4 the key
-          const int key = keyl + 16 * kt, q = qrow + 16 * st;
-          const u32x4 ctr = {(uint32_t)key >> 2, (uint32_t)q >> 2, (uint32_t)hq, (uint32_t)b};
-          const u32x4 x = philox4x32_10(ctr, p.seed_lo, p.seed_hi);
-          const int byte = key & 3;
+          // One Philox call per 4 x 4 block (keys k & ~3 .., rows 0..3 of a row
+          // group): word r is row r, byte k % 4 the key.  The four lanes of a key
+          // quad share their blocks, so lane q draws one of them (key tile q % KT
+          // of sub-block st + q / KT; with two key tiles, the even step draws the
+          // odd step's blocks too) and a byte and quad transpose give every lane
+          // its bytes: word w, byte r = row r of block w of this lane's key.
+          constexpr bool DRAW = kt == 0 && st % (4 / KT) == 0;
+          if constexpr (DRAW) {
+            const int q4 = l16 & 3, bkt = q4 % KT, bst = st + q4 / KT;
+            const u32x4 ctr = {(uint32_t)(keyl + 16 * bkt) >> 2, (uint32_t)(qrow + 16 * bst) >> 2,
+                               (uint32_t)hq, (uint32_t)b};
+            kw = quad_transpose(byte_transpose(philox4x32_10(ctr, p.seed_lo, p.seed_hi)), q4);
+          }
+          const uint32_t word = kw[KT == 4 ? kt : 2 * (st % 2) + kt];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) zf[kt][r] = keep_factor(x[r], byte, p.keep_t, p.drop_scale);
+          for (int r = 0; r < 4; ++r) zf[kt][r] = keep_factor(word, r, p.keep_t, p.drop_scale);
         }
         float v;
         if constexpr (BIAS)
@@ -564,6 +574,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         using Plan = typename Steps::template P<st>;
         using stp = std::integral_constant<int, st>;
         constexpr DkdvPlace<NK, KT, st, LA, OPS> PL{};
+        static_assert(!DROP || none_before(PL.exp, PL.exp[0][0]), "key tile 0 draws the dropout blocks");
         (void)gc;
         // The copies of a later tile, in steps 2-3 (after the mid-tile barrier).
         static_for<OPS>([&](auto cc) {
@@ -965,6 +976,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       const int krow = kv0 + 4 * j4;  // key of element 0 in sub-block 0
       const int qcol = qw + l16;      // query of this lane's column in query tile 0
       u32x2 bv[QT];  // bias of the current sub-block per query tile (keys in elements)
+      u32x4 qwd;     // keep words of this lane's query in the blocks drawn last
+      static_assert(!DROP || QT == 4 || (QT == 2 && NSB % 2 == 0), "dropout block draw");
 
       // dS of sub-block sb (kept in sc[cp], dp), item e of 5 QT: per query tile four
       // products, then the packed tile into its half of the pair's A operand
@@ -991,13 +1004,20 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         constexpr int e = decltype(ec)::value, st = decltype(st_c)::value, cs = st & 1;
         constexpr int t = e / 4, i = e % 4;
         if constexpr (DROP && i == 0) {
-          // one Philox call for the 4 x 4 block (queries q & ~3 .., keys of this
-          // lane's 4-key group): word q % 4 is this lane's query, byte r key r
-          const u32x4 ctr = {(uint32_t)(krow + 16 * st) >> 2, (uint32_t)(qcol + 16 * t) >> 2,
-                             (uint32_t)h, (uint32_t)b};
-          const u32x4 x = philox4x32_10(ctr, p.seed_lo, p.seed_hi);
-          const int qi = l16 & 3;
-          const uint32_t word = qi == 0 ? x[0] : qi == 1 ? x[1] : qi == 2 ? x[2] : x[3];
+          // One Philox call per 4 x 4 block (queries q & ~3 .., keys of a 4-key
+          // group): word q % 4 is query q, byte r key r.  The four lanes of a query
+          // quad share their blocks, so lane q draws one of them (query tile q % QT
+          // of sub-block st + q / QT; with two query tiles, the even step draws the
+          // odd step's blocks too) and a quad transpose hands every lane its word
+          // of each: word w of block w.
+          constexpr bool DRAW = t == 0 && st % (4 / QT) == 0;
+          if constexpr (DRAW) {
+            const int q4 = l16 & 3, bt = q4 % QT, bst = st + q4 / QT;
+            const u32x4 ctr = {(uint32_t)(krow + 16 * bst) >> 2, (uint32_t)(qcol + 16 * bt) >> 2,
+                               (uint32_t)h, (uint32_t)b};
+            qwd = quad_transpose(philox4x32_10(ctr, p.seed_lo, p.seed_hi), q4);
+          }
+          const uint32_t word = qwd[QT == 4 ? t : 2 * (st % 2) + t];
 #pragma unroll
           for (int r = 0; r < 4; ++r) zf[cs][t][r] = keep_factor(word, r, p.keep_t, p.drop_scale);
         }
@@ -1079,6 +1099,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       auto valu = [&](auto stc, auto mc, auto gc) {
         constexpr int st = decltype(stc)::value, m = decltype(mc)::value, cp = (st + 1) & 1;
         constexpr DqPlace<NK, QT, st, LA, OPS, NBUF == 2> PL{};
+        static_assert(!DROP || none_before(PL.exp, PL.exp[0][0]), "query tile 0 draws the dropout blocks");
         (void)gc;
         // the copies of a later tile, in steps 2-3 (after the mid-tile barrier)
         static_for<OPS>([&](auto cc) {

@@ -581,11 +581,46 @@ __device__ __forceinline__ u32x4 philox4x32_10(u32x4 c, uint32_t k0, uint32_t k1
   return c;
 }
 
-// Keep factors of the four elements of one 4 x 4 block that a lane holds: byte
-// `byte_of(e)` of word `word_of(e)` below keep_t keeps element e, with factor
-// scale; word and byte positions come from the caller's layout.
+// Keep factor of one element: its byte of the block's output below keep_t keeps
+// it, with factor scale.
 __device__ __forceinline__ float keep_factor(uint32_t word, int byte, uint32_t keep_t, float scale) {
   return ((word >> (8 * byte)) & 0xffu) < keep_t ? scale : 0.f;
+}
+
+// 4 x 4 transpose across the four lanes q = 0..3 of a quad: word w of lane q
+// becomes what word q of lane w held.  Two exchange stages (lanes q ^ 2, then
+// q ^ 1) through DPP quad permutations, each keeping or taking two words.
+// Lets the four lanes that share a set of 4 x 4 dropout blocks each draw one
+// block's Philox output and hand the others their parts of it.
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 m, int q) {
+  auto x2 = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false); };
+  auto x1 = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false); };
+  const bool b1 = q & 2, b0 = q & 1;
+  u32x4 p = {x2(m[2]), x2(m[3]), x2(m[0]), x2(m[1])};
+  m = {b1 ? p[0] : m[0], b1 ? p[1] : m[1], b1 ? m[2] : p[2], b1 ? m[3] : p[3]};
+  p = {x1(m[1]), x1(m[0]), x1(m[3]), x1(m[2])};
+  return {b0 ? p[0] : m[0], b0 ? m[1] : p[1], b0 ? p[2] : m[2], b0 ? m[3] : p[3]};
+}
+
+// Whether no entry of slot table s comes before slot v: a value made in slot v
+// (first in its slot) is ready for every item placed by s.
+template <int A, int B>
+constexpr bool none_before(const int (&s)[A][B], int v) {
+  for (int a = 0; a < A; ++a)
+    for (int b = 0; b < B; ++b)
+      if (s[a][b] < v) return false;
+  return true;
+}
+
+// Byte transpose within a lane: byte r of word c of the result is byte c of word r
+// of x (eight byte permutations).
+__device__ __forceinline__ u32x4 byte_transpose(const u32x4& x) {
+  const uint32_t u01 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);  // bytes 0-1 of x0, x1
+  const uint32_t u23 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+  const uint32_t v01 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);  // bytes 2-3
+  const uint32_t v23 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+  return {__builtin_amdgcn_perm(u23, u01, 0x05040100u), __builtin_amdgcn_perm(u23, u01, 0x07060302u),
+          __builtin_amdgcn_perm(v23, v01, 0x05040100u), __builtin_amdgcn_perm(v23, v01, 0x07060302u)};
 }
 
 // max(a, b, c) in one v_max3_f32.  fmaxf on MFMA results costs a canonicalizing

@@ -136,6 +136,15 @@ struct FwdPlace {
   }
 };
 
+// Sub-block 1's dropout draw (at exp[1][0][0]) comes after every item of sub-block
+// 0 that reads the first draw (exp[0][t][0]; the same slot runs sub-block 0 first).
+template <int QT>
+constexpr bool fwd_draw_after_uses(const int (&exp)[2][QT][4]) {
+  for (int t = 0; t < QT; ++t)
+    if (exp[0][t][0] > exp[1][0][0]) return false;
+  return true;
+}
+
 template <int DT, int D, bool CAUSAL, int FT, int MODE = 0>
 __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   constexpr bool BIAS = tile_bias(FT), DROP = FT == FT_DROPOUT || FT == FT_DROP, KB = FT == FT_KEYBIAS;
@@ -304,6 +313,8 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     float mx[QT];
     u32x2 bv[2][QT];  // bias of the pair's sub-blocks per query tile (keys in elements)
     f32x4 zf[2][QT];  // dropout keep factors of the pair's sub-blocks
+    u32x4 qwd;        // keep words of this lane's query in the blocks drawn last
+    static_assert(QT == 4 || QT == 2, "dropout block draw");
 
     using Steps = FwdSteps<NK, QT>;
     auto begin = [&](auto stc) {
@@ -380,6 +391,12 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
       constexpr int st = decltype(stc)::value, mi = decltype(mc)::value;
       using Plan = typename Steps::template P<st>;
       constexpr FwdPlace<NK, QT, st, LA, OPS, NBUF == 2> PL{};
+      // dropout: the draws come first, and a second draw (four query tiles) after
+      // every use of the first
+      static_assert(!DROP || (none_before(PL.exp[0], PL.exp[0][0][0]) &&
+                              none_before(PL.exp[1], QT == 4 ? PL.exp[1][0][0] : PL.exp[0][0][0])),
+                    "the dropout draws precede their uses");
+      static_assert(!DROP || QT == 2 || fwd_draw_after_uses(PL.exp), "second dropout draw after the first's uses");
       (void)gc;
       static_for<OPS>([&](auto cc) {
         if constexpr (PL.copy[decltype(cc)::value] == mi) copy_part(cc, fsrc, fbuf);
@@ -439,13 +456,20 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
             constexpr int i = decltype(ic)::value;
             if constexpr (PL.exp[sb][t][i] == mi) {
               if constexpr (DROP && i == 0) {
-                // one Philox call for the 4 x 4 block (queries q & ~3 .., this lane's
-                // 4 keys): word q % 4 is this lane's query, byte r key r
-                const u32x4 ctr = {(uint32_t)(kv0 + 16 * (2 * st + sb) + 4 * j4) >> 2,
-                                   (uint32_t)(qw + 16 * t + l16) >> 2, (uint32_t)h, (uint32_t)b};
-                const u32x4 x = philox4x32_10(ctr, p.seed_lo, p.seed_hi);
-                const int qi = l16 & 3;
-                const uint32_t word = qi == 0 ? x[0] : qi == 1 ? x[1] : qi == 2 ? x[2] : x[3];
+                // One Philox call per 4 x 4 block (queries q & ~3 .., keys of a
+                // 4-key group): word q % 4 is query q, byte r key r.  The four lanes
+                // of a query quad share their blocks, so lane q draws one of them
+                // (query tile q % QT of sub-block sb + q / QT; with two query tiles,
+                // sub-block 0 draws sub-block 1's blocks too) and a quad transpose
+                // hands every lane its word of each: word w of block w.
+                constexpr bool DRAW = t == 0 && sb % (4 / QT) == 0;
+                if constexpr (DRAW) {
+                  const int q4 = l16 & 3, bt = q4 % QT, bsb = sb + q4 / QT;
+                  const u32x4 ctr = {(uint32_t)(kv0 + 16 * (2 * st + bsb) + 4 * j4) >> 2,
+                                     (uint32_t)(qw + 16 * bt + l16) >> 2, (uint32_t)h, (uint32_t)b};
+                  qwd = quad_transpose(philox4x32_10(ctr, p.seed_lo, p.seed_hi), q4);
+                }
+                const uint32_t word = qwd[QT == 4 ? t : 2 * sb + t];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) zf[sb][t][r] = keep_factor(word, r, p.keep_t, p.drop_scale);
               }
