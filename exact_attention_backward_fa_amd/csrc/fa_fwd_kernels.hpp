@@ -23,20 +23,23 @@
 // sees a key, and P = exp2(s c - m).  P is rounded to the input type for the P V
 // product, so the headroom H above m that a score may reach is set by that type's
 // range: 64 for bf16 (float32's exponent range, P < 2^64) and 15 for fp16, whose
-// largest finite value is 65504 < 2^16 (P < 2^15).  Relative precision does not
-// depend on the size of P, so O and the row sums never need rescaling while no
-// score exceeds m + H.  A score above m + H after the first pair (logits rising by
-// more than 44 nats along the row for bf16, 10.4 nats for fp16) raises m and marks
-// the item; the workgroup then runs the item a second time from zero with the
-// raised references, which no score can exceed by more than H.
-// The plain instances run in two launches.  The first (MODE 1) sets each column's
-// reference from the first pair before its loop, takes no per-pair maxima, and
-// checks at the end that no column's row sum exceeds 2^H: then no P did either and
-// the result is the one the per-pair test would have given.  Otherwise it marks
-// the item (LSE = NaN on its rows) and writes no O, and the second launch
-// (MODE 2) runs the marked items with the per-pair test; its other workgroups
-// exit at once.  The other instances run every item with the per-pair test
-// (MODE 0).
+// largest finite value is 65504 < 2^16 (P < 2^15; with dropout, whose kept P is
+// scaled by Z before rounding, the largest H with 2^H Z < 65520).  Relative
+// precision does not depend on the size of P, so O and the row sums never need
+// rescaling while no score exceeds m + H.  A score above m + H after the first
+// pair (logits rising by more than 44 nats along the row for bf16, 10.4 nats for
+// fp16) raises m and marks the item; the workgroup then runs the item a second
+// time from zero with the raised references, which no score can exceed by more
+// than H.
+// The instances without bias (plain, and dropout alone) run in two launches.  The
+// first (MODE 1) sets each column's reference from the first pair before its loop,
+// takes no per-pair maxima, and checks at the end that no column's row sum exceeds
+// 2^H: then no P did either and the result is the one the per-pair test would have
+// given.  Otherwise it marks the item (LSE = NaN on its rows) and writes no O, and
+// the second launch (MODE 2) runs the marked items with the per-pair test; its
+// other workgroups exit at once.  The bias instances run every item with the
+// per-pair test (MODE 0): a bias may hide a row's first keys, leaving its
+// reference unset before the loop.
 // The row sums l of P are float32 (each lane sums its keys; the four lanes of a
 // column are added at the end; summing the bf16-rounded P through the matrix
 // pipe was measured to miss the LSE bound on short rows).  At the end O is divided
@@ -64,12 +67,28 @@ struct FwdParams {
   long long bias_sb, bias_sh, bias_sq;
   unsigned keep_t, seed_lo, seed_hi;
   float drop_scale;
+  float headroom;  // H of the dropout instances (fwd_headroom_dropout)
 };
 
 // log2 headroom above the reference of a query column: P = exp2(score - m) stays
 // below 2^H, inside the range of the 16-bit type P is rounded to (fp16: 65504)
 template <int DT>
 constexpr float fwd_headroom() { return DT == 0 ? 15.f : 64.f; }
+
+// With dropout, P o Z is rounded (Z = drop_scale, up to 256): for fp16 the headroom
+// drops by whole units until 2^H Z is below 65520, the least value that rounds to
+// inf.  bf16 keeps its 64.
+template <int DT>
+inline float fwd_headroom_dropout(float z) {
+  float h = fwd_headroom<DT>(), top = 32768.f;
+  if (DT == 0) {
+    while (h > 0.f && top * z >= 65520.f) {
+      h -= 1.f;
+      top *= 0.5f;
+    }
+  }
+  return h;
+}
 
 // Step J: S^T of pair J (2 NK operands x QT query tiles) | P V of the previous pair
 // (2 NK head-dim tiles x QT).
@@ -214,11 +233,12 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
   // logits of the bias instances; finite, so that a column with no visible key yet
   // gives exp2(-inf - m) = 0
   constexpr float kUnset = -1e30f;
+  const float H = DROP ? p.headroom : fwd_headroom<DT>();
   float m[QT], thr[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
     m[t] = kUnset;
-    thr[t] = BIAS ? m[t] + fwd_headroom<DT>() : (m[t] + fwd_headroom<DT>()) / c;
+    thr[t] = BIAS ? m[t] + H : (m[t] + H) / c;
   }
   bool dirty = false;  // a reference was raised after it had been used
   __shared__ int s_dirty;
@@ -440,10 +460,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
             float v = BIAS ? mx[t] : mx[t] * c;
             v = fmaxf(v, __shfl_xor(v, 16));
             v = fmaxf(v, __shfl_xor(v, 32));
-            if (v > m[t] + fwd_headroom<DT>()) {
+            if (v > m[t] + H) {
               dirty = dirty || m[t] != kUnset;
               m[t] = v;
-              thr[t] = BIAS ? v + fwd_headroom<DT>() : (v + fwd_headroom<DT>()) / c;
+              thr[t] = BIAS ? v + H : (v + H) / c;
             }
           }
         }
@@ -604,7 +624,7 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
     phase(nkt, std::integral_constant<int, 0>());
     if constexpr (MODE == 1) {
       // no P above 2^H if no column's row sum is (also true for inf and NaN sums)
-      const float limit = exp2f(fwd_headroom<DT>());
+      const float limit = exp2f(H);
 #pragma unroll
       for (int t = 0; t < QT; ++t) {
         float l = lsum[t];
@@ -686,9 +706,10 @@ hipError_t run_fwd(const FwdArgs& a, hipStream_t s) {
   p.seed_lo = (unsigned)(a.x.seed & 0xffffffffu);
   p.seed_hi = (unsigned)(a.x.seed >> 32);
   p.drop_scale = a.x.keep_t > 0 ? 256.f / (float)a.x.keep_t : 0.f;
+  p.headroom = fwd_headroom_dropout<DT>(p.drop_scale);
   constexpr int BM = 4 * 16 * FwdShape<D, FT>::QT;  // queries per workgroup
   const dim3 grid((unsigned)(((pb.Nq + BM - 1) / BM) * pb.Hq * pb.B));
-  if constexpr (FT == FT_PLAIN) {
+  if constexpr (FT == FT_PLAIN || FT == FT_DROP) {
     // the fast pass, then the items it marked
     hipLaunchKernelGGL((fwd_kernel<DT, D, CAUSAL, FT, 1>), grid, dim3(256), 0, s, p);
     const hipError_t e = hipGetLastError();

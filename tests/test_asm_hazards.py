@@ -46,11 +46,12 @@ def _kernels(texts):
 
 def _expected_kernels(unit):
     """Kernels a unit instantiates: one, or two for a dQ pass with a dBias (feature
-    sets 1 and 2: 2-byte and 8-byte dBias stores) and for a plain forward (its fast
-    pass and the rerun of the items that pass marks)."""
+    sets 1 and 2: 2-byte and 8-byte dBias stores) and for a forward without bias
+    (plain or feature set 4, dropout alone: its fast pass and the rerun of the
+    items that pass marks)."""
     if unit.name.startswith("dq_") and unit.name.endswith(("_f1", "_f2")):
         return 2
-    if unit.name.startswith("fwd_") and "_f" not in unit.name:
+    if unit.name.startswith("fwd_") and ("_f" not in unit.name or unit.name.endswith("_f4")):
         return 2
     return 1
 

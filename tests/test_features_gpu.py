@@ -300,6 +300,44 @@ def test_dropout_p_one(device):
     assert np.abs(lse[fin] - ref["lse"][fin]).max() <= 1e-3
 
 
+RISING_DROP = [(64, False, 0.75, 13), (128, True, 0.9, 12)]
+
+
+@pytest.mark.parametrize("d,causal,p,h", RISING_DROP, ids=[f"d{c[0]}_p{c[2]}" for c in RISING_DROP])
+def test_dropout_fp16_rising_scores(d, causal, p, h, device):
+    """fp16 with a high dropout rate and scores that rise about 14 log2 units past
+    the first pair of keys.  The forward rounds P o Z to fp16 for the P V product,
+    with Z = 256 / T up to 4 (p = 0.75) or 9.8 (p = 0.9), so a P below the plain
+    headroom 2^15 could still round to inf once scaled; the headroom drops to h
+    (the largest with 2^h Z < 65520), and items past it rerun with raised
+    references.  O, LSE and the gradients must be finite and match the oracle."""
+    B, Hq, Hkv, N = 1, 2, 1, 384
+    g = torch.Generator().manual_seed(4545)
+    u = torch.full((d,), 1.0 / np.sqrt(d))
+    ramp = torch.arange(N, dtype=torch.float32) / N
+    amp = 10.8 / 5.0
+    x = {
+        "q": (5.0 * u + 0.02 * torch.randn(B, Hq, N, d, generator=g)).half(),
+        "k": (amp * ramp[:, None] * u + 0.02 * torch.randn(B, Hkv, N, d, generator=g)).half(),
+        "v": torch.randn(B, Hkv, N, d, generator=g).half(),
+        "do": torch.randn(B, Hq, N, d, generator=g).half(),
+    }
+    t = int(np.floor((1.0 - p) * 256 + 0.5))
+    assert 2.0 ** h * 256 / t < 65520 <= 2.0 ** (h + 1) * 256 / t
+    # the premise: visible scores more than h but less than 15 log2 units past the
+    # maximum over the first 32 keys, in some rows (causal) or all
+    sc = orc.as_f64(x["q"][0]) @ orc.as_f64(x["k"][0, 0]).T / np.log(2.0)
+    rows = range(32, N)
+    over = np.array([[sc[hh, r, 32:(r + 1 if causal else N)].max() - sc[hh, r, :32].max() for r in rows]
+                     for hh in range(Hq)])
+    assert over.max() < 15.0 and (over > h).mean() > (0.1 if causal else 0.9)
+    case = inputs.Case(f"rising_drop_d{d}", 0, 0, B, Hq, Hkv, N, N, d, "fp16", causal, 1.0)
+    ref = _oracle(case, x, None, p, 99, False)
+    got = _run(case, x, None, p, 99, device, False)
+    assert all(bool(torch.isfinite(got[k]).all()) for k in ("o", "dq", "dk", "dv"))
+    _compare(case, got, ref, case.name)
+
+
 def test_long_sequence_bias_dropout(device):
     """N = 2048 causal GQA bf16 with a full bias and dropout: several work items per
     head in every kernel; every head compared."""
