@@ -17,12 +17,15 @@ timed on the host cores, with the host's CPU model, BLAS library and one-thread
 oracle timings of the small workloads.
 
     python bench.py [--steps K] [--warmup W] [--dq-mode auto|atomic|separate]
-                    [--workload NAME[,NAME...]] [--bias keys|full] [--dbias] [--dropout P]
+                    [--workload NAME[,NAME...]] [--head-dim D] [--bias keys|full] [--dbias]
+                    [--dropout P]
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
+import math
 import os
 import sys
 import time
@@ -308,6 +311,9 @@ def main() -> int:
                          "full [B,Hq,N_q,N_kv] bias (timed through fa_*_bias_dropout)")
     ap.add_argument("--dbias", action="store_true", help="also write dBias [B,Hq,N_q,N_kv]")
     ap.add_argument("--dropout", type=float, default=0.0, help="dropout probability of P")
+    ap.add_argument("--head-dim", type=int, default=None,
+                    help="run the workload(s) with this head dimension instead (softmax "
+                         "scale 1/sqrt(d)); the name gets a _d<D> suffix")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, copy a 512 MiB buffer once (known traffic) so that "
                          "a counter profile of this run can scale FETCH_SIZE/WRITE_SIZE")
@@ -328,6 +334,9 @@ def main() -> int:
 
     names = (args.workload or inputs.HEADLINE).split(",")
     cases = [inputs.case_by_name(nm.strip()) for nm in names]
+    if args.head_dim is not None:
+        cases = [dataclasses.replace(c, name=f"{c.name}_d{args.head_dim}", d=args.head_dim,
+                                     scale=1.0 / math.sqrt(args.head_dim)) for c in cases]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     for case in cases:

@@ -1,8 +1,10 @@
 // Device-side helpers shared by the attention kernels (gfx950 / CDNA4).
 //
-// Matrix products use v_mfma_f32_32x32x16_{f16,bf16}: a 64-lane wave multiplies
-// a 32x16 A tile by a 16x32 B tile into a 32x32 float32 tile.  Operand layout
-// (lane = 0..63, l32 = lane % 32, g = lane / 32):
+// The forward, dK/dV and dQ kernels multiply with v_mfma_f32_16x16x32 (layout
+// below, Mx<DT>); the fused atomic kernel with v_mfma_f32_32x32x16_{f16,bf16}
+// (Dt<DT>::mma): a 64-lane wave multiplies a 32x16 A tile by a 16x32 B tile into a
+// 32x32 float32 tile.  Its operand layout (lane = 0..63, l32 = lane % 32,
+// g = lane / 32):
 //   A: lane holds 8 16-bit values of row l32, at contraction slots 8g..8g+7;
 //   B: lane holds 8 16-bit values of column l32, at the same slots;
 //   C: lane holds 16 floats; element i is row 8*(i/4) + 4g + (i%4), column l32.
