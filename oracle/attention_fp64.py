@@ -357,43 +357,61 @@ def naive_forward(q, k, v, scale: float, causal: bool):
 
 # --- Row-sampled variants for shapes too large to materialise whole --------------
 
-def forward_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows):
-    """O and LSE of selected query rows of one (batch, head); cost O(len(rows)*Nkv*d)."""
+def forward_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows, bias=None,
+                 dropout_p: float = 0.0, seed: int = 0):
+    """O and LSE of selected query rows of one (batch, head); cost O(len(rows)*Nkv*d).
+    ``bias``, ``dropout_p`` and ``seed`` as in ``forward``."""
     rows = np.asarray(rows)
-    Hq, Hkv = q.shape[1], k.shape[1]
-    Nq, Nkv = q.shape[2], k.shape[2]
+    B, Hq, Nq = q.shape[0], q.shape[1], q.shape[2]
+    Hkv, Nkv = k.shape[1], k.shape[2]
     g = kv_head_index(h, Hq, Hkv)
+    bias = _bias_of(bias, B, Hq, Nq, Nkv)
     qr = as_f64(q[b, h][rows])
     kg, vg = as_f64(k[b, g]), as_f64(v[b, g])
-    s = masked_scores(qr, kg, scale, keep_mask(rows, Nq, Nkv, causal))
+    s = masked_scores(qr, kg, scale, keep_mask(rows, Nq, Nkv, causal),
+                      None if bias is None else bias[b, h, rows])
     l_ = log_sum_exp(s)
-    return probabilities(s, l_) @ vg, l_
+    p = probabilities(s, l_)
+    z = _dropout_of(b, h, rows, Nkv, dropout_p, seed)
+    return (p if z is None else p * z) @ vg, l_
 
 
-def dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: int, rows):
-    """dQ of selected query rows; each row needs only its own S, P and dP rows."""
+def dq_rows(q, k, v, do, scale: float, causal: bool, b: int, h: int, rows, bias=None,
+            dropout_p: float = 0.0, seed: int = 0):
+    """dQ of selected query rows; each row needs only its own S, P and dP rows.
+    ``bias``, ``dropout_p`` and ``seed`` as in ``forward``."""
     rows = np.asarray(rows)
-    Hq, Hkv = q.shape[1], k.shape[1]
-    Nq, Nkv = q.shape[2], k.shape[2]
+    B, Hq, Nq = q.shape[0], q.shape[1], q.shape[2]
+    Hkv, Nkv = k.shape[1], k.shape[2]
     g = kv_head_index(h, Hq, Hkv)
+    bias = _bias_of(bias, B, Hq, Nq, Nkv)
     qr, dor = as_f64(q[b, h][rows]), as_f64(do[b, h][rows])
     kg, vg = as_f64(k[b, g]), as_f64(v[b, g])
-    s = masked_scores(qr, kg, scale, keep_mask(rows, Nq, Nkv, causal))
+    s = masked_scores(qr, kg, scale, keep_mask(rows, Nq, Nkv, causal),
+                      None if bias is None else bias[b, h, rows])
     p = probabilities(s, log_sum_exp(s))
-    ds = score_grad(p, dor @ vg.T, row_delta(dor, p @ vg))
+    z = _dropout_of(b, h, rows, Nkv, dropout_p, seed)
+    dp = dor @ vg.T
+    if z is not None:
+        dp = dp * z
+    ds = score_grad(p, dp, row_delta(dor, (p if z is None else p * z) @ vg))
     return grad_q(ds, kg, scale)
 
 
-def dkdv_rows(q, k, v, do, scale: float, causal: bool, b: int, g: int, kv_rows):
+def dkdv_rows(q, k, v, do, scale: float, causal: bool, b: int, g: int, kv_rows, bias=None,
+              dropout_p: float = 0.0, seed: int = 0, heads=None):
     """dK and dV of selected key rows of one (batch, kv head).
 
     Only query rows that can see one of the selected keys contribute; with a
     causal mask and keys near the end of the sequence that is a short tail, so
-    this stays cheap at any length.
+    this stays cheap at any length.  ``heads``: the query heads of the group to
+    sum over (default all of them).  ``bias``, ``dropout_p`` and ``seed`` as in
+    ``forward``.
     """
     kv_rows = np.asarray(kv_rows)
-    Hq, Hkv = q.shape[1], k.shape[1]
-    Nq, Nkv, d = q.shape[2], k.shape[2], q.shape[3]
+    B, Hq, Nq, d = q.shape
+    Hkv, Nkv = k.shape[1], k.shape[2]
+    bias = _bias_of(bias, B, Hq, Nq, Nkv)
     kg, vg = as_f64(k[b, g]), as_f64(v[b, g])
     dk_out = np.zeros((kv_rows.shape[0], d))
     dv_out = np.zeros((kv_rows.shape[0], d))
@@ -401,18 +419,23 @@ def dkdv_rows(q, k, v, do, scale: float, causal: bool, b: int, g: int, kv_rows):
     if causal and kv_rows.shape[0] > 0:
         first = max(0, int(kv_rows.min()) - (Nkv - Nq))
     contributing = np.arange(first, Nq)
-    for h in range(Hq):
+    for h in range(Hq) if heads is None else heads:
         if kv_head_index(h, Hq, Hkv) != g:
             continue
         for rows in _row_chunks(contributing):
             qr, dor = as_f64(q[b, h][rows]), as_f64(do[b, h][rows])
             # LSE and D need whole rows of S and P; dP and dS only the selected
             # key columns
-            s = masked_scores(qr, kg, scale, keep_mask(rows, Nq, Nkv, causal))
+            s = masked_scores(qr, kg, scale, keep_mask(rows, Nq, Nkv, causal),
+                              None if bias is None else bias[b, h, rows])
             p = probabilities(s, log_sum_exp(s))
-            dlt = row_delta(dor, p @ vg)
-            p_sel = p[:, kv_rows]
-            ds_sel = score_grad(p_sel, dor @ vg[kv_rows].T, dlt)
+            z = _dropout_of(b, h, rows, Nkv, dropout_p, seed)
+            pz = p if z is None else p * z
+            dlt = row_delta(dor, pz @ vg)
+            dp_sel = dor @ vg[kv_rows].T
+            if z is not None:
+                dp_sel = dp_sel * z[:, kv_rows]
+            ds_sel = score_grad(p[:, kv_rows], dp_sel, dlt)
             dk_out += grad_k(ds_sel, qr, scale)
-            dv_out += grad_v(p_sel, dor)
+            dv_out += grad_v(pz[:, kv_rows], dor)
     return dk_out, dv_out

@@ -294,6 +294,45 @@ def pin_ext_finite_differences(orc, seed=23) -> float:
     return worst
 
 
+def pin_ext_row_variants(orc, seed=31) -> float:
+    """Row-sampled functions with a bias and dropout against the whole-tensor ones
+    (the mask of each element depends on its true batch, head, row and key), and
+    dK/dV summed head by head (``heads=``) against the whole group."""
+    worst = 0.0
+    rng = np.random.default_rng(seed)
+    for (B, Hq, Hkv, Nq, Nkv, d, causal, bshape, pdrop) in (
+            (2, 4, 2, 13, 17, 8, True, (2, 1, 1, 17), 0.3),
+            (1, 2, 1, 9, 9, 8, False, (1, 2, 9, 9), 0.5),
+            (2, 2, 2, 11, 7, 4, True, None, 0.25)):
+        q = _rand(rng, (B, Hq, Nq, d))
+        k = _rand(rng, (B, Hkv, Nkv, d))
+        v = _rand(rng, (B, Hkv, Nkv, d))
+        do = _rand(rng, (B, Hq, Nq, d))
+        bias = None if bshape is None else _rand(rng, bshape)
+        kw = {"bias": bias, "dropout_p": pdrop, "seed": 4321}
+        o, lse = orc.forward(q, k, v, 0.3, causal, **kw)
+        dq, dk, dv = orc.backward(q, k, v, do, 0.3, causal, **kw)
+        rows = np.array([0, 3, Nq - 2, Nq - 1])
+        kv_rows = np.array([0, 1, Nkv - 2, Nkv - 1])
+        G = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                orow, lrow = orc.forward_rows(q, k, v, 0.3, causal, b, h, rows, **kw)
+                fin = np.isfinite(lse[b, h, rows])
+                worst = max(worst, _rel(orow, o[b, h, rows]),
+                            float(np.abs(lrow[fin] - lse[b, h, rows][fin]).max(initial=0.0)))
+                worst = max(worst, _rel(orc.dq_rows(q, k, v, do, 0.3, causal, b, h, rows, **kw),
+                                        dq[b, h, rows]))
+            for g in range(Hkv):
+                dkr, dvr = orc.dkdv_rows(q, k, v, do, 0.3, causal, b, g, kv_rows, **kw)
+                worst = max(worst, _rel(dkr, dk[b, g, kv_rows]), _rel(dvr, dv[b, g, kv_rows]))
+                parts = [orc.dkdv_rows(q, k, v, do, 0.3, causal, b, g, kv_rows, heads=[h], **kw)
+                         for h in range(g * G, (g + 1) * G)]
+                worst = max(worst, _rel(sum(pp[0] for pp in parts), dkr),
+                            _rel(sum(pp[1] for pp in parts), dvr))
+    return worst
+
+
 def pin_ext_identities(orc, seed=29) -> float:
     """With a bias and dropout: rowsum dS = 0, <Q,dQ> = <K,dK> (Q -> aQ, K -> K/a
     leaves the scores unchanged), <dO,O> = <V,dV> (L is linear in V); a zero bias
@@ -421,6 +460,7 @@ ALL_PINS = [
     ("row_variants", pin_row_variants, NAIVE_TOL),
     ("ext_finite_differences", pin_ext_finite_differences, FD_TOL),
     ("ext_identities", pin_ext_identities, IDENTITY_TOL),
+    ("ext_row_variants", pin_ext_row_variants, NAIVE_TOL),
     ("philox", pin_philox, 0.0),
     ("dropout_unbiased", pin_dropout_unbiased, 0.0),
 ]

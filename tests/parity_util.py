@@ -106,17 +106,17 @@ def assert_within(case, errs: dict) -> None:
         assert v <= bound, f"{case.name}: {k} error {v:.3e} > {bound:.1e}"
 
 
-def dkdv_rows_by_head(case, x: dict, b: int, g: int, kv_rows):
+def dkdv_rows_by_head(case, x: dict, b: int, g: int, kv_rows, **extras):
     """orc.dkdv_rows for key rows of one (batch, kv head), as the sum of each query
     head's own contribution, the G heads computed in parallel threads (NumPy
-    releases the interpreter lock inside its array loops and BLAS calls)."""
+    releases the interpreter lock inside its array loops and BLAS calls).
+    ``extras``: bias, dropout_p and seed, as orc.dkdv_rows takes them."""
     from concurrent.futures import ThreadPoolExecutor
     G = case.Hq // case.Hkv
 
     def one(h):
-        return orc.dkdv_rows(x["q"][b:b + 1, h:h + 1], x["k"][b:b + 1, g:g + 1],
-                             x["v"][b:b + 1, g:g + 1], x["do"][b:b + 1, h:h + 1],
-                             case.scale, case.causal, 0, 0, kv_rows)
+        return orc.dkdv_rows(x["q"], x["k"], x["v"], x["do"], case.scale, case.causal, b, g,
+                             kv_rows, heads=[h], **extras)
 
     with ThreadPoolExecutor(max_workers=G) as ex:
         parts = list(ex.map(one, range(g * G, (g + 1) * G)))

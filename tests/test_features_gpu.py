@@ -338,6 +338,43 @@ def test_dropout_fp16_rising_scores(d, causal, p, h, device):
     _compare(case, got, ref, case.name)
 
 
+@pytest.mark.parametrize("what", ["dropout", "key_mask"])
+def test_headline_shape_features_sampled(what, device):
+    """The full headline workload (causal GQA B=4 Hq=32 Hkv=8 N=8192 d=128 bf16)
+    through the feature entry points, as `bench.py --dropout 0.1` (seed 77) and
+    `bench.py --bias keys` (the last eighth of the keys masked) run it.  Compared
+    with the oracle's row functions under the same mask or bias: 32 query rows
+    (O, LSE, dQ) of the first and the last head, and key rows (dK, dV) of the first
+    and last kv head: the trailing 48, and for the first also the leading 64, whose
+    sums run over every query row of the group."""
+    case = inputs.case_by_name(inputs.HEADLINE)
+    x = inputs.make_inputs(case)
+    N = case.Nkv
+    if what == "dropout":
+        bias, p, seed = None, 0.1, 77
+    else:
+        store = torch.zeros(case.B, 1, 1, (N + 7) // 8 * 8, dtype=case.torch_dtype)
+        store[..., N - N // 8:] = float("-inf")
+        bias, p, seed = store[..., :N], 0.0, 0
+    pu.log(f"[gpu] headline shape, {what}")
+    got = _run(case, x, bias, p, seed, device, False)
+    extras = {"bias": None if bias is None else orc.as_f64(bias), "dropout_p": p, "seed": seed}
+    rng = np.random.default_rng(2024)
+    rows = np.unique(np.concatenate([[0, 1, N // 2, N - 2, N - 1], rng.integers(0, N, 27)]))
+    tail = np.arange(N - 48, N)
+    for n, (b, h, g) in enumerate([(0, 0, 0), (case.B - 1, case.Hq - 1, case.Hkv - 1)]):
+        kv_rows = np.concatenate([np.arange(64), tail]) if n == 0 else tail
+        pu.log(f"[oracle] rows b={b} h={h} g={g} ({len(kv_rows)} key rows)")
+        o, l_ = orc.forward_rows(x["q"], x["k"], x["v"], case.scale, case.causal, b, h, rows, **extras)
+        dq = orc.dq_rows(x["q"], x["k"], x["v"], x["do"], case.scale, case.causal, b, h, rows,
+                         **extras)
+        dk, dv = pu.dkdv_rows_by_head(case, x, b, g, kv_rows, **extras)
+        ref = {"o": o, "lse": l_, "dq": dq, "dk": dk, "dv": dv}
+        sub = {"o": got["o"][b, h, rows], "lse": got["lse"][b, h, rows], "dq": got["dq"][b, h, rows],
+               "dk": got["dk"][b, g, kv_rows], "dv": got["dv"][b, g, kv_rows]}
+        _compare(case, sub, ref, f"{what} rows b={b} h={h}")
+
+
 def test_long_sequence_bias_dropout(device):
     """N = 2048 causal GQA bf16 with a full bias and dropout: several work items per
     head in every kernel; every head compared."""
