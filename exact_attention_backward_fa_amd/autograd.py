@@ -72,7 +72,7 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
 
     q: [B, Hq, Nq, d]; k, v: [B, Hkv, Nkv, d] with Hq a multiple of Hkv (query head h
     reads kv head h // (Hq / Hkv)); float16 or bfloat16 on one HIP device; d in
-    {32, 64, 96, 128, 256}.  ``scale`` defaults to 1/sqrt(d).  The causal mask is
+    {32, 64, ..., 256} (multiples of 32).  ``scale`` defaults to 1/sqrt(d).  The causal mask is
     aligned to the bottom-right corner: query i sees key j when j <= i + (Nkv - Nq).
     ``dq_mode`` picks the backward's dQ path ("auto", "atomic" or "separate").
     ``bias`` (q's dtype, 4-D, each dimension its full size or 1, rows 16-byte

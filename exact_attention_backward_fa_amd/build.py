@@ -33,7 +33,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 # Host-side sources (entry points, dispatch, conversions).
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_api.cpp", "fa_noalloc.hip"]
 # Template instances: (dtype 0 fp16 / 1 bf16, head dim, causal).
-HEAD_DIMS = (32, 64, 96, 128, 256)
+HEAD_DIMS = (32, 64, 96, 128, 160, 192, 224, 256)
 INSTANCES = [(dt, d, c) for dt in (0, 1) for d in HEAD_DIMS for c in (0, 1)]
 # The fused atomic dK/dV/dQ kernel is built for these head dims only.
 ATOMIC_HEAD_DIMS = (64, 128)

@@ -216,8 +216,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_NULLPTR: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "invalid shape (B, Hq, Hkv, N_q, N_kv), Hq % Hkv != 0, or a size limit exceeded";
     case FA_ERR_HEADDIM:
-      return "head dimension d must be 32, 64, 96, 128 or 256 (the atomic dQ path, a score bias "
-             "and dropout: 64 or 128)";
+      return "head dimension d must be a multiple of 32 up to 256: 32, 64, 96, 128, 160, 192, 224 "
+             "or 256 (the atomic dQ path, a score bias and dropout: 64 or 128)";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "softmax_scale must be finite and > 0";
     case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned, or smaller than required";

@@ -9,11 +9,9 @@
 
 namespace fa {
 
-// Head dims with a kernel instance (every kernel family but the fused atomic one,
-// which is built for 64 and 128 only).
-constexpr bool head_dim_supported(int d) {
-  return d == 32 || d == 64 || d == 96 || d == 128 || d == 256;
-}
+// Head dims with a kernel instance: every multiple of 32 up to 256 (every kernel
+// family but the fused atomic one, which is built for 64 and 128 only).
+constexpr bool head_dim_supported(int d) { return d > 0 && d <= 256 && d % 32 == 0; }
 constexpr bool atomic_head_dim(int d) { return d == 64 || d == 128; }
 // Head dims with the score-bias and dropout instances.
 constexpr bool feature_head_dim(int d) { return d == 64 || d == 128; }
@@ -145,6 +143,9 @@ hipError_t dispatch(const Problem& pb, int ft, F&& f) {
       case 64: return by_c(dt, integral_constant<int, 64>());
       case 96: return by_c(dt, integral_constant<int, 96>());
       case 128: return by_c(dt, integral_constant<int, 128>());
+      case 160: return by_c(dt, integral_constant<int, 160>());
+      case 192: return by_c(dt, integral_constant<int, 192>());
+      case 224: return by_c(dt, integral_constant<int, 224>());
       case 256: return by_c(dt, integral_constant<int, 256>());
       default: return hipErrorInvalidValue;
     }

@@ -34,9 +34,10 @@
  *     nearest even.
  *   - Every pointer must be 16-byte aligned.  A pointer may be NULL only when its
  *     tensor has no element.
- *   - d is 32, 64, 96, 128 or 256 (the Liger-Kernel pull request "[Kernel] Flash
- *     attention 2", Details, claims no restriction on the head dimension; these
- *     are the widths with a kernel instance).  The fused atomic dQ path
+ *   - d is a multiple of 32 up to 256: 32, 64, 96, 128, 160, 192, 224 or 256 (the
+ *     Liger-Kernel pull request "[Kernel] Flash attention 2", Details, claims no
+ *     restriction on the head dimension; these are the widths with a kernel
+ *     instance).  The fused atomic dQ path
  *     (FA_DQ_ATOMIC) is built for d = 64 and 128 only.  B, N_q, N_kv >= 0
  *     (zero-size calls are valid), Hq and Hkv >= 1 with Hq % Hkv == 0,
  *     N * d < 2^31 per head, B and Hq <= 65535.
@@ -59,7 +60,7 @@ extern "C" {
 #define FA_OK            0
 #define FA_ERR_NULLPTR  -1  /* required pointer is NULL */
 #define FA_ERR_SHAPE    -2  /* bad B/Hq/Hkv/N_q/N_kv, Hq % Hkv != 0, or size limits */
-#define FA_ERR_HEADDIM  -3  /* d not in {32, 64, 96, 128, 256}, or FA_DQ_ATOMIC, a bias
+#define FA_ERR_HEADDIM  -3  /* d not a multiple of 32 up to 256, or FA_DQ_ATOMIC, a bias
                                or dropout with d not in {64, 128} */
 #define FA_ERR_DTYPE    -4  /* dtype not FP16/BF16 */
 #define FA_ERR_SCALE    -5  /* softmax_scale not finite or <= 0 */

@@ -83,7 +83,7 @@ def bwd(lib, **kw):
 def test_argument_errors(lib, call):
     assert call(lib, dtype=2) == FA_ERR_DTYPE
     assert call(lib, dtype=-1) == FA_ERR_DTYPE
-    for d in (0, 8, 16, 48, 80, 112, 160, 192, 512, -64):
+    for d in (0, 8, 16, 48, 80, 112, 200, 288, 512, -64):
         assert call(lib, d=d) == FA_ERR_HEADDIM, d
     assert call(lib, Hq=3, Hkv=2) == FA_ERR_SHAPE
     assert call(lib, Hkv=0) == FA_ERR_SHAPE
@@ -118,9 +118,9 @@ def test_bwd_specific_errors(lib):
 
 
 def test_head_dims_and_the_atomic_path(lib):
-    """d in {32, 64, 96, 128, 256} is accepted (the call here then stops at the
+    """Every multiple of 32 up to 256 is accepted (the call here then stops at the
     workspace check); the fused atomic dQ kernel exists for 64 and 128 only."""
-    for d in (32, 64, 96, 128, 256):
+    for d in (32, 64, 96, 128, 160, 192, 224, 256):
         assert bwd(lib, d=d, mode=2, ws=0) == FA_ERR_WORKSPACE, d
         assert fwd(lib, d=d, q=0) == FA_ERR_NULLPTR, d
         assert lib.fa_bwd_ex_workspace_bytes(1, 2, 1, 8, 8, d, 0, 0, 2) > 0

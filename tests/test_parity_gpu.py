@@ -193,9 +193,10 @@ def test_edge_shapes(shape, device):
 
 # Head dims beyond 64 and 128 (the Liger-Kernel pull request "[Kernel] Flash
 # attention 2", Details, claims no restriction on the head dimension).  d = 32 and
-# 96 run the same kernels with one and three 32-wide contraction steps; d = 256
-# keeps 32 resident rows per wave and double-buffered tiles.  Shapes are ragged on
-# both sides and span several 256-row (d = 256: 128-row) work items.
+# 96 run the same kernels with one and three 32-wide contraction steps; d = 160,
+# 192, 224 and 256 keep 32 resident rows per wave and double-buffered tiles.
+# Shapes are ragged on both sides and span several 256-row (d > 128: 128-row) work
+# items.
 HEAD_DIM_CASES = [
     # B, Hq, Hkv, Nq, Nkv, d, dtype, causal
     (2, 4, 2, 100, 333, 32, "fp16", True),
@@ -208,6 +209,12 @@ HEAD_DIM_CASES = [
     (1, 4, 2, 600, 600, 256, "bf16", True),
     (1, 2, 1, 333, 450, 256, "bf16", False),
     (1, 4, 4, 129, 64, 256, "fp16", True),      # N_q > N_kv
+    (2, 4, 2, 100, 333, 160, "bf16", True),
+    (1, 4, 2, 300, 300, 160, "fp16", False),
+    (1, 4, 1, 400, 700, 192, "fp16", True),
+    (1, 2, 2, 257, 129, 192, "bf16", True),     # N_q > N_kv
+    (2, 4, 2, 300, 300, 224, "bf16", False),
+    (1, 4, 4, 100, 333, 224, "fp16", True),
 ]
 
 
