@@ -78,7 +78,9 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, causal: bool
     ``bias`` (q's dtype, 4-D, each dimension its full size or 1, rows 16-byte
     aligned) is added to the scaled scores; ``dropout_p`` drops probabilities with
     the library's Philox mask from ``seed`` (the same seed reproduces the same mask).
-    With a bias or dropout, d is 64 or 128 and the separate dQ path runs.
+    With a bias or dropout the separate dQ path runs; a bias that is one value per
+    (batch, key) and needs no gradient runs at every head dim, any other bias and
+    dropout at d = 64 or 128.
     """
     if q.dim() != 4:
         raise ValueError("q must be 4-D [B, Hq, Nq, d]")

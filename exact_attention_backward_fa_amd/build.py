@@ -39,9 +39,11 @@ INSTANCES = [(dt, d, c) for dt in (0, 1) for d in HEAD_DIMS for c in (0, 1)]
 ATOMIC_HEAD_DIMS = (64, 128)
 # Feature sets (1: additive score bias and its gradient, 2: bias and dropout of P,
 # 3: a per-(batch, key) bias without gradient, 4: dropout without bias) are built
-# for these head dims; every head dim has the plain set 0.
+# for these head dims, and set 3 for every head dim; every head dim has the plain
+# set 0.
 FEATURE_HEAD_DIMS = (64, 128)
 FEATURES = (1, 2, 3, 4)
+ALL_DIM_FEATURES = (3,)
 # Backward kernel families compiled per instance (FA_KIND in fa_bwd_inst.hip).
 BWD_KINDS = {0: "pre", 1: "dkdv", 2: "dq", 3: "atomic"}
 
@@ -82,7 +84,7 @@ class Unit:
 def units() -> List[Unit]:
     out = [Unit(os.path.splitext(s)[0], s) for s in SOURCES]
     for dt, d, c in INSTANCES:
-        fts = (0,) + (FEATURES if d in FEATURE_HEAD_DIMS else ())
+        fts = (0,) + tuple(ft for ft in FEATURES if d in FEATURE_HEAD_DIMS or ft in ALL_DIM_FEATURES)
         for ft in fts:
             sfx = f"{dt}_{d}_{c}" + (f"_f{ft}" if ft else "")
             out.append(Unit(f"fwd_{sfx}", "fa_fwd_inst.hip",

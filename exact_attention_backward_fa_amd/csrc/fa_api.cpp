@@ -99,7 +99,7 @@ static int check_extras(const Problem& pb, const void* bias, long long sb, long 
   if (dbias && ((uintptr_t)dbias & 15u) != 0) return FA_ERR_ALIGN;
   // dBias rows of a 128-query work item are addressed with 32-bit byte offsets
   if (dbias && pb.Nkv > (1 << 22)) return FA_ERR_BIAS;
-  if (x->ft() != FT_PLAIN && !feature_head_dim(pb.d)) return FA_ERR_HEADDIM;
+  if (x->ft() != FT_PLAIN && !feature_head_dim(x->ft(), pb.d)) return FA_ERR_HEADDIM;
   return FA_OK;
 }
 
@@ -217,7 +217,8 @@ const char* fa_status_string(int status) {
     case FA_ERR_SHAPE: return "invalid shape (B, Hq, Hkv, N_q, N_kv), Hq % Hkv != 0, or a size limit exceeded";
     case FA_ERR_HEADDIM:
       return "head dimension d must be a multiple of 32 up to 256: 32, 64, 96, 128, 160, 192, 224 "
-             "or 256 (the atomic dQ path, a score bias and dropout: 64 or 128)";
+             "or 256 (the atomic dQ path, a bias that varies along heads or rows, dBias and "
+             "dropout: 64 or 128)";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "softmax_scale must be finite and > 0";
     case FA_ERR_WORKSPACE: return "workspace is NULL, misaligned, or smaller than required";

@@ -1052,11 +1052,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         }
         if constexpr (KB) {
           // the next sub-block's: of this tile, or (step 3, after the mid-tile
-          // barrier) the next tile's first; past the last tile a buffer no product
-          // reads
+          // barrier, which completes the next tile when it is triple-buffered) the
+          // next tile's first; past the last tile a buffer no product reads.  A
+          // double-buffered next tile is complete only after the barrier in next().
           if constexpr (st < NSB - 1)
             cbk[(st + 1) % 2] = key_bias(cur, st + 1);
-          else
+          else if constexpr (NBUF > 2)
             cbk[0] = key_bias(nxt, 0);
         }
       };
@@ -1067,6 +1068,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
           // double buffering: the next tile was copied in this tile's second half
           wait_vmem();
           tile_barrier();
+          if constexpr (KB) cbk[0] = key_bias(nxt, 0);  // now complete
         }
         return dq_operand(std::integral_constant<int, 0>(), oc, Kn, Kt);
       };

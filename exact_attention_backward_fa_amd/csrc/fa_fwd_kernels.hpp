@@ -360,9 +360,11 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         // copies of step 1 may refill the previous buffer.
         wait_vmem();
         tile_barrier();
-        if constexpr (KB) {
-          // pair 0 of the next tile, complete after the barrier (pair 1 of this one
-          // reads cbk[1]); past the last tile a buffer no product reads
+        if constexpr (KB && NBUF > 2) {
+          // pair 0 of the next tile, complete after the barrier when triple-buffered
+          // (pair 1 of this one reads cbk[1]); past the last tile a buffer no product
+          // reads.  A double-buffered next tile is complete only after the barrier
+          // in next().
           cbk[0][0] = key_bias(nxt, 0, 0);
           cbk[0][1] = key_bias(nxt, 0, 1);
         }
@@ -387,6 +389,10 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
         // double buffering: the next tile was copied in this tile's second half
         wait_vmem();
         tile_barrier();
+        if constexpr (KB) {  // pair 0 of the next tile, now complete
+          cbk[0][0] = key_bias(nxt, 0, 0);
+          cbk[0][1] = key_bias(nxt, 0, 1);
+        }
       }
       return pad_row16<D>(Kn, 16 * (o / NK) + l16, 4 * (o % NK) + j4);
     };

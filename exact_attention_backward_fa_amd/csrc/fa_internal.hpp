@@ -13,8 +13,6 @@ namespace fa {
 // family but the fused atomic one, which is built for 64 and 128 only).
 constexpr bool head_dim_supported(int d) { return d > 0 && d <= 256 && d % 32 == 0; }
 constexpr bool atomic_head_dim(int d) { return d == 64 || d == 128; }
-// Head dims with the score-bias and dropout instances.
-constexpr bool feature_head_dim(int d) { return d == 64 || d == 128; }
 
 // Kernel feature set of an instance: 0 plain attention, 1 with an additive score
 // bias (and its gradient), 2 with the bias and dropout of P, 3 with a bias that
@@ -22,6 +20,11 @@ constexpr bool feature_head_dim(int d) { return d == 64 || d == 128; }
 // for it: the plain kernels' shape, the bias entering the score products; 4 with
 // dropout and no bias.
 enum : int { FT_PLAIN = 0, FT_BIAS = 1, FT_DROPOUT = 2, FT_KEYBIAS = 3, FT_DROP = 4 };
+// Head dims with the instances of feature set ft: a bias per (batch, key) at every
+// head dim; bias tiles, dBias and dropout at 64 and 128.
+constexpr bool feature_head_dim(int ft, int d) {
+  return ft == FT_KEYBIAS ? head_dim_supported(d) : (d == 64 || d == 128);
+}
 // instances that stream 2-D bias tiles through LDS (32-row shape)
 constexpr bool tile_bias(int ft) { return ft == FT_BIAS || ft == FT_DROPOUT; }
 
@@ -124,11 +127,13 @@ template <class F>
 hipError_t dispatch(const Problem& pb, int ft, F&& f) {
   using std::integral_constant;
   auto by_ft = [&](auto dt, auto d, auto c) -> hipError_t {
-    if constexpr (feature_head_dim(decltype(d)::value)) {
+    if constexpr (feature_head_dim(FT_BIAS, decltype(d)::value)) {
       if (ft == FT_BIAS) return f(dt, d, c, integral_constant<int, FT_BIAS>());
       if (ft == FT_DROPOUT) return f(dt, d, c, integral_constant<int, FT_DROPOUT>());
-      if (ft == FT_KEYBIAS) return f(dt, d, c, integral_constant<int, FT_KEYBIAS>());
       if (ft == FT_DROP) return f(dt, d, c, integral_constant<int, FT_DROP>());
+    }
+    if constexpr (feature_head_dim(FT_KEYBIAS, decltype(d)::value)) {
+      if (ft == FT_KEYBIAS) return f(dt, d, c, integral_constant<int, FT_KEYBIAS>());
     }
     if (ft != FT_PLAIN) return hipErrorInvalidValue;
     return f(dt, d, c, integral_constant<int, FT_PLAIN>());

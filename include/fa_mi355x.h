@@ -60,8 +60,9 @@ extern "C" {
 #define FA_OK            0
 #define FA_ERR_NULLPTR  -1  /* required pointer is NULL */
 #define FA_ERR_SHAPE    -2  /* bad B/Hq/Hkv/N_q/N_kv, Hq % Hkv != 0, or size limits */
-#define FA_ERR_HEADDIM  -3  /* d not a multiple of 32 up to 256, or FA_DQ_ATOMIC, a bias
-                               or dropout with d not in {64, 128} */
+#define FA_ERR_HEADDIM  -3  /* d not a multiple of 32 up to 256, or FA_DQ_ATOMIC, dBias,
+                               dropout or a bias that varies along heads or rows
+                               with d not in {64, 128} */
 #define FA_ERR_DTYPE    -4  /* dtype not FP16/BF16 */
 #define FA_ERR_SCALE    -5  /* softmax_scale not finite or <= 0 */
 #define FA_ERR_WORKSPACE -6 /* workspace NULL/misaligned or smaller than required */
@@ -190,12 +191,12 @@ int fa_bwd_auto_dq_mode(int B, int Hq, int Hkv, int Nq, int Nkv, int d,
  *   (seed low word, seed high word) is below T = floor((1 - p) * 256 + 1/2); the
  *   keep probability is T / 256 (p rounded to a multiple of 1/256).  LSE is that of
  *   the undropped P, so the backward can rebuild P from it.
- * With bias NULL and dropout_p = 0 this is fa_fwd.  A bias or dropout needs
- * d = 64 or 128 (FA_ERR_HEADDIM otherwise).  A bias with bias_stride_h =
+ * With bias NULL and dropout_p = 0 this is fa_fwd.  A bias with bias_stride_h =
  * bias_stride_q = 0 (one value per batch and key, e.g. a key-padding mask) and no
- * dropout runs on kernels as fast as the plain ones, as does its backward when no
- * dbias is asked for.  Returns FA_OK or an FA_ERR_* code; on error nothing is
- * launched or written.
+ * dropout runs at every head dim, on kernels as fast as the plain ones, as does
+ * its backward when no dbias is asked for; any other bias, and dropout, need
+ * d = 64 or 128 (FA_ERR_HEADDIM otherwise).  Returns FA_OK or an FA_ERR_* code;
+ * on error nothing is launched or written.
  */
 int fa_fwd_bias_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
                         int B, int Hq, int Hkv, int Nq, int Nkv, int d,

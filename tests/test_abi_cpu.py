@@ -238,7 +238,13 @@ def test_bias_dropout_argument_errors(lib, call):
     assert call(lib, sh=12) == FA_ERR_BIAS
     assert call(lib, sq=(1 << 22) + 8) == FA_ERR_BIAS
     assert call(lib, bias=P + 8) == FA_ERR_ALIGN
-    assert call(lib, d=96) == FA_ERR_HEADDIM     # bias needs d = 64 or 128
+    assert call(lib, d=96) == FA_ERR_HEADDIM     # a bias along rows needs d = 64 or 128
+    # a bias per (batch, key) without dBias runs at every head dim: the call goes on
+    # to the pointer checks
+    kb = {"sq": 0, "q": 0, **({"dbias": 0} if call is bwd_bd else {})}
+    for d in (32, 96, 160, 192, 224, 256):
+        assert call(lib, d=d, **kb) == FA_ERR_NULLPTR, d
+    assert call(lib, d=96, p=0.1, **kb) == FA_ERR_HEADDIM  # dropout needs d = 64 or 128
     assert call(lib, d=96, bias=0, p=0.5) == FA_ERR_HEADDIM
     assert call(lib, d=96, bias=0, sq=3, p=0.0, **({"dbias": 0} if call is bwd_bd else {})) != FA_ERR_HEADDIM
     assert call(lib, q=0) == FA_ERR_NULLPTR

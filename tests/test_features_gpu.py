@@ -138,7 +138,7 @@ def test_bias_dropout_parity(cfg, device):
 
 
 # A bias per (batch, key) with no gradient wanted (a key-padding mask, say) runs on
-# the key-bias instances: the plain kernels' 64-row shape, the bias read once per
+# the key-bias instances, at every head dim: the plain kernels' shape, the bias read once per
 # key tile (forward, dQ pass: it starts the score accumulator) or held per key
 # (dK/dV kernel).
 KEY_BIAS_CASES = [
@@ -151,6 +151,13 @@ KEY_BIAS_CASES = [
     # rising along the keys by 0.25 nats per key: the forward's rerun with a key bias
     ("kb_ramp_fp16", 1, 4, 2, 200, 333, 64, "fp16", False, "keyramp"),
     ("kb_ramp_bf16_c", 1, 4, 2, 300, 300, 128, "bf16", True, "keyramp"),
+    # the other head dims (the key-bias instances exist at every d)
+    ("kb_d32_c", 2, 4, 2, 200, 333, 32, "bf16", True, "keys"),
+    ("kb_d96_nc", 1, 4, 4, 300, 257, 96, "fp16", False, "keys"),
+    ("kb_d160_c", 1, 4, 2, 257, 300, 160, "fp16", True, "keys"),
+    ("kb_d192_nc", 1, 4, 1, 300, 400, 192, "bf16", False, "keys"),
+    ("kb_d224_c", 1, 2, 2, 129, 257, 224, "bf16", True, "keys"),
+    ("kb_d256_c", 1, 4, 2, 300, 300, 256, "fp16", True, "keyramp"),
 ]
 
 
