@@ -314,8 +314,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
     // reads, so every iteration issues the same OPS copies per wave (spread over its
     // MFMA stream) and one vmcnt bound covers them.  Waves 0-1 copy the Q tile,
     // waves 2-3 the dO tile, each through a buffer resource based at the tile's first
-    // row; rows past N_q arrive as zeros (and are masked in the math).  Every wave
-    // copies LSE and -D (identical bytes to the same place).
+    // row; rows past N_q arrive as zeros, and so do their LSE and -D, so without a
+    // bias they add nothing to dK and dV.  Every wave copies LSE and -D (identical
+    // bytes to the same place).
     using Copy = PadPairDma<D, BM>;
     struct Src {
       i32x4 t, l, d, bs;  // this wave's Q or dO tile; LSE*log2e; -D; bias (bias instances)
@@ -339,8 +340,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
       sr.d = buf_rsrc(cd, c_left * 4);
       if constexpr (BIAS) {
         // rows past N_q and a null bias read zeros (the resource ends there); a row is
-        // read in whole 16-byte pieces, up to N_kv rounded up to 8 elements; a row is
-      // read in whole 16-byte pieces, up to N_kv rounded up to 8 elements
+        // read in whole 16-byte pieces, up to N_kv rounded up to 8 elements
         const int rows = min(BM, c_left);
         const int bytes = p.bias ? 2 * ((rows - 1) * (int)p.bias_sq + (((p.Nkv + 7) & ~7) - kv0)) : 0;
         sr.bs = buf_rsrc(p.bias ? p.bias + cb : p.k, bytes);
@@ -499,9 +499,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           v = fmaf(sc[kt][i], p.scale_log2, bl[kt] - lq[i]);
         else
           v = sc[kt][i] * p.scale_log2 - lq[i];
-        if constexpr (MASK) {
+        if constexpr (MASK && (CAUSAL || BIAS || KB)) {
+          // A key past N_kv only feeds its own dK and dV rows, which are not stored.
+          // A row past N_q has zero Q, dO, LSE and -D, so without a bias its P is 1
+          // and its terms of dV (P^T dO) and dK (dS^T Q) vanish; a bias could make
+          // that P overflow the 16-bit type (and inf * 0 is NaN), so the bias
+          // instances mask such rows.
           const int key = keyl + 16 * kt, q = qrow + 16 * st + i;
-          if (key >= p.Nkv || q >= p.Nq || (CAUSAL && key > q + p.off)) v = -INFINITY;
+          if (((BIAS || KB) && q >= p.Nq) || (CAUSAL && key > q + p.off)) v = -INFINITY;
         }
         sc[kt][i] = fast_exp2(v);
       };
@@ -850,8 +855,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
       sr.t = buf_rsrc(tsrc + (size_t)k0 * D, (p.Nkv - k0) * D * 2);
       if constexpr (BIAS) {
         // rows past N_q and a null bias read zeros (the resource ends there); a row is
-        // read in whole 16-byte pieces, up to N_kv rounded up to 8 elements; a row is
-      // read in whole 16-byte pieces, up to N_kv rounded up to 8 elements
+        // read in whole 16-byte pieces, up to N_kv rounded up to 8 elements
         const int rows = min(BM, p.Nq - q0);
         const int bytes = p.bias ? 2 * ((rows - 1) * (int)p.bias_sq + (((p.Nkv + 7) & ~7) - k0)) : 0;
         sr.bs = buf_rsrc(p.bias ? p.bias + bq0 + k0 : p.k, bytes);
