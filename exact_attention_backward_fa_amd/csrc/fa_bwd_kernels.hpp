@@ -499,14 +499,17 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
           v = fmaf(sc[kt][i], p.scale_log2, bl[kt] - lq[i]);
         else
           v = sc[kt][i] * p.scale_log2 - lq[i];
-        if constexpr (MASK && (CAUSAL || BIAS || KB)) {
-          // A key past N_kv only feeds its own dK and dV rows, which are not stored.
-          // A row past N_q has zero Q, dO, LSE and -D, so without a bias its P is 1
-          // and its terms of dV (P^T dO) and dK (dS^T Q) vanish; a bias could make
-          // that P overflow the 16-bit type (and inf * 0 is NaN), so the bias
-          // instances mask such rows.
+        if constexpr (MASK && (BIAS || KB)) {
+          // a bias could make the P of a row past N_q overflow the 16-bit type (and
+          // inf * 0 is NaN): every bound
           const int key = keyl + 16 * kt, q = qrow + 16 * st + i;
-          if (((BIAS || KB) && q >= p.Nq) || (CAUSAL && key > q + p.off)) v = -INFINITY;
+          if (key >= p.Nkv || q >= p.Nq || (CAUSAL && key > q + p.off)) v = -INFINITY;
+        } else if constexpr (MASK && CAUSAL) {
+          // Only the causal bound.  A key past N_kv only feeds its own dK and dV rows,
+          // which are not stored.  A row past N_q has zero Q, dO, LSE and -D, so its
+          // P is 1 and its terms of dV (P^T dO) and dK (dS^T Q) vanish.
+          const int key = keyl + 16 * kt, q = qrow + 16 * st + i;
+          if (key > q + p.off) v = -INFINITY;
         }
         sc[kt][i] = fast_exp2(v);
       };
