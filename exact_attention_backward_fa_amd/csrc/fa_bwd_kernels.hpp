@@ -63,19 +63,22 @@ struct DqSteps {
 };
 
 // Resident rows per wave and LDS buffers per head dim and feature set: 64 rows
-// (four 16-row tiles) and triple-buffered streamed tiles up to d = 128; at
-// d = 256 the resident operands and accumulators of 64 rows exceed the 512
-// registers of a lane and three buffers the 160 KB of LDS, so a wave keeps 32
-// rows and the streamed tiles are double-buffered.  The bias and dropout
-// instances take the same shape: the bias tiles need the LDS, the bias and
-// dropout work the registers.
+// (four 16-row tiles) and triple-buffered streamed tiles up to d = 128; above
+// d = 128 the resident operands and accumulators of 64 rows exceed the 512
+// registers of a lane, so a wave keeps 32 rows, and the streamed tiles stay
+// triple-buffered while three buffers fit the 160 KB of LDS (d = 160 and 192;
+// at 192 not with the dQ pass's key-bias slots), else double-buffered.  The bias
+// and dropout instances take the 32-row shape too: the bias tiles need the LDS
+// (two buffers), the bias and dropout work the registers.
 template <int D, int FT = 0, bool KV = false>
 struct TileShape {
   // KV: the dK/dV kernel, whose 64-row shape leaves no registers for dropout at
   // d = 128
   static constexpr bool SMALL = D > 128 || tile_bias(FT) || (KV && FT == FT_DROP && D > 64);
   static constexpr int RT = SMALL ? 2 : 4;    // resident 16-row tiles per wave
-  static constexpr int NBUF = SMALL ? 2 : 3;  // LDS buffers of the streamed tiles
+  // LDS buffers of the streamed tiles
+  static constexpr int NBUF =
+      !SMALL || (!tile_bias(FT) && (D == 160 || (D == 192 && (KV || FT != FT_KEYBIAS)))) ? 3 : 2;
 };
 
 // Slots of the non-MFMA work of dK/dV step ST (NC copies in steps 2-3):

@@ -101,17 +101,20 @@ struct FwdSteps {
 };
 
 // Resident query rows per wave and LDS buffers per head dim: 64 queries (four
-// 16-row tiles) and triple-buffered key/value tiles up to d = 128; at d = 256 a
+// 16-row tiles) and triple-buffered key/value tiles up to d = 128; above d = 128 a
 // wave keeps 32 queries (Q and the O accumulators of 64 would not fit its
-// registers) and the tiles are double-buffered (three would not fit the LDS).
-// The bias-tile and dropout instances take the small shape too (the bias tiles need
-// the LDS, the bias and dropout work the registers); the key-bias instances keep the
-// plain shape.
+// registers), with three tile buffers at d = 160 and 192 and two above, where
+// three would not fit the LDS.  The bias-tile instances (with or without dropout)
+// take the small shape too (the bias tiles need the LDS, the bias and dropout work
+// the registers); the key-bias and dropout-only instances keep the plain shape.
 template <int D, int FT = 0>
 struct FwdShape {
   static constexpr bool SMALL = D > 128 || tile_bias(FT);
   static constexpr int QT = SMALL ? 2 : 4;
-  static constexpr int NBUF = SMALL ? 2 : 3;
+  // three K/V buffers while they fit the LDS (at d = 192 not beside the key-bias
+  // slots), else two
+  static constexpr int NBUF =
+      !SMALL || (!tile_bias(FT) && (D == 160 || (D == 192 && FT != FT_KEYBIAS))) ? 3 : 2;
 };
 
 // Slots of the non-MFMA work of forward step ST (NC copies in step 1): mx[t] (the
