@@ -478,12 +478,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdParams p) {
         constexpr int e = decltype(ec)::value, st = decltype(st_c)::value;
         constexpr int kt = e / 4, i = e % 4;
         if constexpr (DROP && i == 0) {
-          // One Philox call per 4 x 4 block (keys k & ~3 .., rows 0..3 of a row
-          // group): word r is row r, byte k % 4 the key.  The four lanes of a key
-          // quad share their blocks, so lane q draws one of them (key tile q % KT
-          // of sub-block st + q / KT; with two key tiles, the even step draws the
-          // odd step's blocks too) and a byte and quad transpose give every lane
-          // its bytes: word w, byte r = row r of block w of this lane's key.
+          // One Philox call per 4 x 4 block (keys k & ~3 .., rows 0..3 of a row group):
+          // word r is row r, byte k % 4 the key.  The four lanes of a key quad share
+          // their blocks, so lane j of the quad draws one of them (key tile j % KT of
+          // sub-block st + j / KT; with two key tiles, the even step draws the odd
+          // step's blocks too) and a byte and quad transpose give every lane its bytes:
+          // word w, byte r = row r of block w of this lane's key.
           constexpr bool DRAW = kt == 0 && st % (4 / KT) == 0;
           if constexpr (DRAW) {
             const int q4 = l16 & 3, bkt = q4 % KT, bst = st + q4 / KT;
@@ -1014,12 +1014,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dq_kernel(BwdParams p) {
         constexpr int e = decltype(ec)::value, st = decltype(st_c)::value, cs = st & 1;
         constexpr int t = e / 4, i = e % 4;
         if constexpr (DROP && i == 0) {
-          // One Philox call per 4 x 4 block (queries q & ~3 .., keys of a 4-key
-          // group): word q % 4 is query q, byte r key r.  The four lanes of a query
-          // quad share their blocks, so lane q draws one of them (query tile q % QT
-          // of sub-block st + q / QT; with two query tiles, the even step draws the
-          // odd step's blocks too) and a quad transpose hands every lane its word
-          // of each: word w of block w.
+          // One Philox call per 4 x 4 block (queries q & ~3 .., keys of a 4-key group):
+          // word q % 4 is query q, byte r key r.  The four lanes of a query quad share
+          // their blocks, so lane j of the quad draws one of them (query tile j % QT of
+          // sub-block st + j / QT; with two query tiles, the even step draws the odd
+          // step's blocks too) and a quad transpose hands every lane its word of each:
+          // word w of block w.
           constexpr bool DRAW = t == 0 && st % (4 / QT) == 0;
           if constexpr (DRAW) {
             const int q4 = l16 & 3, bt = q4 % QT, bst = st + q4 / QT;

@@ -485,12 +485,12 @@ __global__ __launch_bounds__(256, 1) void fwd_kernel(FwdParams p) {
             constexpr int i = decltype(ic)::value;
             if constexpr (PL.exp[sb][t][i] == mi) {
               if constexpr (DROP && i == 0) {
-                // One Philox call per 4 x 4 block (queries q & ~3 .., keys of a
-                // 4-key group): word q % 4 is query q, byte r key r.  The four lanes
-                // of a query quad share their blocks, so lane q draws one of them
-                // (query tile q % QT of sub-block sb + q / QT; with two query tiles,
-                // sub-block 0 draws sub-block 1's blocks too) and a quad transpose
-                // hands every lane its word of each: word w of block w.
+                // One Philox call per 4 x 4 block (queries q & ~3 .., keys of a 4-key
+                // group): word q % 4 is query q, byte r key r.  The four lanes of a
+                // query quad share their blocks, so lane j of the quad draws one of
+                // them (query tile j % QT of sub-block sb + j / QT; with two query
+                // tiles, sub-block 0 draws sub-block 1's blocks too) and a quad
+                // transpose hands every lane its word of each: word w of block w.
                 constexpr bool DRAW = t == 0 && sb % (4 / QT) == 0;
                 if constexpr (DRAW) {
                   const int q4 = l16 & 3, bt = q4 % QT, bsb = sb + q4 / QT;
