@@ -231,16 +231,18 @@ def test_key_bias_fully_masked_batch(device):
     assert np.all(g["dq"][1] == 0) and np.all(g["dk"][1] == 0) and np.all(g["dv"][1] == 0)
 
 
-def test_autograd_key_mask_without_grad(device):
+@pytest.mark.parametrize("d,dt", [(128, "bf16"), (96, "fp16"), (192, "bf16"), (256, "fp16")])
+def test_autograd_key_mask_without_grad(d, dt, device):
     """attention(..., bias=mask) with a key-padding mask that needs no gradient (the
-    key-bias instances) against the oracle: O and the gradients in q, k, v."""
+    key-bias instances, built at every head dim) against the oracle: O and the
+    gradients in q, k, v."""
     from exact_attention_backward_fa_amd import attention
-    B, Hq, Hkv, Nq, Nkv, d = 2, 8, 2, 257, 384, 128
-    x = inputs.make_custom(78, B, Hq, Hkv, Nq, Nkv, d, "bf16")
-    mask = torch.zeros(B, 1, 1, Nkv, dtype=torch.bfloat16)
+    B, Hq, Hkv, Nq, Nkv = 2, 8, 2, 257, 384
+    x = inputs.make_custom(78 + d, B, Hq, Hkv, Nq, Nkv, d, dt)
+    mask = torch.zeros(B, 1, 1, Nkv, dtype=inputs.TORCH_DTYPE[dt])
     mask[0, ..., 300:] = float("-inf")
     mask[1, ..., 17:40] = float("-inf")
-    case = inputs.Case("autograd_key_mask", 0, 0, B, Hq, Hkv, Nq, Nkv, d, "bf16", True, 1.0 / np.sqrt(d))
+    case = inputs.Case("autograd_key_mask", 0, 0, B, Hq, Hkv, Nq, Nkv, d, dt, True, 1.0 / np.sqrt(d))
     ref = _oracle(case, x, mask, 0.0, 0, False)
     q, k, v = (x[n].to(device).requires_grad_() for n in ("q", "k", "v"))
     o = attention(q, k, v, causal=True, bias=mask.to(device))
